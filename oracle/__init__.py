@@ -1,0 +1,12 @@
+"""Float64 CPU oracle (test infrastructure only; see yoco_oracle)."""
+
+from .yoco_oracle import (  # noqa: F401
+    attention_one_query,
+    cross_attention,
+    cross_attention_group,
+    gather_last,
+    kv_append,
+    kv_project,
+    logical_kv,
+    rms_norm,
+)

@@ -1,0 +1,240 @@
+"""Float64 CPU oracle for the YOCO cross-decoder hot path.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the library calls this module: only the
+tests, the package smoke check and the benchmark's CPU-baseline leg import it.
+It shares no code, tables or helpers with the HIP path, and it never reads a
+value that the HIP path produced: every input it sees comes from the seeded
+generators or from the pages.
+
+It is the plain, slow definition of what the three library calls compute,
+written with NumPy in float64 (bf16 and fp32 inputs convert to float64
+exactly).  Loops run over requests, heads and tokens; a matrix product is the
+only library primitive used.  Where the pages leave a step open, the reading
+taken is named in the docstring of the function it affects.
+
+Pages cited (by title and section):
+  [vLLM]  "You Only Cache Once, in vLLM" (yhshin.com), section
+          "Implementation in vLLM": the scheduling walk-through (R1 with a
+          6-token prompt, R2 with a 2-token prompt) and the statement that the
+          cross-decoder keeps only the last scheduled token of each request;
+          the metadata builder's query_start_loc / seq_lens / slot_mapping /
+          block_table fields.
+  [YOCO]  "YOCO_论文与推理数据流详解" (yuyanqi.com), §3 architecture flowchart
+          (shared projection K̂ = LN(M)W_K, V̂ = LN(M)W_V; one K/V pair appended
+          per token; every cross layer reads the same K̂, V̂), §7.4 (only the last
+          position goes through the cross-decoder), §10.3 (one append per token,
+          not per layer), §10.4 (query differs per layer, K/V are shared),
+          §13.2 (query length 1 against KV length t).
+  [KV]    "KV cache memory systems" (blog.ecitis.org), section "Cache contents"
+          (decode attention softmax(q_t K_{<=t}^T / sqrt(d_h)) V_{<=t}) and
+          section "Contiguous allocation wastes capacity" (every logical block
+          is resolved through the block table).
+
+Parity pins: every function here is pinned by tests that do not re-run its own
+formula (closed forms, invariants, library routines, the pages' worked
+examples); none is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "logical_kv",
+    "attention_one_query",
+    "cross_attention",
+    "cross_attention_group",
+    "rms_norm",
+    "kv_project",
+    "kv_append",
+    "gather_last",
+]
+
+
+def _f64(a) -> np.ndarray:
+    return np.asarray(a, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Paged cache addressing  ([KV] "Contiguous allocation wastes capacity")
+# ---------------------------------------------------------------------------
+
+def logical_kv(k_cache, v_cache, table_row, n: int):
+    """Return the first ``n`` logical K̂ and V̂ rows of one request.
+
+    The cache tensors are laid out ``[num_blocks][num_kv_heads][block_size]
+    [head_dim]``.  Logical position ``j`` lives in physical block
+    ``table_row[j // block_size]`` at offset ``j % block_size``: the block
+    table maps logical token blocks to arbitrary physical pages ([KV],
+    "Contiguous allocation wastes capacity").
+
+    Returns two float64 arrays of shape ``[n, num_kv_heads, head_dim]``.
+    """
+    bs = k_cache.shape[2]
+    table_row = np.asarray(table_row)
+    keys = []
+    values = []
+    for j in range(n):
+        block = int(table_row[j // bs])
+        offset = j % bs
+        keys.append(_f64(k_cache[block, :, offset, :]))
+        values.append(_f64(v_cache[block, :, offset, :]))
+    if n == 0:
+        hkv, d = k_cache.shape[1], k_cache.shape[3]
+        return np.zeros((0, hkv, d)), np.zeros((0, hkv, d))
+    return np.stack(keys), np.stack(values)
+
+
+# ---------------------------------------------------------------------------
+# Causal cross-attention, one query per request  ([KV] "Cache contents";
+# [YOCO] §10.4, §13.2)
+# ---------------------------------------------------------------------------
+
+def attention_one_query(q_vec, keys, values, scale: float) -> np.ndarray:
+    """softmax(scale * keys @ q) @ values for one query vector.
+
+    ``keys`` and ``values`` are ``[n, d]``; the query attends to every one of
+    the n rows (query length 1, KV length n, [YOCO] §13.2).  The maximum score
+    is subtracted before exponentiating; this leaves the softmax unchanged and
+    keeps float64 in range.
+    """
+    q_vec = _f64(q_vec)
+    keys = _f64(keys)
+    values = _f64(values)
+    scores = scale * (keys @ q_vec)
+    weights = np.exp(scores - scores.max())
+    return (weights @ values) / weights.sum()
+
+
+def cross_attention(q, k_cache, v_cache, block_table, seq_lens, scale: float):
+    """One cross layer's attention for every request and query head.
+
+    q: ``[R][Hq][D]``; caches ``[num_blocks][Hkv][block_size][D]``;
+    block_table: ``[R][max_blocks]``; seq_lens: ``[R]``.  Returns float64
+    ``[R][Hq][D]``.
+
+    Readings of the pages taken here:
+      * the context is inclusive: request r's query attends to all
+        ``seq_lens[r]`` cached tokens, its own among them ([KV] writes
+        K_{<=t}; [YOCO] §10.3 appends K̂_t before the cross layers run);
+      * query head h reads KV head ``h // (Hq // Hkv)`` (contiguous GQA groups);
+      * ``scale`` is passed in; the pages' value is 1/sqrt(head_dim);
+      * a request with an empty context yields a zero output row.
+    """
+    q = np.asarray(q)
+    num_reqs, num_q_heads, head_dim = q.shape
+    num_kv_heads = k_cache.shape[1]
+    group = num_q_heads // num_kv_heads
+    out = np.zeros((num_reqs, num_q_heads, head_dim), dtype=np.float64)
+    for r in range(num_reqs):
+        n = int(seq_lens[r])
+        if n == 0:
+            continue
+        keys, values = logical_kv(k_cache, v_cache, block_table[r], n)
+        for h in range(num_q_heads):
+            g = h // group
+            out[r, h] = attention_one_query(q[r, h], keys[:, g, :], values[:, g, :], scale)
+    return out
+
+
+def cross_attention_group(q_heads, keys, values, scale: float) -> np.ndarray:
+    """Attention of the query heads of one KV group over that group's K̂/V̂.
+
+    ``q_heads`` is ``[G][D]``, ``keys``/``values`` are ``[n][D]`` (already in
+    logical order).  Used to check sampled outputs at full size, where the
+    caller fetches one (request, KV head) slice at a time.
+    """
+    return np.stack([attention_one_query(qh, keys, values, scale) for qh in q_heads])
+
+
+# ---------------------------------------------------------------------------
+# Shared K/V projection and append  ([YOCO] §3 flowchart, §7.3, §10.3)
+# ---------------------------------------------------------------------------
+
+def rms_norm(x, weight, eps: float) -> np.ndarray:
+    """Row-wise RMSNorm: x / sqrt(mean(x^2) + eps) * weight.
+
+    The pages write the normalisation before the shared projection as "LN";
+    the self-decoder blocks use RMSNorm, and RMSNorm is the reading taken here
+    (no mean subtraction, no bias, weight multiplies the normalised row).
+    """
+    x = _f64(x)
+    weight = _f64(weight)
+    out = np.empty_like(x)
+    for t in range(x.shape[0]):
+        row = x[t]
+        out[t] = row / np.sqrt(np.mean(row * row) + eps) * weight
+    return out
+
+
+def kv_project(x, rms_weight, eps: float, w_k, w_v, num_kv_heads: int, head_dim: int):
+    """K̂ = LN(M) W_K and V̂ = LN(M) W_V for every row of M ([YOCO] §3, §10.3).
+
+    ``x`` is ``[T][hidden]``; ``w_k``/``w_v`` are ``[num_kv_heads*head_dim]
+    [hidden]`` (output features by input features), so K̂_t = W_K @ x̂_t.  No
+    bias, no positional rotation (the pages' formula has neither).
+
+    Returns ``(k, v, bound_k, bound_v)``, each float64 ``[T][Hkv][D]``.  The
+    bounds are |x̂| @ |W|^T element by element: the scale of the terms summed
+    into each output, which floating-point error bounds are stated against.
+    """
+    xh = rms_norm(x, rms_weight, eps)
+    wk = _f64(w_k)
+    wv = _f64(w_v)
+    t = xh.shape[0]
+    k = (xh @ wk.T).reshape(t, num_kv_heads, head_dim)
+    v = (xh @ wv.T).reshape(t, num_kv_heads, head_dim)
+    bk = (np.abs(xh) @ np.abs(wk).T).reshape(t, num_kv_heads, head_dim)
+    bv = (np.abs(xh) @ np.abs(wv).T).reshape(t, num_kv_heads, head_dim)
+    return k, v, bk, bv
+
+
+def kv_append(x, rms_weight, eps: float, w_k, w_v, slot_mapping, k_cache, v_cache):
+    """Project every scheduled token once and write it into its paged slot.
+
+    Returns float64 copies of both caches with the new rows written.  Token t
+    with ``slot_mapping[t] >= 0`` goes to block ``slot // block_size``, offset
+    ``slot % block_size``, for every KV head; tokens with a negative slot
+    (graph padding) are skipped and write nothing ([vLLM] metadata builder:
+    slot_mapping passes through to the attention layers; [YOCO] §10.3: one
+    K/V pair per token, not one per cross layer).
+    """
+    num_blocks, num_kv_heads, bs, head_dim = k_cache.shape
+    k, v, _, _ = kv_project(x, rms_weight, eps, w_k, w_v, num_kv_heads, head_dim)
+    k_out = _f64(k_cache).copy()
+    v_out = _f64(v_cache).copy()
+    for t, slot in enumerate(np.asarray(slot_mapping)):
+        slot = int(slot)
+        if slot < 0:
+            continue
+        block, offset = divmod(slot, bs)
+        k_out[block, :, offset, :] = k[t]
+        v_out[block, :, offset, :] = v[t]
+    return k_out, v_out
+
+
+# ---------------------------------------------------------------------------
+# Last scheduled token of each request  ([vLLM] "Implementation in vLLM";
+# [YOCO] §7.4)
+# ---------------------------------------------------------------------------
+
+def gather_last(hidden, cu_seqlens):
+    """Select each request's last scheduled row of a token-major batch.
+
+    ``hidden`` is ``[T][...]`` (any dtype; rows are copied bit for bit) and
+    ``cu_seqlens`` is ``[R+1]`` with request r owning rows
+    ``cu_seqlens[r] .. cu_seqlens[r+1]-1``.  Returns ``(rows, index)``:
+    ``rows[r] = hidden[cu_seqlens[r+1]-1]`` and ``index[r]`` that row number.
+    A request with no scheduled rows gets a zero row and index -1 (a reading:
+    the pages assume every scheduled request has a current token).
+    """
+    hidden = np.asarray(hidden)
+    cu = [int(c) for c in np.asarray(cu_seqlens)]
+    num_reqs = len(cu) - 1
+    rows = np.zeros((num_reqs,) + hidden.shape[1:], dtype=hidden.dtype)
+    index = np.full(num_reqs, -1, dtype=np.int32)
+    for r in range(num_reqs):
+        if cu[r + 1] > cu[r]:
+            index[r] = cu[r + 1] - 1
+            rows[r] = hidden[cu[r + 1] - 1]
+    return rows, index

@@ -1,0 +1,171 @@
+"""Plant plausible mistakes in copies of the oracle (on the CPU) and require
+each one to fail at least one pin: evidence that the pins can tell a wrong
+oracle from a right one."""
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import yoco_oracle as yo
+from tests import oracle_pins as pins
+
+
+def _attn_variant(score_fn=None, group_fn=None, n_fn=None, locate=None, combine=None):
+    """A copy of the oracle's attention with one step replaced."""
+    def attn(q, k_cache, v_cache, block_table, seq_lens, scale):
+        q = np.asarray(q)
+        nreq, hq, d = q.shape
+        hkv = k_cache.shape[1]
+        bs = k_cache.shape[2]
+        out = np.zeros((nreq, hq, d))
+        for r in range(nreq):
+            n = int(seq_lens[r]) if n_fn is None else n_fn(int(seq_lens[r]))
+            if n <= 0:
+                continue
+            ks, vs = [], []
+            for j in range(n):
+                blk, off = (block_table[r][j // bs], j % bs) if locate is None else locate(block_table[r], j, bs)
+                ks.append(np.asarray(k_cache[blk, :, off, :], dtype=np.float64))
+                vs.append(np.asarray(v_cache[blk, :, off, :], dtype=np.float64))
+            ks, vs = np.stack(ks), np.stack(vs)
+            for h in range(hq):
+                g = h // (hq // hkv) if group_fn is None else group_fn(h, hq, hkv)
+                s = scale * (ks[:, g, :] @ q[r, h]) if score_fn is None else score_fn(ks[:, g, :], q[r, h], scale)
+                if combine is None:
+                    w = np.exp(s - s.max())
+                    out[r, h] = (w @ vs[:, g, :]) / w.sum()
+                else:
+                    out[r, h] = combine(s, ks[:, g, :], vs[:, g, :])
+        return out
+    return attn
+
+
+ATTN_MUTANTS = {
+    "scale_dropped": _attn_variant(score_fn=lambda k, q, s: k @ q),
+    "sign_flipped": _attn_variant(score_fn=lambda k, q, s: -s * (k @ q)),
+    "gqa_interleaved": _attn_variant(group_fn=lambda h, hq, hkv: h % hkv),
+    "context_exclusive": _attn_variant(n_fn=lambda n: n - 1),
+    "block_offset_swapped": _attn_variant(locate=lambda t, j, bs: (t[j % bs], j // bs) if j % bs < len(t) else (t[0], 0)),
+    "no_normalisation": _attn_variant(combine=lambda s, k, v: np.exp(s - s.max()) @ v),
+    "keys_as_values": _attn_variant(combine=lambda s, k, v: (np.exp(s - s.max()) @ k) / np.exp(s - s.max()).sum()),
+    "no_max_subtraction": _attn_variant(combine=lambda s, k, v: (np.exp(s) @ v) / np.exp(s).sum()),
+}
+
+
+def _proj_variant(norm=None, post=None):
+    def project(x, rms_weight, eps, w_k, w_v, num_kv_heads, head_dim):
+        x = np.asarray(x, dtype=np.float64)
+        w = np.asarray(rms_weight, dtype=np.float64)
+        xh = yo.rms_norm(x, w, eps) if norm is None else norm(x, w, eps)
+        wk = np.asarray(w_k, dtype=np.float64)
+        wv = np.asarray(w_v, dtype=np.float64)
+        t = x.shape[0]
+        k = xh @ wk.T
+        v = xh @ wv.T
+        if post is not None:
+            k, v = post(k, v, num_kv_heads, head_dim)
+        k = k.reshape(t, num_kv_heads, head_dim)
+        v = v.reshape(t, num_kv_heads, head_dim)
+        bk = (np.abs(xh) @ np.abs(wk).T).reshape(t, num_kv_heads, head_dim)
+        bv = (np.abs(xh) @ np.abs(wv).T).reshape(t, num_kv_heads, head_dim)
+        return k, v, bk, bv
+    return project
+
+
+def _dh_order(k, v, hkv, d):
+    t = k.shape[0]
+    return (k.reshape(t, d, hkv).transpose(0, 2, 1).reshape(t, -1),
+            v.reshape(t, d, hkv).transpose(0, 2, 1).reshape(t, -1))
+
+
+PROJ_MUTANTS = {
+    "sum_not_mean": _proj_variant(norm=lambda x, w, e: x / np.sqrt((x * x).sum(axis=1, keepdims=True) + e) * w),
+    "eps_outside_sqrt": _proj_variant(norm=lambda x, w, e: x / (np.sqrt((x * x).mean(axis=1, keepdims=True)) + e) * w),
+    "weight_ignored": _proj_variant(norm=lambda x, w, e: x / np.sqrt((x * x).mean(axis=1, keepdims=True) + e)),
+    "layernorm_centred": _proj_variant(norm=lambda x, w, e: (x - x.mean(axis=1, keepdims=True))
+                                       / np.sqrt(x.var(axis=1, keepdims=True) + e) * w),
+    "k_v_swapped": _proj_variant(post=lambda k, v, h, d: (v, k)),
+    "head_dim_order": _proj_variant(post=_dh_order),
+}
+
+
+def _append_variant(decompose):
+    def append(x, rms_weight, eps, w_k, w_v, slot_mapping, k_cache, v_cache):
+        nb, hkv, bs, d = k_cache.shape
+        k, v, _, _ = yo.kv_project(x, rms_weight, eps, w_k, w_v, hkv, d)
+        kc = np.asarray(k_cache, dtype=np.float64).copy()
+        vc = np.asarray(v_cache, dtype=np.float64).copy()
+        for t, slot in enumerate(slot_mapping):
+            res = decompose(int(slot), bs, nb)
+            if res is None:
+                continue
+            kc[res[0], :, res[1], :] = k[t]
+            vc[res[0], :, res[1], :] = v[t]
+        return kc, vc
+    return append
+
+
+APPEND_MUTANTS = {
+    "offset_block_swapped": _append_variant(lambda s, bs, nb: None if s < 0 else (s % bs, s // bs) if s % bs < nb and s // bs < bs else (0, 0)),
+    "padding_not_skipped": _append_variant(lambda s, bs, nb: divmod(s % (nb * bs), bs)),
+}
+
+
+def _gather_variant(pick):
+    def gather(hidden, cu_seqlens):
+        hidden = np.asarray(hidden)
+        cu = [int(c) for c in cu_seqlens]
+        rows = np.zeros((len(cu) - 1,) + hidden.shape[1:], dtype=hidden.dtype)
+        idx = np.full(len(cu) - 1, -1, dtype=np.int32)
+        for r in range(len(cu) - 1):
+            i = pick(cu, r)
+            if i is not None and 0 <= i < hidden.shape[0]:
+                idx[r] = i
+                rows[r] = hidden[i]
+        return rows, idx
+    return gather
+
+
+GATHER_MUTANTS = {
+    "first_token": _gather_variant(lambda cu, r: cu[r] if cu[r + 1] > cu[r] else None),
+    "off_by_one": _gather_variant(lambda cu, r: cu[r + 1] if cu[r + 1] > cu[r] else None),
+    "empty_not_handled": _gather_variant(lambda cu, r: cu[r + 1] - 1),
+}
+
+
+def _fails_some(checks, fn):
+    failures = 0
+    for check in checks:
+        try:
+            with np.errstate(all="ignore"):
+                check(fn)
+        except (AssertionError, ValueError, IndexError):
+            failures += 1
+    return failures
+
+
+@pytest.mark.parametrize("name", sorted(ATTN_MUTANTS))
+def test_attention_mutant_is_caught(name):
+    assert _fails_some(pins.ATTN_CHECKS, ATTN_MUTANTS[name]) > 0
+
+
+@pytest.mark.parametrize("name", sorted(PROJ_MUTANTS))
+def test_projection_mutant_is_caught(name):
+    assert _fails_some(pins.PROJ_CHECKS, PROJ_MUTANTS[name]) > 0
+
+
+@pytest.mark.parametrize("name", sorted(APPEND_MUTANTS))
+def test_append_mutant_is_caught(name):
+    assert _fails_some(pins.APPEND_CHECKS, APPEND_MUTANTS[name]) > 0
+
+
+@pytest.mark.parametrize("name", sorted(GATHER_MUTANTS))
+def test_gather_mutant_is_caught(name):
+    assert _fails_some(pins.GATHER_CHECKS, GATHER_MUTANTS[name]) > 0
+
+
+def test_unmutated_copies_pass():
+    """The mutant scaffolding itself is faithful when nothing is planted."""
+    assert _fails_some(pins.ATTN_CHECKS, _attn_variant()) == 0
+    assert _fails_some(pins.PROJ_CHECKS, _proj_variant()) == 0
+    assert _fails_some(pins.GATHER_CHECKS, oracle.gather_last) == 0
