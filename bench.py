@@ -1,0 +1,246 @@
+"""Benchmark of one YOCO cross-decoder step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: yoco_kv_append of the
+step's new tokens into the shared cache, yoco_gather_last of each request's
+last row, then the L cross layers in order, each one yoco_cross_attn over the
+same cache (layer l walks its work items in reverse when l is odd, so a layer
+starts where the previous one ended in the last-level cache).
+
+Default workload: decode64 -- 64 decoding requests with contexts drawn from
+U{1024..8192}, bf16 cache of 2 KV heads x 256 dims in blocks of 16, 10 cross
+layers of 8 query heads, hidden 2048.  Inputs are synthetic and seeded and sit
+in HBM before timing starts.  Between steps a 512 MiB buffer is written so the
+256 MB last-level cache starts cold each step (other model work would evict
+it); that write is outside the step's events.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "cross-attn decode tokens/s & achieved HBM GB/s (% of 8 TB/s) on 1 MI355X"
+HBM_PEAK_GBPS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=2, help="synthetic workload id (1-5); 2 = decode64")
+    p.add_argument("--partition-tokens", type=int, default=0, help="0 = library default")
+    p.add_argument("--no-flush", action="store_true", help="keep the last-level cache warm between steps")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--seed", type=int, default=2024)
+    return p.parse_args()
+
+
+def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s):
+    """Time the float64 oracle on host cores on a bounded sample of the same
+    step: whole requests (append of their new token, gather, layer-0
+    attention), scaled to all L layers per request."""
+    import threadpoolctl
+    import torch
+
+    import oracle
+
+    geom = meta.geom
+    scale = 1.0 / math.sqrt(geom.head_dim)
+    bs = geom.block_size
+    w_host = (w_rms.float().cpu().numpy(), w_k.float().cpu().numpy(), w_v.float().cpu().numpy())
+    x_host = x.float().cpu().numpy()
+    done = 0
+    t_attn = 0.0
+    t_other = 0.0
+    with threadpoolctl.threadpool_limits(limits=1):
+        for r in range(meta.num_reqs):
+            n = int(meta.seq_lens[r])
+            nb = -(-n // bs)
+            blocks = torch.from_numpy(meta.block_table[r, :nb].astype(np.int64)).to(k.device)
+            kc = k.index_select(0, blocks).float().cpu().numpy()
+            vc = v.index_select(0, blocks).float().cpu().numpy()
+            qh = q[0, r:r + 1].float().cpu().numpy()
+            tok = slice(int(meta.cu_seqlens[r]), int(meta.cu_seqlens[r + 1]))
+            t0 = time.perf_counter()
+            oracle.kv_project(x_host[tok], *w_host[:1], 1e-6, w_host[1], w_host[2], geom.num_kv_heads, geom.head_dim)
+            oracle.gather_last(x_host[tok], np.array([0, tok.stop - tok.start]))
+            t1 = time.perf_counter()
+            oracle.cross_attention(qh, kc, vc, np.arange(nb)[None, :], np.array([n]), scale)
+            t2 = time.perf_counter()
+            t_other += t1 - t0
+            t_attn += t2 - t1
+            done += 1
+            if t_other + t_attn > budget_s:
+                break
+    per_req = t_other / done + geom.num_layers * t_attn / done
+    return {
+        "value": 1.0 / per_req,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": (f"{done} of {meta.num_reqs} requests: append + gather + layer-0 attention timed "
+                   f"({t_other + t_attn:.1f} s), attention scaled to {geom.num_layers} layers; BLAS limited to 1 thread"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+              "(the hot path runs on a single MI355X).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from yoco_shared_kv_gather_amd import binding as yb
+    from yoco_shared_kv_gather_amd import bytes_model as bm
+    from yoco_shared_kv_gather_amd import synth
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    yb.lib()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    meta = synth.make_metadata(args.workload, "full", args.seed)
+    geom = meta.geom
+    log(f"workload {geom.name}: {meta.num_reqs} requests, {int(meta.seq_lens.sum())} context tokens, "
+        f"{geom.num_layers} layers")
+    k, v = synth.make_cache(meta, dev, args.seed)
+    q = synth.make_queries(meta, dev, args.seed)
+    x, w_rms, w_k, w_v = synth.make_append_inputs(meta, dev, args.seed)
+    table = torch.from_numpy(meta.block_table).to(dev)
+    seq = torch.from_numpy(meta.seq_lens).to(dev)
+    cu = torch.from_numpy(meta.cu_seqlens).to(dev)
+    slots = torch.from_numpy(meta.slot_mapping).to(dev)
+    code = yb.DTYPE_BF16 if geom.dtype == "bf16" else yb.DTYPE_F32
+    part, nparts = yb.describe_launch(meta.num_reqs, geom.num_kv_heads, geom.head_dim, meta.max_seq_len,
+                                      args.partition_tokens)
+    ws = torch.zeros(max(1, yb.cross_attn_workspace_size(meta.num_reqs, geom.num_q_heads, geom.num_kv_heads,
+                                                         geom.head_dim, meta.max_seq_len, args.partition_tokens)),
+                     dtype=torch.uint8, device=dev)
+    ws_append = torch.zeros(max(1, yb.kv_append_workspace_size(code, geom.hidden, geom.num_kv_heads, geom.head_dim)),
+                            dtype=torch.uint8, device=dev)
+    outs = torch.empty((geom.num_layers, meta.num_reqs, geom.num_q_heads, geom.head_dim), dtype=torch.float32,
+                       device=dev)
+    rows = torch.empty((meta.num_reqs, geom.hidden), dtype=x.dtype, device=dev)
+    rows_idx = torch.empty(meta.num_reqs, dtype=torch.int32, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    L = geom.num_layers
+
+    def step(ev_layers=None):
+        yb.kv_append(x, w_rms, 1e-6, w_k, w_v, slots, k, v, workspace=ws_append, stream=stream)
+        yb.gather_last(x, cu, out=rows, out_index=rows_idx, stream=stream)
+        for l in range(L):
+            if ev_layers is not None:
+                ev_layers[l][0].record(stream)
+            yb.cross_attn(q[l], k, v, table, seq, meta.max_seq_len, partition_tokens=args.partition_tokens,
+                          flags=l & 1, out=outs[l], workspace=ws, stream=stream)
+            if ev_layers is not None:
+                ev_layers[l][1].record(stream)
+
+    for i in range(args.warmup):
+        if not args.no_flush:
+            flush.fill_(i & 0xFF)
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps); partition_tokens {part}, {nparts} partitions per request")
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev_l = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
+            for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.fill_((i + 7) & 0xFF)
+        ev[i][0].record(stream)
+        step(ev_l[i])
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    layer_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in ev_l])
+    ms_per_step = float(step_ms.mean())
+    tokens_per_s = meta.num_reqs / (ms_per_step * 1e-3)
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (events), wall {1e3 * wall / args.steps:.3f} ms/step")
+
+    layer_bytes = bm.attn_layer_bytes(meta.seq_lens, geom.num_q_heads, geom.num_kv_heads, geom.head_dim,
+                                      geom.block_size, geom.elem_bytes)
+    written = int((meta.slot_mapping >= 0).sum())
+    step_bytes = (L * layer_bytes
+                  + bm.append_bytes(meta.num_tokens, geom.hidden, geom.num_kv_heads, geom.head_dim, geom.elem_bytes,
+                                    written)
+                  + bm.gather_bytes(meta.num_reqs, geom.hidden * geom.elem_bytes))
+    attn_us = float(layer_ms.mean()) * 1e3
+    achieved = layer_bytes / (attn_us * 1e-6) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": geom.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": geom.name,
+            "num_reqs": meta.num_reqs,
+            "context_tokens": int(meta.seq_lens.sum()),
+            "num_layers": L,
+            "num_q_heads": geom.num_q_heads,
+            "num_kv_heads": geom.num_kv_heads,
+            "head_dim": geom.head_dim,
+            "block_size": geom.block_size,
+            "hidden": geom.hidden,
+            "partition_tokens": part,
+            "partitions_per_request": nparts,
+            "llc_flushed_between_steps": not args.no_flush,
+            "parallelism": "single GPU",
+        },
+        "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
+        "roofline": {
+            "kernel": "cross_attn_partial_kernel",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "bytes_per_launch": layer_bytes,
+            "avg_launch_us": round(attn_us, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,223 @@
+/*
+ * yoco.h -- C ABI of the YOCO cross-decoder hot path on AMD MI355X (gfx950).
+ *
+ * YOCO ("You Only Cache Once") splits a decoder into a self-decoder that
+ * writes one shared, token-level K/V cache and a cross-decoder whose layers
+ * each issue their own query and all read that same cache.  This library
+ * implements the three steps of the cross-decoder side of one inference step:
+ *
+ *   yoco_kv_append   K^ = RMSNorm(M) W_K, V^ = RMSNorm(M) W_V for every
+ *                    scheduled token, written once into the paged cache.
+ *   yoco_gather_last keep only each request's last scheduled token.
+ *   yoco_cross_attn  one cross layer: each request's query heads attend to
+ *                    the request's whole context in the shared paged cache.
+ *
+ * Conventions shared by every call
+ *   - All data pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or synchronises; every call is asynchronous on
+ *     `stream` (a hipStream_t; NULL means the null stream) and may be
+ *     captured in a HIP graph.  A call that returns YOCO_OK has only
+ *     enqueued work.
+ *   - Scalar arguments are validated on the host BEFORE anything is
+ *     launched; on failure nothing is enqueued and a status code is returned
+ *     (yoco_last_error_message() gives the reason, per calling thread).
+ *   - Device-side index data (cu_seqlens, slot_mapping, block_table,
+ *     seq_lens) is not validated: the stated preconditions are the caller's.
+ *     Kernels never read or write outside the buffers the arguments describe
+ *     even when an index breaks them (such entries are skipped); the numbers
+ *     produced for the affected rows are then unspecified.
+ *   - Paged cache layout: two tensors, K and V, each
+ *         [num_blocks][num_kv_heads][block_size][head_dim]
+ *     row-major in the cache dtype.  Token j of a request lives in physical
+ *     block block_table[r][j / block_size], row j % block_size; a slot number
+ *     s names block s / block_size, row s % block_size.
+ *   - dtype: YOCO_DTYPE_F32 (fp32 everywhere) or YOCO_DTYPE_BF16 (bf16
+ *     cache, queries, activations and weights; fp32 accumulation; attention
+ *     output is always fp32).
+ *
+ * The operations are defined on these pages (cited by title and section):
+ *   [vLLM] "You Only Cache Once, in vLLM", section "Implementation in vLLM".
+ *   [YOCO] "YOCO_论文与推理数据流详解", sections 3, 7.4, 9, 10.3, 10.4, 13.
+ *   [KV]   "KV cache memory systems", sections "Cache contents" and
+ *          "Contiguous allocation wastes capacity".
+ */
+#ifndef YOCO_H_
+#define YOCO_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define YOCO_ABI_VERSION 1
+
+typedef enum yoco_status {
+  YOCO_OK = 0,
+  YOCO_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, inconsistent shapes */
+  YOCO_ERR_UNSUPPORTED = 2,        /* a valid shape this build has no kernel for */
+  YOCO_ERR_WORKSPACE_TOO_SMALL = 3,
+  YOCO_ERR_HIP = 4                 /* the HIP runtime refused a launch */
+} yoco_status_t;
+
+typedef enum yoco_dtype { YOCO_DTYPE_F32 = 0, YOCO_DTYPE_BF16 = 1 } yoco_dtype_t;
+
+/* yoco_cross_attn flag: walk the (request, KV head, partition) work items in
+ * reverse order.  Alternating it between consecutive cross layers makes the
+ * first blocks a layer reads the last ones the previous layer read, which may
+ * still sit in the GPU's last-level cache.  Results are bit-identical either
+ * way. */
+#define YOCO_FLAG_REVERSE_ORDER 1u
+
+/* Version of this ABI (YOCO_ABI_VERSION). */
+int32_t yoco_abi_version(void);
+
+/* Static text for a status code. */
+const char* yoco_status_string(int32_t status);
+
+/* Reason for the most recent non-OK status returned on the calling thread
+ * (empty string if none). */
+const char* yoco_last_error_message(void);
+
+/*
+ * yoco_gather_last -- one row per request: its last scheduled token.
+ *
+ * [vLLM] "Implementation in vLLM": within one mixed prefill/decode step the
+ * cross-decoder needs only the last scheduled token of each request, so its
+ * batch collapses to one row per request.  [YOCO] section 7.4: only the last
+ * prompt position enters the cross-decoder at prefill; at decode it is the
+ * new token.
+ *
+ *   hidden      [num_tokens][row_bytes], token-major, row stride row_bytes.
+ *               Rows are copied bit for bit (any element type).
+ *   num_tokens  rows in hidden (graph-padding rows included), >= 0.
+ *   row_bytes   bytes per row; must be a positive multiple of 16, and hidden
+ *               and out must be 16-byte aligned.
+ *   cu_seqlens  int32 [num_reqs + 1]: request r owns rows
+ *               cu_seqlens[r] .. cu_seqlens[r+1]-1.  Precondition:
+ *               non-decreasing, within [0, num_tokens].
+ *   out         [num_reqs][row_bytes]: out[r] = hidden[cu_seqlens[r+1]-1].
+ *               A request with no rows (or whose row index falls outside
+ *               [0, num_tokens)) gets a row of zero bytes.
+ *   out_index   optional int32 [num_reqs] (may be NULL): the row taken, or -1.
+ *
+ * Errors: YOCO_ERR_INVALID_ARGUMENT for null pointers (other than
+ * out_index), negative counts, bad row_bytes or misalignment.  num_reqs == 0
+ * is a no-op.
+ */
+int32_t yoco_gather_last(const void* hidden, int64_t num_tokens, int64_t row_bytes,
+                         const int32_t* cu_seqlens, int32_t num_reqs,
+                         void* out, int32_t* out_index, void* stream);
+
+/*
+ * yoco_kv_append -- the shared K/V projection, once per token, into the cache.
+ *
+ * [YOCO] section 3 (architecture flowchart) and section 10.3: from the
+ * self-decoder output M, K^ = LN(M) W_K and V^ = LN(M) W_V are computed once
+ * per token and appended to the single global cache that every cross layer
+ * reads; nothing is appended per cross layer.  LN is read as RMSNorm:
+ *     xhat = x / sqrt(mean(x^2) + eps) * rms_weight
+ *     K^_t = W_K xhat_t,  V^_t = W_V xhat_t      (no bias)
+ * and K^_t, V^_t (each [num_kv_heads][head_dim]) are written to slot
+ * slot_mapping[t] of the K and V caches.  [vLLM] "Implementation in vLLM":
+ * slot_mapping is the per-token slot list of the attention metadata.
+ *
+ *   dtype        YOCO_DTYPE_F32 or YOCO_DTYPE_BF16: type of x, rms_weight,
+ *                w_k, w_v and the cache.
+ *   x            [num_tokens][hidden] row-major.
+ *   rms_weight   [hidden].
+ *   eps          added to mean(x^2) inside the square root, >= 0.
+ *   w_k, w_v     [num_kv_heads*head_dim][hidden] row-major (output features
+ *                by input features).
+ *   slot_mapping int32 [num_tokens]; a negative slot (graph padding) skips
+ *                the token.  Precondition: non-negative slots are distinct
+ *                and < num_blocks*block_size (larger ones are skipped).
+ *   k_cache, v_cache  the shared cache (layout above), updated in place.
+ *   workspace    device scratch of at least yoco_kv_append_workspace_size()
+ *                bytes (bf16 only; may be NULL when that size is 0).
+ *
+ * bf16 arithmetic: rms_weight is folded into the weights (rounded to bf16),
+ * products accumulate in fp32 on the matrix cores, the RMS scale is applied
+ * in fp32 and the result is rounded to bf16 (nearest-even).  fp32: plain
+ * fp32 throughout.
+ *
+ * Supported: hidden a positive multiple of 64; head_dim in {64, 128, 256};
+ * block_size a power of two in [1, 256].
+ * Errors: YOCO_ERR_INVALID_ARGUMENT, YOCO_ERR_UNSUPPORTED,
+ * YOCO_ERR_WORKSPACE_TOO_SMALL.  num_tokens == 0 is a no-op.
+ */
+int64_t yoco_kv_append_workspace_size(int32_t dtype, int32_t hidden, int32_t num_kv_heads,
+                                      int32_t head_dim);
+int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_tokens, int32_t hidden,
+                       const void* rms_weight, float eps, const void* w_k, const void* w_v,
+                       const int32_t* slot_mapping, void* k_cache, void* v_cache,
+                       int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                       int32_t head_dim, void* workspace, int64_t workspace_bytes,
+                       void* stream);
+
+/*
+ * yoco_cross_attn -- one cross layer's attention over the shared cache.
+ *
+ * [KV] "Cache contents": at decode the current query attends to every cached
+ * key and value, softmax(q_t K_{<=t}^T / sqrt(d_h)) V_{<=t}.  [YOCO] sections
+ * 10.4 and 13.2: each cross layer has its own query for the current position
+ * only (query length 1) and reads the same K^/V^ as every other layer, over
+ * the request's whole context (KV length t).  [KV] "Contiguous allocation
+ * wastes capacity": every logical block is resolved through the block table.
+ *
+ * For request r with n = seq_lens[r] and query head h (KV head
+ * g = h / (num_q_heads / num_kv_heads)):
+ *     out[r][h] = sum_j softmax_j(scale * q[r][h] . K^[r][j][g]) V^[r][j][g],
+ *     j = 0 .. n-1 (the current token's own K^/V^ included).
+ * n == 0 gives a zero row.
+ *
+ *   dtype        type of q and the cache.
+ *   q            [num_seqs][num_q_heads][head_dim].
+ *   k_cache, v_cache  the shared cache (layout above), read only.
+ *   block_table  int32 [num_seqs][max_blocks_per_seq].  Precondition:
+ *                entries used by a context lie in [0, num_blocks) (tokens in
+ *                out-of-range blocks are skipped).
+ *   seq_lens     int32 [num_seqs]; values are clamped to
+ *                [0, min(max_seq_len, max_blocks_per_seq*block_size)].
+ *   max_seq_len  an upper bound of seq_lens; sizes the split into partitions.
+ *   scale        softmax scale; the pages' value is 1/sqrt(head_dim).
+ *   partition_tokens  tokens per split-KV partition: 0 picks one from the
+ *                shape (yoco_cross_attn_partition_tokens), otherwise a
+ *                positive multiple of 64.
+ *   flags        YOCO_FLAG_REVERSE_ORDER or 0.
+ *   out          fp32 [num_seqs][num_q_heads][head_dim].
+ *   workspace    device scratch of at least yoco_cross_attn_workspace_size()
+ *                bytes for the same arguments (per-(request, KV head)
+ *                arrival counters followed by the partitions' partial
+ *                results); may be NULL when that size is 0.  It must be
+ *                zero-filled before its first use; every call leaves the
+ *                counters zero again.  Calls that may run concurrently (other
+ *                streams) need separate workspaces.
+ *
+ * Supported: head_dim in {64, 128, 256}; num_q_heads / num_kv_heads in
+ * {1, 2, 4, 8}; block_size a power of two in [1, 256]; at most 65535
+ * partitions per request.
+ * Errors: YOCO_ERR_INVALID_ARGUMENT, YOCO_ERR_UNSUPPORTED,
+ * YOCO_ERR_WORKSPACE_TOO_SMALL, YOCO_ERR_HIP.  num_seqs == 0 is a no-op.
+ * Results are deterministic: the same inputs give the same bits, with or
+ * without YOCO_FLAG_REVERSE_ORDER.
+ */
+int32_t yoco_cross_attn_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t max_seq_len, int32_t partition_tokens);
+int64_t yoco_cross_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t max_seq_len,
+                                       int32_t partition_tokens);
+int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                        const void* k_cache, const void* v_cache, int32_t num_blocks,
+                        int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                        const int32_t* block_table, int32_t max_blocks_per_seq,
+                        const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                        int32_t partition_tokens, uint32_t flags, float* out,
+                        void* workspace, int64_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* YOCO_H_ */

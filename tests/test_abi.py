@@ -1,0 +1,123 @@
+"""The C ABI library without a GPU: it loads, exports every call that
+include/yoco.h declares, and rejects bad scalar arguments before launching
+anything (these calls return before any HIP call is made)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from yoco_shared_kv_gather_amd import binding as yb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "yoco.h")
+FAKE = 4096          # a non-null, 16-byte aligned address that is never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(yoco_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("yoco_gather_last", "yoco_kv_append", "yoco_cross_attn"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(yb.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(yb.SIGNATURES)
+
+
+def test_version_and_status_strings():
+    lib = yb.lib()
+    assert lib.yoco_abi_version() == yb.ABI_VERSION
+    for code, text in [(0, "ok"), (1, "invalid argument"), (2, "unsupported shape"),
+                       (3, "workspace too small"), (4, "HIP runtime error")]:
+        assert yb.status_string(code) == text
+
+
+def _attn(**kw):
+    args = dict(dtype=1, q=FAKE, num_seqs=2, num_q_heads=8, k=FAKE, v=FAKE, num_blocks=10, num_kv_heads=2,
+                block_size=16, head_dim=128, table=FAKE, max_blocks=4, seq_lens=FAKE, max_seq_len=64, scale=0.1,
+                part=0, flags=0, out=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return yb.lib().yoco_cross_attn(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), yb.YOCO_ERR_UNSUPPORTED),
+    (dict(num_q_heads=6, num_kv_heads=4), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(num_q_heads=48, num_kv_heads=2), yb.YOCO_ERR_UNSUPPORTED),
+    (dict(block_size=12), yb.YOCO_ERR_UNSUPPORTED),
+    (dict(part=100), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(dtype=7), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(flags=2), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(q=None), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(q=FAKE + 4), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(num_seqs=-1), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(max_seq_len=100000, part=64, ws_bytes=16), yb.YOCO_ERR_WORKSPACE_TOO_SMALL),
+    (dict(scale=float("nan")), yb.YOCO_ERR_INVALID_ARGUMENT),
+])
+def test_cross_attn_rejects_before_launch(kw, status):
+    assert _attn(**kw) == status
+    assert yb.last_error_message()
+
+
+def test_cross_attn_empty_batch_is_a_noop():
+    assert _attn(num_seqs=0) == yb.YOCO_OK
+
+
+def test_workspace_and_partition_sizes():
+    # one partition needs no workspace
+    assert yb.cross_attn_workspace_size(4, 8, 2, 128, 64, 64) == 0
+    p = yb.cross_attn_partition_tokens(1, 8, 128, 524288, 0)
+    assert p % 64 == 0 and -(-524288 // p) >= 256
+    np_ = -(-1000 // 64)
+    size = yb.cross_attn_workspace_size(3, 8, 2, 128, 1000, 64)
+    counters = 256                              # 3 requests x 2 KV heads x 4 bytes, padded
+    acc = 3 * 8 * np_ * 128 * 4
+    assert size == counters + -(-acc // 256) * 256 + 3 * 8 * np_ * 2 * 4
+    assert yb.kv_append_workspace_size(yb.DTYPE_BF16, 3072, 8, 128) == 2 * 1024 * 3072 * 2
+    assert yb.kv_append_workspace_size(yb.DTYPE_F32, 256, 1, 64) == 0
+
+
+def _append(**kw):
+    args = dict(dtype=1, x=FAKE, T=4, hidden=256, w=FAKE, eps=1e-6, wk=FAKE, wv=FAKE, slots=FAKE, k=FAKE, v=FAKE,
+                nb=8, hkv=2, bs=16, d=128, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return yb.lib().yoco_kv_append(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=100), yb.YOCO_ERR_UNSUPPORTED),
+    (dict(d=80), yb.YOCO_ERR_UNSUPPORTED),
+    (dict(bs=3), yb.YOCO_ERR_UNSUPPORTED),
+    (dict(eps=-1.0), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(ws_bytes=100), yb.YOCO_ERR_WORKSPACE_TOO_SMALL),
+    (dict(x=None), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(wk=FAKE + 2), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(dtype=0, hidden=32768), yb.YOCO_ERR_UNSUPPORTED),
+])
+def test_kv_append_rejects_before_launch(kw, status):
+    assert _append(**kw) == status
+
+
+def test_kv_append_no_tokens_is_a_noop():
+    assert _append(T=0) == yb.YOCO_OK
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 10, 24, FAKE, 2, FAKE, None, None), yb.YOCO_ERR_INVALID_ARGUMENT),   # row_bytes not /16
+    ((FAKE, 10, 32, None, 2, FAKE, None, None), yb.YOCO_ERR_INVALID_ARGUMENT),   # null cu_seqlens
+    ((FAKE + 8, 10, 32, FAKE, 2, FAKE, None, None), yb.YOCO_ERR_INVALID_ARGUMENT),
+    ((FAKE, -1, 32, FAKE, 2, FAKE, None, None), yb.YOCO_ERR_INVALID_ARGUMENT),
+    ((FAKE, 10, 32, FAKE, 0, FAKE, None, None), yb.YOCO_OK),                    # no requests
+])
+def test_gather_last_rejects_before_launch(args, status):
+    assert yb.lib().yoco_gather_last(*args) == status

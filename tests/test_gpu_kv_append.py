@@ -1,0 +1,94 @@
+"""yoco_kv_append on the GPU against the float64 oracle.
+
+Written slots must match the oracle's projection within the floating-point
+bound derived in tests/gpu_helpers.append_tolerance; every other byte of the
+cache must keep its bits."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_helpers import DeviceWorkload, append_tolerance, bf16_rne, host, say
+from yoco_shared_kv_gather_amd import binding as yb
+
+pytestmark = pytest.mark.gpu
+EPS = 1e-6
+
+
+def _check_rows(w, k_before, v_before, tokens, dtype):
+    """Compare the cache rows written for `tokens` and require every other
+    slot to be unchanged."""
+    meta, geom = w.meta, w.geom
+    x = host(w.x[tokens])
+    kref, vref, kb, vb = oracle.kv_project(x, host(w.w_rms), EPS, host(w.w_k), host(w.w_v),
+                                           geom.num_kv_heads, geom.head_dim)
+    slots = meta.slot_mapping[tokens]
+    bs = geom.block_size
+    worst = 0.0
+    match = []
+    for i, s in enumerate(slots):
+        if s < 0:
+            continue
+        for cache, ref, bound in ((w.k, kref[i], kb[i]), (w.v, vref[i], vb[i])):
+            got = host(cache[s // bs, :, s % bs, :]).astype(np.float64)
+            tol = append_tolerance(ref, bound, geom.hidden, dtype)
+            err = np.abs(got - ref)
+            assert (err <= tol).all(), (i, float(err.max()), float(tol[err > tol].min()))
+            worst = max(worst, float((err / tol).max()))
+            if dtype == "bf16":
+                match.append((got == bf16_rne(ref)).mean())
+    say(f"  worst error / bound {worst:.3f}" + (f", bf16-equal to RNE(ref): {np.mean(match):.4f}" if match else ""))
+    return match
+
+
+def _untouched_equal(w, k_before, v_before):
+    live = torch.zeros(w.meta.num_blocks * w.geom.block_size, dtype=torch.bool, device=w.k.device)
+    sm = w.slot_mapping[w.slot_mapping >= 0].long()
+    live[sm] = True
+    live = live.view(w.meta.num_blocks, 1, w.geom.block_size, 1).expand_as(w.k)
+    ib = torch.int16 if w.k.element_size() == 2 else torch.int32
+    for after, before in ((w.k, k_before), (w.v, v_before)):
+        assert torch.equal(after.view(ib)[~live], before.view(ib)[~live])
+
+
+@pytest.mark.parametrize("cid,size,rms", [(1, "full", "ones"), (1, "full", "random"), (2, "small", "ones"),
+                                          (3, "small", "ones"), (4, "small", "ones"), (4, "small", "random"),
+                                          (5, "small", "ones")])
+def test_append_parity(cid, size, rms):
+    say(f"kv_append parity: workload {cid} {size} rms weight {rms}")
+    w = DeviceWorkload(cid, size, layers=1, with_append=True, rms_weight=rms)
+    k0, v0 = w.k.clone(), w.v.clone()
+    yb.kv_append(w.x, w.w_rms, EPS, w.w_k, w.w_v, w.slot_mapping, w.k, w.v)
+    torch.cuda.synchronize()
+    _untouched_equal(w, k0, v0)
+    match = _check_rows(w, k0, v0, np.arange(w.meta.num_tokens), w.geom.dtype)
+    if w.geom.dtype == "bf16" and rms == "ones":
+        assert np.mean(match) > 0.99
+
+
+def test_append_full_size_mixed_step():
+    """Workload 4 at full size (about 77K rows through the MFMA GEMM): every
+    untouched byte keeps its bits; sampled rows match the oracle."""
+    say("kv_append full size: workload 4")
+    w = DeviceWorkload(4, "full", layers=1, with_append=True)
+    k0, v0 = w.k.clone(), w.v.clone()
+    yb.kv_append(w.x, w.w_rms, EPS, w.w_k, w.w_v, w.slot_mapping, w.k, w.v)
+    torch.cuda.synchronize()
+    _untouched_equal(w, k0, v0)
+    rng = np.random.default_rng(4)
+    last = w.meta.cu_seqlens[1:] - 1
+    sample = np.unique(np.concatenate([last[:8], rng.integers(0, w.meta.num_tokens, size=40),
+                                       [w.meta.num_tokens - 1]]))
+    match = _check_rows(w, k0, v0, sample, "bf16")
+    assert np.mean(match) > 0.99
+
+
+def test_append_twice_is_idempotent():
+    say("kv_append: same call twice gives the same bits")
+    w = DeviceWorkload(2, "small", layers=1, with_append=True)
+    yb.kv_append(w.x, w.w_rms, EPS, w.w_k, w.w_v, w.slot_mapping, w.k, w.v)
+    k1 = w.k.clone()
+    yb.kv_append(w.x, w.w_rms, EPS, w.w_k, w.w_v, w.slot_mapping, w.k, w.v)
+    torch.cuda.synchronize()
+    assert torch.equal(k1.view(torch.int16), w.k.view(torch.int16))

@@ -1,0 +1,226 @@
+"""ctypes binding of libyoco.so (the C ABI in include/yoco.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  Torch tensors supply device memory and the current
+HIP stream.  If the library is missing or cannot load, every call raises; there
+is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional, Tuple
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libyoco.so")
+
+ABI_VERSION = 1
+YOCO_OK = 0
+YOCO_ERR_INVALID_ARGUMENT = 1
+YOCO_ERR_UNSUPPORTED = 2
+YOCO_ERR_WORKSPACE_TOO_SMALL = 3
+YOCO_ERR_HIP = 4
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+FLAG_REVERSE_ORDER = 1
+
+_c = ctypes
+_vp = _c.c_void_p
+_i32 = _c.c_int32
+_i64 = _c.c_int64
+_u32 = _c.c_uint32
+_f32 = _c.c_float
+
+# name -> (restype, argtypes); mirrors include/yoco.h
+SIGNATURES = {
+    "yoco_abi_version": (_i32, []),
+    "yoco_status_string": (_c.c_char_p, [_i32]),
+    "yoco_last_error_message": (_c.c_char_p, []),
+    "yoco_gather_last": (_i32, [_vp, _i64, _i64, _vp, _i32, _vp, _vp, _vp]),
+    "yoco_kv_append_workspace_size": (_i64, [_i32, _i32, _i32, _i32]),
+    "yoco_kv_append": (_i32, [_i32, _vp, _i32, _i32, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                              _vp, _i64, _vp]),
+    "yoco_cross_attn_partition_tokens": (_i32, [_i32, _i32, _i32, _i32, _i32]),
+    "yoco_cross_attn_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "yoco_cross_attn": (_i32, [_i32, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _f32,
+                               _i32, _u32, _vp, _vp, _i64, _vp]),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class YocoError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libyoco.so once and declare its signatures; raises if it cannot."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise ImportError(f"{LIB_PATH} is missing: build it with python -m yoco_shared_kv_gather_amd.build")
+            handle = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(handle, name)
+                fn.restype = res
+                fn.argtypes = args
+            version = handle.yoco_abi_version()
+            if version != ABI_VERSION:
+                raise ImportError(f"libyoco ABI version {version}, binding expects {ABI_VERSION}")
+            _lib = handle
+    return _lib
+
+
+def _check(status: int):
+    if status != YOCO_OK:
+        msg = lib().yoco_last_error_message().decode()
+        raise YocoError(status, msg or lib().yoco_status_string(status).decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def _dev(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _i32_dev(t, name):
+    torch = _torch()
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32")
+    return _dev(t, name)
+
+
+# ---- yoco_gather_last -----------------------------------------------------------
+
+def gather_last(hidden, cu_seqlens, out=None, out_index=None, stream=None):
+    """out[r] = hidden[cu_seqlens[r+1]-1] (bitwise); returns (out, out_index)."""
+    torch = _torch()
+    num_reqs = cu_seqlens.numel() - 1
+    row_shape = tuple(hidden.shape[1:])
+    row_bytes = hidden[0].numel() * hidden.element_size() if hidden.shape[0] > 0 else \
+        math.prod(row_shape) * hidden.element_size()
+    if out is None:
+        out = torch.empty((num_reqs,) + row_shape, dtype=hidden.dtype, device=hidden.device)
+    if out_index is None:
+        out_index = torch.empty(num_reqs, dtype=torch.int32, device=hidden.device)
+    _check(lib().yoco_gather_last(_dev(hidden, "hidden"), hidden.shape[0], row_bytes,
+                                  _i32_dev(cu_seqlens, "cu_seqlens"), num_reqs, _dev(out, "out"),
+                                  _i32_dev(out_index, "out_index"), _stream_handle(stream)))
+    return out, out_index
+
+
+# ---- yoco_kv_append ---------------------------------------------------------------
+
+def kv_append_workspace_size(dtype_code: int, hidden: int, num_kv_heads: int, head_dim: int) -> int:
+    return int(lib().yoco_kv_append_workspace_size(dtype_code, hidden, num_kv_heads, head_dim))
+
+
+def kv_append(x, rms_weight, eps, w_k, w_v, slot_mapping, k_cache, v_cache, workspace=None, stream=None):
+    """RMSNorm + shared K/V projection of every row of x into its cache slot."""
+    torch = _torch()
+    code = _dtype_code(x)
+    num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
+    hidden = x.shape[1]
+    need = kv_append_workspace_size(code, hidden, num_kv_heads, head_dim)
+    if need < 0:
+        raise YocoError(YOCO_ERR_INVALID_ARGUMENT, "bad kv_append shape")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().yoco_kv_append(code, _dev(x, "x"), x.shape[0], hidden, _dev(rms_weight, "rms_weight"), float(eps),
+                                _dev(w_k, "w_k"), _dev(w_v, "w_v"), _i32_dev(slot_mapping, "slot_mapping"),
+                                _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), num_blocks, num_kv_heads,
+                                block_size, head_dim, ws_ptr, ws_bytes, _stream_handle(stream)))
+
+
+# ---- yoco_cross_attn -----------------------------------------------------------------
+
+def cross_attn_partition_tokens(num_seqs, num_kv_heads, head_dim, max_seq_len, partition_tokens=0) -> int:
+    return int(lib().yoco_cross_attn_partition_tokens(num_seqs, num_kv_heads, head_dim, max_seq_len,
+                                                       partition_tokens))
+
+
+def cross_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens=0) -> int:
+    return int(lib().yoco_cross_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                                     partition_tokens))
+
+
+def cross_attn(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale=None, partition_tokens=0, flags=0,
+               out=None, workspace=None, stream=None):
+    """One cross layer: out[r][h] = softmax(scale q.K^T) V over request r's context.
+
+    A caller-supplied ``workspace`` must start zeroed (torch.zeros) before its
+    first use; every call leaves its counters zero again.  Calls that may run
+    concurrently need separate workspaces."""
+    torch = _torch()
+    code = _dtype_code(q)
+    num_seqs, num_q_heads, head_dim = q.shape
+    num_blocks, num_kv_heads, block_size, _ = k_cache.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    if out is None:
+        out = torch.empty((num_seqs, num_q_heads, head_dim), dtype=torch.float32, device=q.device)
+    need = cross_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens)
+    if need < 0:
+        raise YocoError(YOCO_ERR_INVALID_ARGUMENT, "bad cross_attn shape")
+    if workspace is None and need > 0:
+        # the counters at the start of the workspace must be zero before first use
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().yoco_cross_attn(code, _dev(q, "q"), num_seqs, num_q_heads, _dev(k_cache, "k_cache"),
+                                 _dev(v_cache, "v_cache"), num_blocks, num_kv_heads, block_size, head_dim,
+                                 _i32_dev(block_table, "block_table"), block_table.shape[1],
+                                 _i32_dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale),
+                                 int(partition_tokens), int(flags), _dev(out, "out"), ws_ptr, ws_bytes,
+                                 _stream_handle(stream)))
+    return out
+
+
+def status_string(status: int) -> str:
+    return lib().yoco_status_string(status).decode()
+
+
+def last_error_message() -> str:
+    return lib().yoco_last_error_message().decode()
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def describe_launch(num_seqs, num_kv_heads, head_dim, max_seq_len, partition_tokens=0) -> Tuple[int, int]:
+    """(partition_tokens, partitions per request) that yoco_cross_attn will use."""
+    p = cross_attn_partition_tokens(num_seqs, num_kv_heads, head_dim, max_seq_len, partition_tokens)
+    return p, max(1, -(-max(max_seq_len, 1) // p))

@@ -1,0 +1,551 @@
+// yoco_cross_attn: one YOCO cross layer's attention over the shared paged cache.
+//
+// What is computed ("KV cache memory systems", section "Cache contents";
+// "YOCO_论文与推理数据流详解" §10.4 and §13.2): every request has one query per
+// query head, and it attends to the request's whole context of K^/V^ rows in
+// the one cache that all cross layers share; each logical block of the
+// context is found through the block table ("KV cache memory systems",
+// section "Contiguous allocation wastes capacity").
+//
+// How (gfx950):
+//   * Split-KV.  Work item = (request, KV head, partition of
+//     `partition_tokens` context tokens); one wavefront per work item, so a
+//     long context still spreads over every compute unit.  When a request has
+//     more than one partition, each writes an unnormalised partial
+//     (acc, running max m, running sum l) to the workspace and bumps a
+//     per-(request, KV head) counter with agent-scope acquire/release
+//     ordering; the wavefront that brings the counter to the partition count
+//     merges all partials with log-sum-exp weights in partition order (so the
+//     bits do not depend on which wavefront finishes last) and resets the
+//     counter to zero.  One launch per layer, no separate merge kernel.
+//   * One wavefront reads each K^/V^ row exactly once and uses it for all G
+//     query heads of its KV group (GQA); the G queries stay in registers.
+//   * A K^ or V^ row of head_dim elements is split into 16-byte chunks;
+//     LPR lanes cover one row with CPL chunks each, so a wavefront instruction
+//     loads 64/LPR whole rows, fully coalesced within each cache block.
+//   * q.k uses v_dot2_f32_bf16 (two bf16 products per instruction, fp32
+//     accumulation), then a butterfly over the LPR lanes of a row.
+//   * Online softmax in base 2 with a lazy maximum: the running max of a
+//     row group is raised only when a score exceeds it by more than 2^8, so
+//     the rescale of the accumulators is rare; the partial sums stay bounded
+//     by 256 times the true terms, far from fp32 overflow.
+//   * p.v in fp32 FMA; bf16 values widen with one shift or mask.
+
+#include <cmath>
+
+#include "yoco_internal.h"
+
+namespace {
+
+using yoco::bf16_hi;
+using yoco::bf16_lo;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyMaxSlack = 8.0f;      // log2 of the largest un-rescaled term
+constexpr float kInitMax = -1.0e30f;       // finite "minus infinity" for running maxima
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  float* out;
+  uint32_t* counters;   // [num_seqs][Hkv], zero between calls
+  float* ws_acc;        // [num_seqs][Hq][num_parts][D]
+  float* ws_ml;         // [num_seqs][Hq][num_parts][2]  (max, sum), base-2 units
+  int64_t block_stride; // elements per physical block (Hkv * bs * D)
+  int32_t head_stride;  // elements per KV head inside a block (bs * D)
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t bs_shift;
+  int32_t max_blocks;
+  int32_t len_cap;      // seq_lens are clamped to [0, len_cap]
+  int32_t part_tokens;
+  int32_t num_parts;
+  float scale_log2;     // scale * log2(e)
+  uint32_t flags;
+};
+
+template <bool kBf16, int D>
+struct Layout {
+  static constexpr int kEpc = kBf16 ? 8 : 4;              // elements per 16-byte chunk
+  static constexpr int kChunks = D / kEpc;                // chunks per row
+  static constexpr int kLpr = kChunks / 2 < 16 ? kChunks / 2 : 16;   // lanes per row
+  static constexpr int kCpl = kChunks / kLpr;             // chunks per lane
+  static constexpr int kRpw = 64 / kLpr;                  // rows per wave instruction
+};
+
+// Dot product of one 16-byte chunk of q with one of k, accumulated into acc.
+template <bool kBf16>
+__device__ __forceinline__ float chunk_dot(const uint4& q, const uint4& k, float acc);
+
+template <>
+__device__ __forceinline__ float chunk_dot<true>(const uint4& q, const uint4& k, float acc) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, k.x), __builtin_bit_cast(bf2, q.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, k.y), __builtin_bit_cast(bf2, q.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, k.z), __builtin_bit_cast(bf2, q.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf2, k.w), __builtin_bit_cast(bf2, q.w), acc, false);
+  return acc;
+}
+
+template <>
+__device__ __forceinline__ float chunk_dot<false>(const uint4& q, const uint4& k, float acc) {
+  acc = fmaf(__uint_as_float(k.x), __uint_as_float(q.x), acc);
+  acc = fmaf(__uint_as_float(k.y), __uint_as_float(q.y), acc);
+  acc = fmaf(__uint_as_float(k.z), __uint_as_float(q.z), acc);
+  acc = fmaf(__uint_as_float(k.w), __uint_as_float(q.w), acc);
+  return acc;
+}
+
+// Element e of a 16-byte chunk as fp32.
+template <bool kBf16>
+__device__ __forceinline__ float chunk_elem(const uint4& c, int e) {
+  const uint32_t w = e < (kBf16 ? 2 : 1) ? c.x : e < (kBf16 ? 4 : 2) ? c.y : e < (kBf16 ? 6 : 3) ? c.z : c.w;
+  if constexpr (kBf16) {
+    return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+  } else {
+    return __uint_as_float(w);
+  }
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// Wavefront reductions with a fixed butterfly order (deterministic).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int mask = 32; mask > 0; mask >>= 1) v = fmaxf(v, __shfl_xor(v, mask, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int mask = 32; mask > 0; mask >>= 1) v += __shfl_xor(v, mask, 64);
+  return v;
+}
+
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge the np partials of the G query heads hq0.. of request r:
+//   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p,
+// summing partitions in order 0..np-1.  Lanes own head_dim/64 dimensions.
+template <int D, int G>
+__device__ __forceinline__ void merge_partials(const AttnArgs& a, int r, int hq0, int np, int lane) {
+  constexpr int kDpl = D / 64;
+  for (int h = 0; h < G; ++h) {
+    const int64_t rh = static_cast<int64_t>(r) * a.num_q_heads + hq0 + h;
+    const float* ml = a.ws_ml + rh * a.num_parts * 2;
+    const float* acc = a.ws_acc + rh * a.num_parts * D;
+    float mx = kInitMax;
+    for (int p = lane; p < np; p += 64) mx = fmaxf(mx, load_agent(ml + 2 * p));
+    mx = wave_max(mx);
+    float den = 0.0f;
+    for (int p = lane; p < np; p += 64) den += exp2f(load_agent(ml + 2 * p) - mx) * load_agent(ml + 2 * p + 1);
+    den = wave_sum(den);
+    float num[kDpl];
+#pragma unroll
+    for (int i = 0; i < kDpl; ++i) num[i] = 0.0f;
+    for (int p = 0; p < np; ++p) {
+      const float w = exp2f(load_agent(ml + 2 * p) - mx);
+#pragma unroll
+      for (int i = 0; i < kDpl; ++i) num[i] = fmaf(w, load_agent(acc + static_cast<int64_t>(p) * D + lane + 64 * i), num[i]);
+    }
+    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+    for (int i = 0; i < kDpl; ++i) a.out[rh * D + lane + 64 * i] = num[i] * inv;
+  }
+}
+
+template <bool kBf16, int D, int G>
+__global__ __launch_bounds__(64) void cross_attn_partial_kernel(AttnArgs a) {
+  using L = Layout<kBf16, D>;
+  constexpr int kEpc = L::kEpc, kLpr = L::kLpr, kCpl = L::kCpl, kRpw = L::kRpw;
+  constexpr int kU = 2;                       // row sets in flight per iteration
+  constexpr int kElemBytes = kBf16 ? 2 : 4;
+
+  const int lane = threadIdx.x;
+  const int row = lane / kLpr;
+  const int cl = lane % kLpr;
+
+  const uint32_t total = static_cast<uint32_t>(a.num_seqs) * a.num_kv_heads * a.num_parts;
+  uint32_t item = blockIdx.x;
+  if (a.flags & YOCO_FLAG_REVERSE_ORDER) item = total - 1u - item;
+  const int part = static_cast<int>(item % a.num_parts);
+  const uint32_t rg = item / a.num_parts;
+  const int g = static_cast<int>(rg % a.num_kv_heads);
+  const int r = static_cast<int>(rg / a.num_kv_heads);
+
+  int n = a.seq_lens[r];
+  n = n < 0 ? 0 : (n > a.len_cap ? a.len_cap : n);
+  const int start = part * a.part_tokens;
+  const int hq0 = g * G;
+
+  if (start >= n) {
+    // Partitions past the end do nothing; the first one answers an empty
+    // context with zeros.
+    if (n == 0 && part == 0) {
+      for (int i = lane; i < G * D; i += 64) a.out[(static_cast<int64_t>(r) * a.num_q_heads + hq0) * D + i] = 0.0f;
+    }
+    return;
+  }
+  const int end = min(start + a.part_tokens, n);
+
+  // Queries of the G heads of this group, the chunks this lane owns.
+  uint4 qr[G][kCpl];
+  {
+    const char* qb = static_cast<const char*>(a.q) + (static_cast<int64_t>(r) * a.num_q_heads + hq0) * D * kElemBytes;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < kCpl; ++i)
+        qr[h][i] = *reinterpret_cast<const uint4*>(qb + (h * D + (cl + kLpr * i) * kEpc) * kElemBytes);
+  }
+
+  float acc[G][kCpl][kEpc];
+  float m[G], lsum[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = kInitMax;
+    lsum[h] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < kCpl; ++i)
+#pragma unroll
+      for (int e = 0; e < kEpc; ++e) acc[h][i][e] = 0.0f;
+  }
+
+  const int32_t* table = a.block_table + static_cast<int64_t>(r) * a.max_blocks;
+  const char* kb = static_cast<const char*>(a.k) + static_cast<int64_t>(g) * a.head_stride * kElemBytes;
+  const char* vb = static_cast<const char*>(a.v) + static_cast<int64_t>(g) * a.head_stride * kElemBytes;
+  const int off_mask = a.block_size - 1;
+
+  for (int base = start; base < end; base += kRpw * kU) {
+    uint4 kr[kU][kCpl], vr[kU][kCpl];
+    bool valid[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = base + u * kRpw + row;
+      bool ok = j < end;
+      int64_t off = 0;
+      if (ok) {
+        const int blk = table[j >> a.bs_shift];
+        ok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
+        off = (static_cast<int64_t>(blk) * a.block_stride + static_cast<int64_t>(j & off_mask) * D) * kElemBytes;
+      }
+      valid[u] = ok;
+#pragma unroll
+      for (int i = 0; i < kCpl; ++i) {
+        const int64_t c = off + static_cast<int64_t>((cl + kLpr * i) * kEpc) * kElemBytes;
+        if (ok) {
+          kr[u][i] = *reinterpret_cast<const uint4*>(kb + c);
+          vr[u][i] = *reinterpret_cast<const uint4*>(vb + c);
+        } else {
+          kr[u][i] = make_uint4(0u, 0u, 0u, 0u);
+          vr[u][i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+      }
+    }
+
+    // Scores: partial dots over this lane's chunks, then a butterfly over the
+    // kLpr lanes of the row (all of them end with the full sum).
+    float s[kU][G];
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float t = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kCpl; ++i) t = chunk_dot<kBf16>(qr[h][i], kr[u][i], t);
+        s[u][h] = t;
+      }
+#pragma unroll
+    for (int mask = 1; mask < kLpr; mask <<= 1)
+#pragma unroll
+      for (int u = 0; u < kU; ++u)
+#pragma unroll
+        for (int h = 0; h < G; ++h) s[u][h] += shfl_xor_f(s[u][h], mask);
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+#pragma unroll
+      for (int h = 0; h < G; ++h) s[u][h] = valid[u] ? s[u][h] * a.scale_log2 : -INFINITY;
+
+    // Lazy running maximum per row group and head.
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float cand = s[0][h];
+#pragma unroll
+      for (int u = 1; u < kU; ++u) cand = fmaxf(cand, s[u][h]);
+      if (cand > m[h] + kLazyMaxSlack) {
+        const float corr = exp2f(m[h] - cand);
+        lsum[h] *= corr;
+#pragma unroll
+        for (int i = 0; i < kCpl; ++i)
+#pragma unroll
+          for (int e = 0; e < kEpc; ++e) acc[h][i][e] *= corr;
+        m[h] = cand;
+      }
+    }
+
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      float p[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        p[h] = exp2f(s[u][h] - m[h]);
+        lsum[h] += p[h];
+      }
+#pragma unroll
+      for (int i = 0; i < kCpl; ++i)
+#pragma unroll
+        for (int e = 0; e < kEpc; ++e) {
+          const float x = chunk_elem<kBf16>(vr[u][i], e);
+#pragma unroll
+          for (int h = 0; h < G; ++h) acc[h][i][e] = fmaf(p[h], x, acc[h][i][e]);
+        }
+    }
+  }
+
+  // Combine the row groups of the wavefront (lanes with the same cl).
+#pragma unroll
+  for (int mask = kLpr; mask < 64; mask <<= 1) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float mo = shfl_xor_f(m[h], mask);
+      const float lo = shfl_xor_f(lsum[h], mask);
+      const float mx = fmaxf(m[h], mo);
+      const float fa = exp2f(m[h] - mx);
+      const float fb = exp2f(mo - mx);
+      lsum[h] = lsum[h] * fa + lo * fb;
+#pragma unroll
+      for (int i = 0; i < kCpl; ++i)
+#pragma unroll
+        for (int e = 0; e < kEpc; ++e) {
+          const float other = shfl_xor_f(acc[h][i][e], mask);
+          acc[h][i][e] = acc[h][i][e] * fa + other * fb;
+        }
+      m[h] = mx;
+    }
+  }
+
+  const int np_r = (n + a.part_tokens - 1) / a.part_tokens;      // partitions holding tokens
+  if (np_r == 1) {
+    if (row == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const int64_t rh = static_cast<int64_t>(r) * a.num_q_heads + hq0 + h;
+        const float inv = lsum[h] > 0.0f ? 1.0f / lsum[h] : 0.0f;
+        float* o = a.out + rh * D;
+#pragma unroll
+        for (int i = 0; i < kCpl; ++i) {
+          float4* dst = reinterpret_cast<float4*>(o + (cl + kLpr * i) * kEpc);
+#pragma unroll
+          for (int e4 = 0; e4 < kEpc / 4; ++e4)
+            dst[e4] = make_float4(acc[h][i][4 * e4] * inv, acc[h][i][4 * e4 + 1] * inv,
+                                  acc[h][i][4 * e4 + 2] * inv, acc[h][i][4 * e4 + 3] * inv);
+        }
+      }
+    }
+    return;
+  }
+
+  // Several partitions: publish this one's partial.
+  if (row == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const int64_t slot = (static_cast<int64_t>(r) * a.num_q_heads + hq0 + h) * a.num_parts + part;
+      float* o = a.ws_acc + slot * D;
+#pragma unroll
+      for (int i = 0; i < kCpl; ++i) {
+        float4* dst = reinterpret_cast<float4*>(o + (cl + kLpr * i) * kEpc);
+#pragma unroll
+        for (int e4 = 0; e4 < kEpc / 4; ++e4)
+          dst[e4] = make_float4(acc[h][i][4 * e4], acc[h][i][4 * e4 + 1], acc[h][i][4 * e4 + 2],
+                                acc[h][i][4 * e4 + 3]);
+      }
+      if (cl == 0) {
+        a.ws_ml[slot * 2] = m[h];
+        a.ws_ml[slot * 2 + 1] = lsum[h];
+      }
+    }
+  }
+  __threadfence();
+  uint32_t* counter = a.counters + static_cast<int64_t>(r) * a.num_kv_heads + g;
+  uint32_t arrived = 0;
+  if (lane == 0) arrived = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  arrived = __shfl(arrived, 0, 64);
+  if (arrived != static_cast<uint32_t>(np_r - 1)) return;
+  __threadfence();
+  merge_partials<D, G>(a, r, hq0, np_r, lane);
+  if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---- host side ---------------------------------------------------------------
+
+constexpr int kMaxParts = 65535;
+
+int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t requested) {
+  if (requested > 0) return requested;
+  // Aim for about 2048 work items (eight wavefronts per compute unit) with
+  // partitions of 64..16384 tokens.
+  const int64_t items = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
+  const int64_t parts = yoco::ceil_div(2048, items);
+  int64_t p = yoco::round_up(yoco::ceil_div(max_seq_len > 0 ? max_seq_len : 1, parts), 64);
+  if (p < 64) p = 64;
+  if (p > 16384) p = 16384;
+  while (yoco::ceil_div(max_seq_len, p) > kMaxParts) p *= 2;
+  return static_cast<int32_t>(p);
+}
+
+int32_t num_partitions(int32_t max_seq_len, int32_t part_tokens) {
+  const int64_t np = yoco::ceil_div(max_seq_len > 0 ? max_seq_len : 1, part_tokens);
+  return static_cast<int32_t>(np);
+}
+
+// Workspace: [counters uint32 num_seqs*Hkv | pad to 256][acc fp32 | pad][ml fp32].
+// The counters must be zero before the first call; every call leaves them zero.
+struct WorkspaceLayout {
+  int64_t acc_offset = 0;
+  int64_t ml_offset = 0;
+  int64_t total = 0;
+};
+
+WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t num_parts) {
+  WorkspaceLayout w;
+  if (num_parts <= 1) return w;
+  const int64_t slots = static_cast<int64_t>(num_seqs) * num_q_heads * num_parts;
+  w.acc_offset = yoco::round_up(static_cast<int64_t>(num_seqs) * num_kv_heads * 4, 256);
+  w.ml_offset = w.acc_offset + yoco::round_up(slots * head_dim * 4, 256);
+  w.total = w.ml_offset + slots * 2 * 4;
+  return w;
+}
+
+template <bool kBf16, int D, int G>
+void launch_partial(const AttnArgs& a, uint32_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((cross_attn_partial_kernel<kBf16, D, G>), dim3(grid), dim3(64), 0, stream, a);
+}
+
+template <bool kBf16, int D>
+bool dispatch_group(int group, const AttnArgs& a, uint32_t grid, hipStream_t stream) {
+  switch (group) {
+    case 1: launch_partial<kBf16, D, 1>(a, grid, stream); return true;
+    case 2: launch_partial<kBf16, D, 2>(a, grid, stream); return true;
+    case 4: launch_partial<kBf16, D, 4>(a, grid, stream); return true;
+    case 8: launch_partial<kBf16, D, 8>(a, grid, stream); return true;
+    default: return false;
+  }
+}
+
+template <bool kBf16>
+bool dispatch_dim(int head_dim, int group, const AttnArgs& a, uint32_t grid, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return dispatch_group<kBf16, 64>(group, a, grid, stream);
+    case 128: return dispatch_group<kBf16, 128>(group, a, grid, stream);
+    case 256: return dispatch_group<kBf16, 256>(group, a, grid, stream);
+    default: return false;
+  }
+}
+
+bool supported_dim(int d) { return d == 64 || d == 128 || d == 256; }
+
+}  // namespace
+
+extern "C" int32_t yoco_cross_attn_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
+                                                    int32_t max_seq_len, int32_t partition_tokens) {
+  (void)head_dim;
+  if (partition_tokens < 0 || max_seq_len < 0) return -1;
+  return resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
+}
+
+extern "C" int64_t yoco_cross_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                                  int32_t head_dim, int32_t max_seq_len,
+                                                  int32_t partition_tokens) {
+  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || partition_tokens < 0) return -1;
+  const int32_t p = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
+  return workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, num_partitions(max_seq_len, p)).total;
+}
+
+extern "C" int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                   const void* k_cache, const void* v_cache, int32_t num_blocks,
+                                   int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                                   const int32_t* block_table, int32_t max_blocks_per_seq,
+                                   const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                                   int32_t partition_tokens, uint32_t flags, float* out, void* workspace,
+                                   int64_t workspace_bytes, void* stream) {
+  using namespace yoco;
+  if (dtype != YOCO_DTYPE_F32 && dtype != YOCO_DTYPE_BF16)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: unknown dtype %d", dtype);
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+      max_seq_len < 0 || partition_tokens < 0 || workspace_bytes < 0)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: negative or zero size argument");
+  if (num_q_heads % num_kv_heads != 0)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: num_q_heads %d is not a multiple of num_kv_heads %d",
+                num_q_heads, num_kv_heads);
+  if ((flags & ~YOCO_FLAG_REVERSE_ORDER) != 0) return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: unknown flags");
+  if (!std::isfinite(scale)) return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: scale is not finite");
+  if (partition_tokens % 64 != 0)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: partition_tokens %d is not a multiple of 64", partition_tokens);
+  const int group = num_q_heads / num_kv_heads;
+  if (!supported_dim(head_dim)) return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: head_dim %d not in {64,128,256}", head_dim);
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: %d query heads per KV head not in {1,2,4,8}", group);
+  if (!is_pow2(block_size) || block_size > 256)
+    return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: block_size %d is not a power of two <= 256", block_size);
+  if (num_seqs == 0) return YOCO_OK;
+  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr || seq_lens == nullptr ||
+      out == nullptr)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: null pointer");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: q, caches and out must be 16-byte aligned");
+
+  const int32_t part = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
+  const int32_t nparts = num_partitions(max_seq_len, part);
+  if (nparts > kMaxParts)
+    return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: %d partitions per request exceed %d", nparts, kMaxParts);
+  const int64_t grid = static_cast<int64_t>(num_seqs) * num_kv_heads * nparts;
+  if (grid > 0x7fffffffLL) return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: %lld work items is too many", (long long)grid);
+  const WorkspaceLayout ws = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, nparts);
+  if (workspace_bytes < ws.total)
+    return fail(YOCO_ERR_WORKSPACE_TOO_SMALL, "cross_attn: workspace %lld bytes, need %lld",
+                (long long)workspace_bytes, (long long)ws.total);
+  if (ws.total > 0 && (workspace == nullptr || !aligned16(workspace)))
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: workspace must be a 16-byte aligned pointer");
+
+  AttnArgs a;
+  a.q = q;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.block_table = block_table;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  char* wsb = static_cast<char*>(workspace);
+  a.counters = ws.total > 0 ? reinterpret_cast<uint32_t*>(wsb) : nullptr;
+  a.ws_acc = ws.total > 0 ? reinterpret_cast<float*>(wsb + ws.acc_offset) : nullptr;
+  a.ws_ml = ws.total > 0 ? reinterpret_cast<float*>(wsb + ws.ml_offset) : nullptr;
+  a.head_stride = block_size * head_dim;
+  a.block_stride = static_cast<int64_t>(num_kv_heads) * block_size * head_dim;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.num_blocks = num_blocks;
+  a.block_size = block_size;
+  a.bs_shift = ilog2(block_size);
+  a.max_blocks = max_blocks_per_seq;
+  const int64_t cap = static_cast<int64_t>(max_blocks_per_seq) * block_size;
+  a.len_cap = static_cast<int32_t>(cap < max_seq_len ? cap : max_seq_len);
+  a.part_tokens = part;
+  a.num_parts = nparts;
+  a.scale_log2 = scale * kLog2e;
+  a.flags = flags;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  clear_launch_error();
+  const bool ok = dtype == YOCO_DTYPE_BF16 ? dispatch_dim<true>(head_dim, group, a, static_cast<uint32_t>(grid), s)
+                                           : dispatch_dim<false>(head_dim, group, a, static_cast<uint32_t>(grid), s);
+  if (!ok) return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: no kernel for this shape");
+  return launch_result("cross_attn");
+}

@@ -1,0 +1,339 @@
+// yoco_kv_append: RMSNorm + the shared K/V projection, written once per token
+// into the paged cache.
+//
+// "YOCO_论文与推理数据流详解" §3 (architecture flowchart) and §10.3: from the
+// self-decoder output M the model computes K^ = LN(M) W_K and V^ = LN(M) W_V
+// once per token and appends that pair to the single global cache; no cross
+// layer appends anything.  LN is taken as RMSNorm,
+//     xhat = x * rsqrt(mean(x^2) + eps) * w_rms,
+// and the row scale rsqrt(...) commutes with the projection:
+//     K^_t = rsqrt(mean(x_t^2) + eps) * (W_K diag(w_rms)) x_t.
+//
+// bf16 path (matrix cores):
+//   1. fold: W' = bf16(W diag(w_rms)) for [W_K; W_V] (one pass over the
+//      weights into the workspace);
+//   2. one MFMA GEMM  C[T][2*Hkv*D] = x[T][H] W'^T  with
+//      v_mfma_f32_16x16x32_bf16 (fp32 accumulation); the same pass sums x^2
+//      per row from the staged A tiles, and the epilogue multiplies by the
+//      row's rsqrt, rounds to bf16 (nearest even) and scatters each
+//      [Hkv][D] row to its slot.
+// fp32 path: one workgroup per token, fp32 throughout.
+
+#include <cmath>
+
+#include "yoco_internal.h"
+
+namespace {
+
+using yoco::bf16_hi;
+using yoco::bf16_lo;
+using yoco::f32_to_bf16_rne;
+
+// ---- fold W' = W diag(w_rms) -------------------------------------------------
+
+__global__ __launch_bounds__(256) void fold_rms_weight_kernel(const uint4* __restrict__ w_k,
+                                                              const uint4* __restrict__ w_v,
+                                                              const uint4* __restrict__ w_rms,
+                                                              uint4* __restrict__ w_out, int64_t half_chunks,
+                                                              int hidden_chunks) {
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (c >= 2 * half_chunks) return;
+  const uint4 src = c < half_chunks ? w_k[c] : w_v[c - half_chunks];
+  const uint4 sc = w_rms[c % hidden_chunks];
+  const uint32_t* s = reinterpret_cast<const uint32_t*>(&src);
+  const uint32_t* m = reinterpret_cast<const uint32_t*>(&sc);
+  uint4 res;
+  uint32_t* o = reinterpret_cast<uint32_t*>(&res);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = f32_to_bf16_rne(bf16_lo(s[i]) * bf16_lo(m[i]));
+    const uint32_t hi = f32_to_bf16_rne(bf16_hi(s[i]) * bf16_hi(m[i]));
+    o[i] = lo | (hi << 16);
+  }
+  w_out[c] = res;
+}
+
+// ---- bf16 MFMA GEMM with RMS row scale and slot scatter ------------------------
+
+constexpr int kBM = 128;
+constexpr int kBN = 128;
+constexpr int kBK = 64;
+constexpr int kLdsStride = kBK + 8;          // bf16 elements per staged row (16-byte pad)
+constexpr int kGemmThreads = 256;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct AppendArgs {
+  const uint16_t* x;          // [T][H]
+  const uint16_t* w;          // folded [2*Hkv*D][H]
+  const int32_t* slots;       // [T]
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int32_t num_tokens;
+  int32_t hidden;
+  int32_t out_half;           // Hkv * D
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t bs_shift;
+  int32_t num_kv_heads;
+  int64_t num_slots;          // num_blocks * block_size
+  float inv_hidden;
+  float eps;
+};
+
+__global__ __launch_bounds__(kGemmThreads) void kv_append_mfma_kernel(AppendArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t as[2][kBM * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t bs[2][kBN * kLdsStride];
+  __shared__ float row_scale[kBM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;            // wave row (0..1): 64 rows each
+  const int wn = wave & 1;             // wave column (0..1): 64 columns each
+  const int n0 = blockIdx.x * kBN;
+  const int m0 = blockIdx.y * kBM;
+
+  // Staging map: thread loads chunk kc (8 bf16) of rows rbase + 32 i.
+  const int kc = tid & 7;
+  const int rbase = tid >> 3;
+  uint4 ra[4], rb[4];
+  float sumsq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int rowm = m0 + rbase + 32 * i;
+      if (rowm < a.num_tokens) {
+        ra[i] = *reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(rowm) * a.hidden + k0 + kc * 8);
+      } else {
+        ra[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+      rb[i] = *reinterpret_cast<const uint4*>(a.w + static_cast<int64_t>(n0 + rbase + 32 * i) * a.hidden + k0 + kc * 8);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = rbase + 32 * i;
+      *reinterpret_cast<uint4*>(&as[buf][r * kLdsStride + kc * 8]) = ra[i];
+      *reinterpret_cast<uint4*>(&bs[buf][r * kLdsStride + kc * 8]) = rb[i];
+      const uint32_t* u = reinterpret_cast<const uint32_t*>(&ra[i]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_lo(u[e]);
+        const float hi = bf16_hi(u[e]);
+        sumsq[i] = fmaf(lo, lo, sumsq[i]);
+        sumsq[i] = fmaf(hi, hi, sumsq[i]);
+      }
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const int ktiles = a.hidden / kBK;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  const int frag_row = lane & 15;
+  const int frag_k = (lane >> 4) * 8;
+  for (int kt = 0; kt < ktiles; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < ktiles) load_tile((kt + 1) * kBK);
+#pragma unroll
+    for (int ks = 0; ks < kBK; ks += 32) {
+      bf16x8 af[4], bf[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        af[t] = *reinterpret_cast<const bf16x8*>(&as[cur][(wm * 64 + t * 16 + frag_row) * kLdsStride + ks + frag_k]);
+        bf[t] = *reinterpret_cast<const bf16x8*>(&bs[cur][(wn * 64 + t * 16 + frag_row) * kLdsStride + ks + frag_k]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < ktiles) store_tile(cur ^ 1);
+    __syncthreads();
+  }
+
+  // Row scale rsqrt(mean(x^2) + eps): add the eight partial sums of each row.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v = sumsq[i];
+    v += __shfl_xor(v, 1, 64);
+    v += __shfl_xor(v, 2, 64);
+    v += __shfl_xor(v, 4, 64);
+    if (kc == 0) row_scale[rbase + 32 * i] = 1.0f / sqrtf(v * a.inv_hidden + a.eps);
+  }
+  __syncthreads();
+
+  // Epilogue: scale, round, scatter.  Lane holds rows 4*(lane/16)+0..3 of
+  // column lane%16 of each 16x16 tile.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int lrow = wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+      const int t = m0 + lrow;
+      if (t >= a.num_tokens) continue;
+      const int64_t slot = a.slots[t];
+      if (slot < 0 || slot >= a.num_slots) continue;
+      const float sc = row_scale[lrow];
+      const int64_t blk = slot >> a.bs_shift;
+      const int64_t off = slot & (a.block_size - 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int col = n0 + wn * 64 + j * 16 + (lane & 15);
+        const bool is_v = col >= a.out_half;
+        const int hd = is_v ? col - a.out_half : col;
+        const int h = hd / a.head_dim;
+        const int d = hd - h * a.head_dim;
+        uint16_t* cache = is_v ? a.v_cache : a.k_cache;
+        cache[((blk * a.num_kv_heads + h) * a.block_size + off) * a.head_dim + d] = f32_to_bf16_rne(acc[i][j][e] * sc);
+      }
+    }
+  }
+}
+
+// ---- fp32 path -----------------------------------------------------------------
+
+constexpr int kF32Threads = 256;
+
+__global__ __launch_bounds__(kF32Threads) void kv_append_f32_kernel(
+    const float* __restrict__ x, int hidden, const float* __restrict__ w_rms, float eps,
+    const float* __restrict__ w_k, const float* __restrict__ w_v, const int32_t* __restrict__ slots,
+    int64_t num_slots, float* __restrict__ k_cache, float* __restrict__ v_cache, int num_kv_heads,
+    int block_size, int bs_shift, int head_dim) {
+  extern __shared__ float xs[];
+  __shared__ float partial[kF32Threads / 64];
+  const int t = blockIdx.x;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const float* xr = x + static_cast<int64_t>(t) * hidden;
+  float ss = 0.0f;
+  for (int i = tid; i < hidden; i += kF32Threads) {
+    const float v = xr[i];
+    xs[i] = v;
+    ss = fmaf(v, v, ss);
+  }
+#pragma unroll
+  for (int mask = 32; mask > 0; mask >>= 1) ss += __shfl_xor(ss, mask, 64);
+  if (lane == 0) partial[wave] = ss;
+  __syncthreads();
+  float total = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kF32Threads / 64; ++w) total += partial[w];
+  const float scale = 1.0f / sqrtf(total / static_cast<float>(hidden) + eps);
+  for (int i = tid; i < hidden; i += kF32Threads) xs[i] = xs[i] * scale * w_rms[i];
+  __syncthreads();
+
+  const int out_half = num_kv_heads * head_dim;
+  const int64_t blk = slot >> bs_shift;
+  const int64_t off = slot & (block_size - 1);
+  for (int o = wave; o < 2 * out_half; o += kF32Threads / 64) {
+    const bool is_v = o >= out_half;
+    const int hd = is_v ? o - out_half : o;
+    const float* wr = (is_v ? w_v : w_k) + static_cast<int64_t>(hd) * hidden;
+    float acc = 0.0f;
+    for (int i = lane; i < hidden; i += 64) acc = fmaf(wr[i], xs[i], acc);
+#pragma unroll
+    for (int mask = 32; mask > 0; mask >>= 1) acc += __shfl_xor(acc, mask, 64);
+    if (lane == 0) {
+      const int h = hd / head_dim;
+      const int d = hd - h * head_dim;
+      float* cache = is_v ? v_cache : k_cache;
+      cache[((blk * num_kv_heads + h) * block_size + off) * head_dim + d] = acc;
+    }
+  }
+}
+
+bool supported_dim(int d) { return d == 64 || d == 128 || d == 256; }
+
+}  // namespace
+
+extern "C" int64_t yoco_kv_append_workspace_size(int32_t dtype, int32_t hidden, int32_t num_kv_heads,
+                                                 int32_t head_dim) {
+  if (hidden <= 0 || num_kv_heads <= 0 || head_dim <= 0) return -1;
+  if (dtype != YOCO_DTYPE_BF16) return 0;
+  return static_cast<int64_t>(2) * num_kv_heads * head_dim * hidden * 2;
+}
+
+extern "C" int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_tokens, int32_t hidden,
+                                  const void* rms_weight, float eps, const void* w_k, const void* w_v,
+                                  const int32_t* slot_mapping, void* k_cache, void* v_cache, int32_t num_blocks,
+                                  int32_t num_kv_heads, int32_t block_size, int32_t head_dim, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
+  using namespace yoco;
+  if (dtype != YOCO_DTYPE_F32 && dtype != YOCO_DTYPE_BF16)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append: unknown dtype %d", dtype);
+  if (num_tokens < 0 || hidden <= 0 || num_blocks <= 0 || num_kv_heads <= 0 || workspace_bytes < 0)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append: negative or zero size argument");
+  if (!std::isfinite(eps) || eps < 0.0f) return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append: eps must be finite and >= 0");
+  if (!supported_dim(head_dim)) return fail(YOCO_ERR_UNSUPPORTED, "kv_append: head_dim %d not in {64,128,256}", head_dim);
+  if (!is_pow2(block_size) || block_size > 256)
+    return fail(YOCO_ERR_UNSUPPORTED, "kv_append: block_size %d is not a power of two <= 256", block_size);
+  if (hidden % 64 != 0) return fail(YOCO_ERR_UNSUPPORTED, "kv_append: hidden %d is not a multiple of 64", hidden);
+  if (dtype == YOCO_DTYPE_F32 && hidden > 16384)
+    return fail(YOCO_ERR_UNSUPPORTED, "kv_append: fp32 path supports hidden <= 16384");
+  const int64_t need = yoco_kv_append_workspace_size(dtype, hidden, num_kv_heads, head_dim);
+  if (workspace_bytes < need)
+    return fail(YOCO_ERR_WORKSPACE_TOO_SMALL, "kv_append: workspace %lld bytes, need %lld",
+                (long long)workspace_bytes, (long long)need);
+  if (num_tokens == 0) return YOCO_OK;
+  if (x == nullptr || rms_weight == nullptr || w_k == nullptr || w_v == nullptr || slot_mapping == nullptr ||
+      k_cache == nullptr || v_cache == nullptr || (need > 0 && workspace == nullptr))
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append: null pointer");
+  if (!aligned16(x) || !aligned16(rms_weight) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || (need > 0 && !aligned16(workspace)))
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append: buffers must be 16-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  const int bs_shift = ilog2(block_size);
+  clear_launch_error();
+  if (dtype == YOCO_DTYPE_F32) {
+    hipLaunchKernelGGL(kv_append_f32_kernel, dim3(num_tokens), dim3(kF32Threads), hidden * sizeof(float), s,
+                       static_cast<const float*>(x), hidden, static_cast<const float*>(rms_weight), eps,
+                       static_cast<const float*>(w_k), static_cast<const float*>(w_v), slot_mapping, num_slots,
+                       static_cast<float*>(k_cache), static_cast<float*>(v_cache), num_kv_heads, block_size,
+                       bs_shift, head_dim);
+    return launch_result("kv_append");
+  }
+
+  const int64_t out_half = static_cast<int64_t>(num_kv_heads) * head_dim;
+  const int64_t half_chunks = out_half * hidden / 8;
+  const int64_t fold_blocks = ceil_div(2 * half_chunks, 256);
+  hipLaunchKernelGGL(fold_rms_weight_kernel, dim3(static_cast<uint32_t>(fold_blocks)), dim3(256), 0, s,
+                     static_cast<const uint4*>(w_k), static_cast<const uint4*>(w_v),
+                     static_cast<const uint4*>(rms_weight), static_cast<uint4*>(workspace), half_chunks, hidden / 8);
+
+  AppendArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.w = static_cast<const uint16_t*>(workspace);
+  a.slots = slot_mapping;
+  a.k_cache = static_cast<uint16_t*>(k_cache);
+  a.v_cache = static_cast<uint16_t*>(v_cache);
+  a.num_tokens = num_tokens;
+  a.hidden = hidden;
+  a.out_half = static_cast<int32_t>(out_half);
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.bs_shift = bs_shift;
+  a.num_kv_heads = num_kv_heads;
+  a.num_slots = num_slots;
+  a.inv_hidden = 1.0f / static_cast<float>(hidden);
+  a.eps = eps;
+  const dim3 grid(static_cast<uint32_t>(2 * out_half / kBN), static_cast<uint32_t>(ceil_div(num_tokens, kBM)));
+  hipLaunchKernelGGL(kv_append_mfma_kernel, grid, dim3(kGemmThreads), 0, s, a);
+  return launch_result("kv_append");
+}

@@ -1,0 +1,42 @@
+// Internal helpers shared by the HIP sources of libyoco (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "yoco.h"
+
+namespace yoco {
+
+// ---- host side --------------------------------------------------------------
+
+// Record a failure reason for yoco_last_error_message() and return `status`.
+int32_t fail(int32_t status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Clear any stale launch error on this thread (call right before a launch).
+inline void clear_launch_error() { (void)hipGetLastError(); }
+
+// Status of the launches enqueued since clear_launch_error().
+int32_t launch_result(const char* what);
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+inline int ilog2(int64_t v) { int s = 0; while ((int64_t(1) << s) < v) ++s; return s; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// ---- device side ------------------------------------------------------------
+
+// bf16 halves of a 32-bit word, widened exactly to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+}  // namespace yoco
