@@ -133,9 +133,10 @@ def main():
     slots = torch.from_numpy(meta.slot_mapping).to(dev)
     code = yb.DTYPE_BF16 if geom.dtype == "bf16" else yb.DTYPE_F32
     part, nparts = yb.describe_launch(meta.num_reqs, geom.num_kv_heads, geom.head_dim, meta.max_seq_len,
-                                      args.partition_tokens)
+                                      geom.block_size, args.partition_tokens)
     ws = torch.zeros(max(1, yb.cross_attn_workspace_size(meta.num_reqs, geom.num_q_heads, geom.num_kv_heads,
-                                                         geom.head_dim, meta.max_seq_len, args.partition_tokens)),
+                                                         geom.head_dim, meta.max_seq_len, geom.block_size,
+                                                         args.partition_tokens)),
                      dtype=torch.uint8, device=dev)
     ws_append = torch.zeros(max(1, yb.kv_append_workspace_size(code, geom.hidden, geom.num_kv_heads, geom.head_dim)),
                             dtype=torch.uint8, device=dev)

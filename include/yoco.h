@@ -184,29 +184,31 @@ int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_tokens, int32_t
  *   scale        softmax scale; the pages' value is 1/sqrt(head_dim).
  *   partition_tokens  tokens per split-KV partition: 0 picks one from the
  *                shape (yoco_cross_attn_partition_tokens), otherwise a
- *                positive multiple of 64.
+ *                positive multiple of 64 spanning at most 1023 blocks and at
+ *                most 16384 tokens (YOCO_ERR_UNSUPPORTED beyond).
  *   flags        YOCO_FLAG_REVERSE_ORDER or 0.
  *   out          fp32 [num_seqs][num_q_heads][head_dim].
  *   workspace    device scratch of at least yoco_cross_attn_workspace_size()
- *                bytes for the same arguments (per-(request, KV head)
- *                arrival counters followed by the partitions' partial
- *                results); may be NULL when that size is 0.  It must be
- *                zero-filled before its first use; every call leaves the
- *                counters zero again.  Calls that may run concurrently (other
- *                streams) need separate workspaces.
+ *                bytes for the same arguments (the partitions' partial
+ *                results, merged by a second kernel on the same stream);
+ *                may be NULL when that size is 0.  No initial contents are
+ *                needed.  Calls that may run concurrently (other streams)
+ *                need separate workspaces.
  *
  * Supported: head_dim in {64, 128, 256}; num_q_heads / num_kv_heads in
  * {1, 2, 4, 8}; block_size a power of two in [1, 256]; at most 65535
- * partitions per request.
+ * partitions per request.  The two sizing helpers return -1 for invalid
+ * arguments.
  * Errors: YOCO_ERR_INVALID_ARGUMENT, YOCO_ERR_UNSUPPORTED,
  * YOCO_ERR_WORKSPACE_TOO_SMALL, YOCO_ERR_HIP.  num_seqs == 0 is a no-op.
  * Results are deterministic: the same inputs give the same bits, with or
  * without YOCO_FLAG_REVERSE_ORDER.
  */
 int32_t yoco_cross_attn_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                                         int32_t max_seq_len, int32_t partition_tokens);
+                                         int32_t max_seq_len, int32_t block_size,
+                                         int32_t partition_tokens);
 int64_t yoco_cross_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                       int32_t head_dim, int32_t max_seq_len,
+                                       int32_t head_dim, int32_t max_seq_len, int32_t block_size,
                                        int32_t partition_tokens);
 int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seqs, int32_t num_q_heads,
                         const void* k_cache, const void* v_cache, int32_t num_blocks,

@@ -43,8 +43,8 @@ SIGNATURES = {
     "yoco_kv_append_workspace_size": (_i64, [_i32, _i32, _i32, _i32]),
     "yoco_kv_append": (_i32, [_i32, _vp, _i32, _i32, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                               _vp, _i64, _vp]),
-    "yoco_cross_attn_partition_tokens": (_i32, [_i32, _i32, _i32, _i32, _i32]),
-    "yoco_cross_attn_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "yoco_cross_attn_partition_tokens": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "yoco_cross_attn_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "yoco_cross_attn": (_i32, [_i32, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _f32,
                                _i32, _u32, _vp, _vp, _i64, _vp]),
 }
@@ -166,23 +166,23 @@ def kv_append(x, rms_weight, eps, w_k, w_v, slot_mapping, k_cache, v_cache, work
 
 # ---- yoco_cross_attn -----------------------------------------------------------------
 
-def cross_attn_partition_tokens(num_seqs, num_kv_heads, head_dim, max_seq_len, partition_tokens=0) -> int:
-    return int(lib().yoco_cross_attn_partition_tokens(num_seqs, num_kv_heads, head_dim, max_seq_len,
+def cross_attn_partition_tokens(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size,
+                                partition_tokens=0) -> int:
+    return int(lib().yoco_cross_attn_partition_tokens(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size,
                                                        partition_tokens))
 
 
-def cross_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens=0) -> int:
+def cross_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size,
+                              partition_tokens=0) -> int:
     return int(lib().yoco_cross_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
-                                                     partition_tokens))
+                                                     block_size, partition_tokens))
 
 
 def cross_attn(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale=None, partition_tokens=0, flags=0,
                out=None, workspace=None, stream=None):
     """One cross layer: out[r][h] = softmax(scale q.K^T) V over request r's context.
 
-    A caller-supplied ``workspace`` must start zeroed (torch.zeros) before its
-    first use; every call leaves its counters zero again.  Calls that may run
-    concurrently need separate workspaces."""
+    Calls that may run concurrently need separate workspaces."""
     torch = _torch()
     code = _dtype_code(q)
     num_seqs, num_q_heads, head_dim = q.shape
@@ -191,12 +191,12 @@ def cross_attn(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale=No
         scale = 1.0 / math.sqrt(head_dim)
     if out is None:
         out = torch.empty((num_seqs, num_q_heads, head_dim), dtype=torch.float32, device=q.device)
-    need = cross_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, partition_tokens)
+    need = cross_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size,
+                                     partition_tokens)
     if need < 0:
         raise YocoError(YOCO_ERR_INVALID_ARGUMENT, "bad cross_attn shape")
     if workspace is None and need > 0:
-        # the counters at the start of the workspace must be zero before first use
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().yoco_cross_attn(code, _dev(q, "q"), num_seqs, num_q_heads, _dev(k_cache, "k_cache"),
@@ -220,7 +220,7 @@ def library_path() -> str:
     return LIB_PATH
 
 
-def describe_launch(num_seqs, num_kv_heads, head_dim, max_seq_len, partition_tokens=0) -> Tuple[int, int]:
+def describe_launch(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens=0) -> Tuple[int, int]:
     """(partition_tokens, partitions per request) that yoco_cross_attn will use."""
-    p = cross_attn_partition_tokens(num_seqs, num_kv_heads, head_dim, max_seq_len, partition_tokens)
+    p = cross_attn_partition_tokens(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens)
     return p, max(1, -(-max(max_seq_len, 1) // p))

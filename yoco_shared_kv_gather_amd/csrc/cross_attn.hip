@@ -8,27 +8,31 @@
 // section "Contiguous allocation wastes capacity").
 //
 // How (gfx950):
-//   * Split-KV.  Work item = (request, KV head, partition of
-//     `partition_tokens` context tokens); one wavefront per work item, so a
-//     long context still spreads over every compute unit.  When a request has
-//     more than one partition, each writes an unnormalised partial
-//     (acc, running max m, running sum l) to the workspace and bumps a
-//     per-(request, KV head) counter with agent-scope acquire/release
-//     ordering; the wavefront that brings the counter to the partition count
-//     merges all partials with log-sum-exp weights in partition order (so the
-//     bits do not depend on which wavefront finishes last) and resets the
-//     counter to zero.  One launch per layer, no separate merge kernel.
-//   * One wavefront reads each K^/V^ row exactly once and uses it for all G
-//     query heads of its KV group (GQA); the G queries stay in registers.
-//   * A K^ or V^ row of head_dim elements is split into 16-byte chunks;
-//     LPR lanes cover one row with CPL chunks each, so a wavefront instruction
-//     loads 64/LPR whole rows, fully coalesced within each cache block.
+//   * Split-KV.  A workgroup of four wavefronts owns one work item =
+//     (request, KV head, partition of `partition_tokens` context tokens), so a
+//     long context still spreads over every compute unit.  The partition's
+//     block-table slice is staged in LDS once; the four wavefronts take every
+//     fourth iteration of the partition and combine their softmax states in
+//     LDS at the end.
+//   * When a request has more than one partition, each workgroup writes an
+//     unnormalised partial (acc, running max m, running sum l) to the
+//     workspace and a second, small kernel merges them with log-sum-exp
+//     weights in partition order (deterministic).  A request that fits one
+//     partition is finished by the first kernel.  The kernel boundary makes
+//     the partials visible; making them visible from inside the first kernel
+//     would need an agent-scope release (an L2 write-back) per workgroup,
+//     and those serialise per XCD.
+//   * Each K^/V^ row is read once and used for all G query heads of its KV
+//     group (GQA); the G queries stay in registers.
+//   * A row of head_dim elements is split into 16-byte chunks; LPR lanes cover
+//     one row with CPL chunks each, so one wavefront load instruction reads
+//     64/LPR rows, coalesced within each cache block.  The next iteration's
+//     rows are loaded while the current ones are used (two register sets).
 //   * q.k uses v_dot2_f32_bf16 (two bf16 products per instruction, fp32
-//     accumulation), then a butterfly over the LPR lanes of a row.
-//   * Online softmax in base 2 with a lazy maximum: the running max of a
-//     row group is raised only when a score exceeds it by more than 2^8, so
-//     the rescale of the accumulators is rare; the partial sums stay bounded
-//     by 256 times the true terms, far from fp32 overflow.
+//     accumulation) and a DPP all-reduce over the LPR lanes of a row.
+//   * Online softmax in base 2 with a lazy maximum: the running max of a row
+//     group is raised only when a score exceeds it by more than 2^8, so the
+//     accumulators are rescaled rarely; sums stay within 256x the true terms.
 //   * p.v in fp32 FMA; bf16 values widen with one shift or mask.
 
 #include <cmath>
@@ -43,6 +47,9 @@ using yoco::bf16_lo;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyMaxSlack = 8.0f;      // log2 of the largest un-rescaled term
 constexpr float kInitMax = -1.0e30f;       // finite "minus infinity" for running maxima
+constexpr int kWaves = 4;                  // wavefronts per workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kMaxSliceBlocks = 1024;      // block-table entries one partition may span
 
 struct AttnArgs {
   const void* q;
@@ -51,7 +58,6 @@ struct AttnArgs {
   const int32_t* block_table;
   const int32_t* seq_lens;
   float* out;
-  uint32_t* counters;   // [num_seqs][Hkv], zero between calls
   float* ws_acc;        // [num_seqs][Hq][num_parts][D]
   float* ws_ml;         // [num_seqs][Hq][num_parts][2]  (max, sum), base-2 units
   int64_t block_stride; // elements per physical block (Hkv * bs * D)
@@ -77,6 +83,8 @@ struct Layout {
   static constexpr int kLpr = kChunks / 2 < 16 ? kChunks / 2 : 16;   // lanes per row
   static constexpr int kCpl = kChunks / kLpr;             // chunks per lane
   static constexpr int kRpw = 64 / kLpr;                  // rows per wave instruction
+  static constexpr int kU = 2;                            // row sets per iteration
+  static constexpr int kIterTokens = kRpw * kU;
 };
 
 // Dot product of one 16-byte chunk of q with one of k, accumulated into acc.
@@ -113,7 +121,26 @@ __device__ __forceinline__ float chunk_elem(const uint4& c, int e) {
   }
 }
 
-__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+// v + (v of another lane chosen by a DPP control word), in every lane.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int other = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, true);
+  return v + __builtin_bit_cast(float, other);
+}
+
+// Sum over aligned groups of kLanes lanes (4, 8 or 16), result in every lane.
+// quad_perm [1,0,3,2] and [2,3,0,1] pair lanes inside a quad; row_half_mirror
+// pairs each quad of 8 lanes with the other; row_mirror pairs the two halves
+// of a 16-lane row.
+template <int kLanes>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(kLanes == 4 || kLanes == 8 || kLanes == 16, "group of 4, 8 or 16 lanes");
+  v = dpp_add<0xB1>(v);
+  v = dpp_add<0x4E>(v);
+  if constexpr (kLanes >= 8) v = dpp_add<0x141>(v);
+  if constexpr (kLanes >= 16) v = dpp_add<0x140>(v);
+  return v;
+}
 
 // Wavefront reductions with a fixed butterfly order (deterministic).
 __device__ __forceinline__ float wave_max(float v) {
@@ -127,48 +154,64 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ float load_agent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Merge the partials of one (request, query head):
+//   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
+// One wavefront: lanes stride over partitions for M and the denominator,
+// then own head_dim/64 dimensions of the numerator, which adds partitions in
+// order 0..np-1.  Requests with a single partition were finished already.
+template <int D>
+__global__ __launch_bounds__(64) void cross_attn_merge_kernel(AttnArgs a) {
+  constexpr int kDpl = D / 64;
+  const int64_t rh = blockIdx.x;
+  const int r = static_cast<int>(rh / a.num_q_heads);
+  const int lane = threadIdx.x;
+  int n = a.seq_lens[r];
+  n = n < 0 ? 0 : (n > a.len_cap ? a.len_cap : n);
+  const int np = (n + a.part_tokens - 1) / a.part_tokens;
+  if (np <= 1) return;
+  const float* ml = a.ws_ml + rh * a.num_parts * 2;
+  const float* acc = a.ws_acc + rh * a.num_parts * D + lane;
+  float mx = kInitMax;
+  for (int p = lane; p < np; p += 64) mx = fmaxf(mx, ml[2 * p]);
+  mx = wave_max(mx);
+  float den = 0.0f;
+  for (int p = lane; p < np; p += 64) den = fmaf(exp2f(ml[2 * p] - mx), ml[2 * p + 1], den);
+  den = wave_sum(den);
+  float num[kDpl];
+#pragma unroll
+  for (int i = 0; i < kDpl; ++i) num[i] = 0.0f;
+#pragma unroll 4
+  for (int p = 0; p < np; ++p) {
+    const float w = exp2f(ml[2 * p] - mx);
+#pragma unroll
+    for (int i = 0; i < kDpl; ++i) num[i] = fmaf(w, acc[static_cast<int64_t>(p) * D + 64 * i], num[i]);
+  }
+  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+#pragma unroll
+  for (int i = 0; i < kDpl; ++i) a.out[rh * D + lane + 64 * i] = num[i] * inv;
 }
 
-// Merge the np partials of the G query heads hq0.. of request r:
-//   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p,
-// summing partitions in order 0..np-1.  Lanes own head_dim/64 dimensions.
-template <int D, int G>
-__device__ __forceinline__ void merge_partials(const AttnArgs& a, int r, int hq0, int np, int lane) {
-  constexpr int kDpl = D / 64;
-  for (int h = 0; h < G; ++h) {
-    const int64_t rh = static_cast<int64_t>(r) * a.num_q_heads + hq0 + h;
-    const float* ml = a.ws_ml + rh * a.num_parts * 2;
-    const float* acc = a.ws_acc + rh * a.num_parts * D;
-    float mx = kInitMax;
-    for (int p = lane; p < np; p += 64) mx = fmaxf(mx, load_agent(ml + 2 * p));
-    mx = wave_max(mx);
-    float den = 0.0f;
-    for (int p = lane; p < np; p += 64) den += exp2f(load_agent(ml + 2 * p) - mx) * load_agent(ml + 2 * p + 1);
-    den = wave_sum(den);
-    float num[kDpl];
-#pragma unroll
-    for (int i = 0; i < kDpl; ++i) num[i] = 0.0f;
-    for (int p = 0; p < np; ++p) {
-      const float w = exp2f(load_agent(ml + 2 * p) - mx);
-#pragma unroll
-      for (int i = 0; i < kDpl; ++i) num[i] = fmaf(w, load_agent(acc + static_cast<int64_t>(p) * D + lane + 64 * i), num[i]);
-    }
-    const float inv = den > 0.0f ? 1.0f / den : 0.0f;
-#pragma unroll
-    for (int i = 0; i < kDpl; ++i) a.out[rh * D + lane + 64 * i] = num[i] * inv;
-  }
-}
+template <bool kBf16, int D>
+struct RowSet {
+  uint4 k[Layout<kBf16, D>::kU][Layout<kBf16, D>::kCpl];
+  uint4 v[Layout<kBf16, D>::kU][Layout<kBf16, D>::kCpl];
+  bool valid[Layout<kBf16, D>::kU];
+};
 
 template <bool kBf16, int D, int G>
-__global__ __launch_bounds__(64) void cross_attn_partial_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
   using L = Layout<kBf16, D>;
-  constexpr int kEpc = L::kEpc, kLpr = L::kLpr, kCpl = L::kCpl, kRpw = L::kRpw;
-  constexpr int kU = 2;                       // row sets in flight per iteration
+  constexpr int kEpc = L::kEpc, kLpr = L::kLpr, kCpl = L::kCpl, kRpw = L::kRpw, kU = L::kU;
+  constexpr int kIterTokens = L::kIterTokens;
   constexpr int kElemBytes = kBf16 ? 2 : 4;
 
-  const int lane = threadIdx.x;
+  __shared__ int32_t s_blocks[kMaxSliceBlocks];
+  __shared__ float s_acc[kWaves][G][D];
+  __shared__ float s_ml[kWaves][G][2];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int row = lane / kLpr;
   const int cl = lane % kLpr;
 
@@ -189,11 +232,22 @@ __global__ __launch_bounds__(64) void cross_attn_partial_kernel(AttnArgs a) {
     // Partitions past the end do nothing; the first one answers an empty
     // context with zeros.
     if (n == 0 && part == 0) {
-      for (int i = lane; i < G * D; i += 64) a.out[(static_cast<int64_t>(r) * a.num_q_heads + hq0) * D + i] = 0.0f;
+      for (int i = tid; i < G * D; i += kThreads) a.out[(static_cast<int64_t>(r) * a.num_q_heads + hq0) * D + i] = 0.0f;
     }
     return;
   }
   const int end = min(start + a.part_tokens, n);
+
+  // The partition's block-table slice; out-of-range ids become -1 (skipped).
+  const int first_blk = start >> a.bs_shift;
+  const int num_blk = ((end - 1) >> a.bs_shift) - first_blk + 1;
+  {
+    const int32_t* table = a.block_table + static_cast<int64_t>(r) * a.max_blocks + first_blk;
+    for (int i = tid; i < num_blk; i += kThreads) {
+      const int b = table[i];
+      s_blocks[i] = static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks) ? b : -1;
+    }
+  }
 
   // Queries of the G heads of this group, the chunks this lane owns.
   uint4 qr[G][kCpl];
@@ -217,41 +271,38 @@ __global__ __launch_bounds__(64) void cross_attn_partial_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < kEpc; ++e) acc[h][i][e] = 0.0f;
   }
+  __syncthreads();
 
-  const int32_t* table = a.block_table + static_cast<int64_t>(r) * a.max_blocks;
   const char* kb = static_cast<const char*>(a.k) + static_cast<int64_t>(g) * a.head_stride * kElemBytes;
   const char* vb = static_cast<const char*>(a.v) + static_cast<int64_t>(g) * a.head_stride * kElemBytes;
   const int off_mask = a.block_size - 1;
+  const int num_iters = (end - start + kIterTokens - 1) / kIterTokens;
 
-  for (int base = start; base < end; base += kRpw * kU) {
-    uint4 kr[kU][kCpl], vr[kU][kCpl];
-    bool valid[kU];
+  auto load = [&](RowSet<kBf16, D>& rs, int it) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int j = base + u * kRpw + row;
-      bool ok = j < end;
-      int64_t off = 0;
-      if (ok) {
-        const int blk = table[j >> a.bs_shift];
-        ok = static_cast<unsigned>(blk) < static_cast<unsigned>(a.num_blocks);
-        off = (static_cast<int64_t>(blk) * a.block_stride + static_cast<int64_t>(j & off_mask) * D) * kElemBytes;
-      }
-      valid[u] = ok;
+      const int j = start + it * kIterTokens + u * kRpw + row;
+      int blk = -1;
+      if (j < end) blk = s_blocks[(j >> a.bs_shift) - first_blk];
+      const bool ok = blk >= 0;
+      rs.valid[u] = ok;
+      const int64_t off = (static_cast<int64_t>(ok ? blk : 0) * a.block_stride +
+                           static_cast<int64_t>(j & off_mask) * D) * kElemBytes;
 #pragma unroll
       for (int i = 0; i < kCpl; ++i) {
         const int64_t c = off + static_cast<int64_t>((cl + kLpr * i) * kEpc) * kElemBytes;
         if (ok) {
-          kr[u][i] = *reinterpret_cast<const uint4*>(kb + c);
-          vr[u][i] = *reinterpret_cast<const uint4*>(vb + c);
+          rs.k[u][i] = *reinterpret_cast<const uint4*>(kb + c);
+          rs.v[u][i] = *reinterpret_cast<const uint4*>(vb + c);
         } else {
-          kr[u][i] = make_uint4(0u, 0u, 0u, 0u);
-          vr[u][i] = make_uint4(0u, 0u, 0u, 0u);
+          rs.k[u][i] = make_uint4(0u, 0u, 0u, 0u);
+          rs.v[u][i] = make_uint4(0u, 0u, 0u, 0u);
         }
       }
     }
+  };
 
-    // Scores: partial dots over this lane's chunks, then a butterfly over the
-    // kLpr lanes of the row (all of them end with the full sum).
+  auto compute = [&](const RowSet<kBf16, D>& rs) {
     float s[kU][G];
 #pragma unroll
     for (int u = 0; u < kU; ++u)
@@ -259,20 +310,10 @@ __global__ __launch_bounds__(64) void cross_attn_partial_kernel(AttnArgs a) {
       for (int h = 0; h < G; ++h) {
         float t = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kCpl; ++i) t = chunk_dot<kBf16>(qr[h][i], kr[u][i], t);
-        s[u][h] = t;
+        for (int i = 0; i < kCpl; ++i) t = chunk_dot<kBf16>(qr[h][i], rs.k[u][i], t);
+        t = group_sum<kLpr>(t);
+        s[u][h] = rs.valid[u] ? t * a.scale_log2 : -INFINITY;
       }
-#pragma unroll
-    for (int mask = 1; mask < kLpr; mask <<= 1)
-#pragma unroll
-      for (int u = 0; u < kU; ++u)
-#pragma unroll
-        for (int h = 0; h < G; ++h) s[u][h] += shfl_xor_f(s[u][h], mask);
-#pragma unroll
-    for (int u = 0; u < kU; ++u)
-#pragma unroll
-      for (int h = 0; h < G; ++h) s[u][h] = valid[u] ? s[u][h] * a.scale_log2 : -INFINITY;
-
     // Lazy running maximum per row group and head.
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -289,7 +330,6 @@ __global__ __launch_bounds__(64) void cross_attn_partial_kernel(AttnArgs a) {
         m[h] = cand;
       }
     }
-
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       float p[G];
@@ -302,10 +342,29 @@ __global__ __launch_bounds__(64) void cross_attn_partial_kernel(AttnArgs a) {
       for (int i = 0; i < kCpl; ++i)
 #pragma unroll
         for (int e = 0; e < kEpc; ++e) {
-          const float x = chunk_elem<kBf16>(vr[u][i], e);
+          const float x = chunk_elem<kBf16>(rs.v[u][i], e);
 #pragma unroll
           for (int h = 0; h < G; ++h) acc[h][i][e] = fmaf(p[h], x, acc[h][i][e]);
         }
+    }
+  };
+
+  // Wavefront w takes iterations w, w+4, ...; the next one's rows are in
+  // flight while the current ones are used.
+  {
+    RowSet<kBf16, D> buf_a, buf_b;
+    int it = wave;
+    if (it < num_iters) load(buf_a, it);
+    while (it < num_iters) {
+      int nx = it + kWaves;
+      if (nx < num_iters) load(buf_b, nx);
+      compute(buf_a);
+      it = nx;
+      if (it >= num_iters) break;
+      nx = it + kWaves;
+      if (nx < num_iters) load(buf_a, nx);
+      compute(buf_b);
+      it = nx;
     }
   }
 
@@ -314,8 +373,8 @@ __global__ __launch_bounds__(64) void cross_attn_partial_kernel(AttnArgs a) {
   for (int mask = kLpr; mask < 64; mask <<= 1) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mo = shfl_xor_f(m[h], mask);
-      const float lo = shfl_xor_f(lsum[h], mask);
+      const float mo = __shfl_xor(m[h], mask, 64);
+      const float lo = __shfl_xor(lsum[h], mask, 64);
       const float mx = fmaxf(m[h], mo);
       const float fa = exp2f(m[h] - mx);
       const float fb = exp2f(mo - mx);
@@ -324,79 +383,77 @@ __global__ __launch_bounds__(64) void cross_attn_partial_kernel(AttnArgs a) {
       for (int i = 0; i < kCpl; ++i)
 #pragma unroll
         for (int e = 0; e < kEpc; ++e) {
-          const float other = shfl_xor_f(acc[h][i][e], mask);
+          const float other = __shfl_xor(acc[h][i][e], mask, 64);
           acc[h][i][e] = acc[h][i][e] * fa + other * fb;
         }
       m[h] = mx;
     }
   }
-
-  const int np_r = (n + a.part_tokens - 1) / a.part_tokens;      // partitions holding tokens
-  if (np_r == 1) {
-    if (row == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const int64_t rh = static_cast<int64_t>(r) * a.num_q_heads + hq0 + h;
-        const float inv = lsum[h] > 0.0f ? 1.0f / lsum[h] : 0.0f;
-        float* o = a.out + rh * D;
-#pragma unroll
-        for (int i = 0; i < kCpl; ++i) {
-          float4* dst = reinterpret_cast<float4*>(o + (cl + kLpr * i) * kEpc);
-#pragma unroll
-          for (int e4 = 0; e4 < kEpc / 4; ++e4)
-            dst[e4] = make_float4(acc[h][i][4 * e4] * inv, acc[h][i][4 * e4 + 1] * inv,
-                                  acc[h][i][4 * e4 + 2] * inv, acc[h][i][4 * e4 + 3] * inv);
-        }
-      }
-    }
-    return;
-  }
-
-  // Several partitions: publish this one's partial.
   if (row == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const int64_t slot = (static_cast<int64_t>(r) * a.num_q_heads + hq0 + h) * a.num_parts + part;
-      float* o = a.ws_acc + slot * D;
 #pragma unroll
-      for (int i = 0; i < kCpl; ++i) {
-        float4* dst = reinterpret_cast<float4*>(o + (cl + kLpr * i) * kEpc);
+      for (int i = 0; i < kCpl; ++i)
 #pragma unroll
-        for (int e4 = 0; e4 < kEpc / 4; ++e4)
-          dst[e4] = make_float4(acc[h][i][4 * e4], acc[h][i][4 * e4 + 1], acc[h][i][4 * e4 + 2],
-                                acc[h][i][4 * e4 + 3]);
-      }
+        for (int e = 0; e < kEpc; ++e) s_acc[wave][h][(cl + kLpr * i) * kEpc + e] = acc[h][i][e];
       if (cl == 0) {
-        a.ws_ml[slot * 2] = m[h];
-        a.ws_ml[slot * 2 + 1] = lsum[h];
+        s_ml[wave][h][0] = m[h];
+        s_ml[wave][h][1] = lsum[h];
       }
     }
   }
-  __threadfence();
-  uint32_t* counter = a.counters + static_cast<int64_t>(r) * a.num_kv_heads + g;
-  uint32_t arrived = 0;
-  if (lane == 0) arrived = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-  arrived = __shfl(arrived, 0, 64);
-  if (arrived != static_cast<uint32_t>(np_r - 1)) return;
-  __threadfence();
-  merge_partials<D, G>(a, r, hq0, np_r, lane);
-  if (lane == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+
+  // Combine the four wavefronts, then finish (one partition) or publish.
+  const int np_r = (n + a.part_tokens - 1) / a.part_tokens;
+  for (int e = tid; e < G * D; e += kThreads) {
+    const int h = e / D;
+    const int d = e - h * D;
+    float mx = s_ml[0][h][0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, s_ml[w][h][0]);
+    float den = 0.0f, num = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float f = exp2f(s_ml[w][h][0] - mx);
+      den = fmaf(f, s_ml[w][h][1], den);
+      num = fmaf(f, s_acc[w][h][d], num);
+    }
+    const int64_t rh = static_cast<int64_t>(r) * a.num_q_heads + hq0 + h;
+    if (np_r == 1) {
+      a.out[rh * D + d] = den > 0.0f ? num / den : 0.0f;
+    } else {
+      const int64_t slot = rh * a.num_parts + part;
+      a.ws_acc[slot * D + d] = num;
+      if (d == 0) {
+        a.ws_ml[slot * 2] = mx;
+        a.ws_ml[slot * 2 + 1] = den;
+      }
+    }
+  }
 }
 
 // ---- host side ---------------------------------------------------------------
 
 constexpr int kMaxParts = 65535;
 
-int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t requested) {
+// Largest partition whose block-table slice fits the LDS staging array.
+int32_t max_partition(int32_t block_size) {
+  const int64_t cap = static_cast<int64_t>(kMaxSliceBlocks - 1) * block_size / 64 * 64;
+  return static_cast<int32_t>(cap < 16384 ? cap : 16384);
+}
+
+int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t block_size,
+                          int32_t requested) {
   if (requested > 0) return requested;
-  // Aim for about 2048 work items (eight wavefronts per compute unit) with
-  // partitions of 64..16384 tokens.
+  // Aim for about 2048 workgroups (8192 wavefronts, 32 per compute unit when
+  // every context is full length) with partitions of 64 tokens or more.
   const int64_t items = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
   const int64_t parts = yoco::ceil_div(2048, items);
   int64_t p = yoco::round_up(yoco::ceil_div(max_seq_len > 0 ? max_seq_len : 1, parts), 64);
+  const int64_t cap = max_partition(block_size > 0 ? block_size : 1);
+  if (p > cap) p = cap;
   if (p < 64) p = 64;
-  if (p > 16384) p = 16384;
-  while (yoco::ceil_div(max_seq_len, p) > kMaxParts) p *= 2;
   return static_cast<int32_t>(p);
 }
 
@@ -405,8 +462,7 @@ int32_t num_partitions(int32_t max_seq_len, int32_t part_tokens) {
   return static_cast<int32_t>(np);
 }
 
-// Workspace: [counters uint32 num_seqs*Hkv | pad to 256][acc fp32 | pad][ml fp32].
-// The counters must be zero before the first call; every call leaves them zero.
+// Workspace: [acc fp32 num_seqs*Hq*num_parts*D | pad to 256][ml fp32 num_seqs*Hq*num_parts*2].
 struct WorkspaceLayout {
   int64_t acc_offset = 0;
   int64_t ml_offset = 0;
@@ -418,24 +474,25 @@ WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t 
   WorkspaceLayout w;
   if (num_parts <= 1) return w;
   const int64_t slots = static_cast<int64_t>(num_seqs) * num_q_heads * num_parts;
-  w.acc_offset = yoco::round_up(static_cast<int64_t>(num_seqs) * num_kv_heads * 4, 256);
-  w.ml_offset = w.acc_offset + yoco::round_up(slots * head_dim * 4, 256);
+  (void)num_kv_heads;
+  w.acc_offset = 0;
+  w.ml_offset = yoco::round_up(slots * head_dim * 4, 256);
   w.total = w.ml_offset + slots * 2 * 4;
   return w;
 }
 
 template <bool kBf16, int D, int G>
-void launch_partial(const AttnArgs& a, uint32_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((cross_attn_partial_kernel<kBf16, D, G>), dim3(grid), dim3(64), 0, stream, a);
+void launch(const AttnArgs& a, uint32_t grid, hipStream_t stream) {
+  hipLaunchKernelGGL((cross_attn_kernel<kBf16, D, G>), dim3(grid), dim3(kThreads), 0, stream, a);
 }
 
 template <bool kBf16, int D>
 bool dispatch_group(int group, const AttnArgs& a, uint32_t grid, hipStream_t stream) {
   switch (group) {
-    case 1: launch_partial<kBf16, D, 1>(a, grid, stream); return true;
-    case 2: launch_partial<kBf16, D, 2>(a, grid, stream); return true;
-    case 4: launch_partial<kBf16, D, 4>(a, grid, stream); return true;
-    case 8: launch_partial<kBf16, D, 8>(a, grid, stream); return true;
+    case 1: launch<kBf16, D, 1>(a, grid, stream); return true;
+    case 2: launch<kBf16, D, 2>(a, grid, stream); return true;
+    case 4: launch<kBf16, D, 4>(a, grid, stream); return true;
+    case 8: launch<kBf16, D, 8>(a, grid, stream); return true;
     default: return false;
   }
 }
@@ -455,17 +512,20 @@ bool supported_dim(int d) { return d == 64 || d == 128 || d == 256; }
 }  // namespace
 
 extern "C" int32_t yoco_cross_attn_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
-                                                    int32_t max_seq_len, int32_t partition_tokens) {
+                                                    int32_t max_seq_len, int32_t block_size,
+                                                    int32_t partition_tokens) {
   (void)head_dim;
-  if (partition_tokens < 0 || max_seq_len < 0) return -1;
-  return resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
+  if (partition_tokens < 0 || max_seq_len < 0 || block_size <= 0) return -1;
+  return resolve_partition(num_seqs, num_kv_heads, max_seq_len, block_size, partition_tokens);
 }
 
 extern "C" int64_t yoco_cross_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                                                  int32_t head_dim, int32_t max_seq_len,
+                                                  int32_t head_dim, int32_t max_seq_len, int32_t block_size,
                                                   int32_t partition_tokens) {
-  if (num_seqs < 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || partition_tokens < 0) return -1;
-  const int32_t p = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
+  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0 ||
+      block_size <= 0 || partition_tokens < 0)
+    return -1;
+  const int32_t p = resolve_partition(num_seqs, num_kv_heads, max_seq_len, block_size, partition_tokens);
   return workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, num_partitions(max_seq_len, p)).total;
 }
 
@@ -495,6 +555,9 @@ extern "C" int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seq
     return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: %d query heads per KV head not in {1,2,4,8}", group);
   if (!is_pow2(block_size) || block_size > 256)
     return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: block_size %d is not a power of two <= 256", block_size);
+  if (partition_tokens > max_partition(block_size))
+    return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: partition_tokens %d exceeds %d for block_size %d",
+                partition_tokens, max_partition(block_size), block_size);
   if (num_seqs == 0) return YOCO_OK;
   if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr || seq_lens == nullptr ||
       out == nullptr)
@@ -502,7 +565,7 @@ extern "C" int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seq
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: q, caches and out must be 16-byte aligned");
 
-  const int32_t part = resolve_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
+  const int32_t part = resolve_partition(num_seqs, num_kv_heads, max_seq_len, block_size, partition_tokens);
   const int32_t nparts = num_partitions(max_seq_len, part);
   if (nparts > kMaxParts)
     return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: %d partitions per request exceed %d", nparts, kMaxParts);
@@ -523,7 +586,6 @@ extern "C" int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seq
   a.seq_lens = seq_lens;
   a.out = out;
   char* wsb = static_cast<char*>(workspace);
-  a.counters = ws.total > 0 ? reinterpret_cast<uint32_t*>(wsb) : nullptr;
   a.ws_acc = ws.total > 0 ? reinterpret_cast<float*>(wsb + ws.acc_offset) : nullptr;
   a.ws_ml = ws.total > 0 ? reinterpret_cast<float*>(wsb + ws.ml_offset) : nullptr;
   a.head_stride = block_size * head_dim;
@@ -547,5 +609,13 @@ extern "C" int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seq
   const bool ok = dtype == YOCO_DTYPE_BF16 ? dispatch_dim<true>(head_dim, group, a, static_cast<uint32_t>(grid), s)
                                            : dispatch_dim<false>(head_dim, group, a, static_cast<uint32_t>(grid), s);
   if (!ok) return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: no kernel for this shape");
+  if (nparts > 1) {
+    const uint32_t mgrid = static_cast<uint32_t>(static_cast<int64_t>(num_seqs) * num_q_heads);
+    switch (head_dim) {
+      case 64: hipLaunchKernelGGL(cross_attn_merge_kernel<64>, dim3(mgrid), dim3(64), 0, s, a); break;
+      case 128: hipLaunchKernelGGL(cross_attn_merge_kernel<128>, dim3(mgrid), dim3(64), 0, s, a); break;
+      default: hipLaunchKernelGGL(cross_attn_merge_kernel<256>, dim3(mgrid), dim3(64), 0, s, a); break;
+    }
+  }
   return launch_result("cross_attn");
 }
