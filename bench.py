@@ -50,7 +50,24 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=2024)
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB mebibytes (reference for HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain copy of known size: reads and writes mib MiB once per launch.
+    Its FETCH_SIZE/WRITE_SIZE counter readings scale the counters of the
+    hot-path kernels to bytes."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
 def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s):
@@ -103,6 +120,9 @@ def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
               "(the hot path runs on a single MI355X).", file=sys.stderr)

@@ -23,7 +23,7 @@
 //     would need an agent-scope release (an L2 write-back) per workgroup,
 //     and those serialise per XCD.
 //   * Each K^/V^ row is read once and used for all G query heads of its KV
-//     group (GQA); the G queries stay in registers.
+//     group (GQA); the G queries are staged in LDS.
 //   * A row of head_dim elements is split into 16-byte chunks; LPR lanes cover
 //     one row with CPL chunks each, so one wavefront load instruction reads
 //     64/LPR rows, coalesced within each cache block.  The next iteration's
@@ -121,6 +121,11 @@ __device__ __forceinline__ float chunk_elem(const uint4& c, int e) {
   }
 }
 
+// 2^x with the hardware instruction (no denormal range reduction): the
+// softmax terms here are 2^(s - m) with s - m <= 8, and terms below 2^-126
+// flushed to zero change no output bit that matters next to the max term.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // v + (v of another lane chosen by a DPP control word), in every lane.
 template <int kCtrl>
 __device__ __forceinline__ float dpp_add(float v) {
@@ -206,6 +211,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
   constexpr int kElemBytes = kBf16 ? 2 : 4;
 
   __shared__ int32_t s_blocks[kMaxSliceBlocks];
+  __shared__ uint4 s_q[G * D * kElemBytes / 16];
   __shared__ float s_acc[kWaves][G][D];
   __shared__ float s_ml[kWaves][G][2];
 
@@ -218,8 +224,13 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
   const uint32_t total = static_cast<uint32_t>(a.num_seqs) * a.num_kv_heads * a.num_parts;
   uint32_t item = blockIdx.x;
   if (a.flags & YOCO_FLAG_REVERSE_ORDER) item = total - 1u - item;
-  const int part = static_cast<int>(item % a.num_parts);
-  const uint32_t rg = item / a.num_parts;
+  // (request, KV head) varies fastest: the hardware deals consecutive
+  // workgroups to the eight XCDs in turn, so every XCD gets an even share of
+  // the partitions that hold tokens, and the empty tail partitions of short
+  // requests come last.
+  const uint32_t pairs = static_cast<uint32_t>(a.num_seqs) * a.num_kv_heads;
+  const int part = static_cast<int>(item / pairs);
+  const uint32_t rg = item % pairs;
   const int g = static_cast<int>(rg % a.num_kv_heads);
   const int r = static_cast<int>(rg / a.num_kv_heads);
 
@@ -249,15 +260,12 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     }
   }
 
-  // Queries of the G heads of this group, the chunks this lane owns.
-  uint4 qr[G][kCpl];
+  // Queries of the G heads of this group, staged in LDS: each lane reads the
+  // chunks it owns when it needs them (keeps G*CPL*4 registers free).
   {
-    const char* qb = static_cast<const char*>(a.q) + (static_cast<int64_t>(r) * a.num_q_heads + hq0) * D * kElemBytes;
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < kCpl; ++i)
-        qr[h][i] = *reinterpret_cast<const uint4*>(qb + (h * D + (cl + kLpr * i) * kEpc) * kElemBytes);
+    const uint4* qg = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
+                                                     (static_cast<int64_t>(r) * a.num_q_heads + hq0) * D * kElemBytes);
+    for (int i = tid; i < G * D * kElemBytes / 16; i += kThreads) s_q[i] = qg[i];
   }
 
   float acc[G][kCpl][kEpc];
@@ -278,26 +286,25 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
   const int off_mask = a.block_size - 1;
   const int num_iters = (end - start + kIterTokens - 1) / kIterTokens;
 
+  // Loads are unconditional (no branch around them, so the next iteration's
+  // loads stay in flight while the current rows are used).  A row past the
+  // end of the partition, or in an out-of-range block, reads the first row of
+  // the partition (or block 0) instead and is masked out of the softmax.
   auto load = [&](RowSet<kBf16, D>& rs, int it) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int j = start + it * kIterTokens + u * kRpw + row;
-      int blk = -1;
-      if (j < end) blk = s_blocks[(j >> a.bs_shift) - first_blk];
-      const bool ok = blk >= 0;
-      rs.valid[u] = ok;
-      const int64_t off = (static_cast<int64_t>(ok ? blk : 0) * a.block_stride +
-                           static_cast<int64_t>(j & off_mask) * D) * kElemBytes;
+      const bool in_range = j < end;
+      const int jj = in_range ? j : start;
+      const int blk = s_blocks[(jj >> a.bs_shift) - first_blk];
+      rs.valid[u] = in_range && blk >= 0;
+      const int64_t off = (static_cast<int64_t>(blk >= 0 ? blk : 0) * a.block_stride +
+                           static_cast<int64_t>(jj & off_mask) * D) * kElemBytes;
 #pragma unroll
       for (int i = 0; i < kCpl; ++i) {
         const int64_t c = off + static_cast<int64_t>((cl + kLpr * i) * kEpc) * kElemBytes;
-        if (ok) {
-          rs.k[u][i] = *reinterpret_cast<const uint4*>(kb + c);
-          rs.v[u][i] = *reinterpret_cast<const uint4*>(vb + c);
-        } else {
-          rs.k[u][i] = make_uint4(0u, 0u, 0u, 0u);
-          rs.v[u][i] = make_uint4(0u, 0u, 0u, 0u);
-        }
+        rs.k[u][i] = *reinterpret_cast<const uint4*>(kb + c);
+        rs.v[u][i] = *reinterpret_cast<const uint4*>(vb + c);
       }
     }
   };
@@ -305,15 +312,19 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
   auto compute = [&](const RowSet<kBf16, D>& rs) {
     float s[kU][G];
 #pragma unroll
-    for (int u = 0; u < kU; ++u)
+    for (int h = 0; h < G; ++h) {
+      uint4 qh[kCpl];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+      for (int i = 0; i < kCpl; ++i) qh[i] = s_q[(h * D + (cl + kLpr * i) * kEpc) * kElemBytes / 16];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
         float t = 0.0f;
 #pragma unroll
-        for (int i = 0; i < kCpl; ++i) t = chunk_dot<kBf16>(qr[h][i], rs.k[u][i], t);
+        for (int i = 0; i < kCpl; ++i) t = chunk_dot<kBf16>(qh[i], rs.k[u][i], t);
         t = group_sum<kLpr>(t);
         s[u][h] = rs.valid[u] ? t * a.scale_log2 : -INFINITY;
       }
+    }
     // Lazy running maximum per row group and head.
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -321,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int u = 1; u < kU; ++u) cand = fmaxf(cand, s[u][h]);
       if (cand > m[h] + kLazyMaxSlack) {
-        const float corr = exp2f(m[h] - cand);
+        const float corr = fast_exp2(m[h] - cand);
         lsum[h] *= corr;
 #pragma unroll
         for (int i = 0; i < kCpl; ++i)
@@ -335,7 +346,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
       float p[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        p[h] = exp2f(s[u][h] - m[h]);
+        p[h] = fast_exp2(s[u][h] - m[h]);
         lsum[h] += p[h];
       }
 #pragma unroll
@@ -350,21 +361,22 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
   };
 
   // Wavefront w takes iterations w, w+4, ...; the next one's rows are in
-  // flight while the current ones are used.
+  // flight while the current ones are used.  The prefetch is issued even past
+  // the last iteration (all rows then masked) so the loop body has no branch
+  // around a load and the compiler's wait counts keep the prefetch in flight.
   {
     RowSet<kBf16, D> buf_a, buf_b;
-    int it = wave;
-    if (it < num_iters) load(buf_a, it);
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    int it = wave_u;
+    load(buf_a, it);
     while (it < num_iters) {
-      int nx = it + kWaves;
-      if (nx < num_iters) load(buf_b, nx);
+      load(buf_b, it + kWaves);
       compute(buf_a);
-      it = nx;
+      it += kWaves;
       if (it >= num_iters) break;
-      nx = it + kWaves;
-      if (nx < num_iters) load(buf_a, nx);
+      load(buf_a, it + kWaves);
       compute(buf_b);
-      it = nx;
+      it += kWaves;
     }
   }
 
