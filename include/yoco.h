@@ -137,10 +137,12 @@ int32_t yoco_gather_last(const void* hidden, int64_t num_tokens, int64_t row_byt
  *   workspace    device scratch of at least yoco_kv_append_workspace_size()
  *                bytes (bf16 only; may be NULL when that size is 0).
  *
- * bf16 arithmetic: rms_weight is folded into the weights (rounded to bf16),
- * products accumulate in fp32 on the matrix cores, the RMS scale is applied
- * in fp32 and the result is rounded to bf16 (nearest-even).  fp32: plain
- * fp32 throughout.
+ * bf16 arithmetic: rms_weight multiplies either the weights (many tokens:
+ * folded once into the workspace) or the activations (num_tokens <= 64 and
+ * hidden a multiple of 128: the workspace is not touched); that product is
+ * rounded to bf16 once.  Products accumulate in fp32 on the matrix cores,
+ * the RMS scale is applied in fp32 and the result is rounded to bf16
+ * (nearest-even).  fp32: plain fp32 throughout.
  *
  * Supported: hidden a positive multiple of 64; head_dim in {64, 128, 256};
  * block_size a power of two in [1, 256].

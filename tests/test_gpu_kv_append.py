@@ -11,6 +11,7 @@ import torch
 import oracle
 from tests.gpu_helpers import DeviceWorkload, append_tolerance, bf16_rne, host, say
 from yoco_shared_kv_gather_amd import binding as yb
+from yoco_shared_kv_gather_amd import synth
 
 pytestmark = pytest.mark.gpu
 EPS = 1e-6
@@ -53,8 +54,8 @@ def _untouched_equal(w, k_before, v_before):
 
 
 @pytest.mark.parametrize("cid,size,rms", [(1, "full", "ones"), (1, "full", "random"), (2, "small", "ones"),
-                                          (3, "small", "ones"), (4, "small", "ones"), (4, "small", "random"),
-                                          (5, "small", "ones")])
+                                          (2, "small", "random"), (2, "full", "random"), (3, "small", "ones"),
+                                          (4, "small", "ones"), (4, "small", "random"), (5, "small", "ones")])
 def test_append_parity(cid, size, rms):
     say(f"kv_append parity: workload {cid} {size} rms weight {rms}")
     w = DeviceWorkload(cid, size, layers=1, with_append=True, rms_weight=rms)
@@ -92,3 +93,27 @@ def test_append_twice_is_idempotent():
     yb.kv_append(w.x, w.w_rms, EPS, w.w_k, w.w_v, w.slot_mapping, w.k, w.v)
     torch.cuda.synchronize()
     assert torch.equal(k1.view(torch.int16), w.k.view(torch.int16))
+
+
+@pytest.mark.parametrize("num_tokens", [1, 16, 17, 33, 64, 65, 300])
+def test_append_token_counts_both_paths(num_tokens):
+    """Token counts on both sides of the 64-token switch between the decode
+    (skinny) and prefill (tiled GEMM) bf16 paths, with partial 16-row tiles,
+    a padding row and a random RMS weight."""
+    say(f"kv_append: {num_tokens} tokens, hidden 3072 -> 8 x 128")
+    w = DeviceWorkload(3, "small", layers=1, with_append=True, rms_weight="random")
+    meta = w.meta
+    rng = np.random.default_rng(num_tokens)
+    live = np.flatnonzero(synth.live_slot_mask(meta).reshape(-1))
+    slots = rng.choice(live, size=num_tokens, replace=False).astype(np.int32)
+    if num_tokens > 2:
+        slots[num_tokens // 2] = -1                         # a graph-padding row
+    meta.slot_mapping = slots
+    meta.num_tokens = num_tokens
+    w.slot_mapping = torch.from_numpy(slots).to(w.k.device)
+    w.x = torch.randn(num_tokens, meta.geom.hidden, device=w.k.device).to(torch.bfloat16)
+    k0, v0 = w.k.clone(), w.v.clone()
+    yb.kv_append(w.x, w.w_rms, EPS, w.w_k, w.w_v, w.slot_mapping, w.k, w.v)
+    torch.cuda.synchronize()
+    _untouched_equal(w, k0, v0)
+    _check_rows(w, k0, v0, np.arange(num_tokens), "bf16")

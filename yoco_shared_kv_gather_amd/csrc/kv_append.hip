@@ -9,14 +9,18 @@
 // and the row scale rsqrt(...) commutes with the projection:
 //     K^_t = rsqrt(mean(x_t^2) + eps) * (W_K diag(w_rms)) x_t.
 //
-// bf16 path (matrix cores):
-//   1. fold: W' = bf16(W diag(w_rms)) for [W_K; W_V] (one pass over the
-//      weights into the workspace);
-//   2. one MFMA GEMM  C[T][2*Hkv*D] = x[T][H] W'^T  with
-//      v_mfma_f32_16x16x32_bf16 (fp32 accumulation); the same pass sums x^2
-//      per row from the staged A tiles, and the epilogue multiplies by the
-//      row's rsqrt, rounds to bf16 (nearest even) and scatters each
-//      [Hkv][D] row to its slot.
+// bf16 path (matrix cores), two shapes:
+//   * many tokens (prefill): fold W' = bf16(W diag(w_rms)) for [W_K; W_V]
+//     once into the workspace, then one MFMA GEMM C[T][2*Hkv*D] = x W'^T
+//     with v_mfma_f32_16x16x32_bf16 (fp32 accumulation) in 128x128 tiles;
+//     the same pass sums x^2 per row from the staged A tiles, and the
+//     epilogue multiplies by the row's rsqrt, rounds to bf16 (nearest even)
+//     and scatters each [Hkv][D] row to its slot.
+//   * few tokens (decode, T <= 64): reading the weights is the whole cost,
+//     so every workgroup takes 16 output features for all tokens and its four
+//     wavefronts split the hidden dimension; the RMS weight multiplies the
+//     few activation rows instead (one bf16 rounding of x*w, as the fold
+//     rounds W*w once), and no fold pass or workspace is used.
 // fp32 path: one workgroup per token, fp32 throughout.
 
 #include <cmath>
@@ -257,6 +261,120 @@ __global__ __launch_bounds__(kF32Threads) void kv_append_f32_kernel(
   }
 }
 
+// ---- bf16 skinny path: T <= 64 -------------------------------------------------
+
+constexpr int kSkinnyCols = 16;   // output features per workgroup
+
+struct SkinnyArgs {
+  const uint16_t* x;          // [T][H]
+  const uint16_t* w_rms;      // [H]
+  const uint16_t* w_k;        // [Hkv*D][H]
+  const uint16_t* w_v;
+  const int32_t* slots;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int32_t num_tokens;
+  int32_t hidden;
+  int32_t out_half;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t bs_shift;
+  int32_t num_kv_heads;
+  int64_t num_slots;
+  float inv_hidden;
+  float eps;
+};
+
+// kMT tiles of 16 tokens (T <= 16*kMT).  Wavefront w covers hidden columns
+// [w*H/4, (w+1)*H/4); the four partial products and sums of squares are
+// added in LDS in wavefront order.
+template <int kMT>
+__global__ __launch_bounds__(256) void kv_append_skinny_kernel(SkinnyArgs a) {
+  __shared__ f32x4 s_acc[4][kMT][64];
+  __shared__ float s_ssq[4][kMT * 16];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n0 = blockIdx.x * kSkinnyCols;
+  const bool is_v = n0 >= a.out_half;           // out_half is a multiple of 64: no tile straddles K and V
+  const int col = n0 + (lane & 15);
+  const uint16_t* wrow = (is_v ? a.w_v : a.w_k) + static_cast<int64_t>(col - (is_v ? a.out_half : 0)) * a.hidden;
+  const int kq = a.hidden / 4;
+  const int k_begin = wave * kq;
+  const int kofs = (lane >> 4) * 8;
+
+  f32x4 acc[kMT];
+  float ssq[kMT];
+  int xrow[kMT];
+  bool xok[kMT];
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) {
+    acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    ssq[mt] = 0.0f;
+    const int row = mt * 16 + (lane & 15);
+    xok[mt] = row < a.num_tokens;
+    xrow[mt] = xok[mt] ? row : a.num_tokens - 1;     // in bounds; zeroed below when past T
+  }
+#pragma unroll 2
+  for (int k = k_begin; k < k_begin + kq; k += 32) {
+    const uint4 wb = *reinterpret_cast<const uint4*>(wrow + k + kofs);
+    const uint4 wr = *reinterpret_cast<const uint4*>(a.w_rms + k + kofs);
+    const uint32_t* wru = reinterpret_cast<const uint32_t*>(&wr);
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) {
+      uint4 xv = *reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(xrow[mt]) * a.hidden + k + kofs);
+      if (!xok[mt]) xv = make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t* xu = reinterpret_cast<const uint32_t*>(&xv);
+      uint4 av;
+      uint32_t* au = reinterpret_cast<uint32_t*>(&av);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_lo(xu[e]);
+        const float hi = bf16_hi(xu[e]);
+        ssq[mt] = fmaf(lo, lo, ssq[mt]);
+        ssq[mt] = fmaf(hi, hi, ssq[mt]);
+        au[e] = yoco::pack_bf16x2(lo * bf16_lo(wru[e]), hi * bf16_hi(wru[e]));
+      }
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                       __builtin_bit_cast(bf16x8, wb), acc[mt], 0, 0, 0);
+    }
+  }
+  // Sums of squares: lanes l, l^16, l^32, l^48 hold the same row.
+#pragma unroll
+  for (int mt = 0; mt < kMT; ++mt) {
+    float v = ssq[mt];
+    v += __shfl_xor(v, 16, 64);
+    v += __shfl_xor(v, 32, 64);
+    if (lane < 16) s_ssq[wave][mt * 16 + lane] = v;
+    s_acc[wave][mt][lane] = acc[mt];
+  }
+  __syncthreads();
+
+  // Lane l of the MFMA output holds rows 4*(l/16)+0..3 of column l%16.
+  for (int e = tid; e < kMT * 64 * 4; e += 256) {
+    const int mt = e / 256;
+    const int l = (e / 4) & 63;
+    const int i = e & 3;
+    const int row = mt * 16 + (l >> 4) * 4 + i;
+    if (row >= a.num_tokens) continue;
+    const int64_t slot = a.slots[row];
+    if (slot < 0 || slot >= a.num_slots) continue;
+    float sum = 0.0f, sq = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      sum += s_acc[w][mt][l][i];
+      sq += s_ssq[w][mt * 16 + (l >> 4) * 4 + i];
+    }
+    const float scale = 1.0f / sqrtf(sq * a.inv_hidden + a.eps);
+    const int c = n0 + (l & 15) - (is_v ? a.out_half : 0);
+    const int h = c / a.head_dim;
+    const int d = c - h * a.head_dim;
+    uint16_t* cache = is_v ? a.v_cache : a.k_cache;
+    cache[(((slot >> a.bs_shift) * a.num_kv_heads + h) * a.block_size + (slot & (a.block_size - 1))) * a.head_dim + d] =
+        f32_to_bf16_rne(sum * scale);
+  }
+}
+
 bool supported_dim(int d) { return d == 64 || d == 128 || d == 256; }
 
 }  // namespace
@@ -311,6 +429,35 @@ extern "C" int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_toke
   }
 
   const int64_t out_half = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if (num_tokens <= 64 && hidden % 128 == 0) {
+    SkinnyArgs k;
+    k.x = static_cast<const uint16_t*>(x);
+    k.w_rms = static_cast<const uint16_t*>(rms_weight);
+    k.w_k = static_cast<const uint16_t*>(w_k);
+    k.w_v = static_cast<const uint16_t*>(w_v);
+    k.slots = slot_mapping;
+    k.k_cache = static_cast<uint16_t*>(k_cache);
+    k.v_cache = static_cast<uint16_t*>(v_cache);
+    k.num_tokens = num_tokens;
+    k.hidden = hidden;
+    k.out_half = static_cast<int32_t>(out_half);
+    k.head_dim = head_dim;
+    k.block_size = block_size;
+    k.bs_shift = bs_shift;
+    k.num_kv_heads = num_kv_heads;
+    k.num_slots = num_slots;
+    k.inv_hidden = 1.0f / static_cast<float>(hidden);
+    k.eps = eps;
+    const dim3 grid(static_cast<uint32_t>(2 * out_half / kSkinnyCols));
+    if (num_tokens <= 16) {
+      hipLaunchKernelGGL(kv_append_skinny_kernel<1>, grid, dim3(256), 0, s, k);
+    } else if (num_tokens <= 32) {
+      hipLaunchKernelGGL(kv_append_skinny_kernel<2>, grid, dim3(256), 0, s, k);
+    } else {
+      hipLaunchKernelGGL(kv_append_skinny_kernel<4>, grid, dim3(256), 0, s, k);
+    }
+    return launch_result("kv_append");
+  }
   const int64_t half_chunks = out_half * hidden / 8;
   const int64_t fold_blocks = ceil_div(2 * half_chunks, 256);
   hipLaunchKernelGGL(fold_rms_weight_kernel, dim3(static_cast<uint32_t>(fold_blocks)), dim3(256), 0, s,
