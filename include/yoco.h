@@ -139,7 +139,7 @@ int32_t yoco_gather_last(const void* hidden, int64_t num_tokens, int64_t row_byt
  *
  * bf16 arithmetic: rms_weight multiplies either the weights (many tokens:
  * folded once into the workspace) or the activations (num_tokens <= 64 and
- * hidden a multiple of 128: the workspace is not touched); that product is
+ * hidden a multiple of 256: the workspace is not touched); that product is
  * rounded to bf16 once.  Products accumulate in fp32 on the matrix cores,
  * the RMS scale is applied in fp32 and the result is rounded to bf16
  * (nearest-even).  fp32: plain fp32 throughout.

@@ -161,39 +161,65 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 // Merge the partials of one (request, query head):
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
-// One wavefront: lanes stride over partitions for M and the denominator,
-// then own head_dim/64 dimensions of the numerator, which adds partitions in
-// order 0..np-1.  Requests with a single partition were finished already.
+// 256 threads: thread t owns the float4 slice (t % (D/4)) of head_dim and
+// partitions p = t / (D/4) + k * (256 / (D/4)); the per-group sums are then
+// added in group order through LDS.  Requests with one partition were
+// finished by the first kernel.
 template <int D>
-__global__ __launch_bounds__(64) void cross_attn_merge_kernel(AttnArgs a) {
-  constexpr int kDpl = D / 64;
+__global__ __launch_bounds__(kThreads) void cross_attn_merge_kernel(AttnArgs a) {
+  constexpr int kSlices = D / 4;                 // float4 slices of a head
+  constexpr int kGroups = kThreads / kSlices;    // partition groups
+  __shared__ float s_red[kWaves];
+  __shared__ float4 s_num[kGroups][kSlices];
+  __shared__ float s_den[kGroups];
   const int64_t rh = blockIdx.x;
   const int r = static_cast<int>(rh / a.num_q_heads);
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
   int n = a.seq_lens[r];
   n = n < 0 ? 0 : (n > a.len_cap ? a.len_cap : n);
   const int np = (n + a.part_tokens - 1) / a.part_tokens;
   if (np <= 1) return;
   const float* ml = a.ws_ml + rh * a.num_parts * 2;
-  const float* acc = a.ws_acc + rh * a.num_parts * D + lane;
+  const float4* acc = reinterpret_cast<const float4*>(a.ws_acc + rh * a.num_parts * D);
+
   float mx = kInitMax;
-  for (int p = lane; p < np; p += 64) mx = fmaxf(mx, ml[2 * p]);
+  for (int p = tid; p < np; p += kThreads) mx = fmaxf(mx, ml[2 * p]);
   mx = wave_max(mx);
+  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+
+  const int slice = tid % kSlices;
+  const int grp = tid / kSlices;
+  float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float den = 0.0f;
-  for (int p = lane; p < np; p += 64) den = fmaf(exp2f(ml[2 * p] - mx), ml[2 * p + 1], den);
-  den = wave_sum(den);
-  float num[kDpl];
-#pragma unroll
-  for (int i = 0; i < kDpl; ++i) num[i] = 0.0f;
-#pragma unroll 4
-  for (int p = 0; p < np; ++p) {
+  for (int p = grp; p < np; p += kGroups) {
     const float w = exp2f(ml[2 * p] - mx);
-#pragma unroll
-    for (int i = 0; i < kDpl; ++i) num[i] = fmaf(w, acc[static_cast<int64_t>(p) * D + 64 * i], num[i]);
+    den = fmaf(w, ml[2 * p + 1], den);
+    const float4 v = acc[static_cast<int64_t>(p) * kSlices + slice];
+    num.x = fmaf(w, v.x, num.x);
+    num.y = fmaf(w, v.y, num.y);
+    num.z = fmaf(w, v.z, num.z);
+    num.w = fmaf(w, v.w, num.w);
   }
-  const float inv = den > 0.0f ? 1.0f / den : 0.0f;
+  s_num[grp][slice] = num;
+  if (slice == 0) s_den[grp] = den;
+  __syncthreads();
+  if (tid < kSlices) {
+    float4 t = s_num[0][tid];
+    float dsum = s_den[0];
 #pragma unroll
-  for (int i = 0; i < kDpl; ++i) a.out[rh * D + lane + 64 * i] = num[i] * inv;
+    for (int g2 = 1; g2 < kGroups; ++g2) {
+      const float4 u = s_num[g2][tid];
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
+      dsum += s_den[g2];
+    }
+    const float inv = dsum > 0.0f ? 1.0f / dsum : 0.0f;
+    reinterpret_cast<float4*>(a.out + rh * D)[tid] = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+  }
 }
 
 template <bool kBf16, int D>
@@ -624,9 +650,9 @@ extern "C" int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seq
   if (nparts > 1) {
     const uint32_t mgrid = static_cast<uint32_t>(static_cast<int64_t>(num_seqs) * num_q_heads);
     switch (head_dim) {
-      case 64: hipLaunchKernelGGL(cross_attn_merge_kernel<64>, dim3(mgrid), dim3(64), 0, s, a); break;
-      case 128: hipLaunchKernelGGL(cross_attn_merge_kernel<128>, dim3(mgrid), dim3(64), 0, s, a); break;
-      default: hipLaunchKernelGGL(cross_attn_merge_kernel<256>, dim3(mgrid), dim3(64), 0, s, a); break;
+      case 64: hipLaunchKernelGGL(cross_attn_merge_kernel<64>, dim3(mgrid), dim3(kThreads), 0, s, a); break;
+      case 128: hipLaunchKernelGGL(cross_attn_merge_kernel<128>, dim3(mgrid), dim3(kThreads), 0, s, a); break;
+      default: hipLaunchKernelGGL(cross_attn_merge_kernel<256>, dim3(mgrid), dim3(kThreads), 0, s, a); break;
     }
   }
   return launch_result("cross_attn");

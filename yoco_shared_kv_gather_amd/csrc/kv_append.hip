@@ -17,8 +17,8 @@
 //     epilogue multiplies by the row's rsqrt, rounds to bf16 (nearest even)
 //     and scatters each [Hkv][D] row to its slot.
 //   * few tokens (decode, T <= 64): reading the weights is the whole cost,
-//     so every workgroup takes 16 output features for all tokens and its four
-//     wavefronts split the hidden dimension; the RMS weight multiplies the
+//     so every workgroup takes 16 output features for all tokens and its
+//     eight wavefronts split the hidden dimension; the RMS weight multiplies the
 //     few activation rows instead (one bf16 rounding of x*w, as the fold
 //     rounds W*w once), and no fold pass or workspace is used.
 // fp32 path: one workgroup per token, fp32 throughout.
@@ -285,13 +285,15 @@ struct SkinnyArgs {
   float eps;
 };
 
-// kMT tiles of 16 tokens (T <= 16*kMT).  Wavefront w covers hidden columns
-// [w*H/4, (w+1)*H/4); the four partial products and sums of squares are
-// added in LDS in wavefront order.
+// kMT tiles of 16 tokens (T <= 16*kMT).  Wavefront w of kSkinnyWaves covers
+// hidden columns [w*H/8, (w+1)*H/8); the partial products and sums of
+// squares are added in LDS in wavefront order.
+constexpr int kSkinnyWaves = 8;
+
 template <int kMT>
-__global__ __launch_bounds__(256) void kv_append_skinny_kernel(SkinnyArgs a) {
-  __shared__ f32x4 s_acc[4][kMT][64];
-  __shared__ float s_ssq[4][kMT * 16];
+__global__ __launch_bounds__(64 * kSkinnyWaves) void kv_append_skinny_kernel(SkinnyArgs a) {
+  __shared__ f32x4 s_acc[kSkinnyWaves][kMT][64];
+  __shared__ float s_ssq[kSkinnyWaves][kMT * 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(256) void kv_append_skinny_kernel(SkinnyArgs a) {
   const bool is_v = n0 >= a.out_half;           // out_half is a multiple of 64: no tile straddles K and V
   const int col = n0 + (lane & 15);
   const uint16_t* wrow = (is_v ? a.w_v : a.w_k) + static_cast<int64_t>(col - (is_v ? a.out_half : 0)) * a.hidden;
-  const int kq = a.hidden / 4;
+  const int kq = a.hidden / kSkinnyWaves;
   const int k_begin = wave * kq;
   const int kofs = (lane >> 4) * 8;
 
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(256) void kv_append_skinny_kernel(SkinnyArgs a) {
     xok[mt] = row < a.num_tokens;
     xrow[mt] = xok[mt] ? row : a.num_tokens - 1;     // in bounds; zeroed below when past T
   }
-#pragma unroll 2
+#pragma unroll 4
   for (int k = k_begin; k < k_begin + kq; k += 32) {
     const uint4 wb = *reinterpret_cast<const uint4*>(wrow + k + kofs);
     const uint4 wr = *reinterpret_cast<const uint4*>(a.w_rms + k + kofs);
@@ -351,7 +353,7 @@ __global__ __launch_bounds__(256) void kv_append_skinny_kernel(SkinnyArgs a) {
   __syncthreads();
 
   // Lane l of the MFMA output holds rows 4*(l/16)+0..3 of column l%16.
-  for (int e = tid; e < kMT * 64 * 4; e += 256) {
+  for (int e = tid; e < kMT * 64 * 4; e += 64 * kSkinnyWaves) {
     const int mt = e / 256;
     const int l = (e / 4) & 63;
     const int i = e & 3;
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(256) void kv_append_skinny_kernel(SkinnyArgs a) {
     if (slot < 0 || slot >= a.num_slots) continue;
     float sum = 0.0f, sq = 0.0f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kSkinnyWaves; ++w) {
       sum += s_acc[w][mt][l][i];
       sq += s_ssq[w][mt * 16 + (l >> 4) * 4 + i];
     }
@@ -429,7 +431,7 @@ extern "C" int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_toke
   }
 
   const int64_t out_half = static_cast<int64_t>(num_kv_heads) * head_dim;
-  if (num_tokens <= 64 && hidden % 128 == 0) {
+  if (num_tokens <= 64 && hidden % (32 * kSkinnyWaves) == 0) {
     SkinnyArgs k;
     k.x = static_cast<const uint16_t*>(x);
     k.w_rms = static_cast<const uint16_t*>(rms_weight);
@@ -449,12 +451,13 @@ extern "C" int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_toke
     k.inv_hidden = 1.0f / static_cast<float>(hidden);
     k.eps = eps;
     const dim3 grid(static_cast<uint32_t>(2 * out_half / kSkinnyCols));
+    const dim3 block(64 * kSkinnyWaves);
     if (num_tokens <= 16) {
-      hipLaunchKernelGGL(kv_append_skinny_kernel<1>, grid, dim3(256), 0, s, k);
+      hipLaunchKernelGGL(kv_append_skinny_kernel<1>, grid, block, 0, s, k);
     } else if (num_tokens <= 32) {
-      hipLaunchKernelGGL(kv_append_skinny_kernel<2>, grid, dim3(256), 0, s, k);
+      hipLaunchKernelGGL(kv_append_skinny_kernel<2>, grid, block, 0, s, k);
     } else {
-      hipLaunchKernelGGL(kv_append_skinny_kernel<4>, grid, dim3(256), 0, s, k);
+      hipLaunchKernelGGL(kv_append_skinny_kernel<4>, grid, block, 0, s, k);
     }
     return launch_result("kv_append");
   }

@@ -1,0 +1,164 @@
+"""Turn rocprofv3 output of bench.py into a short text summary.
+
+The summary is what profiles/*.md hold: per-kernel average durations from a
+kernel trace, and HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE counter
+passes, each scaled by what the same counter reads for a plain device copy of
+known size (bench.py --copy-calibration).  It also records a hash of the HIP
+sources, so bench.py can tell whether the measured traffic still describes the
+kernels it runs.
+
+Expected layout of the rocprofv3 output directory (one `-d` per pass, `-o run`
+and `-f csv`):
+    trace/       --kernel-trace --stats           (bench.py)
+    fetch/       --pmc FETCH_SIZE                 (bench.py)
+    write/       --pmc WRITE_SIZE                 (bench.py)
+    copy_fetch/  --pmc FETCH_SIZE                 (bench.py --copy-calibration MIB)
+    copy_write/  --pmc WRITE_SIZE                 (bench.py --copy-calibration MIB)
+plus copy_fetch.json, the calibration run's stdout.
+
+Usage: python -m yoco_shared_kv_gather_amd.profiling OUTDIR --workload NAME --command "..." > profiles/X.md
+"""
+
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import statistics
+from typing import Dict, List, Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG_DIR, "csrc")
+ROOT = os.path.dirname(PKG_DIR)
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_hash() -> str:
+    """sha256 over the HIP sources and the public header, in name order."""
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(ROOT, "include", "yoco.h")]
+    for path in files:
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def short_name(name: str) -> str:
+    name = name.replace("(anonymous namespace)::", "")
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for i, c in enumerate(name):
+        if c == "<":
+            depth += 1
+        elif c == ">":
+            depth -= 1
+        elif c == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def _counters(path: str) -> Dict[str, List[float]]:
+    d: Dict[str, List[float]] = collections.defaultdict(list)
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            d[row["Kernel_Name"]].append(float(row["Counter_Value"]))
+    return d
+
+
+def _calibration(out: str, sub: str) -> float:
+    """Bytes per counter unit, from the plain copy of known size."""
+    copy_bytes = json.load(open(os.path.join(out, "copy_fetch.json")))["copy_calibration_bytes"]
+    counts = _counters(os.path.join(out, sub, "run_counter_collection.csv"))
+    # the copy is the kernel with the largest reading in the calibration run
+    best = max(statistics.median(v) for v in counts.values())
+    return copy_bytes / best
+
+
+def summarize(out: str, workload: str, command: str, top: int = 10) -> str:
+    stats = list(csv.DictReader(open(os.path.join(out, "trace", "run_kernel_stats.csv"))))
+    fetch = _counters(os.path.join(out, "fetch", "run_counter_collection.csv"))
+    write = _counters(os.path.join(out, "write", "run_counter_collection.csv"))
+    f_scale = _calibration(out, "copy_fetch")
+    w_scale = _calibration(out, "copy_write")
+    bench = json.load(open(os.path.join(out, "trace_bench.json")))
+    lines = [
+        f"# rocprofv3 summary: {workload}",
+        "",
+        f"source_hash: {source_hash()}",
+        f"workload: {workload}",
+        f"counter_scale_fetch_bytes_per_unit: {f_scale:.4f}",
+        f"counter_scale_write_bytes_per_unit: {w_scale:.4f}",
+        "",
+        "Commands (run from the repository root on the GPU machine):",
+        "",
+        "```",
+        command.strip(),
+        "```",
+        "",
+        f"bench.py line of the traced run: ms_per_step {bench['ms_per_step']}, value {bench['value']} {bench['unit']}, "
+        f"roofline achieved {bench['roofline']['achieved']} GB/s (event-timed)",
+        "",
+        "| kernel | calls | avg us | HBM read MB/dispatch | HBM write MB/dispatch |",
+        "|---|---:|---:|---:|---:|",
+    ]
+    records = {}
+    ours = [row for row in stats if not short_name(row["Name"]).startswith(("at::", "__amd", "c10::"))]
+    lines.insert(len(lines) - 3, "Kernels of this library only (input generation and cache flushing omitted).")
+    lines.insert(len(lines) - 3, "")
+    for row in ours[:top]:
+        name = row["Name"]
+        fr = statistics.mean(fetch[name]) * f_scale if name in fetch else None
+        wr = statistics.mean(write[name]) * w_scale if name in write else None
+        avg_us = float(row["AverageNs"]) / 1e3
+        records[short_name(name)] = (avg_us, fr, wr)
+        lines.append(f"| {short_name(name)} | {row['Calls']} | {avg_us:.2f} | "
+                     f"{'' if fr is None else f'{fr / 1e6:.2f}'} | {'' if wr is None else f'{wr / 1e6:.2f}'} |")
+    lines.append("")
+    for name, (avg_us, fr, wr) in records.items():
+        if fr is not None and wr is not None:
+            lines.append(f"kernel_bytes: {name} | {avg_us:.3f} | {fr:.0f} | {wr:.0f}")
+    return "\n".join(lines) + "\n"
+
+
+def measured_traffic(workload: str, kernels: List[str]) -> Optional[dict]:
+    """HBM bytes per dispatch summed over `kernels`, from the committed profile
+    of `workload` -- or None if there is none or the sources changed since."""
+    path = os.path.join(PROFILES, f"cross_attn_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"^source_hash: (\S+)", text, re.M)
+    if not m or m.group(1) != source_hash():
+        return None
+    total_r = total_w = 0.0
+    found = 0
+    for line in text.splitlines():
+        if line.startswith("kernel_bytes: "):
+            name, _us, r, w = [f.strip() for f in line[len("kernel_bytes: "):].split("|")]
+            if name in kernels:
+                total_r += float(r)
+                total_w += float(w)
+                found += 1
+    if found != len(kernels):
+        return None
+    return {"read_bytes": total_r, "write_bytes": total_w, "profile": os.path.relpath(path, ROOT)}
+
+
+def main():
+    p = argparse.ArgumentParser(description="summarize rocprofv3 output of bench.py")
+    p.add_argument("out")
+    p.add_argument("--workload", required=True)
+    p.add_argument("--command", required=True, help="the commands that produced OUT (recorded in the summary)")
+    args = p.parse_args()
+    print(summarize(args.out, args.workload, args.command), end="")
+
+
+if __name__ == "__main__":
+    main()
