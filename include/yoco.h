@@ -172,14 +172,16 @@ int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_tokens, int32_t
  * g = h / (num_q_heads / num_kv_heads)):
  *     out[r][h] = sum_j softmax_j(scale * q[r][h] . K^[r][j][g]) V^[r][j][g],
  *     j = 0 .. n-1 (the current token's own K^/V^ included).
- * n == 0 gives a zero row.
+ * n == 0 gives a zero row.  A NaN in a context row gives NaN outputs.
  *
  *   dtype        type of q and the cache.
  *   q            [num_seqs][num_q_heads][head_dim].
  *   k_cache, v_cache  the shared cache (layout above), read only.
  *   block_table  int32 [num_seqs][max_blocks_per_seq].  Precondition:
- *                entries used by a context lie in [0, num_blocks) (tokens in
- *                out-of-range blocks are skipped).
+ *                entries used by a context lie in [0, num_blocks).  An entry
+ *                outside that range is never dereferenced and its tokens are
+ *                left out of the softmax; if it is the first block of a
+ *                split-KV partition the request's output is unspecified.
  *   seq_lens     int32 [num_seqs]; values are clamped to
  *                [0, min(max_seq_len, max_blocks_per_seq*block_size)].
  *   max_seq_len  an upper bound of seq_lens; sizes the split into partitions.

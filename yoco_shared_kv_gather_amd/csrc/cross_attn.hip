@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_merge_kernel(AttnArgs a) 
       t.w += u.w;
       dsum += s_den[g2];
     }
-    const float inv = dsum > 0.0f ? 1.0f / dsum : 0.0f;
+    const float inv = dsum == 0.0f ? 0.0f : 1.0f / dsum;
     reinterpret_cast<float4*>(a.out + rh * D)[tid] = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
   }
 }
@@ -314,18 +314,22 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
 
   // Loads are unconditional (no branch around them, so the next iteration's
   // loads stay in flight while the current rows are used).  A row past the
-  // end of the partition, or in an out-of-range block, reads the first row of
-  // the partition (or block 0) instead and is masked out of the softmax.
+  // end of the partition, or in an out-of-range block, reads the partition's
+  // first row instead and is masked out of the softmax (its p is 0 and the
+  // row it reads is a context row; block 0 if even that block is invalid).
+  const int64_t dummy_off =
+      (static_cast<int64_t>(s_blocks[0] >= 0 ? s_blocks[0] : 0) * a.block_stride +
+       static_cast<int64_t>(start & off_mask) * D) * kElemBytes;
   auto load = [&](RowSet<kBf16, D>& rs, int it) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int j = start + it * kIterTokens + u * kRpw + row;
       const bool in_range = j < end;
-      const int jj = in_range ? j : start;
-      const int blk = s_blocks[(jj >> a.bs_shift) - first_blk];
+      const int blk = s_blocks[((in_range ? j : start) >> a.bs_shift) - first_blk];
       rs.valid[u] = in_range && blk >= 0;
-      const int64_t off = (static_cast<int64_t>(blk >= 0 ? blk : 0) * a.block_stride +
-                           static_cast<int64_t>(jj & off_mask) * D) * kElemBytes;
+      const int64_t off = rs.valid[u] ? (static_cast<int64_t>(blk) * a.block_stride +
+                                         static_cast<int64_t>(j & off_mask) * D) * kElemBytes
+                                      : dummy_off;
 #pragma unroll
       for (int i = 0; i < kCpl; ++i) {
         const int64_t c = off + static_cast<int64_t>((cl + kLpr * i) * kEpc) * kElemBytes;
@@ -459,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     }
     const int64_t rh = static_cast<int64_t>(r) * a.num_q_heads + hq0 + h;
     if (np_r == 1) {
-      a.out[rh * D + d] = den > 0.0f ? num / den : 0.0f;
+      a.out[rh * D + d] = den == 0.0f ? 0.0f : num / den;
     } else {
       const int64_t slot = rh * a.num_parts + part;
       a.ws_acc[slot * D + d] = num;

@@ -104,6 +104,12 @@ def _seed_seq(config_id: int, size: str, seed: int) -> np.random.SeedSequence:
     return np.random.SeedSequence([seed, config_id, size_tag])
 
 
+def custom_geometry(dtype: str, num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                    hidden: int = 256, num_layers: int = 1) -> Geometry:
+    return Geometry(f"custom_{dtype}_{num_q_heads}x{num_kv_heads}x{head_dim}_bs{block_size}", dtype, num_q_heads,
+                    num_kv_heads, head_dim, block_size, num_layers, hidden)
+
+
 def _child_seed(ss: np.random.SeedSequence, index: int) -> int:
     """A 63-bit integer seed for child stream ``index`` of ``ss``."""
     child = np.random.SeedSequence(entropy=ss.entropy, spawn_key=ss.spawn_key + (index,))
@@ -196,6 +202,37 @@ def make_metadata(config_id: int, size: str = "full", seed: int = SEED_BASE) -> 
     if config_id == 3:
         meta.outlier_prob, meta.outlier_scale = 0.001, 20.0
     return meta
+
+
+def make_custom_metadata(geom: Geometry, seq_lens, seed: int = SEED_BASE, spare_table_entries: int = 1,
+                         tag: int = 99) -> Metadata:
+    """A decode batch of any head geometry: one scheduled token per request
+    (none for an empty context), blocks handed out in seeded random order
+    from a pool ~1.25x the need, NaN-poisoned spare blocks."""
+    ss = np.random.SeedSequence([seed, tag, len(seq_lens)])
+    bs = geom.block_size
+    seq = np.asarray(seq_lens, dtype=np.int32)
+    qlens = (seq > 0).astype(np.int32)
+    need = [(-(-int(c) // bs)) for c in seq]
+    total = int(sum(need))
+    num_blocks = int(math.ceil(1.25 * total)) + 1
+    perm = _rng(ss, _S_PERM).permutation(num_blocks).astype(np.int32)
+    poison = int(perm[total])
+    table = np.full((len(seq), max(1, max(need) + spare_table_entries)), poison, dtype=np.int32)
+    cursor = 0
+    for r, nb in enumerate(need):
+        table[r, :nb] = perm[cursor:cursor + nb]
+        cursor += nb
+    cu = np.zeros(len(seq) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(qlens)
+    slots = np.full(int(cu[-1]), -1, dtype=np.int32)
+    for r in range(len(seq)):
+        if qlens[r]:
+            pos = int(seq[r]) - 1
+            slots[cu[r]] = table[r, pos // bs] * bs + pos % bs
+    return Metadata(config_id=tag, size="small", geom=geom, seq_lens=seq, query_lens=qlens, cu_seqlens=cu,
+                    num_tokens=int(cu[-1]), slot_mapping=slots, block_table=table, num_blocks=num_blocks,
+                    poison_block=poison)
 
 
 def live_slot_mask(meta: Metadata) -> np.ndarray:
