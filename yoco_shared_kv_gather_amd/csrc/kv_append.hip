@@ -12,7 +12,7 @@
 // bf16 path (matrix cores), two shapes:
 //   * many tokens (prefill): fold W' = bf16(W diag(w_rms)) for [W_K; W_V]
 //     once into the workspace, then one MFMA GEMM C[T][2*Hkv*D] = x W'^T
-//     with v_mfma_f32_16x16x32_bf16 (fp32 accumulation) in 128x128 tiles;
+//     with v_mfma_f32_16x16x32_bf16 (fp32 accumulation) in 128x256 tiles;
 //     the same pass sums x^2 per row from the staged A tiles, and the
 //     epilogue multiplies by the row's rsqrt, rounds to bf16 (nearest even)
 //     and scatters each [Hkv][D] row to its slot.
@@ -59,10 +59,12 @@ __global__ __launch_bounds__(256) void fold_rms_weight_kernel(const uint4* __res
 
 // ---- bf16 MFMA GEMM with RMS row scale and slot scatter ------------------------
 
-constexpr int kBM = 128;
-constexpr int kBN = 128;
+constexpr int kBM = 128;                     // tokens per workgroup tile
+constexpr int kBN = 256;                     // output features per workgroup tile
 constexpr int kBK = 64;
-constexpr int kLdsStride = kBK + 8;          // bf16 elements per staged row (16-byte pad)
+constexpr int kLdsStride = kBK + 8;          // bf16 elements per staged row (16-byte pad: conflict-free reads)
+constexpr int kStage = (kBM + kBN) * kLdsStride;
+constexpr int kOutStride = kBN + 8;          // bf16 elements per row of the staged output tile
 constexpr int kGemmThreads = 256;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -81,48 +83,62 @@ struct AppendArgs {
   int32_t block_size;
   int32_t bs_shift;
   int32_t num_kv_heads;
+  int32_t n_tiles;            // ceil(2 * out_half / kBN)
   int64_t num_slots;          // num_blocks * block_size
   float inv_hidden;
   float eps;
 };
 
+// One workgroup: 128 tokens x 256 output features, four wavefronts of 64 x 128
+// (4 x 8 MFMA tiles of 16x16, K step 32).  Workgroup id -> (token tile =
+// id / n_tiles, feature tile = id % n_tiles): consecutive workgroups go to
+// different XCDs, so each XCD keeps re-reading the same weight panels from its
+// own L2 while the XCDs share each activation tile through the last-level
+// cache.  Global -> registers -> LDS staging, two LDS stages, one barrier per
+// K step.  The epilogue scales by the row's rsqrt, rounds to bf16 into LDS and
+// writes each token's features as 16-byte chunks to its slot.
 __global__ __launch_bounds__(kGemmThreads) void kv_append_mfma_kernel(AppendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t as[2][kBM * kLdsStride];
-  __shared__ __attribute__((aligned(16))) uint16_t bs[2][kBN * kLdsStride];
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
   __shared__ float row_scale[kBM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;            // wave row (0..1): 64 rows each
-  const int wn = wave & 1;             // wave column (0..1): 64 columns each
-  const int n0 = blockIdx.x * kBN;
-  const int m0 = blockIdx.y * kBM;
+  const int wm = wave >> 1;            // 64-row half of the tile
+  const int wn = wave & 1;             // 128-column half of the tile
+  const int m0 = static_cast<int>(blockIdx.x / a.n_tiles) * kBM;
+  const int n0 = static_cast<int>(blockIdx.x % a.n_tiles) * kBN;
+  const int n_total = 2 * a.out_half;
 
-  // Staging map: thread loads chunk kc (8 bf16) of rows rbase + 32 i.
+  // Staging map: thread moves chunk kc (8 bf16) of A rows rbase+32i (i<4)
+  // and of B rows rbase+32i (i<8).
   const int kc = tid & 7;
   const int rbase = tid >> 3;
-  uint4 ra[4], rb[4];
+  uint4 ra[4], rb[8];
   float sumsq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 
   auto load_tile = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int rowm = m0 + rbase + 32 * i;
-      if (rowm < a.num_tokens) {
-        ra[i] = *reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(rowm) * a.hidden + k0 + kc * 8);
-      } else {
-        ra[i] = make_uint4(0u, 0u, 0u, 0u);
-      }
-      rb[i] = *reinterpret_cast<const uint4*>(a.w + static_cast<int64_t>(n0 + rbase + 32 * i) * a.hidden + k0 + kc * 8);
+      const int row = m0 + rbase + 32 * i;
+      ra[i] = row < a.num_tokens
+                  ? *reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(row) * a.hidden + k0 + kc * 8)
+                  : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int col = n0 + rbase + 32 * i;
+      rb[i] = col < n_total
+                  ? *reinterpret_cast<const uint4*>(a.w + static_cast<int64_t>(col) * a.hidden + k0 + kc * 8)
+                  : make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int stage) {
+    uint16_t* as = lds + stage * kStage;
+    uint16_t* bs = as + kBM * kLdsStride;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = rbase + 32 * i;
-      *reinterpret_cast<uint4*>(&as[buf][r * kLdsStride + kc * 8]) = ra[i];
-      *reinterpret_cast<uint4*>(&bs[buf][r * kLdsStride + kc * 8]) = rb[i];
+      *reinterpret_cast<uint4*>(&as[(rbase + 32 * i) * kLdsStride + kc * 8]) = ra[i];
       const uint32_t* u = reinterpret_cast<const uint32_t*>(&ra[i]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -132,13 +148,15 @@ __global__ __launch_bounds__(kGemmThreads) void kv_append_mfma_kernel(AppendArgs
         sumsq[i] = fmaf(hi, hi, sumsq[i]);
       }
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&bs[(rbase + 32 * i) * kLdsStride + kc * 8]) = rb[i];
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int ktiles = a.hidden / kBK;
   load_tile(0);
@@ -150,18 +168,21 @@ __global__ __launch_bounds__(kGemmThreads) void kv_append_mfma_kernel(AppendArgs
   for (int kt = 0; kt < ktiles; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < ktiles) load_tile((kt + 1) * kBK);
+    const uint16_t* as = lds + cur * kStage;
+    const uint16_t* bs = as + kBM * kLdsStride;
 #pragma unroll
     for (int ks = 0; ks < kBK; ks += 32) {
-      bf16x8 af[4], bf[4];
+      bf16x8 af[4], bf[8];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        af[t] = *reinterpret_cast<const bf16x8*>(&as[cur][(wm * 64 + t * 16 + frag_row) * kLdsStride + ks + frag_k]);
-        bf[t] = *reinterpret_cast<const bf16x8*>(&bs[cur][(wn * 64 + t * 16 + frag_row) * kLdsStride + ks + frag_k]);
-      }
+      for (int t = 0; t < 4; ++t)
+        af[t] = *reinterpret_cast<const bf16x8*>(&as[(wm * 64 + t * 16 + frag_row) * kLdsStride + ks + frag_k]);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+        bf[t] = *reinterpret_cast<const bf16x8*>(&bs[(wn * 128 + t * 16 + frag_row) * kLdsStride + ks + frag_k]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
     if (kt + 1 < ktiles) store_tile(cur ^ 1);
     __syncthreads();
@@ -178,31 +199,40 @@ __global__ __launch_bounds__(kGemmThreads) void kv_append_mfma_kernel(AppendArgs
   }
   __syncthreads();
 
-  // Epilogue: scale, round, scatter.  Lane holds rows 4*(lane/16)+0..3 of
-  // column lane%16 of each 16x16 tile.
+  // Scaled, rounded tile into LDS (the staging buffers are free now).  Lane
+  // holds rows 4*(lane/16)+0..3 of column lane%16 of each 16x16 tile.
+  uint16_t* ot = lds;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int lrow = wm * 64 + i * 16 + (lane >> 4) * 4 + e;
-      const int t = m0 + lrow;
-      if (t >= a.num_tokens) continue;
-      const int64_t slot = a.slots[t];
-      if (slot < 0 || slot >= a.num_slots) continue;
       const float sc = row_scale[lrow];
-      const int64_t blk = slot >> a.bs_shift;
-      const int64_t off = slot & (a.block_size - 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 64 + j * 16 + (lane & 15);
-        const bool is_v = col >= a.out_half;
-        const int hd = is_v ? col - a.out_half : col;
-        const int h = hd / a.head_dim;
-        const int d = hd - h * a.head_dim;
-        uint16_t* cache = is_v ? a.v_cache : a.k_cache;
-        cache[((blk * a.num_kv_heads + h) * a.block_size + off) * a.head_dim + d] = f32_to_bf16_rne(acc[i][j][e] * sc);
+      for (int j = 0; j < 8; ++j) {
+        const int lcol = wn * 128 + j * 16 + (lane & 15);
+        ot[lrow * kOutStride + lcol] = static_cast<uint16_t>(yoco::pack_bf16x2(acc[i][j][e] * sc, 0.0f));
       }
     }
+  __syncthreads();
+
+  // Each token's features, 16 bytes (8 features, inside one head) at a time.
+  for (int c = tid; c < kBM * (kBN / 8); c += kGemmThreads) {
+    const int lrow = c / (kBN / 8);
+    const int lcol = (c % (kBN / 8)) * 8;
+    const int t = m0 + lrow;
+    const int col = n0 + lcol;
+    if (t >= a.num_tokens || col >= n_total) continue;
+    const int64_t slot = a.slots[t];
+    if (slot < 0 || slot >= a.num_slots) continue;
+    const bool is_v = col >= a.out_half;
+    const int hd = is_v ? col - a.out_half : col;
+    const int h = hd / a.head_dim;
+    const int d = hd - h * a.head_dim;
+    uint16_t* cache = is_v ? a.v_cache : a.k_cache;
+    const int64_t dst = (((slot >> a.bs_shift) * a.num_kv_heads + h) * a.block_size + (slot & (a.block_size - 1))) *
+                            a.head_dim + d;
+    *reinterpret_cast<uint4*>(cache + dst) = *reinterpret_cast<const uint4*>(&ot[lrow * kOutStride + lcol]);
   }
 }
 
@@ -483,7 +513,8 @@ extern "C" int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_toke
   a.num_slots = num_slots;
   a.inv_hidden = 1.0f / static_cast<float>(hidden);
   a.eps = eps;
-  const dim3 grid(static_cast<uint32_t>(2 * out_half / kBN), static_cast<uint32_t>(ceil_div(num_tokens, kBM)));
-  hipLaunchKernelGGL(kv_append_mfma_kernel, grid, dim3(kGemmThreads), 0, s, a);
+  a.n_tiles = static_cast<int32_t>(ceil_div(2 * out_half, kBN));
+  const int64_t tiles = ceil_div(num_tokens, kBM) * a.n_tiles;
+  hipLaunchKernelGGL(kv_append_mfma_kernel, dim3(static_cast<uint32_t>(tiles)), dim3(kGemmThreads), 0, s, a);
   return launch_result("kv_append");
 }
