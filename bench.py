@@ -165,7 +165,10 @@ def main():
                        device=dev)
     rows = torch.empty((meta.num_reqs, geom.hidden), dtype=x.dtype, device=dev)
     rows_idx = torch.empty(meta.num_reqs, dtype=torch.int32, device=dev)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # Between steps, read 1 GiB of other memory: that evicts the cache from the
+    # L2s and the last-level cache without leaving dirty lines behind (a fill
+    # would, and writing them back would slow the first kernel of the step).
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     L = geom.num_layers
 
@@ -182,7 +185,7 @@ def main():
 
     for i in range(args.warmup):
         if not args.no_flush:
-            flush.fill_(i & 0xFF)
+            flush.sum(dtype=torch.int64)
         step()
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps); partition_tokens {part}, {nparts} partitions per request")
@@ -194,7 +197,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         if not args.no_flush:
-            flush.fill_((i + 7) & 0xFF)
+            flush.sum(dtype=torch.int64)
         ev[i][0].record(stream)
         step(ev_l[i])
         ev[i][1].record(stream)

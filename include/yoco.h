@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define YOCO_ABI_VERSION 1
+#define YOCO_ABI_VERSION 2
 
 typedef enum yoco_status {
   YOCO_OK = 0,
@@ -69,6 +69,12 @@ typedef enum yoco_dtype { YOCO_DTYPE_F32 = 0, YOCO_DTYPE_BF16 = 1 } yoco_dtype_t
  * still sit in the GPU's last-level cache.  Results are bit-identical either
  * way. */
 #define YOCO_FLAG_REVERSE_ORDER 1u
+
+/* The first YOCO_CROSS_ATTN_QUEUE_BYTES bytes of a yoco_cross_attn workspace
+ * are the work-queue counters of its persistent schedule: they must be zero
+ * before the first call with that workspace, and every call leaves them zero
+ * again. */
+#define YOCO_CROSS_ATTN_QUEUE_BYTES 2048
 
 /* Version of this ABI (YOCO_ABI_VERSION). */
 int32_t yoco_abi_version(void);
@@ -193,11 +199,18 @@ int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_tokens, int32_t
  *   flags        YOCO_FLAG_REVERSE_ORDER or 0.
  *   out          fp32 [num_seqs][num_q_heads][head_dim].
  *   workspace    device scratch of at least yoco_cross_attn_workspace_size()
- *                bytes for the same arguments (the partitions' partial
- *                results, merged by a second kernel on the same stream);
- *                may be NULL when that size is 0.  No initial contents are
- *                needed.  Calls that may run concurrently (other streams)
- *                need separate workspaces.
+ *                bytes for the same arguments: the work-queue counters
+ *                (YOCO_CROSS_ATTN_QUEUE_BYTES, zero before the first call
+ *                with this workspace, left zero by every call), then the
+ *                partitions' partial results, merged by a second kernel on
+ *                the same stream.  Calls that may run concurrently (other
+ *                streams) need separate workspaces.
+ *
+ * Schedule: with num_seqs <= 2048 the attention kernel keeps as many
+ * workgroups as fit on the GPU at once, and each takes (request, KV head,
+ * partition) work items from device-side counters until none is left;
+ * partitions past the end of a context are never scheduled.  With more
+ * requests every work item gets a workgroup of its own.
  *
  * Supported: head_dim in {64, 128, 256}; num_q_heads / num_kv_heads in
  * {1, 2, 4, 8}; block_size a power of two in [1, 256]; at most 65535

@@ -62,6 +62,8 @@ def _attn(**kw):
     (dict(q=FAKE + 4), yb.YOCO_ERR_INVALID_ARGUMENT),
     (dict(num_seqs=-1), yb.YOCO_ERR_INVALID_ARGUMENT),
     (dict(max_seq_len=100000, part=64, ws_bytes=16), yb.YOCO_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws_bytes=yb.CROSS_ATTN_QUEUE_BYTES - 16), yb.YOCO_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws=None), yb.YOCO_ERR_INVALID_ARGUMENT),
     (dict(scale=float("nan")), yb.YOCO_ERR_INVALID_ARGUMENT),
     (dict(block_size=4, part=4096), yb.YOCO_ERR_UNSUPPORTED),
 ])
@@ -75,15 +77,15 @@ def test_cross_attn_empty_batch_is_a_noop():
 
 
 def test_workspace_and_partition_sizes():
-    # one partition needs no workspace
-    assert yb.cross_attn_workspace_size(4, 8, 2, 128, 64, 16, 64) == 0
+    # one partition needs only the work-queue counters
+    assert yb.cross_attn_workspace_size(4, 8, 2, 128, 64, 16, 64) == yb.CROSS_ATTN_QUEUE_BYTES
     p = yb.cross_attn_partition_tokens(1, 8, 128, 524288, 32, 0)
     assert p % 64 == 0 and -(-524288 // p) >= 256
     assert yb.cross_attn_partition_tokens(1, 8, 128, 524288, 1, 0) <= 1023      # slice of <= 1023 blocks
     np_ = -(-1000 // 64)
     size = yb.cross_attn_workspace_size(3, 8, 2, 128, 1000, 16, 64)
     acc = 3 * 8 * np_ * 128 * 4
-    assert size == -(-acc // 256) * 256 + 3 * 8 * np_ * 2 * 4
+    assert size == yb.CROSS_ATTN_QUEUE_BYTES + -(-acc // 256) * 256 + 3 * 8 * np_ * 2 * 4
     assert yb.kv_append_workspace_size(yb.DTYPE_BF16, 3072, 8, 128) == 2 * 1024 * 3072 * 2
     assert yb.kv_append_workspace_size(yb.DTYPE_F32, 256, 1, 64) == 0
 

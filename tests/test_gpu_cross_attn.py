@@ -5,12 +5,17 @@ full-size workloads, in the launch configuration the benchmark uses, on
 sampled (request, KV head) groups.  Tolerance: 2e-3 absolute on every output.
 """
 
+import math
+
 import numpy as np
 import pytest
 import torch
 
-from tests.gpu_helpers import ATTN_ATOL, DeviceWorkload, oracle_attention_full, oracle_attention_group, say
+import oracle
+from tests.gpu_helpers import (ATTN_ATOL, DeviceWorkload, dev, host, oracle_attention_full, oracle_attention_group,
+                               say)
 from yoco_shared_kv_gather_amd import binding as yb
+from yoco_shared_kv_gather_amd import synth
 
 pytestmark = pytest.mark.gpu
 
@@ -97,3 +102,73 @@ def test_many_partitions_long_context():
     err = _max_err(out, ref)
     say(f"  max abs err {err:.3e}")
     assert err <= ATTN_ATOL
+
+
+def _custom(geom, ctx, seed):
+    meta = synth.make_custom_metadata(geom, ctx, seed=seed)
+    d = dev()
+    k, v = synth.make_cache(meta, d, seed)
+    q = synth.make_queries(meta, d, seed, num_layers=1)[0]
+    table = torch.from_numpy(meta.block_table).to(d)
+    seq = torch.from_numpy(meta.seq_lens).to(d)
+    return meta, q, k, v, table, seq
+
+
+def _oracle(meta, q, k, v):
+    return oracle.cross_attention(host(q), host(k), host(v), meta.block_table, meta.seq_lens,
+                                  1.0 / math.sqrt(meta.geom.head_dim))
+
+
+def test_queue_counters_left_zero_between_calls():
+    """The persistent schedule's work-queue counters are zero again after each
+    call, so one workspace serves call after call with the same bits."""
+    say("cross_attn: work-queue counters across calls on one workspace")
+    w = DeviceWorkload(2, "small", layers=1)
+    g = w.geom
+    need = yb.cross_attn_workspace_size(w.meta.num_reqs, g.num_q_heads, g.num_kv_heads, g.head_dim,
+                                        w.meta.max_seq_len, g.block_size, 64)
+    ws = torch.zeros(need, dtype=torch.uint8, device=w.k.device)
+    ref = oracle_attention_full(w, 0)
+    first = None
+    for i in range(4):
+        out = yb.cross_attn(w.q[0], w.k, w.v, w.block_table, w.seq_lens, w.meta.max_seq_len, partition_tokens=64,
+                            flags=i & 1, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:yb.CROSS_ATTN_QUEUE_BYTES].count_nonzero()) == 0
+        assert _max_err(out, ref) <= ATTN_ATOL
+        if first is None:
+            first = out.clone()
+        assert torch.equal(first.view(torch.int32), out.view(torch.int32))
+
+
+@pytest.mark.parametrize("ctx", [[5], [5, 0, 17], [0], [0, 0, 1]])
+def test_fewer_work_items_than_queues(ctx):
+    """One to three work items: the grid shrinks to the item count and only
+    that many queues are used."""
+    say(f"cross_attn: contexts {ctx} with one KV head")
+    geom = synth.custom_geometry("bf16", 4, 1, 128, 16)
+    meta, q, k, v, table, seq = _custom(geom, ctx, seed=11)
+    out = yb.cross_attn(q, k, v, table, seq, meta.max_seq_len)
+    torch.cuda.synchronize()
+    assert _max_err(out, _oracle(meta, q, k, v)) <= ATTN_ATOL
+
+
+@pytest.mark.parametrize("num_reqs", [2048, 2049])
+def test_request_count_at_the_schedule_switch(num_reqs):
+    """2048 requests fill the persistent schedule's prefix exactly; one more
+    takes the one-workgroup-per-item schedule.  Both match the oracle."""
+    say(f"cross_attn: {num_reqs} requests")
+    rng = np.random.default_rng(num_reqs)
+    ctx = [int(c) for c in rng.integers(0, 48, size=num_reqs)]
+    geom = synth.custom_geometry("bf16", 2, 1, 64, 16)
+    meta, q, k, v, table, seq = _custom(geom, ctx, seed=13)
+    ref = _oracle(meta, q, k, v)
+    # a max_seq_len far past what the table rows span: partitions beyond the
+    # rows must not touch the table
+    for max_len in (meta.max_seq_len, 40 * meta.max_seq_len):
+        for part in (0, 64):
+            out = yb.cross_attn(q, k, v, table, seq, max_len, partition_tokens=part)
+            torch.cuda.synchronize()
+            err = _max_err(out, ref)
+            say(f"  max_seq_len {max_len} partition {part}: max abs err {err:.3e}")
+            assert err <= ATTN_ATOL

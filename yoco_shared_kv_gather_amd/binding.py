@@ -17,7 +17,7 @@ from typing import Optional, Tuple
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libyoco.so")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 YOCO_OK = 0
 YOCO_ERR_INVALID_ARGUMENT = 1
 YOCO_ERR_UNSUPPORTED = 2
@@ -25,6 +25,7 @@ YOCO_ERR_WORKSPACE_TOO_SMALL = 3
 YOCO_ERR_HIP = 4
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+CROSS_ATTN_QUEUE_BYTES = 2048
 FLAG_REVERSE_ORDER = 1
 
 _c = ctypes
@@ -182,7 +183,9 @@ def cross_attn(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale=No
                out=None, workspace=None, stream=None):
     """One cross layer: out[r][h] = softmax(scale q.K^T) V over request r's context.
 
-    Calls that may run concurrently need separate workspaces."""
+    A workspace passed in must start with CROSS_ATTN_QUEUE_BYTES zero bytes
+    before its first use (every call leaves them zero); allocate it with
+    torch.zeros.  Calls that may run concurrently need separate workspaces."""
     torch = _torch()
     code = _dtype_code(q)
     num_seqs, num_q_heads, head_dim = q.shape
@@ -195,10 +198,10 @@ def cross_attn(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale=No
                                      partition_tokens)
     if need < 0:
         raise YocoError(YOCO_ERR_INVALID_ARGUMENT, "bad cross_attn shape")
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace")
+    ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().yoco_cross_attn(code, _dev(q, "q"), num_seqs, num_q_heads, _dev(k_cache, "k_cache"),
                                  _dev(v_cache, "v_cache"), num_blocks, num_kv_heads, block_size, head_dim,
                                  _i32_dev(block_table, "block_table"), block_table.shape[1],

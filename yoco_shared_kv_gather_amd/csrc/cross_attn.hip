@@ -36,6 +36,9 @@
 //   * p.v in fp32 FMA; bf16 values widen with one shift or mask.
 
 #include <cmath>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "yoco_internal.h"
 
@@ -50,6 +53,10 @@ constexpr float kInitMax = -1.0e30f;       // finite "minus infinity" for runnin
 constexpr int kWaves = 4;                  // wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxSliceBlocks = 1024;      // block-table entries one partition may span
+constexpr int kMaxQueueSeqs = 2048;        // requests the persistent schedule's LDS prefix holds
+constexpr int kQueueLineWords = 32;        // the two queue counters sit on separate 128-byte lines
+constexpr int64_t kQueueHeaderBytes = 2048; // queue counters, the rest reserved
+static_assert(kQueueHeaderBytes == YOCO_CROSS_ATTN_QUEUE_BYTES, "queue header size");
 
 struct AttnArgs {
   const void* q;
@@ -60,6 +67,7 @@ struct AttnArgs {
   float* out;
   float* ws_acc;        // [num_seqs][Hq][num_parts][D]
   float* ws_ml;         // [num_seqs][Hq][num_parts][2]  (max, sum), base-2 units
+  uint32_t* queue;      // persistent schedule: fetch counters, then done counters; nullptr otherwise
   int64_t block_stride; // elements per physical block (Hkv * bs * D)
   int32_t head_stride;  // elements per KV head inside a block (bs * D)
   int32_t num_seqs;
@@ -193,6 +201,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_merge_kernel(AttnArgs a) 
   const int grp = tid / kSlices;
   float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float den = 0.0f;
+#pragma unroll 8
   for (int p = grp; p < np; p += kGroups) {
     const float w = exp2f(ml[2 * p] - mx);
     den = fmaf(w, ml[2 * p + 1], den);
@@ -229,103 +238,229 @@ struct RowSet {
   bool valid[Layout<kBf16, D>::kU];
 };
 
+// Shared memory of one workgroup: block-table slices and queries of the
+// current and the next work item (double buffered), the per-wavefront softmax
+// states and, for the persistent schedule, every request's clamped length and
+// the prefix of work-item counts.
+template <bool kBf16, int D, int G>
+struct AttnSmem {
+  static constexpr int kQChunks = G * D * (kBf16 ? 2 : 4) / 16;   // 16-byte chunks of a group's queries
+  int32_t blocks[2][kMaxSliceBlocks];
+  uint4 q[2][kQChunks];
+  float acc[kWaves][G][D];
+  float ml[kWaves][G][2];
+  int32_t len[kMaxQueueSeqs];
+  int32_t pref[kMaxQueueSeqs + 1];
+  int32_t wsum[kWaves];
+  uint32_t next;
+};
+
+// One work item: query heads g*G .. g*G+G-1 of request r (context length n)
+// over context tokens [start, end), which span block-table entries
+// first_blk .. first_blk+num_blk-1.  `valid` is false past the last item.
+struct Item {
+  bool valid;
+  int r, g, part, n, start, end, first_blk, num_blk;
+};
+
+// The fields are the same in every lane (the inputs come from LDS or from
+// ballots): readfirstlane keeps them in scalar registers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ Item make_item(const AttnArgs& a, bool valid, int r, int g, int part, int n) {
+  Item it;
+  it.valid = valid;
+  it.r = valid ? uniform(r) : 0;
+  it.g = valid ? uniform(g) : 0;
+  it.part = valid ? uniform(part) : 0;
+  it.n = valid ? uniform(n) : 0;
+  it.start = it.part * a.part_tokens;
+  it.end = min(it.start + a.part_tokens, it.n);
+  // An item without rows stages (harmlessly) the first table entry of its
+  // row: its start may lie past the row's last entry.
+  it.first_blk = it.end > it.start ? it.start >> a.bs_shift : 0;
+  it.num_blk = it.end > it.start ? ((it.end - 1) >> a.bs_shift) - it.first_blk + 1 : 0;
+  return it;
+}
+
+// Largest r in [0, R) with pref[r] <= k, for pref strictly increasing with
+// pref[0] = 0 <= k < pref[R]: each step tests 64 evenly spaced candidates
+// with one ballot, so R <= 4096 takes two steps.  Wave-uniform result.
+__device__ __forceinline__ int find_request(const int32_t* pref, int R, uint32_t k) {
+  const int lane = threadIdx.x & 63;
+  int lo = 0, span = R;
+  while (span > 1) {
+    const int stride = (span + 63) >> 6;
+    const int off = lane * stride;
+    const bool le = off < span && static_cast<uint32_t>(pref[lo + min(off, span - 1)]) <= k;
+    const unsigned long long mask = __ballot(le);
+    const int j = 63 - __clzll(mask);
+    const int nlo = lo + j * stride;
+    span = min(stride, lo + span - nlo);
+    lo = nlo;
+  }
+  return lo;
+}
+
+// Work items are (request, KV head, partition).  Two schedules:
+//   * persistent (a.queue != nullptr): as many workgroups as fit on the GPU at
+//     once.  Items are numbered request by request, counting only the
+//     partitions that hold tokens (an empty context has one item, which
+//     writes its zero rows), so no workgroup is spent on an empty partition.
+//     Workgroup w starts with item w; after that every workgroup takes the
+//     next unclaimed item from one device-wide counter, so a workgroup that
+//     runs faster (the XCDs do not all get the same share of HBM bandwidth)
+//     takes more items.  The last workgroup to finish
+//     resets the counter to zero: it knows it is last from a second (done)
+//     counter, and every workgroup's final fetch has returned before it
+//     counts itself done, so no fetch can follow the reset.  Same-line
+//     atomics serialise, so the two counters sit on separate 128-byte lines.
+//   * one item per workgroup (more requests than the LDS prefix holds):
+//     (request, KV head) varies fastest; the hardware deals consecutive
+//     workgroups to the eight XCDs in turn, so every XCD gets an even share
+//     of the partitions that hold tokens, and the empty tail partitions of
+//     short requests come last.
+// Items are pipelined: while one item streams, the next item's index is
+// known, its block-table slice and queries are loaded into registers and the
+// index after it is fetched; when the stream ends they go to the other LDS
+// buffer and the next item's first rows are requested before the finished
+// item's wavefronts are combined and written.
 template <bool kBf16, int D, int G>
 __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
   using L = Layout<kBf16, D>;
+  using Smem = AttnSmem<kBf16, D, G>;
   constexpr int kEpc = L::kEpc, kLpr = L::kLpr, kCpl = L::kCpl, kRpw = L::kRpw, kU = L::kU;
   constexpr int kIterTokens = L::kIterTokens;
   constexpr int kElemBytes = kBf16 ? 2 : 4;
+  constexpr int kQChunks = Smem::kQChunks;
+  constexpr int kTblPer = kMaxSliceBlocks / kThreads;               // table entries per thread
+  constexpr int kQPer = (kQChunks + kThreads - 1) / kThreads;       // query chunks per thread
+  static_assert(kMaxSliceBlocks % kThreads == 0, "slice staging");
 
-  __shared__ int32_t s_blocks[kMaxSliceBlocks];
-  __shared__ uint4 s_q[G * D * kElemBytes / 16];
-  __shared__ float s_acc[kWaves][G][D];
-  __shared__ float s_ml[kWaves][G][2];
-
+  __shared__ Smem sm;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int row = lane / kLpr;
   const int cl = lane % kLpr;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool reverse = (a.flags & YOCO_FLAG_REVERSE_ORDER) != 0;
+  const bool persistent = a.queue != nullptr;
+  const int R = a.num_seqs;
+  uint32_t* fetch_ctr = a.queue;
+  uint32_t* done_ctr = persistent ? a.queue + kQueueLineWords : nullptr;
+  uint32_t total = 0;
 
-  const uint32_t total = static_cast<uint32_t>(a.num_seqs) * a.num_kv_heads * a.num_parts;
-  uint32_t item = blockIdx.x;
-  if (a.flags & YOCO_FLAG_REVERSE_ORDER) item = total - 1u - item;
-  // (request, KV head) varies fastest: the hardware deals consecutive
-  // workgroups to the eight XCDs in turn, so every XCD gets an even share of
-  // the partitions that hold tokens, and the empty tail partitions of short
-  // requests come last.
-  const uint32_t pairs = static_cast<uint32_t>(a.num_seqs) * a.num_kv_heads;
-  const int part = static_cast<int>(item / pairs);
-  const uint32_t rg = item % pairs;
-  const int g = static_cast<int>(rg % a.num_kv_heads);
-  const int r = static_cast<int>(rg / a.num_kv_heads);
-
-  int n = a.seq_lens[r];
-  n = n < 0 ? 0 : (n > a.len_cap ? a.len_cap : n);
-  const int start = part * a.part_tokens;
-  const int hq0 = g * G;
-
-  if (start >= n) {
-    // Partitions past the end do nothing; the first one answers an empty
-    // context with zeros.
-    if (n == 0 && part == 0) {
-      for (int i = tid; i < G * D; i += kThreads) a.out[(static_cast<int64_t>(r) * a.num_q_heads + hq0) * D + i] = 0.0f;
+  uint32_t first_fetch = 0;
+  if (persistent) {
+    // The second item's index: fetched first thing, it is needed only once
+    // the first item is under way.
+    if (tid == 0) first_fetch = gridDim.x + atomicAdd(fetch_ctr, 1u);
+    // Clamped lengths and the exclusive prefix of work items per request.
+    for (int i = tid; i < R; i += kThreads) {
+      const int n = a.seq_lens[i];
+      sm.len[i] = n < 0 ? 0 : (n > a.len_cap ? a.len_cap : n);
     }
-    return;
-  }
-  const int end = min(start + a.part_tokens, n);
-
-  // The partition's block-table slice; out-of-range ids become -1 (skipped).
-  const int first_blk = start >> a.bs_shift;
-  const int num_blk = ((end - 1) >> a.bs_shift) - first_blk + 1;
-  {
-    const int32_t* table = a.block_table + static_cast<int64_t>(r) * a.max_blocks + first_blk;
-    for (int i = tid; i < num_blk; i += kThreads) {
-      const int b = table[i];
-      s_blocks[i] = static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks) ? b : -1;
+    __syncthreads();
+    const int per = (R + kThreads - 1) / kThreads;
+    const int lo = min(tid * per, R);
+    const int hi = min(lo + per, R);
+    int local = 0;
+    for (int i = lo; i < hi; ++i) {
+      const int n = sm.len[i];
+      local += (n == 0 ? 1 : (n + a.part_tokens - 1) / a.part_tokens) * a.num_kv_heads;
     }
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
+    }
+    if (lane == 63) sm.wsum[wave] = incl;
+    __syncthreads();
+    int run = incl - local;
+    for (int w = 0; w < wave; ++w) run += sm.wsum[w];
+    for (int i = lo; i < hi; ++i) {
+      sm.pref[i] = run;
+      const int n = sm.len[i];
+      run += (n == 0 ? 1 : (n + a.part_tokens - 1) / a.part_tokens) * a.num_kv_heads;
+    }
+    if (tid == kThreads - 1) sm.pref[R] = run;
+    if (tid == 0) sm.next = first_fetch;
+    __syncthreads();
+    total = static_cast<uint32_t>(uniform(sm.pref[R]));
   }
 
-  // Queries of the G heads of this group, staged in LDS: each lane reads the
-  // chunks it owns when it needs them (keeps G*CPL*4 registers free).
-  {
+  // Item number k of the persistent schedule.
+  auto item_at = [&](uint32_t k) -> Item {
+    if (k >= total) return make_item(a, false, 0, 0, 0, 0);
+    const uint32_t kk = reverse ? total - 1u - k : k;
+    const int r = find_request(sm.pref, R, kk);
+    const int idx = static_cast<int>(kk - static_cast<uint32_t>(sm.pref[r]));
+    const int part = idx / a.num_kv_heads;
+    return make_item(a, true, r, idx - part * a.num_kv_heads, part, sm.len[r]);
+  };
+
+  // Block-table slice and queries of an item: loaded into registers (indices
+  // clamped into the slice, so the loads need no branch), then stored to LDS.
+  // Each lane also keeps the block ids of the rows it reads first in that
+  // item (and the item's first block), so those rows can be requested before
+  // the slice is in LDS.
+  int32_t st_tbl[kTblPer];
+  uint4 st_q[kQPer];
+  int32_t st_nb[kU];
+  int32_t st_nb0;
+  auto valid_block = [&](int b) { return static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks) ? b : -1; };
+  auto stage_load = [&](const Item& it) {
+    const int32_t* row_table = a.block_table + static_cast<int64_t>(it.r) * a.max_blocks;
+    const int32_t* table = row_table + it.first_blk;
+    const int last = it.num_blk > 0 ? it.num_blk - 1 : 0;
+#pragma unroll
+    for (int j = 0; j < kTblPer; ++j) st_tbl[j] = table[min(tid + j * kThreads, last)];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = it.start + wave_u * kIterTokens + u * kRpw + row;
+      st_nb[u] = valid_block(row_table[j < it.end ? (j >> a.bs_shift) : it.first_blk]);
+    }
+    st_nb0 = valid_block(table[0]);
     const uint4* qg = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
-                                                     (static_cast<int64_t>(r) * a.num_q_heads + hq0) * D * kElemBytes);
-    for (int i = tid; i < G * D * kElemBytes / 16; i += kThreads) s_q[i] = qg[i];
-  }
-
-  float acc[G][kCpl][kEpc];
-  float m[G], lsum[G];
+                                                     (static_cast<int64_t>(it.r) * a.num_q_heads + it.g * G) * D *
+                                                         kElemBytes);
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kInitMax;
-    lsum[h] = 0.0f;
+    for (int j = 0; j < kQPer; ++j) st_q[j] = qg[min(tid + j * kThreads, kQChunks - 1)];
+  };
+  auto stage_store = [&](const Item& it, int buf) {
 #pragma unroll
-    for (int i = 0; i < kCpl; ++i)
+    for (int j = 0; j < kTblPer; ++j) {
+      const int i = tid + j * kThreads;
+      if (i < it.num_blk) sm.blocks[buf][i] = valid_block(st_tbl[j]);
+    }
 #pragma unroll
-      for (int e = 0; e < kEpc; ++e) acc[h][i][e] = 0.0f;
-  }
-  __syncthreads();
-
-  const char* kb = static_cast<const char*>(a.k) + static_cast<int64_t>(g) * a.head_stride * kElemBytes;
-  const char* vb = static_cast<const char*>(a.v) + static_cast<int64_t>(g) * a.head_stride * kElemBytes;
-  const int off_mask = a.block_size - 1;
-  const int num_iters = (end - start + kIterTokens - 1) / kIterTokens;
+    for (int j = 0; j < kQPer; ++j) {
+      const int i = tid + j * kThreads;
+      if (i < kQChunks) sm.q[buf][i] = st_q[j];
+    }
+  };
 
   // Loads are unconditional (no branch around them, so the next iteration's
   // loads stay in flight while the current rows are used).  A row past the
-  // end of the partition, or in an out-of-range block, reads the partition's
-  // first row instead and is masked out of the softmax (its p is 0 and the
-  // row it reads is a context row; block 0 if even that block is invalid).
-  const int64_t dummy_off =
-      (static_cast<int64_t>(s_blocks[0] >= 0 ? s_blocks[0] : 0) * a.block_stride +
-       static_cast<int64_t>(start & off_mask) * D) * kElemBytes;
-  auto load = [&](RowSet<kBf16, D>& rs, int it) {
+  // end of the item, or in an out-of-range block, reads the item's first row
+  // instead and is masked out of the softmax (its p is 0 and the row it reads
+  // is a context row; block 0 if even that block is invalid).  Only items
+  // with rows (num_blk > 0) are ever loaded.
+  auto load = [&](RowSet<kBf16, D>& rs, const Item& it, int buf, int iter) {
+    const char* kb = static_cast<const char*>(a.k) + static_cast<int64_t>(it.g) * a.head_stride * kElemBytes;
+    const char* vb = static_cast<const char*>(a.v) + static_cast<int64_t>(it.g) * a.head_stride * kElemBytes;
+    const int off_mask = a.block_size - 1;
+    const int b0 = sm.blocks[buf][0];
+    const int64_t dummy_off =
+        (static_cast<int64_t>(b0 >= 0 ? b0 : 0) * a.block_stride + static_cast<int64_t>(it.start & off_mask) * D) *
+        kElemBytes;
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      const int j = start + it * kIterTokens + u * kRpw + row;
-      const bool in_range = j < end;
-      const int blk = s_blocks[((in_range ? j : start) >> a.bs_shift) - first_blk];
+      const int j = it.start + iter * kIterTokens + u * kRpw + row;
+      const bool in_range = j < it.end;
+      const int blk = sm.blocks[buf][((in_range ? j : it.start) >> a.bs_shift) - it.first_blk];
       rs.valid[u] = in_range && blk >= 0;
       const int64_t off = rs.valid[u] ? (static_cast<int64_t>(blk) * a.block_stride +
                                          static_cast<int64_t>(j & off_mask) * D) * kElemBytes
@@ -339,13 +474,51 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     }
   };
 
-  auto compute = [&](const RowSet<kBf16, D>& rs) {
+  // Rows of one iteration of a wavefront: iteration `iter` of item `it`
+  // (slice in LDS buffer `buf`), or, once iter reaches num_iters, the
+  // wavefront's first rows of item `nx` (block ids from the staging
+  // registers).  One branch-free set of loads either way.
+  auto load_step = [&](RowSet<kBf16, D>& rs, const Item& it, int buf, int iter, int num_iters, const Item& nx) {
+    const bool to_nx = iter >= num_iters;
+    const int g = to_nx ? nx.g : it.g;
+    const char* kb = static_cast<const char*>(a.k) + static_cast<int64_t>(g) * a.head_stride * kElemBytes;
+    const char* vb = static_cast<const char*>(a.v) + static_cast<int64_t>(g) * a.head_stride * kElemBytes;
+    const int off_mask = a.block_size - 1;
+    const int start = to_nx ? nx.start : it.start;
+    const int end = to_nx ? nx.end : it.end;
+    const int b0 = to_nx ? st_nb0 : sm.blocks[buf][0];
+    const int64_t dummy_off =
+        (static_cast<int64_t>(b0 >= 0 ? b0 : 0) * a.block_stride + static_cast<int64_t>(start & off_mask) * D) *
+        kElemBytes;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int j = (to_nx ? nx.start + wave_u * kIterTokens : it.start + iter * kIterTokens) + u * kRpw + row;
+      const bool in_range = j < end;
+      const int lds_blk = sm.blocks[buf][((in_range && !to_nx ? j : it.start) >> a.bs_shift) - it.first_blk];
+      const int blk = to_nx ? st_nb[u] : lds_blk;
+      rs.valid[u] = in_range && blk >= 0;
+      const int64_t off = rs.valid[u] ? (static_cast<int64_t>(blk) * a.block_stride +
+                                         static_cast<int64_t>(j & off_mask) * D) * kElemBytes
+                                      : dummy_off;
+#pragma unroll
+      for (int i = 0; i < kCpl; ++i) {
+        const int64_t c = off + static_cast<int64_t>((cl + kLpr * i) * kEpc) * kElemBytes;
+        rs.k[u][i] = *reinterpret_cast<const uint4*>(kb + c);
+        rs.v[u][i] = *reinterpret_cast<const uint4*>(vb + c);
+      }
+    }
+  };
+
+  float acc[G][kCpl][kEpc];
+  float m[G], lsum[G];
+
+  auto compute = [&](const RowSet<kBf16, D>& rs, int buf) {
     float s[kU][G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       uint4 qh[kCpl];
 #pragma unroll
-      for (int i = 0; i < kCpl; ++i) qh[i] = s_q[(h * D + (cl + kLpr * i) * kEpc) * kElemBytes / 16];
+      for (int i = 0; i < kCpl; ++i) qh[i] = sm.q[buf][(h * D + (cl + kLpr * i) * kEpc) * kElemBytes / 16];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         float t = 0.0f;
@@ -390,87 +563,165 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     }
   };
 
-  // Wavefront w takes iterations w, w+4, ...; the next one's rows are in
-  // flight while the current ones are used.  The prefetch is issued even past
-  // the last iteration (all rows then masked) so the loop body has no branch
-  // around a load and the compiler's wait counts keep the prefetch in flight.
-  {
-    RowSet<kBf16, D> buf_a, buf_b;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    int it = wave_u;
-    load(buf_a, it);
-    while (it < num_iters) {
-      load(buf_b, it + kWaves);
-      compute(buf_a);
-      it += kWaves;
-      if (it >= num_iters) break;
-      load(buf_a, it + kWaves);
-      compute(buf_b);
-      it += kWaves;
-    }
+  // The first item, and the index of the next.
+  Item cur;
+  uint32_t k_next;
+  if (persistent) {
+    cur = item_at(blockIdx.x);
+    k_next = static_cast<uint32_t>(uniform(static_cast<int>(sm.next)));
+  } else {
+    const uint32_t items = static_cast<uint32_t>(R) * a.num_kv_heads * a.num_parts;
+    const uint32_t item = reverse ? items - 1u - blockIdx.x : blockIdx.x;
+    const uint32_t pairs = static_cast<uint32_t>(R) * a.num_kv_heads;
+    const int part = static_cast<int>(item / pairs);
+    const uint32_t rg = item % pairs;
+    const int r = static_cast<int>(rg / a.num_kv_heads);
+    int n = a.seq_lens[r];
+    n = n < 0 ? 0 : (n > a.len_cap ? a.len_cap : n);
+    cur = make_item(a, true, r, static_cast<int>(rg % a.num_kv_heads), part, n);
+    k_next = 0;
   }
 
-  // Combine the row groups of the wavefront (lanes with the same cl).
+  RowSet<kBf16, D> buf_a, buf_b;
+  bool first_in_b = false;                     // the current item's first rows sit in buf_b
+  int lb = 0;                                  // LDS buffer of the current item
+  if (cur.valid) {
+    stage_load(cur);
+    stage_store(cur, 0);
+    __syncthreads();
+    if (cur.num_blk > 0) load(buf_a, cur, 0, wave_u);
+  }
+
+  while (cur.valid) {
+    const Item nxt = persistent ? item_at(k_next) : make_item(a, false, 0, 0, 0, 0);
+    uint32_t fetched = 0;
+    if (nxt.valid && tid == 0) fetched = gridDim.x + atomicAdd(fetch_ctr, 1u);
+    stage_load(nxt);
+    if (first_in_b) buf_a = buf_b;
+    first_in_b = false;
+
+    const int num_iters = (cur.end - cur.start + kIterTokens - 1) / kIterTokens;
+    if (cur.num_blk > 0) {
 #pragma unroll
-  for (int mask = kLpr; mask < 64; mask <<= 1) {
+      for (int h = 0; h < G; ++h) {
+        m[h] = kInitMax;
+        lsum[h] = 0.0f;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], mask, 64);
-      const float lo = __shfl_xor(lsum[h], mask, 64);
-      const float mx = fmaxf(m[h], mo);
-      const float fa = exp2f(m[h] - mx);
-      const float fb = exp2f(mo - mx);
-      lsum[h] = lsum[h] * fa + lo * fb;
+        for (int i = 0; i < kCpl; ++i)
 #pragma unroll
-      for (int i = 0; i < kCpl; ++i)
-#pragma unroll
-        for (int e = 0; e < kEpc; ++e) {
-          const float other = __shfl_xor(acc[h][i][e], mask, 64);
-          acc[h][i][e] = acc[h][i][e] * fa + other * fb;
+          for (int e = 0; e < kEpc; ++e) acc[h][i][e] = 0.0f;
+      }
+      // Wavefront w takes iterations w, w+4, ... (buf_a already holds
+      // iteration w); the next one's rows are in flight while the current
+      // ones are used.  Past the last iteration the prefetch requests the
+      // wavefront's first rows of the next item.
+      int it = wave_u;
+      while (it < num_iters) {
+        load_step(buf_b, cur, lb, it + kWaves, num_iters, nxt);
+        compute(buf_a, lb);
+        it += kWaves;
+        if (it >= num_iters) {
+          first_in_b = true;
+          break;
         }
-      m[h] = mx;
-    }
-  }
-  if (row == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int i = 0; i < kCpl; ++i)
-#pragma unroll
-        for (int e = 0; e < kEpc; ++e) s_acc[wave][h][(cl + kLpr * i) * kEpc + e] = acc[h][i][e];
-      if (cl == 0) {
-        s_ml[wave][h][0] = m[h];
-        s_ml[wave][h][1] = lsum[h];
+        load_step(buf_a, cur, lb, it + kWaves, num_iters, nxt);
+        compute(buf_b, lb);
+        it += kWaves;
       }
-    }
-  }
-  __syncthreads();
 
-  // Combine the four wavefronts, then finish (one partition) or publish.
-  const int np_r = (n + a.part_tokens - 1) / a.part_tokens;
-  for (int e = tid; e < G * D; e += kThreads) {
-    const int h = e / D;
-    const int d = e - h * D;
-    float mx = s_ml[0][h][0];
+      // Combine the row groups of the wavefront (lanes with the same cl).
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, s_ml[w][h][0]);
-    float den = 0.0f, num = 0.0f;
+      for (int mask = kLpr; mask < 64; mask <<= 1) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float f = exp2f(s_ml[w][h][0] - mx);
-      den = fmaf(f, s_ml[w][h][1], den);
-      num = fmaf(f, s_acc[w][h][d], num);
-    }
-    const int64_t rh = static_cast<int64_t>(r) * a.num_q_heads + hq0 + h;
-    if (np_r == 1) {
-      a.out[rh * D + d] = den == 0.0f ? 0.0f : num / den;
-    } else {
-      const int64_t slot = rh * a.num_parts + part;
-      a.ws_acc[slot * D + d] = num;
-      if (d == 0) {
-        a.ws_ml[slot * 2] = mx;
-        a.ws_ml[slot * 2 + 1] = den;
+        for (int h = 0; h < G; ++h) {
+          const float mo = __shfl_xor(m[h], mask, 64);
+          const float lo = __shfl_xor(lsum[h], mask, 64);
+          const float mx = fmaxf(m[h], mo);
+          const float fa = exp2f(m[h] - mx);
+          const float fb = exp2f(mo - mx);
+          lsum[h] = lsum[h] * fa + lo * fb;
+#pragma unroll
+          for (int i = 0; i < kCpl; ++i)
+#pragma unroll
+            for (int e = 0; e < kEpc; ++e) {
+              const float other = __shfl_xor(acc[h][i][e], mask, 64);
+              acc[h][i][e] = acc[h][i][e] * fa + other * fb;
+            }
+          m[h] = mx;
+        }
       }
+      if (row == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+#pragma unroll
+          for (int i = 0; i < kCpl; ++i)
+#pragma unroll
+            for (int e = 0; e < kEpc; ++e) sm.acc[wave][h][(cl + kLpr * i) * kEpc + e] = acc[h][i][e];
+          if (cl == 0) {
+            sm.ml[wave][h][0] = m[h];
+            sm.ml[wave][h][1] = lsum[h];
+          }
+        }
+      }
+    }
+
+    // A wavefront that had no iteration of this item (or an item without
+    // rows) has not requested its first rows of the next item yet.
+    if (wave_u >= num_iters) load_step(buf_a, cur, lb, num_iters, num_iters, nxt);
+
+    // Hand over to the next item: its slice and queries into the other LDS
+    // buffer, then the finished item written.
+    if (nxt.valid) stage_store(nxt, lb ^ 1);
+    if (nxt.valid && tid == 0) sm.next = fetched;
+    __syncthreads();
+    const uint32_t k_after = static_cast<uint32_t>(uniform(static_cast<int>(sm.next)));
+
+    const int64_t rh0 = static_cast<int64_t>(cur.r) * a.num_q_heads + cur.g * G;
+    if (cur.num_blk > 0) {
+      // Combine the four wavefronts, then finish (one partition) or publish.
+      const int np_r = (cur.n + a.part_tokens - 1) / a.part_tokens;
+      for (int e = tid; e < G * D; e += kThreads) {
+        const int h = e / D;
+        const int d = e - h * D;
+        float mx = sm.ml[0][h][0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm.ml[w][h][0]);
+        float den = 0.0f, num = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float f = exp2f(sm.ml[w][h][0] - mx);
+          den = fmaf(f, sm.ml[w][h][1], den);
+          num = fmaf(f, sm.acc[w][h][d], num);
+        }
+        const int64_t rh = rh0 + h;
+        if (np_r == 1) {
+          a.out[rh * D + d] = den == 0.0f ? 0.0f : num / den;
+        } else {
+          const int64_t slot = rh * a.num_parts + cur.part;
+          a.ws_acc[slot * D + d] = num;
+          if (d == 0) {
+            a.ws_ml[slot * 2] = mx;
+            a.ws_ml[slot * 2 + 1] = den;
+          }
+        }
+      }
+    } else if (cur.n == 0 && cur.part == 0) {
+      // An empty context answers zeros (partitions past the end of a
+      // non-empty context, one-item-per-workgroup schedule only, do nothing).
+      for (int i = tid; i < G * D; i += kThreads) a.out[rh0 * D + i] = 0.0f;
+    }
+    __syncthreads();                           // sm.acc, sm.ml and sm.next are reused
+
+    cur = nxt;
+    lb ^= 1;
+    k_next = k_after;
+  }
+
+  if (persistent && tid == 0) {
+    const uint32_t d = atomicAdd(done_ctr, 1u);
+    if (d == gridDim.x - 1) {
+      atomicExch(fetch_ctr, 0u);
+      atomicExch(done_ctr, 0u);
     }
   }
 }
@@ -488,11 +739,24 @@ int32_t max_partition(int32_t block_size) {
 int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t block_size,
                           int32_t requested) {
   if (requested > 0) return requested;
-  // Aim for about 2048 workgroups (8192 wavefronts, 32 per compute unit when
-  // every context is full length) with partitions of 64 tokens or more.
-  const int64_t items = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
-  const int64_t parts = yoco::ceil_div(2048, items);
-  int64_t p = yoco::round_up(yoco::ceil_div(max_seq_len > 0 ? max_seq_len : 1, parts), 64);
+  const int64_t pairs = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
+  const int64_t len = max_seq_len > 0 ? max_seq_len : 1;
+  int64_t p;
+  if (num_seqs <= kMaxQueueSeqs) {
+    // Persistent schedule: about 8192 items when every context is full
+    // length (16 per resident workgroup on 256 compute units), so the
+    // device-wide queue can even out the workgroups' unequal speeds; at
+    // least 256 tokens per item, and at most 512 partitions per request so
+    // the merge stays small next to the stream.
+    p = yoco::round_up(yoco::ceil_div(len, yoco::ceil_div(8192, pairs)), 64);
+    if (p < 256) p = 256;
+    const int64_t p_merge = yoco::round_up(yoco::ceil_div(len, 512), 64);
+    if (p < p_merge) p = p_merge;
+  } else {
+    // One workgroup per item: about 2048 workgroups with partitions of 64
+    // tokens or more.
+    p = yoco::round_up(yoco::ceil_div(len, yoco::ceil_div(2048, pairs)), 64);
+  }
   const int64_t cap = max_partition(block_size > 0 ? block_size : 1);
   if (p > cap) p = cap;
   if (p < 64) p = 64;
@@ -504,48 +768,85 @@ int32_t num_partitions(int32_t max_seq_len, int32_t part_tokens) {
   return static_cast<int32_t>(np);
 }
 
-// Workspace: [acc fp32 num_seqs*Hq*num_parts*D | pad to 256][ml fp32 num_seqs*Hq*num_parts*2].
+// Workspace: [work-queue counters, kQueueHeaderBytes][acc fp32 num_seqs*Hq*num_parts*D | pad to 256]
+// [ml fp32 num_seqs*Hq*num_parts*2]; the partials only when there is more than one partition.
 struct WorkspaceLayout {
   int64_t acc_offset = 0;
   int64_t ml_offset = 0;
   int64_t total = 0;
 };
 
-WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                                 int32_t num_parts) {
+WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t num_parts) {
   WorkspaceLayout w;
+  w.total = kQueueHeaderBytes;
   if (num_parts <= 1) return w;
   const int64_t slots = static_cast<int64_t>(num_seqs) * num_q_heads * num_parts;
-  (void)num_kv_heads;
-  w.acc_offset = 0;
-  w.ml_offset = yoco::round_up(slots * head_dim * 4, 256);
+  w.acc_offset = kQueueHeaderBytes;
+  w.ml_offset = yoco::round_up(w.acc_offset + slots * head_dim * 4, 256);
   w.total = w.ml_offset + slots * 2 * 4;
   return w;
 }
 
+// Workgroups of one kernel instance resident on the current device at once
+// (compute units x workgroups per compute unit), cached per device and kernel.
+int resident_workgroups(const void* kernel, int per_cu_query(int*)) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(dev, kernel);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 0;
+  if (per_cu_query(&per_cu) != 0 || per_cu <= 0) return 0;
+  cache[key] = cus * per_cu;
+  return cus * per_cu;
+}
+
 template <bool kBf16, int D, int G>
-void launch(const AttnArgs& a, uint32_t grid, hipStream_t stream) {
-  hipLaunchKernelGGL((cross_attn_kernel<kBf16, D, G>), dim3(grid), dim3(kThreads), 0, stream, a);
+int per_cu_workgroups(int* out) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, cross_attn_kernel<kBf16, D, G>, kThreads, 0) == hipSuccess
+             ? 0 : 1;
+}
+
+// Launch the attention kernel: persistent (grid = resident workgroups, at
+// most one per work item) when the requests fit the LDS prefix, else one
+// workgroup per work item.  Returns false if the occupancy query failed.
+template <bool kBf16, int D, int G>
+bool launch(AttnArgs a, int64_t items, hipStream_t stream) {
+  int64_t grid = items;
+  if (a.queue != nullptr) {
+    const int slots = resident_workgroups(reinterpret_cast<const void*>(cross_attn_kernel<kBf16, D, G>),
+                                          per_cu_workgroups<kBf16, D, G>);
+    if (slots <= 0) return false;
+    grid = items < slots ? items : slots;
+  }
+  hipLaunchKernelGGL((cross_attn_kernel<kBf16, D, G>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
+                     a);
+  return true;
 }
 
 template <bool kBf16, int D>
-bool dispatch_group(int group, const AttnArgs& a, uint32_t grid, hipStream_t stream) {
+int dispatch_group(int group, const AttnArgs& a, int64_t items, hipStream_t stream) {
   switch (group) {
-    case 1: launch<kBf16, D, 1>(a, grid, stream); return true;
-    case 2: launch<kBf16, D, 2>(a, grid, stream); return true;
-    case 4: launch<kBf16, D, 4>(a, grid, stream); return true;
-    case 8: launch<kBf16, D, 8>(a, grid, stream); return true;
-    default: return false;
+    case 1: return launch<kBf16, D, 1>(a, items, stream) ? 1 : -1;
+    case 2: return launch<kBf16, D, 2>(a, items, stream) ? 1 : -1;
+    case 4: return launch<kBf16, D, 4>(a, items, stream) ? 1 : -1;
+    case 8: return launch<kBf16, D, 8>(a, items, stream) ? 1 : -1;
+    default: return 0;
   }
 }
 
+// 1: launched, 0: no kernel for the shape, -1: the occupancy query failed.
 template <bool kBf16>
-bool dispatch_dim(int head_dim, int group, const AttnArgs& a, uint32_t grid, hipStream_t stream) {
+int dispatch_dim(int head_dim, int group, const AttnArgs& a, int64_t items, hipStream_t stream) {
   switch (head_dim) {
-    case 64: return dispatch_group<kBf16, 64>(group, a, grid, stream);
-    case 128: return dispatch_group<kBf16, 128>(group, a, grid, stream);
-    case 256: return dispatch_group<kBf16, 256>(group, a, grid, stream);
-    default: return false;
+    case 64: return dispatch_group<kBf16, 64>(group, a, items, stream);
+    case 128: return dispatch_group<kBf16, 128>(group, a, items, stream);
+    case 256: return dispatch_group<kBf16, 256>(group, a, items, stream);
+    default: return 0;
   }
 }
 
@@ -568,7 +869,7 @@ extern "C" int64_t yoco_cross_attn_workspace_size(int32_t num_seqs, int32_t num_
       block_size <= 0 || partition_tokens < 0)
     return -1;
   const int32_t p = resolve_partition(num_seqs, num_kv_heads, max_seq_len, block_size, partition_tokens);
-  return workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, num_partitions(max_seq_len, p)).total;
+  return workspace_layout(num_seqs, num_q_heads, head_dim, num_partitions(max_seq_len, p)).total;
 }
 
 extern "C" int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seqs, int32_t num_q_heads,
@@ -611,13 +912,13 @@ extern "C" int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seq
   const int32_t nparts = num_partitions(max_seq_len, part);
   if (nparts > kMaxParts)
     return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: %d partitions per request exceed %d", nparts, kMaxParts);
-  const int64_t grid = static_cast<int64_t>(num_seqs) * num_kv_heads * nparts;
-  if (grid > 0x7fffffffLL) return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: %lld work items is too many", (long long)grid);
-  const WorkspaceLayout ws = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, nparts);
+  const int64_t items = static_cast<int64_t>(num_seqs) * num_kv_heads * nparts;
+  if (items > 0x7fffffffLL) return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: %lld work items is too many", (long long)items);
+  const WorkspaceLayout ws = workspace_layout(num_seqs, num_q_heads, head_dim, nparts);
   if (workspace_bytes < ws.total)
     return fail(YOCO_ERR_WORKSPACE_TOO_SMALL, "cross_attn: workspace %lld bytes, need %lld",
                 (long long)workspace_bytes, (long long)ws.total);
-  if (ws.total > 0 && (workspace == nullptr || !aligned16(workspace)))
+  if (workspace == nullptr || !aligned16(workspace))
     return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: workspace must be a 16-byte aligned pointer");
 
   AttnArgs a;
@@ -628,8 +929,9 @@ extern "C" int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seq
   a.seq_lens = seq_lens;
   a.out = out;
   char* wsb = static_cast<char*>(workspace);
-  a.ws_acc = ws.total > 0 ? reinterpret_cast<float*>(wsb + ws.acc_offset) : nullptr;
-  a.ws_ml = ws.total > 0 ? reinterpret_cast<float*>(wsb + ws.ml_offset) : nullptr;
+  a.ws_acc = nparts > 1 ? reinterpret_cast<float*>(wsb + ws.acc_offset) : nullptr;
+  a.ws_ml = nparts > 1 ? reinterpret_cast<float*>(wsb + ws.ml_offset) : nullptr;
+  a.queue = num_seqs <= kMaxQueueSeqs ? reinterpret_cast<uint32_t*>(wsb) : nullptr;
   a.head_stride = block_size * head_dim;
   a.block_stride = static_cast<int64_t>(num_kv_heads) * block_size * head_dim;
   a.num_seqs = num_seqs;
@@ -648,9 +950,10 @@ extern "C" int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seq
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   clear_launch_error();
-  const bool ok = dtype == YOCO_DTYPE_BF16 ? dispatch_dim<true>(head_dim, group, a, static_cast<uint32_t>(grid), s)
-                                           : dispatch_dim<false>(head_dim, group, a, static_cast<uint32_t>(grid), s);
-  if (!ok) return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: no kernel for this shape");
+  const int launched = dtype == YOCO_DTYPE_BF16 ? dispatch_dim<true>(head_dim, group, a, items, s)
+                                                : dispatch_dim<false>(head_dim, group, a, items, s);
+  if (launched == 0) return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: no kernel for this shape");
+  if (launched < 0) return fail(YOCO_ERR_HIP, "cross_attn: occupancy query failed on the current device");
   if (nparts > 1) {
     const uint32_t mgrid = static_cast<uint32_t>(static_cast<int64_t>(num_seqs) * num_q_heads);
     switch (head_dim) {
