@@ -307,8 +307,9 @@ __device__ __forceinline__ int find_request(const int32_t* pref, int R, uint32_t
 //     once.  Items are numbered request by request, counting only the
 //     partitions that hold tokens (an empty context has one item, which
 //     writes its zero rows), so no workgroup is spent on an empty partition.
-//     Workgroup w starts with item w; after that every workgroup takes the
-//     next unclaimed item from one device-wide counter, so a workgroup that
+//     Workgroup w starts with item w (no atomic on the critical path at the
+//     start); after that every workgroup takes the next unclaimed item from
+//     one device-wide counter, so a workgroup that
 //     runs faster (the XCDs do not all get the same share of HBM bandwidth)
 //     takes more items.  The last workgroup to finish
 //     resets the counter to zero: it knows it is last from a second (done)
@@ -320,10 +321,10 @@ __device__ __forceinline__ int find_request(const int32_t* pref, int R, uint32_t
 //     workgroups to the eight XCDs in turn, so every XCD gets an even share
 //     of the partitions that hold tokens, and the empty tail partitions of
 //     short requests come last.
-// Items are pipelined: while one item streams, the next item's index is
-// known, its block-table slice and queries are loaded into registers and the
-// index after it is fetched; when the stream ends they go to the other LDS
-// buffer and the next item's first rows are requested before the finished
+// Items are pipelined: near the end of an item's stream the next item's index
+// is fetched and its block-table slice and queries are loaded into registers;
+// the last iteration requests the next item's first rows, and when the stream
+// ends the slice and queries go to the other LDS buffer while the finished
 // item's wavefronts are combined and written.
 template <bool kBf16, int D, int G>
 __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
@@ -351,11 +352,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
   uint32_t* done_ctr = persistent ? a.queue + kQueueLineWords : nullptr;
   uint32_t total = 0;
 
-  uint32_t first_fetch = 0;
   if (persistent) {
-    // The second item's index: fetched first thing, it is needed only once
-    // the first item is under way.
-    if (tid == 0) first_fetch = gridDim.x + atomicAdd(fetch_ctr, 1u);
     // Clamped lengths and the exclusive prefix of work items per request.
     for (int i = tid; i < R; i += kThreads) {
       const int n = a.seq_lens[i];
@@ -386,7 +383,6 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
       run += (n == 0 ? 1 : (n + a.part_tokens - 1) / a.part_tokens) * a.num_kv_heads;
     }
     if (tid == kThreads - 1) sm.pref[R] = run;
-    if (tid == 0) sm.next = first_fetch;
     __syncthreads();
     total = static_cast<uint32_t>(uniform(sm.pref[R]));
   }
@@ -563,12 +559,13 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     }
   };
 
-  // The first item, and the index of the next.
-  Item cur;
-  uint32_t k_next;
+  // The first item (workgroup w starts with item w; the persistent schedule
+  // fetches the next one while it runs).
+  Item cur, nxt;
+  bool nxt_known = !persistent;
   if (persistent) {
     cur = item_at(blockIdx.x);
-    k_next = static_cast<uint32_t>(uniform(static_cast<int>(sm.next)));
+    nxt = cur;
   } else {
     const uint32_t items = static_cast<uint32_t>(R) * a.num_kv_heads * a.num_parts;
     const uint32_t item = reverse ? items - 1u - blockIdx.x : blockIdx.x;
@@ -579,7 +576,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     int n = a.seq_lens[r];
     n = n < 0 ? 0 : (n > a.len_cap ? a.len_cap : n);
     cur = make_item(a, true, r, static_cast<int>(rg % a.num_kv_heads), part, n);
-    k_next = 0;
+    nxt = make_item(a, false, 0, 0, 0, 0);
   }
 
   RowSet<kBf16, D> buf_a, buf_b;
@@ -593,14 +590,37 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
   }
 
   while (cur.valid) {
-    const Item nxt = persistent ? item_at(k_next) : make_item(a, false, 0, 0, 0, 0);
-    uint32_t fetched = 0;
-    if (nxt.valid && tid == 0) fetched = gridDim.x + atomicAdd(fetch_ctr, 1u);
-    stage_load(nxt);
+    const int num_iters = (cur.end - cur.start + kIterTokens - 1) / kIterTokens;
+    // The next item is fetched late, so that when the queue runs dry a
+    // workgroup holds little more than the item it is streaming: in an item
+    // of three or more rounds (a round = one iteration of every wavefront)
+    // the fetch is issued three rounds before the end, its result is shared
+    // one round later (one barrier) and the next item's staging loads go
+    // out then, in time for the last round to request its first rows.  A
+    // shorter item fetches at its start.
+    const int rounds = num_iters / kWaves;
+    const bool late = !nxt_known && rounds >= 3;
+    if (!nxt_known && !late) {
+      if (tid == 0) sm.next = gridDim.x + atomicAdd(fetch_ctr, 1u);
+      __syncthreads();
+      nxt = item_at(static_cast<uint32_t>(uniform(static_cast<int>(sm.next))));
+      nxt_known = true;
+    }
+    if (nxt_known) stage_load(nxt);
     if (first_in_b) buf_a = buf_b;
     first_in_b = false;
+    uint32_t pending = 0;
+    auto late_fetch = [&](int rd) {
+      if (!late) return;
+      if (rd == rounds - 3 && tid == 0) pending = atomicAdd(fetch_ctr, 1u);
+      if (rd == rounds - 2) {
+        if (tid == 0) sm.next = gridDim.x + pending;
+        __syncthreads();
+        nxt = item_at(static_cast<uint32_t>(uniform(static_cast<int>(sm.next))));
+        stage_load(nxt);
+      }
+    };
 
-    const int num_iters = (cur.end - cur.start + kIterTokens - 1) / kIterTokens;
     if (cur.num_blk > 0) {
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -616,17 +636,22 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
       // ones are used.  Past the last iteration the prefetch requests the
       // wavefront's first rows of the next item.
       int it = wave_u;
+      int rd = 0;
       while (it < num_iters) {
+        late_fetch(rd);
         load_step(buf_b, cur, lb, it + kWaves, num_iters, nxt);
         compute(buf_a, lb);
         it += kWaves;
+        ++rd;
         if (it >= num_iters) {
           first_in_b = true;
           break;
         }
+        late_fetch(rd);
         load_step(buf_a, cur, lb, it + kWaves, num_iters, nxt);
         compute(buf_b, lb);
         it += kWaves;
+        ++rd;
       }
 
       // Combine the row groups of the wavefront (lanes with the same cl).
@@ -672,9 +697,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     // Hand over to the next item: its slice and queries into the other LDS
     // buffer, then the finished item written.
     if (nxt.valid) stage_store(nxt, lb ^ 1);
-    if (nxt.valid && tid == 0) sm.next = fetched;
     __syncthreads();
-    const uint32_t k_after = static_cast<uint32_t>(uniform(static_cast<int>(sm.next)));
 
     const int64_t rh0 = static_cast<int64_t>(cur.r) * a.num_q_heads + cur.g * G;
     if (cur.num_blk > 0) {
@@ -713,8 +736,8 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     __syncthreads();                           // sm.acc, sm.ml and sm.next are reused
 
     cur = nxt;
+    nxt_known = !persistent;                   // the one-item-per-workgroup schedule stops here
     lb ^= 1;
-    k_next = k_after;
   }
 
   if (persistent && tid == 0) {
@@ -746,11 +769,11 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_se
     // Persistent schedule: about 8192 items when every context is full
     // length (16 per resident workgroup on 256 compute units), so the
     // device-wide queue can even out the workgroups' unequal speeds; at
-    // least 256 tokens per item, and at most 512 partitions per request so
+    // least 256 tokens per item, and at most 256 partitions per request so
     // the merge stays small next to the stream.
     p = yoco::round_up(yoco::ceil_div(len, yoco::ceil_div(8192, pairs)), 64);
     if (p < 256) p = 256;
-    const int64_t p_merge = yoco::round_up(yoco::ceil_div(len, 512), 64);
+    const int64_t p_merge = yoco::round_up(yoco::ceil_div(len, 256), 64);
     if (p < p_merge) p = p_merge;
   } else {
     // One workgroup per item: about 2048 workgroups with partitions of 64

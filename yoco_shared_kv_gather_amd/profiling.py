@@ -128,8 +128,9 @@ def summarize(out: str, workload: str, command: str, top: int = 10) -> str:
 
 
 def measured_traffic(workload: str, kernels: List[str]) -> Optional[dict]:
-    """HBM bytes per dispatch summed over `kernels`, from the committed profile
-    of `workload` -- or None if there is none or the sources changed since."""
+    """HBM bytes per dispatch and average kernel time summed over `kernels`,
+    from the committed profile of `workload` -- or None if there is none or
+    the sources changed since."""
     path = os.path.join(PROFILES, f"cross_attn_{workload}.md")
     if not os.path.exists(path):
         return None
@@ -137,18 +138,20 @@ def measured_traffic(workload: str, kernels: List[str]) -> Optional[dict]:
     m = re.search(r"^source_hash: (\S+)", text, re.M)
     if not m or m.group(1) != source_hash():
         return None
-    total_r = total_w = 0.0
+    total_r = total_w = total_us = 0.0
     found = 0
     for line in text.splitlines():
         if line.startswith("kernel_bytes: "):
-            name, _us, r, w = [f.strip() for f in line[len("kernel_bytes: "):].split("|")]
+            name, us, r, w = [f.strip() for f in line[len("kernel_bytes: "):].split("|")]
             if name in kernels:
                 total_r += float(r)
                 total_w += float(w)
+                total_us += float(us)
                 found += 1
     if found != len(kernels):
         return None
-    return {"read_bytes": total_r, "write_bytes": total_w, "profile": os.path.relpath(path, ROOT)}
+    return {"read_bytes": total_r, "write_bytes": total_w, "kernel_us": total_us,
+            "profile": os.path.relpath(path, ROOT)}
 
 
 def main():
