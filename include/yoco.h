@@ -186,16 +186,19 @@ int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_tokens, int32_t
  *   block_table  int32 [num_seqs][max_blocks_per_seq].  Precondition:
  *                entries used by a context lie in [0, num_blocks).  An entry
  *                outside that range is never dereferenced and its tokens are
- *                left out of the softmax; if it is the first block of a
- *                split-KV partition the request's output is unspecified.
+ *                left out of the softmax (a context whose every entry is out
+ *                of range gives a zero row).
  *   seq_lens     int32 [num_seqs]; values are clamped to
  *                [0, min(max_seq_len, max_blocks_per_seq*block_size)].
  *   max_seq_len  an upper bound of seq_lens; sizes the split into partitions.
  *   scale        softmax scale; the pages' value is 1/sqrt(head_dim).
- *   partition_tokens  tokens per split-KV partition: 0 picks one from the
+ *   partition_tokens  split-KV partition size P: 0 picks one from the
  *                shape (yoco_cross_attn_partition_tokens), otherwise a
- *                positive multiple of 64 spanning at most 1023 blocks and at
- *                most 16384 tokens (YOCO_ERR_UNSUPPORTED beyond).
+ *                positive multiple of 64 spanning at most 511 blocks and at
+ *                most 16384 tokens (YOCO_ERR_UNSUPPORTED beyond).  A context
+ *                of n tokens is split into ceil(n/P) partitions of P tokens
+ *                (the last one shorter); every context's last two come last
+ *                in the schedule.
  *   flags        YOCO_FLAG_REVERSE_ORDER or 0.
  *   out          fp32 [num_seqs][num_q_heads][head_dim].
  *   workspace    device scratch of at least yoco_cross_attn_workspace_size()

@@ -55,36 +55,43 @@ def test_block_sizes(block_size):
         assert err <= ATTN_ATOL, err
 
 
-def test_out_of_range_block_ids_are_skipped():
+@pytest.mark.parametrize("lost_blocks", [(1, 2), (0,), (0, 1, 2, 3, 4, 5, 6)])
+def test_out_of_range_block_ids_are_skipped(lost_blocks):
     """A table entry outside [0, num_blocks) inside a context is a broken
     precondition: the kernel must stay in bounds, leave those tokens out of
-    the softmax (the first block of each partition is valid here), and leave
-    the other requests' outputs exact."""
-    say("shapes: out-of-range block ids")
+    the softmax wherever the entry sits (inside a partition, at the start of
+    one, or every entry of the context: a zero row), and leave the other
+    requests' outputs exact.  Free blocks hold NaN, so a masked row that
+    leaked into the sums would show."""
+    say(f"shapes: out-of-range block ids at {lost_blocks} of request 0")
     geom = synth.custom_geometry("bf16", 8, 2, 128, 16)
     meta = synth.make_custom_metadata(geom, [100, 40, 70], seed=3)
     d = dev()
     k, v = synth.make_cache(meta, d, 3)
     q = synth.make_queries(meta, d, 3, num_layers=1)[0]
     bad = meta.block_table.copy()
-    bad[0, 1] = meta.num_blocks + 5          # request 0 loses tokens 16..31
-    bad[0, 2] = -3                           # and 32..47
+    for i, b in enumerate(lost_blocks):
+        bad[0, b] = meta.num_blocks + 5 if i % 2 == 0 else -3
     table = torch.from_numpy(bad).to(d)
     seq = torch.from_numpy(meta.seq_lens).to(d)
     scale = 1.0 / math.sqrt(geom.head_dim)
+    keep = np.ones(100, dtype=bool)
+    for b in lost_blocks:
+        keep[16 * b:16 * (b + 1)] = False
+    kk, vv = oracle.logical_kv(host(k), host(v), meta.block_table[0], 100)
     for part in (0, 64):
         out = host(yb.cross_attn(q, k, v, table, seq, meta.max_seq_len, partition_tokens=part))
         torch.cuda.synchronize()
         ref = oracle.cross_attention(host(q), host(k), host(v), meta.block_table, meta.seq_lens, scale)
         assert np.isfinite(out).all()
         np.testing.assert_allclose(out[1:], ref[1:], atol=ATTN_ATOL, rtol=0)
-        # request 0 equals attention over its remaining tokens
-        keep = np.ones(100, dtype=bool)
-        keep[16:48] = False
-        kk, vv = oracle.logical_kv(host(k), host(v), meta.block_table[0], 100)
+        # request 0 equals attention over its remaining tokens (none: zeros)
         for h in range(geom.num_q_heads):
             g = h // 4
-            r0 = oracle.attention_one_query(host(q)[0, h], kk[keep, g], vv[keep, g], scale)
+            if keep.any():
+                r0 = oracle.attention_one_query(host(q)[0, h], kk[keep, g], vv[keep, g], scale)
+            else:
+                r0 = np.zeros(geom.head_dim)
             np.testing.assert_allclose(out[0, h], r0, atol=ATTN_ATOL, rtol=0)
 
 

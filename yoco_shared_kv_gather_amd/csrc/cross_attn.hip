@@ -52,7 +52,7 @@ constexpr float kLazyMaxSlack = 8.0f;      // log2 of the largest un-rescaled te
 constexpr float kInitMax = -1.0e30f;       // finite "minus infinity" for running maxima
 constexpr int kWaves = 4;                  // wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxSliceBlocks = 1024;      // block-table entries one partition may span
+constexpr int kMaxSliceBlocks = 512;       // block-table entries one partition may span
 constexpr int kMaxQueueSeqs = 2048;        // requests the persistent schedule's LDS prefix holds
 constexpr int kQueueLineWords = 32;        // the two queue counters sit on separate 128-byte lines
 constexpr int64_t kQueueHeaderBytes = 2048; // queue counters, the rest reserved
@@ -155,76 +155,85 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Wavefront reductions with a fixed butterfly order (deterministic).
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int mask = 32; mask > 0; mask >>= 1) v = fmaxf(v, __shfl_xor(v, mask, 64));
-  return v;
+// Partitions of a context of n tokens: ceil(n/P) pieces of P tokens (the
+// last one shorter; an empty context has one, empty, partition).  For the
+// schedule they fall in two groups: the leading n/P - 1 partitions when
+// n >= 2P ("big"), and the last one or two ("small"), which hold the short
+// piece.  All big items are scheduled before all small ones, so the work ends
+// on the short pieces.
+__host__ __device__ inline int big_parts(int n, int P) {
+  const int nb = n / P;
+  return nb >= 2 ? nb - 1 : 0;
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int mask = 32; mask > 0; mask >>= 1) v += __shfl_xor(v, mask, 64);
-  return v;
+__host__ __device__ inline int small_parts(int n, int P) {
+  return n <= 0 ? 1 : (n - big_parts(n, P) * P + P - 1) / P;
 }
+__host__ __device__ inline int parts_of(int n, int P) { return big_parts(n, P) + small_parts(n, P); }
 
 // Merge the partials of one (request, query head):
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
 // 256 threads: thread t owns the float4 slice (t % (D/4)) of head_dim and
-// partitions p = t / (D/4) + k * (256 / (D/4)); the per-group sums are then
-// added in group order through LDS.  Requests with one partition were
+// partitions p = t / (D/4) + k * (256 / (D/4)).  Each thread sums its
+// partitions relative to their own maximum, so the partial loads need not
+// wait for the global one; the groups are then rescaled and added in group
+// order through LDS (deterministic).  Requests with one partition were
 // finished by the first kernel.
 template <int D>
 __global__ __launch_bounds__(kThreads) void cross_attn_merge_kernel(AttnArgs a) {
   constexpr int kSlices = D / 4;                 // float4 slices of a head
   constexpr int kGroups = kThreads / kSlices;    // partition groups
-  __shared__ float s_red[kWaves];
   __shared__ float4 s_num[kGroups][kSlices];
   __shared__ float s_den[kGroups];
+  __shared__ float s_max[kGroups];
   const int64_t rh = blockIdx.x;
   const int r = static_cast<int>(rh / a.num_q_heads);
   const int tid = threadIdx.x;
   int n = a.seq_lens[r];
   n = n < 0 ? 0 : (n > a.len_cap ? a.len_cap : n);
-  const int np = (n + a.part_tokens - 1) / a.part_tokens;
+  const int np = parts_of(n, a.part_tokens);
   if (np <= 1) return;
-  const float* ml = a.ws_ml + rh * a.num_parts * 2;
+  const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + rh * a.num_parts;
   const float4* acc = reinterpret_cast<const float4*>(a.ws_acc + rh * a.num_parts * D);
-
-  float mx = kInitMax;
-  for (int p = tid; p < np; p += kThreads) mx = fmaxf(mx, ml[2 * p]);
-  mx = wave_max(mx);
-  if ((tid & 63) == 0) s_red[tid >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-
   const int slice = tid % kSlices;
   const int grp = tid / kSlices;
+
+  float m_loc = kInitMax;
+#pragma unroll 8
+  for (int p = grp; p < np; p += kGroups) m_loc = fmaxf(m_loc, ml[p].x);
   float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float den = 0.0f;
 #pragma unroll 8
   for (int p = grp; p < np; p += kGroups) {
-    const float w = exp2f(ml[2 * p] - mx);
-    den = fmaf(w, ml[2 * p + 1], den);
+    const float2 part = ml[p];
     const float4 v = acc[static_cast<int64_t>(p) * kSlices + slice];
+    const float w = exp2f(part.x - m_loc);
+    den = fmaf(w, part.y, den);
     num.x = fmaf(w, v.x, num.x);
     num.y = fmaf(w, v.y, num.y);
     num.z = fmaf(w, v.z, num.z);
     num.w = fmaf(w, v.w, num.w);
   }
   s_num[grp][slice] = num;
-  if (slice == 0) s_den[grp] = den;
+  if (slice == 0) {
+    s_den[grp] = den;
+    s_max[grp] = m_loc;
+  }
   __syncthreads();
   if (tid < kSlices) {
-    float4 t = s_num[0][tid];
-    float dsum = s_den[0];
+    float mx = s_max[0];
 #pragma unroll
-    for (int g2 = 1; g2 < kGroups; ++g2) {
+    for (int g2 = 1; g2 < kGroups; ++g2) mx = fmaxf(mx, s_max[g2]);
+    float4 t = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float dsum = 0.0f;
+#pragma unroll
+    for (int g2 = 0; g2 < kGroups; ++g2) {
+      const float f = exp2f(s_max[g2] - mx);
       const float4 u = s_num[g2][tid];
-      t.x += u.x;
-      t.y += u.y;
-      t.z += u.z;
-      t.w += u.w;
-      dsum += s_den[g2];
+      t.x = fmaf(f, u.x, t.x);
+      t.y = fmaf(f, u.y, t.y);
+      t.z = fmaf(f, u.z, t.z);
+      t.w = fmaf(f, u.w, t.w);
+      dsum = fmaf(f, s_den[g2], dsum);
     }
     const float inv = dsum == 0.0f ? 0.0f : 1.0f / dsum;
     reinterpret_cast<float4*>(a.out + rh * D)[tid] = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
@@ -251,7 +260,8 @@ struct AttnSmem {
   float ml[kWaves][G][2];
   int32_t len[kMaxQueueSeqs];
   int32_t pref[kMaxQueueSeqs + 1];
-  int32_t wsum[kWaves];
+  int32_t pref2[kMaxQueueSeqs + 1];
+  int32_t wsum[2 * kWaves];
   uint32_t next;
 };
 
@@ -350,10 +360,12 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
   const int R = a.num_seqs;
   uint32_t* fetch_ctr = a.queue;
   uint32_t* done_ctr = persistent ? a.queue + kQueueLineWords : nullptr;
-  uint32_t total = 0;
+  uint32_t total = 0, total_big = 0;
 
   if (persistent) {
-    // Clamped lengths and the exclusive prefix of work items per request.
+    // Clamped lengths, and the exclusive prefixes of the big items (pref) and
+    // of the small items (pref2) per request: all big items are numbered
+    // before all small ones.
     for (int i = tid; i < R; i += kThreads) {
       const int n = a.seq_lens[i];
       sm.len[i] = n < 0 ? 0 : (n > a.len_cap ? a.len_cap : n);
@@ -362,39 +374,59 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     const int per = (R + kThreads - 1) / kThreads;
     const int lo = min(tid * per, R);
     const int hi = min(lo + per, R);
-    int local = 0;
+    int local_b = 0, local_s = 0;
     for (int i = lo; i < hi; ++i) {
-      const int n = sm.len[i];
-      local += (n == 0 ? 1 : (n + a.part_tokens - 1) / a.part_tokens) * a.num_kv_heads;
+      local_b += big_parts(sm.len[i], a.part_tokens);
+      local_s += small_parts(sm.len[i], a.part_tokens);
     }
-    int incl = local;
+    int incl_b = local_b, incl_s = local_s;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int t = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += t;
+      const int tb = __shfl_up(incl_b, off, 64);
+      const int ts = __shfl_up(incl_s, off, 64);
+      if (lane >= off) {
+        incl_b += tb;
+        incl_s += ts;
+      }
     }
-    if (lane == 63) sm.wsum[wave] = incl;
+    if (lane == 63) {
+      sm.wsum[wave] = incl_b;
+      sm.wsum[kWaves + wave] = incl_s;
+    }
     __syncthreads();
-    int run = incl - local;
-    for (int w = 0; w < wave; ++w) run += sm.wsum[w];
+    int run_b = incl_b - local_b, run_s = incl_s - local_s;
+    for (int w = 0; w < wave; ++w) {
+      run_b += sm.wsum[w];
+      run_s += sm.wsum[kWaves + w];
+    }
     for (int i = lo; i < hi; ++i) {
-      sm.pref[i] = run;
-      const int n = sm.len[i];
-      run += (n == 0 ? 1 : (n + a.part_tokens - 1) / a.part_tokens) * a.num_kv_heads;
+      sm.pref[i] = run_b * a.num_kv_heads;
+      sm.pref2[i] = run_s * a.num_kv_heads;
+      run_b += big_parts(sm.len[i], a.part_tokens);
+      run_s += small_parts(sm.len[i], a.part_tokens);
     }
-    if (tid == kThreads - 1) sm.pref[R] = run;
+    if (tid == kThreads - 1) {
+      sm.pref[R] = run_b * a.num_kv_heads;
+      sm.pref2[R] = run_s * a.num_kv_heads;
+    }
     __syncthreads();
-    total = static_cast<uint32_t>(uniform(sm.pref[R]));
+    total_big = static_cast<uint32_t>(uniform(sm.pref[R]));
+    total = total_big + static_cast<uint32_t>(uniform(sm.pref2[R]));
   }
 
   // Item number k of the persistent schedule.
   auto item_at = [&](uint32_t k) -> Item {
     if (k >= total) return make_item(a, false, 0, 0, 0, 0);
     const uint32_t kk = reverse ? total - 1u - k : k;
-    const int r = find_request(sm.pref, R, kk);
-    const int idx = static_cast<int>(kk - static_cast<uint32_t>(sm.pref[r]));
-    const int part = idx / a.num_kv_heads;
-    return make_item(a, true, r, idx - part * a.num_kv_heads, part, sm.len[r]);
+    const bool big = kk < total_big;
+    const int32_t* pref = big ? sm.pref : sm.pref2;
+    const uint32_t j = big ? kk : kk - total_big;
+    const int r = find_request(pref, R, j);
+    const int idx = static_cast<int>(j - static_cast<uint32_t>(pref[r]));
+    const int n = sm.len[r];
+    const int sub = idx / a.num_kv_heads;
+    const int part = big ? sub : big_parts(n, a.part_tokens) + sub;
+    return make_item(a, true, r, idx - sub * a.num_kv_heads, part, n);
   };
 
   // Block-table slice and queries of an item: loaded into registers (indices
@@ -441,9 +473,9 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
   // Loads are unconditional (no branch around them, so the next iteration's
   // loads stay in flight while the current rows are used).  A row past the
   // end of the item, or in an out-of-range block, reads the item's first row
-  // instead and is masked out of the softmax (its p is 0 and the row it reads
-  // is a context row; block 0 if even that block is invalid).  Only items
-  // with rows (num_blk > 0) are ever loaded.
+  // instead (block 0 if that block is out of range too) and is masked: its
+  // score is -inf and its values are zeroed.  Only items with rows
+  // (num_blk > 0) are ever loaded.
   auto load = [&](RowSet<kBf16, D>& rs, const Item& it, int buf, int iter) {
     const char* kb = static_cast<const char*>(a.k) + static_cast<int64_t>(it.g) * a.head_stride * kElemBytes;
     const char* vb = static_cast<const char*>(a.v) + static_cast<int64_t>(it.g) * a.head_stride * kElemBytes;
@@ -549,13 +581,17 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
         lsum[h] += p[h];
       }
 #pragma unroll
-      for (int i = 0; i < kCpl; ++i)
+      for (int i = 0; i < kCpl; ++i) {
+        // A masked row (p = 0) read some other row, which may hold NaN:
+        // zero its values so that it adds exactly nothing.
+        const uint4 vc = rs.valid[u] ? rs.v[u][i] : make_uint4(0u, 0u, 0u, 0u);
 #pragma unroll
         for (int e = 0; e < kEpc; ++e) {
-          const float x = chunk_elem<kBf16>(rs.v[u][i], e);
+          const float x = chunk_elem<kBf16>(vc, e);
 #pragma unroll
           for (int h = 0; h < G; ++h) acc[h][i][e] = fmaf(p[h], x, acc[h][i][e]);
         }
+      }
     }
   };
 
@@ -702,7 +738,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     const int64_t rh0 = static_cast<int64_t>(cur.r) * a.num_q_heads + cur.g * G;
     if (cur.num_blk > 0) {
       // Combine the four wavefronts, then finish (one partition) or publish.
-      const int np_r = (cur.n + a.part_tokens - 1) / a.part_tokens;
+      const int np_r = parts_of(cur.n, a.part_tokens);
       for (int e = tid; e < G * D; e += kThreads) {
         const int h = e / D;
         const int d = e - h * D;
@@ -759,19 +795,22 @@ int32_t max_partition(int32_t block_size) {
   return static_cast<int32_t>(cap < 16384 ? cap : 16384);
 }
 
-int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len, int32_t block_size,
-                          int32_t requested) {
+int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                          int32_t block_size, int32_t requested) {
   if (requested > 0) return requested;
   const int64_t pairs = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
   const int64_t len = max_seq_len > 0 ? max_seq_len : 1;
+  const int64_t d = head_dim > 0 ? head_dim : 128;
   int64_t p;
   if (num_seqs <= kMaxQueueSeqs) {
-    // Persistent schedule: about 8192 items when every context is full
-    // length (16 per resident workgroup on 256 compute units), so the
-    // device-wide queue can even out the workgroups' unequal speeds; at
-    // least 256 tokens per item, and at most 256 partitions per request so
-    // the merge stays small next to the stream.
-    p = yoco::round_up(yoco::ceil_div(len, yoco::ceil_div(8192, pairs)), 64);
+    // Persistent schedule: items of about 512 KB of bf16 K^/V^ (P*D = 2^17:
+    // measured best on all four workloads within ~1.5%), but at least about
+    // 1024 items when every context is full length (two per resident
+    // workgroup) and at most 256 partitions per request, so the merge stays
+    // small next to the stream.
+    p = yoco::round_up((int64_t{1} << 17) / d, 64);
+    const int64_t p_items = yoco::round_up(yoco::ceil_div(len, yoco::ceil_div(1024, pairs)), 64);
+    if (p > p_items) p = p_items;
     if (p < 256) p = 256;
     const int64_t p_merge = yoco::round_up(yoco::ceil_div(len, 256), 64);
     if (p < p_merge) p = p_merge;
@@ -880,9 +919,8 @@ bool supported_dim(int d) { return d == 64 || d == 128 || d == 256; }
 extern "C" int32_t yoco_cross_attn_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
                                                     int32_t max_seq_len, int32_t block_size,
                                                     int32_t partition_tokens) {
-  (void)head_dim;
   if (partition_tokens < 0 || max_seq_len < 0 || block_size <= 0) return -1;
-  return resolve_partition(num_seqs, num_kv_heads, max_seq_len, block_size, partition_tokens);
+  return resolve_partition(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens);
 }
 
 extern "C" int64_t yoco_cross_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -891,7 +929,7 @@ extern "C" int64_t yoco_cross_attn_workspace_size(int32_t num_seqs, int32_t num_
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0 ||
       block_size <= 0 || partition_tokens < 0)
     return -1;
-  const int32_t p = resolve_partition(num_seqs, num_kv_heads, max_seq_len, block_size, partition_tokens);
+  const int32_t p = resolve_partition(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens);
   return workspace_layout(num_seqs, num_q_heads, head_dim, num_partitions(max_seq_len, p)).total;
 }
 
@@ -931,7 +969,7 @@ extern "C" int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seq
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: q, caches and out must be 16-byte aligned");
 
-  const int32_t part = resolve_partition(num_seqs, num_kv_heads, max_seq_len, block_size, partition_tokens);
+  const int32_t part = resolve_partition(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens);
   const int32_t nparts = num_partitions(max_seq_len, part);
   if (nparts > kMaxParts)
     return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: %d partitions per request exceed %d", nparts, kMaxParts);
