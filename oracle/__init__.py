@@ -4,6 +4,10 @@ from .yoco_oracle import (  # noqa: F401
     attention_one_query,
     cross_attention,
     cross_attention_group,
+    cross_attention_varlen,
+    cross_metadata,
+    gather_rows,
+    query_positions,
     gather_last,
     kv_append,
     kv_project,

@@ -48,6 +48,10 @@ __all__ = [
     "kv_project",
     "kv_append",
     "gather_last",
+    "cross_metadata",
+    "gather_rows",
+    "query_positions",
+    "cross_attention_varlen",
 ]
 
 
@@ -238,3 +242,102 @@ def gather_last(hidden, cu_seqlens):
             index[r] = cu[r + 1] - 1
             rows[r] = hidden[cu[r + 1] - 1]
     return rows, index
+
+
+# ---------------------------------------------------------------------------
+# Several logits positions per request  ([vLLM] "Implementation in vLLM":
+# the cross-decoder metadata builder and its printed example)
+# ---------------------------------------------------------------------------
+
+def cross_metadata(logits_indices, query_start_loc):
+    """Rebuild the cross-decoder's query_start_loc from the logits positions.
+
+    ``query_start_loc`` ``[R+1]``: request r owns token rows
+    ``query_start_loc[r] .. query_start_loc[r+1]-1`` of the step's batch.
+    ``logits_indices`` lists the token rows whose logits are needed (graph
+    padding already cut off).  As in the page's builder, each index is assigned
+    to the request whose row range holds it, the indices of each request are
+    counted, and the counts are summed into a new ``[R+1]`` offset array.
+
+    Returns ``(request_ids, counts, cross_query_start_loc, max_query_len)``.
+    An index outside ``[query_start_loc[0], query_start_loc[R])`` belongs to
+    no request: its request id is -1 and it is not counted (a reading; the
+    page assumes every index lies inside the batch).
+    """
+    qsl = [int(c) for c in np.asarray(query_start_loc)]
+    num_reqs = len(qsl) - 1
+    request_ids = np.full(len(np.asarray(logits_indices)), -1, dtype=np.int64)
+    counts = np.zeros(num_reqs, dtype=np.int64)
+    for i, idx in enumerate(np.asarray(logits_indices)):
+        idx = int(idx)
+        for r in range(num_reqs):
+            if qsl[r] <= idx < qsl[r + 1]:
+                request_ids[i] = r
+                counts[r] += 1
+                break
+    cross_qsl = np.zeros(num_reqs + 1, dtype=np.int64)
+    for r in range(num_reqs):
+        cross_qsl[r + 1] = cross_qsl[r] + counts[r]
+    max_query_len = int(counts.max()) if num_reqs else 0
+    return request_ids, counts, cross_qsl, max_query_len
+
+
+def gather_rows(hidden, logits_indices):
+    """``rows[i] = hidden[logits_indices[i]]`` bit for bit; an index outside
+    ``[0, T)`` gives a zero row (the cross-decoder's batch is the selected
+    rows, [vLLM] "Implementation in vLLM")."""
+    hidden = np.asarray(hidden)
+    idx = [int(i) for i in np.asarray(logits_indices)]
+    rows = np.zeros((len(idx),) + hidden.shape[1:], dtype=hidden.dtype)
+    for i, t in enumerate(idx):
+        if 0 <= t < hidden.shape[0]:
+            rows[i] = hidden[t]
+    return rows
+
+
+def query_positions(seq_len: int, num_queries: int):
+    """Logical positions of a request's queries in the cross-decoder.
+
+    The metadata the page builds keeps ``seq_lens`` and marks the attention
+    causal, so a request with n cached tokens and q query rows has its queries
+    at the last q positions n-q .. n-1 (for the page's example, request 1 with
+    seq_len 31 and logits rows 18, 19 queries positions 29 and 30).  A
+    position below zero (more queries than cached tokens) has no keys.
+    """
+    return [seq_len - num_queries + i for i in range(num_queries)]
+
+
+def cross_attention_varlen(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale: float,
+                           window: int = 0):
+    """One cross layer with any number of query rows per request.
+
+    q: ``[Nq][Hq][D]`` where request r's rows are ``query_start_loc[r] ..
+    query_start_loc[r+1]-1``; caches and block table as in
+    :func:`cross_attention`.  The query at position p (:func:`query_positions`)
+    attends causally to positions ``j <= p`` of the request's context; with
+    ``window > 0`` only to the last ``window`` of them, ``p - window < j <= p``
+    (a sliding-window cross layer reading a shared sliding-window cache, as
+    Gemma 3n's cross layers reuse the 19th layer's sliding-window cache, [vLLM]
+    "Gemma 3n").  A query with no keys yields a zero row.  Returns float64
+    ``[Nq][Hq][D]``.
+    """
+    q = np.asarray(q)
+    num_rows, num_q_heads, head_dim = q.shape
+    num_kv_heads = k_cache.shape[1]
+    group = num_q_heads // num_kv_heads
+    qsl = [int(c) for c in np.asarray(query_start_loc)]
+    out = np.zeros((num_rows, num_q_heads, head_dim), dtype=np.float64)
+    for r in range(len(qsl) - 1):
+        n = int(seq_lens[r])
+        rows = list(range(qsl[r], qsl[r + 1]))
+        if not rows or n <= 0:
+            continue
+        keys, values = logical_kv(k_cache, v_cache, block_table[r], n)
+        for row, p in zip(rows, query_positions(n, len(rows))):
+            lo = 0 if window <= 0 else max(0, p - window + 1)
+            if p < 0:
+                continue
+            for h in range(num_q_heads):
+                g = h // group
+                out[row, h] = attention_one_query(q[row, h], keys[lo:p + 1, g, :], values[lo:p + 1, g, :], scale)
+    return out

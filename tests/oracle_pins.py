@@ -364,3 +364,156 @@ def check_gather_bits(gather):
 
 
 GATHER_CHECKS = [check_gather_pages, check_gather_bits]
+
+
+# ---------------------------------------------------------------------------
+# several query rows per request, sliding window  (varlen attention)
+# ---------------------------------------------------------------------------
+
+def _band_mask(n, positions, window):
+    """bool [len(positions)][n]: query at p sees j <= p, and j > p - window
+    when window > 0 (built here directly from the statement, test side)."""
+    m = np.zeros((len(positions), n), dtype=bool)
+    for i, p in enumerate(positions):
+        for j in range(n):
+            m[i, j] = j <= p and (window <= 0 or j > p - window)
+    return m
+
+
+def check_varlen_decode_reduction(attn_varlen):
+    """One query row per request and no window is the decode attention of
+    every request's whole context: the pinned single-query oracle."""
+    import oracle
+    rng = np.random.default_rng(51)
+    q, kc, vc, tables, seq, _, _ = random_problem(rng, [9, 1, 30], 4, 2, 8, 4)
+    qsl = np.arange(4)
+    got = attn_varlen(q, kc, vc, tables, seq, qsl, 0.3, 0)
+    np.testing.assert_allclose(got, oracle.cross_attention(q, kc, vc, tables, seq, 0.3), rtol=0, atol=1e-13)
+
+
+def check_varlen_sdpa(attn_varlen):
+    """Library routine: torch SDPA in float64 with an explicit boolean mask
+    (queries on the last positions, causal, optional window) and GQA."""
+    rng = np.random.default_rng(52)
+    for hq, hkv, d, bs, lens, qlens, window in [
+            (4, 2, 8, 4, [11, 6, 17], [3, 1, 2], 0),
+            (4, 1, 8, 4, [13, 5], [4, 2], 5),
+            (2, 2, 16, 8, [40, 3, 9], [1, 3, 9], 7),
+            (8, 2, 4, 2, [2, 21], [5, 1], 1)]:
+        _, kc, vc, tables, seq, keys, values = random_problem(rng, lens, hq, hkv, d, bs)
+        qsl = np.concatenate([[0], np.cumsum(qlens)])
+        q = rng.standard_normal((int(qsl[-1]), hq, d))
+        got = attn_varlen(q, kc, vc, tables, seq, qsl, 1.0 / np.sqrt(d), window)
+        for r, n in enumerate(lens):
+            ql = qlens[r]
+            pos = [n - ql + i for i in range(ql)]
+            mask = _band_mask(n, pos, window)
+            qt = torch.from_numpy(q[qsl[r]:qsl[r + 1]]).permute(1, 0, 2).reshape(1, hq, ql, d).contiguous()
+            kt = torch.from_numpy(keys[r]).permute(1, 0, 2).reshape(1, hkv, n, d).contiguous()
+            vt = torch.from_numpy(values[r]).permute(1, 0, 2).reshape(1, hkv, n, d).contiguous()
+            live = mask.any(axis=1)
+            ref = F.scaled_dot_product_attention(qt[:, :, live], kt, vt, attn_mask=torch.from_numpy(mask[live]),
+                                                 enable_gqa=(hq != hkv))
+            ref = ref.reshape(hq, int(live.sum()), d).permute(1, 0, 2).numpy()
+            np.testing.assert_allclose(got[qsl[r]:qsl[r + 1]][live], ref, rtol=0, atol=1e-12)
+            assert not got[qsl[r]:qsl[r + 1]][~live].any()
+
+
+def check_varlen_closed_forms(attn_varlen):
+    """A window of one returns each query's own V row exactly; a window as
+    long as the context changes nothing; with more queries than cached tokens
+    the queries before position 0 give zeros; the last query of a request
+    sees the whole context."""
+    import oracle
+    rng = np.random.default_rng(53)
+    lens, qlens = [10, 4, 7], [3, 6, 1]
+    _, kc, vc, tables, seq, keys, values = random_problem(rng, lens, 4, 2, 8, 4)
+    qsl = np.concatenate([[0], np.cumsum(qlens)])
+    q = rng.standard_normal((int(qsl[-1]), 4, 8))
+    one = attn_varlen(q, kc, vc, tables, seq, qsl, 0.5, 1)
+    for r, n in enumerate(lens):
+        for i in range(qlens[r]):
+            p = n - qlens[r] + i
+            row = one[qsl[r] + i]
+            if p < 0:
+                assert not row.any()
+            else:
+                for h in range(4):
+                    assert np.array_equal(row[h], values[r][p, h // 2])
+    full = attn_varlen(q, kc, vc, tables, seq, qsl, 0.5, 0)
+    np.testing.assert_allclose(attn_varlen(q, kc, vc, tables, seq, qsl, 0.5, 10), full, rtol=0, atol=0)
+    assert not full[qsl[1]:qsl[1] + 2].any()           # request 1: positions -2, -1
+    last = q[qsl[1:] - 1]
+    np.testing.assert_allclose(full[qsl[1:] - 1], oracle.cross_attention(last, kc, vc, tables, seq, 0.5),
+                               rtol=0, atol=1e-13)
+
+
+def check_varlen_decimal(attn_varlen):
+    """Brute force in 50-digit decimal: each query over its own causal window."""
+    rng = np.random.default_rng(54)
+    for window in (0, 3):
+        lens, qlens = [7, 5], [3, 2]
+        _, kc, vc, tables, seq, keys, values = random_problem(rng, lens, 2, 1, 4, 4)
+        qsl = np.concatenate([[0], np.cumsum(qlens)])
+        q = rng.standard_normal((int(qsl[-1]), 2, 4))
+        got = attn_varlen(q, kc, vc, tables, seq, qsl, 0.5, window)
+        for r, n in enumerate(lens):
+            for i in range(qlens[r]):
+                p = n - qlens[r] + i
+                lo = 0 if window == 0 else max(0, p - window + 1)
+                for h in range(2):
+                    ref = _dec_attention(q[qsl[r] + i, h], keys[r][lo:p + 1, 0], values[r][lo:p + 1, 0], 0.5)
+                    np.testing.assert_allclose(got[qsl[r] + i, h], ref, rtol=0, atol=1e-13)
+
+
+VARLEN_CHECKS = [check_varlen_decode_reduction, check_varlen_sdpa, check_varlen_closed_forms, check_varlen_decimal]
+
+
+def check_metadata_page_example(meta_fn):
+    """The page's printed example: logits rows [14,18,19,27] of a batch with
+    query_start_loc [0,15,20,28] belong to requests [0,1,1,2], counted
+    [1,2,1], giving the cross-decoder query_start_loc [0,1,3,4]."""
+    fx = load_golden("vllm_logits_indices_example.json")["printed"]
+    rid, counts, qsl, mx = meta_fn(np.array(fx["logits_indices"]), np.array(fx["query_start_loc"]))
+    assert rid.tolist() == fx["request_ids"]
+    assert counts.tolist() == fx["num_decode_tokens"]
+    assert qsl.tolist() == fx["decode_query_start_loc"]
+    assert mx == max(fx["num_decode_tokens"])
+
+
+def check_metadata_torch(meta_fn):
+    """Library routines: torch.bucketize(right=True) over query_start_loc[1:],
+    bincount and cumsum on random batches (indices inside the batch), with
+    empty requests and indices on request boundaries."""
+    rng = np.random.default_rng(55)
+    for trial in range(20):
+        lens = rng.integers(0, 6, size=int(rng.integers(1, 7)))
+        qsl = np.concatenate([[0], np.cumsum(lens)])
+        total = int(qsl[-1])
+        if total == 0:
+            continue
+        idx = np.sort(rng.choice(total, size=int(rng.integers(1, total + 1)), replace=False))
+        idx = np.unique(np.concatenate([idx, qsl[1:-1][qsl[1:-1] < total]]))
+        rid, counts, cross, mx = meta_fn(idx, qsl)
+        t_rid = torch.bucketize(torch.from_numpy(idx), torch.from_numpy(qsl[1:]), right=True)
+        t_cnt = torch.bincount(t_rid, minlength=len(lens))
+        assert rid.tolist() == t_rid.tolist()
+        assert counts.tolist() == t_cnt.tolist()
+        assert cross.tolist() == [0] + torch.cumsum(t_cnt, 0).tolist()
+        assert mx == int(t_cnt.max())
+
+
+def check_gather_rows_bits(gather_rows_fn):
+    """Selected rows are copied bit for bit in the order given; an index
+    outside the batch gives a zero row."""
+    rng = np.random.default_rng(56)
+    bits = rng.integers(0, 2 ** 32, size=(8, 5), dtype=np.uint64).astype(np.uint32)
+    bits[6, 2] = 0x7FC0BEEF
+    rows = gather_rows_fn(bits, np.array([6, 0, 6, 9, -1, 7]))
+    assert np.array_equal(rows[0], bits[6]) and np.array_equal(rows[1], bits[0])
+    assert np.array_equal(rows[2], bits[6]) and np.array_equal(rows[5], bits[7])
+    assert not rows[3].any() and not rows[4].any()
+
+
+METADATA_CHECKS = [check_metadata_page_example, check_metadata_torch]
+GATHER_ROWS_CHECKS = [check_gather_rows_bits]

@@ -133,6 +133,67 @@ GATHER_MUTANTS = {
 }
 
 
+def _varlen_variant(positions=None, keep=None):
+    """A copy of the varlen attention with the query placement or the key
+    selection replaced."""
+    def attn(q, k_cache, v_cache, block_table, seq_lens, query_start_loc, scale, window=0):
+        q = np.asarray(q)
+        nrow, hq, d = q.shape
+        hkv = k_cache.shape[1]
+        qsl = [int(c) for c in query_start_loc]
+        out = np.zeros((nrow, hq, d))
+        for r in range(len(qsl) - 1):
+            n = int(seq_lens[r])
+            ql = qsl[r + 1] - qsl[r]
+            if ql == 0 or n <= 0:
+                continue
+            ks, vs = yo.logical_kv(k_cache, v_cache, block_table[r], n)
+            pos = [n - ql + i for i in range(ql)] if positions is None else positions(n, ql)
+            for i, p in enumerate(pos):
+                sel = [j for j in range(n) if (j <= p and (window <= 0 or j > p - window))] if keep is None \
+                    else [j for j in range(n) if keep(j, p, window)]
+                if not sel:
+                    continue
+                for h in range(hq):
+                    g = h // (hq // hkv)
+                    out[qsl[r] + i, h] = yo.attention_one_query(q[qsl[r] + i, h], ks[sel, g], vs[sel, g], scale)
+        return out
+    return attn
+
+
+VARLEN_MUTANTS = {
+    "queries_at_start": _varlen_variant(positions=lambda n, ql: list(range(ql))),
+    "not_causal": _varlen_variant(keep=lambda j, p, w: w <= 0 or j > p - w),
+    "window_ignored": _varlen_variant(keep=lambda j, p, w: j <= p),
+    "window_one_longer": _varlen_variant(keep=lambda j, p, w: j <= p and (w <= 0 or j >= p - w)),
+    "current_token_excluded": _varlen_variant(keep=lambda j, p, w: j < p and (w <= 0 or j > p - w)),
+}
+
+
+def _metadata_variant(owner=None, offsets=None):
+    def meta(logits_indices, query_start_loc):
+        qsl = [int(c) for c in query_start_loc]
+        nreq = len(qsl) - 1
+        rid = np.full(len(logits_indices), -1)
+        counts = np.zeros(nreq, dtype=np.int64)
+        for i, idx in enumerate(logits_indices):
+            r = owner(int(idx), qsl) if owner is not None else \
+                next((r for r in range(nreq) if qsl[r] <= int(idx) < qsl[r + 1]), -1)
+            if 0 <= r < nreq:
+                rid[i] = r
+                counts[r] += 1
+        cross = np.concatenate([[0], np.cumsum(counts)]) if offsets is None else offsets(counts)
+        return rid, counts, cross, int(counts.max()) if nreq else 0
+    return meta
+
+
+METADATA_MUTANTS = {
+    "boundary_to_previous": _metadata_variant(owner=lambda idx, qsl: next(
+        (r for r in range(len(qsl) - 1) if qsl[r] < idx <= qsl[r + 1]), -1)),
+    "exclusive_offsets": _metadata_variant(offsets=lambda c: np.concatenate([[0, 0], np.cumsum(c)[:-1]])),
+}
+
+
 def _fails_some(checks, fn):
     failures = 0
     for check in checks:
@@ -169,3 +230,18 @@ def test_unmutated_copies_pass():
     assert _fails_some(pins.ATTN_CHECKS, _attn_variant()) == 0
     assert _fails_some(pins.PROJ_CHECKS, _proj_variant()) == 0
     assert _fails_some(pins.GATHER_CHECKS, oracle.gather_last) == 0
+
+
+@pytest.mark.parametrize("name", sorted(VARLEN_MUTANTS))
+def test_varlen_mutant_is_caught(name):
+    assert _fails_some(pins.VARLEN_CHECKS, VARLEN_MUTANTS[name]) > 0
+
+
+@pytest.mark.parametrize("name", sorted(METADATA_MUTANTS))
+def test_metadata_mutant_is_caught(name):
+    assert _fails_some(pins.METADATA_CHECKS, METADATA_MUTANTS[name]) > 0
+
+
+def test_unmutated_varlen_copies_pass():
+    assert _fails_some(pins.VARLEN_CHECKS, _varlen_variant()) == 0
+    assert _fails_some(pins.METADATA_CHECKS, _metadata_variant()) == 0

@@ -25,3 +25,18 @@ def test_append_pins(check):
 @pytest.mark.parametrize("check", pins.GATHER_CHECKS, ids=lambda c: c.__name__)
 def test_gather_pins(check):
     check(oracle.gather_last)
+
+
+@pytest.mark.parametrize("check", pins.VARLEN_CHECKS, ids=lambda c: c.__name__)
+def test_varlen_pins(check):
+    check(oracle.cross_attention_varlen)
+
+
+@pytest.mark.parametrize("check", pins.METADATA_CHECKS, ids=lambda c: c.__name__)
+def test_metadata_pins(check):
+    check(oracle.cross_metadata)
+
+
+@pytest.mark.parametrize("check", pins.GATHER_ROWS_CHECKS, ids=lambda c: c.__name__)
+def test_gather_rows_pins(check):
+    check(oracle.gather_rows)
