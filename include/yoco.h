@@ -12,6 +12,15 @@
  *   yoco_cross_attn  one cross layer: each request's query heads attend to
  *                    the request's whole context in the shared paged cache.
  *
+ * and the general forms the same pages call for:
+ *
+ *   yoco_gather_logits      any number of rows per request (the logits
+ *                           positions), with the cross-decoder's
+ *                           query_start_loc rebuilt on the device.
+ *   yoco_cross_attn_varlen  several query rows per request (causal, aligned
+ *                           to the end of the context) and an optional
+ *                           sliding window.
+ *
  * Conventions shared by every call
  *   - All data pointers are DEVICE pointers owned by the caller.  The library
  *     never allocates, frees or synchronises; every call is asynchronous on
@@ -40,6 +49,8 @@
  *   [YOCO] "YOCO_论文与推理数据流详解", sections 3, 7.4, 9, 10.3, 10.4, 13.
  *   [KV]   "KV cache memory systems", sections "Cache contents" and
  *          "Contiguous allocation wastes capacity".
+ *   [Gemma] "You Only Cache Once, in vLLM", section "Gemma 3n": cross layers
+ *          that reuse a sliding-window layer's cache.
  */
 #ifndef YOCO_H_
 #define YOCO_H_
@@ -51,7 +62,7 @@
 extern "C" {
 #endif
 
-#define YOCO_ABI_VERSION 2
+#define YOCO_ABI_VERSION 3
 
 typedef enum yoco_status {
   YOCO_OK = 0,
@@ -237,6 +248,91 @@ int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seqs, int32_t 
                         const int32_t* seq_lens, int32_t max_seq_len, float scale,
                         int32_t partition_tokens, uint32_t flags, float* out,
                         void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * yoco_gather_logits -- the rows of the logits positions, and the
+ * cross-decoder's query offsets rebuilt from them.
+ *
+ * [vLLM] "Implementation in vLLM": the cross-decoder's batch is the rows at
+ * the logits positions (several per request under speculative decoding), and
+ * its attention metadata is rebuilt from them: each position is assigned to
+ * the request whose scheduled rows hold it, the positions of each request are
+ * counted, and the counts are summed into a new query_start_loc (the page's
+ * example: positions [14,18,19,27] with query_start_loc [0,15,20,28] give
+ * [0,1,3,4]).  Here that runs on the device without a host synchronisation.
+ *
+ *   hidden, num_tokens, row_bytes   as in yoco_gather_last.
+ *   logits_indices  int32 [num_indices]: rows to take.  Precondition (as the
+ *                   page's builder assumes): non-decreasing, so each
+ *                   request's rows are consecutive in out_rows.
+ *   query_start_loc int32 [num_reqs + 1] of the scheduled batch
+ *                   (non-decreasing).
+ *   out_rows        [num_indices][row_bytes]: out_rows[i] =
+ *                   hidden[logits_indices[i]], or zero bytes when the index
+ *                   lies outside [0, num_tokens).
+ *   out_query_start_loc  int32 [num_reqs + 1]: 0, then the running count of
+ *                   indices that lie in each request's row range; an index in
+ *                   no request's range is not counted.
+ *   out_max_query_len    optional int32 [1] (may be NULL): the largest count.
+ *
+ * Errors: YOCO_ERR_INVALID_ARGUMENT as in yoco_gather_last;
+ * YOCO_ERR_UNSUPPORTED for num_reqs > 8192.  num_reqs == 0 and
+ * num_indices == 0 write only what is left to write (offsets of zeros).
+ */
+int32_t yoco_gather_logits(const void* hidden, int64_t num_tokens, int64_t row_bytes,
+                           const int32_t* logits_indices, int32_t num_indices,
+                           const int32_t* query_start_loc, int32_t num_reqs, void* out_rows,
+                           int32_t* out_query_start_loc, int32_t* out_max_query_len, void* stream);
+
+/*
+ * yoco_cross_attn_varlen -- one cross layer with any number of query rows per
+ * request and an optional sliding window.
+ *
+ * [vLLM] "Implementation in vLLM": the rebuilt cross-decoder metadata keeps
+ * seq_lens and is causal, so request r with n = seq_lens[r] and
+ * ql = query_start_loc[r+1] - query_start_loc[r] query rows has its i-th row
+ * at logical position p = n - ql + i, which attends to positions j <= p.
+ * [Gemma]: a sliding-window cross layer reads only the last `window`
+ * positions, p - window < j <= p.  Output row query_start_loc[r] + i:
+ *     out[row][h] = sum_j softmax_j(scale * q[row][h] . K^[r][j][g]) V^[r][j][g]
+ * over those j (g = h / (num_q_heads / num_kv_heads)); a row with no
+ * position (p < 0, or n == 0) gives zeros.
+ *
+ *   dtype, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale,
+ *   partition_tokens, flags, workspace: as in yoco_cross_attn, except that
+ *   the partitions split the longest range a request's rows read,
+ *   min(max_seq_len, window + max_query_len - 1) with a window (max_seq_len
+ *   without), and the workspace size comes from
+ *   yoco_cross_attn_varlen_workspace_size().
+ *   q, out          [num_rows][num_q_heads][head_dim] (q in the cache dtype,
+ *                   out fp32).
+ *   query_start_loc int32 [num_seqs + 1], non-decreasing, values within
+ *                   [0, num_rows]; NULL means one row per request (row r,
+ *                   num_rows == num_seqs, max_query_len == 1), which runs
+ *                   the decode kernel of yoco_cross_attn.
+ *   max_query_len   an upper bound of the rows per request; a request's rows
+ *                   beyond it are not written.
+ *   window          0 for the whole context, else the window in tokens.
+ *   k_scale, v_scale  scales of an 8-bit cache; must be NULL for
+ *                   YOCO_DTYPE_F32 and YOCO_DTYPE_BF16.
+ *
+ * With query_start_loc: num_seqs <= 2048 (YOCO_ERR_UNSUPPORTED beyond); a
+ * work item streams its K^/V^ rows once for up to 8 query vectors (rows x
+ * heads of one KV group).  Errors as in yoco_cross_attn.
+ */
+int64_t yoco_cross_attn_varlen_workspace_size(int32_t num_rows, int32_t num_seqs, int32_t num_q_heads,
+                                              int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                                              int32_t max_query_len, int32_t window, int32_t block_size,
+                                              int32_t partition_tokens);
+int32_t yoco_cross_attn_varlen(int32_t dtype, const void* q, int32_t num_rows,
+                               const int32_t* query_start_loc, int32_t num_seqs, int32_t max_query_len,
+                               int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                               const float* k_scale, const float* v_scale, int32_t num_blocks,
+                               int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                               const int32_t* block_table, int32_t max_blocks_per_seq,
+                               const int32_t* seq_lens, int32_t max_seq_len, int32_t window, float scale,
+                               int32_t partition_tokens, uint32_t flags, float* out, void* workspace,
+                               int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

@@ -124,3 +124,54 @@ def test_kv_append_no_tokens_is_a_noop():
 ])
 def test_gather_last_rejects_before_launch(args, status):
     assert yb.lib().yoco_gather_last(*args) == status
+
+
+def _varlen(**kw):
+    args = dict(dtype=1, q=FAKE, num_rows=6, qsl=FAKE, num_seqs=2, max_qlen=4, num_q_heads=8, k=FAKE, v=FAKE,
+                k_scale=None, v_scale=None, num_blocks=10, num_kv_heads=2, block_size=16, head_dim=128, table=FAKE,
+                max_blocks=4, seq_lens=FAKE, max_seq_len=64, window=0, scale=0.1, part=0, flags=0, out=FAKE,
+                ws=FAKE, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return yb.lib().yoco_cross_attn_varlen(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(qsl=None), yb.YOCO_ERR_INVALID_ARGUMENT),                 # one row per request needs num_rows == num_seqs
+    (dict(qsl=None, num_rows=2, max_qlen=2), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(window=-1), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(max_qlen=-1), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(k_scale=FAKE), yb.YOCO_ERR_INVALID_ARGUMENT),              # scales only for an 8-bit cache
+    (dict(num_seqs=2049), yb.YOCO_ERR_UNSUPPORTED),
+    (dict(head_dim=96), yb.YOCO_ERR_UNSUPPORTED),
+    (dict(max_seq_len=100000, part=64, ws_bytes=4096), yb.YOCO_ERR_WORKSPACE_TOO_SMALL),
+    (dict(out=None), yb.YOCO_ERR_INVALID_ARGUMENT),
+])
+def test_cross_attn_varlen_rejects_before_launch(kw, status):
+    assert _varlen(**kw) == status
+    assert yb.last_error_message()
+
+
+def test_cross_attn_varlen_nothing_to_do():
+    assert _varlen(num_rows=0) == yb.YOCO_OK
+    assert _varlen(max_qlen=0) == yb.YOCO_OK
+
+
+def test_varlen_workspace_follows_the_window():
+    # a window caps the range the partitions split: window + max_query_len - 1 tokens
+    full = yb.cross_attn_varlen_workspace_size(8, 2, 8, 2, 128, 100000, 4, 0, 16, 64)
+    win = yb.cross_attn_varlen_workspace_size(8, 2, 8, 2, 128, 100000, 4, 637, 16, 64)
+    np_full, np_win = -(-100000 // 64), -(-640 // 64)
+    assert full == yb.CROSS_ATTN_QUEUE_BYTES + -(-8 * 8 * np_full * 128 * 4 // 256) * 256 + 8 * 8 * np_full * 8
+    assert win == yb.CROSS_ATTN_QUEUE_BYTES + -(-8 * 8 * np_win * 128 * 4 // 256) * 256 + 8 * 8 * np_win * 8
+
+
+@pytest.mark.parametrize("args,status", [
+    ((FAKE, 10, 24, FAKE, 2, FAKE, 2, FAKE, FAKE, None, None), yb.YOCO_ERR_INVALID_ARGUMENT),   # row_bytes
+    ((FAKE, 10, 32, None, 2, FAKE, 2, FAKE, FAKE, None, None), yb.YOCO_ERR_INVALID_ARGUMENT),   # indices
+    ((FAKE, 10, 32, FAKE, 2, None, 2, FAKE, FAKE, None, None), yb.YOCO_ERR_INVALID_ARGUMENT),   # offsets
+    ((FAKE, 10, 32, FAKE, 2, FAKE, 2, FAKE, None, None, None), yb.YOCO_ERR_INVALID_ARGUMENT),   # out offsets
+    ((FAKE, 10, 32, FAKE, 2, FAKE, 8193, FAKE, FAKE, None, None), yb.YOCO_ERR_UNSUPPORTED),
+    ((FAKE, 10, 32, FAKE, -2, FAKE, 2, FAKE, FAKE, None, None), yb.YOCO_ERR_INVALID_ARGUMENT),
+])
+def test_gather_logits_rejects_before_launch(args, status):
+    assert yb.lib().yoco_gather_logits(*args) == status

@@ -17,7 +17,7 @@ from typing import Optional, Tuple
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libyoco.so")
 
-ABI_VERSION = 2
+ABI_VERSION = 3
 YOCO_OK = 0
 YOCO_ERR_INVALID_ARGUMENT = 1
 YOCO_ERR_UNSUPPORTED = 2
@@ -48,6 +48,10 @@ SIGNATURES = {
     "yoco_cross_attn_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "yoco_cross_attn": (_i32, [_i32, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _f32,
                                _i32, _u32, _vp, _vp, _i64, _vp]),
+    "yoco_gather_logits": (_i32, [_vp, _i64, _i64, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]),
+    "yoco_cross_attn_varlen_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "yoco_cross_attn_varlen": (_i32, [_i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                      _i32, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _u32, _vp, _vp, _i64, _vp]),
 }
 
 _lock = threading.Lock()
@@ -208,6 +212,72 @@ def cross_attn(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale=No
                                  _i32_dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale),
                                  int(partition_tokens), int(flags), _dev(out, "out"), ws_ptr, ws_bytes,
                                  _stream_handle(stream)))
+    return out
+
+
+# ---- yoco_gather_logits --------------------------------------------------------------
+
+def gather_logits(hidden, logits_indices, query_start_loc, out=None, out_query_start_loc=None, out_max_query_len=None,
+                  stream=None):
+    """Rows at the logits positions and the cross-decoder's query_start_loc,
+    rebuilt on the device.  Returns (rows, query_start_loc, max_query_len),
+    the last two as int32 device tensors ([R+1] and [1])."""
+    torch = _torch()
+    num_idx = logits_indices.numel()
+    num_reqs = query_start_loc.numel() - 1
+    row_shape = tuple(hidden.shape[1:])
+    row_bytes = math.prod(row_shape) * hidden.element_size()
+    if out is None:
+        out = torch.empty((num_idx,) + row_shape, dtype=hidden.dtype, device=hidden.device)
+    if out_query_start_loc is None:
+        out_query_start_loc = torch.empty(num_reqs + 1, dtype=torch.int32, device=hidden.device)
+    if out_max_query_len is None:
+        out_max_query_len = torch.empty(1, dtype=torch.int32, device=hidden.device)
+    _check(lib().yoco_gather_logits(_dev(hidden, "hidden"), hidden.shape[0], row_bytes,
+                                    _i32_dev(logits_indices, "logits_indices"), num_idx,
+                                    _i32_dev(query_start_loc, "query_start_loc"), num_reqs, _dev(out, "out"),
+                                    _i32_dev(out_query_start_loc, "out_query_start_loc"),
+                                    _i32_dev(out_max_query_len, "out_max_query_len"), _stream_handle(stream)))
+    return out, out_query_start_loc, out_max_query_len
+
+
+# ---- yoco_cross_attn_varlen ------------------------------------------------------------
+
+def cross_attn_varlen_workspace_size(num_rows, num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                     max_query_len, window, block_size, partition_tokens=0) -> int:
+    return int(lib().yoco_cross_attn_varlen_workspace_size(num_rows, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                            max_seq_len, max_query_len, window, block_size,
+                                                            partition_tokens))
+
+
+def cross_attn_varlen(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, query_start_loc=None, max_query_len=1,
+                      window=0, scale=None, partition_tokens=0, flags=0, out=None, workspace=None, stream=None):
+    """One cross layer with several query rows per request (query_start_loc,
+    rows aligned to the end of each context, causal) and an optional sliding
+    window.  q and out are [num_rows][Hq][D]."""
+    torch = _torch()
+    code = _dtype_code(q)
+    num_rows, num_q_heads, head_dim = q.shape
+    num_blocks, num_kv_heads, block_size, _ = k_cache.shape
+    num_seqs = seq_lens.numel()
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    if out is None:
+        out = torch.empty((num_rows, num_q_heads, head_dim), dtype=torch.float32, device=q.device)
+    need = cross_attn_varlen_workspace_size(num_rows, num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
+                                            max_query_len, window, block_size, partition_tokens)
+    if need < 0:
+        raise YocoError(YOCO_ERR_INVALID_ARGUMENT, "bad cross_attn_varlen shape")
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    qsl_ptr = _i32_dev(query_start_loc, "query_start_loc") if query_start_loc is not None else None
+    _check(lib().yoco_cross_attn_varlen(code, _dev(q, "q"), num_rows, qsl_ptr, num_seqs, int(max_query_len),
+                                        num_q_heads, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), None, None,
+                                        num_blocks, num_kv_heads, block_size, head_dim,
+                                        _i32_dev(block_table, "block_table"), block_table.shape[1],
+                                        _i32_dev(seq_lens, "seq_lens"), int(max_seq_len), int(window), float(scale),
+                                        int(partition_tokens), int(flags), _dev(out, "out"), _dev(workspace, "workspace"),
+                                        workspace.numel() * workspace.element_size(), _stream_handle(stream)))
     return out
 
 

@@ -34,6 +34,18 @@
 //     group is raised only when a score exceeds it by more than 2^8, so the
 //     accumulators are rescaled rarely; sums stay within 256x the true terms.
 //   * p.v in fp32 FMA; bf16 values widen with one shift or mask.
+//
+// yoco_cross_attn_varlen generalises the query side ("You Only Cache Once, in
+// vLLM", section "Implementation in vLLM": the cross-decoder metadata keeps
+// seq_lens and marks attention causal, so a request with q logits rows has
+// queries at its last q positions; Gemma 3n's sliding-window cross layers read
+// a shared sliding-window cache, same page, section "Gemma 3n"):
+//   * a window of W tokens restricts the query at position p to keys
+//     p-W < j <= p.  With one query per request this only moves the start of
+//     the range the partitions cover, so the decode kernel is unchanged.
+//   * several query rows per request: a work item carries QPI consecutive
+//     query rows of one request (QPI*G <= 8 "virtual heads" share every K^/V^
+//     row), and each row masks the keys outside its own causal window.
 
 #include <cmath>
 #include <map>
@@ -82,7 +94,20 @@ struct AttnArgs {
   int32_t num_parts;
   float scale_log2;     // scale * log2(e)
   uint32_t flags;
+  const int32_t* qsl;   // query_start_loc [num_seqs+1] (several query rows per request), nullptr otherwise
+  int32_t num_rows;     // query rows of q and out (num_seqs without qsl)
+  int32_t max_qlen;     // query rows per request are clamped to this (1 without qsl)
+  int32_t window;       // sliding window in tokens; 0 = the whole context
 };
+
+// First context position any query of a request can see: its queries sit at
+// positions n-ql .. n-1, and with a window of W tokens the earliest key of the
+// first one is n-ql-W+1 (without a window, position 0).
+__host__ __device__ inline int range_lo(int n, int ql, int window) {
+  if (window <= 0) return 0;
+  const int lo = n - ql - window + 1;
+  return lo > 0 ? lo : 0;
+}
 
 template <bool kBf16, int D>
 struct Layout {
@@ -170,14 +195,16 @@ __host__ __device__ inline int small_parts(int n, int P) {
 }
 __host__ __device__ inline int parts_of(int n, int P) { return big_parts(n, P) + small_parts(n, P); }
 
-// Merge the partials of one (request, query head):
+// Merge the partials of one (query row, query head):
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
-// 256 threads: thread t owns the float4 slice (t % (D/4)) of head_dim and
-// partitions p = t / (D/4) + k * (256 / (D/4)).  Each thread sums its
-// partitions relative to their own maximum, so the partial loads need not
-// wait for the global one; the groups are then rescaled and added in group
-// order through LDS (deterministic).  Requests with one partition were
-// finished by the first kernel.
+// One workgroup per (request, query row of the request, head); rows past the
+// request's query count return at once.  256 threads: thread t owns the
+// float4 slice (t % (D/4)) of head_dim and partitions
+// p = t / (D/4) + k * (256 / (D/4)).  Each thread sums its partitions relative
+// to their own maximum, so the partial loads need not wait for the global
+// one; the groups are then rescaled and added in group order through LDS
+// (deterministic).  Rows whose context fits one partition were finished by
+// the first kernel.
 template <int D>
 __global__ __launch_bounds__(kThreads) void cross_attn_merge_kernel(AttnArgs a) {
   constexpr int kSlices = D / 4;                 // float4 slices of a head
@@ -185,13 +212,25 @@ __global__ __launch_bounds__(kThreads) void cross_attn_merge_kernel(AttnArgs a) 
   __shared__ float4 s_num[kGroups][kSlices];
   __shared__ float s_den[kGroups];
   __shared__ float s_max[kGroups];
-  const int64_t rh = blockIdx.x;
-  const int r = static_cast<int>(rh / a.num_q_heads);
+  const int64_t per_req = static_cast<int64_t>(a.max_qlen) * a.num_q_heads;
+  const int r = static_cast<int>(blockIdx.x / per_req);
+  const int rem = static_cast<int>(blockIdx.x - r * per_req);
+  const int qi = rem / a.num_q_heads;
+  const int h = rem - qi * a.num_q_heads;
   const int tid = threadIdx.x;
   int n = a.seq_lens[r];
   n = n < 0 ? 0 : (n > a.len_cap ? a.len_cap : n);
-  const int np = parts_of(n, a.part_tokens);
+  int ql = 1, row = r;
+  if (a.qsl != nullptr) {
+    const int qb = min(max(a.qsl[r], 0), a.num_rows);
+    const int qe = min(max(a.qsl[r + 1], 0), a.num_rows);
+    ql = min(max(qe - qb, 0), a.max_qlen);
+    row = qb + qi;
+  }
+  if (qi >= ql) return;
+  const int np = parts_of(n - range_lo(n, ql, a.window), a.part_tokens);
   if (np <= 1) return;
+  const int64_t rh = static_cast<int64_t>(row) * a.num_q_heads + h;
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + rh * a.num_parts;
   const float4* acc = reinterpret_cast<const float4*>(a.ws_acc + rh * a.num_parts * D);
   const int slice = tid % kSlices;
@@ -245,20 +284,23 @@ struct RowSet {
   uint4 k[Layout<kBf16, D>::kU][Layout<kBf16, D>::kCpl];
   uint4 v[Layout<kBf16, D>::kU][Layout<kBf16, D>::kCpl];
   bool valid[Layout<kBf16, D>::kU];
+  int pos[Layout<kBf16, D>::kU];     // logical position of the row (masks of the several-query path)
 };
 
 // Shared memory of one workgroup: block-table slices and queries of the
 // current and the next work item (double buffered), the per-wavefront softmax
-// states and, for the persistent schedule, every request's clamped length and
-// the prefix of work-item counts.
-template <bool kBf16, int D, int G>
+// states and, for the persistent schedule, every request's clamped length,
+// (several-query path) its first query row, and the prefix of work-item
+// counts.  VG = query vectors per item (G heads times the rows per item).
+template <bool kBf16, int D, int VG, bool kVar>
 struct AttnSmem {
-  static constexpr int kQChunks = G * D * (kBf16 ? 2 : 4) / 16;   // 16-byte chunks of a group's queries
+  static constexpr int kQChunks = VG * D * (kBf16 ? 2 : 4) / 16;   // 16-byte chunks of an item's queries
   int32_t blocks[2][kMaxSliceBlocks];
   uint4 q[2][kQChunks];
-  float acc[kWaves][G][D];
-  float ml[kWaves][G][2];
+  float acc[kWaves][VG][D];
+  float ml[kWaves][VG][2];
   int32_t len[kMaxQueueSeqs];
+  int32_t qs[kVar ? kMaxQueueSeqs + 1 : 1];
   int32_t pref[kMaxQueueSeqs + 1];
   int32_t pref2[kMaxQueueSeqs + 1];
   int32_t wsum[2 * kWaves];
@@ -267,24 +309,33 @@ struct AttnSmem {
 
 // One work item: query heads g*G .. g*G+G-1 of request r (context length n)
 // over context tokens [start, end), which span block-table entries
-// first_blk .. first_blk+num_blk-1.  `valid` is false past the last item.
+// first_blk .. first_blk+num_blk-1.  The request's partitions cover
+// [lo, n).  Several-query path: the item's query rows are row0 ..
+// row0+nq-1, the first of them at logical position pbase (decode path: row0
+// = r, nq = 1).  `valid` is false past the last item.
 struct Item {
   bool valid;
-  int r, g, part, n, start, end, first_blk, num_blk;
+  int r, g, part, n, lo, start, end, first_blk, num_blk;
+  int row0, nq, pbase;
 };
 
 // The fields are the same in every lane (the inputs come from LDS or from
 // ballots): readfirstlane keeps them in scalar registers.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-__device__ __forceinline__ Item make_item(const AttnArgs& a, bool valid, int r, int g, int part, int n) {
+__device__ __forceinline__ Item make_item(const AttnArgs& a, bool valid, int r, int g, int part, int n, int lo,
+                                          int row0, int nq, int pbase) {
   Item it;
   it.valid = valid;
   it.r = valid ? uniform(r) : 0;
   it.g = valid ? uniform(g) : 0;
   it.part = valid ? uniform(part) : 0;
   it.n = valid ? uniform(n) : 0;
-  it.start = it.part * a.part_tokens;
+  it.lo = valid ? uniform(lo) : 0;
+  it.row0 = valid ? uniform(row0) : 0;
+  it.nq = valid ? uniform(nq) : 0;
+  it.pbase = valid ? uniform(pbase) : 0;
+  it.start = it.lo + it.part * a.part_tokens;
   it.end = min(it.start + a.part_tokens, it.n);
   // An item without rows stages (harmlessly) the first table entry of its
   // row: its start may lie past the row's last entry.
@@ -293,7 +344,7 @@ __device__ __forceinline__ Item make_item(const AttnArgs& a, bool valid, int r, 
   return it;
 }
 
-// Largest r in [0, R) with pref[r] <= k, for pref strictly increasing with
+// Largest r in [0, R) with pref[r] <= k, for pref non-decreasing with
 // pref[0] = 0 <= k < pref[R]: each step tests 64 evenly spaced candidates
 // with one ballot, so R <= 4096 takes two steps.  Wave-uniform result.
 __device__ __forceinline__ int find_request(const int32_t* pref, int R, uint32_t k) {
@@ -312,7 +363,8 @@ __device__ __forceinline__ int find_request(const int32_t* pref, int R, uint32_t
   return lo;
 }
 
-// Work items are (request, KV head, partition).  Two schedules:
+// Work items are (request, KV head, [query-row group,] partition).  Two
+// schedules:
 //   * persistent (a.queue != nullptr): as many workgroups as fit on the GPU at
 //     once.  Items are numbered request by request, counting only the
 //     partitions that hold tokens (an empty context has one item, which
@@ -326,27 +378,36 @@ __device__ __forceinline__ int find_request(const int32_t* pref, int R, uint32_t
 //     counter, and every workgroup's final fetch has returned before it
 //     counts itself done, so no fetch can follow the reset.  Same-line
 //     atomics serialise, so the two counters sit on separate 128-byte lines.
-//   * one item per workgroup (more requests than the LDS prefix holds):
-//     (request, KV head) varies fastest; the hardware deals consecutive
-//     workgroups to the eight XCDs in turn, so every XCD gets an even share
-//     of the partitions that hold tokens, and the empty tail partitions of
-//     short requests come last.
+//   * one item per workgroup (decode path with more requests than the LDS
+//     prefix holds): (request, KV head) varies fastest; the hardware deals
+//     consecutive workgroups to the eight XCDs in turn, so every XCD gets an
+//     even share of the partitions that hold tokens, and the empty tail
+//     partitions of short requests come last.
 // Items are pipelined: near the end of an item's stream the next item's index
 // is fetched and its block-table slice and queries are loaded into registers;
 // the last iteration requests the next item's first rows, and when the stream
 // ends the slice and queries go to the other LDS buffer while the finished
 // item's wavefronts are combined and written.
-template <bool kBf16, int D, int G>
+//
+// QPI = 0: one query row per request (row r), every head of an item sees the
+// item's whole range.  QPI >= 1: QPI query rows of one request per item, each
+// with its own causal (and window) limits.
+template <bool kBf16, int D, int G, int QPI>
 __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
   using L = Layout<kBf16, D>;
-  using Smem = AttnSmem<kBf16, D, G>;
+  constexpr bool kVar = QPI > 0;
+  constexpr int kQ = kVar ? QPI : 1;                               // query rows per item
+  constexpr int VG = G * kQ;                                       // query vectors per item
+  using Smem = AttnSmem<kBf16, D, VG, kVar>;
   constexpr int kEpc = L::kEpc, kLpr = L::kLpr, kCpl = L::kCpl, kRpw = L::kRpw, kU = L::kU;
   constexpr int kIterTokens = L::kIterTokens;
   constexpr int kElemBytes = kBf16 ? 2 : 4;
   constexpr int kQChunks = Smem::kQChunks;
+  constexpr int kHeadChunks = D * kElemBytes / 16;                 // 16-byte chunks of one query vector
   constexpr int kTblPer = kMaxSliceBlocks / kThreads;               // table entries per thread
   constexpr int kQPer = (kQChunks + kThreads - 1) / kThreads;       // query chunks per thread
   static_assert(kMaxSliceBlocks % kThreads == 0, "slice staging");
+  static_assert(VG <= 8, "at most eight query vectors per item");
 
   __shared__ Smem sm;
   const int tid = threadIdx.x;
@@ -362,22 +423,44 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
   uint32_t* done_ctr = persistent ? a.queue + kQueueLineWords : nullptr;
   uint32_t total = 0, total_big = 0;
 
+  // Query rows of request r (several-query path), clamped to max_qlen.
+  auto qlen_of = [&](int r) -> int {
+    if constexpr (kVar) {
+      return min(max(sm.qs[r + 1] - sm.qs[r], 0), a.max_qlen);
+    } else {
+      return 1;
+    }
+  };
+
   if (persistent) {
-    // Clamped lengths, and the exclusive prefixes of the big items (pref) and
-    // of the small items (pref2) per request: all big items are numbered
-    // before all small ones.
+    // Clamped lengths (and first query rows), then the exclusive prefixes of
+    // the big items (pref) and of the small items (pref2) per request: all
+    // big items are numbered before all small ones.
     for (int i = tid; i < R; i += kThreads) {
       const int n = a.seq_lens[i];
       sm.len[i] = n < 0 ? 0 : (n > a.len_cap ? a.len_cap : n);
+    }
+    if constexpr (kVar) {
+      for (int i = tid; i <= R; i += kThreads) sm.qs[i] = min(max(a.qsl[i], 0), a.num_rows);
     }
     __syncthreads();
     const int per = (R + kThreads - 1) / kThreads;
     const int lo = min(tid * per, R);
     const int hi = min(lo + per, R);
+    auto counts = [&](int i, int& nb, int& ns) {
+      const int n = sm.len[i];
+      const int ql = qlen_of(i);
+      const int m = n - range_lo(n, ql, a.window);
+      const int groups = kVar ? (ql + kQ - 1) / kQ : 1;
+      nb = big_parts(m, a.part_tokens) * a.num_kv_heads * groups;
+      ns = small_parts(m, a.part_tokens) * a.num_kv_heads * groups;
+    };
     int local_b = 0, local_s = 0;
     for (int i = lo; i < hi; ++i) {
-      local_b += big_parts(sm.len[i], a.part_tokens);
-      local_s += small_parts(sm.len[i], a.part_tokens);
+      int nb, ns;
+      counts(i, nb, ns);
+      local_b += nb;
+      local_s += ns;
     }
     int incl_b = local_b, incl_s = local_s;
 #pragma unroll
@@ -400,23 +483,26 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
       run_s += sm.wsum[kWaves + w];
     }
     for (int i = lo; i < hi; ++i) {
-      sm.pref[i] = run_b * a.num_kv_heads;
-      sm.pref2[i] = run_s * a.num_kv_heads;
-      run_b += big_parts(sm.len[i], a.part_tokens);
-      run_s += small_parts(sm.len[i], a.part_tokens);
+      sm.pref[i] = run_b;
+      sm.pref2[i] = run_s;
+      int nb, ns;
+      counts(i, nb, ns);
+      run_b += nb;
+      run_s += ns;
     }
     if (tid == kThreads - 1) {
-      sm.pref[R] = run_b * a.num_kv_heads;
-      sm.pref2[R] = run_s * a.num_kv_heads;
+      sm.pref[R] = run_b;
+      sm.pref2[R] = run_s;
     }
     __syncthreads();
     total_big = static_cast<uint32_t>(uniform(sm.pref[R]));
     total = total_big + static_cast<uint32_t>(uniform(sm.pref2[R]));
   }
 
-  // Item number k of the persistent schedule.
+  // Item number k of the persistent schedule.  Within a request, the KV head
+  // varies fastest, then the query-row group, then the partition.
   auto item_at = [&](uint32_t k) -> Item {
-    if (k >= total) return make_item(a, false, 0, 0, 0, 0);
+    if (k >= total) return make_item(a, false, 0, 0, 0, 0, 0, 0, 0, 0);
     const uint32_t kk = reverse ? total - 1u - k : k;
     const bool big = kk < total_big;
     const int32_t* pref = big ? sm.pref : sm.pref2;
@@ -424,9 +510,21 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     const int r = find_request(pref, R, j);
     const int idx = static_cast<int>(j - static_cast<uint32_t>(pref[r]));
     const int n = sm.len[r];
-    const int sub = idx / a.num_kv_heads;
-    const int part = big ? sub : big_parts(n, a.part_tokens) + sub;
-    return make_item(a, true, r, idx - sub * a.num_kv_heads, part, n);
+    const int ql = qlen_of(r);
+    const int lo = range_lo(n, ql, a.window);
+    const int groups = kVar ? (ql + kQ - 1) / kQ : 1;
+    const int per = max(a.num_kv_heads * groups, 1);
+    const int sub = idx / per;
+    const int rem = idx - sub * per;
+    const int qgrp = rem / a.num_kv_heads;
+    const int g = rem - qgrp * a.num_kv_heads;
+    const int part = big ? sub : big_parts(n - lo, a.part_tokens) + sub;
+    if constexpr (kVar) {
+      return make_item(a, true, r, g, part, n, lo, sm.qs[r] + qgrp * kQ, min(kQ, ql - qgrp * kQ),
+                       n - ql + qgrp * kQ);
+    } else {
+      return make_item(a, true, r, g, part, n, lo, r, 1, n - 1);
+    }
   };
 
   // Block-table slice and queries of an item: loaded into registers (indices
@@ -451,11 +549,27 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
       st_nb[u] = valid_block(row_table[j < it.end ? (j >> a.bs_shift) : it.first_blk]);
     }
     st_nb0 = valid_block(table[0]);
-    const uint4* qg = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
-                                                     (static_cast<int64_t>(it.r) * a.num_q_heads + it.g * G) * D *
-                                                         kElemBytes);
+    if constexpr (kVar) {
+      // Query vector v = i*G + h is head g*G+h of row row0+i; rows past the
+      // item's nq repeat its last row (loaded, never used).
 #pragma unroll
-    for (int j = 0; j < kQPer; ++j) st_q[j] = qg[min(tid + j * kThreads, kQChunks - 1)];
+      for (int j = 0; j < kQPer; ++j) {
+        const int c = min(tid + j * kThreads, kQChunks - 1);
+        const int v = c / kHeadChunks;
+        const int i = v / G;
+        const int qrow = it.row0 + max(0, min(i, it.nq - 1));
+        const uint4* qg = reinterpret_cast<const uint4*>(
+            static_cast<const char*>(a.q) +
+            ((static_cast<int64_t>(qrow) * a.num_q_heads + it.g * G + (v - i * G)) * D) * kElemBytes);
+        st_q[j] = qg[c - v * kHeadChunks];
+      }
+    } else {
+      const uint4* qg = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
+                                                       (static_cast<int64_t>(it.r) * a.num_q_heads + it.g * G) * D *
+                                                           kElemBytes);
+#pragma unroll
+      for (int j = 0; j < kQPer; ++j) st_q[j] = qg[min(tid + j * kThreads, kQChunks - 1)];
+    }
   };
   auto stage_store = [&](const Item& it, int buf) {
 #pragma unroll
@@ -490,6 +604,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
       const bool in_range = j < it.end;
       const int blk = sm.blocks[buf][((in_range ? j : it.start) >> a.bs_shift) - it.first_blk];
       rs.valid[u] = in_range && blk >= 0;
+      rs.pos[u] = j;
       const int64_t off = rs.valid[u] ? (static_cast<int64_t>(blk) * a.block_stride +
                                          static_cast<int64_t>(j & off_mask) * D) * kElemBytes
                                       : dummy_off;
@@ -525,6 +640,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
       const int lds_blk = sm.blocks[buf][((in_range && !to_nx ? j : it.start) >> a.bs_shift) - it.first_blk];
       const int blk = to_nx ? st_nb[u] : lds_blk;
       rs.valid[u] = in_range && blk >= 0;
+      rs.pos[u] = j;
       const int64_t off = rs.valid[u] ? (static_cast<int64_t>(blk) * a.block_stride +
                                          static_cast<int64_t>(j & off_mask) * D) * kElemBytes
                                       : dummy_off;
@@ -537,13 +653,24 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     }
   };
 
-  float acc[G][kCpl][kEpc];
-  float m[G], lsum[G];
+  float acc[VG][kCpl][kEpc];
+  float m[VG], lsum[VG];
+  // Several-query path: keys [qlo[i], qhi[i]) are visible to the item's
+  // query row i (its causal limit and window); empty for rows past nq.
+  int qlo[kQ], qhi[kQ];
+  auto set_limits = [&](const Item& it) {
+#pragma unroll
+    for (int i = 0; i < kQ; ++i) {
+      const int p = it.pbase + i;
+      qhi[i] = i < it.nq ? p + 1 : 0;
+      qlo[i] = a.window > 0 ? p - a.window + 1 : 0;
+    }
+  };
 
   auto compute = [&](const RowSet<kBf16, D>& rs, int buf) {
-    float s[kU][G];
+    float s[kU][VG];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < VG; ++h) {
       uint4 qh[kCpl];
 #pragma unroll
       for (int i = 0; i < kCpl; ++i) qh[i] = sm.q[buf][(h * D + (cl + kLpr * i) * kEpc) * kElemBytes / 16];
@@ -553,12 +680,17 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < kCpl; ++i) t = chunk_dot<kBf16>(qh[i], rs.k[u][i], t);
         t = group_sum<kLpr>(t);
-        s[u][h] = rs.valid[u] ? t * a.scale_log2 : -INFINITY;
+        bool ok = rs.valid[u];
+        if constexpr (kVar) {
+          const int qi = h / G;
+          ok = ok && rs.pos[u] >= qlo[qi] && rs.pos[u] < qhi[qi];
+        }
+        s[u][h] = ok ? t * a.scale_log2 : -INFINITY;
       }
     }
     // Lazy running maximum per row group and head.
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = 0; h < VG; ++h) {
       float cand = s[0][h];
 #pragma unroll
       for (int u = 1; u < kU; ++u) cand = fmaxf(cand, s[u][h]);
@@ -574,9 +706,9 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      float p[G];
+      float p[VG];
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+      for (int h = 0; h < VG; ++h) {
         p[h] = fast_exp2(s[u][h] - m[h]);
         lsum[h] += p[h];
       }
@@ -589,7 +721,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
         for (int e = 0; e < kEpc; ++e) {
           const float x = chunk_elem<kBf16>(vc, e);
 #pragma unroll
-          for (int h = 0; h < G; ++h) acc[h][i][e] = fmaf(p[h], x, acc[h][i][e]);
+          for (int h = 0; h < VG; ++h) acc[h][i][e] = fmaf(p[h], x, acc[h][i][e]);
         }
       }
     }
@@ -611,8 +743,9 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     const int r = static_cast<int>(rg / a.num_kv_heads);
     int n = a.seq_lens[r];
     n = n < 0 ? 0 : (n > a.len_cap ? a.len_cap : n);
-    cur = make_item(a, true, r, static_cast<int>(rg % a.num_kv_heads), part, n);
-    nxt = make_item(a, false, 0, 0, 0, 0);
+    cur = make_item(a, true, r, static_cast<int>(rg % a.num_kv_heads), part, n, range_lo(n, 1, a.window), r, 1,
+                    n - 1);
+    nxt = make_item(a, false, 0, 0, 0, 0, 0, 0, 0, 0);
   }
 
   RowSet<kBf16, D> buf_a, buf_b;
@@ -658,8 +791,9 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     };
 
     if (cur.num_blk > 0) {
+      if constexpr (kVar) set_limits(cur);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
+      for (int h = 0; h < VG; ++h) {
         m[h] = kInitMax;
         lsum[h] = 0.0f;
 #pragma unroll
@@ -694,7 +828,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int mask = kLpr; mask < 64; mask <<= 1) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
+        for (int h = 0; h < VG; ++h) {
           const float mo = __shfl_xor(m[h], mask, 64);
           const float lo = __shfl_xor(lsum[h], mask, 64);
           const float mx = fmaxf(m[h], mo);
@@ -713,7 +847,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
       }
       if (row == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
+        for (int h = 0; h < VG; ++h) {
 #pragma unroll
           for (int i = 0; i < kCpl; ++i)
 #pragma unroll
@@ -735,13 +869,23 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     if (nxt.valid) stage_store(nxt, lb ^ 1);
     __syncthreads();
 
-    const int64_t rh0 = static_cast<int64_t>(cur.r) * a.num_q_heads + cur.g * G;
+    // Output slot of query vector v of the item (-1: a padding row).
+    auto out_row = [&](int v) -> int64_t {
+      if constexpr (kVar) {
+        const int i = v / G;
+        return i < cur.nq ? static_cast<int64_t>(cur.row0 + i) * a.num_q_heads + cur.g * G + (v - i * G) : -1;
+      } else {
+        return static_cast<int64_t>(cur.r) * a.num_q_heads + cur.g * G + v;
+      }
+    };
     if (cur.num_blk > 0) {
       // Combine the four wavefronts, then finish (one partition) or publish.
-      const int np_r = parts_of(cur.n, a.part_tokens);
-      for (int e = tid; e < G * D; e += kThreads) {
+      const int np_r = parts_of(cur.n - cur.lo, a.part_tokens);
+      for (int e = tid; e < VG * D; e += kThreads) {
         const int h = e / D;
         const int d = e - h * D;
+        const int64_t rh = out_row(h);
+        if (rh < 0) continue;
         float mx = sm.ml[0][h][0];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm.ml[w][h][0]);
@@ -752,7 +896,6 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
           den = fmaf(f, sm.ml[w][h][1], den);
           num = fmaf(f, sm.acc[w][h][d], num);
         }
-        const int64_t rh = rh0 + h;
         if (np_r == 1) {
           a.out[rh * D + d] = den == 0.0f ? 0.0f : num / den;
         } else {
@@ -767,7 +910,11 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     } else if (cur.n == 0 && cur.part == 0) {
       // An empty context answers zeros (partitions past the end of a
       // non-empty context, one-item-per-workgroup schedule only, do nothing).
-      for (int i = tid; i < G * D; i += kThreads) a.out[rh0 * D + i] = 0.0f;
+      for (int e = tid; e < VG * D; e += kThreads) {
+        const int h = e / D;
+        const int64_t rh = out_row(h);
+        if (rh >= 0) a.out[rh * D + (e - h * D)] = 0.0f;
+      }
     }
     __syncthreads();                           // sm.acc, sm.ml and sm.next are reused
 
@@ -838,11 +985,11 @@ struct WorkspaceLayout {
   int64_t total = 0;
 };
 
-WorkspaceLayout workspace_layout(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t num_parts) {
+WorkspaceLayout workspace_layout(int32_t num_rows, int32_t num_q_heads, int32_t head_dim, int32_t num_parts) {
   WorkspaceLayout w;
   w.total = kQueueHeaderBytes;
   if (num_parts <= 1) return w;
-  const int64_t slots = static_cast<int64_t>(num_seqs) * num_q_heads * num_parts;
+  const int64_t slots = static_cast<int64_t>(num_rows) * num_q_heads * num_parts;
   w.acc_offset = kQueueHeaderBytes;
   w.ml_offset = yoco::round_up(w.acc_offset + slots * head_dim * 4, 256);
   w.total = w.ml_offset + slots * 2 * 4;
@@ -867,52 +1014,215 @@ int resident_workgroups(const void* kernel, int per_cu_query(int*)) {
   return cus * per_cu;
 }
 
-template <bool kBf16, int D, int G>
+template <bool kBf16, int D, int G, int QPI>
 int per_cu_workgroups(int* out) {
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, cross_attn_kernel<kBf16, D, G>, kThreads, 0) == hipSuccess
-             ? 0 : 1;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, cross_attn_kernel<kBf16, D, G, QPI>, kThreads, 0) ==
+                 hipSuccess ? 0 : 1;
 }
 
 // Launch the attention kernel: persistent (grid = resident workgroups, at
 // most one per work item) when the requests fit the LDS prefix, else one
 // workgroup per work item.  Returns false if the occupancy query failed.
-template <bool kBf16, int D, int G>
+template <bool kBf16, int D, int G, int QPI>
 bool launch(AttnArgs a, int64_t items, hipStream_t stream) {
   int64_t grid = items;
   if (a.queue != nullptr) {
-    const int slots = resident_workgroups(reinterpret_cast<const void*>(cross_attn_kernel<kBf16, D, G>),
-                                          per_cu_workgroups<kBf16, D, G>);
+    const int slots = resident_workgroups(reinterpret_cast<const void*>(cross_attn_kernel<kBf16, D, G, QPI>),
+                                          per_cu_workgroups<kBf16, D, G, QPI>);
     if (slots <= 0) return false;
     grid = items < slots ? items : slots;
   }
-  hipLaunchKernelGGL((cross_attn_kernel<kBf16, D, G>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, stream,
-                     a);
+  hipLaunchKernelGGL((cross_attn_kernel<kBf16, D, G, QPI>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0,
+                     stream, a);
   return true;
 }
 
+// Query rows per work item: 0 for the decode kernel (one row per request);
+// with query_start_loc, 8/G rows (eight query vectors per item) when a request
+// may have more than one row, else 1.
+template <bool kBf16, int D, int G>
+int dispatch_rows(int qpi, const AttnArgs& a, int64_t items, hipStream_t stream) {
+  constexpr int kWide = 8 / G;
+  if (qpi == 0) return launch<kBf16, D, G, 0>(a, items, stream) ? 1 : -1;
+  if (qpi == 1) return launch<kBf16, D, G, 1>(a, items, stream) ? 1 : -1;
+  if constexpr (kWide > 1) {
+    if (qpi == kWide) return launch<kBf16, D, G, kWide>(a, items, stream) ? 1 : -1;
+  }
+  return 0;
+}
+
 template <bool kBf16, int D>
-int dispatch_group(int group, const AttnArgs& a, int64_t items, hipStream_t stream) {
+int dispatch_group(int group, int qpi, const AttnArgs& a, int64_t items, hipStream_t stream) {
   switch (group) {
-    case 1: return launch<kBf16, D, 1>(a, items, stream) ? 1 : -1;
-    case 2: return launch<kBf16, D, 2>(a, items, stream) ? 1 : -1;
-    case 4: return launch<kBf16, D, 4>(a, items, stream) ? 1 : -1;
-    case 8: return launch<kBf16, D, 8>(a, items, stream) ? 1 : -1;
+    case 1: return dispatch_rows<kBf16, D, 1>(qpi, a, items, stream);
+    case 2: return dispatch_rows<kBf16, D, 2>(qpi, a, items, stream);
+    case 4: return dispatch_rows<kBf16, D, 4>(qpi, a, items, stream);
+    case 8: return dispatch_rows<kBf16, D, 8>(qpi, a, items, stream);
     default: return 0;
   }
 }
 
 // 1: launched, 0: no kernel for the shape, -1: the occupancy query failed.
 template <bool kBf16>
-int dispatch_dim(int head_dim, int group, const AttnArgs& a, int64_t items, hipStream_t stream) {
+int dispatch_dim(int head_dim, int group, int qpi, const AttnArgs& a, int64_t items, hipStream_t stream) {
   switch (head_dim) {
-    case 64: return dispatch_group<kBf16, 64>(group, a, items, stream);
-    case 128: return dispatch_group<kBf16, 128>(group, a, items, stream);
-    case 256: return dispatch_group<kBf16, 256>(group, a, items, stream);
+    case 64: return dispatch_group<kBf16, 64>(group, qpi, a, items, stream);
+    case 128: return dispatch_group<kBf16, 128>(group, qpi, a, items, stream);
+    case 256: return dispatch_group<kBf16, 256>(group, qpi, a, items, stream);
     default: return 0;
   }
 }
 
 bool supported_dim(int d) { return d == 64 || d == 128 || d == 256; }
+
+// Length the partitions of the longest context cover: with a window, a
+// request's queries see at most window + max_query_len - 1 positions.
+int32_t effective_len(int32_t max_seq_len, int32_t max_qlen, int32_t window) {
+  if (window <= 0) return max_seq_len;
+  const int64_t span = static_cast<int64_t>(window) + (max_qlen > 1 ? max_qlen : 1) - 1;
+  return static_cast<int32_t>(span < max_seq_len ? span : max_seq_len);
+}
+
+struct AttnCall {
+  int32_t dtype;
+  const void* q;
+  int32_t num_rows;
+  const int32_t* qsl;
+  int32_t num_seqs;
+  int32_t max_qlen;
+  int32_t num_q_heads;
+  const void* k_cache;
+  const void* v_cache;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t block_size;
+  int32_t head_dim;
+  const int32_t* block_table;
+  int32_t max_blocks_per_seq;
+  const int32_t* seq_lens;
+  int32_t max_seq_len;
+  int32_t window;
+  float scale;
+  int32_t partition_tokens;
+  uint32_t flags;
+  float* out;
+  void* workspace;
+  int64_t workspace_bytes;
+  void* stream;
+};
+
+int32_t run_cross_attn(const AttnCall& c, const char* who) {
+  using namespace yoco;
+  if (c.dtype != YOCO_DTYPE_F32 && c.dtype != YOCO_DTYPE_BF16)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: unknown dtype %d", who, c.dtype);
+  if (c.num_seqs < 0 || c.num_rows < 0 || c.num_q_heads <= 0 || c.num_kv_heads <= 0 || c.num_blocks <= 0 ||
+      c.max_blocks_per_seq <= 0 || c.max_seq_len < 0 || c.partition_tokens < 0 || c.workspace_bytes < 0 ||
+      c.window < 0 || c.max_qlen < 0)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: negative or zero size argument", who);
+  if (c.qsl == nullptr && (c.num_rows != c.num_seqs || c.max_qlen != 1))
+    return fail(YOCO_ERR_INVALID_ARGUMENT,
+                "%s: without query_start_loc there is one query row per request (num_rows %d, num_seqs %d, "
+                "max_query_len %d)", who, c.num_rows, c.num_seqs, c.max_qlen);
+  if (c.num_q_heads % c.num_kv_heads != 0)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", who,
+                c.num_q_heads, c.num_kv_heads);
+  if ((c.flags & ~YOCO_FLAG_REVERSE_ORDER) != 0) return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: unknown flags", who);
+  if (!std::isfinite(c.scale)) return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: scale is not finite", who);
+  if (c.partition_tokens % 64 != 0)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: partition_tokens %d is not a multiple of 64", who,
+                c.partition_tokens);
+  if (c.k_scale != nullptr || c.v_scale != nullptr)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: cache scales are only read for an 8-bit cache", who);
+  const int group = c.num_q_heads / c.num_kv_heads;
+  if (!supported_dim(c.head_dim))
+    return fail(YOCO_ERR_UNSUPPORTED, "%s: head_dim %d not in {64,128,256}", who, c.head_dim);
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(YOCO_ERR_UNSUPPORTED, "%s: %d query heads per KV head not in {1,2,4,8}", who, group);
+  if (!is_pow2(c.block_size) || c.block_size > 256)
+    return fail(YOCO_ERR_UNSUPPORTED, "%s: block_size %d is not a power of two <= 256", who, c.block_size);
+  if (c.partition_tokens > max_partition(c.block_size))
+    return fail(YOCO_ERR_UNSUPPORTED, "%s: partition_tokens %d exceeds %d for block_size %d", who,
+                c.partition_tokens, max_partition(c.block_size), c.block_size);
+  if (c.qsl != nullptr && c.num_seqs > kMaxQueueSeqs)
+    return fail(YOCO_ERR_UNSUPPORTED, "%s: %d requests with query_start_loc exceed %d", who, c.num_seqs,
+                kMaxQueueSeqs);
+  if (c.num_seqs == 0 || c.num_rows == 0 || c.max_qlen == 0) return YOCO_OK;
+  if (c.q == nullptr || c.k_cache == nullptr || c.v_cache == nullptr || c.block_table == nullptr ||
+      c.seq_lens == nullptr || c.out == nullptr)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: null pointer", who);
+  if (!aligned16(c.q) || !aligned16(c.k_cache) || !aligned16(c.v_cache) || !aligned16(c.out))
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: q, caches and out must be 16-byte aligned", who);
+
+  const int32_t span = effective_len(c.max_seq_len, c.max_qlen, c.window);
+  const int32_t part = resolve_partition(c.num_seqs, c.num_kv_heads, c.head_dim, span, c.block_size,
+                                         c.partition_tokens);
+  const int32_t nparts = num_partitions(span, part);
+  if (nparts > kMaxParts)
+    return fail(YOCO_ERR_UNSUPPORTED, "%s: %d partitions per request exceed %d", who, nparts, kMaxParts);
+  const int qpi = c.qsl == nullptr ? 0 : (c.max_qlen > 1 ? 8 / group : 1);
+  const int64_t groups = qpi == 0 ? 1 : yoco::ceil_div(c.max_qlen, qpi);
+  const int64_t items = static_cast<int64_t>(c.num_seqs) * c.num_kv_heads * groups * nparts;
+  if (items > 0x7fffffffLL)
+    return fail(YOCO_ERR_UNSUPPORTED, "%s: %lld work items is too many", who, (long long)items);
+  const WorkspaceLayout ws = workspace_layout(c.num_rows, c.num_q_heads, c.head_dim, nparts);
+  if (c.workspace_bytes < ws.total)
+    return fail(YOCO_ERR_WORKSPACE_TOO_SMALL, "%s: workspace %lld bytes, need %lld", who,
+                (long long)c.workspace_bytes, (long long)ws.total);
+  if (c.workspace == nullptr || !aligned16(c.workspace))
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: workspace must be a 16-byte aligned pointer", who);
+  const int64_t merge_grid = static_cast<int64_t>(c.num_seqs) * c.max_qlen * c.num_q_heads;
+  if (nparts > 1 && merge_grid > 0x7fffffffLL)
+    return fail(YOCO_ERR_UNSUPPORTED, "%s: merge grid of %lld workgroups is too many", who, (long long)merge_grid);
+
+  AttnArgs a;
+  a.q = c.q;
+  a.k = c.k_cache;
+  a.v = c.v_cache;
+  a.block_table = c.block_table;
+  a.seq_lens = c.seq_lens;
+  a.out = c.out;
+  char* wsb = static_cast<char*>(c.workspace);
+  a.ws_acc = nparts > 1 ? reinterpret_cast<float*>(wsb + ws.acc_offset) : nullptr;
+  a.ws_ml = nparts > 1 ? reinterpret_cast<float*>(wsb + ws.ml_offset) : nullptr;
+  a.queue = c.num_seqs <= kMaxQueueSeqs ? reinterpret_cast<uint32_t*>(wsb) : nullptr;
+  a.head_stride = c.block_size * c.head_dim;
+  a.block_stride = static_cast<int64_t>(c.num_kv_heads) * c.block_size * c.head_dim;
+  a.num_seqs = c.num_seqs;
+  a.num_q_heads = c.num_q_heads;
+  a.num_kv_heads = c.num_kv_heads;
+  a.num_blocks = c.num_blocks;
+  a.block_size = c.block_size;
+  a.bs_shift = ilog2(c.block_size);
+  a.max_blocks = c.max_blocks_per_seq;
+  const int64_t cap = static_cast<int64_t>(c.max_blocks_per_seq) * c.block_size;
+  a.len_cap = static_cast<int32_t>(cap < c.max_seq_len ? cap : c.max_seq_len);
+  a.part_tokens = part;
+  a.num_parts = nparts;
+  a.scale_log2 = c.scale * kLog2e;
+  a.flags = c.flags;
+  a.qsl = c.qsl;
+  a.num_rows = c.num_rows;
+  a.max_qlen = c.max_qlen;
+  a.window = c.window;
+
+  hipStream_t s = static_cast<hipStream_t>(c.stream);
+  clear_launch_error();
+  const int launched = c.dtype == YOCO_DTYPE_BF16 ? dispatch_dim<true>(c.head_dim, group, qpi, a, items, s)
+                                                  : dispatch_dim<false>(c.head_dim, group, qpi, a, items, s);
+  if (launched == 0) return fail(YOCO_ERR_UNSUPPORTED, "%s: no kernel for this shape", who);
+  if (launched < 0) return fail(YOCO_ERR_HIP, "%s: occupancy query failed on the current device", who);
+  if (nparts > 1) {
+    const uint32_t mgrid = static_cast<uint32_t>(merge_grid);
+    switch (c.head_dim) {
+      case 64: hipLaunchKernelGGL(cross_attn_merge_kernel<64>, dim3(mgrid), dim3(kThreads), 0, s, a); break;
+      case 128: hipLaunchKernelGGL(cross_attn_merge_kernel<128>, dim3(mgrid), dim3(kThreads), 0, s, a); break;
+      default: hipLaunchKernelGGL(cross_attn_merge_kernel<256>, dim3(mgrid), dim3(kThreads), 0, s, a); break;
+    }
+  }
+  return launch_result(who);
+}
 
 }  // namespace
 
@@ -933,6 +1243,19 @@ extern "C" int64_t yoco_cross_attn_workspace_size(int32_t num_seqs, int32_t num_
   return workspace_layout(num_seqs, num_q_heads, head_dim, num_partitions(max_seq_len, p)).total;
 }
 
+extern "C" int64_t yoco_cross_attn_varlen_workspace_size(int32_t num_rows, int32_t num_seqs, int32_t num_q_heads,
+                                                         int32_t num_kv_heads, int32_t head_dim,
+                                                         int32_t max_seq_len, int32_t max_query_len,
+                                                         int32_t window, int32_t block_size,
+                                                         int32_t partition_tokens) {
+  if (num_rows < 0 || num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0 ||
+      max_query_len < 0 || window < 0 || block_size <= 0 || partition_tokens < 0)
+    return -1;
+  const int32_t span = effective_len(max_seq_len, max_query_len, window);
+  const int32_t p = resolve_partition(num_seqs, num_kv_heads, head_dim, span, block_size, partition_tokens);
+  return workspace_layout(num_rows, num_q_heads, head_dim, num_partitions(span, p)).total;
+}
+
 extern "C" int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seqs, int32_t num_q_heads,
                                    const void* k_cache, const void* v_cache, int32_t num_blocks,
                                    int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
@@ -940,88 +1263,24 @@ extern "C" int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seq
                                    const int32_t* seq_lens, int32_t max_seq_len, float scale,
                                    int32_t partition_tokens, uint32_t flags, float* out, void* workspace,
                                    int64_t workspace_bytes, void* stream) {
-  using namespace yoco;
-  if (dtype != YOCO_DTYPE_F32 && dtype != YOCO_DTYPE_BF16)
-    return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: unknown dtype %d", dtype);
-  if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
-      max_seq_len < 0 || partition_tokens < 0 || workspace_bytes < 0)
-    return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: negative or zero size argument");
-  if (num_q_heads % num_kv_heads != 0)
-    return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: num_q_heads %d is not a multiple of num_kv_heads %d",
-                num_q_heads, num_kv_heads);
-  if ((flags & ~YOCO_FLAG_REVERSE_ORDER) != 0) return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: unknown flags");
-  if (!std::isfinite(scale)) return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: scale is not finite");
-  if (partition_tokens % 64 != 0)
-    return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: partition_tokens %d is not a multiple of 64", partition_tokens);
-  const int group = num_q_heads / num_kv_heads;
-  if (!supported_dim(head_dim)) return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: head_dim %d not in {64,128,256}", head_dim);
-  if (group != 1 && group != 2 && group != 4 && group != 8)
-    return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: %d query heads per KV head not in {1,2,4,8}", group);
-  if (!is_pow2(block_size) || block_size > 256)
-    return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: block_size %d is not a power of two <= 256", block_size);
-  if (partition_tokens > max_partition(block_size))
-    return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: partition_tokens %d exceeds %d for block_size %d",
-                partition_tokens, max_partition(block_size), block_size);
-  if (num_seqs == 0) return YOCO_OK;
-  if (q == nullptr || k_cache == nullptr || v_cache == nullptr || block_table == nullptr || seq_lens == nullptr ||
-      out == nullptr)
-    return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: null pointer");
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
-    return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: q, caches and out must be 16-byte aligned");
+  const AttnCall c{dtype, q, num_seqs, nullptr, num_seqs, 1, num_q_heads, k_cache, v_cache, nullptr, nullptr,
+                   num_blocks, num_kv_heads, block_size, head_dim, block_table, max_blocks_per_seq, seq_lens,
+                   max_seq_len, 0, scale, partition_tokens, flags, out, workspace, workspace_bytes, stream};
+  return run_cross_attn(c, "cross_attn");
+}
 
-  const int32_t part = resolve_partition(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens);
-  const int32_t nparts = num_partitions(max_seq_len, part);
-  if (nparts > kMaxParts)
-    return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: %d partitions per request exceed %d", nparts, kMaxParts);
-  const int64_t items = static_cast<int64_t>(num_seqs) * num_kv_heads * nparts;
-  if (items > 0x7fffffffLL) return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: %lld work items is too many", (long long)items);
-  const WorkspaceLayout ws = workspace_layout(num_seqs, num_q_heads, head_dim, nparts);
-  if (workspace_bytes < ws.total)
-    return fail(YOCO_ERR_WORKSPACE_TOO_SMALL, "cross_attn: workspace %lld bytes, need %lld",
-                (long long)workspace_bytes, (long long)ws.total);
-  if (workspace == nullptr || !aligned16(workspace))
-    return fail(YOCO_ERR_INVALID_ARGUMENT, "cross_attn: workspace must be a 16-byte aligned pointer");
-
-  AttnArgs a;
-  a.q = q;
-  a.k = k_cache;
-  a.v = v_cache;
-  a.block_table = block_table;
-  a.seq_lens = seq_lens;
-  a.out = out;
-  char* wsb = static_cast<char*>(workspace);
-  a.ws_acc = nparts > 1 ? reinterpret_cast<float*>(wsb + ws.acc_offset) : nullptr;
-  a.ws_ml = nparts > 1 ? reinterpret_cast<float*>(wsb + ws.ml_offset) : nullptr;
-  a.queue = num_seqs <= kMaxQueueSeqs ? reinterpret_cast<uint32_t*>(wsb) : nullptr;
-  a.head_stride = block_size * head_dim;
-  a.block_stride = static_cast<int64_t>(num_kv_heads) * block_size * head_dim;
-  a.num_seqs = num_seqs;
-  a.num_q_heads = num_q_heads;
-  a.num_kv_heads = num_kv_heads;
-  a.num_blocks = num_blocks;
-  a.block_size = block_size;
-  a.bs_shift = ilog2(block_size);
-  a.max_blocks = max_blocks_per_seq;
-  const int64_t cap = static_cast<int64_t>(max_blocks_per_seq) * block_size;
-  a.len_cap = static_cast<int32_t>(cap < max_seq_len ? cap : max_seq_len);
-  a.part_tokens = part;
-  a.num_parts = nparts;
-  a.scale_log2 = scale * kLog2e;
-  a.flags = flags;
-
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  clear_launch_error();
-  const int launched = dtype == YOCO_DTYPE_BF16 ? dispatch_dim<true>(head_dim, group, a, items, s)
-                                                : dispatch_dim<false>(head_dim, group, a, items, s);
-  if (launched == 0) return fail(YOCO_ERR_UNSUPPORTED, "cross_attn: no kernel for this shape");
-  if (launched < 0) return fail(YOCO_ERR_HIP, "cross_attn: occupancy query failed on the current device");
-  if (nparts > 1) {
-    const uint32_t mgrid = static_cast<uint32_t>(static_cast<int64_t>(num_seqs) * num_q_heads);
-    switch (head_dim) {
-      case 64: hipLaunchKernelGGL(cross_attn_merge_kernel<64>, dim3(mgrid), dim3(kThreads), 0, s, a); break;
-      case 128: hipLaunchKernelGGL(cross_attn_merge_kernel<128>, dim3(mgrid), dim3(kThreads), 0, s, a); break;
-      default: hipLaunchKernelGGL(cross_attn_merge_kernel<256>, dim3(mgrid), dim3(kThreads), 0, s, a); break;
-    }
-  }
-  return launch_result("cross_attn");
+extern "C" int32_t yoco_cross_attn_varlen(int32_t dtype, const void* q, int32_t num_rows,
+                                          const int32_t* query_start_loc, int32_t num_seqs, int32_t max_query_len,
+                                          int32_t num_q_heads, const void* k_cache, const void* v_cache,
+                                          const float* k_scale, const float* v_scale, int32_t num_blocks,
+                                          int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                                          const int32_t* block_table, int32_t max_blocks_per_seq,
+                                          const int32_t* seq_lens, int32_t max_seq_len, int32_t window,
+                                          float scale, int32_t partition_tokens, uint32_t flags, float* out,
+                                          void* workspace, int64_t workspace_bytes, void* stream) {
+  const AttnCall c{dtype, q, num_rows, query_start_loc, num_seqs, max_query_len, num_q_heads, k_cache, v_cache,
+                   k_scale, v_scale, num_blocks, num_kv_heads, block_size, head_dim, block_table,
+                   max_blocks_per_seq, seq_lens, max_seq_len, window, scale, partition_tokens, flags, out,
+                   workspace, workspace_bytes, stream};
+  return run_cross_attn(c, "cross_attn_varlen");
 }

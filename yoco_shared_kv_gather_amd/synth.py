@@ -235,6 +235,30 @@ def make_custom_metadata(geom: Geometry, seq_lens, seed: int = SEED_BASE, spare_
                     poison_block=poison)
 
 
+def make_varlen_metadata(geom: Geometry, seq_lens, query_lens, seed: int = SEED_BASE, tag: int = 98) -> Metadata:
+    """A batch where request r has query_lens[r] query rows (its newest
+    positions, as under speculative decoding) over seq_lens[r] cached tokens;
+    blocks handed out as in make_custom_metadata.  A request may have more
+    rows than cached tokens or none at all."""
+    base = make_custom_metadata(geom, seq_lens, seed=seed, tag=tag)
+    qlens = np.asarray(query_lens, dtype=np.int32)
+    cu = np.zeros(len(qlens) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(qlens)
+    bs = geom.block_size
+    slots = np.full(int(cu[-1]), -1, dtype=np.int32)
+    for r in range(len(qlens)):
+        n = int(base.seq_lens[r])
+        for i in range(int(qlens[r])):
+            pos = n - int(qlens[r]) + i
+            if pos >= 0:
+                slots[cu[r] + i] = base.block_table[r, pos // bs] * bs + pos % bs
+    base.query_lens = qlens
+    base.cu_seqlens = cu
+    base.num_tokens = int(cu[-1])
+    base.slot_mapping = slots
+    return base
+
+
 def live_slot_mask(meta: Metadata) -> np.ndarray:
     """bool [num_blocks][block_size]: True for slots inside some context."""
     bs = meta.geom.block_size
@@ -318,12 +342,14 @@ def make_cache(meta: Metadata, device="cpu", seed: int = SEED_BASE):
     return k, v
 
 
-def make_queries(meta: Metadata, device="cpu", seed: int = SEED_BASE, num_layers: Optional[int] = None):
-    """q for every cross layer: ``[L][R][Hq][D]`` N(0,1) in the workload dtype."""
+def make_queries(meta: Metadata, device="cpu", seed: int = SEED_BASE, num_layers: Optional[int] = None,
+                 rows: Optional[int] = None):
+    """q for every cross layer: ``[L][rows][Hq][D]`` N(0,1) in the workload
+    dtype; rows defaults to one per request."""
     geom = meta.geom
     ss = _seed_seq(meta.config_id, meta.size, seed)
     layers = geom.num_layers if num_layers is None else num_layers
-    shape = (layers, meta.num_reqs, geom.num_q_heads, geom.head_dim)
+    shape = (layers, meta.num_reqs if rows is None else rows, geom.num_q_heads, geom.head_dim)
     return _randn(shape, torch_dtype(geom), device, _child_seed(ss, _S_Q))
 
 
