@@ -9,9 +9,9 @@ starts where the previous one ended in the last-level cache).
 Default workload: decode64 -- 64 decoding requests with contexts drawn from
 U{1024..8192}, bf16 cache of 2 KV heads x 256 dims in blocks of 16, 10 cross
 layers of 8 query heads, hidden 2048.  Inputs are synthetic and seeded and sit
-in HBM before timing starts.  Between steps a 512 MiB buffer is written so the
-256 MB last-level cache starts cold each step (other model work would evict
-it); that write is outside the step's events.
+in HBM before timing starts.  Between steps a 1 GiB buffer is read so the
+L2s and the 256 MB last-level cache start cold each step (other model work
+would evict them); that read is outside the step's events.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", type=int, default=2, help="synthetic workload id (1-5); 2 = decode64")
     p.add_argument("--partition-tokens", type=int, default=0, help="0 = library default")
+    p.add_argument("--query-rows", type=int, default=1, help="query rows per request (decode workloads 2, 3, 5)")
+    p.add_argument("--window", type=int, default=0, help="sliding window of every cross layer in tokens (0 = none)")
     p.add_argument("--no-flush", action="store_true", help="keep the last-level cache warm between steps")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -70,7 +72,7 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
-def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s):
+def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s, rows_per_req=1, window=0):
     """Time the float64 oracle on host cores on a bounded sample of the same
     step: the append and gather of all scheduled tokens, then whole cross
     layers (every request) until the time budget is spent; the per-layer
@@ -83,6 +85,7 @@ def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s):
     geom = meta.geom
     scale = 1.0 / math.sqrt(geom.head_dim)
     bs = geom.block_size
+    Q = rows_per_req
     w_host = (w_rms.float().cpu().numpy(), w_k.float().cpu().numpy(), w_v.float().cpu().numpy())
     x_host = x.float().cpu().numpy()
     per_req = []
@@ -95,7 +98,12 @@ def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s):
     with threadpoolctl.threadpool_limits(limits=1):
         t0 = time.perf_counter()
         oracle.kv_project(x_host, w_host[0], 1e-6, w_host[1], w_host[2], geom.num_kv_heads, geom.head_dim)
-        oracle.gather_last(x_host, meta.cu_seqlens)
+        if Q > 1:
+            idx = np.arange(meta.num_tokens)
+            oracle.cross_metadata(idx, meta.cu_seqlens)
+            oracle.gather_rows(x_host, idx)
+        else:
+            oracle.gather_last(x_host, meta.cu_seqlens)
         t_other = time.perf_counter() - t0
         layers = 0
         t_attn = 0.0
@@ -103,12 +111,17 @@ def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s):
             t1 = time.perf_counter()
             qh = q[layers].float().cpu().numpy()
             for r, (n, nb, kc, vc) in enumerate(per_req):
-                oracle.cross_attention(qh[r:r + 1], kc, vc, np.arange(max(nb, 1))[None, :], np.array([n]), scale)
+                table = np.arange(max(nb, 1))[None, :]
+                if Q > 1 or window > 0:
+                    oracle.cross_attention_varlen(qh[r * Q:(r + 1) * Q], kc, vc, table, np.array([n]),
+                                                  np.array([0, Q]), scale, window)
+                else:
+                    oracle.cross_attention(qh[r:r + 1], kc, vc, table, np.array([n]), scale)
             t_attn += time.perf_counter() - t1
             layers += 1
     step_s = t_other + geom.num_layers * t_attn / layers
     return {
-        "value": round(meta.num_reqs / step_s, 3),
+        "value": round(meta.num_reqs * Q / step_s, 3),
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
@@ -142,29 +155,45 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     meta = synth.make_metadata(args.workload, "full", args.seed)
+    Q, W = args.query_rows, args.window
+    varlen = Q > 1 or W > 0
+    if Q > 1:
+        if args.workload not in (2, 3, 5):
+            log("--query-rows applies to the decode workloads 2, 3 and 5")
+            sys.exit(2)
+        meta = synth.with_query_rows(meta, Q)
     geom = meta.geom
-    log(f"workload {geom.name}: {meta.num_reqs} requests, {int(meta.seq_lens.sum())} context tokens, "
-        f"{geom.num_layers} layers")
+    R = meta.num_reqs
+    num_rows = R * Q
+    log(f"workload {geom.name}: {R} requests, {int(meta.seq_lens.sum())} context tokens, "
+        f"{geom.num_layers} layers, {Q} query rows per request, window {W}")
     k, v = synth.make_cache(meta, dev, args.seed)
-    q = synth.make_queries(meta, dev, args.seed)
+    q = synth.make_queries(meta, dev, args.seed, rows=num_rows)
     x, w_rms, w_k, w_v = synth.make_append_inputs(meta, dev, args.seed)
     table = torch.from_numpy(meta.block_table).to(dev)
     seq = torch.from_numpy(meta.seq_lens).to(dev)
     cu = torch.from_numpy(meta.cu_seqlens).to(dev)
     slots = torch.from_numpy(meta.slot_mapping).to(dev)
     code = yb.DTYPE_BF16 if geom.dtype == "bf16" else yb.DTYPE_F32
-    part, nparts = yb.describe_launch(meta.num_reqs, geom.num_kv_heads, geom.head_dim, meta.max_seq_len,
-                                      geom.block_size, args.partition_tokens)
-    ws = torch.zeros(max(1, yb.cross_attn_workspace_size(meta.num_reqs, geom.num_q_heads, geom.num_kv_heads,
-                                                         geom.head_dim, meta.max_seq_len, geom.block_size,
-                                                         args.partition_tokens)),
-                     dtype=torch.uint8, device=dev)
+    span = meta.max_seq_len if W <= 0 else min(meta.max_seq_len, W + Q - 1)
+    part, nparts = yb.describe_launch(R, geom.num_kv_heads, geom.head_dim, span, geom.block_size,
+                                      args.partition_tokens)
+    if varlen:
+        ws_bytes = yb.cross_attn_varlen_workspace_size(num_rows, R, geom.num_q_heads, geom.num_kv_heads,
+                                                       geom.head_dim, meta.max_seq_len, Q, W, geom.block_size,
+                                                       args.partition_tokens)
+    else:
+        ws_bytes = yb.cross_attn_workspace_size(R, geom.num_q_heads, geom.num_kv_heads, geom.head_dim,
+                                                meta.max_seq_len, geom.block_size, args.partition_tokens)
+    ws = torch.zeros(max(1, ws_bytes), dtype=torch.uint8, device=dev)
     ws_append = torch.zeros(max(1, yb.kv_append_workspace_size(code, geom.hidden, geom.num_kv_heads, geom.head_dim)),
                             dtype=torch.uint8, device=dev)
-    outs = torch.empty((geom.num_layers, meta.num_reqs, geom.num_q_heads, geom.head_dim), dtype=torch.float32,
-                       device=dev)
-    rows = torch.empty((meta.num_reqs, geom.hidden), dtype=x.dtype, device=dev)
-    rows_idx = torch.empty(meta.num_reqs, dtype=torch.int32, device=dev)
+    outs = torch.empty((geom.num_layers, num_rows, geom.num_q_heads, geom.head_dim), dtype=torch.float32, device=dev)
+    rows = torch.empty((num_rows, geom.hidden), dtype=x.dtype, device=dev)
+    rows_idx = torch.empty(R, dtype=torch.int32, device=dev)
+    logits_idx = torch.arange(num_rows, dtype=torch.int32, device=dev)     # every scheduled row is verified
+    cross_qsl = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    cross_max = torch.empty(1, dtype=torch.int32, device=dev)
     # Between steps, read 1 GiB of other memory: that evicts the cache from the
     # L2s and the last-level cache without leaving dirty lines behind (a fill
     # would, and writing them back would slow the first kernel of the step).
@@ -174,12 +203,22 @@ def main():
 
     def step(ev_layers=None):
         yb.kv_append(x, w_rms, 1e-6, w_k, w_v, slots, k, v, workspace=ws_append, stream=stream)
-        yb.gather_last(x, cu, out=rows, out_index=rows_idx, stream=stream)
+        if Q > 1:
+            yb.gather_logits(x, logits_idx, cu, out=rows, out_query_start_loc=cross_qsl, out_max_query_len=cross_max,
+                             stream=stream)
+        else:
+            yb.gather_last(x, cu, out=rows[:R], out_index=rows_idx, stream=stream)
         for l in range(L):
             if ev_layers is not None:
                 ev_layers[l][0].record(stream)
-            yb.cross_attn(q[l], k, v, table, seq, meta.max_seq_len, partition_tokens=args.partition_tokens,
-                          flags=l & 1, out=outs[l], workspace=ws, stream=stream)
+            if varlen:
+                yb.cross_attn_varlen(q[l], k, v, table, seq, meta.max_seq_len,
+                                     query_start_loc=cross_qsl if Q > 1 else None, max_query_len=Q, window=W,
+                                     partition_tokens=args.partition_tokens, flags=l & 1, out=outs[l], workspace=ws,
+                                     stream=stream)
+            else:
+                yb.cross_attn(q[l], k, v, table, seq, meta.max_seq_len, partition_tokens=args.partition_tokens,
+                              flags=l & 1, out=outs[l], workspace=ws, stream=stream)
             if ev_layers is not None:
                 ev_layers[l][1].record(stream)
 
@@ -206,22 +245,26 @@ def main():
     step_ms = np.array([a.elapsed_time(b) for a, b in ev])
     layer_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in ev_l])
     ms_per_step = float(step_ms.mean())
-    tokens_per_s = meta.num_reqs / (ms_per_step * 1e-3)
+    tokens_per_s = num_rows / (ms_per_step * 1e-3)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (events), wall {1e3 * wall / args.steps:.3f} ms/step")
 
     layer_bytes = bm.attn_layer_bytes(meta.seq_lens, geom.num_q_heads, geom.num_kv_heads, geom.head_dim,
-                                      geom.block_size, geom.elem_bytes)
+                                      geom.block_size, geom.elem_bytes, query_lens=meta.query_lens if Q > 1 else None,
+                                      window=W)
     written = int((meta.slot_mapping >= 0).sum())
     step_bytes = (L * layer_bytes
                   + bm.append_bytes(meta.num_tokens, geom.hidden, geom.num_kv_heads, geom.head_dim, geom.elem_bytes,
                                     written)
-                  + bm.gather_bytes(meta.num_reqs, geom.hidden * geom.elem_bytes))
+                  + bm.gather_bytes(num_rows, geom.hidden * geom.elem_bytes))
     attn_us = float(layer_ms.mean()) * 1e3
     achieved = layer_bytes / (attn_us * 1e-6) / 1e9
     group = geom.num_q_heads // geom.num_kv_heads
-    attn_kernel = f"cross_attn_kernel<{'true' if geom.dtype == 'bf16' else 'false'}, {geom.head_dim}, {group}>"
+    rows_per_item = 0 if Q == 1 else 8 // group
+    attn_kernel = (f"cross_attn_kernel<{'true' if geom.dtype == 'bf16' else 'false'}, {geom.head_dim}, {group}, "
+                   f"{rows_per_item}>")
     merge_kernel = f"cross_attn_merge_kernel<{geom.head_dim}>"
-    measured = profiling.measured_traffic(geom.name, [attn_kernel, merge_kernel] if nparts > 1 else [attn_kernel])
+    variant = geom.name + (f"_q{Q}" if Q > 1 else "") + (f"_w{W}" if W > 0 else "")
+    measured = profiling.measured_traffic(variant, [attn_kernel, merge_kernel] if nparts > 1 else [attn_kernel])
     traffic = None
     profile_us = None
     if measured is not None:
@@ -243,8 +286,10 @@ def main():
         "dtype": geom.dtype,
         "data": "synthetic",
         "config": {
-            "workload": geom.name,
-            "num_reqs": meta.num_reqs,
+            "workload": variant,
+            "num_reqs": R,
+            "query_rows_per_request": Q,
+            "window": W,
             "context_tokens": int(meta.seq_lens.sum()),
             "num_layers": L,
             "num_q_heads": geom.num_q_heads,
@@ -261,7 +306,7 @@ def main():
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
         "roofline": {
-            "kernel": f"yoco_cross_attn: {attn_kernel} + {merge_kernel}",
+            "kernel": f"{'yoco_cross_attn_varlen' if varlen else 'yoco_cross_attn'}: {attn_kernel} + {merge_kernel}",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBPS,
@@ -278,7 +323,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, args.cpu_seconds, Q, W)
     print(json.dumps(result), flush=True)
 
 

@@ -21,16 +21,30 @@ def kv_bytes(layers: int, sequence: int, kv_heads: int, head_dim: int, bytes_per
     return 2 * layers * sequence * kv_heads * head_dim * bytes_per_scalar
 
 
-def attn_layer_bytes(seq_lens, num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
-                     elem_bytes: int) -> int:
-    """One yoco_cross_attn call: every context K/V row once, q in, fp32 out,
-    the block-table entries the contexts use, and seq_lens."""
+def attn_ranges(seq_lens, query_lens=None, window: int = 0):
+    """Per request, the context range [lo, n) its query rows read: the whole
+    context, or with a window of W tokens and q rows at the last q positions,
+    from n - q - W + 1 on."""
     seq = np.asarray(seq_lens, dtype=np.int64)
-    kv = int(sum(kv_bytes(1, int(n), num_kv_heads, head_dim, elem_bytes) for n in seq))
-    r = len(seq)
-    q_out = r * num_q_heads * head_dim * (elem_bytes + 4)
-    table = int(np.sum(-(-seq // block_size))) * 4
-    return kv + q_out + table + 4 * r
+    ql = np.ones_like(seq) if query_lens is None else np.asarray(query_lens, dtype=np.int64)
+    lo = np.zeros_like(seq) if window <= 0 else np.maximum(0, seq - ql - window + 1)
+    lo = np.where(ql > 0, lo, seq)           # a request without rows reads nothing
+    return lo, seq
+
+
+def attn_layer_bytes(seq_lens, num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
+                     elem_bytes: int, query_lens=None, window: int = 0) -> int:
+    """One cross-attention call: every K/V row of the range each request reads
+    once, q in and fp32 out for every query row, the block-table entries the
+    ranges span, seq_lens (and query_start_loc when there are several rows)."""
+    lo, n = attn_ranges(seq_lens, query_lens, window)
+    kv = int(sum(kv_bytes(1, int(b - a), num_kv_heads, head_dim, elem_bytes) for a, b in zip(lo, n)))
+    r = len(n)
+    rows = r if query_lens is None else int(np.sum(query_lens))
+    q_out = rows * num_q_heads * head_dim * (elem_bytes + 4)
+    spanned = np.where(n > lo, (np.maximum(n, 1) - 1) // block_size - lo // block_size + 1, 0)
+    table = int(np.sum(spanned)) * 4
+    return kv + q_out + table + 4 * r + (0 if query_lens is None else 4 * (r + 1))
 
 
 def attn_layer_flops(seq_lens, num_q_heads: int, head_dim: int) -> int:

@@ -259,6 +259,24 @@ def make_varlen_metadata(geom: Geometry, seq_lens, query_lens, seed: int = SEED_
     return base
 
 
+def with_query_rows(meta: Metadata, rows: int) -> Metadata:
+    """The same batch with `rows` scheduled tokens per request (its newest
+    positions, as a speculative-decoding step appends and verifies them):
+    slots for those positions, offsets [0, rows, 2*rows, ...], no padding."""
+    bs = meta.geom.block_size
+    r = meta.num_reqs
+    qlens = np.full(r, rows, dtype=np.int32)
+    cu = (np.arange(r + 1) * rows).astype(np.int32)
+    slots = np.full(r * rows, -1, dtype=np.int32)
+    for i in range(r):
+        n = int(meta.seq_lens[i])
+        for j in range(rows):
+            pos = n - rows + j
+            if pos >= 0:
+                slots[i * rows + j] = meta.block_table[i, pos // bs] * bs + pos % bs
+    return dataclasses.replace(meta, query_lens=qlens, cu_seqlens=cu, num_tokens=r * rows, slot_mapping=slots)
+
+
 def live_slot_mask(meta: Metadata) -> np.ndarray:
     """bool [num_blocks][block_size]: True for slots inside some context."""
     bs = meta.geom.block_size
