@@ -8,6 +8,12 @@ from .yoco_oracle import (  # noqa: F401
     cross_metadata,
     gather_rows,
     query_positions,
+    dequantize_cache,
+    e4m3_decode,
+    e4m3_encode,
+    kv_append_fp8,
+    kv_scatter,
+    quantize_rows,
     gather_last,
     kv_append,
     kv_project,

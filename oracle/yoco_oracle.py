@@ -52,6 +52,12 @@ __all__ = [
     "gather_rows",
     "query_positions",
     "cross_attention_varlen",
+    "e4m3_decode",
+    "e4m3_encode",
+    "quantize_rows",
+    "dequantize_cache",
+    "kv_scatter",
+    "kv_append_fp8",
 ]
 
 
@@ -341,3 +347,133 @@ def cross_attention_varlen(q, k_cache, v_cache, block_table, seq_lens, query_sta
                 g = h // group
                 out[row, h] = attention_one_query(q[row, h], keys[lo:p + 1, g, :], values[lo:p + 1, g, :], scale)
     return out
+
+
+# ---------------------------------------------------------------------------
+# 8-bit shared cache  ("KV cache memory systems", section "Quantized cache
+# changes attention inputs"; [YOCO] §18.2: build compression or quantization
+# of the shared K/V once and reuse it in every cross layer)
+# ---------------------------------------------------------------------------
+#
+# Readings taken (the pages fix none of these):
+#   * format: FP8 E4M3 in the finite-only variant (1 sign bit, 4 exponent bits
+#     with bias 7, 3 mantissa bits; exponent field 15 with mantissa 7 is NaN;
+#     no infinities; largest finite 448; subnormals m * 2^-9);
+#   * one fp32 scale per (token, KV head), separately for K and for V (the
+#     page: keys and values may need different calibration), chosen when the
+#     token is appended as s = max|x| / 448, so the row's largest value maps
+#     to the format's largest; a stored value means code * s;
+#   * the scale and the division x / s are fp32 operations (IEEE, rounded to
+#     nearest even), and x / s is rounded to E4M3 to nearest even -- the
+#     precision the kernel takes this integer decision in.
+
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    """Value of every FP8 E4M3 (finite-only) code, as float64."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    out = np.empty(codes.shape, dtype=np.float64)
+    for idx, c in np.ndenumerate(codes):
+        c = int(c)
+        sign = -1.0 if c & 0x80 else 1.0
+        e = (c >> 3) & 0xF
+        m = c & 0x7
+        if e == 0xF and m == 0x7:
+            out[idx] = np.nan
+        elif e == 0:
+            out[idx] = sign * m * 2.0 ** -9            # subnormal: 0.mmm * 2^-6
+        else:
+            out[idx] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return out
+
+
+def e4m3_encode(x) -> np.ndarray:
+    """Round each value to the nearest FP8 E4M3 value, ties to the even code
+    (mantissa bit 0 clear); magnitudes above 448 saturate to 448; NaN gives the
+    NaN code 0x7F with the value's sign bit.  Enumerates the 127 non-negative
+    finite values and picks by distance, which is the definition itself."""
+    grid = e4m3_decode(np.arange(0x7F, dtype=np.uint8))          # codes 0x00..0x7E: 0 .. 448, increasing
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.uint8)
+    for idx, v in np.ndenumerate(x):
+        if np.isnan(v):
+            out[idx] = 0xFF if np.signbit(v) else 0x7F
+            continue
+        a = min(abs(v), E4M3_MAX)
+        j = int(np.searchsorted(grid, a))                          # grid[j-1] < a <= grid[j]
+        if j < len(grid) and grid[j] == a:
+            code = j
+        else:
+            lo, hi = j - 1, j
+            dl, dh = a - grid[lo], grid[hi] - a
+            code = lo if dl < dh else hi if dh < dl else (lo if lo % 2 == 0 else hi)
+        out[idx] = code | (0x80 if np.signbit(v) else 0)
+    return out
+
+
+def quantize_rows(rows):
+    """Quantize each row (last axis) of fp32 values to (codes, scale).
+
+    scale = max|row| / 448 and code = E4M3(row / scale), both divisions in
+    fp32; a row of zeros gets scale 0 and zero codes.  Returns uint8 codes
+    shaped like ``rows`` and fp32 scales with the last axis dropped.
+    """
+    rows = np.asarray(rows, dtype=np.float32)
+    codes = np.zeros(rows.shape, dtype=np.uint8)
+    scales = np.zeros(rows.shape[:-1], dtype=np.float32)
+    for idx in np.ndindex(rows.shape[:-1]):
+        row = rows[idx]
+        amax = np.float32(np.max(np.abs(row))) if not np.isnan(row).any() else np.float32(np.nan)
+        s = np.float32(amax / np.float32(E4M3_MAX))
+        scales[idx] = s
+        if s == 0:
+            continue
+        codes[idx] = e4m3_encode(np.float32(row / s) if np.isfinite(s) else np.full(row.shape, np.nan, np.float32))
+    return codes, scales
+
+
+def dequantize_cache(codes, scales) -> np.ndarray:
+    """The values an 8-bit cache holds: code value times its row's scale
+    (exact in float64).  codes ``[..., D]``, scales ``[...]``."""
+    return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def kv_scatter(rows_k, rows_v, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None):
+    """Write given K/V rows ``[T][Hkv][D]`` into their slots ([vLLM]
+    slot_mapping; slot s is block s // block_size, row s % block_size;
+    negative slots are skipped).  Without scales the rows are copied as they
+    are; with scales (an 8-bit cache) each (token, KV head) row is quantized
+    with :func:`quantize_rows`.  Returns updated copies of the cache arrays
+    (and of the scales)."""
+    bs = np.asarray(k_cache).shape[2]
+    kc, vc = np.array(k_cache, copy=True), np.array(v_cache, copy=True)
+    quant = k_scale is not None
+    if quant:
+        ks, vs = np.array(k_scale, copy=True), np.array(v_scale, copy=True)
+        ck, sk = quantize_rows(rows_k)
+        cv, sv = quantize_rows(rows_v)
+    for t, slot in enumerate(np.asarray(slot_mapping)):
+        slot = int(slot)
+        if slot < 0:
+            continue
+        block, offset = divmod(slot, bs)
+        if quant:
+            kc[block, :, offset, :], ks[block, :, offset] = ck[t], sk[t]
+            vc[block, :, offset, :], vs[block, :, offset] = cv[t], sv[t]
+        else:
+            kc[block, :, offset, :] = rows_k[t]
+            vc[block, :, offset, :] = rows_v[t]
+    return (kc, vc, ks, vs) if quant else (kc, vc)
+
+
+def kv_append_fp8(x, rms_weight, eps: float, w_k, w_v, slot_mapping, num_kv_heads: int, head_dim: int):
+    """The shared projection (:func:`kv_project`, float64) of every scheduled
+    token, quantized per (token, KV head) as :func:`quantize_rows` does after
+    rounding the projected values to fp32.  Returns, per token, float64 K/V
+    ``[T][Hkv][D]``, their fp32-rounded codes and scales, and the error-bound
+    scales of :func:`kv_project` (the slots are the caller's to apply)."""
+    k, v, bk, bv = kv_project(x, rms_weight, eps, w_k, w_v, num_kv_heads, head_dim)
+    ck, sk = quantize_rows(k.astype(np.float32))
+    cv, sv = quantize_rows(v.astype(np.float32))
+    return k, v, (ck, sk), (cv, sv), bk, bv

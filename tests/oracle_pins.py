@@ -517,3 +517,94 @@ def check_gather_rows_bits(gather_rows_fn):
 
 METADATA_CHECKS = [check_metadata_page_example, check_metadata_torch]
 GATHER_ROWS_CHECKS = [check_gather_rows_bits]
+
+
+# ---------------------------------------------------------------------------
+# 8-bit cache: FP8 E4M3 codes, per-row scales
+# ---------------------------------------------------------------------------
+
+def check_e4m3_decode(decode):
+    """Library routine: torch's float8_e4m3fn interpretation of all 256 codes;
+    closed forms: 0x7E = 448 (largest), 0x01 = 2^-9 (smallest subnormal),
+    0x08 = 2^-6 (smallest normal), 0x38 = 1, 0x7F and 0xFF are NaN."""
+    codes = np.arange(256, dtype=np.uint8)
+    got = decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(got, ref, equal_nan=True)
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6 and got[0x38] == 1.0
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and got[0xFE] == -448.0
+
+
+def check_e4m3_encode(encode):
+    """Library routine: torch's round-to-nearest-even conversion to
+    float8_e4m3fn on values across the whole range (subnormals included);
+    closed forms: ties go to the even code (1 + 1/16 -> 1, 1 + 3/16 -> 1.25),
+    448 -> 0x7E, -0.0 -> 0x80, NaN -> 0x7F."""
+    rng = np.random.default_rng(61)
+    x = np.concatenate([rng.standard_normal(4000) * 60, rng.standard_normal(2000) * 2.0 ** -7,
+                        rng.uniform(-448, 448, 2000)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(encode(x), ref)
+    ties = np.array([1.0625, 1.1875, -1.0625, 2.0 ** -10, 3 * 2.0 ** -10, 448.0, -0.0, np.nan], dtype=np.float32)
+    assert encode(ties).tolist() == [0x38, 0x3A, 0xB8, 0x00, 0x02, 0x7E, 0x80, 0x7F]
+
+
+def check_quantize_rows(quantize):
+    """Each row's largest magnitude becomes the code of +-448 and its scale is
+    the value that maps back to it; codes equal torch's conversion of the fp32
+    quotient; scaling a row by 2^k scales its scale by 2^k and keeps the codes;
+    a zero row has scale 0 and zero codes; every value comes back within half
+    an E4M3 step."""
+    rng = np.random.default_rng(62)
+    rows = (rng.standard_normal((5, 3, 16)) * rng.uniform(0.01, 30, size=(5, 3, 1))).astype(np.float32)
+    rows[1, 2] = 0.0
+    codes, scales = quantize(rows)
+    assert codes.dtype == np.uint8 and scales.dtype == np.float32 and scales.shape == (5, 3)
+    for idx in np.ndindex(5, 3):
+        row = rows[idx]
+        if not row.any():
+            assert scales[idx] == 0 and not codes[idx].any()
+            continue
+        j = int(np.argmax(np.abs(row)))
+        assert codes[idx][j] == (0xFE if row[j] < 0 else 0x7E)
+        quotient = torch.from_numpy(row) / torch.tensor(scales[idx])
+        assert np.array_equal(codes[idx], quotient.to(torch.float8_e4m3fn).view(torch.uint8).numpy())
+        back = torch.from_numpy(codes[idx]).view(torch.float8_e4m3fn).to(torch.float64).numpy() * float(scales[idx])
+        step = np.maximum(np.abs(row) * 2.0 ** -3, float(scales[idx]) * 2.0 ** -9)   # one ulp bound per value
+        assert (np.abs(back - row) <= step / 2 * (1 + 1e-6)).all()
+        assert abs(float(scales[idx]) * 448.0 - float(np.abs(row).max())) <= float(np.abs(row).max()) * 2.0 ** -23
+    c2, s2 = quantize(rows * np.float32(8.0))
+    assert np.array_equal(c2, codes) and np.array_equal(s2, scales * np.float32(8.0))
+
+
+def check_kv_scatter(scatter):
+    """Rows land in slot s = block s // block_size, row s % block_size for every
+    KV head (hand-worked: block size 4, slot 10 -> block 2 row 2); negative
+    slots write nothing; with an 8-bit cache the stored code times the scale
+    gives the row back within half an E4M3 step; untouched entries keep their
+    bits."""
+    rng = np.random.default_rng(63)
+    nb, hkv, bs, d = 5, 2, 4, 8
+    rows_k = rng.standard_normal((3, hkv, d)).astype(np.float32)
+    rows_v = rng.standard_normal((3, hkv, d)).astype(np.float32)
+    slots = np.array([10, -1, 17])
+    kc0 = np.full((nb, hkv, bs, d), -3.5, dtype=np.float32)
+    kc, vc = scatter(rows_k, rows_v, slots, kc0, kc0)
+    assert np.array_equal(kc[2, :, 2], rows_k[0]) and np.array_equal(vc[4, :, 1], rows_v[2])
+    assert (kc != kc0).any(axis=(1, 3)).sum() == 2
+    codes0 = np.full((nb, hkv, bs, d), 0x55, dtype=np.uint8)
+    sc0 = np.full((nb, hkv, bs), 9.0, dtype=np.float32)
+    kq, vq, ks, vs = scatter(rows_k, rows_v, slots, codes0, codes0, sc0, sc0)
+    for t, (blk, off) in {0: (2, 2), 2: (4, 1)}.items():
+        for rows, codes, sc in ((rows_k, kq, ks), (rows_v, vq, vs)):
+            back = torch.from_numpy(codes[blk, :, off]).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+            back = back * sc[blk, :, off][:, None]
+            assert (np.abs(back - rows[t]) <= np.abs(rows[t]) * 2.0 ** -4 + sc[blk, :, off][:, None] * 2.0 ** -10).all()
+    changed = (kq != codes0).any(axis=(1, 3)) | (ks != sc0).any(axis=1)
+    assert changed.sum() == 2
+
+
+FP8_DECODE_CHECKS = [check_e4m3_decode]
+FP8_ENCODE_CHECKS = [check_e4m3_encode]
+QUANT_CHECKS = [check_quantize_rows]
+SCATTER_CHECKS = [check_kv_scatter]

@@ -194,6 +194,68 @@ METADATA_MUTANTS = {
 }
 
 
+def _decode_variant(bias=7, subnormal_as_normal=False):
+    def decode(codes):
+        codes = np.asarray(codes, dtype=np.uint8)
+        out = np.empty(codes.shape)
+        for idx, c in np.ndenumerate(codes):
+            c = int(c)
+            sign = -1.0 if c & 0x80 else 1.0
+            e, m = (c >> 3) & 0xF, c & 7
+            if e == 15 and m == 7:
+                out[idx] = np.nan
+            elif e == 0 and not subnormal_as_normal:
+                out[idx] = sign * m * 2.0 ** (1 - bias - 3)
+            else:
+                out[idx] = sign * (1 + m / 8) * 2.0 ** (e - bias)
+        return out
+    return decode
+
+
+def _encode_variant(ties_up=False, no_subnormals=False):
+    def encode(x):
+        grid = yo.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+        x = np.asarray(x, dtype=np.float64)
+        out = np.empty(x.shape, dtype=np.uint8)
+        for idx, v in np.ndenumerate(x):
+            if np.isnan(v):
+                out[idx] = 0x7F
+                continue
+            a = min(abs(v), 448.0)
+            if no_subnormals and a < 2.0 ** -6:
+                a = 0.0
+            j = int(np.searchsorted(grid, a))
+            if j < len(grid) and grid[j] == a:
+                code = j
+            else:
+                dl, dh = a - grid[j - 1], grid[j] - a
+                code = j - 1 if dl < dh else j if dh < dl else (j if ties_up else (j - 1 if (j - 1) % 2 == 0 else j))
+            out[idx] = code | (0x80 if np.signbit(v) else 0)
+        return out
+    return encode
+
+
+def _quant_variant(qmax=448.0, scale_from_mean=False):
+    def quantize(rows):
+        rows = np.asarray(rows, dtype=np.float32)
+        codes = np.zeros(rows.shape, dtype=np.uint8)
+        scales = np.zeros(rows.shape[:-1], dtype=np.float32)
+        for idx in np.ndindex(rows.shape[:-1]):
+            row = rows[idx]
+            ref = np.abs(row).mean() * 3 if scale_from_mean else np.abs(row).max()
+            s = np.float32(np.float32(ref) / np.float32(qmax))
+            scales[idx] = s
+            if s:
+                codes[idx] = yo.e4m3_encode(np.float32(row / s))
+        return codes, scales
+    return quantize
+
+
+FP8_DECODE_MUTANTS = {"bias_8": _decode_variant(bias=8), "subnormal_as_normal": _decode_variant(subnormal_as_normal=True)}
+FP8_ENCODE_MUTANTS = {"ties_up": _encode_variant(ties_up=True), "no_subnormals": _encode_variant(no_subnormals=True)}
+QUANT_MUTANTS = {"int8_range": _quant_variant(qmax=127.0), "scale_from_mean": _quant_variant(scale_from_mean=True)}
+
+
 def _fails_some(checks, fn):
     failures = 0
     for check in checks:
@@ -245,3 +307,24 @@ def test_metadata_mutant_is_caught(name):
 def test_unmutated_varlen_copies_pass():
     assert _fails_some(pins.VARLEN_CHECKS, _varlen_variant()) == 0
     assert _fails_some(pins.METADATA_CHECKS, _metadata_variant()) == 0
+
+
+@pytest.mark.parametrize("name", sorted(FP8_DECODE_MUTANTS))
+def test_e4m3_decode_mutant_is_caught(name):
+    assert _fails_some(pins.FP8_DECODE_CHECKS, FP8_DECODE_MUTANTS[name]) > 0
+
+
+@pytest.mark.parametrize("name", sorted(FP8_ENCODE_MUTANTS))
+def test_e4m3_encode_mutant_is_caught(name):
+    assert _fails_some(pins.FP8_ENCODE_CHECKS, FP8_ENCODE_MUTANTS[name]) > 0
+
+
+@pytest.mark.parametrize("name", sorted(QUANT_MUTANTS))
+def test_quantize_mutant_is_caught(name):
+    assert _fails_some(pins.QUANT_CHECKS, QUANT_MUTANTS[name]) > 0
+
+
+def test_unmutated_fp8_copies_pass():
+    assert _fails_some(pins.FP8_DECODE_CHECKS, _decode_variant()) == 0
+    assert _fails_some(pins.FP8_ENCODE_CHECKS, _encode_variant()) == 0
+    assert _fails_some(pins.QUANT_CHECKS, _quant_variant()) == 0

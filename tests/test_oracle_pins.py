@@ -40,3 +40,33 @@ def test_metadata_pins(check):
 @pytest.mark.parametrize("check", pins.GATHER_ROWS_CHECKS, ids=lambda c: c.__name__)
 def test_gather_rows_pins(check):
     check(oracle.gather_rows)
+
+
+@pytest.mark.parametrize("check", pins.FP8_DECODE_CHECKS, ids=lambda c: c.__name__)
+def test_e4m3_decode_pins(check):
+    check(oracle.e4m3_decode)
+
+
+@pytest.mark.parametrize("check", pins.FP8_ENCODE_CHECKS, ids=lambda c: c.__name__)
+def test_e4m3_encode_pins(check):
+    check(oracle.e4m3_encode)
+
+
+@pytest.mark.parametrize("check", pins.QUANT_CHECKS, ids=lambda c: c.__name__)
+def test_quantize_pins(check):
+    check(oracle.quantize_rows)
+
+
+@pytest.mark.parametrize("check", pins.SCATTER_CHECKS, ids=lambda c: c.__name__)
+def test_scatter_pins(check):
+    check(oracle.kv_scatter)
+
+
+def test_dequantize_cache_is_code_times_scale():
+    """Closed form: code 0x38 (1.0) with scale 2.5 is 2.5; 0xC0 (-2.0) with
+    scale 2.5 is -5.0; scale 0 gives 0."""
+    import numpy as np
+    codes = np.array([[[[0x38, 0xC0]], [[0x7E, 0x01]]]], dtype=np.uint8)     # [1][2][1][2]
+    scales = np.array([[[2.5], [0.0]]], dtype=np.float32)
+    out = oracle.dequantize_cache(codes, scales)
+    assert out.tolist() == [[[[2.5, -5.0]], [[0.0, 0.0]]]]
