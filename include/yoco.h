@@ -72,7 +72,11 @@ typedef enum yoco_status {
   YOCO_ERR_HIP = 4                 /* the HIP runtime refused a launch */
 } yoco_status_t;
 
-typedef enum yoco_dtype { YOCO_DTYPE_F32 = 0, YOCO_DTYPE_BF16 = 1 } yoco_dtype_t;
+/* YOCO_DTYPE_FP8_E4M3 is a cache dtype only: one byte per element in the
+ * FP8 E4M3 format (finite-only variant: bias 7, 0x7F/0xFF NaN, largest 448),
+ * plus one fp32 scale per (token, KV head) for K and one for V, laid out
+ * [num_blocks][num_kv_heads][block_size]; an element means code * scale. */
+typedef enum yoco_dtype { YOCO_DTYPE_F32 = 0, YOCO_DTYPE_BF16 = 1, YOCO_DTYPE_FP8_E4M3 = 2 } yoco_dtype_t;
 
 /* yoco_cross_attn flag: walk the (request, KV head, partition) work items in
  * reverse order.  Alternating it between consecutive cross layers makes the
@@ -174,6 +178,52 @@ int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_tokens, int32_t
                        int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
                        int32_t head_dim, void* workspace, int64_t workspace_bytes,
                        void* stream);
+
+/*
+ * yoco_kv_scatter -- write given K^/V^ rows into their cache slots, and
+ * yoco_kv_append_fp8 -- the shared projection into an 8-bit cache.
+ *
+ * [KV] "Quantized cache changes attention inputs": a quantized cache stores
+ * fewer bytes per scalar plus scale metadata, and keys and values may need
+ * their own calibration.  [YOCO] section 18.2: quantize the shared K/V once
+ * and let every cross layer reuse it.  Into a YOCO_DTYPE_FP8_E4M3 cache each
+ * (token, KV head) row x of head_dim values is stored as
+ *     s = max|x| / 448,  code_i = E4M3(x_i / s)
+ * (both divisions fp32, round to nearest even; a zero row gives s = 0 and
+ * zero codes; a row holding inf or NaN gives NaN codes), K and V with their
+ * own scales; code_i * s is the stored value.
+ *
+ * yoco_kv_scatter:
+ *   src_dtype     YOCO_DTYPE_F32 or YOCO_DTYPE_BF16: type of k_rows, v_rows.
+ *   k_rows, v_rows  [num_tokens][num_kv_heads][head_dim].
+ *   slot_mapping  int32 [num_tokens]; negative (or >= num_blocks*block_size)
+ *                 slots are skipped.
+ *   cache_dtype   src_dtype (rows copied bit for bit) or
+ *                 YOCO_DTYPE_FP8_E4M3 (quantized as above).
+ *   k_scale, v_scale  fp32 [num_blocks][num_kv_heads][block_size]: required
+ *                 for, and only for, the FP8 cache.
+ *   Supported head_dim {64, 128, 256}; block_size a power of two <= 256.
+ *
+ * yoco_kv_append_fp8: yoco_kv_append with the cache in FP8 E4M3: the fp32
+ * projection of each token (before any bf16 rounding) is quantized.  `dtype`
+ * is the type of x, rms_weight, w_k and w_v.  The workspace holds the
+ * projected fp32 rows: at least yoco_kv_append_fp8_workspace_size() bytes
+ * (grows with num_tokens).  Caches and scales need 4-byte alignment.
+ *
+ * Errors: YOCO_ERR_INVALID_ARGUMENT, YOCO_ERR_UNSUPPORTED,
+ * YOCO_ERR_WORKSPACE_TOO_SMALL.  num_tokens == 0 is a no-op.
+ */
+int32_t yoco_kv_scatter(int32_t src_dtype, const void* k_rows, const void* v_rows, int32_t num_tokens,
+                        const int32_t* slot_mapping, int32_t cache_dtype, void* k_cache, void* v_cache,
+                        float* k_scale, float* v_scale, int32_t num_blocks, int32_t num_kv_heads,
+                        int32_t block_size, int32_t head_dim, void* stream);
+int64_t yoco_kv_append_fp8_workspace_size(int32_t dtype, int32_t num_tokens, int32_t hidden,
+                                          int32_t num_kv_heads, int32_t head_dim);
+int32_t yoco_kv_append_fp8(int32_t dtype, const void* x, int32_t num_tokens, int32_t hidden,
+                           const void* rms_weight, float eps, const void* w_k, const void* w_v,
+                           const int32_t* slot_mapping, void* k_cache, void* v_cache, float* k_scale,
+                           float* v_scale, int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                           int32_t head_dim, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
  * yoco_cross_attn -- one cross layer's attention over the shared cache.
@@ -313,12 +363,16 @@ int32_t yoco_gather_logits(const void* hidden, int64_t num_tokens, int64_t row_b
  *   max_query_len   an upper bound of the rows per request; a request's rows
  *                   beyond it are not written.
  *   window          0 for the whole context, else the window in tokens.
- *   k_scale, v_scale  scales of an 8-bit cache; must be NULL for
- *                   YOCO_DTYPE_F32 and YOCO_DTYPE_BF16.
+ *   dtype           cache dtype; with YOCO_DTYPE_FP8_E4M3 the caches hold
+ *                   codes, q is bf16, and k_scale, v_scale (fp32
+ *                   [num_blocks][num_kv_heads][block_size]) give each row's
+ *                   scale: the attention reads code * scale, dequantized in
+ *                   the kernel.  k_scale, v_scale must be NULL otherwise.
  *
  * With query_start_loc: num_seqs <= 2048 (YOCO_ERR_UNSUPPORTED beyond); a
  * work item streams its K^/V^ rows once for up to 8 query vectors (rows x
- * heads of one KV group).  Errors as in yoco_cross_attn.
+ * heads of one KV group).  A NaN in a row that some of a request's rows read
+ * may give NaN in all of that request's rows.  Errors as in yoco_cross_attn.
  */
 int64_t yoco_cross_attn_varlen_workspace_size(int32_t num_rows, int32_t num_seqs, int32_t num_q_heads,
                                               int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,

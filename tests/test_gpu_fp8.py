@@ -1,0 +1,225 @@
+"""The 8-bit (FP8 E4M3) shared cache on the GPU against the float64 oracle.
+
+* yoco_kv_scatter: codes and scales bit for bit equal to the oracle's
+  quantizer fed with the same fp32 (or bf16) rows; copies into bf16 / fp32
+  caches bit for bit; untouched cache bytes keep their bits.
+* yoco_kv_append_fp8: every stored value within a derived bound of the
+  float64 projection (the append's own floating-point error plus half an
+  E4M3 step), scales within the same error.
+* yoco_cross_attn_varlen over FP8 caches: within 2e-3 of the oracle's
+  attention over the dequantized cache.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_helpers import ATTN_ATOL, U_BF16, U_F32, dev, host, say
+from yoco_shared_kv_gather_amd import binding as yb
+from yoco_shared_kv_gather_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _codes_equal(a, b):
+    return np.array_equal(np.asarray(a, dtype=np.uint8), np.asarray(b, dtype=np.uint8))
+
+
+def _scales_equal(a, b):
+    return np.array_equal(np.asarray(a, dtype=np.float32).view(np.uint32)[np.isfinite(a)],
+                          np.asarray(b, dtype=np.float32).view(np.uint32)[np.isfinite(b)]) and \
+        np.array_equal(np.isfinite(a), np.isfinite(b))
+
+
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+@pytest.mark.parametrize("hkv,d,bs", [(1, 64, 4), (2, 128, 16), (8, 128, 16), (2, 256, 32)])
+def test_scatter_quantizes_bit_exact(src, hkv, d, bs):
+    say(f"kv_scatter -> FP8: {src} rows, {hkv} KV heads x {d}, block {bs}")
+    rng = np.random.default_rng(hkv * 1000 + d + bs)
+    t, nb = 37, 40
+    rows = rng.standard_normal((2, t, hkv, d)).astype(np.float32)
+    rows[0, 3] *= 40.0                                   # large rows
+    rows[1, 5] *= 1e-4                                   # codes in the subnormal range
+    rows[0, 7, 0] = 0.0                                  # a zero row
+    rows[1, 9, 0, 3] = np.nan                            # a row holding NaN
+    rows[0, 11, 0, 1] = -np.inf
+    if src == "bf16":
+        rows_t = torch.from_numpy(rows).to(torch.bfloat16)
+        rows = rows_t.float().numpy()                    # exact widening: what the kernel reads
+    else:
+        rows_t = torch.from_numpy(rows)
+    slots = rng.permutation(nb * bs)[:t].astype(np.int32)
+    slots[4] = -1
+    codes0 = np.full((nb, hkv, bs, d), 0x5A, dtype=np.uint8)
+    sc0 = np.full((nb, hkv, bs), 7.0, dtype=np.float32)
+    kc, vc = torch.from_numpy(codes0).to(dev()), torch.from_numpy(codes0).to(dev())
+    ks, vs = torch.from_numpy(sc0).to(dev()), torch.from_numpy(sc0).to(dev())
+    kr, vr = rows_t[0].contiguous().to(dev()), rows_t[1].contiguous().to(dev())
+    yb.kv_scatter(kr, vr, torch.from_numpy(slots).to(dev()), kc, vc, ks, vs)
+    torch.cuda.synchronize()
+    ref_k, ref_v, ref_ks, ref_vs = oracle.kv_scatter(rows[0], rows[1], slots, codes0, codes0, sc0, sc0)
+    assert _codes_equal(kc.cpu().numpy(), ref_k) and _codes_equal(vc.cpu().numpy(), ref_v)
+    assert _scales_equal(ks.cpu().numpy(), ref_ks) and _scales_equal(vs.cpu().numpy(), ref_vs)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_scatter_copies_bit_exact(dtype):
+    say(f"kv_scatter copy: {dtype}")
+    rng = np.random.default_rng(7)
+    t, nb, hkv, bs, d = 21, 9, 2, 8, 64
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    rows = torch.from_numpy(rng.standard_normal((2, t, hkv, d)).astype(np.float32)).to(tdt)
+    slots = rng.permutation(nb * bs)[:t].astype(np.int32)
+    slots[[2, 6]] = -1
+    cache0 = torch.full((nb, hkv, bs, d), -2.75, dtype=tdt)
+    kc, vc = cache0.clone().to(dev()), cache0.clone().to(dev())
+    yb.kv_scatter(rows[0].contiguous().to(dev()), rows[1].contiguous().to(dev()), torch.from_numpy(slots).to(dev()),
+                  kc, vc)
+    torch.cuda.synchronize()
+    ref_k, ref_v = oracle.kv_scatter(rows[0].float().numpy(), rows[1].float().numpy(), slots,
+                                     cache0.float().numpy(), cache0.float().numpy())
+    assert np.array_equal(kc.float().cpu().numpy(), ref_k) and np.array_equal(vc.float().cpu().numpy(), ref_v)
+
+
+def _append_error(bound, hidden, dtype):
+    """The append's error before the final store (see gpu_helpers.append_tolerance):
+    bf16: (u_b + (2H+9) u_f)(1+u_b) B; fp32: (2H+10) u_f B."""
+    if dtype == "bf16":
+        return (U_BF16 + (2 * hidden + 9) * U_F32) * (1 + U_BF16) * bound
+    return (2 * hidden + 10) * U_F32 * bound
+
+
+@pytest.mark.parametrize("cid,size", [(1, "full"), (2, "small"), (4, "small"), (3, "full")])
+def test_append_fp8_within_bound(cid, size):
+    """Every written row: |code*s - ref| <= err + half an E4M3 step of the
+    stored value (2^-4 relative, s*2^-10 in the subnormal range), and the
+    scale times 448 within the append error of the row's largest |ref|."""
+    meta = synth.make_metadata(cid, size)
+    geom = meta.geom
+    say(f"kv_append_fp8: workload {cid} {size}, {meta.num_tokens} tokens")
+    d = dev()
+    x, w_rms, w_k, w_v = synth.make_append_inputs(meta, d, rms_weight="random")
+    shape = (meta.num_blocks, geom.num_kv_heads, geom.block_size, geom.head_dim)
+    kc = torch.full(shape, 0x5A, dtype=torch.uint8, device=d)
+    vc = kc.clone()
+    ks = torch.full(shape[:-1], 7.0, dtype=torch.float32, device=d)
+    vs = ks.clone()
+    slots = torch.from_numpy(meta.slot_mapping).to(d)
+    yb.kv_append_fp8(x, w_rms, 1e-6, w_k, w_v, slots, kc, vc, ks, vs)
+    torch.cuda.synchronize()
+    k, v, _, _, bk, bv = oracle.kv_append_fp8(host(x), host(w_rms), 1e-6, host(w_k), host(w_v), meta.slot_mapping,
+                                             geom.num_kv_heads, geom.head_dim)
+    kq, vq = kc.cpu().numpy(), vc.cpu().numpy()
+    ksn, vsn = ks.cpu().numpy(), vs.cpu().numpy()
+    bs = geom.block_size
+    worst = 0.0
+    same = total = 0
+    for t, slot in enumerate(meta.slot_mapping):
+        if slot < 0:
+            continue
+        blk, off = divmod(int(slot), bs)
+        for ref, bound, codes, scales in ((k[t], bk[t], kq, ksn), (v[t], bv[t], vq, vsn)):
+            err = _append_error(bound, geom.hidden, geom.dtype)                 # [Hkv][D]
+            s = scales[blk, :, off].astype(np.float64)                          # [Hkv]
+            got = oracle.e4m3_decode(codes[blk, :, off]) * s[:, None]
+            step = np.maximum((np.abs(ref) + err) * 2.0 ** -4, s[:, None] * 2.0 ** -10)
+            assert (np.abs(got - ref) <= err + step * (1 + 1e-6)).all()
+            amax = np.abs(ref).max(axis=1)
+            assert (np.abs(s * 448.0 - amax) <= err.max(axis=1) + amax * 2.0 ** -22).all()
+            worst = max(worst, float((np.abs(got - ref) / (err + step)).max()))
+            same += int((codes[blk, :, off] == oracle.quantize_rows(ref.astype(np.float32))[0]).sum())
+            total += ref.size
+    live = meta.slot_mapping[meta.slot_mapping >= 0]
+    untouched = np.ones((meta.num_blocks, bs), dtype=bool)
+    untouched[live // bs, live % bs] = False
+    assert (kq.transpose(0, 2, 1, 3)[untouched] == 0x5A).all() and (ksn.transpose(0, 2, 1)[untouched] == 7.0).all()
+    say(f"  worst error / bound {worst:.3f}; codes equal to the float64 reference's {same / total:.4%}")
+
+
+def _fp8_case(geom, ctx, qlens, seed):
+    meta = synth.make_varlen_metadata(geom, ctx, qlens, seed=seed)
+    d = dev()
+    kc, ks, vc, vs = synth.make_fp8_cache(meta, d, seed)
+    rows = int(meta.cu_seqlens[-1])
+    q = synth.make_queries(meta, d, seed, num_layers=1, rows=rows)[0]
+    return meta, q, kc, ks, vc, vs
+
+
+@pytest.mark.parametrize("hq,hkv,d", [(4, 1, 64), (8, 2, 128), (8, 2, 256), (8, 8, 128), (16, 2, 64)])
+@pytest.mark.parametrize("several", [False, True])
+@pytest.mark.parametrize("window", [0, 50])
+def test_attention_fp8(hq, hkv, d, several, window):
+    say(f"cross_attn_varlen FP8: {hq}x{hkv}x{d} several rows {several} window {window}")
+    geom = synth.custom_geometry("bf16", hq, hkv, d, 16)
+    ctx = [5, 300, 1, 0, 64, 129, 3, 700, 2]
+    qlens = [3, 4, 1, 2, 5, 1, 6, 2, 0] if several else [1 if c > 0 else 0 for c in ctx]
+    meta, q, kc, ks, vc, vs = _fp8_case(geom, ctx, qlens, seed=hq + d + window)
+    table = torch.from_numpy(meta.block_table).to(dev())
+    seq = torch.from_numpy(meta.seq_lens).to(dev())
+    kd = oracle.dequantize_cache(kc.cpu().numpy(), ks.cpu().numpy())
+    vd = oracle.dequantize_cache(vc.cpu().numpy(), vs.cpu().numpy())
+    ref = oracle.cross_attention_varlen(host(q), kd, vd, meta.block_table, meta.seq_lens, meta.cu_seqlens,
+                                        1.0 / math.sqrt(d), window)
+    for part in (0, 64):
+        qsl = torch.from_numpy(meta.cu_seqlens).to(dev()) if several else None
+        qq = q if several else q[:0]
+        if not several:
+            # one row per request, no offsets: requests with an empty context still own a row
+            qq = torch.zeros((meta.num_reqs, hq, d), dtype=torch.bfloat16, device=dev())
+            qq[torch.from_numpy(np.nonzero(np.asarray(qlens))[0]).to(dev())] = q
+        out = yb.cross_attn_varlen(qq, kc, vc, table, seq, meta.max_seq_len, query_start_loc=qsl,
+                                   max_query_len=max(qlens) if several else 1, window=window, partition_tokens=part,
+                                   k_scale=ks, v_scale=vs)
+        torch.cuda.synchronize()
+        got = out.cpu().double().numpy()
+        if not several:
+            got = got[np.nonzero(np.asarray(qlens))[0]]
+        assert np.isfinite(got).all()
+        err = float(np.abs(got - ref).max())
+        say(f"  partition {part}: max abs err {err:.3e}")
+        assert err <= ATTN_ATOL
+
+
+def test_scatter_then_attention_chain():
+    """The product chain -- quantize a bf16 cache's rows with yoco_kv_scatter,
+    then attend over the FP8 cache -- against the oracle's quantizer and
+    attention on the same bf16 rows."""
+    say("kv_scatter(FP8) -> cross_attn_varlen chain, workload 2 small")
+    meta = synth.make_metadata(2, "small")
+    geom = meta.geom
+    d = dev()
+    k, v = synth.make_cache(meta, d)
+    q = synth.make_queries(meta, d, num_layers=1)[0]
+    bs = geom.block_size
+    # every context position as a row to scatter
+    slots, rows_k, rows_v = [], [], []
+    for r in range(meta.num_reqs):
+        for j in range(int(meta.seq_lens[r])):
+            b = int(meta.block_table[r, j // bs])
+            slots.append(b * bs + j % bs)
+    slots = np.array(slots, dtype=np.int32)
+    blk = torch.from_numpy(slots // bs).long().to(d)
+    off = torch.from_numpy(slots % bs).long().to(d)
+    rk = k[blk, :, off].contiguous()           # [T][Hkv][D] bf16
+    rv = v[blk, :, off].contiguous()
+    shape = (meta.num_blocks, geom.num_kv_heads, bs, geom.head_dim)
+    kc = torch.full(shape, 0x7F, dtype=torch.uint8, device=d)
+    vc = kc.clone()
+    ks = torch.full(shape[:-1], float("nan"), dtype=torch.float32, device=d)
+    vs = ks.clone()
+    yb.kv_scatter(rk, rv, torch.from_numpy(slots).to(d), kc, vc, ks, vs)
+    table = torch.from_numpy(meta.block_table).to(d)
+    seq = torch.from_numpy(meta.seq_lens).to(d)
+    out = yb.cross_attn_varlen(q, kc, vc, table, seq, meta.max_seq_len, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    codes0 = np.full(shape, 0x7F, dtype=np.uint8)
+    sc0 = np.full(shape[:-1], np.nan, dtype=np.float32)
+    ok_, ov_, oks, ovs = oracle.kv_scatter(host(rk), host(rv), slots, codes0, codes0, sc0, sc0)
+    ref = oracle.cross_attention(host(q), oracle.dequantize_cache(ok_, oks), oracle.dequantize_cache(ov_, ovs),
+                                 meta.block_table, meta.seq_lens, 1.0 / math.sqrt(geom.head_dim))
+    err = float(np.abs(out.cpu().double().numpy() - ref).max())
+    say(f"  max abs err {err:.3e}")
+    assert err <= ATTN_ATOL

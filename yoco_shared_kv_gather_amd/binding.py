@@ -25,6 +25,7 @@ YOCO_ERR_WORKSPACE_TOO_SMALL = 3
 YOCO_ERR_HIP = 4
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+DTYPE_FP8_E4M3 = 2
 CROSS_ATTN_QUEUE_BYTES = 2048
 FLAG_REVERSE_ORDER = 1
 
@@ -49,6 +50,10 @@ SIGNATURES = {
     "yoco_cross_attn": (_i32, [_i32, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _f32,
                                _i32, _u32, _vp, _vp, _i64, _vp]),
     "yoco_gather_logits": (_i32, [_vp, _i64, _i64, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]),
+    "yoco_kv_scatter": (_i32, [_i32, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
+    "yoco_kv_append_fp8_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32]),
+    "yoco_kv_append_fp8": (_i32, [_i32, _vp, _i32, _i32, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                  _i32, _vp, _i64, _vp]),
     "yoco_cross_attn_varlen_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "yoco_cross_attn_varlen": (_i32, [_i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                       _i32, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _u32, _vp, _vp, _i64, _vp]),
@@ -169,6 +174,57 @@ def kv_append(x, rms_weight, eps, w_k, w_v, slot_mapping, k_cache, v_cache, work
                                 block_size, head_dim, ws_ptr, ws_bytes, _stream_handle(stream)))
 
 
+def _cache_code(k_cache, q_or_rows) -> int:
+    """Cache dtype code: uint8 storage is an FP8 E4M3 cache, else the cache
+    has the dtype of the queries (or rows)."""
+    torch = _torch()
+    if k_cache.dtype == torch.uint8:
+        return DTYPE_FP8_E4M3
+    code = _dtype_code(k_cache)
+    if code != _dtype_code(q_or_rows):
+        raise TypeError("cache and queries (rows) must share a dtype unless the cache is FP8 (uint8)")
+    return code
+
+
+def kv_scatter(k_rows, v_rows, slot_mapping, k_cache, v_cache, k_scale=None, v_scale=None, stream=None):
+    """Write K/V rows [T][Hkv][D] into their slots; into an FP8 (uint8) cache
+    they are quantized with one scale per (token, KV head)."""
+    src = _dtype_code(k_rows)
+    cache = _cache_code(k_cache, k_rows)
+    num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
+    _check(lib().yoco_kv_scatter(src, _dev(k_rows, "k_rows"), _dev(v_rows, "v_rows"), k_rows.shape[0],
+                                 _i32_dev(slot_mapping, "slot_mapping"), cache, _dev(k_cache, "k_cache"),
+                                 _dev(v_cache, "v_cache"), _dev(k_scale, "k_scale") if k_scale is not None else None,
+                                 _dev(v_scale, "v_scale") if v_scale is not None else None, num_blocks, num_kv_heads,
+                                 block_size, head_dim, _stream_handle(stream)))
+
+
+def kv_append_fp8_workspace_size(dtype_code: int, num_tokens: int, hidden: int, num_kv_heads: int,
+                                 head_dim: int) -> int:
+    return int(lib().yoco_kv_append_fp8_workspace_size(dtype_code, num_tokens, hidden, num_kv_heads, head_dim))
+
+
+def kv_append_fp8(x, rms_weight, eps, w_k, w_v, slot_mapping, k_cache, v_cache, k_scale, v_scale, workspace=None,
+                  stream=None):
+    """RMSNorm + shared K/V projection of every row of x, quantized into an
+    FP8 (uint8) cache with per-(token, KV head) scales."""
+    torch = _torch()
+    code = _dtype_code(x)
+    num_blocks, num_kv_heads, block_size, head_dim = k_cache.shape
+    hidden = x.shape[1]
+    need = kv_append_fp8_workspace_size(code, x.shape[0], hidden, num_kv_heads, head_dim)
+    if need < 0:
+        raise YocoError(YOCO_ERR_INVALID_ARGUMENT, "bad kv_append_fp8 shape")
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(lib().yoco_kv_append_fp8(code, _dev(x, "x"), x.shape[0], hidden, _dev(rms_weight, "rms_weight"),
+                                    float(eps), _dev(w_k, "w_k"), _dev(w_v, "w_v"),
+                                    _i32_dev(slot_mapping, "slot_mapping"), _dev(k_cache, "k_cache"),
+                                    _dev(v_cache, "v_cache"), _dev(k_scale, "k_scale"), _dev(v_scale, "v_scale"),
+                                    num_blocks, num_kv_heads, block_size, head_dim, _dev(workspace, "workspace"),
+                                    workspace.numel(), _stream_handle(stream)))
+
+
 # ---- yoco_cross_attn -----------------------------------------------------------------
 
 def cross_attn_partition_tokens(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size,
@@ -251,12 +307,16 @@ def cross_attn_varlen_workspace_size(num_rows, num_seqs, num_q_heads, num_kv_hea
 
 
 def cross_attn_varlen(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, query_start_loc=None, max_query_len=1,
-                      window=0, scale=None, partition_tokens=0, flags=0, out=None, workspace=None, stream=None):
+                      window=0, scale=None, partition_tokens=0, flags=0, out=None, workspace=None, stream=None,
+                      k_scale=None, v_scale=None):
     """One cross layer with several query rows per request (query_start_loc,
     rows aligned to the end of each context, causal) and an optional sliding
-    window.  q and out are [num_rows][Hq][D]."""
+    window.  q and out are [num_rows][Hq][D].  An FP8 cache is uint8 storage
+    with k_scale / v_scale [num_blocks][Hkv][block_size] (q in bf16)."""
     torch = _torch()
-    code = _dtype_code(q)
+    code = _cache_code(k_cache, q)
+    if code == DTYPE_FP8_E4M3 and q.dtype != torch.bfloat16:
+        raise TypeError("queries must be bfloat16 with an FP8 cache")
     num_rows, num_q_heads, head_dim = q.shape
     num_blocks, num_kv_heads, block_size, _ = k_cache.shape
     num_seqs = seq_lens.numel()
@@ -272,7 +332,9 @@ def cross_attn_varlen(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, q
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     qsl_ptr = _i32_dev(query_start_loc, "query_start_loc") if query_start_loc is not None else None
     _check(lib().yoco_cross_attn_varlen(code, _dev(q, "q"), num_rows, qsl_ptr, num_seqs, int(max_query_len),
-                                        num_q_heads, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), None, None,
+                                        num_q_heads, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+                                        _dev(k_scale, "k_scale") if k_scale is not None else None,
+                                        _dev(v_scale, "v_scale") if v_scale is not None else None,
                                         num_blocks, num_kv_heads, block_size, head_dim,
                                         _i32_dev(block_table, "block_table"), block_table.shape[1],
                                         _i32_dev(seq_lens, "seq_lens"), int(max_seq_len), int(window), float(scale),

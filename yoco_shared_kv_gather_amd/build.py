@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libyoco.so")
 
-SOURCES = ["abi.hip", "gather_last.hip", "kv_append.hip", "cross_attn.hip"]
+SOURCES = ["abi.hip", "gather_last.hip", "kv_append.hip", "cross_attn.hip", "cross_attn_f32.hip", "cross_attn_bf16.hip",
+           "cross_attn_fp8.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [
@@ -52,7 +53,7 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
+def build(verbose: bool = False, jobs: int = 7) -> str:
     """Compile every source and link libyoco.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()

@@ -22,6 +22,14 @@
 //     few activation rows instead (one bf16 rounding of x*w, as the fold
 //     rounds W*w once), and no fold pass or workspace is used.
 // fp32 path: one workgroup per token, fp32 throughout.
+//
+// 8-bit cache ("KV cache memory systems", section "Quantized cache changes
+// attention inputs"; "YOCO_论文与推理数据流详解" §18.2: quantize the shared
+// K/V once and let every cross layer reuse it): the same kernels write each
+// token's fp32 K^/V^ row to a workspace instead of the cache, and a
+// quantizing scatter stores FP8 E4M3 codes with one fp32 scale per (token,
+// KV head), s = max|x| / 448, code = E4M3(x / s) rounded to nearest even.
+// That scatter is also the public yoco_kv_scatter (rows computed elsewhere).
 
 #include <cmath>
 
@@ -87,6 +95,7 @@ struct AppendArgs {
   int64_t num_slots;          // num_blocks * block_size
   float inv_hidden;
   float eps;
+  float* rows_out;            // fp32 [T][2*Hkv*D] instead of the cache (8-bit cache), or nullptr
 };
 
 // One workgroup: 128 tokens x 256 output features, four wavefronts of 64 x 128
@@ -199,6 +208,26 @@ __global__ __launch_bounds__(kGemmThreads) void kv_append_mfma_kernel(AppendArgs
   }
   __syncthreads();
 
+  if (a.rows_out != nullptr) {
+    // fp32 rows for the quantizing scatter: lane holds rows 4*(lane/16)+0..3
+    // of column lane%16 of each 16x16 tile.
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int lrow = wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+        const int t = m0 + lrow;
+        if (t >= a.num_tokens) continue;
+        const float sc = row_scale[lrow];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int col = n0 + wn * 128 + j * 16 + (lane & 15);
+          if (col < n_total) a.rows_out[static_cast<int64_t>(t) * n_total + col] = acc[i][j][e] * sc;
+        }
+      }
+    return;
+  }
+
   // Scaled, rounded tile into LDS (the staging buffers are free now).  Lane
   // holds rows 4*(lane/16)+0..3 of column lane%16 of each 16x16 tile.
   uint16_t* ot = lds;
@@ -244,7 +273,7 @@ __global__ __launch_bounds__(kF32Threads) void kv_append_f32_kernel(
     const float* __restrict__ x, int hidden, const float* __restrict__ w_rms, float eps,
     const float* __restrict__ w_k, const float* __restrict__ w_v, const int32_t* __restrict__ slots,
     int64_t num_slots, float* __restrict__ k_cache, float* __restrict__ v_cache, int num_kv_heads,
-    int block_size, int bs_shift, int head_dim) {
+    int block_size, int bs_shift, int head_dim, float* __restrict__ rows_out) {
   extern __shared__ float xs[];
   __shared__ float partial[kF32Threads / 64];
   const int t = blockIdx.x;
@@ -285,8 +314,12 @@ __global__ __launch_bounds__(kF32Threads) void kv_append_f32_kernel(
     if (lane == 0) {
       const int h = hd / head_dim;
       const int d = hd - h * head_dim;
-      float* cache = is_v ? v_cache : k_cache;
-      cache[((blk * num_kv_heads + h) * block_size + off) * head_dim + d] = acc;
+      if (rows_out != nullptr) {
+        rows_out[static_cast<int64_t>(t) * 2 * out_half + o] = acc;
+      } else {
+        float* cache = is_v ? v_cache : k_cache;
+        cache[((blk * num_kv_heads + h) * block_size + off) * head_dim + d] = acc;
+      }
     }
   }
 }
@@ -313,6 +346,7 @@ struct SkinnyArgs {
   int64_t num_slots;
   float inv_hidden;
   float eps;
+  float* rows_out;            // fp32 [T][2*Hkv*D] instead of the cache (8-bit cache), or nullptr
 };
 
 // kMT tiles of 16 tokens (T <= 16*kMT).  Wavefront w of kSkinnyWaves covers
@@ -398,12 +432,106 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void kv_append_skinny_kernel(Ski
       sq += s_ssq[w][mt * 16 + (l >> 4) * 4 + i];
     }
     const float scale = 1.0f / sqrtf(sq * a.inv_hidden + a.eps);
+    if (a.rows_out != nullptr) {
+      a.rows_out[static_cast<int64_t>(row) * 2 * a.out_half + n0 + (l & 15)] = sum * scale;
+      continue;
+    }
     const int c = n0 + (l & 15) - (is_v ? a.out_half : 0);
     const int h = c / a.head_dim;
     const int d = c - h * a.head_dim;
     uint16_t* cache = is_v ? a.v_cache : a.k_cache;
     cache[(((slot >> a.bs_shift) * a.num_kv_heads + h) * a.block_size + (slot & (a.block_size - 1))) * a.head_dim + d] =
         f32_to_bf16_rne(sum * scale);
+  }
+}
+
+// ---- scatter of given rows, optionally quantizing to FP8 E4M3 ---------------------
+
+constexpr int kScatterThreads = 256;
+
+struct ScatterArgs {
+  const void* k_src;          // K rows: token t, KV head h at k_src + t*token_stride + h*D (source elements)
+  const void* v_src;
+  int64_t token_stride;       // source elements between tokens
+  const int32_t* slots;
+  void* k_cache;
+  void* v_cache;
+  float* k_scale;             // [num_blocks][Hkv][bs] (8-bit cache), else nullptr
+  float* v_scale;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t bs_shift;
+  int64_t num_slots;
+};
+
+// One workgroup per token; wavefront w takes the (K or V, KV head) rows
+// w, w+4, ...  Quantizing: lane l holds D/64 consecutive values, the row's
+// largest magnitude comes from a wavefront max over the fp32 bit patterns
+// (ordered like the magnitudes, and above every finite value for inf and
+// NaN), s = max / 448 and code = E4M3(x / s), both divisions in fp32; a row
+// holding inf or NaN is stored as NaN codes (its scale is inf or NaN), a row
+// of zeros as zero codes with scale 0.  Copying: the row's bytes as they are.
+template <bool kSrcF32, bool kQuant>
+__global__ __launch_bounds__(kScatterThreads) void kv_scatter_kernel(ScatterArgs a) {
+  const int t = blockIdx.x;
+  const int64_t slot = a.slots[t];
+  if (slot < 0 || slot >= a.num_slots) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t blk = slot >> a.bs_shift;
+  const int64_t off = slot & (a.block_size - 1);
+  const int D = a.head_dim;
+  constexpr int kSrcBytes = kSrcF32 ? 4 : 2;
+  for (int p = wave; p < 2 * a.num_kv_heads; p += kScatterThreads / 64) {
+    const bool is_v = p >= a.num_kv_heads;
+    const int h = is_v ? p - a.num_kv_heads : p;
+    const char* src = static_cast<const char*>(is_v ? a.v_src : a.k_src) +
+                      (static_cast<int64_t>(t) * a.token_stride + static_cast<int64_t>(h) * D) * kSrcBytes;
+    const int64_t row = (blk * a.num_kv_heads + h) * a.block_size + off;
+    if constexpr (kQuant) {
+      const int per = D / 64;                          // 1, 2 or 4 values per lane
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (e >= per) break;
+        const int i = lane * per + e;
+        if constexpr (kSrcF32) {
+          x[e] = reinterpret_cast<const float*>(src)[i];
+        } else {
+          x[e] = __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(src)[i]) << 16);
+        }
+      }
+      uint32_t mbits = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e < per) mbits = max(mbits, __float_as_uint(x[e]) & 0x7fffffffu);
+#pragma unroll
+      for (int mask = 32; mask > 0; mask >>= 1)
+        mbits = max(mbits, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mbits), mask, 64)));
+      const float s = __uint_as_float(mbits) / 448.0f;
+      const bool finite = mbits < 0x7f800000u;
+      uint32_t packed = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (e >= per) break;
+        const uint32_t code = !finite ? 0x7fu : (s == 0.0f ? 0u : yoco::f32_to_e4m3_rne(x[e] / s));
+        packed |= code << (8 * e);
+      }
+      uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache) + row * D + lane * per;
+      if (per == 1) {
+        *dst = static_cast<uint8_t>(packed);
+      } else if (per == 2) {
+        *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(packed);
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = packed;
+      }
+      if (lane == 0) (is_v ? a.v_scale : a.k_scale)[row] = s;
+    } else {
+      const int chunks = D * kSrcBytes / 16;
+      uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(is_v ? a.v_cache : a.k_cache) + row * D * kSrcBytes);
+      for (int c = lane; c < chunks; c += 64) dst[c] = reinterpret_cast<const uint4*>(src)[c];
+    }
   }
 }
 
@@ -418,11 +546,16 @@ extern "C" int64_t yoco_kv_append_workspace_size(int32_t dtype, int32_t hidden, 
   return static_cast<int64_t>(2) * num_kv_heads * head_dim * hidden * 2;
 }
 
-extern "C" int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_tokens, int32_t hidden,
-                                  const void* rms_weight, float eps, const void* w_k, const void* w_v,
-                                  const int32_t* slot_mapping, void* k_cache, void* v_cache, int32_t num_blocks,
-                                  int32_t num_kv_heads, int32_t block_size, int32_t head_dim, void* workspace,
-                                  int64_t workspace_bytes, void* stream) {
+namespace {
+
+// The projection of every scheduled token: into its cache slots
+// (rows_out == nullptr; caches in `dtype`) or as fp32 rows [T][2*Hkv*D] into
+// rows_out (the caches are then not touched).  The fold workspace is the
+// first `fold` bytes of `workspace`.
+int32_t append_impl(int32_t dtype, const void* x, int32_t num_tokens, int32_t hidden, const void* rms_weight,
+                    float eps, const void* w_k, const void* w_v, const int32_t* slot_mapping, void* k_cache,
+                    void* v_cache, int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                    void* workspace, int64_t workspace_bytes, float* rows_out, int64_t rows_bytes, void* stream) {
   using namespace yoco;
   if (dtype != YOCO_DTYPE_F32 && dtype != YOCO_DTYPE_BF16)
     return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append: unknown dtype %d", dtype);
@@ -435,16 +568,16 @@ extern "C" int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_toke
   if (hidden % 64 != 0) return fail(YOCO_ERR_UNSUPPORTED, "kv_append: hidden %d is not a multiple of 64", hidden);
   if (dtype == YOCO_DTYPE_F32 && hidden > 16384)
     return fail(YOCO_ERR_UNSUPPORTED, "kv_append: fp32 path supports hidden <= 16384");
-  const int64_t need = yoco_kv_append_workspace_size(dtype, hidden, num_kv_heads, head_dim);
+  const int64_t need = yoco_kv_append_workspace_size(dtype, hidden, num_kv_heads, head_dim) + rows_bytes;
   if (workspace_bytes < need)
     return fail(YOCO_ERR_WORKSPACE_TOO_SMALL, "kv_append: workspace %lld bytes, need %lld",
                 (long long)workspace_bytes, (long long)need);
   if (num_tokens == 0) return YOCO_OK;
   if (x == nullptr || rms_weight == nullptr || w_k == nullptr || w_v == nullptr || slot_mapping == nullptr ||
-      k_cache == nullptr || v_cache == nullptr || (need > 0 && workspace == nullptr))
+      (rows_out == nullptr && (k_cache == nullptr || v_cache == nullptr)) || (need > 0 && workspace == nullptr))
     return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append: null pointer");
-  if (!aligned16(x) || !aligned16(rms_weight) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(k_cache) ||
-      !aligned16(v_cache) || (need > 0 && !aligned16(workspace)))
+  if (!aligned16(x) || !aligned16(rms_weight) || !aligned16(w_k) || !aligned16(w_v) ||
+      (rows_out == nullptr && (!aligned16(k_cache) || !aligned16(v_cache))) || (need > 0 && !aligned16(workspace)))
     return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append: buffers must be 16-byte aligned");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -456,7 +589,7 @@ extern "C" int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_toke
                        static_cast<const float*>(x), hidden, static_cast<const float*>(rms_weight), eps,
                        static_cast<const float*>(w_k), static_cast<const float*>(w_v), slot_mapping, num_slots,
                        static_cast<float*>(k_cache), static_cast<float*>(v_cache), num_kv_heads, block_size,
-                       bs_shift, head_dim);
+                       bs_shift, head_dim, rows_out);
     return launch_result("kv_append");
   }
 
@@ -480,6 +613,7 @@ extern "C" int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_toke
     k.num_slots = num_slots;
     k.inv_hidden = 1.0f / static_cast<float>(hidden);
     k.eps = eps;
+    k.rows_out = rows_out;
     const dim3 grid(static_cast<uint32_t>(2 * out_half / kSkinnyCols));
     const dim3 block(64 * kSkinnyWaves);
     if (num_tokens <= 16) {
@@ -513,8 +647,128 @@ extern "C" int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_toke
   a.num_slots = num_slots;
   a.inv_hidden = 1.0f / static_cast<float>(hidden);
   a.eps = eps;
+  a.rows_out = rows_out;
   a.n_tiles = static_cast<int32_t>(ceil_div(2 * out_half, kBN));
   const int64_t tiles = ceil_div(num_tokens, kBM) * a.n_tiles;
   hipLaunchKernelGGL(kv_append_mfma_kernel, dim3(static_cast<uint32_t>(tiles)), dim3(kGemmThreads), 0, s, a);
   return launch_result("kv_append");
+}
+
+bool is_f8(int32_t dtype) { return dtype == YOCO_DTYPE_FP8_E4M3; }
+
+// Launch the scatter of rows [T][Hkv][D] (token stride given) into the cache.
+int32_t scatter_impl(bool src_f32, bool quant, const void* k_src, const void* v_src, int64_t token_stride,
+                     int32_t num_tokens, const int32_t* slot_mapping, void* k_cache, void* v_cache, float* k_scale,
+                     float* v_scale, int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                     hipStream_t s) {
+  ScatterArgs a;
+  a.k_src = k_src;
+  a.v_src = v_src;
+  a.token_stride = token_stride;
+  a.slots = slot_mapping;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.block_size = block_size;
+  a.bs_shift = yoco::ilog2(block_size);
+  a.num_slots = static_cast<int64_t>(num_blocks) * block_size;
+  const dim3 grid(static_cast<uint32_t>(num_tokens)), block(kScatterThreads);
+  if (quant) {
+    if (src_f32) hipLaunchKernelGGL((kv_scatter_kernel<true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((kv_scatter_kernel<false, true>), grid, block, 0, s, a);
+  } else {
+    if (src_f32) hipLaunchKernelGGL((kv_scatter_kernel<true, false>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((kv_scatter_kernel<false, false>), grid, block, 0, s, a);
+  }
+  return yoco::launch_result("kv_scatter");
+}
+
+int64_t rows_bytes_of(int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim) {
+  return static_cast<int64_t>(num_tokens) * 2 * num_kv_heads * head_dim * 4;
+}
+
+}  // namespace
+
+extern "C" int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_tokens, int32_t hidden,
+                                  const void* rms_weight, float eps, const void* w_k, const void* w_v,
+                                  const int32_t* slot_mapping, void* k_cache, void* v_cache, int32_t num_blocks,
+                                  int32_t num_kv_heads, int32_t block_size, int32_t head_dim, void* workspace,
+                                  int64_t workspace_bytes, void* stream) {
+  return append_impl(dtype, x, num_tokens, hidden, rms_weight, eps, w_k, w_v, slot_mapping, k_cache, v_cache,
+                     num_blocks, num_kv_heads, block_size, head_dim, workspace, workspace_bytes, nullptr, 0, stream);
+}
+
+extern "C" int64_t yoco_kv_append_fp8_workspace_size(int32_t dtype, int32_t num_tokens, int32_t hidden,
+                                                     int32_t num_kv_heads, int32_t head_dim) {
+  if (num_tokens < 0) return -1;
+  const int64_t fold = yoco_kv_append_workspace_size(dtype, hidden, num_kv_heads, head_dim);
+  if (fold < 0) return -1;
+  return yoco::round_up(fold, 256) + rows_bytes_of(num_tokens, num_kv_heads, head_dim);
+}
+
+extern "C" int32_t yoco_kv_append_fp8(int32_t dtype, const void* x, int32_t num_tokens, int32_t hidden,
+                                      const void* rms_weight, float eps, const void* w_k, const void* w_v,
+                                      const int32_t* slot_mapping, void* k_cache, void* v_cache, float* k_scale,
+                                      float* v_scale, int32_t num_blocks, int32_t num_kv_heads, int32_t block_size,
+                                      int32_t head_dim, void* workspace, int64_t workspace_bytes, void* stream) {
+  using namespace yoco;
+  if (num_tokens < 0 || hidden <= 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append_fp8: negative or zero size argument");
+  const int64_t fold = yoco_kv_append_workspace_size(dtype, hidden, num_kv_heads, head_dim);
+  const int64_t need = yoco_kv_append_fp8_workspace_size(dtype, num_tokens, hidden, num_kv_heads, head_dim);
+  if (fold < 0 || need < 0) return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append_fp8: bad dtype or shape");
+  if (workspace_bytes < need)
+    return fail(YOCO_ERR_WORKSPACE_TOO_SMALL, "kv_append_fp8: workspace %lld bytes, need %lld",
+                (long long)workspace_bytes, (long long)need);
+  if (num_tokens > 0 && (k_cache == nullptr || v_cache == nullptr || k_scale == nullptr || v_scale == nullptr ||
+                         workspace == nullptr))
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append_fp8: null pointer");
+  if (num_tokens > 0 && (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(k_cache) & 3) != 0 ||
+                         (reinterpret_cast<uintptr_t>(v_cache) & 3) != 0 ||
+                         (reinterpret_cast<uintptr_t>(k_scale) & 3) != 0 ||
+                         (reinterpret_cast<uintptr_t>(v_scale) & 3) != 0))
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append_fp8: workspace must be 16-byte and caches 4-byte aligned");
+  float* rows = num_tokens > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(fold, 256))
+                               : nullptr;
+  const int64_t rb = rows_bytes_of(num_tokens, num_kv_heads, head_dim);
+  int32_t st = append_impl(dtype, x, num_tokens, hidden, rms_weight, eps, w_k, w_v, slot_mapping, k_cache, v_cache,
+                           num_blocks, num_kv_heads, block_size, head_dim, workspace, workspace_bytes - rb, rows, 0,
+                           stream);
+  if (st != YOCO_OK || num_tokens == 0) return st;
+  const int64_t out_half = static_cast<int64_t>(num_kv_heads) * head_dim;
+  return scatter_impl(true, true, rows, rows + out_half, 2 * out_half, num_tokens, slot_mapping, k_cache, v_cache,
+                      k_scale, v_scale, num_blocks, num_kv_heads, block_size, head_dim,
+                      static_cast<hipStream_t>(stream));
+}
+
+extern "C" int32_t yoco_kv_scatter(int32_t src_dtype, const void* k_rows, const void* v_rows, int32_t num_tokens,
+                                   const int32_t* slot_mapping, int32_t cache_dtype, void* k_cache, void* v_cache,
+                                   float* k_scale, float* v_scale, int32_t num_blocks, int32_t num_kv_heads,
+                                   int32_t block_size, int32_t head_dim, void* stream) {
+  using namespace yoco;
+  if (src_dtype != YOCO_DTYPE_F32 && src_dtype != YOCO_DTYPE_BF16)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_scatter: unknown source dtype %d", src_dtype);
+  const bool quant = is_f8(cache_dtype);
+  if (!quant && cache_dtype != src_dtype)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_scatter: cache dtype %d must be the source dtype or FP8", cache_dtype);
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_scatter: negative or zero size argument");
+  if (!supported_dim(head_dim)) return fail(YOCO_ERR_UNSUPPORTED, "kv_scatter: head_dim %d not in {64,128,256}", head_dim);
+  if (!is_pow2(block_size) || block_size > 256)
+    return fail(YOCO_ERR_UNSUPPORTED, "kv_scatter: block_size %d is not a power of two <= 256", block_size);
+  if (quant != (k_scale != nullptr) || quant != (v_scale != nullptr))
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_scatter: scales are required for, and only for, an FP8 cache");
+  if (num_tokens == 0) return YOCO_OK;
+  if (k_rows == nullptr || v_rows == nullptr || slot_mapping == nullptr || k_cache == nullptr || v_cache == nullptr)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_scatter: null pointer");
+  if (!aligned16(k_rows) || !aligned16(v_rows) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_scatter: rows and caches must be 16-byte aligned");
+  clear_launch_error();
+  return scatter_impl(src_dtype == YOCO_DTYPE_F32, quant, k_rows, v_rows,
+                      static_cast<int64_t>(num_kv_heads) * head_dim, num_tokens, slot_mapping, k_cache, v_cache,
+                      k_scale, v_scale, num_blocks, num_kv_heads, block_size, head_dim,
+                      static_cast<hipStream_t>(stream));
 }

@@ -48,4 +48,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf2));
 }
 
+// fp32 -> FP8 E4M3 (finite-only variant: bias 7, no infinities, 0x7F/0xFF
+// NaN, largest finite 448), rounded to nearest with ties to the even code.
+// Magnitudes above 448 saturate to 448; NaN gives 0x7F.  Integer steps from
+// the format definition, so the result does not depend on a conversion
+// instruction's rounding or overflow mode.
+__device__ __forceinline__ uint32_t f32_to_e4m3_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;                       // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;               // >= 448: saturate
+  if (a < 0x3c800000u) {                                   // below 2^-6: subnormal codes m * 2^-9
+    const float t = __uint_as_float(a) * 512.0f;           // exact scaling
+    return sign | static_cast<uint32_t>(__builtin_rintf(t));   // 0..8 (8 is the smallest normal)
+  }
+  // normal: keep 3 of the 23 mantissa bits, ties to even, then rebias 127 -> 7
+  const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+  const uint32_t code = (r >> 20) - (120u << 3);
+  return sign | (code < 0x7eu ? code : 0x7eu);
+}
+
 }  // namespace yoco

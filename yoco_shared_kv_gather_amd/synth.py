@@ -360,6 +360,29 @@ def make_cache(meta: Metadata, device="cpu", seed: int = SEED_BASE):
     return k, v
 
 
+def make_fp8_cache(meta: Metadata, device="cpu", seed: int = SEED_BASE):
+    """An 8-bit (FP8 E4M3) cache: codes ``uint8 [num_blocks][Hkv][block_size]
+    [D]`` and fp32 scales ``[num_blocks][Hkv][block_size]`` for K and for V.
+    Live slots hold codes drawn uniformly from the 254 finite codes and
+    scales from U(0.002, 0.02) (stored values of magnitude up to ~9); free
+    blocks and tail slots hold the NaN code 0x7F and NaN scales."""
+    import torch
+    geom = meta.geom
+    ss = _seed_seq(meta.config_id, meta.size, seed)
+    shape = (meta.num_blocks, geom.num_kv_heads, geom.block_size, geom.head_dim)
+    live = torch.from_numpy(live_slot_mask(meta)).to(device).view(meta.num_blocks, 1, geom.block_size)
+    out = []
+    for stream in (_S_K, _S_V):
+        g = _generator(device, _child_seed(ss, stream))
+        codes = torch.randint(0, 254, shape, generator=g, device=device, dtype=torch.int32)
+        codes = torch.where(codes >= 0x7F, codes + 1, codes).to(torch.uint8)         # skip 0x7F; 0xFF is > 253 + 1
+        scales = torch.rand(shape[:-1], generator=g, device=device, dtype=torch.float32) * 0.018 + 0.002
+        codes.masked_fill_(~live.unsqueeze(-1), 0x7F)
+        scales.masked_fill_(~live, float("nan"))
+        out += [codes, scales]
+    return tuple(out)          # k_codes, k_scale, v_codes, v_scale
+
+
 def make_queries(meta: Metadata, device="cpu", seed: int = SEED_BASE, num_layers: Optional[int] = None,
                  rows: Optional[int] = None):
     """q for every cross layer: ``[L][rows][Hq][D]`` N(0,1) in the workload
