@@ -48,6 +48,7 @@ def parse():
     p.add_argument("--partition-tokens", type=int, default=0, help="0 = library default")
     p.add_argument("--query-rows", type=int, default=1, help="query rows per request (decode workloads 2, 3, 5)")
     p.add_argument("--window", type=int, default=0, help="sliding window of every cross layer in tokens (0 = none)")
+    p.add_argument("--fp8", action="store_true", help="8-bit shared cache (FP8 E4M3 codes, per-row scales)")
     p.add_argument("--no-flush", action="store_true", help="keep the last-level cache warm between steps")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -72,7 +73,7 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
-def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s, rows_per_req=1, window=0):
+def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s, rows_per_req=1, window=0, ks=None, vs=None):
     """Time the float64 oracle on host cores on a bounded sample of the same
     step: the append and gather of all scheduled tokens, then whole cross
     layers (every request) until the time budget is spent; the per-layer
@@ -93,11 +94,22 @@ def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s, rows_per_req=1, wi
         n = int(meta.seq_lens[r])
         nb = -(-n // bs)
         blocks = torch.from_numpy(meta.block_table[r, :nb].astype(np.int64)).to(k.device)
+        if ks is not None:
+            # an 8-bit cache: the values it holds (dequantized once, outside the timing)
+            per_req.append((n, nb, oracle.dequantize_cache(k.index_select(0, blocks).cpu().numpy(),
+                                                           ks.index_select(0, blocks).cpu().numpy()),
+                            oracle.dequantize_cache(v.index_select(0, blocks).cpu().numpy(),
+                                                    vs.index_select(0, blocks).cpu().numpy())))
+            continue
         per_req.append((n, nb, k.index_select(0, blocks).float().cpu().numpy(),
                         v.index_select(0, blocks).float().cpu().numpy()))
     with threadpoolctl.threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        oracle.kv_project(x_host, w_host[0], 1e-6, w_host[1], w_host[2], geom.num_kv_heads, geom.head_dim)
+        if ks is not None:
+            oracle.kv_append_fp8(x_host, w_host[0], 1e-6, w_host[1], w_host[2], meta.slot_mapping, geom.num_kv_heads,
+                                 geom.head_dim)
+        else:
+            oracle.kv_project(x_host, w_host[0], 1e-6, w_host[1], w_host[2], geom.num_kv_heads, geom.head_dim)
         if Q > 1:
             idx = np.arange(meta.num_tokens)
             oracle.cross_metadata(idx, meta.cu_seqlens)
@@ -112,7 +124,7 @@ def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s, rows_per_req=1, wi
             qh = q[layers].float().cpu().numpy()
             for r, (n, nb, kc, vc) in enumerate(per_req):
                 table = np.arange(max(nb, 1))[None, :]
-                if Q > 1 or window > 0:
+                if Q > 1 or window > 0 or ks is not None:
                     oracle.cross_attention_varlen(qh[r * Q:(r + 1) * Q], kc, vc, table, np.array([n]),
                                                   np.array([0, Q]), scale, window)
                 else:
@@ -129,6 +141,33 @@ def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s, rows_per_req=1, wi
                    f"over all {meta.num_reqs} requests ({t_other + t_attn:.1f} s of CPU time, float64 numpy, "
                    f"BLAS limited to 1 thread); per-layer time scaled to {geom.num_layers} layers"),
     }
+
+
+def quantize_cache(meta, k, v, yb, torch):
+    """The workload's bf16 cache rows, quantized into an FP8 cache with the
+    library's own scatter (free blocks and tail slots keep NaN codes/scales)."""
+    bs = meta.geom.block_size
+    dev = k.device
+    live = torch.from_numpy(synth_live(meta)).to(dev)
+    slots = torch.nonzero(live.reshape(-1)).reshape(-1).to(torch.int32)
+    kc = torch.full(k.shape, 0x7F, dtype=torch.uint8, device=dev)
+    vc = torch.full(v.shape, 0x7F, dtype=torch.uint8, device=dev)
+    ks = torch.full(k.shape[:-1], float("nan"), dtype=torch.float32, device=dev)
+    vs = torch.full(v.shape[:-1], float("nan"), dtype=torch.float32, device=dev)
+    step = 1 << 18
+    for s0 in range(0, slots.numel(), step):
+        sl = slots[s0:s0 + step]
+        blk, off = (sl // bs).long(), (sl % bs).long()
+        rk = k[blk, :, off].contiguous()
+        rv = v[blk, :, off].contiguous()
+        yb.kv_scatter(rk, rv, sl.contiguous(), kc, vc, ks, vs)
+    torch.cuda.synchronize()
+    return kc, vc, ks, vs
+
+
+def synth_live(meta):
+    from yoco_shared_kv_gather_amd import synth
+    return synth.live_slot_mask(meta)
 
 
 def main():
@@ -156,7 +195,7 @@ def main():
     torch.cuda.set_device(dev)
     meta = synth.make_metadata(args.workload, "full", args.seed)
     Q, W = args.query_rows, args.window
-    varlen = Q > 1 or W > 0
+    varlen = Q > 1 or W > 0 or args.fp8
     if Q > 1:
         if args.workload not in (2, 3, 5):
             log("--query-rows applies to the decode workloads 2, 3 and 5")
@@ -168,6 +207,12 @@ def main():
     log(f"workload {geom.name}: {R} requests, {int(meta.seq_lens.sum())} context tokens, "
         f"{geom.num_layers} layers, {Q} query rows per request, window {W}")
     k, v = synth.make_cache(meta, dev, args.seed)
+    ks = vs = None
+    if args.fp8:
+        if geom.dtype != "bf16":
+            log("--fp8 needs a bf16 workload")
+            sys.exit(2)
+        k, v, ks, vs = quantize_cache(meta, k, v, yb, torch)
     q = synth.make_queries(meta, dev, args.seed, rows=num_rows)
     x, w_rms, w_k, w_v = synth.make_append_inputs(meta, dev, args.seed)
     table = torch.from_numpy(meta.block_table).to(dev)
@@ -186,8 +231,12 @@ def main():
         ws_bytes = yb.cross_attn_workspace_size(R, geom.num_q_heads, geom.num_kv_heads, geom.head_dim,
                                                 meta.max_seq_len, geom.block_size, args.partition_tokens)
     ws = torch.zeros(max(1, ws_bytes), dtype=torch.uint8, device=dev)
-    ws_append = torch.zeros(max(1, yb.kv_append_workspace_size(code, geom.hidden, geom.num_kv_heads, geom.head_dim)),
-                            dtype=torch.uint8, device=dev)
+    if args.fp8:
+        ws_append_bytes = yb.kv_append_fp8_workspace_size(code, meta.num_tokens, geom.hidden, geom.num_kv_heads,
+                                                          geom.head_dim)
+    else:
+        ws_append_bytes = yb.kv_append_workspace_size(code, geom.hidden, geom.num_kv_heads, geom.head_dim)
+    ws_append = torch.zeros(max(16, ws_append_bytes), dtype=torch.uint8, device=dev)
     outs = torch.empty((geom.num_layers, num_rows, geom.num_q_heads, geom.head_dim), dtype=torch.float32, device=dev)
     rows = torch.empty((num_rows, geom.hidden), dtype=x.dtype, device=dev)
     rows_idx = torch.empty(R, dtype=torch.int32, device=dev)
@@ -202,7 +251,10 @@ def main():
     L = geom.num_layers
 
     def step(ev_layers=None):
-        yb.kv_append(x, w_rms, 1e-6, w_k, w_v, slots, k, v, workspace=ws_append, stream=stream)
+        if args.fp8:
+            yb.kv_append_fp8(x, w_rms, 1e-6, w_k, w_v, slots, k, v, ks, vs, workspace=ws_append, stream=stream)
+        else:
+            yb.kv_append(x, w_rms, 1e-6, w_k, w_v, slots, k, v, workspace=ws_append, stream=stream)
         if Q > 1:
             yb.gather_logits(x, logits_idx, cu, out=rows, out_query_start_loc=cross_qsl, out_max_query_len=cross_max,
                              stream=stream)
@@ -215,7 +267,7 @@ def main():
                 yb.cross_attn_varlen(q[l], k, v, table, seq, meta.max_seq_len,
                                      query_start_loc=cross_qsl if Q > 1 else None, max_query_len=Q, window=W,
                                      partition_tokens=args.partition_tokens, flags=l & 1, out=outs[l], workspace=ws,
-                                     stream=stream)
+                                     stream=stream, k_scale=ks, v_scale=vs)
             else:
                 yb.cross_attn(q[l], k, v, table, seq, meta.max_seq_len, partition_tokens=args.partition_tokens,
                               flags=l & 1, out=outs[l], workspace=ws, stream=stream)
@@ -248,22 +300,24 @@ def main():
     tokens_per_s = num_rows / (ms_per_step * 1e-3)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (events), wall {1e3 * wall / args.steps:.3f} ms/step")
 
+    cache_bytes = 1 if args.fp8 else geom.elem_bytes
     layer_bytes = bm.attn_layer_bytes(meta.seq_lens, geom.num_q_heads, geom.num_kv_heads, geom.head_dim,
-                                      geom.block_size, geom.elem_bytes, query_lens=meta.query_lens if Q > 1 else None,
-                                      window=W)
+                                      geom.block_size, cache_bytes, query_lens=meta.query_lens if Q > 1 else None,
+                                      window=W, q_bytes=geom.elem_bytes, scale_bytes=8 if args.fp8 else 0)
     written = int((meta.slot_mapping >= 0).sum())
     step_bytes = (L * layer_bytes
                   + bm.append_bytes(meta.num_tokens, geom.hidden, geom.num_kv_heads, geom.head_dim, geom.elem_bytes,
                                     written)
+                  - (written * 2 * geom.num_kv_heads * geom.head_dim * (geom.elem_bytes - 1) if args.fp8 else 0)
                   + bm.gather_bytes(num_rows, geom.hidden * geom.elem_bytes))
     attn_us = float(layer_ms.mean()) * 1e3
     achieved = layer_bytes / (attn_us * 1e-6) / 1e9
     group = geom.num_q_heads // geom.num_kv_heads
     rows_per_item = 0 if Q == 1 else 8 // group
-    attn_kernel = (f"cross_attn_kernel<{'true' if geom.dtype == 'bf16' else 'false'}, {geom.head_dim}, {group}, "
-                   f"{rows_per_item}>")
+    elem_type = 2 if args.fp8 else (1 if geom.dtype == "bf16" else 0)
+    attn_kernel = f"cross_attn_kernel<{elem_type}, {geom.head_dim}, {group}, {rows_per_item}>"
     merge_kernel = f"cross_attn_merge_kernel<{geom.head_dim}>"
-    variant = geom.name + (f"_q{Q}" if Q > 1 else "") + (f"_w{W}" if W > 0 else "")
+    variant = geom.name + (f"_q{Q}" if Q > 1 else "") + (f"_w{W}" if W > 0 else "") + ("_fp8" if args.fp8 else "")
     measured = profiling.measured_traffic(variant, [attn_kernel, merge_kernel] if nparts > 1 else [attn_kernel])
     traffic = None
     profile_us = None
@@ -283,7 +337,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": geom.dtype,
+        "dtype": "fp8_e4m3 cache, bf16 queries" if args.fp8 else geom.dtype,
         "data": "synthetic",
         "config": {
             "workload": variant,
@@ -323,7 +377,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, args.cpu_seconds, Q, W)
+        result["cpu_baseline"] = cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, args.cpu_seconds, Q, W, ks, vs)
     print(json.dumps(result), flush=True)
 
 

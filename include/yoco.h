@@ -85,6 +85,11 @@ typedef enum yoco_dtype { YOCO_DTYPE_F32 = 0, YOCO_DTYPE_BF16 = 1, YOCO_DTYPE_FP
  * way. */
 #define YOCO_FLAG_REVERSE_ORDER 1u
 
+/* yoco_cross_attn_varlen flag: run the vector-ALU kernel even where the
+ * matrix-core kernel is the default (an FP8 cache, or several query rows per
+ * request).  Same results within the attention tolerance; for comparisons. */
+#define YOCO_FLAG_VECTOR_KERNEL 2u
+
 /* The first YOCO_CROSS_ATTN_QUEUE_BYTES bytes of a yoco_cross_attn workspace
  * are the work-queue counters of its persistent schedule: they must be zero
  * before the first call with that workspace, and every call leaves them zero

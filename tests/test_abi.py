@@ -57,7 +57,7 @@ def _attn(**kw):
     (dict(block_size=12), yb.YOCO_ERR_UNSUPPORTED),
     (dict(part=100), yb.YOCO_ERR_INVALID_ARGUMENT),
     (dict(dtype=7), yb.YOCO_ERR_INVALID_ARGUMENT),
-    (dict(flags=2), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(flags=4), yb.YOCO_ERR_INVALID_ARGUMENT),
     (dict(q=None), yb.YOCO_ERR_INVALID_ARGUMENT),
     (dict(q=FAKE + 4), yb.YOCO_ERR_INVALID_ARGUMENT),
     (dict(num_seqs=-1), yb.YOCO_ERR_INVALID_ARGUMENT),

@@ -148,11 +148,12 @@ def _fp8_case(geom, ctx, qlens, seed):
     return meta, q, kc, ks, vc, vs
 
 
-@pytest.mark.parametrize("hq,hkv,d", [(4, 1, 64), (8, 2, 128), (8, 2, 256), (8, 8, 128), (16, 2, 64)])
+@pytest.mark.parametrize("hq,hkv,d", [(4, 1, 64), (8, 2, 128), (8, 2, 256), (8, 8, 128), (16, 2, 64), (32, 8, 128)])
 @pytest.mark.parametrize("several", [False, True])
 @pytest.mark.parametrize("window", [0, 50])
-def test_attention_fp8(hq, hkv, d, several, window):
-    say(f"cross_attn_varlen FP8: {hq}x{hkv}x{d} several rows {several} window {window}")
+@pytest.mark.parametrize("kernel", ["default", "vector"])
+def test_attention_fp8(hq, hkv, d, several, window, kernel):
+    say(f"cross_attn_varlen FP8: {hq}x{hkv}x{d} several rows {several} window {window} {kernel}")
     geom = synth.custom_geometry("bf16", hq, hkv, d, 16)
     ctx = [5, 300, 1, 0, 64, 129, 3, 700, 2]
     qlens = [3, 4, 1, 2, 5, 1, 6, 2, 0] if several else [1 if c > 0 else 0 for c in ctx]
@@ -172,7 +173,7 @@ def test_attention_fp8(hq, hkv, d, several, window):
             qq[torch.from_numpy(np.nonzero(np.asarray(qlens))[0]).to(dev())] = q
         out = yb.cross_attn_varlen(qq, kc, vc, table, seq, meta.max_seq_len, query_start_loc=qsl,
                                    max_query_len=max(qlens) if several else 1, window=window, partition_tokens=part,
-                                   k_scale=ks, v_scale=vs)
+                                   k_scale=ks, v_scale=vs, flags=yb.FLAG_VECTOR_KERNEL if kernel == "vector" else 0)
         torch.cuda.synchronize()
         got = out.cpu().double().numpy()
         if not several:

@@ -97,22 +97,25 @@ class VarlenCase:
                                              1.0 / math.sqrt(self.geom.head_dim), window)
 
 
-GEOMS = [("bf16", 4, 1, 128), ("bf16", 8, 2, 256), ("bf16", 8, 8, 64), ("bf16", 8, 1, 128), ("f32", 4, 2, 64),
-         ("f32", 16, 2, 128)]
+GEOMS = [("bf16", 4, 1, 128), ("bf16", 8, 2, 256), ("bf16", 8, 8, 64), ("bf16", 8, 1, 128), ("bf16", 2, 1, 64),
+         ("f32", 4, 2, 64), ("f32", 16, 2, 128)]
 
 
 @pytest.mark.parametrize("dtype,hq,hkv,d", GEOMS)
 @pytest.mark.parametrize("window", [0, 1, 37])
 @pytest.mark.parametrize("partition_tokens", [0, 64])
-def test_varlen_rows_and_window(dtype, hq, hkv, d, window, partition_tokens):
+@pytest.mark.parametrize("kernel", ["default", "vector"])
+def test_varlen_rows_and_window(dtype, hq, hkv, d, window, partition_tokens, kernel):
     """Several rows per request, including more rows than cached tokens, no
-    rows, an empty context, exact block multiples and ragged tails."""
-    say(f"cross_attn_varlen: {dtype} {hq}x{hkv}x{d} window {window} partition {partition_tokens}")
+    rows, an empty context, exact block multiples and ragged tails; with the
+    kernel the library picks (matrix cores for bf16) and the vector kernel."""
+    say(f"cross_attn_varlen: {dtype} {hq}x{hkv}x{d} window {window} partition {partition_tokens} {kernel}")
     geom = synth.custom_geometry(dtype, hq, hkv, d, 16)
     ctx = [5, 300, 1, 0, 64, 129, 3, 700, 2]
     ql = [3, 4, 1, 2, 5, 1, 6, 2, 0]
     case = VarlenCase(geom, ctx, ql, seed=hq * 7 + d + window)
-    out = case.run(window=window, partition_tokens=partition_tokens)
+    out = case.run(window=window, partition_tokens=partition_tokens,
+                   flags=yb.FLAG_VECTOR_KERNEL if kernel == "vector" else 0)
     torch.cuda.synchronize()
     err = _max_err(out, case.oracle(window))
     say(f"  max abs err {err:.3e}")
@@ -155,14 +158,17 @@ def test_varlen_one_row_matches_decode_call():
     assert float((rows - base).abs().max()) <= 1e-5
 
 
-def test_varlen_deterministic_and_order_independent():
-    say("cross_attn_varlen determinism: both work orders")
+@pytest.mark.parametrize("kernel", [0, yb.FLAG_VECTOR_KERNEL])
+def test_varlen_deterministic_and_order_independent(kernel):
+    say(f"cross_attn_varlen determinism: both work orders, kernel flag {kernel}")
     geom = synth.custom_geometry("bf16", 8, 2, 128, 16)
     case = VarlenCase(geom, [900, 40, 1500, 7], [4, 2, 3, 1], seed=21)
-    a = case.run(window=300, partition_tokens=64).clone()
-    b = case.run(window=300, partition_tokens=64, flags=yb.FLAG_REVERSE_ORDER).clone()
+    a = case.run(window=300, partition_tokens=64, flags=kernel).clone()
+    b = case.run(window=300, partition_tokens=64, flags=kernel | yb.FLAG_REVERSE_ORDER).clone()
+    c = case.run(window=300, partition_tokens=64, flags=kernel).clone()
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    assert torch.equal(a.view(torch.int32), c.view(torch.int32))
     assert _max_err(a, case.oracle(300)) <= ATTN_ATOL
 
 

@@ -28,6 +28,7 @@ DTYPE_BF16 = 1
 DTYPE_FP8_E4M3 = 2
 CROSS_ATTN_QUEUE_BYTES = 2048
 FLAG_REVERSE_ORDER = 1
+FLAG_VECTOR_KERNEL = 2
 
 _c = ctypes
 _vp = _c.c_void_p

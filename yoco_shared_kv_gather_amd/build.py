@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libyoco.so")
 
 SOURCES = ["abi.hip", "gather_last.hip", "kv_append.hip", "cross_attn.hip", "cross_attn_f32.hip", "cross_attn_bf16.hip",
-           "cross_attn_fp8.hip"]
+           "cross_attn_fp8.hip", "cross_attn_mfma_bf16.hip", "cross_attn_mfma_fp8.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [
@@ -53,7 +53,7 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, jobs: int = 7) -> str:
+def build(verbose: bool = False, jobs: int = 8) -> str:
     """Compile every source and link libyoco.so; returns the library path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()

@@ -33,15 +33,18 @@ def attn_ranges(seq_lens, query_lens=None, window: int = 0):
 
 
 def attn_layer_bytes(seq_lens, num_q_heads: int, num_kv_heads: int, head_dim: int, block_size: int,
-                     elem_bytes: int, query_lens=None, window: int = 0) -> int:
+                     elem_bytes: int, query_lens=None, window: int = 0, q_bytes=None, scale_bytes: int = 0) -> int:
     """One cross-attention call: every K/V row of the range each request reads
-    once, q in and fp32 out for every query row, the block-table entries the
-    ranges span, seq_lens (and query_start_loc when there are several rows)."""
+    once (with an 8-bit cache: 1-byte elements plus the row's K and V scales,
+    scale_bytes per token and KV head), q in and fp32 out for every query row,
+    the block-table entries the ranges span, seq_lens (and query_start_loc
+    when there are several rows)."""
     lo, n = attn_ranges(seq_lens, query_lens, window)
     kv = int(sum(kv_bytes(1, int(b - a), num_kv_heads, head_dim, elem_bytes) for a, b in zip(lo, n)))
+    kv += int(np.sum(n - lo)) * num_kv_heads * scale_bytes
     r = len(n)
     rows = r if query_lens is None else int(np.sum(query_lens))
-    q_out = rows * num_q_heads * head_dim * (elem_bytes + 4)
+    q_out = rows * num_q_heads * head_dim * ((elem_bytes if q_bytes is None else q_bytes) + 4)
     spanned = np.where(n > lo, (np.maximum(n, 1) - 1) // block_size - lo // block_size + 1, 0)
     table = int(np.sum(spanned)) * 4
     return kv + q_out + table + 4 * r + (0 if query_lens is None else 4 * (r + 1))

@@ -199,7 +199,8 @@ int32_t run_cross_attn(const AttnCall& c, const char* who) {
   if (c.num_q_heads % c.num_kv_heads != 0)
     return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: num_q_heads %d is not a multiple of num_kv_heads %d", who,
                 c.num_q_heads, c.num_kv_heads);
-  if ((c.flags & ~YOCO_FLAG_REVERSE_ORDER) != 0) return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: unknown flags", who);
+  if ((c.flags & ~(YOCO_FLAG_REVERSE_ORDER | YOCO_FLAG_VECTOR_KERNEL)) != 0)
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: unknown flags", who);
   if (!std::isfinite(c.scale)) return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: scale is not finite", who);
   if (c.partition_tokens % 64 != 0)
     return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: partition_tokens %d is not a multiple of 64", who,
@@ -233,7 +234,12 @@ int32_t run_cross_attn(const AttnCall& c, const char* who) {
   const int32_t nparts = num_partitions(span, part);
   if (nparts > kMaxParts)
     return fail(YOCO_ERR_UNSUPPORTED, "%s: %d partitions per request exceed %d", who, nparts, kMaxParts);
-  const int qpi = c.qsl == nullptr ? 0 : (c.max_qlen > 1 ? 8 / group : 1);
+  // Matrix cores where the work per byte outgrows the vector ALUs: an FP8
+  // cache, or several query rows per request (bf16); persistent schedule only.
+  const bool mfma = (c.flags & YOCO_FLAG_VECTOR_KERNEL) == 0 && c.num_seqs <= kMaxQueueSeqs &&
+                    (f8 || (c.dtype == YOCO_DTYPE_BF16 && c.qsl != nullptr && c.max_qlen > 1));
+  const int rows_wide = (mfma ? 16 : 8) / group;
+  const int qpi = c.qsl == nullptr ? 0 : (c.max_qlen > 1 ? rows_wide : 1);
   const int64_t groups = qpi == 0 ? 1 : yoco::ceil_div(c.max_qlen, qpi);
   const int64_t items = static_cast<int64_t>(c.num_seqs) * c.num_kv_heads * groups * nparts;
   if (items > 0x7fffffffLL)
@@ -283,9 +289,11 @@ int32_t run_cross_attn(const AttnCall& c, const char* who) {
 
   hipStream_t s = static_cast<hipStream_t>(c.stream);
   clear_launch_error();
-  const int launched = c.dtype == YOCO_DTYPE_BF16 ? dispatch_bf16(c.head_dim, group, qpi, a, items, s)
-                       : f8                       ? dispatch_fp8(c.head_dim, group, qpi, a, items, s)
-                                                  : dispatch_f32(c.head_dim, group, qpi, a, items, s);
+  const int launched = mfma ? (f8 ? dispatch_mfma_fp8(c.head_dim, group, qpi, a, items, s)
+                                   : dispatch_mfma_bf16(c.head_dim, group, qpi, a, items, s))
+                       : c.dtype == YOCO_DTYPE_BF16 ? dispatch_bf16(c.head_dim, group, qpi, a, items, s)
+                       : f8                         ? dispatch_fp8(c.head_dim, group, qpi, a, items, s)
+                                                    : dispatch_f32(c.head_dim, group, qpi, a, items, s);
   if (launched == 0) return fail(YOCO_ERR_UNSUPPORTED, "%s: no kernel for this shape", who);
   if (launched < 0) return fail(YOCO_ERR_HIP, "%s: occupancy query failed on the current device", who);
   if (nparts > 1) {

@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "yoco_internal.h"
 
@@ -963,6 +964,12 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
 }
 
 
+}  // namespace yoco_attn
+
+#include "cross_attn_mfma.h"
+
+namespace yoco_attn {
+
 // ---- launch helpers (host) ------------------------------------------------------
 
 // Workgroups of `kernel` resident on the current device at once (compute
@@ -1030,10 +1037,62 @@ int dispatch_dim(int head_dim, int group, int qpi, const AttnArgs& a, int64_t it
 }
 
 
-// Per element type (cross_attn_f32.hip, cross_attn_bf16.hip, cross_attn_fp8.hip):
+// The matrix-core kernel (persistent schedule only): grid = resident
+// workgroups, at most one per work item.
+template <int kT, int D, int G, int QPI>
+int per_cu_workgroups_mfma(int* out) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(out, cross_attn_mfma_kernel<kT, D, G, QPI>, kThreads, 0) ==
+                 hipSuccess ? 0 : 1;
+}
+
+template <int kT, int D, int G, int QPI>
+bool launch_mfma(AttnArgs a, int64_t items, hipStream_t stream) {
+  const int slots = resident_workgroups(reinterpret_cast<const void*>(cross_attn_mfma_kernel<kT, D, G, QPI>),
+                                        per_cu_workgroups_mfma<kT, D, G, QPI>);
+  if (slots <= 0) return false;
+  const int64_t grid = items < slots ? items : slots;
+  hipLaunchKernelGGL((cross_attn_mfma_kernel<kT, D, G, QPI>), dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0,
+                     stream, a);
+  return true;
+}
+
+// Query rows per item of the matrix-core kernel: 0 (decode), 1, or 16/G.
+template <int kT, int D, int G>
+int dispatch_rows_mfma(int qpi, const AttnArgs& a, int64_t items, hipStream_t stream) {
+  constexpr int kWide = 16 / G;
+  if (qpi == 0) return launch_mfma<kT, D, G, 0>(a, items, stream) ? 1 : -1;
+  if (qpi == 1) return launch_mfma<kT, D, G, 1>(a, items, stream) ? 1 : -1;
+  if (qpi == kWide) return launch_mfma<kT, D, G, kWide>(a, items, stream) ? 1 : -1;
+  return 0;
+}
+
+template <int kT>
+int dispatch_dim_mfma(int head_dim, int group, int qpi, const AttnArgs& a, int64_t items, hipStream_t stream) {
+  auto by_group = [&](auto dim) -> int {
+    constexpr int D = decltype(dim)::value;
+    switch (group) {
+      case 1: return dispatch_rows_mfma<kT, D, 1>(qpi, a, items, stream);
+      case 2: return dispatch_rows_mfma<kT, D, 2>(qpi, a, items, stream);
+      case 4: return dispatch_rows_mfma<kT, D, 4>(qpi, a, items, stream);
+      case 8: return dispatch_rows_mfma<kT, D, 8>(qpi, a, items, stream);
+      default: return 0;
+    }
+  };
+  switch (head_dim) {
+    case 64: return by_group(std::integral_constant<int, 64>());
+    case 128: return by_group(std::integral_constant<int, 128>());
+    case 256: return by_group(std::integral_constant<int, 256>());
+    default: return 0;
+  }
+}
+
+// Per element type (cross_attn_f32.hip, cross_attn_bf16.hip, cross_attn_fp8.hip;
+// the matrix-core kernels in cross_attn_mfma_bf16.hip, cross_attn_mfma_fp8.hip):
 // 1 = launched, 0 = no kernel for the shape, -1 = the occupancy query failed.
 int dispatch_f32(int head_dim, int group, int qpi, const AttnArgs& a, int64_t items, hipStream_t stream);
 int dispatch_bf16(int head_dim, int group, int qpi, const AttnArgs& a, int64_t items, hipStream_t stream);
 int dispatch_fp8(int head_dim, int group, int qpi, const AttnArgs& a, int64_t items, hipStream_t stream);
+int dispatch_mfma_bf16(int head_dim, int group, int qpi, const AttnArgs& a, int64_t items, hipStream_t stream);
+int dispatch_mfma_fp8(int head_dim, int group, int qpi, const AttnArgs& a, int64_t items, hipStream_t stream);
 
 }  // namespace yoco_attn

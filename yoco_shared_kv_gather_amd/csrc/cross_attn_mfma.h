@@ -1,0 +1,520 @@
+// Matrix-core variant of the cross-attention kernel (included by
+// cross_attn_kernels.h, after the VALU kernel whose helpers it uses).
+//
+// When the work per K^/V^ byte grows -- an 8-bit cache (twice the rows per
+// byte) or several query rows per request (up to 16 query vectors per KV
+// group) -- the VALU kernel runs out of vector throughput, while q.k and p.v
+// are then small dense contractions.  Here a work item's query vectors
+// (G heads x its query rows, padded to 16) sit in registers as an MFMA
+// operand, and each wavefront streams 16-key tiles of its item:
+//
+//   S^T[16 keys][16 q] = K[16 keys][D] . Q^T[D][16 q]
+//       v_mfma_f32_16x16x32_bf16 over head_dim; K rows are loaded from the
+//       paged cache directly in the A-operand layout (lane l: key l%16, eight
+//       head_dim elements), FP8 rows widened exactly to bf16 in registers.
+//   online softmax: lane l owns query l%16 and four keys of each tile; the
+//       running max of a query is shared by its four lanes (two shuffles).
+//   O^T[D][16 q] += V^T[D][16 keys] . P^T[16 keys][16 q]
+//       v_mfma_f32_16x16x16_bf16; V goes through a per-wavefront LDS tile
+//       (written row-major, read as the transposed A operand with 16-bit
+//       reads), P^T is exactly the lane's own softmax weights.  P is split
+//       into bf16 high and low parts (two products), so the weights keep ~17
+//       bits; K, V (bf16 or widened FP8) and q are exact bf16 values, and all
+//       sums are fp32.  Each lane's O^T column belongs to its own query, so
+//       rescaling on a new maximum stays lane-local.
+//
+// The schedule, work items, partials and the merge kernel are those of the
+// VALU kernel; the item pipeline is simpler (the next item is fetched at the
+// start of the current one, rows are double-buffered within an item).
+
+#pragma once
+
+namespace yoco_attn {
+
+typedef __bf16 mfma_bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 mfma_bf16x4 __attribute__((ext_vector_type(4)));
+typedef float mfma_f32x4 __attribute__((ext_vector_type(4)));
+
+template <int kT, int D>
+struct MfmaLayout {
+  static_assert(kT == kBF16 || kT == kFP8, "bf16 or FP8 cache");
+  static constexpr int kEb = kT == kFP8 ? 1 : 2;                       // cache element bytes
+  static constexpr int kRowBytes = D * kEb;
+  // keys per wavefront iteration: about 8 KB of K^/V^, at least one tile
+  static constexpr int kNK = 8192 / (2 * kRowBytes) < 16 ? 16 : (8192 / (2 * kRowBytes) > 64 ? 64 : 8192 / (2 * kRowBytes));
+  static constexpr int kNT = kNK / 16;                                 // 16-key tiles per iteration
+  static constexpr int kKS = D / 32;                                   // MFMA k-steps over head_dim
+  static constexpr int kKL = kT == kFP8 ? D / 64 : D / 32;             // 16-byte K loads per tile per lane
+  static constexpr int kVC = kNK * kRowBytes / 16 / 64;                // 16-byte V chunks per lane per iteration
+  static constexpr int kChunksPerRow = kRowBytes / 16;
+  static constexpr int kVStride = D + 4;                               // bf16 elements per LDS row of a V tile
+  static_assert(kVC >= 1 && kNK * kRowBytes % (16 * 64) == 0, "V tile split");
+};
+
+// Head_dim offset of the eight k-elements that lane group gi (= lane/16)
+// holds at MFMA k-step ks.  bf16: one 16-byte load per step; FP8: one
+// 16-byte load covers two steps.  A and B operands use the same map.
+template <int kT>
+__device__ __forceinline__ int mfma_d_of(int gi, int ks) {
+  if constexpr (kT == kFP8) {
+    return 64 * (ks >> 1) + 16 * gi + 8 * (ks & 1);
+  } else {
+    return 32 * ks + 8 * gi;
+  }
+}
+
+template <int kT, int D, int VG, bool kVar>
+struct MfmaSmem {
+  using ML = MfmaLayout<kT, D>;
+  int32_t len[kMaxQueueSeqs];
+  int32_t qs[kVar ? kMaxQueueSeqs + 1 : 1];
+  int32_t pref[kMaxQueueSeqs + 1];
+  int32_t pref2[kMaxQueueSeqs + 1];
+  int32_t wsum[2 * kWaves];
+  uint32_t next;
+  int32_t blocks[kMaxSliceBlocks];
+  __attribute__((aligned(16))) uint16_t q[16][D + 8];   // the item's query vectors, bf16, rows past VG zero
+  float ml[kWaves][VG][2];
+  union __attribute__((aligned(16))) {
+    uint16_t vt[kWaves][ML::kNK][ML::kVStride];     // per-wavefront V tile, bf16 row-major
+    float acc[kWaves][VG][D];                       // per-wavefront outputs for the final combine
+  } u;
+};
+
+template <int kT, int D, int G, int QPI>
+__global__ __launch_bounds__(kThreads) void cross_attn_mfma_kernel(AttnArgs a) {
+  using ML = MfmaLayout<kT, D>;
+  constexpr bool kVar = QPI > 0;
+  constexpr bool kF8 = kT == kFP8;
+  constexpr int kQ = kVar ? QPI : 1;
+  constexpr int VG = G * kQ;
+  static_assert(VG <= 16, "at most 16 query vectors per item");
+  constexpr int kNK = ML::kNK, kNT = ML::kNT, kKS = ML::kKS, kKL = ML::kKL, kVC = ML::kVC;
+  constexpr int kEb = ML::kEb;
+  constexpr int kDT = D / 16;                       // 16-row tiles of O^T
+  using Smem = MfmaSmem<kT, D, VG, kVar>;
+  __shared__ Smem sm;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int l16 = lane & 15;                        // key (A/S rows) or query (B/S columns) within a tile
+  const int gi = lane >> 4;                         // lane group
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const bool reverse = (a.flags & YOCO_FLAG_REVERSE_ORDER) != 0;
+  const int R = a.num_seqs;
+  uint32_t* fetch_ctr = a.queue;
+  uint32_t* done_ctr = a.queue + kQueueLineWords;
+
+  auto qlen_of = [&](int r) -> int {
+    if constexpr (kVar) {
+      return min(max(sm.qs[r + 1] - sm.qs[r], 0), a.max_qlen);
+    } else {
+      return 1;
+    }
+  };
+
+  // ---- schedule: per-request item counts and their prefixes (as in the VALU kernel)
+  for (int i = tid; i < R; i += kThreads) {
+    const int n = a.seq_lens[i];
+    sm.len[i] = n < 0 ? 0 : (n > a.len_cap ? a.len_cap : n);
+  }
+  if constexpr (kVar) {
+    for (int i = tid; i <= R; i += kThreads) sm.qs[i] = min(max(a.qsl[i], 0), a.num_rows);
+  }
+  __syncthreads();
+  uint32_t total = 0, total_big = 0;
+  {
+    const int per = (R + kThreads - 1) / kThreads;
+    const int lo = min(tid * per, R);
+    const int hi = min(lo + per, R);
+    auto counts = [&](int i, int& nb, int& ns) {
+      const int n = sm.len[i];
+      const int ql = qlen_of(i);
+      const int m = n - range_lo(n, ql, a.window);
+      const int groups = kVar ? (ql + kQ - 1) / kQ : 1;
+      nb = big_parts(m, a.part_tokens) * a.num_kv_heads * groups;
+      ns = small_parts(m, a.part_tokens) * a.num_kv_heads * groups;
+    };
+    int local_b = 0, local_s = 0;
+    for (int i = lo; i < hi; ++i) {
+      int nb, ns;
+      counts(i, nb, ns);
+      local_b += nb;
+      local_s += ns;
+    }
+    int incl_b = local_b, incl_s = local_s;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int tb = __shfl_up(incl_b, off, 64);
+      const int ts = __shfl_up(incl_s, off, 64);
+      if (lane >= off) {
+        incl_b += tb;
+        incl_s += ts;
+      }
+    }
+    if (lane == 63) {
+      sm.wsum[wave] = incl_b;
+      sm.wsum[kWaves + wave] = incl_s;
+    }
+    __syncthreads();
+    int run_b = incl_b - local_b, run_s = incl_s - local_s;
+    for (int w = 0; w < wave; ++w) {
+      run_b += sm.wsum[w];
+      run_s += sm.wsum[kWaves + w];
+    }
+    for (int i = lo; i < hi; ++i) {
+      sm.pref[i] = run_b;
+      sm.pref2[i] = run_s;
+      int nb, ns;
+      counts(i, nb, ns);
+      run_b += nb;
+      run_s += ns;
+    }
+    if (tid == kThreads - 1) {
+      sm.pref[R] = run_b;
+      sm.pref2[R] = run_s;
+    }
+    __syncthreads();
+    total_big = static_cast<uint32_t>(uniform(sm.pref[R]));
+    total = total_big + static_cast<uint32_t>(uniform(sm.pref2[R]));
+  }
+
+  auto item_at = [&](uint32_t k) -> Item {
+    if (k >= total) return make_item(a, false, 0, 0, 0, 0, 0, 0, 0, 0);
+    const uint32_t kk = reverse ? total - 1u - k : k;
+    const bool big = kk < total_big;
+    const int32_t* pref = big ? sm.pref : sm.pref2;
+    const uint32_t j = big ? kk : kk - total_big;
+    const int r = find_request(pref, R, j);
+    const int idx = static_cast<int>(j - static_cast<uint32_t>(pref[r]));
+    const int n = sm.len[r];
+    const int ql = qlen_of(r);
+    const int lo = range_lo(n, ql, a.window);
+    const int groups = kVar ? (ql + kQ - 1) / kQ : 1;
+    const int per = max(a.num_kv_heads * groups, 1);
+    const int sub = idx / per;
+    const int rem = idx - sub * per;
+    const int qgrp = rem / a.num_kv_heads;
+    const int g = rem - qgrp * a.num_kv_heads;
+    const int part = big ? sub : big_parts(n - lo, a.part_tokens) + sub;
+    if constexpr (kVar) {
+      return make_item(a, true, r, g, part, n, lo, sm.qs[r] + qgrp * kQ, min(kQ, ql - qgrp * kQ),
+                       n - ql + qgrp * kQ);
+    } else {
+      return make_item(a, true, r, g, part, n, lo, r, 1, n - 1);
+    }
+  };
+
+  auto valid_block = [&](int b) { return static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks) ? b : -1; };
+
+  // ---- registers of one iteration: this wavefront's K (A-operand layout), V
+  // (row chunks for the LDS tile), per-key validity and FP8 scales
+  struct Rows {
+    uint4 k[kNT][kKL];
+    uint4 v[kVC];
+    bool vok[kVC];                 // the V chunk's key is a context row (else its values are zeroed)
+    bool sok[kNT][4];              // this lane's score keys (base + 16t + 4gi + e): context rows
+    int base;                      // logical position of the iteration's first key
+    float ks[kNT][4];              // FP8: their K and V scales
+    float vs[kNT][4];
+  };
+
+  const int off_mask = a.block_size - 1;
+  // Byte offset of context position j's row (for KV head g) and whether it is
+  // a context row of the current item; otherwise the item's first row (or
+  // block 0) is read and the row is masked.
+  auto row_of = [&](const Item& it, int j, int64_t& off) -> bool {
+    const bool in_range = j < it.end;
+    const int blk = sm.blocks[((in_range ? j : it.start) >> a.bs_shift) - it.first_blk];
+    const bool ok = in_range && blk >= 0;
+    const int b0 = sm.blocks[0];
+    const int64_t row = ok ? static_cast<int64_t>(blk) * a.num_kv_heads * a.block_size + (j & off_mask)
+                           : static_cast<int64_t>(b0 >= 0 ? b0 : 0) * a.num_kv_heads * a.block_size +
+                                 (it.start & off_mask);
+    off = row;                     // row index in [block][head][slot] order without the head term
+    return ok;
+  };
+
+  auto load_rows = [&](Rows& rs, const Item& it, int iter) {
+    const char* kb = static_cast<const char*>(a.k) + static_cast<int64_t>(it.g) * a.block_size * ML::kRowBytes;
+    const char* vb = static_cast<const char*>(a.v) + static_cast<int64_t>(it.g) * a.block_size * ML::kRowBytes;
+    const int base = it.start + iter * kNK;
+    rs.base = base;
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+      int64_t row;
+      row_of(it, base + 16 * t + l16, row);
+#pragma unroll
+      for (int c = 0; c < kKL; ++c) {
+        const int d = kF8 ? 64 * c + 16 * gi : 32 * c + 8 * gi;
+        rs.k[t][c] = *reinterpret_cast<const uint4*>(kb + row * ML::kRowBytes + d * kEb);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = base + 16 * t + 4 * gi + e;
+        int64_t srow;
+        rs.sok[t][e] = row_of(it, j, srow);
+        if constexpr (kF8) {
+          const int64_t sidx = srow + static_cast<int64_t>(it.g) * a.block_size;
+          rs.ks[t][e] = a.k_scale[sidx];
+          rs.vs[t][e] = a.v_scale[sidx];
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < kVC; ++c) {
+      const int chunk = lane + 64 * c;
+      const int key = chunk / ML::kChunksPerRow;
+      const int cb = (chunk - key * ML::kChunksPerRow) * 16;          // byte offset in the row
+      int64_t row;
+      rs.vok[c] = row_of(it, base + key, row);
+      rs.v[c] = *reinterpret_cast<const uint4*>(vb + row * ML::kRowBytes + cb);
+    }
+  };
+
+  // Query operand (B of S^T): query l16's eight elements at each k-step.
+  mfma_bf16x8 qop[kKS];
+  float m_run = kInitMax, l_run = 0.0f;
+  mfma_f32x4 oacc[kDT];
+  int qlo = 0, qhi = 0;                             // keys [qlo, qhi) visible to this lane's query
+  bool qlive = false;                               // this lane's query column is a real query vector
+
+  auto compute = [&](const Rows& rs) {
+    uint16_t(*vt)[ML::kVStride] = sm.u.vt[wave];
+    // the previous iteration's reads of this wavefront's tile come first
+    __builtin_amdgcn_wave_barrier();
+    // V chunks -> this wavefront's LDS tile as bf16 (masked rows zero)
+#pragma unroll
+    for (int c = 0; c < kVC; ++c) {
+      const int chunk = lane + 64 * c;
+      const int key = chunk / ML::kChunksPerRow;
+      const int e0 = (chunk - key * ML::kChunksPerRow) * (16 / kEb);  // first element of the chunk
+      const uint4 vc = rs.vok[c] ? rs.v[c] : make_uint4(0u, 0u, 0u, 0u);
+      if constexpr (kF8) {
+        uint4 lo8, hi8;
+        fp8_to_bf16(vc, lo8, hi8);
+        *reinterpret_cast<uint2*>(&vt[key][e0]) = make_uint2(lo8.x, lo8.y);
+        *reinterpret_cast<uint2*>(&vt[key][e0 + 4]) = make_uint2(lo8.z, lo8.w);
+        *reinterpret_cast<uint2*>(&vt[key][e0 + 8]) = make_uint2(hi8.x, hi8.y);
+        *reinterpret_cast<uint2*>(&vt[key][e0 + 12]) = make_uint2(hi8.z, hi8.w);
+      } else {
+        *reinterpret_cast<uint2*>(&vt[key][e0]) = make_uint2(vc.x, vc.y);
+        *reinterpret_cast<uint2*>(&vt[key][e0 + 4]) = make_uint2(vc.z, vc.w);
+      }
+    }
+    // the tile's rows come from other lanes of this wavefront: wait for the
+    // LDS writes before reading them back
+    __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    // S^T tiles
+    float s[kNT][4];
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+      mfma_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int c = 0; c < kKL; ++c) {
+        if constexpr (kF8) {
+          uint4 lo8, hi8;
+          fp8_to_bf16(rs.k[t][c], lo8, hi8);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mfma_bf16x8, lo8), qop[2 * c], acc, 0, 0,
+                                                         0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mfma_bf16x8, hi8), qop[2 * c + 1], acc,
+                                                         0, 0, 0);
+        } else {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(mfma_bf16x8, rs.k[t][c]), qop[c], acc,
+                                                         0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = rs.base + 16 * t + 4 * gi + e;
+        const bool ok = rs.sok[t][e] && qlive && j >= qlo && j < qhi;
+        const float sc = kF8 ? a.scale_log2 * rs.ks[t][e] : a.scale_log2;
+        s[t][e] = ok ? acc[e] * sc : -INFINITY;
+      }
+    }
+    // online softmax of this lane's query: the iteration's max over its four
+    // lanes, lazy rescale, weights
+    float tmax = s[0][0];
+#pragma unroll
+    for (int t = 0; t < kNT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, s[t][e]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    if (tmax > m_run + kLazyMaxSlack) {
+      const float corr = fast_exp2(m_run - tmax);
+      l_run *= corr;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) oacc[dt] *= corr;
+      m_run = tmax;
+    }
+    mfma_bf16x4 p_hi[kNT], p_lo[kNT];
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+      float pv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p = fast_exp2(s[t][e] - m_run);
+        l_run += p;
+        pv[e] = kF8 ? p * (rs.sok[t][e] ? rs.vs[t][e] : 0.0f) : p;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const __bf16 h = static_cast<__bf16>(pv[e]);
+        p_hi[t][e] = h;
+        p_lo[t][e] = static_cast<__bf16>(pv[e] - static_cast<float>(h));
+      }
+    }
+    // O^T += V^T P^T per 16-row tile of head_dim
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) {
+        const int d = 16 * dt + l16;
+        const int k0 = 16 * t + 4 * gi;
+        uint32_t w0 = static_cast<uint32_t>(vt[k0][d]) | (static_cast<uint32_t>(vt[k0 + 1][d]) << 16);
+        uint32_t w1 = static_cast<uint32_t>(vt[k0 + 2][d]) | (static_cast<uint32_t>(vt[k0 + 3][d]) << 16);
+        const mfma_bf16x4 va = __builtin_bit_cast(mfma_bf16x4, make_uint2(w0, w1));
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, p_hi[t], oacc[dt], 0, 0, 0);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, p_lo[t], oacc[dt], 0, 0, 0);
+      }
+    }
+  };
+
+  // ---- items
+  Item cur = item_at(blockIdx.x);
+  while (cur.valid) {
+    // next item now (the queue counter sits on its own line)
+    if (tid == 0) sm.next = gridDim.x + atomicAdd(fetch_ctr, 1u);
+    // stage the block-table slice and the query vectors
+    {
+      const int32_t* table = a.block_table + static_cast<int64_t>(cur.r) * a.max_blocks + cur.first_blk;
+      for (int i = tid; i < cur.num_blk; i += kThreads) sm.blocks[i] = valid_block(table[i]);
+      for (int i = tid; i < 16 * (D / 8); i += kThreads) {
+        const int v = i / (D / 8);
+        const int c = i - v * (D / 8);
+        uint4 val = make_uint4(0u, 0u, 0u, 0u);
+        if (v < VG) {
+          const int qi = v / G;
+          const int h = v - qi * G;
+          const int qrow = kVar ? cur.row0 + min(qi, max(cur.nq - 1, 0)) : cur.r;
+          val = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
+                                                ((static_cast<int64_t>(qrow) * a.num_q_heads + cur.g * G + h) * D +
+                                                 c * 8) * 2);
+        }
+        *reinterpret_cast<uint4*>(&sm.q[v][c * 8]) = val;
+      }
+    }
+    __syncthreads();
+    const Item nxt = item_at(static_cast<uint32_t>(uniform(static_cast<int>(sm.next))));
+
+    if (cur.num_blk > 0) {
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks)
+        qop[ks] = *reinterpret_cast<const mfma_bf16x8*>(&sm.q[l16][mfma_d_of<kT>(gi, ks)]);
+      // this lane's query column: vector l16 = query row l16 / G, head l16 % G
+      {
+        const int qi = l16 / G;
+        qlive = l16 < VG && qi < cur.nq;
+        const int p = cur.pbase + qi;
+        qhi = kVar ? p + 1 : 0x7fffffff;
+        qlo = (kVar && a.window > 0) ? p - a.window + 1 : -0x7fffffff;
+      }
+      m_run = kInitMax;
+      l_run = 0.0f;
+#pragma unroll
+      for (int dt = 0; dt < kDT; ++dt) oacc[dt] = mfma_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      const int num_iters = (cur.end - cur.start + kNK - 1) / kNK;
+      Rows ra, rb;
+      int it = wave_u;
+      if (it < num_iters) load_rows(ra, cur, it);
+      while (it < num_iters) {
+        if (it + kWaves < num_iters) load_rows(rb, cur, it + kWaves);
+        compute(ra);
+        it += kWaves;
+        if (it >= num_iters) break;
+        if (it + kWaves < num_iters) load_rows(ra, cur, it + kWaves);
+        compute(rb);
+        it += kWaves;
+      }
+    }
+    __syncthreads();                                 // every wavefront done with its V tile
+
+    if (cur.num_blk > 0) {
+      // this wavefront's partial: O^T column l16 rows 16dt+4gi+e; sum of weights
+      // over the query's four lanes
+      float lq = l_run;
+      lq += __shfl_xor(lq, 16, 64);
+      lq += __shfl_xor(lq, 32, 64);
+      if (l16 < VG) {
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sm.u.acc[wave][l16][16 * dt + 4 * gi + e] = oacc[dt][e];
+        if (gi == 0) {
+          sm.ml[wave][l16][0] = m_run;
+          sm.ml[wave][l16][1] = lq;
+        }
+      }
+    }
+    __syncthreads();
+
+    auto out_row = [&](int v) -> int64_t {
+      if constexpr (kVar) {
+        const int i = v / G;
+        return i < cur.nq ? static_cast<int64_t>(cur.row0 + i) * a.num_q_heads + cur.g * G + (v - i * G) : -1;
+      } else {
+        return static_cast<int64_t>(cur.r) * a.num_q_heads + cur.g * G + v;
+      }
+    };
+    if (cur.num_blk > 0) {
+      const int np_r = parts_of(cur.n - cur.lo, a.part_tokens);
+      for (int e = tid; e < VG * D; e += kThreads) {
+        const int h = e / D;
+        const int d = e - h * D;
+        const int64_t rh = out_row(h);
+        if (rh < 0) continue;
+        float mx = sm.ml[0][h][0];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm.ml[w][h][0]);
+        float den = 0.0f, num = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float f = exp2f(sm.ml[w][h][0] - mx);
+          den = fmaf(f, sm.ml[w][h][1], den);
+          num = fmaf(f, sm.u.acc[w][h][d], num);
+        }
+        if (np_r == 1) {
+          a.out[rh * D + d] = den == 0.0f ? 0.0f : num / den;
+        } else {
+          const int64_t slot = rh * a.num_parts + cur.part;
+          a.ws_acc[slot * D + d] = num;
+          if (d == 0) {
+            a.ws_ml[slot * 2] = mx;
+            a.ws_ml[slot * 2 + 1] = den;
+          }
+        }
+      }
+    } else if (cur.n == 0 && cur.part == 0) {
+      for (int e = tid; e < VG * D; e += kThreads) {
+        const int h = e / D;
+        const int64_t rh = out_row(h);
+        if (rh >= 0) a.out[rh * D + (e - h * D)] = 0.0f;
+      }
+    }
+    __syncthreads();                                 // sm reused by the next item
+    cur = nxt;
+  }
+
+  if (tid == 0) {
+    const uint32_t d = atomicAdd(done_ctr, 1u);
+    if (d == gridDim.x - 1) {
+      atomicExch(fetch_ctr, 0u);
+      atomicExch(done_ctr, 0u);
+    }
+  }
+}
+
+}  // namespace yoco_attn

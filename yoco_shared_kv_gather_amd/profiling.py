@@ -50,7 +50,7 @@ def source_hash() -> str:
 
 
 def short_name(name: str) -> str:
-    name = name.replace("(anonymous namespace)::", "")
+    name = name.replace("(anonymous namespace)::", "").replace("yoco_attn::", "")
     if name.startswith("void "):
         name = name[5:]
     depth = 0
