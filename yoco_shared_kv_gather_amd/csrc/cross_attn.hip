@@ -251,7 +251,7 @@ int32_t run_cross_attn(const AttnCall& c, const char* who) {
   if (c.workspace == nullptr || !aligned16(c.workspace))
     return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: workspace must be a 16-byte aligned pointer", who);
   const int64_t merge_grid = static_cast<int64_t>(c.num_seqs) * c.max_qlen * c.num_q_heads;
-  if (nparts > 1 && merge_grid > 0x7fffffffLL)
+  if (nparts > 1 && merge_grid * 8 > 0xffffffffLL)
     return fail(YOCO_ERR_UNSUPPORTED, "%s: merge grid of %lld workgroups is too many", who, (long long)merge_grid);
 
   AttnArgs a;
@@ -297,11 +297,26 @@ int32_t run_cross_attn(const AttnCall& c, const char* who) {
   if (launched == 0) return fail(YOCO_ERR_UNSUPPORTED, "%s: no kernel for this shape", who);
   if (launched < 0) return fail(YOCO_ERR_HIP, "%s: occupancy query failed on the current device", who);
   if (nparts > 1) {
-    const uint32_t mgrid = static_cast<uint32_t>(merge_grid);
-    switch (c.head_dim) {
-      case 64: hipLaunchKernelGGL(cross_attn_merge_kernel<64>, dim3(mgrid), dim3(kThreads), 0, s, a); break;
-      case 128: hipLaunchKernelGGL(cross_attn_merge_kernel<128>, dim3(mgrid), dim3(kThreads), 0, s, a); break;
-      default: hipLaunchKernelGGL(cross_attn_merge_kernel<256>, dim3(mgrid), dim3(kThreads), 0, s, a); break;
+    // split head_dim over up to 8 workgroups when there are fewer than ~512
+    // triples, keeping at least 8 float4 slices per workgroup (at most 32
+    // partition groups to combine at the end)
+    int split = 1;
+    while (split < 8 && merge_grid * split < 512 && c.head_dim / 4 / (split * 2) >= 8) split *= 2;
+    const uint32_t mgrid = static_cast<uint32_t>(merge_grid * split);
+    auto go = [&](auto kernel) { hipLaunchKernelGGL(kernel, dim3(mgrid), dim3(kThreads), 0, s, a); };
+    switch (c.head_dim * 16 + split) {
+      case 64 * 16 + 1: go(cross_attn_merge_kernel<64, 1>); break;
+      case 64 * 16 + 2: go(cross_attn_merge_kernel<64, 2>); break;
+      case 64 * 16 + 4: go(cross_attn_merge_kernel<64, 4>); break;
+      case 64 * 16 + 8: go(cross_attn_merge_kernel<64, 8>); break;
+      case 128 * 16 + 1: go(cross_attn_merge_kernel<128, 1>); break;
+      case 128 * 16 + 2: go(cross_attn_merge_kernel<128, 2>); break;
+      case 128 * 16 + 4: go(cross_attn_merge_kernel<128, 4>); break;
+      case 128 * 16 + 8: go(cross_attn_merge_kernel<128, 8>); break;
+      case 256 * 16 + 1: go(cross_attn_merge_kernel<256, 1>); break;
+      case 256 * 16 + 2: go(cross_attn_merge_kernel<256, 2>); break;
+      case 256 * 16 + 4: go(cross_attn_merge_kernel<256, 4>); break;
+      default: go(cross_attn_merge_kernel<256, 8>); break;
     }
   }
   return launch_result(who);

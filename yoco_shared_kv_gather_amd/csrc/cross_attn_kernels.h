@@ -189,24 +189,27 @@ __host__ __device__ inline int parts_of(int n, int P) { return big_parts(n, P) +
 
 // Merge the partials of one (query row, query head):
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
-// One workgroup per (request, query row of the request, head); rows past the
-// request's query count return at once.  256 threads: thread t owns the
-// float4 slice (t % (D/4)) of head_dim and partitions
-// p = t / (D/4) + k * (256 / (D/4)).  Each thread sums its partitions relative
-// to their own maximum, so the partial loads need not wait for the global
-// one; the groups are then rescaled and added in group order through LDS
-// (deterministic).  Rows whose context fits one partition were finished by
+// S workgroups per (request, query row of the request, head), each for D/S
+// of head_dim (S > 1 when there are few such triples, so that the merge
+// still spreads over the GPU); rows past the request's query count return at
+// once.  256 threads: thread t owns float4 slice t % (D/4/S) of its part of
+// head_dim and partitions p = t / (D/4/S) + k * (256 / (D/4/S)).  Each thread sums its partitions relative
+// to its own running maximum in one pass (the loads of a batch of 8
+// partitions are all in flight at once); the groups are then rescaled and
+// added in group order through LDS (deterministic).  Rows whose context fits one partition were finished by
 // the first kernel.
-template <int D>
+template <int D, int S>
 __global__ __launch_bounds__(kThreads) void cross_attn_merge_kernel(AttnArgs a) {
-  constexpr int kSlices = D / 4;                 // float4 slices of a head
+  constexpr int kSlices = D / 4 / S;             // float4 slices of a head this workgroup merges
   constexpr int kGroups = kThreads / kSlices;    // partition groups
   __shared__ float4 s_num[kGroups][kSlices];
   __shared__ float s_den[kGroups];
   __shared__ float s_max[kGroups];
+  const int64_t pair = blockIdx.x / S;           // (request, query row, head)
+  const int part_of_d = static_cast<int>(blockIdx.x - pair * S);
   const int64_t per_req = static_cast<int64_t>(a.max_qlen) * a.num_q_heads;
-  const int r = static_cast<int>(blockIdx.x / per_req);
-  const int rem = static_cast<int>(blockIdx.x - r * per_req);
+  const int r = static_cast<int>(pair / per_req);
+  const int rem = static_cast<int>(pair - r * per_req);
   const int qi = rem / a.num_q_heads;
   const int h = rem - qi * a.num_q_heads;
   const int tid = threadIdx.x;
@@ -224,25 +227,46 @@ __global__ __launch_bounds__(kThreads) void cross_attn_merge_kernel(AttnArgs a) 
   if (np <= 1) return;
   const int64_t rh = static_cast<int64_t>(row) * a.num_q_heads + h;
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + rh * a.num_parts;
-  const float4* acc = reinterpret_cast<const float4*>(a.ws_acc + rh * a.num_parts * D);
+  const float4* acc = reinterpret_cast<const float4*>(a.ws_acc + rh * a.num_parts * D) + part_of_d * kSlices;
   const int slice = tid % kSlices;
   const int grp = tid / kSlices;
 
+  // One pass, online: each batch issues all of its loads before using any,
+  // and the running sums are rescaled when a larger maximum comes in.
+  constexpr int kBatch = 8;
   float m_loc = kInitMax;
-#pragma unroll 8
-  for (int p = grp; p < np; p += kGroups) m_loc = fmaxf(m_loc, ml[p].x);
   float4 num = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
   float den = 0.0f;
-#pragma unroll 8
-  for (int p = grp; p < np; p += kGroups) {
-    const float2 part = ml[p];
-    const float4 v = acc[static_cast<int64_t>(p) * kSlices + slice];
-    const float w = exp2f(part.x - m_loc);
-    den = fmaf(w, part.y, den);
-    num.x = fmaf(w, v.x, num.x);
-    num.y = fmaf(w, v.y, num.y);
-    num.z = fmaf(w, v.z, num.z);
-    num.w = fmaf(w, v.w, num.w);
+  for (int p0 = grp; p0 < np; p0 += kGroups * kBatch) {
+    float2 part[kBatch];
+    float4 v[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int p = p0 + k * kGroups;
+      if (p < np) {
+        part[k] = ml[p];
+        v[k] = acc[static_cast<int64_t>(p) * (D / 4) + slice];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (p0 + k * kGroups >= np) break;
+      if (part[k].x > m_loc) {
+        const float c = exp2f(m_loc - part[k].x);
+        den *= c;
+        num.x *= c;
+        num.y *= c;
+        num.z *= c;
+        num.w *= c;
+        m_loc = part[k].x;
+      }
+      const float w = exp2f(part[k].x - m_loc);
+      den = fmaf(w, part[k].y, den);
+      num.x = fmaf(w, v[k].x, num.x);
+      num.y = fmaf(w, v[k].y, num.y);
+      num.z = fmaf(w, v[k].z, num.z);
+      num.w = fmaf(w, v[k].w, num.w);
+    }
   }
   s_num[grp][slice] = num;
   if (slice == 0) {
@@ -267,7 +291,8 @@ __global__ __launch_bounds__(kThreads) void cross_attn_merge_kernel(AttnArgs a) 
       dsum = fmaf(f, s_den[g2], dsum);
     }
     const float inv = dsum == 0.0f ? 0.0f : 1.0f / dsum;
-    reinterpret_cast<float4*>(a.out + rh * D)[tid] = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+    reinterpret_cast<float4*>(a.out + rh * D)[part_of_d * kSlices + tid] =
+        make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
   }
 }
 
