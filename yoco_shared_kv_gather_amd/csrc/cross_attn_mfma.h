@@ -82,7 +82,7 @@ struct MfmaSmem {
 };
 
 template <int kT, int D, int G, int QPI>
-__global__ __launch_bounds__(kThreads) void cross_attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kT == kBF16 && D <= 128 ? 2 : 1))) void cross_attn_mfma_kernel(AttnArgs a) {
   using ML = MfmaLayout<kT, D>;
   constexpr bool kVar = QPI > 0;
   constexpr bool kF8 = kT == kFP8;
@@ -209,67 +209,62 @@ __global__ __launch_bounds__(kThreads) void cross_attn_mfma_kernel(AttnArgs a) {
   auto valid_block = [&](int b) { return static_cast<unsigned>(b) < static_cast<unsigned>(a.num_blocks) ? b : -1; };
 
   // ---- registers of one iteration: this wavefront's K (A-operand layout), V
-  // (row chunks for the LDS tile), per-key validity and FP8 scales
+  // (row chunks for the LDS tile), the validity of its score keys and (FP8)
+  // their scales.
+  //
+  // A wavefront iteration covers kNK keys from a 16-aligned position, so with
+  // block_size >= 16 every 16-key tile lies inside one cache block: one
+  // block-table entry per tile gives a wave-uniform 64-bit row base, and lanes
+  // add 32-bit offsets.  Keys before the item's start or past its end, and
+  // tiles in an out-of-range block (which read block 0), are masked.
   struct Rows {
     uint4 k[kNT][kKL];
     uint4 v[kVC];
-    bool vok[kVC];                 // the V chunk's key is a context row (else its values are zeroed)
-    bool sok[kNT][4];              // this lane's score keys (base + 16t + 4gi + e): context rows
+    uint32_t vmask;                // bit c: V chunk c's key is an item row in a valid block (else zeroed)
+    uint32_t tmask;                // bit t: tile t is a valid block
     int base;                      // logical position of the iteration's first key
-    float ks[kNT][4];              // FP8: their K and V scales
-    float vs[kNT][4];
+    float4 ks[kNT];                // FP8: scales of this lane's score keys base + 16t + 4gi + 0..3
+    float4 vs[kNT];
   };
 
   const int off_mask = a.block_size - 1;
-  // Byte offset of context position j's row (for KV head g) and whether it is
-  // a context row of the current item; otherwise the item's first row (or
-  // block 0) is read and the row is masked.
-  auto row_of = [&](const Item& it, int j, int64_t& off) -> bool {
-    const bool in_range = j < it.end;
-    const int blk = sm.blocks[((in_range ? j : it.start) >> a.bs_shift) - it.first_blk];
-    const bool ok = in_range && blk >= 0;
-    const int b0 = sm.blocks[0];
-    const int64_t row = ok ? static_cast<int64_t>(blk) * a.num_kv_heads * a.block_size + (j & off_mask)
-                           : static_cast<int64_t>(b0 >= 0 ? b0 : 0) * a.num_kv_heads * a.block_size +
-                                 (it.start & off_mask);
-    off = row;                     // row index in [block][head][slot] order without the head term
-    return ok;
-  };
-
-  auto load_rows = [&](Rows& rs, const Item& it, int iter) {
-    const char* kb = static_cast<const char*>(a.k) + static_cast<int64_t>(it.g) * a.block_size * ML::kRowBytes;
-    const char* vb = static_cast<const char*>(a.v) + static_cast<int64_t>(it.g) * a.block_size * ML::kRowBytes;
-    const int base = it.start + iter * kNK;
+  auto load_rows = [&](Rows& rs, const Item& it, int base) {
     rs.base = base;
+    rs.tmask = 0u;
+    int64_t tile_row[kNT];         // cache row (block*Hkv + g)*bs + slot of each tile's first key
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
-      int64_t row;
-      row_of(it, base + 16 * t + l16, row);
+      const int p0 = base + 16 * t;
+      const int in = p0 < it.end ? p0 : it.start;
+      const int blk = uniform(sm.blocks[(in >> a.bs_shift) - it.first_blk]);
+      const bool ok = blk >= 0;
+      rs.tmask |= ok ? (1u << t) : 0u;
+      tile_row[t] = (static_cast<int64_t>(ok ? blk : 0) * a.num_kv_heads + it.g) * a.block_size + (in & off_mask);
+      const char* kt = static_cast<const char*>(a.k) + tile_row[t] * ML::kRowBytes;
 #pragma unroll
       for (int c = 0; c < kKL; ++c) {
         const int d = kF8 ? 64 * c + 16 * gi : 32 * c + 8 * gi;
-        rs.k[t][c] = *reinterpret_cast<const uint4*>(kb + row * ML::kRowBytes + d * kEb);
+        rs.k[t][c] = *reinterpret_cast<const uint4*>(kt + l16 * ML::kRowBytes + d * kEb);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = base + 16 * t + 4 * gi + e;
-        int64_t srow;
-        rs.sok[t][e] = row_of(it, j, srow);
-        if constexpr (kF8) {
-          const int64_t sidx = srow + static_cast<int64_t>(it.g) * a.block_size;
-          rs.ks[t][e] = a.k_scale[sidx];
-          rs.vs[t][e] = a.v_scale[sidx];
-        }
+      if constexpr (kF8) {
+        rs.ks[t] = *reinterpret_cast<const float4*>(a.k_scale + tile_row[t] + 4 * gi);
+        rs.vs[t] = *reinterpret_cast<const float4*>(a.v_scale + tile_row[t] + 4 * gi);
       }
     }
+    rs.vmask = 0u;
 #pragma unroll
     for (int c = 0; c < kVC; ++c) {
+      // the 64 chunks of one load instruction belong to 64 / kChunksPerRow <= 16
+      // consecutive keys of one tile
+      constexpr int kKeysPerInst = 64 / ML::kChunksPerRow;
+      const int t = (c * kKeysPerInst) / 16;
       const int chunk = lane + 64 * c;
       const int key = chunk / ML::kChunksPerRow;
-      const int cb = (chunk - key * ML::kChunksPerRow) * 16;          // byte offset in the row
-      int64_t row;
-      rs.vok[c] = row_of(it, base + key, row);
-      rs.v[c] = *reinterpret_cast<const uint4*>(vb + row * ML::kRowBytes + cb);
+      const int cb = (chunk - key * ML::kChunksPerRow) * 16;
+      const int j = base + key;
+      rs.vmask |= ((rs.tmask >> t & 1u) != 0u && j >= it.start && j < it.end ? 1u : 0u) << c;
+      rs.v[c] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v) +
+                                                 (tile_row[t] + (key - 16 * t)) * ML::kRowBytes + cb);
     }
   };
 
@@ -277,7 +272,8 @@ __global__ __launch_bounds__(kThreads) void cross_attn_mfma_kernel(AttnArgs a) {
   mfma_bf16x8 qop[kKS];
   float m_run = kInitMax, l_run = 0.0f;
   mfma_f32x4 oacc[kDT];
-  int qlo = 0, qhi = 0;                             // keys [qlo, qhi) visible to this lane's query
+  int jlo = 0, jhi = 0;                             // keys [jlo, jhi) visible to this lane's query
+  int item_lo = 0, item_hi = 0;                     // the item's range [start, end)
   bool qlive = false;                               // this lane's query column is a real query vector
 
   auto compute = [&](const Rows& rs) {
@@ -290,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_mfma_kernel(AttnArgs a) {
       const int chunk = lane + 64 * c;
       const int key = chunk / ML::kChunksPerRow;
       const int e0 = (chunk - key * ML::kChunksPerRow) * (16 / kEb);  // first element of the chunk
-      const uint4 vc = rs.vok[c] ? rs.v[c] : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 vc = (rs.vmask >> c & 1u) ? rs.v[c] : make_uint4(0u, 0u, 0u, 0u);
       if constexpr (kF8) {
         uint4 lo8, hi8;
         fp8_to_bf16(vc, lo8, hi8);
@@ -309,6 +305,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_mfma_kernel(AttnArgs a) {
     __builtin_amdgcn_wave_barrier();
     // S^T tiles
     float s[kNT][4];
+    bool inrange[kNT][4];          // the key is a row of the item (its V and scale are real)
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
       mfma_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -326,11 +323,14 @@ __global__ __launch_bounds__(kThreads) void cross_attn_mfma_kernel(AttnArgs a) {
                                                          0, 0, 0);
         }
       }
+      const bool tile_ok = (rs.tmask >> t & 1u) != 0u;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = rs.base + 16 * t + 4 * gi + e;
-        const bool ok = rs.sok[t][e] && qlive && j >= qlo && j < qhi;
-        const float sc = kF8 ? a.scale_log2 * rs.ks[t][e] : a.scale_log2;
+        inrange[t][e] = tile_ok && j >= item_lo && j < item_hi;
+        const bool ok = inrange[t][e] && qlive && j >= jlo && j < jhi;
+        float sc = a.scale_log2;
+        if constexpr (kF8) sc *= e == 0 ? rs.ks[t].x : e == 1 ? rs.ks[t].y : e == 2 ? rs.ks[t].z : rs.ks[t].w;
         s[t][e] = ok ? acc[e] * sc : -INFINITY;
       }
     }
@@ -358,7 +358,12 @@ __global__ __launch_bounds__(kThreads) void cross_attn_mfma_kernel(AttnArgs a) {
       for (int e = 0; e < 4; ++e) {
         const float p = fast_exp2(s[t][e] - m_run);
         l_run += p;
-        pv[e] = kF8 ? p * (rs.sok[t][e] ? rs.vs[t][e] : 0.0f) : p;
+        if constexpr (kF8) {
+          const float vsc = e == 0 ? rs.vs[t].x : e == 1 ? rs.vs[t].y : e == 2 ? rs.vs[t].z : rs.vs[t].w;
+          pv[e] = inrange[t][e] ? p * vsc : 0.0f;
+        } else {
+          pv[e] = p;
+        }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -419,23 +424,27 @@ __global__ __launch_bounds__(kThreads) void cross_attn_mfma_kernel(AttnArgs a) {
         const int qi = l16 / G;
         qlive = l16 < VG && qi < cur.nq;
         const int p = cur.pbase + qi;
-        qhi = kVar ? p + 1 : 0x7fffffff;
-        qlo = (kVar && a.window > 0) ? p - a.window + 1 : -0x7fffffff;
+        item_lo = cur.start;
+        item_hi = cur.end;
+        // the item's range [start, end), cut to the query's causal window
+        jhi = kVar ? min(cur.end, p + 1) : cur.end;
+        jlo = (kVar && a.window > 0) ? max(cur.start, p - a.window + 1) : cur.start;
       }
       m_run = kInitMax;
       l_run = 0.0f;
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) oacc[dt] = mfma_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      const int num_iters = (cur.end - cur.start + kNK - 1) / kNK;
+      const int base0 = cur.start & ~15;           // iterations start 16-aligned
+      const int num_iters = (cur.end - base0 + kNK - 1) / kNK;
       Rows ra, rb;
       int it = wave_u;
-      if (it < num_iters) load_rows(ra, cur, it);
+      if (it < num_iters) load_rows(ra, cur, base0 + it * kNK);
       while (it < num_iters) {
-        if (it + kWaves < num_iters) load_rows(rb, cur, it + kWaves);
+        if (it + kWaves < num_iters) load_rows(rb, cur, base0 + (it + kWaves) * kNK);
         compute(ra);
         it += kWaves;
         if (it >= num_iters) break;
-        if (it + kWaves < num_iters) load_rows(ra, cur, it + kWaves);
+        if (it + kWaves < num_iters) load_rows(ra, cur, base0 + (it + kWaves) * kNK);
         compute(rb);
         it += kWaves;
       }
