@@ -40,8 +40,10 @@ struct MfmaLayout {
   static_assert(kT == kBF16 || kT == kFP8, "bf16 or FP8 cache");
   static constexpr int kEb = kT == kFP8 ? 1 : 2;                       // cache element bytes
   static constexpr int kRowBytes = D * kEb;
-  // keys per wavefront iteration: about 8 KB of K^/V^, at least one tile
-  static constexpr int kNK = 8192 / (2 * kRowBytes) < 16 ? 16 : (8192 / (2 * kRowBytes) > 64 ? 64 : 8192 / (2 * kRowBytes));
+  // keys per wavefront iteration: about 8 KB of K^/V^ (bf16) or 4 KB (FP8,
+  // which keeps two wavefronts per SIMD in registers), at least one tile
+  static constexpr int kBudget = kT == kFP8 ? 4096 : 8192;
+  static constexpr int kNK = kBudget / (2 * kRowBytes) < 16 ? 16 : (kBudget / (2 * kRowBytes) > 64 ? 64 : kBudget / (2 * kRowBytes));
   static constexpr int kNT = kNK / 16;                                 // 16-key tiles per iteration
   static constexpr int kKS = D / 32;                                   // MFMA k-steps over head_dim
   static constexpr int kKL = kT == kFP8 ? D / 64 : D / 32;             // 16-byte K loads per tile per lane
@@ -82,7 +84,7 @@ struct MfmaSmem {
 };
 
 template <int kT, int D, int G, int QPI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kT == kBF16 && D <= 128 ? 2 : 1))) void cross_attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1))) void cross_attn_mfma_kernel(AttnArgs a) {
   using ML = MfmaLayout<kT, D>;
   constexpr bool kVar = QPI > 0;
   constexpr bool kF8 = kT == kFP8;
