@@ -313,10 +313,18 @@ def main():
     attn_us = float(layer_ms.mean()) * 1e3
     achieved = layer_bytes / (attn_us * 1e-6) / 1e9
     group = geom.num_q_heads // geom.num_kv_heads
-    rows_per_item = 0 if Q == 1 else 8 // group
+    # the kernel the library picks: matrix cores for an FP8 cache or several
+    # query rows per request (bf16), with block_size >= 16 and <= 2048 requests
+    mfma = (args.fp8 or (geom.dtype == "bf16" and Q > 1)) and R <= 2048 and geom.block_size >= 16
+    rows_per_item = 0 if Q == 1 else (16 if mfma else 8) // group
     elem_type = 2 if args.fp8 else (1 if geom.dtype == "bf16" else 0)
-    attn_kernel = f"cross_attn_kernel<{elem_type}, {geom.head_dim}, {group}, {rows_per_item}>"
-    merge_kernel = f"cross_attn_merge_kernel<{geom.head_dim}>"
+    kname = "cross_attn_mfma_kernel" if mfma else "cross_attn_kernel"
+    attn_kernel = f"{kname}<{elem_type}, {geom.head_dim}, {group}, {rows_per_item}>"
+    merge_split = 1
+    triples = R * Q * geom.num_q_heads
+    while merge_split < 8 and triples * merge_split < 512 and geom.head_dim // 4 // (merge_split * 2) >= 8:
+        merge_split *= 2
+    merge_kernel = f"cross_attn_merge_kernel<{geom.head_dim}, {merge_split}>"
     variant = geom.name + (f"_q{Q}" if Q > 1 else "") + (f"_w{W}" if W > 0 else "") + ("_fp8" if args.fp8 else "")
     measured = profiling.measured_traffic(variant, [attn_kernel, merge_kernel] if nparts > 1 else [attn_kernel])
     traffic = None

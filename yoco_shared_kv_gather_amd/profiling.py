@@ -109,7 +109,8 @@ def summarize(out: str, workload: str, command: str, top: int = 10) -> str:
         "|---|---:|---:|---:|---:|",
     ]
     records = {}
-    ours = [row for row in stats if not short_name(row["Name"]).startswith(("at::", "__amd", "c10::"))]
+    ours = [row for row in stats
+            if not short_name(row["Name"]).startswith(("at::", "__amd", "c10::", "rocprim::", "hipcub::"))]
     lines.insert(len(lines) - 3, "Kernels of this library only (input generation and cache flushing omitted).")
     lines.insert(len(lines) - 3, "")
     for row in ours[:top]:
