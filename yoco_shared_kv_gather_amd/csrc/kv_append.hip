@@ -69,8 +69,8 @@ __global__ __launch_bounds__(256) void fold_rms_weight_kernel(const uint4* __res
 
 constexpr int kBM = 128;                     // tokens per workgroup tile
 constexpr int kBN = 256;                     // output features per workgroup tile
-constexpr int kBK = 64;
-constexpr int kLdsStride = kBK + 8;          // bf16 elements per staged row (16-byte pad: conflict-free reads)
+constexpr int kBK = 32;
+constexpr int kLdsStride = kBK + 8;          // bf16 elements per staged row (16-byte pad)
 constexpr int kStage = (kBM + kBN) * kLdsStride;
 constexpr int kOutStride = kBN + 8;          // bf16 elements per row of the staged output tile
 constexpr int kGemmThreads = 256;
@@ -99,15 +99,17 @@ struct AppendArgs {
 };
 
 // One workgroup: 128 tokens x 256 output features, four wavefronts of 64 x 128
-// (4 x 8 MFMA tiles of 16x16, K step 32).  Workgroup id -> (token tile =
-// id / n_tiles, feature tile = id % n_tiles): consecutive workgroups go to
+// (4 x 8 MFMA tiles of 16x16), K step 32, two workgroups per compute unit
+// (K step 64 left one, with nothing to cover its LDS waits).  Workgroup id ->
+// (token tile = id / n_tiles, feature tile = id % n_tiles): consecutive workgroups go to
 // different XCDs, so each XCD keeps re-reading the same weight panels from its
 // own L2 while the XCDs share each activation tile through the last-level
 // cache.  Global -> registers -> LDS staging, two LDS stages, one barrier per
 // K step.  The epilogue scales by the row's rsqrt, rounds to bf16 into LDS and
 // writes each token's features as 16-byte chunks to its slot.
-__global__ __launch_bounds__(kGemmThreads) void kv_append_mfma_kernel(AppendArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * kStage];
+__global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2))) void kv_append_mfma_kernel(AppendArgs a) {
+  constexpr int kLdsElems = 2 * kStage > kBM * kOutStride ? 2 * kStage : kBM * kOutStride;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
   __shared__ float row_scale[kBM];
 
   const int tid = threadIdx.x;
@@ -119,24 +121,29 @@ __global__ __launch_bounds__(kGemmThreads) void kv_append_mfma_kernel(AppendArgs
   const int n0 = static_cast<int>(blockIdx.x % a.n_tiles) * kBN;
   const int n_total = 2 * a.out_half;
 
-  // Staging map: thread moves chunk kc (8 bf16) of A rows rbase+32i (i<4)
-  // and of B rows rbase+32i (i<8).
-  const int kc = tid & 7;
-  const int rbase = tid >> 3;
-  uint4 ra[4], rb[8];
-  float sumsq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // Staging map: thread moves chunk kc (8 bf16) of A rows rbase+kRp*i
+  // (i<kAP) and of B rows rbase+kRp*i (i<kBP).
+  constexpr int kCk = kBK / 8;                 // 16-byte chunks per staged row
+  constexpr int kRp = kGemmThreads / kCk;      // rows per staging pass
+  constexpr int kAP = kBM / kRp, kBP = kBN / kRp;
+  const int kc = tid % kCk;
+  const int rbase = tid / kCk;
+  uint4 ra[kAP], rb[kBP];
+  float sumsq[kAP];
+#pragma unroll
+  for (int i = 0; i < kAP; ++i) sumsq[i] = 0.0f;
 
   auto load_tile = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = m0 + rbase + 32 * i;
+    for (int i = 0; i < kAP; ++i) {
+      const int row = m0 + rbase + kRp * i;
       ra[i] = row < a.num_tokens
                   ? *reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(row) * a.hidden + k0 + kc * 8)
                   : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int col = n0 + rbase + 32 * i;
+    for (int i = 0; i < kBP; ++i) {
+      const int col = n0 + rbase + kRp * i;
       rb[i] = col < n_total
                   ? *reinterpret_cast<const uint4*>(a.w + static_cast<int64_t>(col) * a.hidden + k0 + kc * 8)
                   : make_uint4(0u, 0u, 0u, 0u);
@@ -146,8 +153,8 @@ __global__ __launch_bounds__(kGemmThreads) void kv_append_mfma_kernel(AppendArgs
     uint16_t* as = lds + stage * kStage;
     uint16_t* bs = as + kBM * kLdsStride;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<uint4*>(&as[(rbase + 32 * i) * kLdsStride + kc * 8]) = ra[i];
+    for (int i = 0; i < kAP; ++i) {
+      *reinterpret_cast<uint4*>(&as[(rbase + kRp * i) * kLdsStride + kc * 8]) = ra[i];
       const uint32_t* u = reinterpret_cast<const uint32_t*>(&ra[i]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -158,7 +165,7 @@ __global__ __launch_bounds__(kGemmThreads) void kv_append_mfma_kernel(AppendArgs
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&bs[(rbase + 32 * i) * kLdsStride + kc * 8]) = rb[i];
+    for (int i = 0; i < kBP; ++i) *reinterpret_cast<uint4*>(&bs[(rbase + kRp * i) * kLdsStride + kc * 8]) = rb[i];
   };
 
   f32x4 acc[4][8];
@@ -168,16 +175,10 @@ __global__ __launch_bounds__(kGemmThreads) void kv_append_mfma_kernel(AppendArgs
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   const int ktiles = a.hidden / kBK;
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
   const int frag_row = lane & 15;
   const int frag_k = (lane >> 4) * 8;
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < ktiles) load_tile((kt + 1) * kBK);
-    const uint16_t* as = lds + cur * kStage;
+  auto mma = [&](int stage) {
+    const uint16_t* as = lds + stage * kStage;
     const uint16_t* bs = as + kBM * kLdsStride;
 #pragma unroll
     for (int ks = 0; ks < kBK; ks += 32) {
@@ -193,18 +194,26 @@ __global__ __launch_bounds__(kGemmThreads) void kv_append_mfma_kernel(AppendArgs
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < ktiles) store_tile(cur ^ 1);
+  };
+
+  // Tile kt is in LDS stage kt&1 while tile kt+1 is fetched into registers.
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int kt = 0; kt < ktiles; ++kt) {
+    if (kt + 1 < ktiles) load_tile((kt + 1) * kBK);
+    mma(kt & 1);
+    if (kt + 1 < ktiles) store_tile((kt + 1) & 1);
     __syncthreads();
   }
 
-  // Row scale rsqrt(mean(x^2) + eps): add the eight partial sums of each row.
+  // Row scale rsqrt(mean(x^2) + eps): add the kCk partial sums of each row.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < kAP; ++i) {
     float v = sumsq[i];
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    v += __shfl_xor(v, 4, 64);
-    if (kc == 0) row_scale[rbase + 32 * i] = 1.0f / sqrtf(v * a.inv_hidden + a.eps);
+#pragma unroll
+    for (int off = 1; off < kCk; off <<= 1) v += __shfl_xor(v, off, 64);
+    if (kc == 0) row_scale[rbase + kRp * i] = 1.0f / sqrtf(v * a.inv_hidden + a.eps);
   }
   __syncthreads();
 
