@@ -375,8 +375,11 @@ int32_t yoco_gather_logits(const void* hidden, int64_t num_tokens, int64_t row_b
  *                   the kernel.  k_scale, v_scale must be NULL otherwise.
  *
  * With query_start_loc: num_seqs <= 2048 (YOCO_ERR_UNSUPPORTED beyond); a
- * work item streams its K^/V^ rows once for up to 8 query vectors (rows x
- * heads of one KV group).  A NaN in a row that some of a request's rows read
+ * work item streams its K^/V^ rows once for several query vectors (rows x
+ * heads of one KV group): up to 16 on the matrix-core kernel, which runs an
+ * FP8 cache and bf16 with several rows per request when block_size >= 16
+ * (and the scales are 16-byte aligned), up to 8 on the vector kernel
+ * otherwise or with YOCO_FLAG_VECTOR_KERNEL.  A NaN in a row that some of a request's rows read
  * may give NaN in all of that request's rows.  Errors as in yoco_cross_attn.
  */
 int64_t yoco_cross_attn_varlen_workspace_size(int32_t num_rows, int32_t num_seqs, int32_t num_q_heads,
