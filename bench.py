@@ -250,7 +250,7 @@ def main():
     stream = torch.cuda.current_stream()
     L = geom.num_layers
 
-    def step(ev_layers=None):
+    def step(ev_layers_start=None):
         if args.fp8:
             yb.kv_append_fp8(x, w_rms, 1e-6, w_k, w_v, slots, k, v, ks, vs, workspace=ws_append, stream=stream)
         else:
@@ -260,9 +260,9 @@ def main():
                              stream=stream)
         else:
             yb.gather_last(x, cu, out=rows[:R], out_index=rows_idx, stream=stream)
+        if ev_layers_start is not None:
+            ev_layers_start.record(stream)
         for l in range(L):
-            if ev_layers is not None:
-                ev_layers[l][0].record(stream)
             if varlen:
                 yb.cross_attn_varlen(q[l], k, v, table, seq, meta.max_seq_len,
                                      query_start_loc=cross_qsl if Q > 1 else None, max_query_len=Q, window=W,
@@ -271,8 +271,6 @@ def main():
             else:
                 yb.cross_attn(q[l], k, v, table, seq, meta.max_seq_len, partition_tokens=args.partition_tokens,
                               flags=l & 1, out=outs[l], workspace=ws, stream=stream)
-            if ev_layers is not None:
-                ev_layers[l][1].record(stream)
 
     for i in range(args.warmup):
         if not args.no_flush:
@@ -281,21 +279,21 @@ def main():
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} steps); partition_tokens {part}, {nparts} partitions per request")
 
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    ev_l = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(L)]
-            for _ in range(args.steps)]
+    # Three events per step: step start, start of the cross layers, step end
+    # (an event between every layer would add its own gap to every call).
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         if not args.no_flush:
             flush.sum(dtype=torch.int64)
         ev[i][0].record(stream)
-        step(ev_l[i])
-        ev[i][1].record(stream)
+        step(ev[i][1])
+        ev[i][2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
-    layer_ms = np.array([[a.elapsed_time(b) for a, b in row] for row in ev_l])
+    step_ms = np.array([a.elapsed_time(c) for a, _, c in ev])
+    layer_ms = np.array([b.elapsed_time(c) / L for _, b, c in ev])    # average call, inter-layer gaps included
     ms_per_step = float(step_ms.mean())
     tokens_per_s = num_rows / (ms_per_step * 1e-3)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (events), wall {1e3 * wall / args.steps:.3f} ms/step")
@@ -378,8 +376,8 @@ def main():
             "bytes_per_launch": layer_bytes,
             "avg_launch_us": round(attn_us, 2),
             # the same kernels' summed average durations in the committed
-            # rocprofv3 trace (the event time also holds the launch gap
-            # between the attention and the merge kernel)
+            # rocprofv3 trace (avg_launch_us is the span of the L serial
+            # calls over L, so it also holds the gaps between the kernels)
             "profile_kernel_us": profile_us,
         },
     }
