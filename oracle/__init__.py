@@ -11,6 +11,7 @@ from .yoco_oracle import (  # noqa: F401
     dequantize_cache,
     e4m3_decode,
     e4m3_encode,
+    gated_retention,
     kv_append_fp8,
     kv_scatter,
     quantize_rows,

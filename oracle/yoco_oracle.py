@@ -6,7 +6,7 @@ It shares no code, tables or helpers with the HIP path, and it never reads a
 value that the HIP path produced: every input it sees comes from the seeded
 generators or from the pages.
 
-It is the plain, slow definition of what the three library calls compute,
+It is the plain, slow definition of what the library's calls compute,
 written with NumPy in float64 (bf16 and fp32 inputs convert to float64
 exactly).  Loops run over requests, heads and tokens; a matrix product is the
 only library primitive used.  Where the pages leave a step open, the reading
@@ -24,7 +24,9 @@ Pages cited (by title and section):
           per token; every cross layer reads the same K̂, V̂), §7.4 (only the last
           position goes through the cross-decoder), §10.3 (one append per token,
           not per layer), §10.4 (query differs per layer, K/V are shared),
-          §13.2 (query length 1 against KV length t).
+          §13.2 (query length 1 against KV length t), §4.1-4.2 (the
+          self-decoder's gated retention: a gated linear recurrence over a
+          fixed-size state, with parallel, recurrent and chunkwise forms).
   [KV]    "KV cache memory systems" (blog.ecitis.org), section "Cache contents"
           (decode attention softmax(q_t K_{<=t}^T / sqrt(d_h)) V_{<=t}) and
           section "Contiguous allocation wastes capacity" (every logical block
@@ -58,6 +60,7 @@ __all__ = [
     "dequantize_cache",
     "kv_scatter",
     "kv_append_fp8",
+    "gated_retention",
 ]
 
 
@@ -477,3 +480,44 @@ def kv_append_fp8(x, rms_weight, eps: float, w_k, w_v, slot_mapping, num_kv_head
     ck, sk = quantize_rows(k.astype(np.float32))
     cv, sv = quantize_rows(v.astype(np.float32))
     return k, v, (ck, sk), (cv, sv), bk, bv
+
+
+# ---------------------------------------------------------------------------
+# Self-decoder gated retention  ([YOCO] §4.1-4.2)
+# ---------------------------------------------------------------------------
+#
+# The page describes gated retention as a linear recurrence with a
+# data-dependent forget gate gamma_t: a fixed-size state S compresses the
+# history, K_t^T V_t writes the current token into it, and the query reads
+# from it; parallel, recurrent and chunkwise forms compute the same thing.
+# Its formulas did not survive extraction.  Reading taken: per head,
+#     S_t = gamma_t * S_{t-1} + k_t^T v_t      (S: [d_k][d_v], k_t^T v_t the outer product)
+#     o_t = q_t S_t                           (the current token included)
+# with gamma_t in (0, 1] given per (token, head) (how the model computes it
+# from the input is not on the page), no output normalisation, no scale.
+
+def gated_retention(q, k, v, gamma, cu_seqlens, state, state_indices):
+    """The recurrent form, token by token, for a batch of requests.
+
+    q, k: ``[T][H][Dk]``; v: ``[T][H][Dv]``; gamma: ``[T][H]``; request r owns
+    rows ``cu_seqlens[r] .. cu_seqlens[r+1]-1`` in order; state: ``[slots][H]
+    [Dk][Dv]``, request r starting from slot ``state_indices[r]`` (a negative
+    index starts from zeros and stores nothing).  Returns float64 ``(out
+    [T][H][Dv], new_state)``: every request's final state written to its slot.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    gamma = _f64(gamma)
+    out = np.zeros(v.shape, dtype=np.float64)
+    new_state = _f64(state).copy()
+    cu = [int(c) for c in np.asarray(cu_seqlens)]
+    num_heads = q.shape[1]
+    for r in range(len(cu) - 1):
+        slot = int(state_indices[r])
+        for h in range(num_heads):
+            s = new_state[slot, h].copy() if slot >= 0 else np.zeros((k.shape[2], v.shape[2]))
+            for t in range(cu[r], cu[r + 1]):
+                s = gamma[t, h] * s + np.outer(k[t, h], v[t, h])
+                out[t, h] = q[t, h] @ s
+            if slot >= 0:
+                new_state[slot, h] = s
+    return out, new_state

@@ -608,3 +608,116 @@ FP8_DECODE_CHECKS = [check_e4m3_decode]
 FP8_ENCODE_CHECKS = [check_e4m3_encode]
 QUANT_CHECKS = [check_quantize_rows]
 SCATTER_CHECKS = [check_kv_scatter]
+
+
+# ---------------------------------------------------------------------------
+# gated retention (self-decoder)
+# ---------------------------------------------------------------------------
+
+def _retention_problem(rng, lens, h=2, dk=4, dv=3, slots=4, gamma_range=(0.5, 1.0)):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    t = int(cu[-1])
+    q = rng.standard_normal((t, h, dk))
+    k = rng.standard_normal((t, h, dk))
+    v = rng.standard_normal((t, h, dv))
+    g = rng.uniform(*gamma_range, size=(t, h))
+    state = rng.standard_normal((slots, h, dk, dv))
+    idx = rng.permutation(slots)[:len(lens)]
+    return q, k, v, g, cu, state, idx
+
+
+def check_retention_parallel_form(ret):
+    """The parallel form, derived by unrolling the recurrence (written here
+    independently as a double sum): o_t = sum_{s<=t} (prod_{s<u<=t} g_u)
+    (q_t . k_s) v_s + (prod_{u<=t} g_u) q_t S_0, over each request's rows."""
+    rng = np.random.default_rng(71)
+    q, k, v, g, cu, state, idx = _retention_problem(rng, [5, 1, 7])
+    out, new_state = ret(q, k, v, g, cu, state, idx)
+    for r in range(len(cu) - 1):
+        a, b = int(cu[r]), int(cu[r + 1])
+        for h in range(q.shape[1]):
+            for t in range(a, b):
+                ref = np.prod(g[a:t + 1, h]) * (q[t, h] @ state[idx[r], h])
+                for s_ in range(a, t + 1):
+                    ref = ref + np.prod(g[s_ + 1:t + 1, h]) * (q[t, h] @ k[s_, h]) * v[s_, h]
+                np.testing.assert_allclose(out[t, h], ref, rtol=0, atol=1e-12)
+            fin = np.prod(g[a:b, h]) * state[idx[r], h]
+            for s_ in range(a, b):
+                fin = fin + np.prod(g[s_ + 1:b, h]) * np.outer(k[s_, h], v[s_, h])
+            np.testing.assert_allclose(new_state[idx[r], h], fin, rtol=0, atol=1e-12)
+
+
+def check_retention_linear_attention(ret):
+    """Library routine: with gamma = 1 and a zero state it is causal linear
+    attention, tril(Q K^T) V per head (torch matmul + tril in float64)."""
+    rng = np.random.default_rng(72)
+    q, k, v, g, cu, state, idx = _retention_problem(rng, [9, 4])
+    g[:] = 1.0
+    state[:] = 0.0
+    out, _ = ret(q, k, v, g, cu, state, idx)
+    for r in range(len(cu) - 1):
+        a, b = int(cu[r]), int(cu[r + 1])
+        for h in range(q.shape[1]):
+            qt, kt, vt = (torch.from_numpy(x[a:b, h]) for x in (q, k, v))
+            ref = torch.tril(qt @ kt.T) @ vt
+            np.testing.assert_allclose(out[a:b, h], ref.numpy(), rtol=0, atol=1e-12)
+
+
+def check_retention_closed_forms(ret):
+    """gamma = 0 keeps only the current token: o_t = (q_t . k_t) v_t and the
+    final state is k_T^T v_T; a negative slot starts from zeros and leaves
+    every slot unchanged."""
+    rng = np.random.default_rng(73)
+    q, k, v, g, cu, state, idx = _retention_problem(rng, [3, 6])
+    g[:] = 0.0
+    out, new_state = ret(q, k, v, g, cu, state, idx)
+    for t in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            np.testing.assert_allclose(out[t, h], (q[t, h] @ k[t, h]) * v[t, h], rtol=0, atol=1e-13)
+    for r in range(2):
+        last = int(cu[r + 1]) - 1
+        for h in range(q.shape[1]):
+            np.testing.assert_allclose(new_state[idx[r], h], np.outer(k[last, h], v[last, h]), rtol=0, atol=1e-13)
+    q, k, v, g, cu, state, idx = _retention_problem(rng, [4])
+    out, new_state = ret(q, k, v, g, cu, state, np.array([-1]))
+    assert np.array_equal(new_state, state)
+    ref, _ = ret(q, k, v, g, cu, np.zeros_like(state), np.array([0]))
+    np.testing.assert_allclose(out, ref, rtol=0, atol=0)
+
+
+def check_retention_carry(ret):
+    """Splitting every request's rows into two calls, the state carried in
+    its slot, gives the single call's outputs and final state."""
+    rng = np.random.default_rng(74)
+    lens = [6, 3, 8]
+    q, k, v, g, cu, state, idx = _retention_problem(rng, lens)
+    out, fin = ret(q, k, v, g, cu, state, idx)
+    first = [2, 1, 5]
+    rows1 = np.concatenate([np.arange(cu[r], cu[r] + first[r]) for r in range(3)])
+    rows2 = np.concatenate([np.arange(cu[r] + first[r], cu[r + 1]) for r in range(3)])
+    cu1 = np.concatenate([[0], np.cumsum(first)])
+    cu2 = np.concatenate([[0], np.cumsum(np.array(lens) - np.array(first))])
+    o1, s1 = ret(q[rows1], k[rows1], v[rows1], g[rows1], cu1, state, idx)
+    o2, s2 = ret(q[rows2], k[rows2], v[rows2], g[rows2], cu2, s1, idx)
+    np.testing.assert_allclose(o1, out[rows1], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o2, out[rows2], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(s2, fin, rtol=0, atol=1e-12)
+
+
+def check_retention_decimal(ret):
+    """Brute force in 50-digit decimal on a tiny sequence."""
+    getcontext().prec = 50
+    rng = np.random.default_rng(75)
+    q, k, v, g, cu, state, idx = _retention_problem(rng, [4], h=1, dk=2, dv=2, slots=1)
+    out, _ = ret(q, k, v, g, cu, state, np.array([0]))
+    S = [[Decimal(float(state[0, 0, i, j])) for j in range(2)] for i in range(2)]
+    for t in range(4):
+        gt = Decimal(float(g[t, 0]))
+        S = [[gt * S[i][j] + Decimal(float(k[t, 0, i])) * Decimal(float(v[t, 0, j])) for j in range(2)] for i in range(2)]
+        for j in range(2):
+            ref = sum(Decimal(float(q[t, 0, i])) * S[i][j] for i in range(2))
+            assert abs(out[t, 0, j] - float(ref)) < 1e-13
+
+
+RETENTION_CHECKS = [check_retention_parallel_form, check_retention_linear_attention, check_retention_closed_forms,
+                    check_retention_carry, check_retention_decimal]

@@ -256,6 +256,35 @@ FP8_ENCODE_MUTANTS = {"ties_up": _encode_variant(ties_up=True), "no_subnormals":
 QUANT_MUTANTS = {"int8_range": _quant_variant(qmax=127.0), "scale_from_mean": _quant_variant(scale_from_mean=True)}
 
 
+def _retention_variant(update=None, read_before=False, store=True):
+    def ret(q, k, v, gamma, cu_seqlens, state, state_indices):
+        q, k, v, gamma = (np.asarray(x, dtype=np.float64) for x in (q, k, v, gamma))
+        out = np.zeros(v.shape)
+        new = np.asarray(state, dtype=np.float64).copy()
+        cu = [int(c) for c in cu_seqlens]
+        for r in range(len(cu) - 1):
+            slot = int(state_indices[r])
+            for h in range(q.shape[1]):
+                s = new[slot, h].copy() if slot >= 0 else np.zeros((k.shape[2], v.shape[2]))
+                for t in range(cu[r], cu[r + 1]):
+                    prev = s
+                    s = gamma[t, h] * s + np.outer(k[t, h], v[t, h]) if update is None else update(s, gamma[t, h],
+                                                                                                  k[t, h], v[t, h])
+                    out[t, h] = q[t, h] @ (prev if read_before else s)
+                if slot >= 0 and store:
+                    new[slot, h] = s
+        return out, new
+    return ret
+
+
+RETENTION_MUTANTS = {
+    "gate_after_write": _retention_variant(update=lambda s, g, k, v: g * (s + np.outer(k, v))),
+    "read_before_write": _retention_variant(read_before=True),
+    "gamma_ignored": _retention_variant(update=lambda s, g, k, v: s + np.outer(k, v)),
+    "state_not_stored": _retention_variant(store=False),
+}
+
+
 def _fails_some(checks, fn):
     failures = 0
     for check in checks:
@@ -328,3 +357,12 @@ def test_unmutated_fp8_copies_pass():
     assert _fails_some(pins.FP8_DECODE_CHECKS, _decode_variant()) == 0
     assert _fails_some(pins.FP8_ENCODE_CHECKS, _encode_variant()) == 0
     assert _fails_some(pins.QUANT_CHECKS, _quant_variant()) == 0
+
+
+@pytest.mark.parametrize("name", sorted(RETENTION_MUTANTS))
+def test_retention_mutant_is_caught(name):
+    assert _fails_some(pins.RETENTION_CHECKS, RETENTION_MUTANTS[name]) > 0
+
+
+def test_unmutated_retention_copy_passes():
+    assert _fails_some(pins.RETENTION_CHECKS, _retention_variant()) == 0

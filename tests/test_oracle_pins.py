@@ -70,3 +70,8 @@ def test_dequantize_cache_is_code_times_scale():
     scales = np.array([[[2.5], [0.0]]], dtype=np.float32)
     out = oracle.dequantize_cache(codes, scales)
     assert out.tolist() == [[[[2.5, -5.0]], [[0.0, 0.0]]]]
+
+
+@pytest.mark.parametrize("check", pins.RETENTION_CHECKS, ids=lambda c: c.__name__)
+def test_retention_pins(check):
+    check(oracle.gated_retention)
