@@ -46,7 +46,7 @@
  *
  * The operations are defined on these pages (cited by title and section):
  *   [vLLM] "You Only Cache Once, in vLLM", section "Implementation in vLLM".
- *   [YOCO] "YOCO_论文与推理数据流详解", sections 3, 7.4, 9, 10.3, 10.4, 13.
+ *   [YOCO] "YOCO_论文与推理数据流详解", sections 3, 4.1-4.2, 7.4, 9, 10.3, 10.4, 13.
  *   [KV]   "KV cache memory systems", sections "Cache contents" and
  *          "Contiguous allocation wastes capacity".
  *   [Gemma] "You Only Cache Once, in vLLM", section "Gemma 3n": cross layers
@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define YOCO_ABI_VERSION 3
+#define YOCO_ABI_VERSION 4
 
 typedef enum yoco_status {
   YOCO_OK = 0,
@@ -395,6 +395,54 @@ int32_t yoco_cross_attn_varlen(int32_t dtype, const void* q, int32_t num_rows,
                                const int32_t* seq_lens, int32_t max_seq_len, int32_t window, float scale,
                                int32_t partition_tokens, uint32_t flags, float* out, void* workspace,
                                int64_t workspace_bytes, void* stream);
+
+/*
+ * yoco_gated_retention -- the self-decoder's gated retention over a batch of
+ * requests (prefill chunks and decode tokens alike), with per-request states.
+ *
+ * [YOCO] sections 4.1-4.2: gated retention is a linear recurrence with an
+ * input-dependent forget gate over a fixed-size state per head; the current
+ * token's k^T v is written in and the query reads from the state; prefill
+ * uses the chunkwise form, decode the recurrent one.  The page's formulas did
+ * not survive; this call computes, per request and head, over the request's
+ * rows in order:
+ *     S_t = gamma_t * S_{t-1} + k_t^T v_t        (outer product, [D][D])
+ *     o_t = q_t S_t                              (the current token included)
+ * starting from the request's state slot, and writes the final S_t back to
+ * the slot.  No scale or normalisation is applied.
+ *
+ *   dtype          YOCO_DTYPE_BF16 (q, k, v); YOCO_DTYPE_F32 returns
+ *                  YOCO_ERR_UNSUPPORTED.
+ *   q, k, v        [num_tokens][num_heads][head_dim], token-major, 16-byte
+ *                  aligned.
+ *   gamma          fp32 [num_tokens][num_heads], the gate of each token and
+ *                  head, in [0, 1].  log2 gamma is clamped at -64 (a zero gate
+ *                  weighs 2^-64).
+ *   head_dim       64 or 128 (key and value head_dim alike; else
+ *                  YOCO_ERR_UNSUPPORTED).
+ *   cu_seqlens     int32 [num_reqs + 1]: request r owns rows
+ *                  cu_seqlens[r] .. cu_seqlens[r+1]-1 (clamped to
+ *                  [0, num_tokens]; a request with no rows leaves its slot
+ *                  untouched).
+ *   state          fp32 [num_slots][num_heads][head_dim][head_dim] (key row,
+ *                  value column), read and updated in place.
+ *   state_indices  int32 [num_reqs]: request r's slot.  A slot outside
+ *                  [0, num_slots) starts from zeros and is not stored.
+ *                  Requests with rows must name distinct slots (they run
+ *                  concurrently).
+ *   out            fp32 [num_tokens][num_heads][head_dim]: o_t of every row
+ *                  owned by a request (other rows are not written).
+ *
+ * Computed chunkwise in 32-token chunks on the matrix cores: bf16 q, k, v
+ * exact, fp32 operands (state, decayed scores, gated keys) as two bf16 parts,
+ * fp32 sums.  Errors: YOCO_ERR_INVALID_ARGUMENT (null pointers, negative
+ * counts, misalignment), YOCO_ERR_UNSUPPORTED, YOCO_ERR_HIP.  num_reqs == 0
+ * or num_tokens == 0 is a no-op.
+ */
+int32_t yoco_gated_retention(int32_t dtype, const void* q, const void* k, const void* v, const float* gamma,
+                             int32_t num_tokens, int32_t num_heads, int32_t head_dim,
+                             const int32_t* cu_seqlens, int32_t num_reqs, float* state, int32_t num_slots,
+                             const int32_t* state_indices, float* out, void* stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

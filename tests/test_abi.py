@@ -175,3 +175,36 @@ def test_varlen_workspace_follows_the_window():
 ])
 def test_gather_logits_rejects_before_launch(args, status):
     assert yb.lib().yoco_gather_logits(*args) == status
+
+
+def _retention(**kw):
+    args = dict(dtype=1, q=FAKE, k=FAKE, v=FAKE, gamma=FAKE, num_tokens=40, num_heads=4, head_dim=128, cu=FAKE,
+                num_reqs=2, state=FAKE, num_slots=4, slots=FAKE, out=FAKE, stream=None)
+    args.update(kw)
+    return yb.lib().yoco_gated_retention(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), yb.YOCO_ERR_UNSUPPORTED),                       # fp32 q/k/v: no kernel
+    (dict(dtype=2), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(head_dim=96), yb.YOCO_ERR_UNSUPPORTED),
+    (dict(head_dim=256), yb.YOCO_ERR_UNSUPPORTED),
+    (dict(num_tokens=-1), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(num_slots=-1), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(cu=None), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(slots=None), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(state=None), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(gamma=None), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(out=None), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(q=FAKE + 8), yb.YOCO_ERR_INVALID_ARGUMENT),               # 16-byte alignment
+    (dict(out=FAKE + 2), yb.YOCO_ERR_INVALID_ARGUMENT),
+])
+def test_gated_retention_rejects_before_launch(kw, status):
+    assert _retention(**kw) == status
+    assert yb.last_error_message()
+
+
+def test_gated_retention_nothing_to_do():
+    assert _retention(num_reqs=0) == yb.YOCO_OK
+    assert _retention(num_heads=0) == yb.YOCO_OK
+    assert _retention(num_tokens=0) == yb.YOCO_OK

@@ -17,7 +17,7 @@ from typing import Optional, Tuple
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libyoco.so")
 
-ABI_VERSION = 3
+ABI_VERSION = 4
 YOCO_OK = 0
 YOCO_ERR_INVALID_ARGUMENT = 1
 YOCO_ERR_UNSUPPORTED = 2
@@ -58,6 +58,7 @@ SIGNATURES = {
     "yoco_cross_attn_varlen_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "yoco_cross_attn_varlen": (_i32, [_i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                       _i32, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _u32, _vp, _vp, _i64, _vp]),
+    "yoco_gated_retention": (_i32, [_i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
 }
 
 _lock = threading.Lock()
@@ -341,6 +342,35 @@ def cross_attn_varlen(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, q
                                         _i32_dev(seq_lens, "seq_lens"), int(max_seq_len), int(window), float(scale),
                                         int(partition_tokens), int(flags), _dev(out, "out"), _dev(workspace, "workspace"),
                                         workspace.numel() * workspace.element_size(), _stream_handle(stream)))
+    return out
+
+
+# ---- yoco_gated_retention -------------------------------------------------------
+
+def gated_retention(q, k, v, gamma, cu_seqlens, state, state_indices, out=None, stream=None):
+    """Self-decoder gated retention over each request's rows, chunkwise:
+    S_t = gamma_t S_{t-1} + k_t^T v_t, o_t = q_t S_t per head, from and back
+    to the request's state slot.  q, k, v: bf16 [T][H][D]; gamma: fp32 [T][H];
+    state: fp32 [slots][H][D][D] (updated in place); returns out fp32
+    [T][H][D] (rows of no request are left as allocated)."""
+    torch = _torch()
+    num_tokens, num_heads, head_dim = q.shape
+    if out is None:
+        out = torch.empty((num_tokens, num_heads, head_dim), dtype=torch.float32, device=q.device)
+    if gamma.dtype != torch.float32 or state.dtype != torch.float32 or out.dtype != torch.float32:
+        raise TypeError("gamma, state and out must be float32")
+    if k.shape != q.shape or v.shape != q.shape or tuple(gamma.shape) != (num_tokens, num_heads):
+        raise ValueError("q, k, v must share [T][H][D] and gamma must be [T][H]")
+    if state.dim() != 4 or tuple(state.shape[1:]) != (num_heads, head_dim, head_dim):
+        raise ValueError("state must be [slots][H][D][D]")
+    if state_indices.numel() != cu_seqlens.shape[0] - 1:
+        raise ValueError("state_indices needs one slot per request")
+    num_slots = state.shape[0]
+    _check(lib().yoco_gated_retention(_dtype_code(q), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(gamma, "gamma"),
+                                      num_tokens, num_heads, head_dim, _i32_dev(cu_seqlens, "cu_seqlens"),
+                                      cu_seqlens.shape[0] - 1, _dev(state, "state") if num_slots > 0 else None,
+                                      num_slots, _i32_dev(state_indices, "state_indices"), _dev(out, "out"),
+                                      _stream_handle(stream)))
     return out
 
 

@@ -22,7 +22,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libyoco.so")
 
 SOURCES = ["abi.hip", "gather_last.hip", "kv_append.hip", "cross_attn.hip", "cross_attn_f32.hip", "cross_attn_bf16.hip",
-           "cross_attn_fp8.hip", "cross_attn_mfma_bf16.hip", "cross_attn_mfma_fp8.hip"]
+           "cross_attn_fp8.hip", "cross_attn_mfma_bf16.hip", "cross_attn_mfma_fp8.hip", "retention.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

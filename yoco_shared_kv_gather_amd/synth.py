@@ -418,6 +418,64 @@ def make_append_inputs(meta: Metadata, device="cpu", seed: int = SEED_BASE, rms_
     return x, w, w_k, w_v
 
 
+@dataclasses.dataclass
+class RetentionInputs:
+    """One self-decoder retention layer's inputs for a batch of requests."""
+    lens: np.ndarray            # int64 [R] rows per request
+    cu_seqlens: np.ndarray      # int32 [R + 1]
+    state_indices: np.ndarray   # int32 [R] (distinct; -1 = start from zeros)
+    q: object                   # bf16 [T][H][D]
+    k: object                   # bf16 [T][H][D], drawn with std D^-1/2
+    v: object                   # bf16 [T][H][D]
+    gamma: object               # fp32 [T][H], uniform in gamma_range
+    state: object               # fp32 [slots][H][D][D], N(0, 1/D)
+
+
+def retention_lengths(name: str, seed: int = SEED_BASE) -> np.ndarray:
+    """Rows per request of a retention workload: "mixed48" is the mixed step's
+    request mix (16 prefills, prompts log-uniform in [512, 16384], and 32
+    one-token decodes); "decode64" is 64 one-token decodes."""
+    if name == "mixed48":
+        meta = make_metadata(4, "full", seed)
+        return np.diff(meta.cu_seqlens).astype(np.int64)
+    if name == "decode64":
+        return np.ones(64, dtype=np.int64)
+    raise ValueError(name)
+
+
+def make_retention_inputs(lens, num_heads: int, head_dim: int, device="cpu", seed: int = SEED_BASE,
+                          gamma_range=(0.85, 1.0), num_slots: Optional[int] = None, zero_state_every: int = 0,
+                          tag: int = 77) -> RetentionInputs:
+    """Seeded q, k, v (bf16), gates, initial states and slot numbers for the
+    requests' rows ``lens``.  Slots are a random injective map into
+    ``num_slots`` (default 1.25x the requests); with ``zero_state_every`` = m,
+    every m-th request gets slot -1 (it starts from a zero state)."""
+    import torch
+    lens = np.asarray(lens, dtype=np.int64)
+    num_reqs = len(lens)
+    ss = np.random.SeedSequence([seed, tag, num_reqs, num_heads, head_dim])
+    rng = _rng(ss, 0)
+    cu = np.zeros(num_reqs + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(lens)
+    total = int(cu[-1])
+    slots = num_slots if num_slots is not None else max(1, (5 * num_reqs + 3) // 4)
+    idx = rng.permutation(slots)[:num_reqs].astype(np.int32)
+    if zero_state_every > 0:
+        idx[::zero_state_every] = -1
+    shape = (total, num_heads, head_dim)
+    bf = torch.bfloat16
+    chunk = 1 << 14
+    q = _randn(shape, bf, device, _child_seed(ss, 1), chunk_rows=chunk)
+    k = _randn(shape, bf, device, _child_seed(ss, 2), std=head_dim ** -0.5, chunk_rows=chunk)
+    v = _randn(shape, bf, device, _child_seed(ss, 3), chunk_rows=chunk)
+    lo, hi = gamma_range
+    g = _generator(device, _child_seed(ss, 4))
+    gamma = torch.rand((total, num_heads), generator=g, dtype=torch.float32, device=device).mul_(hi - lo).add_(lo)
+    state = _randn((slots, num_heads, head_dim, head_dim), torch.float32, device, _child_seed(ss, 5),
+                   std=head_dim ** -0.5, chunk_rows=64)
+    return RetentionInputs(lens, cu, idx, q, k, v, gamma, state)
+
+
 def describe(meta: Metadata) -> dict:
     """Small JSON-able summary of a workload."""
     return {
