@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--query-rows", type=int, default=1, help="query rows per request (decode workloads 2, 3, 5)")
     p.add_argument("--window", type=int, default=0, help="sliding window of every cross layer in tokens (0 = none)")
     p.add_argument("--fp8", action="store_true", help="8-bit shared cache (FP8 E4M3 codes, per-row scales)")
+    p.add_argument("--retention", choices=["mixed48", "decode64"], default=None,
+                   help="time the self-decoder's gated retention instead (16 layers, 24 heads x 128) over the "
+                        "mixed step's rows or 64 decode tokens")
     p.add_argument("--no-flush", action="store_true", help="keep the last-level cache warm between steps")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -185,6 +188,171 @@ def synth_live(meta):
     return synth.live_slot_mask(meta)
 
 
+RETENTION_HEADS, RETENTION_DIM, RETENTION_LAYERS = 24, 128, 16
+
+
+def retention_cpu_baseline(layer, budget_s):
+    """The float64 oracle's recurrence on (request, head) slices of one layer,
+    longest requests first, until the budget is spent; rows x heads per
+    second, scaled to the whole pass."""
+    import oracle
+
+    lens = layer["lens"]
+    cu = layer["cu"]
+    order = np.argsort(-lens, kind="stable")
+    done = 0
+    t0 = time.perf_counter()
+    for r in order:
+        a, b = int(cu[r]), int(cu[r + 1])
+        if b == a:
+            continue
+        for h in range(RETENTION_HEADS):
+            sl = lambda x: x[a:b, h:h + 1]
+            oracle.gated_retention(sl(layer["q"]), sl(layer["k"]), sl(layer["v"]), sl(layer["g"]),
+                                   np.array([0, b - a]), layer["s"][:, h:h + 1], np.array([int(layer["idx"][r])]))
+            done += b - a
+            if time.perf_counter() - t0 > budget_s:
+                break
+        if time.perf_counter() - t0 > budget_s:
+            break
+    elapsed = time.perf_counter() - t0
+    rate = done / elapsed                                 # rows x heads per second
+    tokens_per_s = rate / (RETENTION_HEADS * RETENTION_LAYERS)
+    log(f"CPU oracle: {done} row-heads in {elapsed:.1f} s")
+    return {"value": round(tokens_per_s, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"the float64 recurrence on {done} (row, head) pairs of one layer (longest requests first, "
+                      f"{elapsed:.1f} s, one thread), scaled to {RETENTION_HEADS} heads x {RETENTION_LAYERS} layers"}
+
+
+def bench_retention(args):
+    """One self-decoder pass: RETENTION_LAYERS gated-retention layers in order,
+    each over the same rows with its own q, k, v, gates and state slots."""
+    import torch
+
+    from yoco_shared_kv_gather_amd import binding as yb
+    from yoco_shared_kv_gather_amd import bytes_model as bm
+    from yoco_shared_kv_gather_amd import profiling
+    from yoco_shared_kv_gather_amd import synth
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    yb.lib()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    H, D, L = RETENTION_HEADS, RETENTION_DIM, RETENTION_LAYERS
+    lens = synth.retention_lengths(args.retention, args.seed)
+    rows = int(lens.sum())
+    log(f"retention workload {args.retention}: {len(lens)} requests, {rows} rows, {L} layers x {H} heads x {D}")
+    layers = [synth.make_retention_inputs(lens, H, D, dev, seed=args.seed, tag=100 + l) for l in range(L)]
+    cu = torch.from_numpy(layers[0].cu_seqlens).to(dev)
+    idx = [torch.from_numpy(x.state_indices).to(dev) for x in layers]
+    outs = [torch.empty((rows, H, D), dtype=torch.float32, device=dev) for _ in range(L)]
+    max_seqlen = int(lens.max())
+    ws = torch.empty(max(16, yb.gated_retention_workspace_size(rows, len(lens), H, D, max_seqlen)), dtype=torch.uint8,
+                     device=dev)
+    host_layer = None
+    if not args.no_cpu_baseline:
+        x = layers[0]
+        host_layer = dict(lens=lens, cu=x.cu_seqlens, idx=x.state_indices, q=x.q.float().cpu().numpy(),
+                          k=x.k.float().cpu().numpy(), v=x.v.float().cpu().numpy(), g=x.gamma.cpu().numpy(),
+                          s=x.state.cpu().numpy())
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for l in range(L):
+            x = layers[l]
+            yb.gated_retention(x.q, x.k, x.v, x.gamma, cu, x.state, idx[l], max_seqlen=max_seqlen, out=outs[l],
+                               workspace=ws, stream=stream)
+
+    for _ in range(args.warmup):
+        if not args.no_flush:
+            flush.sum(dtype=torch.int64)
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps)")
+    ev = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        if not args.no_flush:
+            flush.sum(dtype=torch.int64)
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_per_step = float(step_ms.mean())
+    call_us = ms_per_step * 1e3 / L
+    log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (events), {call_us:.1f} us per layer")
+    layer_bytes = bm.retention_layer_bytes(lens, layers[0].state_indices, H, D)
+    layer_flops = bm.retention_layer_flops(lens, H, D)
+    achieved = layer_bytes / (call_us * 1e-6) / 1e9
+    # the schedule the library picks from max_seqlen: the recurrent kernel for
+    # decode batches, one chunkwise run per request up to 1024 rows, else a
+    # state pass over the segments of long requests and a full pass
+    if max_seqlen == 1:
+        kernels = [f"gated_retention_decode_kernel<{D}>"]
+    elif max_seqlen <= 1024:
+        kernels = [f"gated_retention_kernel<{D}, 0>"]
+    else:
+        kernels = [f"gated_retention_kernel<{D}, 1>", f"gated_retention_kernel<{D}, 2>"]
+    kernel = " + ".join(kernels)
+    variant = f"retention_{args.retention}"
+    measured = profiling.measured_traffic(f"gated_retention_{args.retention}", kernels)
+    traffic = profile_us = None
+    if measured is not None:
+        traffic = round(measured["read_bytes"] + measured["write_bytes"])
+        profile_us = round(measured["kernel_us"], 2)
+    result = {
+        "metric": METRIC,
+        "value": round(rows / (ms_per_step * 1e-3), 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 q/k/v, fp32 state and outputs",
+        "data": "synthetic",
+        "config": {
+            "workload": variant,
+            "num_reqs": int(len(lens)),
+            "rows": rows,
+            "longest_request_rows": int(lens.max()),
+            "num_layers": L,
+            "num_heads": H,
+            "head_dim": D,
+            "chunk_tokens": 32,
+            "segment_rows": 1024,
+            "max_seqlen": max_seqlen,
+            "llc_flushed_between_steps": not args.no_flush,
+            "parallelism": "single GPU",
+        },
+        "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
+        "mfma_tflops_recurrence": round(layer_flops / (call_us * 1e-6) / 1e12, 2),
+        "roofline": {
+            "kernel": f"yoco_gated_retention: {kernel}",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": layer_bytes,
+            "avg_launch_us": round(call_us, 2),
+            "profile_kernel_us": profile_us,
+        },
+    }
+    if host_layer is not None:
+        log("timing the CPU oracle baseline")
+        result["cpu_baseline"] = retention_cpu_baseline(host_layer, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -194,6 +362,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
               "(the hot path runs on a single MI355X).", file=sys.stderr)
         sys.exit(2)
+    if args.retention:
+        bench_retention(args)
+        return
 
     import torch
 
@@ -339,7 +510,7 @@ def main():
         merge_split *= 2
     merge_kernel = f"cross_attn_merge_kernel<{geom.head_dim}, {merge_split}>"
     variant = geom.name + (f"_q{Q}" if Q > 1 else "") + (f"_w{W}" if W > 0 else "") + ("_fp8" if args.fp8 else "")
-    measured = profiling.measured_traffic(variant, [attn_kernel, merge_kernel] if nparts > 1 else [attn_kernel])
+    measured = profiling.measured_traffic(f"cross_attn_{variant}", [attn_kernel, merge_kernel] if nparts > 1 else [attn_kernel])
     traffic = None
     profile_us = None
     if measured is not None:

@@ -417,32 +417,49 @@ int32_t yoco_cross_attn_varlen(int32_t dtype, const void* q, int32_t num_rows,
  *                  aligned.
  *   gamma          fp32 [num_tokens][num_heads], the gate of each token and
  *                  head, in [0, 1].  log2 gamma is clamped at -64 (a zero gate
- *                  weighs 2^-64).
+ *                  weighs 2^-64) on the chunkwise path.
  *   head_dim       64 or 128 (key and value head_dim alike; else
  *                  YOCO_ERR_UNSUPPORTED).
  *   cu_seqlens     int32 [num_reqs + 1]: request r owns rows
  *                  cu_seqlens[r] .. cu_seqlens[r+1]-1 (clamped to
  *                  [0, num_tokens]; a request with no rows leaves its slot
- *                  untouched).
+ *                  untouched).  Precondition: non-decreasing (with
+ *                  overlapping requests the segmented schedule computes
+ *                  nothing).
+ *   max_seqlen     an upper bound on any request's rows, or 0 if unknown.  It
+ *                  only chooses the schedule: 1 runs the recurrent form (one
+ *                  workgroup per request and head streaming its state), up to
+ *                  1024 one chunkwise run per request, above (or 0) splits
+ *                  long requests into 1024-row segments computed in parallel
+ *                  (needs a workspace).  A request longer than max_seqlen is
+ *                  still computed in full.
  *   state          fp32 [num_slots][num_heads][head_dim][head_dim] (key row,
- *                  value column), read and updated in place.
+ *                  value column), 16-byte aligned, read and updated in place.
  *   state_indices  int32 [num_reqs]: request r's slot.  A slot outside
  *                  [0, num_slots) starts from zeros and is not stored.
  *                  Requests with rows must name distinct slots (they run
  *                  concurrently).
  *   out            fp32 [num_tokens][num_heads][head_dim]: o_t of every row
  *                  owned by a request (other rows are not written).
+ *   workspace      device scratch of yoco_gated_retention_workspace_size()
+ *                  bytes, 16-byte aligned (may be NULL when that is 0); its
+ *                  contents need no initialisation.  Calls sharing a workspace
+ *                  must be ordered on one stream.
  *
- * Computed chunkwise in 32-token chunks on the matrix cores: bf16 q, k, v
- * exact, fp32 operands (state, decayed scores, gated keys) as two bf16 parts,
- * fp32 sums.  Errors: YOCO_ERR_INVALID_ARGUMENT (null pointers, negative
- * counts, misalignment), YOCO_ERR_UNSUPPORTED, YOCO_ERR_HIP.  num_reqs == 0
- * or num_tokens == 0 is a no-op.
+ * The chunkwise form runs in 32-token chunks on the matrix cores: bf16 q, k,
+ * v exact, fp32 operands (state, decayed scores, gated keys) as two bf16
+ * parts, fp32 sums; the recurrent form is fp32 throughout.  Errors:
+ * YOCO_ERR_INVALID_ARGUMENT (null pointers, negative counts, misalignment),
+ * YOCO_ERR_UNSUPPORTED, YOCO_ERR_WORKSPACE_TOO_SMALL, YOCO_ERR_HIP.
+ * num_reqs == 0 or num_tokens == 0 is a no-op.
  */
+int64_t yoco_gated_retention_workspace_size(int32_t num_tokens, int32_t num_reqs, int32_t num_heads,
+                                            int32_t head_dim, int32_t max_seqlen);
 int32_t yoco_gated_retention(int32_t dtype, const void* q, const void* k, const void* v, const float* gamma,
                              int32_t num_tokens, int32_t num_heads, int32_t head_dim,
-                             const int32_t* cu_seqlens, int32_t num_reqs, float* state, int32_t num_slots,
-                             const int32_t* state_indices, float* out, void* stream);
+                             const int32_t* cu_seqlens, int32_t num_reqs, int32_t max_seqlen, float* state,
+                             int32_t num_slots, const int32_t* state_indices, float* out, void* workspace,
+                             int64_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }  /* extern "C" */

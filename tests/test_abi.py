@@ -179,7 +179,8 @@ def test_gather_logits_rejects_before_launch(args, status):
 
 def _retention(**kw):
     args = dict(dtype=1, q=FAKE, k=FAKE, v=FAKE, gamma=FAKE, num_tokens=40, num_heads=4, head_dim=128, cu=FAKE,
-                num_reqs=2, state=FAKE, num_slots=4, slots=FAKE, out=FAKE, stream=None)
+                num_reqs=2, max_seqlen=0, state=FAKE, num_slots=4, slots=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30,
+                stream=None)
     args.update(kw)
     return yb.lib().yoco_gated_retention(*args.values())
 
@@ -198,6 +199,10 @@ def _retention(**kw):
     (dict(out=None), yb.YOCO_ERR_INVALID_ARGUMENT),
     (dict(q=FAKE + 8), yb.YOCO_ERR_INVALID_ARGUMENT),               # 16-byte alignment
     (dict(out=FAKE + 2), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(state=FAKE + 4), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(max_seqlen=-1), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(ws=None), yb.YOCO_ERR_WORKSPACE_TOO_SMALL),               # max_seqlen 0: segmented, needs a workspace
+    (dict(ws_bytes=1024), yb.YOCO_ERR_WORKSPACE_TOO_SMALL),
 ])
 def test_gated_retention_rejects_before_launch(kw, status):
     assert _retention(**kw) == status
@@ -208,3 +213,17 @@ def test_gated_retention_nothing_to_do():
     assert _retention(num_reqs=0) == yb.YOCO_OK
     assert _retention(num_heads=0) == yb.YOCO_OK
     assert _retention(num_tokens=0) == yb.YOCO_OK
+
+
+def test_gated_retention_workspace_follows_the_schedule():
+    # decode (max_seqlen 1) and one run per request (<= 1024 rows) need none;
+    # segments of 1024 rows need a state and a gate per (segment, head)
+    assert yb.gated_retention_workspace_size(5000, 8, 4, 128, 1) == 0
+    assert yb.gated_retention_workspace_size(5000, 8, 4, 128, 1024) == 0
+    segs = (8 + 5000 // 1024) * 4
+    rup = lambda x: -(-x // 256) * 256
+    assert yb.gated_retention_workspace_size(5000, 8, 4, 128, 0) == rup(segs * 128 * 128 * 4) + rup(segs * 4)
+    assert yb.gated_retention_workspace_size(5000, 8, 4, 128, 1025) == rup(segs * 128 * 128 * 4) + rup(segs * 4)
+    # more requests than a segmented launch schedules: one run per request
+    assert yb.gated_retention_workspace_size(5000, 4096, 4, 64, 0) == 0
+    assert yb.gated_retention_workspace_size(-1, 8, 4, 128, 0) == -1

@@ -56,23 +56,35 @@ def _close(name, got, ref, mag):
     assert np.all(err <= bound), name
 
 
-def _run(t, out=None):
+def _run(t, out=None, max_seqlen=0):
     if out is None:
         out = torch.full(t["q"].shape, float("nan"), dtype=torch.float32, device=t["q"].device)
-    yb.gated_retention(t["q"], t["k"], t["v"], t["gamma"], t["cu"], t["state"], t["idx"], out=out)
+    yb.gated_retention(t["q"], t["k"], t["v"], t["gamma"], t["cu"], t["state"], t["idx"], max_seqlen=max_seqlen,
+                       out=out)
     return out
 
 
+# max_seqlen picks the schedule: 1 the recurrent kernel, <= 1024 one chunkwise
+# run per request, 0 (unknown) 1024-row segments in two launches; every
+# schedule computes every request in full
+PLANS = {"recurrent": 1, "whole": 1024, "segmented": 0}
+SHORT = [1, 31, 32, 33, 0, 100, 7, 64, 200]
+LONG = [3000, 1024, 1025, 0, 2048, 5, 1, 2100]
+
+
+@pytest.mark.parametrize("plan", sorted(PLANS))
+@pytest.mark.parametrize("lens", [SHORT, LONG], ids=["short", "long"])
 @pytest.mark.parametrize("head_dim", [64, 128])
-def test_retention_matches_oracle(head_dim):
-    """Requests of 1, 31, 32, 33, 0, 100, 7, 64 and 200 rows (partial, whole
-    and several chunks), three heads, some requests starting from a zero
-    state (slot -1); all outputs and every slot checked."""
-    lens = [1, 31, 32, 33, 0, 100, 7, 64, 200]
-    say(f"retention: lens {lens}, 3 heads x {head_dim}")
-    inp = synth.make_retention_inputs(lens, 3, head_dim, zero_state_every=4)
+def test_retention_matches_oracle(head_dim, lens, plan):
+    """Requests of partial, whole and many chunks (short: up to 200 rows;
+    long: up to 3000 rows, so up to three segments), some starting from a
+    zero state (slot -1), on every schedule; all outputs and every slot
+    checked."""
+    heads = 3 if lens is SHORT else 2
+    say(f"retention: lens {lens}, {heads} heads x {head_dim}, plan {plan}")
+    inp = synth.make_retention_inputs(lens, heads, head_dim, zero_state_every=4)
     t = _to_dev(inp)
-    out = _run(t)
+    out = _run(t, max_seqlen=PLANS[plan])
     torch.cuda.synchronize()
     (ref, new_state), (mag, mag_state) = _oracle_pair(inp)
     _close("outputs", host(out), ref, mag)
@@ -84,15 +96,17 @@ def test_retention_matches_oracle(head_dim):
             assert torch.equal(t["state"][s].cpu().view(torch.int32), inp.state[s].view(torch.int32)), s
 
 
+@pytest.mark.parametrize("plan", sorted(PLANS))
 @pytest.mark.parametrize("gamma_value", [0.0, 1.0])
-def test_retention_gate_edges(gamma_value):
-    """gamma = 1 (no forgetting, the state sums every k^T v over 300 rows)
-    and gamma = 0 (only the current token: o_t = (q_t . k_t) v_t)."""
-    say(f"retention: gamma = {gamma_value}")
-    inp = synth.make_retention_inputs([300, 5, 1], 2, 128)
+def test_retention_gate_edges(gamma_value, plan):
+    """gamma = 1 (no forgetting, the state sums every k^T v over 1300 rows,
+    two segments) and gamma = 0 (only the current token: o_t = (q_t . k_t)
+    v_t), on every schedule."""
+    say(f"retention: gamma = {gamma_value}, plan {plan}")
+    inp = synth.make_retention_inputs([1300, 5, 1], 2, 128)
     inp.gamma.fill_(gamma_value)
     t = _to_dev(inp)
-    out = _run(t)
+    out = _run(t, max_seqlen=PLANS[plan])
     torch.cuda.synchronize()
     (ref, new_state), (mag, mag_state) = _oracle_pair(inp)
     _close("outputs", host(out), ref, mag)
@@ -104,9 +118,11 @@ def test_retention_gate_edges(gamma_value):
 
 
 def test_retention_split_calls_carry_the_state():
-    """A prefill in two calls (the state carried in the slots) and then five
-    one-token decode steps give the single oracle run's outputs and state."""
-    lens = np.array([40, 70, 1, 33, 96], dtype=np.int64)
+    """A prefill in two calls (the state carried in the slots; the longest
+    request two segments in the first call) and then five one-token decode
+    steps on the recurrent kernel give the single oracle run's outputs and
+    state."""
+    lens = np.array([40, 70, 1, 33, 3300], dtype=np.int64)
     steps = 5
     total = lens + steps
     say(f"retention: prefill {list(lens)} in two calls, then {steps} decode steps")
@@ -118,35 +134,36 @@ def test_retention_split_calls_carry_the_state():
     idx = torch.from_numpy(inp.state_indices).to(d)
     q, k, v, g = (x.to(d) for x in (inp.q, inp.k, inp.v, inp.gamma))
 
-    def call(row_lists):
+    def call(row_lists, max_seqlen):
         rows = np.concatenate(row_lists).astype(np.int64)
         c = np.zeros(len(row_lists) + 1, dtype=np.int32)
         c[1:] = np.cumsum([len(r) for r in row_lists])
         ri = torch.from_numpy(rows).to(d)
         o = torch.full((len(rows),) + tuple(q.shape[1:]), float("nan"), dtype=torch.float32, device=d)
         yb.gated_retention(q[ri].contiguous(), k[ri].contiguous(), v[ri].contiguous(), g[ri].contiguous(),
-                           torch.from_numpy(c).to(d), state, idx, out=o)
+                           torch.from_numpy(c).to(d), state, idx, max_seqlen=max_seqlen, out=o)
         return rows, o
 
     got = np.full(ref.shape, np.nan)
     first = lens // 3
     for part in ([np.arange(cu[r], cu[r] + first[r]) for r in range(len(lens))],
                  [np.arange(cu[r] + first[r], cu[r] + lens[r]) for r in range(len(lens))]):
-        rows, o = call(part)
+        rows, o = call(part, 0)
         got[rows] = host(o)
     for step in range(steps):
-        rows, o = call([np.array([cu[r] + lens[r] + step]) for r in range(len(lens))])
+        rows, o = call([np.array([cu[r] + lens[r] + step]) for r in range(len(lens))], 1)
         got[rows] = host(o)
     torch.cuda.synchronize()
     _close("outputs", got, ref, mag)
     _close("states", host(state), new_state, mag_state)
 
 
-def test_retention_is_deterministic_and_writes_only_owned_rows():
+@pytest.mark.parametrize("plan", sorted(PLANS))
+def test_retention_is_deterministic_and_writes_only_owned_rows(plan):
     """Two calls on the same inputs give the same bits; rows that no request
     owns keep their contents, and empty requests leave their slots alone."""
-    say("retention: determinism, unowned rows")
-    inp = synth.make_retention_inputs([50, 0, 17, 0, 90], 2, 128)
+    say(f"retention: determinism, unowned rows, plan {plan}")
+    inp = synth.make_retention_inputs([50, 0, 17, 0, 2090], 2, 128)
     t = _to_dev(inp)
     # rows past the last request: graph padding
     pad = 9
@@ -155,10 +172,10 @@ def test_retention_is_deterministic_and_writes_only_owned_rows():
         t[name] = torch.cat([t[name], torch.randn((pad,) + tuple(t[name].shape[1:]), device=d).to(t[name].dtype)])
     t["gamma"] = torch.cat([t["gamma"], torch.rand((pad, t["gamma"].shape[1]), device=d)])
     s0 = t["state"].clone()
-    out1 = _run(t)
+    out1 = _run(t, max_seqlen=PLANS[plan])
     s1 = t["state"].clone()
     t["state"].copy_(s0)
-    out2 = _run(t)
+    out2 = _run(t, max_seqlen=PLANS[plan])
     torch.cuda.synchronize()
     assert torch.equal(out1[:-pad].view(torch.int32), out2[:-pad].view(torch.int32))
     assert torch.equal(s1.view(torch.int32), t["state"].view(torch.int32))
@@ -171,8 +188,9 @@ def test_retention_is_deterministic_and_writes_only_owned_rows():
 
 def test_retention_full_size_sampled():
     """The mixed step's request mix (16 prefills of 512..16384 rows, 32
-    one-token decodes), 24 heads x 128, in one call: the longest prefill, a
-    short one and a decode, two heads each, against the oracle."""
+    one-token decodes), 24 heads x 128, in one segmented call as the
+    benchmark runs it: the longest prefill, a short one and a decode, two
+    heads each, against the oracle."""
     lens = synth.retention_lengths("mixed48")
     say(f"retention: full mixed48 mix, {int(lens.sum())} rows, 24 heads x 128")
     inp = synth.make_retention_inputs(lens, 24, 128, device=dev())
@@ -180,7 +198,7 @@ def test_retention_full_size_sampled():
     t = dict(q=inp.q, k=inp.k, v=inp.v, gamma=inp.gamma, cu=torch.from_numpy(inp.cu_seqlens).to(dev()),
              idx=torch.from_numpy(inp.state_indices).to(dev()), state=inp.state)
     out = torch.empty(inp.q.shape, dtype=torch.float32, device=dev())
-    _run(t, out)
+    _run(t, out, max_seqlen=int(lens.max()))
     torch.cuda.synchronize()
     order = np.argsort(lens)
     picks = [int(order[-1]), int(next(i for i in order if lens[i] > 1)), int(order[0])]
@@ -197,3 +215,17 @@ def test_retention_full_size_sampled():
             mag, mst = oracle.gated_retention(np.abs(q), np.abs(k), np.abs(v), g, cu1, np.abs(s0), np.array([0]))
             _close(f"request {r} ({b - a} rows) head {h} outputs", host(out[a:b, h:h + 1]), ref, mag)
             _close(f"request {r} head {h} state", host(t["state"][slot:slot + 1, h:h + 1]), st, mst)
+
+
+def test_retention_decode_batch_full_size():
+    """64 one-token decodes, 24 heads x 128, on the recurrent kernel as the
+    benchmark runs it; every output and state against the oracle."""
+    lens = synth.retention_lengths("decode64")
+    say("retention: decode64, 24 heads x 128, recurrent kernel")
+    inp = synth.make_retention_inputs(lens, 24, 128)
+    t = _to_dev(inp)
+    out = _run(t, max_seqlen=1)
+    torch.cuda.synchronize()
+    (ref, new_state), (mag, mag_state) = _oracle_pair(inp)
+    _close("outputs", host(out), ref, mag)
+    _close("states", host(t["state"]), new_state, mag_state)

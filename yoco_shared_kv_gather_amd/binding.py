@@ -58,7 +58,9 @@ SIGNATURES = {
     "yoco_cross_attn_varlen_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "yoco_cross_attn_varlen": (_i32, [_i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                       _i32, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _u32, _vp, _vp, _i64, _vp]),
-    "yoco_gated_retention": (_i32, [_i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _vp, _vp, _vp]),
+    "yoco_gated_retention_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32]),
+    "yoco_gated_retention": (_i32, [_i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _vp,
+                                    _vp, _i64, _vp]),
 }
 
 _lock = threading.Lock()
@@ -347,12 +349,18 @@ def cross_attn_varlen(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, q
 
 # ---- yoco_gated_retention -------------------------------------------------------
 
-def gated_retention(q, k, v, gamma, cu_seqlens, state, state_indices, out=None, stream=None):
-    """Self-decoder gated retention over each request's rows, chunkwise:
+def gated_retention_workspace_size(num_tokens, num_reqs, num_heads, head_dim, max_seqlen=0) -> int:
+    return int(lib().yoco_gated_retention_workspace_size(num_tokens, num_reqs, num_heads, head_dim, max_seqlen))
+
+
+def gated_retention(q, k, v, gamma, cu_seqlens, state, state_indices, max_seqlen=0, out=None, workspace=None,
+                    stream=None):
+    """Self-decoder gated retention over each request's rows:
     S_t = gamma_t S_{t-1} + k_t^T v_t, o_t = q_t S_t per head, from and back
     to the request's state slot.  q, k, v: bf16 [T][H][D]; gamma: fp32 [T][H];
-    state: fp32 [slots][H][D][D] (updated in place); returns out fp32
-    [T][H][D] (rows of no request are left as allocated)."""
+    state: fp32 [slots][H][D][D] (updated in place); max_seqlen: a bound on
+    any request's rows (0 = unknown), which only picks the schedule.  Returns
+    out fp32 [T][H][D] (rows of no request are left as allocated)."""
     torch = _torch()
     num_tokens, num_heads, head_dim = q.shape
     if out is None:
@@ -363,13 +371,19 @@ def gated_retention(q, k, v, gamma, cu_seqlens, state, state_indices, out=None, 
         raise ValueError("q, k, v must share [T][H][D] and gamma must be [T][H]")
     if state.dim() != 4 or tuple(state.shape[1:]) != (num_heads, head_dim, head_dim):
         raise ValueError("state must be [slots][H][D][D]")
-    if state_indices.numel() != cu_seqlens.shape[0] - 1:
+    num_reqs = cu_seqlens.shape[0] - 1
+    if state_indices.numel() != num_reqs:
         raise ValueError("state_indices needs one slot per request")
+    need = gated_retention_workspace_size(num_tokens, num_reqs, num_heads, head_dim, max_seqlen)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     num_slots = state.shape[0]
     _check(lib().yoco_gated_retention(_dtype_code(q), _dev(q, "q"), _dev(k, "k"), _dev(v, "v"), _dev(gamma, "gamma"),
-                                      num_tokens, num_heads, head_dim, _i32_dev(cu_seqlens, "cu_seqlens"),
-                                      cu_seqlens.shape[0] - 1, _dev(state, "state") if num_slots > 0 else None,
-                                      num_slots, _i32_dev(state_indices, "state_indices"), _dev(out, "out"),
+                                      num_tokens, num_heads, head_dim, _i32_dev(cu_seqlens, "cu_seqlens"), num_reqs,
+                                      max_seqlen, _dev(state, "state") if num_slots > 0 else None, num_slots,
+                                      _i32_dev(state_indices, "state_indices"), _dev(out, "out"),
+                                      _dev(workspace, "workspace") if workspace is not None else None,
+                                      workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                       _stream_handle(stream)))
     return out
 

@@ -69,3 +69,24 @@ def append_flops(num_tokens: int, hidden: int, num_kv_heads: int, head_dim: int)
 
 def gather_bytes(num_reqs: int, row_bytes: int) -> int:
     return 2 * num_reqs * row_bytes + 4 * (num_reqs + 1) + 4 * num_reqs
+
+
+def retention_layer_bytes(lens, state_slots, num_heads: int, head_dim: int, qkv_bytes: int = 2) -> int:
+    """One gated-retention layer over a batch: every row's q, k, v, gate (fp32)
+    and output (fp32) once, and the fp32 [D][D] state of each head read and
+    written once for every request that has rows and a state slot
+    ("YOCO_论文与推理数据流详解" §18.1: the fixed-size self-decoder state is
+    read and written back at every token step); plus the int32 offsets and
+    slot numbers."""
+    lens = np.asarray(lens, dtype=np.int64)
+    slots = np.asarray(state_slots, dtype=np.int64)
+    rows = int(lens.sum())
+    per_row = num_heads * (3 * head_dim * qkv_bytes + 4 + 4 * head_dim)
+    stateful = int(((lens > 0) & (slots >= 0)).sum())
+    return rows * per_row + stateful * num_heads * 2 * head_dim * head_dim * 4 + 4 * (2 * len(lens) + 1)
+
+
+def retention_layer_flops(lens, num_heads: int, head_dim: int) -> int:
+    """The recurrence's own multiply-adds, 2 flops each: per row and head,
+    gamma S + k^T v (D^2) and q S (D^2)."""
+    return int(np.asarray(lens, dtype=np.int64).sum()) * num_heads * 4 * head_dim * head_dim

@@ -103,7 +103,7 @@ def summarize(out: str, workload: str, command: str, top: int = 10) -> str:
         "```",
         "",
         f"bench.py line of the traced run: ms_per_step {bench['ms_per_step']}, value {bench['value']} {bench['unit']}, "
-        f"roofline achieved {bench['roofline']['achieved']} GB/s (event-timed)",
+        f"roofline achieved {bench['roofline']['achieved']} {bench['roofline']['unit']} (event-timed)",
         "",
         "| kernel | calls | avg us | HBM read MB/dispatch | HBM write MB/dispatch |",
         "|---|---:|---:|---:|---:|",
@@ -128,11 +128,11 @@ def summarize(out: str, workload: str, command: str, top: int = 10) -> str:
     return "\n".join(lines) + "\n"
 
 
-def measured_traffic(workload: str, kernels: List[str]) -> Optional[dict]:
+def measured_traffic(stem: str, kernels: List[str]) -> Optional[dict]:
     """HBM bytes per dispatch and average kernel time summed over `kernels`,
-    from the committed profile of `workload` -- or None if there is none or
-    the sources changed since."""
-    path = os.path.join(PROFILES, f"cross_attn_{workload}.md")
+    from the committed profile profiles/<stem>.md -- or None if there is none
+    or the sources changed since."""
+    path = os.path.join(PROFILES, f"{stem}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
