@@ -4,8 +4,8 @@ The summary is what profiles/*.md hold: per-kernel average durations from a
 kernel trace, and HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE counter
 passes, each scaled by what the same counter reads for a plain device copy of
 known size (bench.py --copy-calibration).  It also records a hash of the HIP
-sources, so bench.py can tell whether the measured traffic still describes the
-kernels it runs.
+sources behind the profiled kernels, so bench.py can tell whether the measured
+traffic still describes the kernels it runs.
 
 Expected layout of the rocprofv3 output directory (one `-d` per pass, `-o run`
 and `-f csv`):
@@ -16,7 +16,7 @@ and `-f csv`):
     copy_write/  --pmc WRITE_SIZE                 (bench.py --copy-calibration MIB)
 plus copy_fetch.json, the calibration run's stdout.
 
-Usage: python -m yoco_shared_kv_gather_amd.profiling OUTDIR --workload NAME --command "..." > profiles/X.md
+Usage: python -m yoco_shared_kv_gather_amd.profiling OUTDIR --workload NAME --stem X --command "..." > profiles/X.md
 """
 
 from __future__ import annotations
@@ -38,11 +38,29 @@ ROOT = os.path.dirname(PKG_DIR)
 PROFILES = os.path.join(ROOT, "profiles")
 
 
-def source_hash() -> str:
-    """sha256 over the HIP sources and the public header, in name order."""
+# the sources a profile's kernels are built from, by profile name prefix
+FAMILIES = {
+    "cross_attn_": ["cross_attn*", "kv_append.hip", "gather_last.hip", "yoco_internal.h"],
+    "gated_retention_": ["retention.hip", "yoco_internal.h"],
+}
+
+
+def family_sources(stem: Optional[str]) -> List[str]:
+    """The HIP sources behind the kernels of profile `stem` (every source when
+    the stem names no family), plus the public header."""
+    patterns = ["*"]
+    for prefix, pats in FAMILIES.items():
+        if stem is not None and stem.startswith(prefix):
+            patterns = pats
+    files = sorted({f for pat in patterns for f in glob.glob(os.path.join(CSRC, pat))})
+    return files + [os.path.join(ROOT, "include", "yoco.h")]
+
+
+def source_hash(stem: Optional[str] = None) -> str:
+    """sha256 over the sources of profile `stem`'s kernels and the public
+    header, in name order (all sources without a stem)."""
     h = hashlib.sha256()
-    files = sorted(glob.glob(os.path.join(CSRC, "*"))) + [os.path.join(ROOT, "include", "yoco.h")]
-    for path in files:
+    for path in family_sources(stem):
         h.update(os.path.basename(path).encode())
         with open(path, "rb") as f:
             h.update(f.read())
@@ -81,7 +99,7 @@ def _calibration(out: str, sub: str) -> float:
     return copy_bytes / best
 
 
-def summarize(out: str, workload: str, command: str, top: int = 10) -> str:
+def summarize(out: str, workload: str, command: str, top: int = 10, stem: Optional[str] = None) -> str:
     stats = list(csv.DictReader(open(os.path.join(out, "trace", "run_kernel_stats.csv"))))
     fetch = _counters(os.path.join(out, "fetch", "run_counter_collection.csv"))
     write = _counters(os.path.join(out, "write", "run_counter_collection.csv"))
@@ -91,7 +109,8 @@ def summarize(out: str, workload: str, command: str, top: int = 10) -> str:
     lines = [
         f"# rocprofv3 summary: {workload}",
         "",
-        f"source_hash: {source_hash()}",
+        f"source_hash: {source_hash(stem)}",
+        f"sources: {', '.join(os.path.relpath(f, ROOT) for f in family_sources(stem))}",
         f"workload: {workload}",
         f"counter_scale_fetch_bytes_per_unit: {f_scale:.4f}",
         f"counter_scale_write_bytes_per_unit: {w_scale:.4f}",
@@ -110,7 +129,8 @@ def summarize(out: str, workload: str, command: str, top: int = 10) -> str:
     ]
     records = {}
     ours = [row for row in stats
-            if not short_name(row["Name"]).startswith(("at::", "__amd", "c10::", "rocprim::", "hipcub::"))]
+            if not short_name(row["Name"]).startswith(("at::", "__amd", "c10::", "rocprim::", "hipcub::"))
+            and "at::native" not in row["Name"]]
     lines.insert(len(lines) - 3, "Kernels of this library only (input generation and cache flushing omitted).")
     lines.insert(len(lines) - 3, "")
     for row in ours[:top]:
@@ -137,7 +157,7 @@ def measured_traffic(stem: str, kernels: List[str]) -> Optional[dict]:
         return None
     text = open(path).read()
     m = re.search(r"^source_hash: (\S+)", text, re.M)
-    if not m or m.group(1) != source_hash():
+    if not m or m.group(1) != source_hash(stem):
         return None
     total_r = total_w = total_us = 0.0
     found = 0
@@ -160,8 +180,9 @@ def main():
     p.add_argument("out")
     p.add_argument("--workload", required=True)
     p.add_argument("--command", required=True, help="the commands that produced OUT (recorded in the summary)")
+    p.add_argument("--stem", default=None, help="profile file name without .md (picks the sources hashed)")
     args = p.parse_args()
-    print(summarize(args.out, args.workload, args.command), end="")
+    print(summarize(args.out, args.workload, args.command, stem=args.stem), end="")
 
 
 if __name__ == "__main__":
