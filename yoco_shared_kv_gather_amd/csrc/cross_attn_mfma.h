@@ -16,8 +16,9 @@
 //       running max of a query is shared by its four lanes (two shuffles).
 //   O^T[D][16 q] += V^T[D][16 keys] . P^T[16 keys][16 q]
 //       v_mfma_f32_16x16x16_bf16; V goes through a per-wavefront LDS tile
-//       (written row-major, read as the transposed A operand with 16-bit
-//       reads), P^T is exactly the lane's own softmax weights.  P is split
+//       (written row-major, read as the transposed A operand with one
+//       ds_read_b64_tr_b16 per operand), P^T is exactly the lane's own
+//       softmax weights.  P is split
 //       into bf16 high and low parts (two products), so the weights keep ~17
 //       bits; K, V (bf16 or widened FP8) and q are exact bf16 values, and all
 //       sums are fp32.  Each lane's O^T column belongs to its own query, so
@@ -49,7 +50,9 @@ struct MfmaLayout {
   static constexpr int kKL = kT == kFP8 ? D / 64 : D / 32;             // 16-byte K loads per tile per lane
   static constexpr int kVC = kNK * kRowBytes / 16 / 64;                // 16-byte V chunks per lane per iteration
   static constexpr int kChunksPerRow = kRowBytes / 16;
-  static constexpr int kVStride = D + 4;                               // bf16 elements per LDS row of a V tile
+  // bf16 elements per LDS row of a V tile: the row stride is 8 banks mod 32,
+  // so the four rows of one transposed read hit disjoint banks
+  static constexpr int kVStride = D + 16;
   static_assert(kVC >= 1 && kNK * kRowBytes % (16 * 64) == 0, "V tile split");
 };
 
@@ -379,11 +382,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
     for (int t = 0; t < kNT; ++t) {
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) {
-        const int d = 16 * dt + l16;
-        const int k0 = 16 * t + 4 * gi;
-        uint32_t w0 = static_cast<uint32_t>(vt[k0][d]) | (static_cast<uint32_t>(vt[k0 + 1][d]) << 16);
-        uint32_t w1 = static_cast<uint32_t>(vt[k0 + 2][d]) | (static_cast<uint32_t>(vt[k0 + 3][d]) << 16);
-        const mfma_bf16x4 va = __builtin_bit_cast(mfma_bf16x4, make_uint2(w0, w1));
+        // A operand: lane (d = 16dt + l16, keys 16t + 4gi + 0..3).  The
+        // transposed LDS read gives lane i of a 16-lane group element i % 4
+        // of the 8 bytes that lane 4j + i/4 addressed, in slot j; so lane
+        // l16 addresses key 16t + 4gi + l16/4, elements 16dt + 4(l16 % 4)..+3.
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const v4s raw = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (v4s __attribute__((address_space(3)))*)(&vt[16 * t + 4 * gi + (l16 >> 2)][16 * dt + 4 * (l16 & 3)]));
+        const mfma_bf16x4 va = __builtin_bit_cast(mfma_bf16x4, raw);
         oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, p_hi[t], oacc[dt], 0, 0, 0);
         oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, p_lo[t], oacc[dt], 0, 0, 0);
       }
