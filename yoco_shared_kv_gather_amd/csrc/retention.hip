@@ -28,9 +28,11 @@
 // (S_in(j) = G_{j-1} S_in(j-1) + dS_{j-1}, the recurrence being linear in the
 // state) and produces the outputs, the last segment the final state.  Per
 // chunk:
-//   stage    Q, K, V rows (bf16) in LDS row-major; K~^T = (w_s k_s)^T split
-//            into bf16 high and low parts and V^T transposed from there; the
-//            per-token decay terms from one wavefront's prefix sum;
+//   stage    Q, K, V rows (bf16) in LDS row-major, and K~ = w_s k_s split
+//            into bf16 high and low parts, row-major too: the MFMA operands
+//            that need them transposed (V^T, K~^T) come from transposed LDS
+//            reads (ds_read_b64_tr_b16); the per-token decay terms are
+//            computed a chunk ahead by one wavefront's prefix sum;
 //   A = QK^T three 16x16 causal tiles (v_mfma_f32_16x16x32_bf16), each
 //            scaled by 2^{b_t - b_s}, stored as bf16 high + low parts;
 //   O        Q S (the state split into bf16 high + low in registers), rows
@@ -59,6 +61,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kC = 32;                  // tokens per chunk
 constexpr int kRowPad = 8;              // bf16 elements of padding per LDS row
+constexpr int kTrPad = 16;              // padding of the tiles read transposed
 constexpr float kMinLog2Gate = -64.0f;
 constexpr float kMinLazyScale = 0x1p-60f;   // smallest state scale kept apart from the state
 constexpr int kSegRows = 1024;          // rows per segment of a long request (a multiple of kC)
@@ -88,9 +91,8 @@ struct RetArgs {
 
 template <int D>
 struct RowTiles {
-  uint16_t q[kC][D + kRowPad];          // row-major chunk rows
+  uint16_t q[kC][D + kRowPad];          // row-major chunk rows (read by rows)
   uint16_t k[kC][D + kRowPad];
-  uint16_t v[kC][D + kRowPad];
 };
 
 template <int D>
@@ -99,9 +101,11 @@ struct __attribute__((aligned(16))) RetSmem {
     RowTiles<D> r;
     int32_t pref[kMaxSegReqs + 1];      // segment schedule, before the first chunk
   } u;
-  uint16_t kth[D][kC + kRowPad];        // (w_s k_s)^T, bf16 high part
-  uint16_t ktl[D][kC + kRowPad];        // low part
-  uint16_t vt[D][kC + kRowPad];         // V^T
+  // row-major tiles read through transposed LDS reads; a row stride of 8
+  // banks mod 32 keeps the four rows of one read on disjoint banks
+  uint16_t v[kC][D + kTrPad];           // V
+  uint16_t kh[kC][D + kTrPad];          // K~ = w_s k_s (over the state scale), bf16 high part
+  uint16_t kl[kC][D + kTrPad];          // low part
   uint16_t ah[kC][kC + kRowPad];        // decayed causal Q K^T, high part
   uint16_t al[kC][kC + kRowPad];        // low part
   float b[2][kC];                       // inclusive prefix of log2 gamma (by chunk parity)
@@ -118,6 +122,23 @@ __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(static_cast<uint32_t>(h) << 16); }
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// MFMA operand for k-slots 8gi .. 8gi+7 = rows r0 + 8gi + 0..7 of a row-major
+// bf16 tile, for lane l16 of each 16-lane group: column c0 + l16.  Two
+// transposed reads (ds_read_b64_tr_b16): in each 16-lane group lane i's slot
+// j is element i % 4 of the 8 bytes lane 4j + i/4 addressed, so lane m
+// addresses row r0 + 8gi + 4h + m/4, columns c0 + 4(m % 4) .. +3.
+template <int kStride>
+__device__ __forceinline__ bf16x8 tr_operand(const uint16_t* tile, int r0, int c0, int gi, int l16) {
+  const uint16_t* p0 = tile + (r0 + 8 * gi + (l16 >> 2)) * kStride + c0 + 4 * (l16 & 3);
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3)))*)(p0));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3)))*)(p0 + 4 * kStride));
+  const uint2 a = __builtin_bit_cast(uint2, lo);
+  const uint2 b = __builtin_bit_cast(uint2, hi);
+  return __builtin_bit_cast(bf16x8, make_uint4(a.x, a.y, b.x, b.y));
+}
 
 // Two values at once: hi = the nearest bf16 pair (packed, x0 in the low
 // half), lo = the bf16 pair nearest to the remainders x - hi.
@@ -190,9 +211,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int kKS = D / 32;                 // MFMA k-steps over head_dim
   constexpr int kRowChunks = D / 8;           // 16-byte chunks per row
   constexpr int kLoads = kC * kRowChunks / kThreads;   // row chunks per thread per matrix
-  constexpr int kTasks = D * (kC / 8) / kThreads;      // transpose tasks per thread
   static_assert(kLoads >= 1 && kC * kRowChunks % kThreads == 0, "row staging split");
-  static_assert(kTasks >= 1 && D * (kC / 8) % kThreads == 0, "transpose split");
   static_assert(sizeof(RowTiles<D>) >= sizeof(int32_t) * (kMaxSegReqs + 1), "schedule fits the row tiles");
   static_assert(kSegRows % kC == 0, "segments hold whole chunks");
   using Smem = RetSmem<D>;
@@ -362,23 +381,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   float gseg = 1.0f;                          // product of the chunks' total decays
   float scale = 1.0f;                         // the state is scale * sacc
   load_chunk(start);
+  __syncthreads();                            // the first chunk's decay terms
   int buf = 0;
   for (int pos = start; pos < end; pos += kC, buf ^= 1) {
     const int n = min(kC, end - pos);
-    // ---- stage the rows; decay terms from wavefront 0
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int c = tid + kThreads * i;
-      const int s = c / kRowChunks;
-      const int cc = c - s * kRowChunks;
-      if constexpr (kOut) *reinterpret_cast<uint4*>(&sm.u.r.q[s][8 * cc]) = rq[i];
-      *reinterpret_cast<uint4*>(&sm.u.r.k[s][8 * cc]) = rk[i];
-      *reinterpret_cast<uint4*>(&sm.u.r.v[s][8 * cc]) = rv[i];
-    }
-    // the next chunk's rows travel while this one is computed
-    if (pos + kC < end) load_chunk(pos + kC);
-    __syncthreads();
-
     // ---- the state's decay this chunk.  The registers hold S / scale: while
     // scale * 2^{b_{n-1}} stays above 2^-60 only the scale takes the decay
     // and the new keys are weighted by 1 / (scale 2^{b_{n-1}}) instead, which
@@ -389,26 +395,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const bool lazy = cg >= kMinLazyScale;
     const float wscale = lazy ? 1.0f / cg : 1.0f;
 
-    // ---- transposed operands: K~^T (high, low) and V^T; task c = tid + 256 i
-    // is key/value row c % D, tokens 8 (c / D) .. +7
+    // ---- stage the rows: q and k (read by rows), v, and K~ = (w_s / ...) k
+    // split into bf16 high and low parts, all row-major
 #pragma unroll
-    for (int i = 0; i < kTasks; ++i) {
+    for (int i = 0; i < kLoads; ++i) {
       const int c = tid + kThreads * i;
-      const int d = c % D;
-      const int s0 = 8 * (c / D);
-      uint32_t hi[4], lo[4], vw[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float x0 = (sm.w[buf][s0 + 2 * jj] * wscale) * bf16_to_f32(sm.u.r.k[s0 + 2 * jj][d]);
-        const float x1 = (sm.w[buf][s0 + 2 * jj + 1] * wscale) * bf16_to_f32(sm.u.r.k[s0 + 2 * jj + 1][d]);
-        split2(x0, x1, hi[jj], lo[jj]);
-        vw[jj] = static_cast<uint32_t>(sm.u.r.v[s0 + 2 * jj][d]) |
-                 (static_cast<uint32_t>(sm.u.r.v[s0 + 2 * jj + 1][d]) << 16);
+      const int s = c / kRowChunks;
+      const int cc = c - s * kRowChunks;
+      if constexpr (kOut) {
+        *reinterpret_cast<uint4*>(&sm.u.r.q[s][8 * cc]) = rq[i];
+        *reinterpret_cast<uint4*>(&sm.u.r.k[s][8 * cc]) = rk[i];
       }
-      *reinterpret_cast<uint4*>(&sm.kth[d][s0]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-      *reinterpret_cast<uint4*>(&sm.ktl[d][s0]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-      *reinterpret_cast<uint4*>(&sm.vt[d][s0]) = make_uint4(vw[0], vw[1], vw[2], vw[3]);
+      *reinterpret_cast<uint4*>(&sm.v[s][8 * cc]) = rv[i];
+      const float ws = sm.w[buf][s] * wscale;
+      const uint32_t kw[4] = {rk[i].x, rk[i].y, rk[i].z, rk[i].w};
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        split2(ws * yoco::bf16_lo(kw[jj]), ws * yoco::bf16_hi(kw[jj]), hi[jj], lo[jj]);
+      *reinterpret_cast<uint4*>(&sm.kh[s][8 * cc]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+      *reinterpret_cast<uint4*>(&sm.kl[s][8 * cc]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
     }
+    // the next chunk's rows travel while this one is computed
+    if (pos + kC < end) load_chunk(pos + kC);
+    __syncthreads();
     // ---- the next chunk's decay terms (and the gates after it)
     if (wave == kWaves - 1 && pos + kC < end) {
       decay_terms(pos + kC, buf ^ 1);
@@ -441,7 +451,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
     bf16x8 vb[kCT];
 #pragma unroll
-    for (int ct = 0; ct < kCT; ++ct) vb[ct] = *reinterpret_cast<const bf16x8*>(&sm.vt[cw + 16 * ct + l16][8 * gi]);
+    for (int ct = 0; ct < kCT; ++ct) vb[ct] = tr_operand<D + kTrPad>(&sm.v[0][0], 0, cw + 16 * ct, gi, l16);
     if constexpr (kOut) {
       // ---- O = diag(2^b) Q S + A V over this wavefront's columns
       f32x4 oacc[2][kCT];
@@ -519,8 +529,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt) {
-      const bf16x8 kh = *reinterpret_cast<const bf16x8*>(&sm.kth[16 * dt + l16][8 * gi]);
-      const bf16x8 kl = *reinterpret_cast<const bf16x8*>(&sm.ktl[16 * dt + l16][8 * gi]);
+      const bf16x8 kh = tr_operand<D + kTrPad>(&sm.kh[0][0], 0, 16 * dt, gi, l16);
+      const bf16x8 kl = tr_operand<D + kTrPad>(&sm.kl[0][0], 0, 16 * dt, gi, l16);
 #pragma unroll
       for (int ct = 0; ct < kCT; ++ct) {
         sacc[dt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, vb[ct], sacc[dt][ct], 0, 0, 0);
