@@ -291,7 +291,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
       const int chunk = lane + 64 * c;
       const int key = chunk / ML::kChunksPerRow;
       const int e0 = (chunk - key * ML::kChunksPerRow) * (16 / kEb);  // first element of the chunk
-      const uint4 vc = (rs.vmask >> c & 1u) ? rs.v[c] : make_uint4(0u, 0u, 0u, 0u);
+      // masked rows become zero by an AND (a select here compiles to a branch
+      // and register copies)
+      const uint32_t keep = 0u - ((rs.vmask >> c) & 1u);
+      const uint4 vc = make_uint4(rs.v[c].x & keep, rs.v[c].y & keep, rs.v[c].z & keep, rs.v[c].w & keep);
       if constexpr (kF8) {
         uint4 lo8, hi8;
         fp8_to_bf16(vc, lo8, hi8);
@@ -444,17 +447,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
       for (int dt = 0; dt < kDT; ++dt) oacc[dt] = mfma_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       const int base0 = cur.start & ~15;           // iterations start 16-aligned
       const int num_iters = (cur.end - base0 + kNK - 1) / kNK;
+      // The next iteration's rows are always requested, also past the item's
+      // end (load_rows then reads the item's first rows and masks them), so
+      // neither register set is written conditionally: a conditional load
+      // made the compiler copy whole register sets around the loop.
       Rows ra, rb;
       int it = wave_u;
-      if (it < num_iters) load_rows(ra, cur, base0 + it * kNK);
-      while (it < num_iters) {
-        if (it + kWaves < num_iters) load_rows(rb, cur, base0 + (it + kWaves) * kNK);
-        compute(ra);
-        it += kWaves;
-        if (it >= num_iters) break;
-        if (it + kWaves < num_iters) load_rows(ra, cur, base0 + (it + kWaves) * kNK);
-        compute(rb);
-        it += kWaves;
+      if (it < num_iters) {
+        load_rows(ra, cur, base0 + it * kNK);
+        for (;;) {
+          load_rows(rb, cur, base0 + (it + kWaves) * kNK);
+          compute(ra);
+          it += kWaves;
+          if (it >= num_iters) break;
+          load_rows(ra, cur, base0 + (it + kWaves) * kNK);
+          compute(rb);
+          it += kWaves;
+          if (it >= num_iters) break;
+        }
       }
     }
     __syncthreads();                                 // every wavefront done with its V tile
