@@ -229,3 +229,55 @@ def test_retention_decode_batch_full_size():
     (ref, new_state), (mag, mag_state) = _oracle_pair(inp)
     _close("outputs", host(out), ref, mag)
     _close("states", host(t["state"]), new_state, mag_state)
+
+
+def test_retention_in_a_hip_graph():
+    """A segmented retention call (two launches, workspace) and a decode call
+    on the recurrent kernel, captured in one HIP graph and replayed three
+    times with eager work between the replays: every replay gives the eager
+    bits (the calls allocate nothing and write no memsets)."""
+    say("retention: HIP graph capture, segmented + recurrent")
+    d = dev()
+    pre = synth.make_retention_inputs([2500, 700, 0, 33], 2, 128, device=d)
+    dec = synth.make_retention_inputs([1] * 6, 2, 128, device=d, tag=78)
+    ws = torch.empty(max(16, yb.gated_retention_workspace_size(int(pre.lens.sum()), 4, 2, 128, 0)),
+                     dtype=torch.uint8, device=d)
+    cu_p, idx_p = torch.from_numpy(pre.cu_seqlens).to(d), torch.from_numpy(pre.state_indices).to(d)
+    cu_d, idx_d = torch.from_numpy(dec.cu_seqlens).to(d), torch.from_numpy(dec.state_indices).to(d)
+    out_p = torch.empty(pre.q.shape, dtype=torch.float32, device=d)
+    out_d = torch.empty(dec.q.shape, dtype=torch.float32, device=d)
+    sp0, sd0 = pre.state.clone(), dec.state.clone()
+    stream = torch.cuda.Stream()
+
+    def step():
+        s = torch.cuda.current_stream()
+        yb.gated_retention(pre.q, pre.k, pre.v, pre.gamma, cu_p, pre.state, idx_p, max_seqlen=0, out=out_p,
+                           workspace=ws, stream=s)
+        yb.gated_retention(dec.q, dec.k, dec.v, dec.gamma, cu_d, dec.state, idx_d, max_seqlen=1, out=out_d,
+                           stream=s)
+
+    with torch.cuda.stream(stream):
+        step()
+    torch.cuda.synchronize()
+    eager = [x.clone() for x in (out_p, out_d, pre.state, dec.state)]
+    graph = torch.cuda.CUDAGraph()
+    pre.state.copy_(sp0)
+    dec.state.copy_(sd0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    for replay in range(3):
+        out_p.fill_(float("nan"))
+        out_d.fill_(float("nan"))
+        pre.state.copy_(sp0)
+        dec.state.copy_(sd0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        owned = int(pre.cu_seqlens[-1])
+        for got, want in zip((out_p[:owned], out_d, pre.state, dec.state), (eager[0][:owned], *eager[1:])):
+            assert torch.equal(got.view(torch.int32), want.view(torch.int32)), replay
+        # eager work between replays, on the default stream
+        yb.gated_retention(dec.q, dec.k, dec.v, dec.gamma, cu_d, dec.state, idx_d, max_seqlen=1)
+        torch.cuda.synchronize()
+    say("  3 replays identical to the eager calls")
