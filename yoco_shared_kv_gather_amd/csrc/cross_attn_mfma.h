@@ -277,9 +277,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
   mfma_bf16x8 qop[kKS];
   float m_run = kInitMax, l_run = 0.0f;
   mfma_f32x4 oacc[kDT];
-  int jlo = 0, jhi = 0;                             // keys [jlo, jhi) visible to this lane's query
-  int item_lo = 0, item_hi = 0;                     // the item's range [start, end)
-  bool qlive = false;                               // this lane's query column is a real query vector
+  // per-key tests as one unsigned compare each: key j is in [lo, lo + len)
+  // iff unsigned(j - lo) < unsigned(len)
+  int item_lo = 0;                                  // the item's range [item_lo, item_lo + item_len)
+  uint32_t item_len = 0u;
+  int vis_lo = 0;                                   // keys this lane's query sees: [vis_lo, vis_lo + vis_len)
+  uint32_t vis_len = 0u;                            // (0 when the lane's column holds no query)
 
   auto compute = [&](const Rows& rs) {
     uint16_t(*vt)[ML::kVStride] = sm.u.vt[wave];
@@ -335,8 +338,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int j = rs.base + 16 * t + 4 * gi + e;
-        inrange[t][e] = tile_ok && j >= item_lo && j < item_hi;
-        const bool ok = inrange[t][e] && qlive && j >= jlo && j < jhi;
+        inrange[t][e] = tile_ok && static_cast<uint32_t>(j - item_lo) < item_len;
+        const bool ok = tile_ok && static_cast<uint32_t>(j - vis_lo) < vis_len;
         float sc = a.scale_log2;
         if constexpr (kF8) sc *= e == 0 ? rs.ks[t].x : e == 1 ? rs.ks[t].y : e == 2 ? rs.ks[t].z : rs.ks[t].w;
         s[t][e] = ok ? acc[e] * sc : -INFINITY;
@@ -433,13 +436,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
       // this lane's query column: vector l16 = query row l16 / G, head l16 % G
       {
         const int qi = l16 / G;
-        qlive = l16 < VG && qi < cur.nq;
+        const bool qlive = l16 < VG && qi < cur.nq;
         const int p = cur.pbase + qi;
         item_lo = cur.start;
-        item_hi = cur.end;
-        // the item's range [start, end), cut to the query's causal window
-        jhi = kVar ? min(cur.end, p + 1) : cur.end;
-        jlo = (kVar && a.window > 0) ? max(cur.start, p - a.window + 1) : cur.start;
+        item_len = static_cast<uint32_t>(cur.end - cur.start);
+        // the item's range cut to the query's causal window (inside the item)
+        const int jhi = kVar ? min(cur.end, p + 1) : cur.end;
+        const int jlo = (kVar && a.window > 0) ? max(cur.start, p - a.window + 1) : cur.start;
+        vis_lo = jlo;
+        vis_len = qlive && jhi > jlo ? static_cast<uint32_t>(jhi - jlo) : 0u;
       }
       m_run = kInitMax;
       l_run = 0.0f;
