@@ -411,7 +411,6 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void kv_append_skinny_kernel(Ski
     xok[mt] = row < a.num_tokens;
     xrow[mt] = xok[mt] ? row : a.num_tokens - 1;     // in bounds; zeroed below when past T
   }
-#pragma unroll 4
   for (int k = k_begin; k < k_begin + kq; k += 32) {
     const uint4 wb = *reinterpret_cast<const uint4*>(wrow + k + kofs);
     const uint4 wr = *reinterpret_cast<const uint4*>(a.w_rms + k + kofs);

@@ -14,8 +14,8 @@
 // state S (b_t = sum_{u<=t} log2 gamma_u inside the chunk):
 //     o_t    = 2^{b_t} q_t S + sum_{s<=t} 2^{b_t - b_s} (q_t . k_s) v_s
 //     S_next = 2^{b_{n-1}} S + sum_s 2^{b_{n-1} - b_s} k_s^T v_s
-// which is the recurrence unrolled over the chunk.  A decode step is the
-// same with n = 1, so one kernel serves prefill and decode.
+// which is the recurrence unrolled over the chunk (a one-row request inside
+// a mixed batch is the case n = 1).
 //
 // A workgroup walks a run of a request's rows chunk by chunk for one head,
 // with the head's fp32 state resident in registers (wavefront w owns value
@@ -37,16 +37,20 @@
 //            scaled by 2^{b_t - b_s}, stored as bf16 high + low parts;
 //   O        Q S (the state split into bf16 high + low in registers), rows
 //            scaled by 2^{b_t}, plus A V;
-//   S        2^{b_{n-1}} S + K~^T V.
+//   S        2^{b_{n-1}} S + K~^T V; the state's own decay is kept in a
+//            running scale while that stays above 2^-60 (the new keys are
+//            weighted by its inverse instead), so the state is multiplied
+//            out only when the scale would get too small.
 // The next chunk's rows are loaded into registers while the current one is
 // computed.  q, k and v are exact bf16 operands; every fp32 operand (state,
 // A, K~) enters as two bf16 parts (~17 significant bits); sums are fp32.
 // log2 gamma is clamped at -64, so a zero gate weighs 2^-64 instead of 0.
 //
 // Decode batches (at most one row per request) take the recurrent form
-// instead: one workgroup per (request, head) streams the state through
-// registers with 16-byte loads and stores, S = gamma S + k^T v then
-// o = q S, the partial products reduced over row groups in LDS.
+// instead: one workgroup per (request, head, 32-column slice of the state)
+// streams its slice through registers with 16-byte loads and stores,
+// S = gamma S + k^T v then o = q S, the partial products reduced over row
+// groups in LDS.
 
 #include <type_traits>
 
