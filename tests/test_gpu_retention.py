@@ -281,3 +281,19 @@ def test_retention_in_a_hip_graph():
         yb.gated_retention(dec.q, dec.k, dec.v, dec.gamma, cu_d, dec.state, idx_d, max_seqlen=1)
         torch.cuda.synchronize()
     say("  3 replays identical to the eager calls")
+
+
+@pytest.mark.parametrize("plan", sorted(PLANS))
+def test_retention_without_state_slots(plan):
+    """No state tensor rows at all (num_slots = 0): every request starts from
+    zeros and nothing is stored, on every schedule."""
+    say(f"retention: no state slots, plan {plan}")
+    inp = synth.make_retention_inputs([1100, 3, 0, 40], 2, 64)
+    d = dev()
+    t = _to_dev(inp)
+    t["state"] = torch.empty((0, 2, 64, 64), dtype=torch.float32, device=d)
+    out = _run(t, max_seqlen=PLANS[plan])
+    torch.cuda.synchronize()
+    none = -np.ones(len(inp.lens), dtype=np.int64)
+    (ref, _), (mag, _) = _oracle_pair(inp, state=np.zeros((1, 2, 64, 64)), idx=none)
+    _close("outputs", host(out), ref, mag)
