@@ -451,7 +451,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         sm.al[t][s] = bf16_bits(vl);
       }
     }
-    __syncthreads();
+    // the score tiles are read below; the state pass writes none (its next
+    // chunk's decay terms go to the other buffer, read after the last barrier)
+    if constexpr (kOut) __syncthreads();
 
     bf16x8 vb[kCT];
 #pragma unroll
