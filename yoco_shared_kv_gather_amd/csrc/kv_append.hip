@@ -477,6 +477,7 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void kv_append_skinny_kernel(Ski
 // ---- scatter of given rows, optionally quantizing to FP8 E4M3 ---------------------
 
 constexpr int kScatterThreads = 256;
+constexpr int kScatterBatchRows = 16;  // rows a quantizing-scatter wavefront loads before reducing any
 
 struct ScatterArgs {
   const void* k_src;          // K rows: token t, KV head h at k_src + t*token_stride + h*D (source elements)
@@ -494,14 +495,9 @@ struct ScatterArgs {
   int64_t num_slots;
 };
 
-// One workgroup per token; wavefront w takes the (K or V, KV head) rows
-// w, w+4, ...  Quantizing: lane l holds D/64 consecutive values, the row's
-// largest magnitude comes from a wavefront max over the fp32 bit patterns
-// (ordered like the magnitudes, and above every finite value for inf and
-// NaN), s = max / 448 and code = E4M3(x / s), both divisions in fp32; a row
-// holding inf or NaN is stored as NaN codes (its scale is inf or NaN), a row
-// of zeros as zero codes with scale 0.  Copying: the row's bytes as they are.
-template <bool kSrcF32, bool kQuant>
+// One workgroup per token; wavefront w copies the (K or V, KV head) rows
+// w, w+4, ... of its token: the row's bytes as they are.
+template <bool kSrcF32>
 __global__ __launch_bounds__(kScatterThreads) void kv_scatter_kernel(ScatterArgs a) {
   const int t = blockIdx.x;
   const int64_t slot = a.slots[t];
@@ -518,48 +514,97 @@ __global__ __launch_bounds__(kScatterThreads) void kv_scatter_kernel(ScatterArgs
     const char* src = static_cast<const char*>(is_v ? a.v_src : a.k_src) +
                       (static_cast<int64_t>(t) * a.token_stride + static_cast<int64_t>(h) * D) * kSrcBytes;
     const int64_t row = (blk * a.num_kv_heads + h) * a.block_size + off;
-    if constexpr (kQuant) {
-      const int per = D / 64;                          // 1, 2 or 4 values per lane
-      float x[4];
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(is_v ? a.v_cache : a.k_cache) + row * D * kSrcBytes);
+    for (int c = lane; c < D * kSrcBytes / 16; c += 64) dst[c] = reinterpret_cast<const uint4*>(src)[c];
+  }
+}
+
+// Largest of x over the 16 lanes of each DPP row (lanes 16r..16r+15): swap
+// neighbours, then pairs, then mirror within each half row and within the
+// row; every lane ends with the row's value.
+__device__ __forceinline__ uint32_t row16_max(uint32_t x) {
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0xB1, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x4E, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x141, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x140, 0xF, 0xF, false)));
+  return x;
+}
+
+// Quantizing scatter to FP8 E4M3. One wavefront per token; its 2*Hkv rows
+// (K rows, then V rows) are taken four at a time, a row per 16 lanes: lane l
+// works on row 4j + l/16 and holds kVec groups of four consecutive values,
+// group v at columns 64v + 4(l%16) .. +3, so each load instruction reads 64
+// contiguous values of four rows. Up to kScatterBatchRows rows are loaded
+// before any is reduced. The row's largest magnitude is a max over the fp32
+// bit patterns (ordered like the magnitudes, and above every finite value for
+// inf and NaN); s = max / 448 and code = E4M3(x / s), both divisions in fp32;
+// a row holding inf or NaN is stored as NaN codes (its scale is inf or NaN),
+// a row of zeros as zero codes with scale 0.
+template <bool kSrcF32, int kVec>
+__global__ __launch_bounds__(kScatterThreads) void kv_quant_scatter_kernel(ScatterArgs a, int32_t num_tokens) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kScatterThreads / 64) + (threadIdx.x >> 6);
+  if (t >= num_tokens) return;
+  const int64_t slot = a.slots[t];
+  if (slot < 0 || slot >= a.num_slots) return;
+  const int64_t blk = slot >> a.bs_shift;
+  const int64_t off = slot & (a.block_size - 1);
+  constexpr int D = 64 * kVec;
+  constexpr int kQuads = kScatterBatchRows / 4;
+  const int rows = 2 * a.num_kv_heads;
+  const int sub = lane >> 4;         // row within a group of four
+  const int col = 4 * (lane & 15);   // first column of this lane's group 0
+  for (int r0 = 0; r0 < rows; r0 += 4 * kQuads) {
+    float x[kQuads][kVec][4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (e >= per) break;
-        const int i = lane * per + e;
+    for (int j = 0; j < kQuads; ++j) {
+      const int p = min(r0 + 4 * j + sub, rows - 1);   // rows past the end reload the last row
+      const bool is_v = p >= a.num_kv_heads;
+      const int h = is_v ? p - a.num_kv_heads : p;
+      const int64_t e0 = static_cast<int64_t>(t) * a.token_stride + static_cast<int64_t>(h) * D + col;
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) {
         if constexpr (kSrcF32) {
-          x[e] = reinterpret_cast<const float*>(src)[i];
+          const float4 f = *reinterpret_cast<const float4*>(static_cast<const float*>(is_v ? a.v_src : a.k_src) + e0 + 64 * v);
+          x[j][v][0] = f.x; x[j][v][1] = f.y; x[j][v][2] = f.z; x[j][v][3] = f.w;
         } else {
-          x[e] = __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(src)[i]) << 16);
+          const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(is_v ? a.v_src : a.k_src) + e0 + 64 * v);
+          x[j][v][0] = __uint_as_float(u.x << 16); x[j][v][1] = __uint_as_float(u.x & 0xffff0000u);
+          x[j][v][2] = __uint_as_float(u.y << 16); x[j][v][3] = __uint_as_float(u.y & 0xffff0000u);
         }
       }
-      uint32_t mbits = 0;
+    }
+    uint32_t mbits[kQuads];
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (e < per) mbits = max(mbits, __float_as_uint(x[e]) & 0x7fffffffu);
+    for (int j = 0; j < kQuads; ++j) {
+      uint32_t m = 0;
 #pragma unroll
-      for (int mask = 32; mask > 0; mask >>= 1)
-        mbits = max(mbits, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mbits), mask, 64)));
-      const float s = __uint_as_float(mbits) / 448.0f;
-      const bool finite = mbits < 0x7f800000u;
-      uint32_t packed = 0;
+      for (int v = 0; v < kVec; ++v)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (e >= per) break;
-        const uint32_t code = !finite ? 0x7fu : (s == 0.0f ? 0u : yoco::f32_to_e4m3_rne(x[e] / s));
-        packed |= code << (8 * e);
+        for (int e = 0; e < 4; ++e) m = max(m, __float_as_uint(x[j][v][e]) & 0x7fffffffu);
+      mbits[j] = row16_max(m);
+    }
+#pragma unroll
+    for (int j = 0; j < kQuads; ++j) {
+      const int p = r0 + 4 * j + sub;
+      if (p >= rows) continue;
+      const float s = __uint_as_float(mbits[j]) / 448.0f;
+      const bool finite = mbits[j] < 0x7f800000u;
+      const bool is_v = p >= a.num_kv_heads;
+      const int h = is_v ? p - a.num_kv_heads : p;
+      const int64_t row = (blk * a.num_kv_heads + h) * a.block_size + off;
+      uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache) + row * D + col;
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) {
+        uint32_t packed = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t code = !finite ? 0x7fu : (s == 0.0f ? 0u : yoco::f32_to_e4m3_rne(x[j][v][e] / s));
+          packed |= code << (8 * e);
+        }
+        *reinterpret_cast<uint32_t*>(dst + 64 * v) = packed;
       }
-      uint8_t* dst = static_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache) + row * D + lane * per;
-      if (per == 1) {
-        *dst = static_cast<uint8_t>(packed);
-      } else if (per == 2) {
-        *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(packed);
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = packed;
-      }
-      if (lane == 0) (is_v ? a.v_scale : a.k_scale)[row] = s;
-    } else {
-      const int chunks = D * kSrcBytes / 16;
-      uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(is_v ? a.v_cache : a.k_cache) + row * D * kSrcBytes);
-      for (int c = lane; c < chunks; c += 64) dst[c] = reinterpret_cast<const uint4*>(src)[c];
+      if ((lane & 15) == 0) (is_v ? a.v_scale : a.k_scale)[row] = s;
     }
   }
 }
@@ -704,13 +749,24 @@ int32_t scatter_impl(bool src_f32, bool quant, const void* k_src, const void* v_
   a.block_size = block_size;
   a.bs_shift = yoco::ilog2(block_size);
   a.num_slots = static_cast<int64_t>(num_blocks) * block_size;
-  const dim3 grid(static_cast<uint32_t>(num_tokens)), block(kScatterThreads);
+  const dim3 block(kScatterThreads);
   if (quant) {
-    if (src_f32) hipLaunchKernelGGL((kv_scatter_kernel<true, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((kv_scatter_kernel<false, true>), grid, block, 0, s, a);
+    constexpr int kTokensPerGroup = kScatterThreads / 64;
+    const dim3 grid(static_cast<uint32_t>((num_tokens + kTokensPerGroup - 1) / kTokensPerGroup));
+    const int vec = head_dim / 64;
+    if (src_f32) {
+      if (vec == 4) hipLaunchKernelGGL((kv_quant_scatter_kernel<true, 4>), grid, block, 0, s, a, num_tokens);
+      else if (vec == 2) hipLaunchKernelGGL((kv_quant_scatter_kernel<true, 2>), grid, block, 0, s, a, num_tokens);
+      else hipLaunchKernelGGL((kv_quant_scatter_kernel<true, 1>), grid, block, 0, s, a, num_tokens);
+    } else {
+      if (vec == 4) hipLaunchKernelGGL((kv_quant_scatter_kernel<false, 4>), grid, block, 0, s, a, num_tokens);
+      else if (vec == 2) hipLaunchKernelGGL((kv_quant_scatter_kernel<false, 2>), grid, block, 0, s, a, num_tokens);
+      else hipLaunchKernelGGL((kv_quant_scatter_kernel<false, 1>), grid, block, 0, s, a, num_tokens);
+    }
   } else {
-    if (src_f32) hipLaunchKernelGGL((kv_scatter_kernel<true, false>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((kv_scatter_kernel<false, false>), grid, block, 0, s, a);
+    const dim3 grid(static_cast<uint32_t>(num_tokens));
+    if (src_f32) hipLaunchKernelGGL((kv_scatter_kernel<true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((kv_scatter_kernel<false>), grid, block, 0, s, a);
   }
   return yoco::launch_result("kv_scatter");
 }
