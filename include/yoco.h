@@ -211,9 +211,12 @@ int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_tokens, int32_t
  *
  * yoco_kv_append_fp8: yoco_kv_append with the cache in FP8 E4M3: the fp32
  * projection of each token (before any bf16 rounding) is quantized.  `dtype`
- * is the type of x, rms_weight, w_k and w_v.  The workspace holds the
- * projected fp32 rows: at least yoco_kv_append_fp8_workspace_size() bytes
- * (grows with num_tokens).  Caches and scales need 4-byte alignment.
+ * is the type of x, rms_weight, w_k and w_v.  The workspace needs at least
+ * yoco_kv_append_fp8_workspace_size() bytes: the folded weights of the bf16
+ * GEMM, plus the projected fp32 rows [T][2*Hkv*D] where the projection does
+ * not quantize in place (fp32 inputs, or at most 64 tokens), so it grows with
+ * num_tokens only there.  Workspace and caches need 16-byte alignment, scales
+ * 4-byte.
  *
  * Errors: YOCO_ERR_INVALID_ARGUMENT, YOCO_ERR_UNSUPPORTED,
  * YOCO_ERR_WORKSPACE_TOO_SMALL.  num_tokens == 0 is a no-op.

@@ -46,6 +46,17 @@ def test_scatter_quantizes_bit_exact(src, hkv, d, bs):
     rows[0, 7, 0] = 0.0                                  # a zero row
     rows[1, 9, 0, 3] = np.nan                            # a row holding NaN
     rows[0, 11, 0, 1] = -np.inf
+    # values on and next to E4M3 rounding midpoints (ties to even decide):
+    # scale 1/8 exactly (row max 56), and a scale that is no power of two
+    mids = _e4m3_midpoints()
+    for row, scale in ((rows[0, 13, 0], 0.125), (rows[1, 13, 0], np.float32(0.3))):
+        vals = (np.resize(mids, d) * np.float32(scale)).astype(np.float32)
+        vals[1::3] = np.nextafter(vals[1::3], np.float32(np.inf))
+        vals[2::3] = np.nextafter(vals[2::3], np.float32(-np.inf))
+        vals[::2] *= -1
+        vals[0] = np.float32(448.0) * np.float32(scale)
+        row[:] = vals
+    rows[1, 15, -1] = rows[1, 15, -1] * np.float32(1e-39)   # a scale whose reciprocal overflows
     if src == "bf16":
         rows_t = torch.from_numpy(rows).to(torch.bfloat16)
         rows = rows_t.float().numpy()                    # exact widening: what the kernel reads
@@ -63,6 +74,15 @@ def test_scatter_quantizes_bit_exact(src, hkv, d, bs):
     ref_k, ref_v, ref_ks, ref_vs = oracle.kv_scatter(rows[0], rows[1], slots, codes0, codes0, sc0, sc0)
     assert _codes_equal(kc.cpu().numpy(), ref_k) and _codes_equal(vc.cpu().numpy(), ref_v)
     assert _scales_equal(ks.cpu().numpy(), ref_ks) and _scales_equal(vs.cpu().numpy(), ref_vs)
+
+
+def _e4m3_midpoints():
+    """Every point halfway between two neighbouring E4M3 magnitudes below 448
+    (exact in fp32): (k + 1/2) 2^-9 among the subnormals, (1 + (2k+1)/16) 2^e
+    among the normals."""
+    sub = [(k + 0.5) * 2.0 ** -9 for k in range(8)]
+    nrm = [(1 + (2 * k + 1) / 16) * 2.0 ** e for e in range(-6, 9) for k in range(8)]
+    return np.array([m for m in sub + nrm if m < 448], dtype=np.float32)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -99,8 +119,28 @@ def test_append_fp8_within_bound(cid, size, sample):
     stored value (2^-4 relative, s*2^-10 in the subnormal range), and the
     scale times 448 within the append error of the row's largest |ref|."""
     meta = synth.make_metadata(cid, size)
-    geom = meta.geom
     say(f"kv_append_fp8: workload {cid} {size}, {meta.num_tokens} tokens")
+    _check_append_fp8(meta, sample)
+
+
+@pytest.mark.parametrize("hkv,d", [(1, 64), (3, 64), (2, 256), (1, 256)])
+def test_append_fp8_head_dims_tiled(hkv, d):
+    """The tiled bf16 GEMM (more than 64 tokens) at head_dim 64 (two heads per
+    wavefront; an odd head count leaves half a tile of features) and 256 (a
+    head across both column halves of the tile), 150 tokens in a partial
+    128-token tile, every seventh row unscheduled (slot -1)."""
+    geom = synth.custom_geometry("bf16", 2 * hkv, hkv, d, 16, hidden=512)
+    lens = np.random.default_rng(d + hkv).integers(1, 60, size=160)
+    lens[::16] = 0
+    meta = synth.make_custom_metadata(geom, lens, tag=70 + hkv)
+    meta.slot_mapping[::7] = -1
+    say(f"kv_append_fp8: {meta.num_tokens} tokens, hidden 512 -> {hkv} x {d}")
+    assert meta.num_tokens > 64
+    _check_append_fp8(meta, 0)
+
+
+def _check_append_fp8(meta, sample):
+    geom = meta.geom
     d = dev()
     x, w_rms, w_k, w_v = synth.make_append_inputs(meta, d, rms_weight="random")
     shape = (meta.num_blocks, geom.num_kv_heads, geom.block_size, geom.head_dim)
@@ -114,7 +154,8 @@ def test_append_fp8_within_bound(cid, size, sample):
     tokens = list(range(meta.num_tokens))
     if sample:
         # full size: a sample of tokens (the oracle's quantizer runs in Python)
-        tokens = sorted(np.random.default_rng(cid).choice(meta.num_tokens, size=sample, replace=False).tolist())
+        tokens = sorted(np.random.default_rng(meta.config_id).choice(meta.num_tokens, size=sample,
+                                                                     replace=False).tolist())
     k, v, _, _, bk, bv = oracle.kv_append_fp8(host(x)[tokens], host(w_rms), 1e-6, host(w_k), host(w_v),
                                              meta.slot_mapping[tokens], geom.num_kv_heads, geom.head_dim)
     kq, vq = kc.cpu().numpy(), vc.cpu().numpy()
@@ -135,6 +176,9 @@ def test_append_fp8_within_bound(cid, size, sample):
             assert (np.abs(got - ref) <= err + step * (1 + 1e-6)).all()
             amax = np.abs(ref).max(axis=1)
             assert (np.abs(s * 448.0 - amax) <= err.max(axis=1) + amax * 2.0 ** -22).all()
+            # the row's own largest value is what the scale was taken from: it
+            # divides to 448 up to one fp32 rounding, so every row holds +-448
+            assert ((codes[blk, :, off] & 0x7F) == 0x7E).any(axis=1).all()
             worst = max(worst, float((np.abs(got - ref) / (err + step)).max()))
             same += int((codes[blk, :, off] == oracle.quantize_rows(ref.astype(np.float32))[0]).sum())
             total += ref.size

@@ -41,6 +41,17 @@ using yoco::bf16_hi;
 using yoco::bf16_lo;
 using yoco::f32_to_bf16_rne;
 
+// Largest of x over the 16 lanes of each DPP row (lanes 16r..16r+15): swap
+// neighbours, then pairs, then mirror within each half row and within the
+// row; every lane ends with the row's value.
+__device__ __forceinline__ uint32_t row16_max(uint32_t x) {
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0xB1, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x4E, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x141, 0xF, 0xF, false)));
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x140, 0xF, 0xF, false)));
+  return x;
+}
+
 // ---- fold W' = W diag(w_rms) -------------------------------------------------
 
 __global__ __launch_bounds__(256) void fold_rms_weight_kernel(const uint4* __restrict__ w_k,
@@ -95,7 +106,8 @@ struct AppendArgs {
   int64_t num_slots;          // num_blocks * block_size
   float inv_hidden;
   float eps;
-  float* rows_out;            // fp32 [T][2*Hkv*D] instead of the cache (8-bit cache), or nullptr
+  float* k_scale;             // FP8 cache: [num_blocks][Hkv][bs] scales (caches hold bytes), else nullptr
+  float* v_scale;
 };
 
 // One workgroup: 128 tokens x 256 output features, four wavefronts of 64 x 128
@@ -106,7 +118,17 @@ struct AppendArgs {
 // own L2 while the XCDs share each activation tile through the last-level
 // cache.  Global -> registers -> LDS staging, two LDS stages, one barrier per
 // K step.  The epilogue scales by the row's rsqrt, rounds to bf16 into LDS and
-// writes each token's features as 16-byte chunks to its slot.
+// writes each token's features as 16-byte chunks to its slot.  With kQD > 0
+// (the head_dim of an FP8 cache) the epilogue quantizes instead: a tile holds
+// whole heads (256 is a multiple of every head_dim), and for head_dim 128 a
+// 16-lane DPP row of a wavefront holds every column of its rows' head, so
+// the head's largest magnitude is a max over the lane's 8 values and a DPP
+// row (two heads per wavefront for 64; for 256 the two column halves meet in
+// LDS).  s = max / 448 and code = E4M3(y / s) in fp32 on the scaled fp32
+// projection y, exactly as the quantizing scatter would (the quotient's code
+// mostly without the division, as e4m3_of_quotient explains); codes go through an
+// LDS byte tile to 16-byte stores, scales straight from the lanes.
+template <int kQD>
 __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2))) void kv_append_mfma_kernel(AppendArgs a) {
   constexpr int kLdsElems = 2 * kStage > kBM * kOutStride ? 2 * kStage : kBM * kOutStride;
   __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
@@ -238,23 +260,95 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)
   }
   __syncthreads();
 
-  if (a.rows_out != nullptr) {
-    // fp32 rows for the quantizing scatter: lane holds rows 4*(lane/16)+0..3
-    // of column lane%16 of each 16x16 tile.
+  if constexpr (kQD > 0) {
+    constexpr int kHeadsPerWave = kQD >= 128 ? 1 : 128 / kQD;   // heads in a wavefront's 128 columns
+    constexpr int kJPerHead = kQD >= 128 ? 8 : kQD / 16;        // 16-column MFMA tiles per head in a wavefront
+    constexpr int kCodeStride = kBN + 16;                      // bytes per row of the code tile
+    uint8_t* ct = reinterpret_cast<uint8_t*>(lds);
+    float* hmax = reinterpret_cast<float*>(ct + kBM * kCodeStride);   // [2][kBM], head_dim 256 only
+    static_assert(kBM * kCodeStride + 2 * kBM * sizeof(float) <= sizeof(lds), "code tile exceeds the staging LDS");
+    uint32_t mb[4][4][kHeadsPerWave];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int lrow = wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+        const float sc = row_scale[lrow];
+#pragma unroll
+        for (int hw = 0; hw < kHeadsPerWave; ++hw) {
+          uint32_t m = 0;
+#pragma unroll
+          for (int jj = 0; jj < kJPerHead; ++jj) {
+            const int j = hw * kJPerHead + jj;
+            acc[i][j][e] *= sc;
+            m = max(m, __float_as_uint(acc[i][j][e]) & 0x7fffffffu);
+          }
+          mb[i][e][hw] = row16_max(m);
+        }
+      }
+    if constexpr (kQD == 256) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((lane & 15) == 0) hmax[wn * kBM + wm * 64 + i * 16 + (lane >> 4) * 4 + e] = __uint_as_float(mb[i][e][0]);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int lrow = wm * 64 + i * 16 + (lane >> 4) * 4 + e;
+          mb[i][e][0] = max(__float_as_uint(hmax[lrow]), __float_as_uint(hmax[kBM + lrow]));
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int lrow = wm * 64 + i * 16 + (lane >> 4) * 4 + e;
         const int t = m0 + lrow;
-        if (t >= a.num_tokens) continue;
-        const float sc = row_scale[lrow];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int col = n0 + wn * 128 + j * 16 + (lane & 15);
-          if (col < n_total) a.rows_out[static_cast<int64_t>(t) * n_total + col] = acc[i][j][e] * sc;
+        for (int hw = 0; hw < kHeadsPerWave; ++hw) {
+          const float s = __uint_as_float(mb[i][e][hw]) / 448.0f;
+          const bool finite = mb[i][e][hw] < 0x7f800000u;
+          const float r = finite && s > 0.0f ? 1.0f / s : 0.0f;
+#pragma unroll
+          for (int jj = 0; jj < kJPerHead; ++jj) {
+            const int j = hw * kJPerHead + jj;
+            const uint32_t code = !finite ? 0x7fu : (s == 0.0f ? 0u : yoco::e4m3_of_quotient(acc[i][j][e], s, r));
+            ct[lrow * kCodeStride + wn * 128 + j * 16 + (lane & 15)] = static_cast<uint8_t>(code);
+          }
+          const int col0 = n0 + wn * 128 + hw * kQD;
+          if ((lane & 15) == 0 && (kQD < 256 || wn == 0) && t < a.num_tokens && col0 < n_total) {
+            const int64_t slot = a.slots[t];
+            if (slot >= 0 && slot < a.num_slots) {
+              const bool is_v = col0 >= a.out_half;
+              const int h = (is_v ? col0 - a.out_half : col0) / kQD;
+              const int64_t row = ((slot >> a.bs_shift) * a.num_kv_heads + h) * a.block_size + (slot & (a.block_size - 1));
+              (is_v ? a.v_scale : a.k_scale)[row] = s;
+            }
+          }
         }
       }
+    __syncthreads();
+    // Each token's codes, 16 bytes (16 features, inside one head) at a time.
+    for (int c = tid; c < kBM * (kBN / 16); c += kGemmThreads) {
+      const int lrow = c / (kBN / 16);
+      const int lcol = (c % (kBN / 16)) * 16;
+      const int t = m0 + lrow;
+      const int col = n0 + lcol;
+      if (t >= a.num_tokens || col >= n_total) continue;
+      const int64_t slot = a.slots[t];
+      if (slot < 0 || slot >= a.num_slots) continue;
+      const bool is_v = col >= a.out_half;
+      const int hd = is_v ? col - a.out_half : col;
+      const int h = hd / kQD;
+      const int d = hd - h * kQD;
+      uint8_t* cache = reinterpret_cast<uint8_t*>(is_v ? a.v_cache : a.k_cache);
+      const int64_t dst = (((slot >> a.bs_shift) * a.num_kv_heads + h) * a.block_size + (slot & (a.block_size - 1))) *
+                              kQD + d;
+      *reinterpret_cast<uint4*>(cache + dst) = *reinterpret_cast<const uint4*>(&ct[lrow * kCodeStride + lcol]);
+    }
     return;
   }
 
@@ -519,17 +613,6 @@ __global__ __launch_bounds__(kScatterThreads) void kv_scatter_kernel(ScatterArgs
   }
 }
 
-// Largest of x over the 16 lanes of each DPP row (lanes 16r..16r+15): swap
-// neighbours, then pairs, then mirror within each half row and within the
-// row; every lane ends with the row's value.
-__device__ __forceinline__ uint32_t row16_max(uint32_t x) {
-  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0xB1, 0xF, 0xF, false)));
-  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x4E, 0xF, 0xF, false)));
-  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x141, 0xF, 0xF, false)));
-  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x140, 0xF, 0xF, false)));
-  return x;
-}
-
 // Quantizing scatter to FP8 E4M3. One wavefront per token; its 2*Hkv rows
 // (K rows, then V rows) are taken four at a time, a row per 16 lanes: lane l
 // works on row 4j + l/16 and holds kVec groups of four consecutive values,
@@ -537,9 +620,10 @@ __device__ __forceinline__ uint32_t row16_max(uint32_t x) {
 // contiguous values of four rows. Up to kScatterBatchRows rows are loaded
 // before any is reduced. The row's largest magnitude is a max over the fp32
 // bit patterns (ordered like the magnitudes, and above every finite value for
-// inf and NaN); s = max / 448 and code = E4M3(x / s), both divisions in fp32;
-// a row holding inf or NaN is stored as NaN codes (its scale is inf or NaN),
-// a row of zeros as zero codes with scale 0.
+// inf and NaN); s = max / 448 and code = E4M3(x / s), both divisions in fp32
+// (the code mostly found without the second, by e4m3_of_quotient); a row
+// holding inf or NaN is stored as NaN codes (its scale is inf or NaN), a row
+// of zeros as zero codes with scale 0.
 template <bool kSrcF32, int kVec>
 __global__ __launch_bounds__(kScatterThreads) void kv_quant_scatter_kernel(ScatterArgs a, int32_t num_tokens) {
   const int lane = threadIdx.x & 63;
@@ -590,6 +674,7 @@ __global__ __launch_bounds__(kScatterThreads) void kv_quant_scatter_kernel(Scatt
       if (p >= rows) continue;
       const float s = __uint_as_float(mbits[j]) / 448.0f;
       const bool finite = mbits[j] < 0x7f800000u;
+      const float r = finite && s > 0.0f ? 1.0f / s : 0.0f;
       const bool is_v = p >= a.num_kv_heads;
       const int h = is_v ? p - a.num_kv_heads : p;
       const int64_t row = (blk * a.num_kv_heads + h) * a.block_size + off;
@@ -599,7 +684,7 @@ __global__ __launch_bounds__(kScatterThreads) void kv_quant_scatter_kernel(Scatt
         uint32_t packed = 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t code = !finite ? 0x7fu : (s == 0.0f ? 0u : yoco::f32_to_e4m3_rne(x[j][v][e] / s));
+          const uint32_t code = !finite ? 0x7fu : (s == 0.0f ? 0u : yoco::e4m3_of_quotient(x[j][v][e], s, r));
           packed |= code << (8 * e);
         }
         *reinterpret_cast<uint32_t*>(dst + 64 * v) = packed;
@@ -622,15 +707,39 @@ extern "C" int64_t yoco_kv_append_workspace_size(int32_t dtype, int32_t hidden, 
 
 namespace {
 
-// The projection of every scheduled token: into its cache slots
-// (rows_out == nullptr; caches in `dtype`) or as fp32 rows [T][2*Hkv*D] into
-// rows_out (the caches are then not touched).  The fold workspace is the
-// first `fold` bytes of `workspace`.
+// A few tokens whose hidden size the split-K kernel divides go through it;
+// the rest (bf16) through the MFMA GEMM.
+bool uses_skinny(int32_t num_tokens, int32_t hidden) {
+  return num_tokens <= 64 && hidden % (32 * kSkinnyWaves) == 0;
+}
+
+// FP8 cache: every path but the MFMA GEMM (which quantizes in its epilogue)
+// hands fp32 rows to the quantizing scatter.
+bool fp8_needs_rows(int32_t dtype, int32_t num_tokens, int32_t hidden) {
+  return dtype == YOCO_DTYPE_F32 || uses_skinny(num_tokens, hidden);
+}
+
+int64_t rows_bytes_of(int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim) {
+  return static_cast<int64_t>(num_tokens) * 2 * num_kv_heads * head_dim * 4;
+}
+
+int32_t scatter_impl(bool src_f32, bool quant, const void* k_src, const void* v_src, int64_t token_stride,
+                     int32_t num_tokens, const int32_t* slot_mapping, void* k_cache, void* v_cache, float* k_scale,
+                     float* v_scale, int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                     hipStream_t s);
+
 int32_t append_impl(int32_t dtype, const void* x, int32_t num_tokens, int32_t hidden, const void* rms_weight,
                     float eps, const void* w_k, const void* w_v, const int32_t* slot_mapping, void* k_cache,
                     void* v_cache, int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
-                    void* workspace, int64_t workspace_bytes, float* rows_out, int64_t rows_bytes, void* stream) {
+                    void* workspace, int64_t workspace_bytes, float* rows_out, int64_t rows_bytes, float* k_scale,
+                    float* v_scale, void* stream) {
+  // The projection of every scheduled token into its cache slots: caches in
+  // `dtype`, or FP8 codes with scales when k_scale != nullptr.  FP8 through
+  // the MFMA GEMM quantizes in its epilogue; through the other kernels it goes
+  // as fp32 rows [T][2*Hkv*D] into rows_out, then the quantizing scatter.  The
+  // fold workspace is the first `fold` bytes of `workspace`.
   using namespace yoco;
+  const bool quant = k_scale != nullptr;
   if (dtype != YOCO_DTYPE_F32 && dtype != YOCO_DTYPE_BF16)
     return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append: unknown dtype %d", dtype);
   if (num_tokens < 0 || hidden <= 0 || num_blocks <= 0 || num_kv_heads <= 0 || workspace_bytes < 0)
@@ -648,11 +757,19 @@ int32_t append_impl(int32_t dtype, const void* x, int32_t num_tokens, int32_t hi
                 (long long)workspace_bytes, (long long)need);
   if (num_tokens == 0) return YOCO_OK;
   if (x == nullptr || rms_weight == nullptr || w_k == nullptr || w_v == nullptr || slot_mapping == nullptr ||
-      (rows_out == nullptr && (k_cache == nullptr || v_cache == nullptr)) || (need > 0 && workspace == nullptr))
+      k_cache == nullptr || v_cache == nullptr || (need > 0 && workspace == nullptr) ||
+      (quant && (v_scale == nullptr || (fp8_needs_rows(dtype, num_tokens, hidden) && rows_out == nullptr))))
     return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append: null pointer");
-  if (!aligned16(x) || !aligned16(rms_weight) || !aligned16(w_k) || !aligned16(w_v) ||
-      (rows_out == nullptr && (!aligned16(k_cache) || !aligned16(v_cache))) || (need > 0 && !aligned16(workspace)))
+  if (!aligned16(x) || !aligned16(rms_weight) || !aligned16(w_k) || !aligned16(w_v) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || (need > 0 && !aligned16(workspace)))
     return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append: buffers must be 16-byte aligned");
+  const int64_t out_half = static_cast<int64_t>(num_kv_heads) * head_dim;
+  auto quantize_rows = [&](int32_t st) {
+    if (st != YOCO_OK || !quant) return st;
+    return scatter_impl(true, true, rows_out, rows_out + out_half, 2 * out_half, num_tokens, slot_mapping, k_cache,
+                        v_cache, k_scale, v_scale, num_blocks, num_kv_heads, block_size, head_dim,
+                        static_cast<hipStream_t>(stream));
+  };
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
@@ -663,12 +780,11 @@ int32_t append_impl(int32_t dtype, const void* x, int32_t num_tokens, int32_t hi
                        static_cast<const float*>(x), hidden, static_cast<const float*>(rms_weight), eps,
                        static_cast<const float*>(w_k), static_cast<const float*>(w_v), slot_mapping, num_slots,
                        static_cast<float*>(k_cache), static_cast<float*>(v_cache), num_kv_heads, block_size,
-                       bs_shift, head_dim, rows_out);
-    return launch_result("kv_append");
+                       bs_shift, head_dim, quant ? rows_out : nullptr);
+    return quantize_rows(launch_result("kv_append"));
   }
 
-  const int64_t out_half = static_cast<int64_t>(num_kv_heads) * head_dim;
-  if (num_tokens <= 64 && hidden % (32 * kSkinnyWaves) == 0) {
+  if (uses_skinny(num_tokens, hidden)) {
     SkinnyArgs k;
     k.x = static_cast<const uint16_t*>(x);
     k.w_rms = static_cast<const uint16_t*>(rms_weight);
@@ -687,7 +803,7 @@ int32_t append_impl(int32_t dtype, const void* x, int32_t num_tokens, int32_t hi
     k.num_slots = num_slots;
     k.inv_hidden = 1.0f / static_cast<float>(hidden);
     k.eps = eps;
-    k.rows_out = rows_out;
+    k.rows_out = quant ? rows_out : nullptr;
     const dim3 grid(static_cast<uint32_t>(2 * out_half / kSkinnyCols));
     const dim3 block(64 * kSkinnyWaves);
     if (num_tokens <= 16) {
@@ -697,7 +813,7 @@ int32_t append_impl(int32_t dtype, const void* x, int32_t num_tokens, int32_t hi
     } else {
       hipLaunchKernelGGL(kv_append_skinny_kernel<4>, grid, block, 0, s, k);
     }
-    return launch_result("kv_append");
+    return quantize_rows(launch_result("kv_append"));
   }
   const int64_t half_chunks = out_half * hidden / 8;
   const int64_t fold_blocks = ceil_div(2 * half_chunks, 256);
@@ -721,10 +837,15 @@ int32_t append_impl(int32_t dtype, const void* x, int32_t num_tokens, int32_t hi
   a.num_slots = num_slots;
   a.inv_hidden = 1.0f / static_cast<float>(hidden);
   a.eps = eps;
-  a.rows_out = rows_out;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
   a.n_tiles = static_cast<int32_t>(ceil_div(2 * out_half, kBN));
   const int64_t tiles = ceil_div(num_tokens, kBM) * a.n_tiles;
-  hipLaunchKernelGGL(kv_append_mfma_kernel, dim3(static_cast<uint32_t>(tiles)), dim3(kGemmThreads), 0, s, a);
+  const dim3 grid(static_cast<uint32_t>(tiles)), block(kGemmThreads);
+  if (!quant) hipLaunchKernelGGL(kv_append_mfma_kernel<0>, grid, block, 0, s, a);
+  else if (head_dim == 64) hipLaunchKernelGGL(kv_append_mfma_kernel<64>, grid, block, 0, s, a);
+  else if (head_dim == 128) hipLaunchKernelGGL(kv_append_mfma_kernel<128>, grid, block, 0, s, a);
+  else hipLaunchKernelGGL(kv_append_mfma_kernel<256>, grid, block, 0, s, a);
   return launch_result("kv_append");
 }
 
@@ -771,10 +892,6 @@ int32_t scatter_impl(bool src_f32, bool quant, const void* k_src, const void* v_
   return yoco::launch_result("kv_scatter");
 }
 
-int64_t rows_bytes_of(int32_t num_tokens, int32_t num_kv_heads, int32_t head_dim) {
-  return static_cast<int64_t>(num_tokens) * 2 * num_kv_heads * head_dim * 4;
-}
-
 }  // namespace
 
 extern "C" int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_tokens, int32_t hidden,
@@ -783,7 +900,8 @@ extern "C" int32_t yoco_kv_append(int32_t dtype, const void* x, int32_t num_toke
                                   int32_t num_kv_heads, int32_t block_size, int32_t head_dim, void* workspace,
                                   int64_t workspace_bytes, void* stream) {
   return append_impl(dtype, x, num_tokens, hidden, rms_weight, eps, w_k, w_v, slot_mapping, k_cache, v_cache,
-                     num_blocks, num_kv_heads, block_size, head_dim, workspace, workspace_bytes, nullptr, 0, stream);
+                     num_blocks, num_kv_heads, block_size, head_dim, workspace, workspace_bytes, nullptr, 0, nullptr,
+                     nullptr, stream);
 }
 
 extern "C" int64_t yoco_kv_append_fp8_workspace_size(int32_t dtype, int32_t num_tokens, int32_t hidden,
@@ -791,7 +909,8 @@ extern "C" int64_t yoco_kv_append_fp8_workspace_size(int32_t dtype, int32_t num_
   if (num_tokens < 0) return -1;
   const int64_t fold = yoco_kv_append_workspace_size(dtype, hidden, num_kv_heads, head_dim);
   if (fold < 0) return -1;
-  return yoco::round_up(fold, 256) + rows_bytes_of(num_tokens, num_kv_heads, head_dim);
+  return yoco::round_up(fold, 256) +
+         (fp8_needs_rows(dtype, num_tokens, hidden) ? rows_bytes_of(num_tokens, num_kv_heads, head_dim) : 0);
 }
 
 extern "C" int32_t yoco_kv_append_fp8(int32_t dtype, const void* x, int32_t num_tokens, int32_t hidden,
@@ -811,22 +930,16 @@ extern "C" int32_t yoco_kv_append_fp8(int32_t dtype, const void* x, int32_t num_
   if (num_tokens > 0 && (k_cache == nullptr || v_cache == nullptr || k_scale == nullptr || v_scale == nullptr ||
                          workspace == nullptr))
     return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append_fp8: null pointer");
-  if (num_tokens > 0 && (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(k_cache) & 3) != 0 ||
-                         (reinterpret_cast<uintptr_t>(v_cache) & 3) != 0 ||
+  if (num_tokens > 0 && (!aligned16(workspace) || !aligned16(k_cache) || !aligned16(v_cache) ||
                          (reinterpret_cast<uintptr_t>(k_scale) & 3) != 0 ||
                          (reinterpret_cast<uintptr_t>(v_scale) & 3) != 0))
-    return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append_fp8: workspace must be 16-byte and caches 4-byte aligned");
-  float* rows = num_tokens > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(fold, 256))
-                               : nullptr;
-  const int64_t rb = rows_bytes_of(num_tokens, num_kv_heads, head_dim);
-  int32_t st = append_impl(dtype, x, num_tokens, hidden, rms_weight, eps, w_k, w_v, slot_mapping, k_cache, v_cache,
-                           num_blocks, num_kv_heads, block_size, head_dim, workspace, workspace_bytes - rb, rows, 0,
-                           stream);
-  if (st != YOCO_OK || num_tokens == 0) return st;
-  const int64_t out_half = static_cast<int64_t>(num_kv_heads) * head_dim;
-  return scatter_impl(true, true, rows, rows + out_half, 2 * out_half, num_tokens, slot_mapping, k_cache, v_cache,
-                      k_scale, v_scale, num_blocks, num_kv_heads, block_size, head_dim,
-                      static_cast<hipStream_t>(stream));
+    return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_append_fp8: workspace and caches must be 16-byte, scales 4-byte aligned");
+  const bool with_rows = num_tokens > 0 && fp8_needs_rows(dtype, num_tokens, hidden);
+  float* rows = with_rows ? reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(fold, 256)) : nullptr;
+  const int64_t rb = with_rows ? rows_bytes_of(num_tokens, num_kv_heads, head_dim) : 0;
+  return append_impl(dtype, x, num_tokens, hidden, rms_weight, eps, w_k, w_v, slot_mapping, k_cache, v_cache,
+                     num_blocks, num_kv_heads, block_size, head_dim, workspace, workspace_bytes - rb, rows, 0, k_scale,
+                     v_scale, stream);
 }
 
 extern "C" int32_t yoco_kv_scatter(int32_t src_dtype, const void* k_rows, const void* v_rows, int32_t num_tokens,

@@ -69,4 +69,22 @@ __device__ __forceinline__ uint32_t f32_to_e4m3_rne(float f) {
   return sign | (code < 0x7eu ? code : 0x7eu);
 }
 
+// E4M3 code of the fp32 quotient RN(y / s), given r = RN(1 / s) for finite
+// s > 0 (pass r = 0 where the caller overrides the code anyway).  Mostly
+// without a division: q' = RN(y r) is within 2^-23 |y/s| of y/s, so RN(y/s)
+// lies between RN(q'(1 - 2^-21)) and RN(q'(1 + 2^-21)); the hardware
+// encoder (round to nearest even; on every finite input below 464 in
+// magnitude it gives f32_to_e4m3_rne's code) takes both, and since the
+// encoding is monotone in the magnitude, a common code is the quotient's.
+// Where they differ (a rounding midpoint within reach, a few values in a
+// million) or r is infinite, the quotient is divided out.
+__device__ __forceinline__ uint32_t e4m3_of_quotient(float y, float s, float r) {
+  const float q = y * r;
+  const uint32_t pk = static_cast<uint32_t>(
+      __builtin_amdgcn_cvt_pk_fp8_f32(q * (1.0f - 0x1p-21f), q * (1.0f + 0x1p-21f), 0, false));
+  const uint32_t c = pk & 0xffu;
+  if (c == ((pk >> 8) & 0xffu) && r < __builtin_inff()) return c;
+  return f32_to_e4m3_rne(y / s);
+}
+
 }  // namespace yoco
