@@ -2,7 +2,8 @@
 
 Usage: ``python -m yoco_shared_kv_gather_amd.build`` (or ``build()`` from
 Python).  Every source compiles to an object in ``_build/`` in parallel, then
-one link step writes ``libyoco.so`` next to this file.  Packed fp32 VALU
+one link step writes ``libyoco.so`` next to this file.  The standalone check
+programs under ``tests/`` (hardware facts the kernels rely on) build alongside.  Packed fp32 VALU
 instructions are disabled for all device code.
 """
 
@@ -23,6 +24,9 @@ LIB_PATH = os.path.join(PKG_DIR, "libyoco.so")
 
 SOURCES = ["abi.hip", "gather_last.hip", "kv_append.hip", "cross_attn.hip", "cross_attn_f32.hip", "cross_attn_bf16.hip",
            "cross_attn_fp8.hip", "cross_attn_mfma_bf16.hip", "cross_attn_mfma_fp8.hip", "retention.hip"]
+
+# Standalone GPU check programs the tests run (source, binary), built with the library.
+CHECKS = [(os.path.join(ROOT, "tests", "e4m3_encoder_check.hip"), os.path.join(ROOT, "tests", "e4m3_encoder_check"))]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [
@@ -63,6 +67,8 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
         cmds.append([cc, *COMMON_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    for src, exe in CHECKS:
+        cmds.append([cc, *COMMON_FLAGS, src, "-o", exe])
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as pool:
         for out in pool.map(_run, cmds):
             if verbose and out.strip():
