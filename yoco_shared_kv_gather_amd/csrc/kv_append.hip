@@ -477,6 +477,7 @@ struct SkinnyArgs {
 // hidden columns [w*H/8, (w+1)*H/8); the partial products and sums of
 // squares are added in LDS in wavefront order.
 constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyGroup = 4;               // K steps whose loads are issued together
 
 template <int kMT>
 __global__ __launch_bounds__(64 * kSkinnyWaves) void kv_append_skinny_kernel(SkinnyArgs a) {
@@ -493,27 +494,34 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void kv_append_skinny_kernel(Ski
   const int k_begin = wave * kq;
   const int kofs = (lane >> 4) * 8;
 
+  // The epilogue's slots (element e = tid + i*512 of the kMT*64*4 outputs),
+  // loaded now so that their latency hides behind the products.
+  constexpr int kEpi = (kMT * 256 + 64 * kSkinnyWaves - 1) / (64 * kSkinnyWaves);
+  int64_t slot_of[kEpi];
+#pragma unroll
+  for (int i = 0; i < kEpi; ++i) {
+    const int e = tid + i * 64 * kSkinnyWaves;
+    const int row = (e / 256) * 16 + (((e / 4) & 63) >> 4) * 4 + (e & 3);
+    slot_of[i] = e < kMT * 256 && row < a.num_tokens ? static_cast<int64_t>(a.slots[row]) : -1;
+  }
   f32x4 acc[kMT];
   float ssq[kMT];
-  int xrow[kMT];
-  bool xok[kMT];
+  const uint16_t* xptr[kMT];
 #pragma unroll
   for (int mt = 0; mt < kMT; ++mt) {
     acc[mt] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     ssq[mt] = 0.0f;
-    const int row = mt * 16 + (lane & 15);
-    xok[mt] = row < a.num_tokens;
-    xrow[mt] = xok[mt] ? row : a.num_tokens - 1;     // in bounds; zeroed below when past T
+    // rows past the last token read the last one: their outputs and sums of
+    // squares are never used, so the loads need no select (which would make
+    // the compiler wait for them at once)
+    const int row = min(mt * 16 + (lane & 15), a.num_tokens - 1);
+    xptr[mt] = a.x + static_cast<int64_t>(row) * a.hidden + kofs;
   }
-  for (int k = k_begin; k < k_begin + kq; k += 32) {
-    const uint4 wb = *reinterpret_cast<const uint4*>(wrow + k + kofs);
-    const uint4 wr = *reinterpret_cast<const uint4*>(a.w_rms + k + kofs);
+  auto step = [&](const uint4& wb, const uint4& wr, const uint4 (&xv)[kMT]) {
     const uint32_t* wru = reinterpret_cast<const uint32_t*>(&wr);
 #pragma unroll
     for (int mt = 0; mt < kMT; ++mt) {
-      uint4 xv = *reinterpret_cast<const uint4*>(a.x + static_cast<int64_t>(xrow[mt]) * a.hidden + k + kofs);
-      if (!xok[mt]) xv = make_uint4(0u, 0u, 0u, 0u);
-      const uint32_t* xu = reinterpret_cast<const uint32_t*>(&xv);
+      const uint32_t* xu = reinterpret_cast<const uint32_t*>(&xv[mt]);
       uint4 av;
       uint32_t* au = reinterpret_cast<uint32_t*>(&av);
 #pragma unroll
@@ -527,6 +535,32 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void kv_append_skinny_kernel(Ski
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
                                                        __builtin_bit_cast(bf16x8, wb), acc[mt], 0, 0, 0);
     }
+  };
+  // K steps of 32 in groups of kSkinnyGroup: a group's loads are all issued
+  // before any is used, so the wavefront waits once per group.
+  const int n_steps = kq / 32;
+  int st = 0;
+  for (; st + kSkinnyGroup <= n_steps; st += kSkinnyGroup) {
+    uint4 wb[kSkinnyGroup], wr[kSkinnyGroup], xv[kSkinnyGroup][kMT];
+#pragma unroll
+    for (int g = 0; g < kSkinnyGroup; ++g) {
+      const int k = k_begin + (st + g) * 32;
+      wb[g] = *reinterpret_cast<const uint4*>(wrow + k + kofs);
+      wr[g] = *reinterpret_cast<const uint4*>(a.w_rms + k + kofs);
+#pragma unroll
+      for (int mt = 0; mt < kMT; ++mt) xv[g][mt] = *reinterpret_cast<const uint4*>(xptr[mt] + k);
+    }
+#pragma unroll
+    for (int g = 0; g < kSkinnyGroup; ++g) step(wb[g], wr[g], xv[g]);
+  }
+  for (; st < n_steps; ++st) {
+    const int k = k_begin + st * 32;
+    uint4 xv[kMT];
+    const uint4 wb = *reinterpret_cast<const uint4*>(wrow + k + kofs);
+    const uint4 wr = *reinterpret_cast<const uint4*>(a.w_rms + k + kofs);
+#pragma unroll
+    for (int mt = 0; mt < kMT; ++mt) xv[mt] = *reinterpret_cast<const uint4*>(xptr[mt] + k);
+    step(wb, wr, xv);
   }
   // Sums of squares: lanes l, l^16, l^32, l^48 hold the same row.
 #pragma unroll
@@ -540,14 +574,15 @@ __global__ __launch_bounds__(64 * kSkinnyWaves) void kv_append_skinny_kernel(Ski
   __syncthreads();
 
   // Lane l of the MFMA output holds rows 4*(l/16)+0..3 of column l%16.
-  for (int e = tid; e < kMT * 64 * 4; e += 64 * kSkinnyWaves) {
+#pragma unroll
+  for (int ei = 0; ei < kEpi; ++ei) {
+    const int e = tid + ei * 64 * kSkinnyWaves;
     const int mt = e / 256;
     const int l = (e / 4) & 63;
     const int i = e & 3;
     const int row = mt * 16 + (l >> 4) * 4 + i;
-    if (row >= a.num_tokens) continue;
-    const int64_t slot = a.slots[row];
-    if (slot < 0 || slot >= a.num_slots) continue;
+    const int64_t slot = slot_of[ei];
+    if (e >= kMT * 256 || row >= a.num_tokens || slot < 0 || slot >= a.num_slots) continue;
     float sum = 0.0f, sq = 0.0f;
 #pragma unroll
     for (int w = 0; w < kSkinnyWaves; ++w) {
