@@ -266,8 +266,8 @@ int32_t yoco_kv_append_fp8(int32_t dtype, const void* x, int32_t num_tokens, int
  *                positive multiple of 64 spanning at most 511 blocks and at
  *                most 16384 tokens (YOCO_ERR_UNSUPPORTED beyond).  A context
  *                of n tokens is split into ceil(n/P) partitions of P tokens
- *                (the last one shorter); every context's last two come last
- *                in the schedule.
+ *                (the last one shorter); the shorter pieces come after all
+ *                full partitions in the schedule.
  *   flags        YOCO_FLAG_REVERSE_ORDER or 0.
  *   out          fp32 [num_seqs][num_q_heads][head_dim].
  *   workspace    device scratch of at least yoco_cross_attn_workspace_size()

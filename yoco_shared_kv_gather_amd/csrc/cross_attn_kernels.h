@@ -174,17 +174,11 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // Partitions of a context of n tokens: ceil(n/P) pieces of P tokens (the
 // last one shorter; an empty context has one, empty, partition).  For the
-// schedule they fall in two groups: the leading n/P - 1 partitions when
-// n >= 2P ("big"), and the last one or two ("small"), which hold the short
-// piece.  All big items are scheduled before all small ones, so the work ends
-// on the short pieces.
-__host__ __device__ inline int big_parts(int n, int P) {
-  const int nb = n / P;
-  return nb >= 2 ? nb - 1 : 0;
-}
-__host__ __device__ inline int small_parts(int n, int P) {
-  return n <= 0 ? 1 : (n - big_parts(n, P) * P + P - 1) / P;
-}
+// schedule they fall in two groups: the n/P full pieces ("big"), and the
+// shorter last piece if there is one ("small").  All big items are scheduled
+// before all small ones, so the work ends on the short pieces.
+__host__ __device__ inline int big_parts(int n, int P) { return n > 0 ? n / P : 0; }
+__host__ __device__ inline int small_parts(int n, int P) { return n <= 0 || n % P != 0 ? 1 : 0; }
 __host__ __device__ inline int parts_of(int n, int P) { return big_parts(n, P) + small_parts(n, P); }
 
 // Merge the partials of one (query row, query head):
