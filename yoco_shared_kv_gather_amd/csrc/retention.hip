@@ -157,9 +157,13 @@ __device__ __forceinline__ void request_rows(const RetArgs& a, int r, int& start
   end = min(max(a.cu[r + 1], start), a.num_tokens);
 }
 
-__device__ __forceinline__ int num_segments(int rows) { return (rows + kSegRows - 1) / kSegRows; }
+// Segments of a request of `rows` rows; a request without rows has one,
+// empty, segment, so every request has exactly one last segment.
+__device__ __forceinline__ int num_segments(int rows) { return rows > 0 ? (rows + kSegRows - 1) / kSegRows : 1; }
 
-// pref[r] = number of segments of requests 0..r-1 (pref[R] = total), in LDS.
+// pref[r] = number of segments other than the last of requests 0..r-1
+// (pref[R] = their total), in LDS.  Request r's segments are numbered
+// pref[r] + r .. pref[r] + r + nseg - 1 in the workspace.
 __device__ void segment_prefix(const RetArgs& a, int32_t* pref) {
   __shared__ int32_t wsum[kWaves];
   const int tid = threadIdx.x;
@@ -172,7 +176,7 @@ __device__ void segment_prefix(const RetArgs& a, int32_t* pref) {
   auto segs = [&](int r) {
     int b, e;
     request_rows(a, r, b, e);
-    return num_segments(e - b);
+    return num_segments(e - b) - 1;
   };
   int local = 0;
   for (int r = lo; r < hi; ++r) local += segs(r);
@@ -194,8 +198,8 @@ __device__ void segment_prefix(const RetArgs& a, int32_t* pref) {
   __syncthreads();
 }
 
-// The request whose segments hold global segment index seg: largest r with
-// pref[r] <= seg (seg < pref[R]).
+// The request whose segments other than the last hold index seg: largest r
+// with pref[r] <= seg (seg < pref[R]).
 __device__ __forceinline__ int segment_owner(const int32_t* pref, int R, int seg) {
   int lo = 0, hi = R - 1;
   while (lo < hi) {
@@ -237,18 +241,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     request_rows(a, r, start, end);
   } else {
     segment_prefix(a, sm.u.pref);
-    seg = item;
-    // the workspace holds gridDim.x / H segments, enough whenever the offsets
+    // Workgroups take every request's segments other than the last (whole
+    // kSegRows-row runs) first, then the last segment of each request (the
+    // short ones, and one-row decodes), so the launch ends on short work.
+    // The workspace holds gridDim.x / H segments, enough whenever the offsets
     // are non-decreasing; overlapping requests could need more: then nothing
-    // is computed rather than anything written past the workspace
-    const int total = sm.u.pref[a.num_reqs];
-    if (seg >= total || total > static_cast<int>(gridDim.x / H)) return;
-    r = segment_owner(sm.u.pref, a.num_reqs, seg);
-    const int first = sm.u.pref[r];
+    // is computed rather than anything written past the workspace.
+    const int inner = sm.u.pref[a.num_reqs];
+    const int total = inner + a.num_reqs;
+    if (item >= total || total > static_cast<int>(gridDim.x / H)) return;
+    r = item < inner ? segment_owner(sm.u.pref, a.num_reqs, item) : item - inner;
     int rb, re;
     request_rows(a, r, rb, re);
     nseg = num_segments(re - rb);
-    j = seg - first;
+    j = item < inner ? item - sm.u.pref[r] : nseg - 1;
+    seg = sm.u.pref[r] + r + j;
     if (kMode == kSegState && j == nseg - 1) return;   // the last segment's contribution is not needed
     start = rb + j * kSegRows;
     end = min(start + kSegRows, re);
