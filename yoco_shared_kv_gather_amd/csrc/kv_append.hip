@@ -182,15 +182,16 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)
 #pragma unroll
     for (int i = 0; i < kAP; ++i) {
       *reinterpret_cast<uint4*>(&as[(rbase + kRp * i) * kLdsStride + kc * 8]) = r.a[i];
-      if (real) {
-        const uint32_t* u = reinterpret_cast<const uint32_t*>(&r.a[i]);
+      // a repeated tile adds nothing (a select, not a branch: the stores,
+      // loads and products of a half-iteration stay one block the
+      // scheduler can interleave)
+      const uint32_t* u = reinterpret_cast<const uint32_t*>(&r.a[i]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float lo = bf16_lo(u[e]);
-          const float hi = bf16_hi(u[e]);
-          sumsq[i] = fmaf(lo, lo, sumsq[i]);
-          sumsq[i] = fmaf(hi, hi, sumsq[i]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const float lo = real ? bf16_lo(u[e]) : 0.0f;
+        const float hi = real ? bf16_hi(u[e]) : 0.0f;
+        sumsq[i] = fmaf(lo, lo, sumsq[i]);
+        sumsq[i] = fmaf(hi, hi, sumsq[i]);
       }
     }
 #pragma unroll
@@ -226,27 +227,44 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)
   };
 
   // Tile kt is in LDS stage kt&1 while tiles kt+1 and kt+2 are in flight in
-  // the register sets (tile j in set j&1).  (Staging every tile without
-  // branches made the waits exact but the loop slower: 1083 vs 1056 us on
-  // 81k tokens.)
-  // Past the last K tile the loads repeat the last one (never stored): every
-  // iteration issues the same loads in the same order, so the wait before a
-  // set is staged covers that set only, not the one loaded after it.
+  // the register sets (tile j in set j&1).  Past the last K tile the loads
+  // repeat the last one: every iteration issues the same loads in the same
+  // order, so the wait before a set is staged covers that set only, not the
+  // one loaded after it.
   auto kofs = [&](int kt) { return min(kt, ktiles - 1) * kBK; };
   load_tile(r0, 0);
   load_tile(r1, kofs(1));
   store_tile(r0, 0, true);
   load_tile(r0, kofs(2));
   __syncthreads();
+  // hidden is a multiple of 64, so ktiles is even and both halves of every
+  // iteration stage a real tile, except the last half, which stages a repeat
+  // of the last tile into stage 0 (never read, its squares not added).  A
+  // half is one branch-free block, ordered: the fragment reads, then the 32
+  // products with the next tile's LDS stores and global loads spread
+  // between them (81k tokens: 1050 -> 950 us; spreading the fragment reads
+  // too, which keeps the stores behind the last read, 1014 us).
+  static_assert(4 * (kAP + kBP) <= 32, "one store and one load per four products");
+  auto interleave = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);   // fragment reads
+#pragma unroll
+    for (int g = 0; g < kAP + kBP; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // products
+      __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS store
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 32 - 4 * (kAP + kBP), 0);
+  };
   for (int kt = 0; kt < ktiles; kt += 2) {
     mma(0);
-    if (kt + 1 < ktiles) store_tile(r1, 1, true);
+    store_tile(r1, 1, true);
     load_tile(r1, kofs(kt + 3));
+    interleave();
     __syncthreads();
-    if (kt + 1 >= ktiles) break;
     mma(1);
-    if (kt + 2 < ktiles) store_tile(r0, 0, true);
+    store_tile(r0, 0, kt + 2 < ktiles);
     load_tile(r0, kofs(kt + 4));
+    interleave();
     __syncthreads();
   }
 
