@@ -139,6 +139,50 @@ def test_append_fp8_head_dims_tiled(hkv, d):
     _check_append_fp8(meta, 0)
 
 
+@pytest.mark.parametrize("num_tokens", [40, 150])
+def test_append_fp8_special_rows(num_tokens):
+    """Activation rows holding NaN or inf project to non-finite K/V rows:
+    every code of such a (token, KV head) row is the NaN code 0x7F and its
+    scale is NaN; a row of zeros projects to zeros: zero codes, scale 0.  At
+    most 64 tokens the rows go through the quantizing scatter, beyond that the
+    tiled GEMM quantizes them in its epilogue; both against the oracle."""
+    geom = synth.custom_geometry("bf16", 4, 2, 128, 16, hidden=512)
+    lens = np.random.default_rng(num_tokens).integers(1, 60, size=num_tokens)
+    meta = synth.make_custom_metadata(geom, lens, tag=80)
+    say(f"kv_append_fp8 special rows: {meta.num_tokens} tokens")
+    d = dev()
+    x, w_rms, w_k, w_v = synth.make_append_inputs(meta, d, rms_weight="random")
+    nan_t, inf_t, zero_t = 3, 5, 7
+    x[nan_t, 17] = float("nan")
+    x[inf_t, 300] = float("inf")
+    x[zero_t] = 0
+    shape = (meta.num_blocks, geom.num_kv_heads, geom.block_size, geom.head_dim)
+    kc = torch.full(shape, 0x5A, dtype=torch.uint8, device=d)
+    vc = kc.clone()
+    ks = torch.full(shape[:-1], 7.0, dtype=torch.float32, device=d)
+    vs = ks.clone()
+    yb.kv_append_fp8(x, w_rms, 1e-6, w_k, w_v, torch.from_numpy(meta.slot_mapping).to(d), kc, vc, ks, vs)
+    torch.cuda.synchronize()
+    tokens = [nan_t, inf_t, zero_t, 0, num_tokens - 1]
+    _, _, (ck, sk), (cv, sv), _, _ = oracle.kv_append_fp8(host(x)[tokens], host(w_rms), 1e-6, host(w_k), host(w_v),
+                                                       meta.slot_mapping[tokens], geom.num_kv_heads, geom.head_dim)
+    kq, vq = kc.cpu().numpy(), vc.cpu().numpy()
+    ksn, vsn = ks.cpu().numpy(), vs.cpu().numpy()
+    bs = geom.block_size
+    for i, t in enumerate(tokens):
+        blk, off = divmod(int(meta.slot_mapping[t]), bs)
+        for codes, scales, rc, rs in ((kq, ksn, ck, sk), (vq, vsn, cv, sv)):
+            got_c, got_s = codes[blk, :, off], scales[blk, :, off]
+            if t in (nan_t, inf_t):
+                assert (got_c == 0x7F).all() and np.isnan(got_s).all()
+                assert (rc[i] == 0x7F).all() and not np.isfinite(rs[i]).any()
+            elif t == zero_t:
+                assert (got_c == 0).all() and (got_s == 0).all()
+                assert (rc[i] == 0).all() and (rs[i] == 0).all()
+            else:
+                assert np.isfinite(got_s).all() and (got_s > 0).all()
+
+
 def _check_append_fp8(meta, sample):
     geom = meta.geom
     d = dev()
