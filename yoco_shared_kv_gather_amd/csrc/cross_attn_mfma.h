@@ -26,7 +26,9 @@
 //
 // The schedule, work items, partials and the merge kernel are those of the
 // VALU kernel; the item pipeline is simpler (the next item is fetched at the
-// start of the current one, rows are double-buffered within an item).
+// start of the current one and its block-table slice and queries are loaded
+// into registers while the current one streams; rows are double-buffered
+// within an item).
 
 #pragma once
 
@@ -402,32 +404,61 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
     }
   };
 
+  // ---- an item's block-table slice and query vectors: loaded into
+  // registers one item ahead (while the previous item streams), stored to LDS
+  // when the item starts.  Indices are clamped into range so the loads need
+  // no branch; what they stand in for is masked at the store.
+  constexpr int kTblPer = kMaxSliceBlocks / kThreads;
+  constexpr int kQChunks = 16 * (D / 8);                 // 16-byte chunks of the 16 query vectors
+  constexpr int kQPer = (kQChunks + kThreads - 1) / kThreads;
+  static_assert(kMaxSliceBlocks % kThreads == 0, "slice staging");
+  int32_t st_tbl[kTblPer];
+  uint4 st_q[kQPer];
+  auto stage_load = [&](const Item& it) {
+    if (it.num_blk > 0) {
+      const int32_t* table = a.block_table + static_cast<int64_t>(it.r) * a.max_blocks + it.first_blk;
+#pragma unroll
+      for (int k = 0; k < kTblPer; ++k) st_tbl[k] = table[min(tid + kThreads * k, it.num_blk - 1)];
+    }
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+      const int i = min(tid + kThreads * k, kQChunks - 1);
+      const int v = min(i / (D / 8), VG - 1);
+      const int c = i % (D / 8);
+      const int qi = v / G;
+      const int h = v - qi * G;
+      const int qrow = kVar ? it.row0 + min(qi, max(it.nq - 1, 0)) : it.r;
+      st_q[k] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
+                                                ((static_cast<int64_t>(qrow) * a.num_q_heads + it.g * G + h) * D +
+                                                 c * 8) * 2);
+    }
+  };
+  auto stage_store = [&](const Item& it) {
+#pragma unroll
+    for (int k = 0; k < kTblPer; ++k) {
+      const int i = tid + kThreads * k;
+      if (i < it.num_blk) sm.blocks[i] = valid_block(st_tbl[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < kQPer; ++k) {
+      const int i = tid + kThreads * k;
+      if (i < kQChunks) {
+        const int v = i / (D / 8);
+        *reinterpret_cast<uint4*>(&sm.q[v][(i % (D / 8)) * 8]) = v < VG ? st_q[k] : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+
   // ---- items
   Item cur = item_at(blockIdx.x);
+  if (cur.valid) stage_load(cur);
   while (cur.valid) {
     // next item now (the queue counter sits on its own line)
     if (tid == 0) sm.next = gridDim.x + atomicAdd(fetch_ctr, 1u);
-    // stage the block-table slice and the query vectors
-    {
-      const int32_t* table = a.block_table + static_cast<int64_t>(cur.r) * a.max_blocks + cur.first_blk;
-      for (int i = tid; i < cur.num_blk; i += kThreads) sm.blocks[i] = valid_block(table[i]);
-      for (int i = tid; i < 16 * (D / 8); i += kThreads) {
-        const int v = i / (D / 8);
-        const int c = i - v * (D / 8);
-        uint4 val = make_uint4(0u, 0u, 0u, 0u);
-        if (v < VG) {
-          const int qi = v / G;
-          const int h = v - qi * G;
-          const int qrow = kVar ? cur.row0 + min(qi, max(cur.nq - 1, 0)) : cur.r;
-          val = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
-                                                ((static_cast<int64_t>(qrow) * a.num_q_heads + cur.g * G + h) * D +
-                                                 c * 8) * 2);
-        }
-        *reinterpret_cast<uint4*>(&sm.q[v][c * 8]) = val;
-      }
-    }
+    stage_store(cur);
     __syncthreads();
     const Item nxt = item_at(static_cast<uint32_t>(uniform(static_cast<int>(sm.next))));
+    if (nxt.valid) stage_load(nxt);
 
     if (cur.num_blk > 0) {
 #pragma unroll
