@@ -227,3 +227,59 @@ def test_gated_retention_workspace_follows_the_schedule():
     # more requests than a segmented launch schedules: one run per request
     assert yb.gated_retention_workspace_size(5000, 4096, 4, 64, 0) == 0
     assert yb.gated_retention_workspace_size(-1, 8, 4, 128, 0) == -1
+
+
+def test_fp8_append_workspace_follows_the_path():
+    # the tiled GEMM (bf16, more than 64 tokens) quantizes in its epilogue:
+    # only the folded weights; the few-token and fp32 paths add fp32 rows
+    fold = yb.kv_append_workspace_size(yb.DTYPE_BF16, 3072, 8, 128)
+    rup = -(-fold // 256) * 256
+    rows = lambda t: t * 2 * 8 * 128 * 4
+    assert yb.kv_append_fp8_workspace_size(yb.DTYPE_BF16, 81000, 3072, 8, 128) == rup
+    assert yb.kv_append_fp8_workspace_size(yb.DTYPE_BF16, 64, 3072, 8, 128) == rup + rows(64)
+    assert yb.kv_append_fp8_workspace_size(yb.DTYPE_BF16, 65, 3072, 8, 128) == rup
+    assert yb.kv_append_fp8_workspace_size(yb.DTYPE_F32, 100, 256, 1, 64) == 100 * 2 * 64 * 4
+    assert yb.kv_append_fp8_workspace_size(yb.DTYPE_BF16, -1, 3072, 8, 128) == -1
+
+
+def _append_fp8(**kw):
+    args = dict(dtype=1, x=FAKE, T=100, hidden=256, w=FAKE, eps=1e-6, wk=FAKE, wv=FAKE, slots=FAKE, k=FAKE, v=FAKE,
+                ks=FAKE, vs=FAKE, nb=8, hkv=2, bs=16, d=128, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return yb.lib().yoco_kv_append_fp8(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=FAKE + 4), yb.YOCO_ERR_INVALID_ARGUMENT),                # caches 16-byte aligned
+    (dict(vs=FAKE + 2), yb.YOCO_ERR_INVALID_ARGUMENT),               # scales 4-byte aligned
+    (dict(ks=None), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(ws_bytes=16), yb.YOCO_ERR_WORKSPACE_TOO_SMALL),
+    (dict(d=96), yb.YOCO_ERR_UNSUPPORTED),
+    (dict(dtype=7), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(T=-1), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(T=0, ws=None, ws_bytes=1 << 20), yb.YOCO_OK),              # nothing to do
+])
+def test_append_fp8_rejects(kw, status):
+    assert _append_fp8(**kw) == status
+
+
+def _scatter(**kw):
+    args = dict(src=yb.DTYPE_F32, k_rows=FAKE, v_rows=FAKE, T=5, slots=FAKE, cache=yb.DTYPE_FP8_E4M3, k=FAKE,
+                v=FAKE, ks=FAKE, vs=FAKE, nb=8, hkv=2, bs=16, d=128, stream=None)
+    args.update(kw)
+    return yb.lib().yoco_kv_scatter(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=yb.DTYPE_FP8_E4M3), yb.YOCO_ERR_INVALID_ARGUMENT),     # rows are fp32 or bf16
+    (dict(cache=yb.DTYPE_BF16), yb.YOCO_ERR_INVALID_ARGUMENT),       # copy only into the same dtype
+    (dict(ks=None), yb.YOCO_ERR_INVALID_ARGUMENT),                   # an FP8 cache needs scales
+    (dict(cache=yb.DTYPE_F32), yb.YOCO_ERR_INVALID_ARGUMENT),        # a copy takes none
+    (dict(k_rows=FAKE + 8), yb.YOCO_ERR_INVALID_ARGUMENT),           # 16-byte alignment
+    (dict(d=80), yb.YOCO_ERR_UNSUPPORTED),
+    (dict(bs=24), yb.YOCO_ERR_UNSUPPORTED),
+    (dict(nb=0), yb.YOCO_ERR_INVALID_ARGUMENT),
+    (dict(T=0), yb.YOCO_OK),
+])
+def test_scatter_rejects(kw, status):
+    assert _scatter(**kw) == status
