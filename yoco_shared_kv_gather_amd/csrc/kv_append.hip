@@ -25,11 +25,13 @@
 //
 // 8-bit cache ("KV cache memory systems", section "Quantized cache changes
 // attention inputs"; "YOCO_论文与推理数据流详解" §18.2: quantize the shared
-// K/V once and let every cross layer reuse it): the same kernels write each
-// token's fp32 K^/V^ row to a workspace instead of the cache, and a
-// quantizing scatter stores FP8 E4M3 codes with one fp32 scale per (token,
-// KV head), s = max|x| / 448, code = E4M3(x / s) rounded to nearest even.
-// That scatter is also the public yoco_kv_scatter (rows computed elsewhere).
+// K/V once and let every cross layer reuse it): FP8 E4M3 codes with one fp32
+// scale per (token, KV head), s = max|x| / 448, code = E4M3(x / s) rounded to
+// nearest even, both divisions in fp32 on the fp32 projection.  The tiled
+// GEMM quantizes in its epilogue; the few-token and fp32 kernels write each
+// token's fp32 K^/V^ row to a workspace, and a quantizing scatter stores the
+// codes.  That scatter is also the public yoco_kv_scatter (rows computed
+// elsewhere).
 
 #include <cmath>
 
