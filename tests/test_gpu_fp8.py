@@ -183,6 +183,18 @@ def test_append_fp8_special_rows(num_tokens):
                 assert np.isfinite(got_s).all() and (got_s > 0).all()
 
 
+@pytest.mark.parametrize("num_tokens", [1, 10, 130])
+def test_append_fp8_hidden_not_multiple_of_256(num_tokens):
+    """hidden 320 (a multiple of 64 but not of 256) sends even a single token
+    through the tiled GEMM: a 128-token tile of mostly repeated rows,
+    quantized in its epilogue."""
+    geom = synth.custom_geometry("bf16", 4, 2, 128, 16, hidden=320)
+    lens = np.random.default_rng(num_tokens + 5).integers(1, 40, size=num_tokens)
+    meta = synth.make_custom_metadata(geom, lens, tag=90)
+    say(f"kv_append_fp8: {meta.num_tokens} tokens, hidden 320 -> 2 x 128")
+    _check_append_fp8(meta, 0)
+
+
 def _check_append_fp8(meta, sample):
     geom = meta.geom
     d = dev()

@@ -117,3 +117,33 @@ def test_append_token_counts_both_paths(num_tokens):
     torch.cuda.synchronize()
     _untouched_equal(w, k0, v0)
     _check_rows(w, k0, v0, np.arange(num_tokens), "bf16")
+
+
+@pytest.mark.parametrize("num_tokens", [1, 10, 130])
+def test_append_hidden_not_multiple_of_256(num_tokens):
+    """hidden 320 (a multiple of 64 but not of 256): every token count goes
+    through the tiled GEMM, down to one token in a 128-token tile."""
+    from tests.gpu_helpers import dev
+    geom = synth.custom_geometry("bf16", 4, 2, 128, 16, hidden=320)
+    lens = np.random.default_rng(num_tokens + 7).integers(1, 40, size=num_tokens)
+    meta = synth.make_custom_metadata(geom, lens, tag=91)
+    say(f"kv_append: {meta.num_tokens} tokens, hidden 320 -> 2 x 128")
+    d = dev()
+    x, w_rms, w_k, w_v = synth.make_append_inputs(meta, d, rms_weight="random")
+    shape = (meta.num_blocks, geom.num_kv_heads, geom.block_size, geom.head_dim)
+    k = torch.full(shape, float("nan"), dtype=torch.bfloat16, device=d)
+    v = k.clone()
+    slots = torch.from_numpy(meta.slot_mapping).to(d)
+    yb.kv_append(x, w_rms, EPS, w_k, w_v, slots, k, v)
+    torch.cuda.synchronize()
+    kref, vref, kb, vb = oracle.kv_project(host(x), host(w_rms), EPS, host(w_k), host(w_v),
+                                           geom.num_kv_heads, geom.head_dim)
+    bs = geom.block_size
+    for t, s in enumerate(meta.slot_mapping):
+        for cache, ref, bound in ((k, kref[t], kb[t]), (v, vref[t], vb[t])):
+            got = host(cache[s // bs, :, s % bs, :]).astype(np.float64)
+            assert (np.abs(got - ref) <= append_tolerance(ref, bound, geom.hidden, "bf16")).all()
+    written = torch.zeros(meta.num_blocks * bs, dtype=torch.bool, device=d)
+    written[slots.long()] = True
+    untouched = ~written.view(meta.num_blocks, 1, bs, 1).expand_as(k)
+    assert torch.isnan(k[untouched].float()).all() and torch.isnan(v[untouched].float()).all()
