@@ -359,7 +359,7 @@ def main():
         copy_calibration(args.copy_calibration)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the hot path runs on a single MI355X).", file=sys.stderr)
         sys.exit(2)
     if args.retention:

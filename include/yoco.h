@@ -67,7 +67,7 @@ extern "C" {
 typedef enum yoco_status {
   YOCO_OK = 0,
   YOCO_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, inconsistent shapes */
-  YOCO_ERR_UNSUPPORTED = 2,        /* a valid shape this build has no kernel for */
+  YOCO_ERR_UNSUPPORTED = 2,        /* a valid shape the library has no kernel for */
   YOCO_ERR_WORKSPACE_TOO_SMALL = 3,
   YOCO_ERR_HIP = 4                 /* the HIP runtime refused a launch */
 } yoco_status_t;
