@@ -3,7 +3,6 @@
 from .yoco_oracle import (  # noqa: F401
     attention_one_query,
     cross_attention,
-    cross_attention_group,
     cross_attention_varlen,
     cross_metadata,
     gather_rows,

@@ -45,7 +45,6 @@ __all__ = [
     "logical_kv",
     "attention_one_query",
     "cross_attention",
-    "cross_attention_group",
     "rms_norm",
     "kv_project",
     "kv_append",
@@ -148,16 +147,6 @@ def cross_attention(q, k_cache, v_cache, block_table, seq_lens, scale: float):
             g = h // group
             out[r, h] = attention_one_query(q[r, h], keys[:, g, :], values[:, g, :], scale)
     return out
-
-
-def cross_attention_group(q_heads, keys, values, scale: float) -> np.ndarray:
-    """Attention of the query heads of one KV group over that group's K̂/V̂.
-
-    ``q_heads`` is ``[G][D]``, ``keys``/``values`` are ``[n][D]`` (already in
-    logical order).  Used to check sampled outputs at full size, where the
-    caller fetches one (request, KV head) slice at a time.
-    """
-    return np.stack([attention_one_query(qh, keys, values, scale) for qh in q_heads])
 
 
 # ---------------------------------------------------------------------------

@@ -604,10 +604,132 @@ def check_kv_scatter(scatter):
     assert changed.sum() == 2
 
 
+def check_append_fp8_rounding(append_fp8):
+    """The 8-bit append quantizes the projection after one rounding to fp32
+    (the precision the kernel decides each code in): with x a row of ones and
+    eps = 0, xhat is exactly the RMS weight, and unit-vector weight rows copy
+    chosen entries of it into K and V.  The entries are built so that the
+    fp32-rounded value and the exact value lie on opposite sides of an E4M3
+    rounding midpoint (or a bf16 rounding moves the value onto one).  The
+    scale is the power of two 2^-3 (the largest entry is 448 * 2^-3), so every
+    quotient is exact and the expected codes are hand-worked closed forms;
+    torch's float8_e4m3fn conversion of the fp32 quotient (library routine)
+    must agree with them and with every other code."""
+    e = 2.0 ** -3
+    entries = np.array([
+        448.0 * e,                              # the largest: code 0x7E, scale 2^-3
+        (1.0625 + 2.0 ** -26) * e,              # fp32 -> midpoint 1 + 1/16 -> even 1.0 (0x38); exact -> 1.125
+        -(1.1875 - 2.0 ** -26) * e,             # fp32 -> midpoint 1 + 3/16 -> even -1.25 (0xBA); exact -> -1.125
+        (1.5 - 2.0 ** -26) * 2.0 ** -9 * e,     # fp32 -> subnormal midpoint 1.5 * 2^-9 -> 2 * 2^-9 (0x02); exact -> 0x01
+        (1.0625 + 2.0 ** -9) * e,               # kept by fp32 -> 1.125 (0x39); a bf16 rounding -> 1.0625 -> 0x38
+        0.0,
+        2.3 * e,
+        -300.0 * e,
+    ])
+    hand = {0: 0x7E, 1: 0x38, 2: 0xBA, 3: 0x02, 4: 0x39, 5: 0x00}
+    hidden = len(entries)
+    x = np.ones((1, hidden))
+    wk = np.eye(hidden)                         # K = xhat
+    wv = np.eye(hidden)[::-1].copy()            # V = xhat reversed
+    k, v, (ck, sk), (cv, sv), _, _ = append_fp8(x, entries, 0.0, wk, wv, np.array([0]), 1, hidden)
+    np.testing.assert_array_equal(np.asarray(k).reshape(-1), entries)
+    np.testing.assert_array_equal(np.asarray(v).reshape(-1), entries[::-1])
+    assert np.asarray(sk).reshape(-1).tolist() == [e] and np.asarray(sv).reshape(-1).tolist() == [e]
+    k32 = torch.from_numpy(entries).to(torch.float32)
+    ref = (k32 / torch.tensor(e, dtype=torch.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    for i, code in hand.items():
+        assert ref[i] == code, (i, hex(int(ref[i])))
+    assert np.asarray(ck).reshape(-1).tolist() == ref.tolist()
+    assert np.asarray(cv).reshape(-1).tolist() == ref[::-1].tolist()
+
+
 FP8_DECODE_CHECKS = [check_e4m3_decode]
 FP8_ENCODE_CHECKS = [check_e4m3_encode]
 QUANT_CHECKS = [check_quantize_rows]
 SCATTER_CHECKS = [check_kv_scatter]
+APPEND_FP8_CHECKS = [check_append_fp8_rounding]
+
+
+# ---------------------------------------------------------------------------
+# helpers the pinned functions are built from, pinned on their own
+# ---------------------------------------------------------------------------
+
+def check_logical_kv(logical_kv):
+    """The pages' Replay figure: logical blocks 0,1,2,3 on physical pages
+    0,2,1,4 (pages 3 and 5 free) come back in logical order, the last block
+    cut at the context length; a context of 0 gives empty arrays."""
+    fx = load_golden("kv_block_table_replay.json")
+    table = np.array(fx["block_table"])
+    bs, hkv, d = 4, 2, 3
+    pages = len(fx["physical_pages"])
+    kc = np.full((pages, hkv, bs, d), np.nan)
+    vc = np.full((pages, hkv, bs, d), np.nan)
+    for logical, page in enumerate(table):
+        for off in range(bs):
+            for g in range(hkv):
+                kc[page, g, off] = 100 * logical + 10 * off + g + np.arange(d) / 8
+                vc[page, g, off] = -kc[page, g, off]
+    n = 14
+    keys, values = logical_kv(kc, vc, table, n)
+    assert keys.shape == (n, hkv, d) and values.shape == (n, hkv, d)
+    for j in range(n):
+        for g in range(hkv):
+            want = 100 * (j // bs) + 10 * (j % bs) + g + np.arange(d) / 8
+            assert np.array_equal(keys[j, g], want) and np.array_equal(values[j, g], -want)
+    k0, v0 = logical_kv(kc, vc, table, 0)
+    assert k0.shape == (0, hkv, d) and v0.shape == (0, hkv, d)
+
+
+def check_attention_one_query(attn_one):
+    """Library routine: torch SDPA in float64 for one query; closed forms: one
+    key gives its value row exactly, identical keys give the mean of the
+    values."""
+    rng = np.random.default_rng(71)
+    for n, d in [(1, 4), (9, 8), (33, 16)]:
+        q = rng.standard_normal(d)
+        keys = rng.standard_normal((n, d))
+        values = rng.standard_normal((n, d))
+        got = attn_one(q, keys, values, 0.37)
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q).reshape(1, 1, d),
+                                             torch.from_numpy(keys).reshape(1, n, d),
+                                             torch.from_numpy(values).reshape(1, n, d), scale=0.37).reshape(d)
+        np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-12)
+    values = rng.standard_normal((1, 5))
+    assert np.array_equal(attn_one(rng.standard_normal(5), rng.standard_normal((1, 5)), values, 1.0), values[0])
+    keys = np.tile(rng.standard_normal(5), (6, 1))
+    values = rng.standard_normal((6, 5))
+    np.testing.assert_allclose(attn_one(rng.standard_normal(5), keys, values, 0.5), values.mean(axis=0), atol=1e-14)
+
+
+def check_rms_norm(rms):
+    """Library routine: torch.nn.functional.rms_norm in float64; closed form:
+    a constant row c gives c / sqrt(c^2 + eps) * w."""
+    rng = np.random.default_rng(72)
+    x = rng.standard_normal((4, 10)) * rng.uniform(0.1, 9.0, size=(4, 1))
+    w = rng.uniform(0.5, 1.5, size=10)
+    for eps in (1e-6, 0.5):
+        ref = F.rms_norm(torch.from_numpy(x), (10,), torch.from_numpy(w), eps=eps).numpy()
+        np.testing.assert_allclose(rms(x, w, eps), ref, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(rms(np.full((1, 10), -2.0), w, 0.25), -2.0 / np.sqrt(4.25) * w[None, :], atol=1e-15)
+
+
+def check_query_positions(positions):
+    """The vLLM page's example: request 1 has seq_len 31 and two logits rows,
+    which sit at its last two positions, 29 and 30; more query rows than
+    context tokens put the first ones below position 0."""
+    fx = load_golden("vllm_logits_indices_example.json")["printed"]
+    assert positions(fx["seq_lens"][1], fx["num_decode_tokens"][1]) == [29, 30]
+    assert positions(fx["seq_lens"][0], 1) == [40]
+    assert positions(2, 4) == [-2, -1, 0, 1]
+    assert positions(5, 0) == []
+
+
+HELPER_CHECKS = {
+    "logical_kv": check_logical_kv,
+    "attention_one_query": check_attention_one_query,
+    "rms_norm": check_rms_norm,
+    "query_positions": check_query_positions,
+}
 
 
 # ---------------------------------------------------------------------------

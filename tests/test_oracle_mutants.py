@@ -4,6 +4,7 @@ oracle from a right one."""
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from oracle import yoco_oracle as yo
@@ -251,6 +252,37 @@ def _quant_variant(qmax=448.0, scale_from_mean=False):
     return quantize
 
 
+def _append_fp8_variant(round_projection):
+    """The 8-bit append quantizing a differently rounded projection."""
+    def append_fp8(x, rms_weight, eps, w_k, w_v, slot_mapping, num_kv_heads, head_dim):
+        k, v, bk, bv = yo.kv_project(x, rms_weight, eps, w_k, w_v, num_kv_heads, head_dim)
+        return k, v, round_projection(k), round_projection(v), bk, bv
+    return append_fp8
+
+
+def _quantize_float64(rows):
+    """Scale and quotient in float64, no fp32 rounding anywhere."""
+    rows = np.asarray(rows, dtype=np.float64)
+    scales = np.abs(rows).max(axis=-1) / 448.0
+    codes = np.zeros(rows.shape, dtype=np.uint8)
+    for idx in np.ndindex(rows.shape[:-1]):
+        if scales[idx]:
+            codes[idx] = yo.e4m3_encode(rows[idx] / scales[idx])
+    return codes, scales.astype(np.float32)
+
+
+def _quantize_bf16(rows):
+    """The projection rounded to bf16 first, then the fp32 quantizer."""
+    r = torch.from_numpy(np.asarray(rows, dtype=np.float64)).to(torch.bfloat16).to(torch.float32).numpy()
+    return yo.quantize_rows(r)
+
+
+APPEND_FP8_MUTANTS = {
+    "quantize_float64_projection": _append_fp8_variant(_quantize_float64),
+    "quantize_bf16_projection": _append_fp8_variant(_quantize_bf16),
+}
+
+
 FP8_DECODE_MUTANTS = {"bias_8": _decode_variant(bias=8), "subnormal_as_normal": _decode_variant(subnormal_as_normal=True)}
 FP8_ENCODE_MUTANTS = {"ties_up": _encode_variant(ties_up=True), "no_subnormals": _encode_variant(no_subnormals=True)}
 QUANT_MUTANTS = {"int8_range": _quant_variant(qmax=127.0), "scale_from_mean": _quant_variant(scale_from_mean=True)}
@@ -366,3 +398,42 @@ def test_retention_mutant_is_caught(name):
 
 def test_unmutated_retention_copy_passes():
     assert _fails_some(pins.RETENTION_CHECKS, _retention_variant()) == 0
+
+
+@pytest.mark.parametrize("name", sorted(APPEND_FP8_MUTANTS))
+def test_append_fp8_mutant_is_caught(name):
+    assert _fails_some(pins.APPEND_FP8_CHECKS, APPEND_FP8_MUTANTS[name]) > 0
+
+
+def test_unmutated_append_fp8_copy_passes():
+    assert _fails_some(pins.APPEND_FP8_CHECKS, _append_fp8_variant(lambda k: yo.quantize_rows(k.astype(np.float32)))) == 0
+
+
+def _helper_mutants():
+    def logical_block_offset_swapped(k_cache, v_cache, table_row, n):
+        bs = k_cache.shape[2]
+        if n == 0:
+            return yo.logical_kv(k_cache, v_cache, table_row, 0)
+        keys = [np.asarray(k_cache[table_row[j % bs], :, j // bs], float) for j in range(n)]
+        values = [np.asarray(v_cache[table_row[j % bs], :, j // bs], float) for j in range(n)]
+        return np.stack(keys), np.stack(values)
+
+    def attn_one_scale_dropped(q, keys, values, scale):
+        s = np.asarray(keys) @ np.asarray(q)
+        w = np.exp(s - s.max())
+        return (w @ values) / w.sum()
+
+    def rms_sum(x, w, eps):
+        x = np.asarray(x, float)
+        return x / np.sqrt((x * x).sum(axis=1, keepdims=True) + eps) * w
+
+    def positions_first(n, ql):
+        return list(range(ql))
+
+    return {"logical_kv": logical_block_offset_swapped, "attention_one_query": attn_one_scale_dropped, "rms_norm": rms_sum,
+            "query_positions": positions_first}
+
+
+@pytest.mark.parametrize("name", sorted(_helper_mutants()))
+def test_helper_mutant_is_caught(name):
+    assert _fails_some([pins.HELPER_CHECKS[name]], _helper_mutants()[name]) > 0

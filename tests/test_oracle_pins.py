@@ -62,6 +62,26 @@ def test_scatter_pins(check):
     check(oracle.kv_scatter)
 
 
+@pytest.mark.parametrize("check", pins.APPEND_FP8_CHECKS, ids=lambda c: c.__name__)
+def test_append_fp8_pins(check):
+    check(oracle.kv_append_fp8)
+
+
+@pytest.mark.parametrize("name", sorted(pins.HELPER_CHECKS))
+def test_helper_pins(name):
+    pins.HELPER_CHECKS[name](getattr(oracle, name))
+
+
+def test_every_exported_function_has_a_pin():
+    """Every function the oracle exports is run by at least one pin above (or
+    by the dequantize closed form below)."""
+    from oracle import yoco_oracle
+    pinned = {"cross_attention", "kv_project", "kv_append", "gather_last", "cross_attention_varlen",
+              "cross_metadata", "gather_rows", "e4m3_decode", "e4m3_encode", "quantize_rows", "kv_scatter",
+              "kv_append_fp8", "gated_retention", "dequantize_cache"} | set(pins.HELPER_CHECKS)
+    assert set(yoco_oracle.__all__) == pinned
+
+
 def test_dequantize_cache_is_code_times_scale():
     """Closed form: code 0x38 (1.0) with scale 2.5 is 2.5; 0xC0 (-2.0) with
     scale 2.5 is -5.0; scale 0 gives 0."""
