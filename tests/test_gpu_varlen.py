@@ -235,3 +235,52 @@ def test_varlen_full_size_sampled(cid, ql, window):
         err = _max_err(out[r * ql:(r + 1) * ql, g * group:(g + 1) * group], ref)
         say(f"  request {r} (ctx {n}) kv head {g}: max abs err {err:.3e}")
         assert err <= ATTN_ATOL
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("ql,window", [(3, 37), (1, 37), (4, 100), (2, 1)])
+def test_window_start_in_last_block_of_exact_pool(fp8, ql, window):
+    """A windowed item whose first block is the pool's last physical block,
+    read for every KV head (the last one included), with a pool of exactly
+    the blocks the context needs and a window start that is not 16-aligned:
+    the matrix-core kernel's stand-in tiles past the item's end stay inside
+    that block.  Checked against the oracle."""
+    say(f"window start in the last block: fp8 {fp8}, {ql} rows, window {window}")
+    hq, hkv, d, bs, n = 8, 2, 128, 16, 300
+    nb = -(-n // bs)
+    lo = max(0, n - ql - window + 1)
+    assert lo % 16 != 0
+    rng = np.random.default_rng(ql * 100 + window)
+    table = rng.permutation(nb).astype(np.int32)
+    j = int(np.where(table == nb - 1)[0][0])
+    table[j], table[lo // bs] = table[lo // bs], table[j]           # the window's first block is physical nb-1
+    assert table[lo // bs] == nb - 1
+    tail = n - (nb - 1) * bs                                        # rows used in the last logical block
+    d_ = dev()
+    if fp8:
+        shape = (nb, hkv, bs, d)
+        codes = rng.integers(0, 254, size=(2,) + shape)
+        codes = np.where(codes >= 0x7F, codes + 1, codes).astype(np.uint8)
+        scales = rng.uniform(0.002, 0.02, size=(2,) + shape[:-1]).astype(np.float32)
+        last = table[nb - 1]
+        codes[:, last, :, tail:] = 0x7F
+        scales[:, last, :, tail:] = np.nan
+        kc, vc = (torch.from_numpy(codes[i].copy()).to(d_) for i in range(2))
+        ks, vs = (torch.from_numpy(scales[i].copy()).to(d_) for i in range(2))
+        kref, vref = (oracle.dequantize_cache(codes[i], scales[i]) for i in range(2))
+    else:
+        kv = rng.standard_normal((2, nb, hkv, bs, d)).astype(np.float32)
+        kv[:, table[nb - 1], :, tail:] = np.nan
+        kc, vc = (torch.from_numpy(kv[i].copy()).to(d_).to(torch.bfloat16) for i in range(2))
+        ks = vs = None
+        kref, vref = host(kc), host(vc)
+    q = torch.from_numpy(rng.standard_normal((ql, hq, d)).astype(np.float32)).to(d_).to(torch.bfloat16)
+    qsl = np.array([0, ql], dtype=np.int32)
+    out = yb.cross_attn_varlen(q, kc, vc, _i32(table[None, :]), _i32([n]), n, query_start_loc=_i32(qsl),
+                               max_query_len=ql, window=window, partition_tokens=64, k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    ref = oracle.cross_attention_varlen(host(q), kref, vref, table[None, :], np.array([n]), qsl,
+                                        1.0 / math.sqrt(d), window)
+    err = _max_err(out, ref)
+    say(f"  max abs err {err:.3e}")
+    assert err <= ATTN_ATOL

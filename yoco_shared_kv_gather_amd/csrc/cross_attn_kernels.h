@@ -617,7 +617,8 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     for (int u = 0; u < kU; ++u) {
       const int j = it.start + iter * kIterTokens + u * kRpw + row;
       const bool in_range = j < it.end;
-      const int blk = sm.blocks[buf][((in_range ? j : it.start) >> a.bs_shift) - it.first_blk];
+      // slice entry of the row; a masked row reads entry 0 (its value is unused)
+      const int blk = sm.blocks[buf][in_range ? (j >> a.bs_shift) - it.first_blk : 0];
       rs.valid[u] = in_range && blk >= 0;
       rs.pos[u] = j;
       const int64_t off = rs.valid[u] ? (static_cast<int64_t>(blk) * a.block_stride +
@@ -658,7 +659,10 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     for (int u = 0; u < kU; ++u) {
       const int j = (to_nx ? nx.start + wave_u * kIterTokens : it.start + iter * kIterTokens) + u * kRpw + row;
       const bool in_range = j < end;
-      const int lds_blk = sm.blocks[buf][((in_range && !to_nx ? j : it.start) >> a.bs_shift) - it.first_blk];
+      // slice entry of the row in the current item; rows of the next item, and
+      // masked rows, read entry 0 instead (unused: an item without rows has
+      // first_blk 0 while its start may lie far past the slice)
+      const int lds_blk = sm.blocks[buf][in_range && !to_nx ? (j >> a.bs_shift) - it.first_blk : 0];
       const int blk = to_nx ? st_nb[u] : lds_blk;
       rs.valid[u] = in_range && blk >= 0;
       rs.pos[u] = j;

@@ -223,7 +223,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
   // block_size >= 16 every 16-key tile lies inside one cache block: one
   // block-table entry per tile gives a wave-uniform 64-bit row base, and lanes
   // add 32-bit offsets.  Keys before the item's start or past its end, and
-  // tiles in an out-of-range block (which read block 0), are masked.
+  // tiles in an out-of-range block (which read block 0), are masked.  A tile
+  // wholly past the item's end reads the 16-aligned tile that holds the
+  // item's first key instead (never the item's start itself: with a window
+  // the start is rarely 16-aligned, and 16 rows from it could cross the end
+  // of its block -- and of the cache, for the last block's last KV head).
   struct Rows {
     uint4 k[kNT][kKL];
     uint4 v[kVC];
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
       const int p0 = base + 16 * t;
-      const int in = p0 < it.end ? p0 : it.start;
+      const int in = p0 < it.end ? p0 : (it.start & ~15);
       const int blk = uniform(sm.blocks[(in >> a.bs_shift) - it.first_blk]);
       const bool ok = blk >= 0;
       rs.tmask |= ok ? (1u << t) : 0u;
