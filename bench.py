@@ -6,12 +6,18 @@ last row, then the L cross layers in order, each one yoco_cross_attn over the
 same cache (layer l walks its work items in reverse when l is odd, so a layer
 starts where the previous one ended in the last-level cache).
 
-Default workload: decode64 -- 64 decoding requests with contexts drawn from
-U{1024..8192}, bf16 cache of 2 KV heads x 256 dims in blocks of 16, 10 cross
-layers of 8 query heads, hidden 2048.  Inputs are synthetic and seeded and sit
-in HBM before timing starts.  Between steps a 1 GiB buffer is read so the
-L2s and the 256 MB last-level cache start cold each step (other model work
-would evict them); that read is outside the step's events.
+Default workload: decode32x32k -- 32 decoding requests at 32768 tokens of
+context each, bf16 cache of 8 KV heads x 128 dims in blocks of 16 (0.1% of key
+vectors scaled by 20), 16 cross layers of 32 query heads, hidden 3072; the
+largest single-GPU workload and the long-context case.  Inputs are synthetic
+and seeded and sit in HBM before timing starts.  Between steps a 1 GiB buffer
+is read so the L2s and the 256 MB last-level cache start cold each step (other
+model work would evict them); that read is outside the step's events.
+
+The CPU baseline runs the float64 oracle on the host's cores: worker
+processes (started before the GPU is touched, one BLAS thread each) each own
+a share of the (request, KV head) groups, hold those groups' K/V rows, and
+compute every layer's attention for them.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -44,7 +50,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", type=int, default=2, help="synthetic workload id (1-5); 2 = decode64")
+    p.add_argument("--workload", type=int, default=3, help="synthetic workload id (1-5); 3 = decode32x32k")
     p.add_argument("--partition-tokens", type=int, default=0, help="0 = library default")
     p.add_argument("--query-rows", type=int, default=1, help="query rows per request (decode workloads 2, 3, 5)")
     p.add_argument("--window", type=int, default=0, help="sliding window of every cross layer in tokens (0 = none)")
@@ -54,6 +60,8 @@ def parse():
                         "mixed step's rows or 64 decode tokens")
     p.add_argument("--no-flush", action="store_true", help="keep the last-level cache warm between steps")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
+    p.add_argument("--cpu-workers", type=int, default=0,
+                   help="worker processes of the CPU baseline (0 = the usable host cores, at most 16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=2024)
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -76,11 +84,137 @@ def copy_calibration(mib):
     print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
 
 
-def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s, rows_per_req=1, window=0, ks=None, vs=None):
-    """Time the float64 oracle on host cores on a bounded sample of the same
-    step: the append and gather of all scheduled tokens, then whole cross
-    layers (every request) until the time budget is spent; the per-layer
-    time is scaled to all L layers."""
+# ---------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on the host's cores
+# ---------------------------------------------------------------------------
+
+def host_cores():
+    """(os.cpu_count(), usable cores from the affinity mask)."""
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count() or 1
+    return os.cpu_count() or 1, usable
+
+
+def _oracle_worker(conn):
+    """Worker process of the CPU baseline: holds the K/V rows (or retention
+    slices) of its share of the groups and runs the oracle on them when asked.
+    One BLAS thread per worker: the workers are the parallelism."""
+    import threadpoolctl
+
+    threadpoolctl.threadpool_limits(limits=1)
+    import oracle
+
+    groups = {}
+    while True:
+        msg = conn.recv()
+        kind = msg[0]
+        if kind == "stop":
+            break
+        if kind == "load":
+            groups[msg[1]] = msg[2]
+            conn.send(None)
+        elif kind == "attn":
+            # msg[1]: list of (group key, q rows [Q][G][D]); msg[2]: (scale, window, varlen)
+            scale, window, varlen = msg[2]
+            t0 = time.perf_counter()
+            for key, qg in msg[1]:
+                n, nb, kc, vc = groups[key]
+                table = np.arange(max(nb, 1))[None, :]
+                if varlen:
+                    oracle.cross_attention_varlen(qg, kc, vc, table, np.array([n]), np.array([0, qg.shape[0]]),
+                                                  scale, window)
+                else:
+                    oracle.cross_attention(qg, kc, vc, table, np.array([n]), scale)
+            conn.send(time.perf_counter() - t0)
+        elif kind == "retention":
+            # msg[1]: group keys in order; msg[2]: seconds; each group is one (request, head) slice
+            budget = msg[2]
+            t0 = time.perf_counter()
+            done = 0
+            for key in msg[1]:
+                q, k, v, g, s, idx = groups[key]
+                oracle.gated_retention(q, k, v, g, np.array([0, q.shape[0]]), s, np.array([idx]))
+                done += q.shape[0]
+                if time.perf_counter() - t0 > budget:
+                    break
+            conn.send((done, time.perf_counter() - t0))
+
+
+class OraclePool:
+    """Worker processes for the CPU baseline.  They are forked before the
+    process touches the GPU (a fork after HIP is initialised is not safe) and
+    get their data through pipes during set-up, outside any timing."""
+
+    def __init__(self, workers):
+        import multiprocessing
+
+        ctx = multiprocessing.get_context("fork")
+        self.conns, self.procs = [], []
+        for _ in range(workers):
+            parent, child = ctx.Pipe()
+            proc = ctx.Process(target=_oracle_worker, args=(child,), daemon=True)
+            proc.start()
+            child.close()
+            self.conns.append(parent)
+            self.procs.append(proc)
+
+    @property
+    def size(self):
+        return len(self.conns)
+
+    def load(self, worker, key, value):
+        self.conns[worker].send(("load", key, value))
+        self.conns[worker].recv()
+
+    def run(self, per_worker, kind, arg):
+        """Send every worker its share at once, wait for all; returns the
+        replies (workers with an empty share are not asked)."""
+        busy = [w for w in range(self.size) if per_worker[w]]
+        for w in busy:
+            self.conns[w].send((kind, per_worker[w], arg))
+        return [self.conns[w].recv() for w in busy]
+
+    def close(self):
+        for c in self.conns:
+            try:
+                c.send(("stop",))
+            except (BrokenPipeError, OSError):
+                pass
+        for p in self.procs:
+            p.join(timeout=10)
+
+
+def start_cpu_pool(args):
+    """The CPU baseline's workers: one per usable core, at most 16 (a GPU machine
+    grants one GPU's share of its CPUs)."""
+    if args.no_cpu_baseline:
+        return None
+    _, usable = host_cores()
+    workers = args.cpu_workers if args.cpu_workers > 0 else min(usable, 16)
+    return OraclePool(max(1, workers))
+
+
+def _balance(sizes, workers):
+    """Assign items (largest first) to the least loaded worker."""
+    order = sorted(range(len(sizes)), key=lambda i: -sizes[i])
+    load = [0] * workers
+    share = [[] for _ in range(workers)]
+    for i in order:
+        w = min(range(workers), key=lambda j: load[j])
+        share[w].append(i)
+        load[w] += sizes[i]
+    return share
+
+
+def cpu_baseline(pool, meta, k, v, q, x, w_rms, w_k, w_v, budget_s, rows_per_req=1, window=0, ks=None, vs=None):
+    """Time the float64 oracle on the host's cores on a bounded sample of the
+    same step: the append and gather of all scheduled tokens (BLAS threads =
+    the pool's size), then whole cross layers over every (request, KV head)
+    group, spread over the worker processes, until the time budget is spent;
+    the per-layer time is scaled to all L layers.  For the tiny and decode64
+    workloads the same layer is also run on one thread."""
     import threadpoolctl
     import torch
 
@@ -89,33 +223,53 @@ def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s, rows_per_req=1, wi
     geom = meta.geom
     scale = 1.0 / math.sqrt(geom.head_dim)
     bs = geom.block_size
+    hkv = geom.num_kv_heads
+    group = geom.num_q_heads // hkv
     Q = rows_per_req
+    varlen = Q > 1 or window > 0 or ks is not None
+    cpu_count, usable = host_cores()
+    workers = pool.size
+    single = meta.config_id in (1, 2)
     w_host = (w_rms.float().cpu().numpy(), w_k.float().cpu().numpy(), w_v.float().cpu().numpy())
     x_host = x.float().cpu().numpy()
-    per_req = []
     # an 8-bit cache holds code * scale: the codes' values from the oracle's
-    # decoder, once for all 256 codes (setup, outside the timing)
+    # decoder, once for all 256 codes (set-up, outside the timing)
     code_value = oracle.e4m3_decode(np.arange(256, dtype=np.uint8)) if ks is not None else None
-    log(f"cpu baseline: fetching {meta.num_reqs} requests' contexts to the host")
+    keys = [(r, g) for r in range(meta.num_reqs) for g in range(hkv)]
+    sizes = [max(int(meta.seq_lens[r]), 1) for r, _ in keys]
+    share = _balance(sizes, workers)
+    owner = {}
+    for w, items in enumerate(share):
+        for i in items:
+            owner[keys[i]] = w
+    kept = {}
+    log(f"cpu baseline: handing {meta.num_reqs} requests' contexts ({len(keys)} groups) to {workers} workers")
     for r in range(meta.num_reqs):
         n = int(meta.seq_lens[r])
         nb = -(-n // bs)
-        blocks = torch.from_numpy(meta.block_table[r, :nb].astype(np.int64)).to(k.device)
+        blocks = torch.from_numpy(meta.block_table[r, :max(nb, 1)].astype(np.int64)).to(k.device)
         if ks is not None:
             kc = code_value[k.index_select(0, blocks).cpu().numpy()] * \
                 ks.index_select(0, blocks).cpu().numpy().astype(np.float64)[..., None]
             vc = code_value[v.index_select(0, blocks).cpu().numpy()] * \
                 vs.index_select(0, blocks).cpu().numpy().astype(np.float64)[..., None]
-            per_req.append((n, nb, kc, vc))
-            continue
-        per_req.append((n, nb, k.index_select(0, blocks).float().cpu().numpy(),
-                        v.index_select(0, blocks).float().cpu().numpy()))
-    with threadpoolctl.threadpool_limits(limits=1):
+        else:
+            kc = k.index_select(0, blocks).float().cpu().numpy()
+            vc = v.index_select(0, blocks).float().cpu().numpy()
+        for g in range(hkv):
+            item = (n, nb, np.ascontiguousarray(kc[:, g:g + 1]), np.ascontiguousarray(vc[:, g:g + 1]))
+            pool.load(owner[(r, g)], (r, g), item)
+            if single:
+                kept[(r, g)] = item
+        del kc, vc
+
+    def append_gather():
+        """Seconds of the step's append and gather (the 8-bit append's
+        quantizer runs element by element in Python: a sample of at most 256
+        tokens, scaled to all of them)."""
         t0 = time.perf_counter()
         append_scale = 1.0
         if ks is not None:
-            # the 8-bit append's quantizer runs element by element in Python: a
-            # sample of at most 256 tokens, scaled to all of them
             n_s = min(meta.num_tokens, 256)
             oracle.kv_append_fp8(x_host[:n_s], w_host[0], 1e-6, w_host[1], w_host[2], meta.slot_mapping[:n_s],
                                  geom.num_kv_heads, geom.head_dim)
@@ -130,35 +284,64 @@ def cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, budget_s, rows_per_req=1, wi
             oracle.gather_rows(x_host, idx)
         else:
             oracle.gather_last(x_host, meta.cu_seqlens)
-        t_other = t_append + time.perf_counter() - t0
-        log(f"cpu baseline: append + gather {t_other:.1f} s; timing cross layers")
-        layers = 0
-        t_attn = 0.0
-        while layers < geom.num_layers and (layers == 0 or t_other + t_attn < budget_s):
-            t1 = time.perf_counter()
-            qh = q[layers].float().cpu().numpy()
-            for r, (n, nb, kc, vc) in enumerate(per_req):
-                table = np.arange(max(nb, 1))[None, :]
-                if Q > 1 or window > 0 or ks is not None:
-                    oracle.cross_attention_varlen(qh[r * Q:(r + 1) * Q], kc, vc, table, np.array([n]),
-                                                  np.array([0, Q]), scale, window)
-                else:
-                    oracle.cross_attention(qh[r:r + 1], kc, vc, table, np.array([n]), scale)
-            t_attn += time.perf_counter() - t1
-            layers += 1
+        return t_append + time.perf_counter() - t0
+
+    with threadpoolctl.threadpool_limits(limits=workers):
+        t_other = append_gather()
+    log(f"cpu baseline: append + gather {t_other:.1f} s; timing cross layers on {workers} workers")
+
+    def layer_tasks(layer):
+        qh = q[layer].float().cpu().numpy()
+        per_worker = [[] for _ in range(workers)]
+        for (r, g), w in owner.items():
+            per_worker[w].append(((r, g), np.ascontiguousarray(qh[r * Q:(r + 1) * Q, g * group:(g + 1) * group])))
+        return per_worker
+
+    layers = 0
+    t_attn = 0.0
+    busiest = 0.0
+    while layers < geom.num_layers and (layers == 0 or t_other + t_attn < budget_s):
+        tasks = layer_tasks(layers)
+        t1 = time.perf_counter()
+        replies = pool.run(tasks, "attn", (scale, window, varlen))
+        t_attn += time.perf_counter() - t1
+        busiest = max(busiest, max(replies))
+        layers += 1
     step_s = t_other + geom.num_layers * t_attn / layers
-    return {
+    used = sum(1 for items in share if items)
+    result = {
         "value": round(meta.num_reqs * Q / step_s, 3),
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": used,
         "kind": "oracle",
+        "cpu_count": cpu_count,
+        "usable_cores": usable,
+        "worker_processes": used,
+        "blas_threads_per_worker": 1,
+        "blas_threads_append": workers,
         "sample": (f"append + gather of all {meta.num_tokens} tokens"
                    + (f" (8-bit append timed on {min(meta.num_tokens, 256)} tokens and scaled)" if ks is not None
                       else "")
-                   + f" and {layers} of {geom.num_layers} cross layers over all {meta.num_reqs} requests "
-                   f"({t_other + t_attn:.1f} s of CPU time, float64 numpy, BLAS limited to 1 thread); per-layer time "
-                   f"scaled to {geom.num_layers} layers"),
+                   + f", then {layers} of {geom.num_layers} cross layers over all {len(keys)} (request, KV head) "
+                   f"groups spread over {used} worker processes ({t_other + t_attn:.1f} s wall, float64 numpy); "
+                   f"per-layer wall time scaled to {geom.num_layers} layers"),
     }
+    if single:
+        with threadpoolctl.threadpool_limits(limits=1):
+            t_other1 = append_gather()
+            qh = q[0].float().cpu().numpy()
+            t0 = time.perf_counter()
+            for (r, g), (n, nb, kc, vc) in kept.items():
+                qg = qh[r * Q:(r + 1) * Q, g * group:(g + 1) * group]
+                table = np.arange(max(nb, 1))[None, :]
+                if varlen:
+                    oracle.cross_attention_varlen(qg, kc, vc, table, np.array([n]), np.array([0, Q]), scale, window)
+                else:
+                    oracle.cross_attention(qg, kc, vc, table, np.array([n]), scale)
+            t_layer1 = time.perf_counter() - t0
+        result["single_thread_value"] = round(meta.num_reqs * Q / (t_other1 + geom.num_layers * t_layer1), 3)
+        result["single_thread_sample"] = "the same append + gather and one cross layer on one thread, scaled to L"
+    return result
 
 
 def quantize_cache(meta, k, v, yb, torch):
@@ -191,40 +374,42 @@ def synth_live(meta):
 RETENTION_HEADS, RETENTION_DIM, RETENTION_LAYERS = 24, 128, 16
 
 
-def retention_cpu_baseline(layer, budget_s):
+def retention_cpu_baseline(pool, layer, budget_s):
     """The float64 oracle's recurrence on (request, head) slices of one layer,
-    longest requests first, until the budget is spent; rows x heads per
-    second, scaled to the whole pass."""
-    import oracle
-
+    spread over the worker processes (longest first on each), until the
+    budget is spent; rows x heads per second, scaled to the whole pass."""
     lens = layer["lens"]
     cu = layer["cu"]
-    order = np.argsort(-lens, kind="stable")
-    done = 0
+    keys = [(int(r), h) for r in np.argsort(-lens, kind="stable") if lens[r] > 0 for h in range(RETENTION_HEADS)]
+    share = _balance([int(lens[r]) for r, _ in keys], pool.size)
+    per_worker = []
+    for w, items in enumerate(share):
+        mine = []
+        for i in items:
+            r, h = keys[i]
+            a, b = int(cu[r]), int(cu[r + 1])
+            sl = lambda x: np.ascontiguousarray(x[a:b, h:h + 1])
+            pool.load(w, (r, h), (sl(layer["q"]), sl(layer["k"]), sl(layer["v"]), sl(layer["g"]),
+                                  np.ascontiguousarray(layer["s"][:, h:h + 1]), int(layer["idx"][r])))
+            mine.append((r, h))
+        per_worker.append(mine)
     t0 = time.perf_counter()
-    for r in order:
-        a, b = int(cu[r]), int(cu[r + 1])
-        if b == a:
-            continue
-        for h in range(RETENTION_HEADS):
-            sl = lambda x: x[a:b, h:h + 1]
-            oracle.gated_retention(sl(layer["q"]), sl(layer["k"]), sl(layer["v"]), sl(layer["g"]),
-                                   np.array([0, b - a]), layer["s"][:, h:h + 1], np.array([int(layer["idx"][r])]))
-            done += b - a
-            if time.perf_counter() - t0 > budget_s:
-                break
-        if time.perf_counter() - t0 > budget_s:
-            break
+    replies = pool.run(per_worker, "retention", budget_s)
     elapsed = time.perf_counter() - t0
+    done = sum(d for d, _ in replies)
     rate = done / elapsed                                 # rows x heads per second
     tokens_per_s = rate / (RETENTION_HEADS * RETENTION_LAYERS)
-    log(f"CPU oracle: {done} row-heads in {elapsed:.1f} s")
-    return {"value": round(tokens_per_s, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"the float64 recurrence on {done} (row, head) pairs of one layer (longest requests first, "
-                      f"{elapsed:.1f} s, one thread), scaled to {RETENTION_HEADS} heads x {RETENTION_LAYERS} layers"}
+    cpu_count, usable = host_cores()
+    log(f"CPU oracle: {done} row-heads in {elapsed:.1f} s on {len(replies)} workers")
+    return {"value": round(tokens_per_s, 3), "unit": "tokens/s", "cores": len(replies), "kind": "oracle",
+            "cpu_count": cpu_count, "usable_cores": usable, "worker_processes": len(replies),
+            "blas_threads_per_worker": 1,
+            "sample": f"the float64 recurrence on {done} (row, head) pairs of one layer ((request, head) slices "
+                      f"longest first on {len(replies)} worker processes, {elapsed:.1f} s wall), scaled to "
+                      f"{RETENTION_HEADS} heads x {RETENTION_LAYERS} layers"}
 
 
-def bench_retention(args):
+def bench_retention(args, pool):
     """One self-decoder pass: RETENTION_LAYERS gated-retention layers in order,
     each over the same rows with its own q, k, v, gates and state slots."""
     import torch
@@ -349,7 +534,7 @@ def bench_retention(args):
     }
     if host_layer is not None:
         log("timing the CPU oracle baseline")
-        result["cpu_baseline"] = retention_cpu_baseline(host_layer, args.cpu_seconds)
+        result["cpu_baseline"] = retention_cpu_baseline(pool, host_layer, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
@@ -362,9 +547,20 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the hot path runs on a single MI355X).", file=sys.stderr)
         sys.exit(2)
-    if args.retention:
-        bench_retention(args)
-        return
+    # the CPU baseline's workers are forked here, before anything touches the GPU
+    pool = start_cpu_pool(args)
+    try:
+        if args.retention:
+            bench_retention(args, pool)
+        else:
+            bench_cross(args, pool)
+    finally:
+        if pool is not None:
+            pool.close()
+
+
+def bench_cross(args, pool):
+    """One cross-decoder step of the chosen workload (module docstring)."""
 
     import torch
 
@@ -569,7 +765,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle baseline")
-        result["cpu_baseline"] = cpu_baseline(meta, k, v, q, x, w_rms, w_k, w_v, args.cpu_seconds, Q, W, ks, vs)
+        result["cpu_baseline"] = cpu_baseline(pool, meta, k, v, q, x, w_rms, w_k, w_v, args.cpu_seconds, Q, W, ks, vs)
     print(json.dumps(result), flush=True)
 
 
