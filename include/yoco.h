@@ -308,6 +308,35 @@ int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seqs, int32_t 
                         void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * yoco_cross_attn_noalloc -- yoco_cross_attn for callers that cannot allocate.
+ *
+ * For code that may not call hipMalloc (inside HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same computation,
+ * arguments and results as yoco_cross_attn, but the workspace is a static
+ * device array of YOCO_CROSS_ATTN_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library, one per GPU the library runs on, held until the process ends.
+ * The call allocates nothing.  Its first call on a device looks up that
+ * device's array and clears its work-queue counters with a small kernel on
+ * `stream`; every call leaves them zero.
+ *
+ * All calls on one GPU share that GPU's array: calls that may overlap on one
+ * GPU (different streams, or host threads without ordering) race and must
+ * not be issued; use yoco_cross_attn with separate workspaces for those.
+ *
+ * Errors: as yoco_cross_attn; YOCO_ERR_WORKSPACE_TOO_SMALL when the call
+ * needs more than YOCO_CROSS_ATTN_NOALLOC_SCRATCH_BYTES of workspace
+ * (yoco_cross_attn_workspace_size() for the same arguments); YOCO_ERR_HIP
+ * when the array's device address cannot be looked up.
+ */
+#define YOCO_CROSS_ATTN_NOALLOC_SCRATCH_BYTES (32LL * 1024 * 1024)
+int32_t yoco_cross_attn_noalloc(int32_t dtype, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                const void* k_cache, const void* v_cache, int32_t num_blocks,
+                                int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                                int32_t partition_tokens, uint32_t flags, float* out, void* stream);
+
+/*
  * yoco_gather_logits -- the rows of the logits positions, and the
  * cross-decoder's query offsets rebuilt from them.
  *

@@ -50,6 +50,8 @@ SIGNATURES = {
     "yoco_cross_attn_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "yoco_cross_attn": (_i32, [_i32, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _f32,
                                _i32, _u32, _vp, _vp, _i64, _vp]),
+    "yoco_cross_attn_noalloc": (_i32, [_i32, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32,
+                                       _f32, _i32, _u32, _vp, _vp]),
     "yoco_gather_logits": (_i32, [_vp, _i64, _i64, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]),
     "yoco_kv_scatter": (_i32, [_i32, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp]),
     "yoco_kv_append_fp8_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32]),
@@ -272,6 +274,27 @@ def cross_attn(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, scale=No
                                  _i32_dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale),
                                  int(partition_tokens), int(flags), _dev(out, "out"), ws_ptr, ws_bytes,
                                  _stream_handle(stream)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 32 * 1024 * 1024
+
+
+def cross_attn_noalloc(q, k_cache, v_cache, block_table, seq_lens, max_seq_len, out, scale=None, partition_tokens=0,
+                       flags=0, stream=None):
+    """yoco_cross_attn with the library's static scratch as workspace (no
+    allocation by the library; `out` is the caller's).  Calls that overlap
+    on one GPU race."""
+    num_seqs, num_q_heads, head_dim = q.shape
+    num_blocks, num_kv_heads, block_size, _ = k_cache.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    code = _dtype_code(k_cache)
+    _check(lib().yoco_cross_attn_noalloc(code, _dev(q, "q"), num_seqs, num_q_heads, _dev(k_cache, "k_cache"),
+                                         _dev(v_cache, "v_cache"), num_blocks, num_kv_heads, block_size, head_dim,
+                                         _i32_dev(block_table, "block_table"), block_table.shape[1],
+                                         _i32_dev(seq_lens, "seq_lens"), int(max_seq_len), float(scale),
+                                         int(partition_tokens), int(flags), _dev(out, "out"), _stream_handle(stream)))
     return out
 
 

@@ -326,6 +326,84 @@ int32_t run_cross_attn(const AttnCall& c, const char* who) {
 
 }  // namespace
 
+// ---- the entry point that allocates nothing -----------------------------------------
+//
+// yoco_cross_attn_noalloc runs yoco_cross_attn with the workspace in a static
+// device array instead of caller memory.  The array lives in every device's
+// copy of this library's code object; host code never passes its name (a
+// host-side stand-in) to a kernel, only the device address looked up once per
+// device with hipGetSymbolAddress.
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[YOCO_CROSS_ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+
+// Zero the queue counters of one device's scratch (a kernel, not a memset,
+// so that a caller's graph capture records nothing it must not replay).
+__global__ __launch_bounds__(256) void clear_queue_kernel(uint32_t* queue, int words) {
+  for (int i = threadIdx.x; i < words; i += blockDim.x) queue[i] = 0u;
+}
+
+// Device address of `scratch` on the current device, looked up (and its
+// queue counters cleared on `stream`) the first time a device is seen.
+int32_t scratch_of_current_device(void** out, hipStream_t stream, const char* who) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return yoco::fail(YOCO_ERR_HIP, "%s: no current device (or device index >= %d)", who, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || ptr == nullptr)
+      return yoco::fail(YOCO_ERR_HIP, "%s: hipGetSymbolAddress of the static scratch failed: %s", who,
+                        hipGetErrorString(err));
+    yoco::clear_launch_error();
+    hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(256), 0, stream, static_cast<uint32_t*>(ptr),
+                       static_cast<int>(kQueueHeaderBytes / 4));
+    const int32_t st = yoco::launch_result(who);
+    if (st != YOCO_OK) return st;
+    addr[dev] = ptr;
+  }
+  *out = addr[dev];
+  return YOCO_OK;
+}
+
+}  // namespace
+
+extern "C" int32_t yoco_cross_attn_noalloc(int32_t dtype, const void* q, int32_t num_seqs, int32_t num_q_heads,
+                                           const void* k_cache, const void* v_cache, int32_t num_blocks,
+                                           int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
+                                           const int32_t* block_table, int32_t max_blocks_per_seq,
+                                           const int32_t* seq_lens, int32_t max_seq_len, float scale,
+                                           int32_t partition_tokens, uint32_t flags, float* out, void* stream) {
+  const char* who = "cross_attn_noalloc";
+  // the scratch the call needs, checked before anything is looked up or launched
+  if (num_seqs >= 0 && num_q_heads > 0 && num_kv_heads > 0 && head_dim > 0 && max_seq_len >= 0 && block_size > 0 &&
+      partition_tokens >= 0) {
+    const int32_t p = resolve_partition(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens);
+    const int64_t need = workspace_layout(num_seqs, num_q_heads, head_dim, num_partitions(max_seq_len, p)).total;
+    if (need > YOCO_CROSS_ATTN_NOALLOC_SCRATCH_BYTES)
+      return yoco::fail(YOCO_ERR_WORKSPACE_TOO_SMALL,
+                        "%s: the call needs %lld bytes of scratch, the static scratch holds %lld (use "
+                        "yoco_cross_attn with a workspace)", who, (long long)need,
+                        (long long)YOCO_CROSS_ATTN_NOALLOC_SCRATCH_BYTES);
+  }
+  void* ws = nullptr;
+  if (num_seqs > 0) {
+    const int32_t st = scratch_of_current_device(&ws, static_cast<hipStream_t>(stream), who);
+    if (st != YOCO_OK) return st;
+  }
+  const AttnCall c{dtype, q, num_seqs, nullptr, num_seqs, 1, num_q_heads, k_cache, v_cache, nullptr, nullptr,
+                   num_blocks, num_kv_heads, block_size, head_dim, block_table, max_blocks_per_seq, seq_lens,
+                   max_seq_len, 0, scale, partition_tokens, flags, out, ws,
+                   ws == nullptr ? 0 : YOCO_CROSS_ATTN_NOALLOC_SCRATCH_BYTES, stream};
+  return run_cross_attn(c, who);
+}
+
 extern "C" int32_t yoco_cross_attn_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
                                                     int32_t max_seq_len, int32_t block_size,
                                                     int32_t partition_tokens) {
