@@ -59,6 +59,9 @@ def parse():
                    help="time the self-decoder's gated retention instead (16 layers, 24 heads x 128) over the "
                         "mixed step's rows or 64 decode tokens")
     p.add_argument("--no-flush", action="store_true", help="keep the last-level cache warm between steps")
+    p.add_argument("--no-alternate", action="store_true",
+                   help="every cross layer walks its work items in the same order (no last-level-cache reuse "
+                        "between consecutive layers; for comparison)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU oracle baseline")
     p.add_argument("--cpu-workers", type=int, default=0,
                    help="worker processes of the CPU baseline (0 = the usable host cores, at most 16)")
@@ -632,6 +635,11 @@ def bench_cross(args, pool):
     stream = torch.cuda.current_stream()
     L = geom.num_layers
 
+    def order(layer):
+        """Work order of a layer: odd layers reversed, so each layer starts on
+        the blocks the previous one read last (unless --no-alternate)."""
+        return 0 if args.no_alternate else (layer & 1) * yb.FLAG_REVERSE_ORDER
+
     def step(ev_layers_start=None):
         if args.fp8:
             yb.kv_append_fp8(x, w_rms, 1e-6, w_k, w_v, slots, k, v, ks, vs, workspace=ws_append, stream=stream)
@@ -648,11 +656,11 @@ def bench_cross(args, pool):
             if varlen:
                 yb.cross_attn_varlen(q[l], k, v, table, seq, meta.max_seq_len,
                                      query_start_loc=cross_qsl if Q > 1 else None, max_query_len=Q, window=W,
-                                     partition_tokens=args.partition_tokens, flags=l & 1, out=outs[l], workspace=ws,
-                                     stream=stream, k_scale=ks, v_scale=vs)
+                                     partition_tokens=args.partition_tokens, flags=order(l), out=outs[l],
+                                     workspace=ws, stream=stream, k_scale=ks, v_scale=vs)
             else:
                 yb.cross_attn(q[l], k, v, table, seq, meta.max_seq_len, partition_tokens=args.partition_tokens,
-                              flags=l & 1, out=outs[l], workspace=ws, stream=stream)
+                              flags=order(l), out=outs[l], workspace=ws, stream=stream)
 
     for i in range(args.warmup):
         if not args.no_flush:
@@ -742,6 +750,7 @@ def bench_cross(args, pool):
             "partition_tokens": part,
             "partitions_per_request": nparts,
             "llc_flushed_between_steps": not args.no_flush,
+            "alternating_layer_order": not args.no_alternate,
             "parallelism": "single GPU",
         },
         "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),

@@ -1,11 +1,16 @@
 """Turn rocprofv3 output of bench.py into a short text summary.
 
 The summary is what profiles/*.md hold: per-kernel average durations from a
-kernel trace, and HBM bytes per dispatch from FETCH_SIZE / WRITE_SIZE counter
-passes, each scaled by what the same counter reads for a plain device copy of
-known size (bench.py --copy-calibration).  It also records a hash of the HIP
-sources behind the profiled kernels, so bench.py can tell whether the measured
-traffic still describes the kernels it runs.
+kernel trace, and the bytes each dispatch moves between the L2 caches and
+memory from FETCH_SIZE / WRITE_SIZE counter passes, each scaled by what the
+same counter reads for a plain device copy of known size (bench.py
+--copy-calibration).  FETCH_SIZE counts L2 misses: bytes served by HBM or by
+the last-level (Infinity) cache in front of it, which no counter of this
+tool tells apart.  Averages cover the timed steps only: bench.py runs W
+warm-up steps and then K timed steps with the same kernels, so the last
+K / (W + K) of each kernel's dispatches are the timed ones.  The summary also
+records a hash of the HIP sources behind the profiled kernels, so bench.py can
+tell whether the measured traffic still describes the kernels it runs.
 
 Expected layout of the rocprofv3 output directory (one `-d` per pass, `-o run`
 and `-f csv`):
@@ -14,7 +19,8 @@ and `-f csv`):
     write/       --pmc WRITE_SIZE                 (bench.py)
     copy_fetch/  --pmc FETCH_SIZE                 (bench.py --copy-calibration MIB)
     copy_write/  --pmc WRITE_SIZE                 (bench.py --copy-calibration MIB)
-plus copy_fetch.json, the calibration run's stdout.
+plus copy_fetch.json, the calibration run's stdout, and trace_bench.json, the
+traced bench run's stdout (its steps and warmup pick the timed dispatches).
 
 Usage: python -m yoco_shared_kv_gather_amd.profiling OUTDIR --workload NAME --stem X --command "..." > profiles/X.md
 """
@@ -82,12 +88,34 @@ def short_name(name: str) -> str:
     return name
 
 
-def _counters(path: str) -> Dict[str, List[float]]:
-    d: Dict[str, List[float]] = collections.defaultdict(list)
+def _timed(values: List[float], steps: int, warmup: int) -> List[float]:
+    """The timed steps' share of one kernel's dispatches (in dispatch order):
+    the last steps / (warmup + steps) of them, when the count divides evenly
+    (else all of them)."""
+    total = steps + warmup
+    if steps <= 0 or total <= 0 or len(values) % total != 0:
+        return values
+    per_step = len(values) // total
+    return values[warmup * per_step:]
+
+
+def _counters(path: str, steps: int = 0, warmup: int = 0) -> Dict[str, List[float]]:
+    rows: Dict[str, List[tuple]] = collections.defaultdict(list)
     with open(path) as f:
         for row in csv.DictReader(f):
-            d[row["Kernel_Name"]].append(float(row["Counter_Value"]))
-    return d
+            rows[row["Kernel_Name"]].append((int(row.get("Dispatch_Id") or 0), float(row["Counter_Value"])))
+    return {name: _timed([v for _, v in sorted(vals)], steps, warmup) for name, vals in rows.items()}
+
+
+def _durations(path: str, steps: int, warmup: int) -> Dict[str, List[float]]:
+    """Per-dispatch durations (ns) of each kernel from the kernel trace, timed
+    steps only."""
+    rows: Dict[str, List[tuple]] = collections.defaultdict(list)
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            rows[row["Kernel_Name"]].append((int(row["Start_Timestamp"]),
+                                             int(row["End_Timestamp"]) - int(row["Start_Timestamp"])))
+    return {name: _timed([d for _, d in sorted(vals)], steps, warmup) for name, vals in rows.items()}
 
 
 def _calibration(out: str, sub: str) -> float:
@@ -100,12 +128,14 @@ def _calibration(out: str, sub: str) -> float:
 
 
 def summarize(out: str, workload: str, command: str, top: int = 10, stem: Optional[str] = None) -> str:
+    bench = json.load(open(os.path.join(out, "trace_bench.json")))
+    steps, warmup = int(bench.get("steps", 0)), int(bench.get("warmup", 0))
     stats = list(csv.DictReader(open(os.path.join(out, "trace", "run_kernel_stats.csv"))))
-    fetch = _counters(os.path.join(out, "fetch", "run_counter_collection.csv"))
-    write = _counters(os.path.join(out, "write", "run_counter_collection.csv"))
+    durations = _durations(os.path.join(out, "trace", "run_kernel_trace.csv"), steps, warmup)
+    fetch = _counters(os.path.join(out, "fetch", "run_counter_collection.csv"), steps, warmup)
+    write = _counters(os.path.join(out, "write", "run_counter_collection.csv"), steps, warmup)
     f_scale = _calibration(out, "copy_fetch")
     w_scale = _calibration(out, "copy_write")
-    bench = json.load(open(os.path.join(out, "trace_bench.json")))
     lines = [
         f"# rocprofv3 summary: {workload}",
         "",
@@ -124,22 +154,26 @@ def summarize(out: str, workload: str, command: str, top: int = 10, stem: Option
         f"bench.py line of the traced run: ms_per_step {bench['ms_per_step']}, value {bench['value']} {bench['unit']}, "
         f"roofline achieved {bench['roofline']['achieved']} {bench['roofline']['unit']} (event-timed)",
         "",
-        "| kernel | calls | avg us | HBM read MB/dispatch | HBM write MB/dispatch |",
+        f"Kernels of this library only (input generation and cache flushing omitted).  Times and bytes are "
+        f"averages over the {steps} timed steps' dispatches ({warmup} warm-up steps left out).  'L2-miss read' is "
+        f"FETCH_SIZE and 'L2 write-back' WRITE_SIZE, scaled to bytes by the plain copy: traffic between the L2s and "
+        f"memory, where a read may be served by HBM or by the last-level (Infinity) cache.",
+        "",
+        "| kernel | timed calls | avg us | L2-miss read MB/dispatch | L2 write-back MB/dispatch |",
         "|---|---:|---:|---:|---:|",
     ]
     records = {}
     ours = [row for row in stats
             if not short_name(row["Name"]).startswith(("at::", "__amd", "c10::", "rocprim::", "hipcub::"))
             and "at::native" not in row["Name"]]
-    lines.insert(len(lines) - 3, "Kernels of this library only (input generation and cache flushing omitted).")
-    lines.insert(len(lines) - 3, "")
     for row in ours[:top]:
         name = row["Name"]
-        fr = statistics.mean(fetch[name]) * f_scale if name in fetch else None
-        wr = statistics.mean(write[name]) * w_scale if name in write else None
-        avg_us = float(row["AverageNs"]) / 1e3
+        fr = statistics.mean(fetch[name]) * f_scale if fetch.get(name) else None
+        wr = statistics.mean(write[name]) * w_scale if write.get(name) else None
+        timed = durations.get(name) or []
+        avg_us = statistics.mean(timed) / 1e3 if timed else float(row["AverageNs"]) / 1e3
         records[short_name(name)] = (avg_us, fr, wr)
-        lines.append(f"| {short_name(name)} | {row['Calls']} | {avg_us:.2f} | "
+        lines.append(f"| {short_name(name)} | {len(timed)} | {avg_us:.2f} | "
                      f"{'' if fr is None else f'{fr / 1e6:.2f}'} | {'' if wr is None else f'{wr / 1e6:.2f}'} |")
     lines.append("")
     for name, (avg_us, fr, wr) in records.items():
@@ -148,8 +182,48 @@ def summarize(out: str, workload: str, command: str, top: int = 10, stem: Option
     return "\n".join(lines) + "\n"
 
 
+def per_position(out: str, kernel: str) -> List[str]:
+    """Average duration of `kernel` by its position within a step (the k-th
+    dispatch of the kernel in each timed step): for the cross layers, layer k.
+    Shows what a layer gains from the last-level cache holding blocks the
+    previous layer read (the first layer of a step starts cold)."""
+    bench = json.load(open(os.path.join(out, "trace_bench.json")))
+    steps, warmup = int(bench.get("steps", 0)), int(bench.get("warmup", 0))
+    durations = _durations(os.path.join(out, "trace", "run_kernel_trace.csv"), steps, warmup)
+    name = next((n for n in durations if short_name(n) == kernel), None)
+    if name is None or steps <= 0 or len(durations[name]) % steps != 0:
+        return []
+    per_step = len(durations[name]) // steps
+    lines = [f"Per-layer average of {kernel} over the {steps} timed steps (layer order "
+             f"{'alternating' if bench['config'].get('alternating_layer_order', True) else 'the same every layer'}):",
+             "", "| layer | avg us |", "|---:|---:|"]
+    for k in range(per_step):
+        vals = durations[name][k::per_step]
+        lines.append(f"| {k} | {statistics.mean(vals) / 1e3:.2f} |")
+    return lines + [""]
+
+
+def extra_counters(out: str, sub: str, kernels: List[str]) -> List[str]:
+    """Timed-step averages per dispatch of every counter in pass `sub` (raw
+    counter units, summed over the GPU's instances), for `kernels`."""
+    bench = json.load(open(os.path.join(out, "trace_bench.json")))
+    steps, warmup = int(bench.get("steps", 0)), int(bench.get("warmup", 0))
+    rows: Dict[tuple, List[tuple]] = collections.defaultdict(list)
+    with open(os.path.join(out, sub, "run_counter_collection.csv")) as f:
+        for row in csv.DictReader(f):
+            if short_name(row["Kernel_Name"]) in kernels:
+                rows[(short_name(row["Kernel_Name"]), row["Counter_Name"])].append(
+                    (int(row.get("Dispatch_Id") or 0), float(row["Counter_Value"])))
+    lines = [f"Counter pass `{sub}` (timed-step average per dispatch):", "", "| kernel | counter | value |",
+             "|---|---|---:|"]
+    for (kname, counter), vals in sorted(rows.items()):
+        timed = _timed([v for _, v in sorted(vals)], steps, warmup)
+        lines.append(f"| {kname} | {counter} | {statistics.mean(timed):.6g} |")
+    return lines + [""]
+
+
 def measured_traffic(stem: str, kernels: List[str]) -> Optional[dict]:
-    """HBM bytes per dispatch and average kernel time summed over `kernels`,
+    """L2-miss bytes per dispatch and average kernel time summed over `kernels`,
     from the committed profile profiles/<stem>.md -- or None if there is none
     or the sources changed since."""
     path = os.path.join(PROFILES, f"{stem}.md")
@@ -181,8 +255,18 @@ def main():
     p.add_argument("--workload", required=True)
     p.add_argument("--command", required=True, help="the commands that produced OUT (recorded in the summary)")
     p.add_argument("--stem", default=None, help="profile file name without .md (picks the sources hashed)")
+    p.add_argument("--per-position", default=None, help="kernel (short name) to break down by layer")
+    p.add_argument("--extra", action="append", default=[], metavar="SUBDIR",
+                   help="extra counter pass under OUT to tabulate for the --kernels")
+    p.add_argument("--kernels", action="append", default=[], help="short kernel names for --extra")
     args = p.parse_args()
-    print(summarize(args.out, args.workload, args.command, stem=args.stem), end="")
+    text = summarize(args.out, args.workload, args.command, stem=args.stem)
+    extra = []
+    if args.per_position:
+        extra += per_position(args.out, args.per_position)
+    for sub in args.extra:
+        extra += extra_counters(args.out, sub, args.kernels)
+    print(text + ("\n" + "\n".join(extra) if extra else ""), end="")
 
 
 if __name__ == "__main__":
