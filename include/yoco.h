@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define YOCO_ABI_VERSION 4
+#define YOCO_ABI_VERSION 5
 
 typedef enum yoco_status {
   YOCO_OK = 0,
@@ -95,6 +95,54 @@ typedef enum yoco_dtype { YOCO_DTYPE_F32 = 0, YOCO_DTYPE_BF16 = 1, YOCO_DTYPE_FP
  * before the first call with that workspace, and every call leaves them zero
  * again. */
 #define YOCO_CROSS_ATTN_QUEUE_BYTES 2048
+
+/*
+ * Precondition checks (debugging aid).
+ *
+ * The calls do not validate device-side index data (see the conventions
+ * above).  With validation on -- YOCO_VALIDATE=1 (any value but 0) in the
+ * environment when the library first asks, or yoco_set_validation(1) --
+ * every call copies its index arrays to the host, synchronises `stream`,
+ * checks them with the functions below and returns YOCO_ERR_INVALID_ARGUMENT
+ * (yoco_last_error_message() names the first violation) before launching
+ * anything.  Calls then wait for the GPU, so this is for debugging only; on
+ * a stream being captured into a graph the checks are skipped.
+ *
+ * The checks take HOST arrays and return YOCO_OK or YOCO_ERR_INVALID_ARGUMENT:
+ *   yoco_validate_offsets         cu_seqlens / query_start_loc [num_reqs+1]:
+ *                                 non-decreasing, within [0, num_rows].
+ *   yoco_validate_slots           slot_mapping [num_tokens]: every
+ *                                 non-negative slot < num_blocks*block_size,
+ *                                 no slot twice.
+ *   yoco_validate_block_table     seq_lens [num_seqs] in [0, max_seq_len] and
+ *                                 within a table row; every block the call
+ *                                 reads (from the first position any query of
+ *                                 the request sees, with query_start_loc and
+ *                                 window as in yoco_cross_attn_varlen; NULL
+ *                                 query_start_loc = one row per request) in
+ *                                 [0, num_blocks); query_start_loc checked as
+ *                                 offsets of num_rows rows.
+ *   yoco_validate_logits_indices  non-decreasing, each inside the batch's rows
+ *                                 [query_start_loc[0], query_start_loc[R]).
+ *   yoco_validate_state_indices   each slot < num_slots (negative = none), no
+ *                                 slot twice.
+ * Pages: "KV cache memory systems", section "Contiguous allocation wastes
+ * capacity" (each logical block resolves through the block table to a
+ * physical page); "You Only Cache Once, in vLLM", section "Implementation in
+ * vLLM" (the metadata: offsets of consecutive rows, per-token slots, logits
+ * positions in order).
+ */
+void yoco_set_validation(int32_t enabled);
+int32_t yoco_validation_enabled(void);
+int32_t yoco_validate_offsets(const int32_t* offsets, int32_t num_reqs, int64_t num_rows);
+int32_t yoco_validate_slots(const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks, int32_t block_size);
+int32_t yoco_validate_block_table(const int32_t* block_table, int32_t num_seqs, int32_t max_blocks_per_seq,
+                                  const int32_t* seq_lens, int32_t max_seq_len, int32_t num_blocks,
+                                  int32_t block_size, const int32_t* query_start_loc, int32_t num_rows,
+                                  int32_t window);
+int32_t yoco_validate_logits_indices(const int32_t* logits_indices, int32_t num_indices,
+                                     const int32_t* query_start_loc, int32_t num_reqs, int64_t num_tokens);
+int32_t yoco_validate_state_indices(const int32_t* state_indices, int32_t num_reqs, int32_t num_slots);
 
 /* Version of this ABI (YOCO_ABI_VERSION). */
 int32_t yoco_abi_version(void);

@@ -15,9 +15,11 @@ import threading
 from typing import Optional, Tuple
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libyoco.so")
+# YOCO_LIBRARY names another build of the same library (the host-ASan copy
+# the CPU tests load); by default the one built next to this file.
+LIB_PATH = os.environ.get("YOCO_LIBRARY") or os.path.join(PKG_DIR, "libyoco.so")
 
-ABI_VERSION = 4
+ABI_VERSION = 5
 YOCO_OK = 0
 YOCO_ERR_INVALID_ARGUMENT = 1
 YOCO_ERR_UNSUPPORTED = 2
@@ -60,6 +62,13 @@ SIGNATURES = {
     "yoco_cross_attn_varlen_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "yoco_cross_attn_varlen": (_i32, [_i32, _vp, _i32, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
                                       _i32, _vp, _i32, _vp, _i32, _i32, _f32, _i32, _u32, _vp, _vp, _i64, _vp]),
+    "yoco_set_validation": (None, [_i32]),
+    "yoco_validation_enabled": (_i32, []),
+    "yoco_validate_offsets": (_i32, [_vp, _i32, _i64]),
+    "yoco_validate_slots": (_i32, [_vp, _i32, _i32, _i32]),
+    "yoco_validate_block_table": (_i32, [_vp, _i32, _i32, _vp, _i32, _i32, _i32, _vp, _i32, _i32]),
+    "yoco_validate_logits_indices": (_i32, [_vp, _i32, _vp, _i32, _i64]),
+    "yoco_validate_state_indices": (_i32, [_vp, _i32, _i32]),
     "yoco_gated_retention_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32]),
     "yoco_gated_retention": (_i32, [_i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _i32, _vp, _i32, _vp, _vp,
                                     _vp, _i64, _vp]),

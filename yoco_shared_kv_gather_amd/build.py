@@ -23,7 +23,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libyoco.so")
 
 SOURCES = ["abi.hip", "gather_last.hip", "kv_append.hip", "cross_attn.hip", "cross_attn_f32.hip", "cross_attn_bf16.hip",
-           "cross_attn_fp8.hip", "cross_attn_mfma_bf16.hip", "cross_attn_mfma_fp8.hip", "retention.hip"]
+           "cross_attn_fp8.hip", "cross_attn_mfma_bf16.hip", "cross_attn_mfma_fp8.hip", "retention.hip", "validate.hip"]
 
 # Standalone GPU check programs the tests run (source, binary), built with the library.
 CHECKS = [(os.path.join(ROOT, "tests", "e4m3_encoder_check.hip"), os.path.join(ROOT, "tests", "e4m3_encoder_check"))]
@@ -81,5 +81,59 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     return LIB_PATH
 
 
+ASAN_DIR = os.path.join(BUILD_DIR, "asan")
+ASAN_LIB_PATH = os.path.join(ASAN_DIR, "libyoco_asan.so")
+# AddressSanitizer on the host half only: each -fsanitize applies to the host
+# compilation (device code is built exactly as in the library).
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer", "-g"]
+
+
+def asan_runtime() -> str:
+    """The AddressSanitizer runtime that must be preloaded into the process
+    that loads the instrumented library."""
+    out = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], stdout=subprocess.PIPE,
+                         stderr=subprocess.DEVNULL, text=True).stdout.strip()
+    if out and os.path.isabs(out) and os.path.exists(out):
+        return out
+    import glob
+    found = sorted(glob.glob("/opt/rocm/llvm/lib/clang/*/lib/*/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise RuntimeError("AddressSanitizer runtime not found")
+    return found[-1]
+
+
+def build_asan(jobs: int = 8) -> str:
+    """A copy of the library whose host code (argument checks, launch set-up,
+    validation) is built with AddressSanitizer, for the CPU tests of the C
+    ABI.  Rebuilt only when a source changed."""
+    import hashlib
+    os.makedirs(ASAN_DIR, exist_ok=True)
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)) + ["../../include/yoco.h"]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    h.update(" ".join(COMMON_FLAGS + ASAN_FLAGS).encode())
+    stamp = os.path.join(ASAN_DIR, "sources.sha256")
+    digest = h.hexdigest()
+    if os.path.exists(ASAN_LIB_PATH) and os.path.exists(stamp) and open(stamp).read() == digest:
+        return ASAN_LIB_PATH
+    cc = hipcc()
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(ASAN_DIR, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([cc, *COMMON_FLAGS, *ASAN_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as pool:
+        list(pool.map(_run, cmds))
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address", *objs, "-o",
+          ASAN_LIB_PATH])
+    with open(stamp, "w") as f:
+        f.write(digest)
+    return ASAN_LIB_PATH
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--asan" in sys.argv:
+        print(build_asan())
+    else:
+        print(build(verbose="-v" in sys.argv))

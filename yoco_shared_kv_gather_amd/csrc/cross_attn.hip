@@ -290,6 +290,19 @@ int32_t run_cross_attn(const AttnCall& c, const char* who) {
   a.v_scale = c.v_scale;
 
   hipStream_t s = static_cast<hipStream_t>(c.stream);
+  if (yoco_validation_enabled()) {
+    std::vector<int32_t> table, lens, qsl;
+    bool skip = false;
+    int32_t st = fetch_indices(c.block_table, int64_t{c.num_seqs} * c.max_blocks_per_seq, s, table, skip, who);
+    if (st == YOCO_OK) st = fetch_indices(c.seq_lens, c.num_seqs, s, lens, skip, who);
+    if (st == YOCO_OK && c.qsl != nullptr) st = fetch_indices(c.qsl, int64_t{c.num_seqs} + 1, s, qsl, skip, who);
+    if (st != YOCO_OK) return st;
+    if (!skip && yoco_validate_block_table(table.data(), c.num_seqs, c.max_blocks_per_seq, lens.data(),
+                                           c.max_seq_len, c.num_blocks, c.block_size,
+                                           c.qsl != nullptr ? qsl.data() : nullptr, c.num_rows,
+                                           c.window) != YOCO_OK)
+      return YOCO_ERR_INVALID_ARGUMENT;
+  }
   clear_launch_error();
   const int launched = mfma ? (f8 ? dispatch_mfma_fp8(c.head_dim, group, qpi, a, items, s)
                                    : dispatch_mfma_bf16(c.head_dim, group, qpi, a, items, s))

@@ -149,6 +149,15 @@ extern "C" int32_t yoco_gather_logits(const void* hidden, int64_t num_tokens, in
   if (!aligned16(hidden) || !aligned16(out_rows))
     return fail(YOCO_ERR_INVALID_ARGUMENT, "gather_logits: hidden and out_rows must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (yoco_validation_enabled()) {
+    std::vector<int32_t> idx, qsl;
+    bool skip = false;
+    int32_t st = fetch_indices(logits_indices, num_indices, s, idx, skip, "gather_logits");
+    if (st == YOCO_OK) st = fetch_indices(query_start_loc, int64_t{num_reqs} + 1, s, qsl, skip, "gather_logits");
+    if (st != YOCO_OK) return st;
+    if (!skip && yoco_validate_logits_indices(idx.data(), num_indices, qsl.data(), num_reqs, num_tokens) != YOCO_OK)
+      return YOCO_ERR_INVALID_ARGUMENT;
+  }
   clear_launch_error();
   if (num_indices > 0)
     hipLaunchKernelGGL(gather_rows_kernel, dim3(num_indices), dim3(kThreads), 0, s,
@@ -172,6 +181,14 @@ extern "C" int32_t yoco_gather_last(const void* hidden, int64_t num_tokens, int6
                 static_cast<long long>(row_bytes));
   if (!aligned16(hidden) || !aligned16(out))
     return fail(YOCO_ERR_INVALID_ARGUMENT, "gather_last: hidden and out must be 16-byte aligned");
+  if (yoco_validation_enabled()) {
+    std::vector<int32_t> cu;
+    bool skip = false;
+    const int32_t st = fetch_indices(cu_seqlens, int64_t{num_reqs} + 1, static_cast<hipStream_t>(stream), cu, skip,
+                                     "gather_last");
+    if (st != YOCO_OK) return st;
+    if (!skip && yoco_validate_offsets(cu.data(), num_reqs, num_tokens) != YOCO_OK) return YOCO_ERR_INVALID_ARGUMENT;
+  }
   clear_launch_error();
   hipLaunchKernelGGL(gather_last_kernel, dim3(num_reqs), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<const uint4*>(hidden), num_tokens,

@@ -783,6 +783,18 @@ int32_t scatter_impl(bool src_f32, bool quant, const void* k_src, const void* v_
                      float* v_scale, int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
                      hipStream_t s);
 
+// Validation mode only: the slots checked on a host copy (distinct, inside
+// the cache).
+int32_t validate_slot_mapping(const int32_t* slot_mapping, int32_t num_tokens, int32_t num_blocks, int32_t block_size,
+                              hipStream_t s, const char* who) {
+  if (!yoco_validation_enabled()) return YOCO_OK;
+  std::vector<int32_t> slots;
+  bool skip = false;
+  const int32_t st = yoco::fetch_indices(slot_mapping, num_tokens, s, slots, skip, who);
+  if (st != YOCO_OK || skip) return st;
+  return yoco_validate_slots(slots.data(), num_tokens, num_blocks, block_size);
+}
+
 int32_t append_impl(int32_t dtype, const void* x, int32_t num_tokens, int32_t hidden, const void* rms_weight,
                     float eps, const void* w_k, const void* w_v, const int32_t* slot_mapping, void* k_cache,
                     void* v_cache, int32_t num_blocks, int32_t num_kv_heads, int32_t block_size, int32_t head_dim,
@@ -827,6 +839,8 @@ int32_t append_impl(int32_t dtype, const void* x, int32_t num_tokens, int32_t hi
   };
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int32_t vst = validate_slot_mapping(slot_mapping, num_tokens, num_blocks, block_size, s, "kv_append");
+  if (vst != YOCO_OK) return vst;
   const int64_t num_slots = static_cast<int64_t>(num_blocks) * block_size;
   const int bs_shift = ilog2(block_size);
   clear_launch_error();
@@ -1019,6 +1033,9 @@ extern "C" int32_t yoco_kv_scatter(int32_t src_dtype, const void* k_rows, const 
     return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_scatter: null pointer");
   if (!aligned16(k_rows) || !aligned16(v_rows) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(YOCO_ERR_INVALID_ARGUMENT, "kv_scatter: rows and caches must be 16-byte aligned");
+  const int32_t vst = validate_slot_mapping(slot_mapping, num_tokens, num_blocks, block_size,
+                                            static_cast<hipStream_t>(stream), "kv_scatter");
+  if (vst != YOCO_OK) return vst;
   clear_launch_error();
   return scatter_impl(src_dtype == YOCO_DTYPE_F32, quant, k_rows, v_rows,
                       static_cast<int64_t>(num_kv_heads) * head_dim, num_tokens, slot_mapping, k_cache, v_cache,

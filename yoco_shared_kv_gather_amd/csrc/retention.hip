@@ -718,6 +718,18 @@ extern "C" int32_t yoco_gated_retention(int32_t dtype, const void* q, const void
     return fail(YOCO_ERR_WORKSPACE_TOO_SMALL, "gated_retention: workspace of %lld bytes needed (16-byte aligned)",
                 static_cast<long long>(need));
   if (num_tokens == 0) return YOCO_OK;
+  if (yoco_validation_enabled()) {
+    std::vector<int32_t> cu, idx;
+    bool skip = false;
+    int32_t st = fetch_indices(cu_seqlens, int64_t{num_reqs} + 1, static_cast<hipStream_t>(stream), cu, skip,
+                               "gated_retention");
+    if (st == YOCO_OK)
+      st = fetch_indices(state_indices, num_reqs, static_cast<hipStream_t>(stream), idx, skip, "gated_retention");
+    if (st != YOCO_OK) return st;
+    if (!skip && (yoco_validate_offsets(cu.data(), num_reqs, num_tokens) != YOCO_OK ||
+                  yoco_validate_state_indices(idx.data(), num_reqs, num_slots) != YOCO_OK))
+      return YOCO_ERR_INVALID_ARGUMENT;
+  }
 
   RetArgs args;
   args.q = static_cast<const uint16_t*>(q);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "yoco.h"
 
 namespace yoco {
@@ -18,6 +20,12 @@ inline void clear_launch_error() { (void)hipGetLastError(); }
 
 // Status of the launches enqueued since clear_launch_error().
 int32_t launch_result(const char* what);
+
+// Host copy of `count` int32 values at `src` (device or host memory), made on
+// `stream` and waited for (validation mode only).  If the stream is being
+// captured into a graph nothing may wait: `skip` is set and nothing copied.
+int32_t fetch_indices(const int32_t* src, int64_t count, hipStream_t stream, std::vector<int32_t>& dst, bool& skip,
+                      const char* who);
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool is_pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
