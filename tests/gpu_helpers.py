@@ -57,22 +57,6 @@ def oracle_attention_full(w: DeviceWorkload, layer=0):
     return oracle.cross_attention(host(w.q[layer]), host(w.k), host(w.v), w.meta.block_table, w.meta.seq_lens, scale)
 
 
-def oracle_attention_group(w: DeviceWorkload, r: int, g: int, layer=0):
-    """Oracle output of the G query heads of (request r, KV head g), fetching only
-    the physical blocks of that request's context for that KV head."""
-    meta = w.meta
-    n = int(meta.seq_lens[r])
-    bs = w.geom.block_size
-    group = w.geom.num_q_heads // w.geom.num_kv_heads
-    nb = -(-n // bs)
-    blocks = torch.from_numpy(meta.block_table[r, :nb].astype(np.int64)).to(w.k.device)
-    kc = host(w.k.index_select(0, blocks)[:, g:g + 1])          # [nb][1][bs][D]
-    vc = host(w.v.index_select(0, blocks)[:, g:g + 1])
-    q = host(w.q[layer, r:r + 1, g * group:(g + 1) * group])    # [1][G][D]
-    scale = 1.0 / math.sqrt(w.geom.head_dim)
-    return oracle.cross_attention(q, kc, vc, np.arange(max(nb, 1))[None, :], np.array([n]), scale)[0]
-
-
 def append_tolerance(ref, bound, hidden, dtype):
     """Per-element bound on |gpu - ref| for yoco_kv_append.
 

@@ -113,7 +113,7 @@ def _append_error(bound, hidden, dtype):
 
 
 @pytest.mark.parametrize("cid,size,sample", [(1, "full", 0), (2, "small", 0), (4, "small", 0), (3, "full", 0),
-                                             (4, "full", 300)])
+                                             (4, "full", 128)])
 def test_append_fp8_within_bound(cid, size, sample):
     """Every written row: |code*s - ref| <= err + half an E4M3 step of the
     stored value (2^-4 relative, s*2^-10 in the subnormal range), and the
@@ -209,9 +209,12 @@ def _check_append_fp8(meta, sample):
     torch.cuda.synchronize()
     tokens = list(range(meta.num_tokens))
     if sample:
-        # full size: a sample of tokens (the oracle's quantizer runs in Python)
-        tokens = sorted(np.random.default_rng(meta.config_id).choice(meta.num_tokens, size=sample,
-                                                                     replace=False).tolist())
+        # full size: one random row of every `sample`-row tile of the GEMM
+        # (each row covers every feature tile), plus the last row (the
+        # oracle's quantizer runs in Python)
+        rng = np.random.default_rng(meta.config_id)
+        tokens = sorted({min(t0 + int(rng.integers(0, sample)), meta.num_tokens - 1)
+                         for t0 in range(0, meta.num_tokens, sample)} | {meta.num_tokens - 1})
     k, v, _, _, bk, bv = oracle.kv_append_fp8(host(x)[tokens], host(w_rms), 1e-6, host(w_k), host(w_v),
                                              meta.slot_mapping[tokens], geom.num_kv_heads, geom.head_dim)
     kq, vq = kc.cpu().numpy(), vc.cpu().numpy()
@@ -288,6 +291,45 @@ def test_attention_fp8(hq, hkv, d, several, window, kernel):
         err = float(np.abs(got - ref).max())
         say(f"  partition {part}: max abs err {err:.3e}")
         assert err <= ATTN_ATOL
+
+
+@pytest.mark.parametrize("cid,ql", [(2, 1), (3, 1), (5, 1), (3, 4)])
+def test_attention_fp8_full_size_every_output(cid, ql):
+    """Full-size workloads over an 8-bit cache (codes and scales drawn as in
+    make_fp8_cache), ql query rows per request: every output row and head
+    against the oracle over the dequantized values (the oracle's decoder
+    applied to all 256 codes, times each row's scale)."""
+    meta = synth.make_metadata(cid, "full")
+    geom = meta.geom
+    say(f"cross_attn_varlen FP8 full size: workload {cid}, {ql} rows per request")
+    d = dev()
+    kc, ks, vc, vs = synth.make_fp8_cache(meta, d)
+    rows = meta.num_reqs * ql
+    q = synth.make_queries(meta, d, num_layers=1, rows=rows)[0]
+    qsl = (np.arange(meta.num_reqs + 1) * ql).astype(np.int32)
+    table = torch.from_numpy(meta.block_table).to(d)
+    seq = torch.from_numpy(meta.seq_lens).to(d)
+    out = yb.cross_attn_varlen(q, kc, vc, table, seq, meta.max_seq_len,
+                               query_start_loc=torch.from_numpy(qsl).to(d) if ql > 1 else None, max_query_len=ql,
+                               k_scale=ks, v_scale=vs)
+    torch.cuda.synchronize()
+    got_all = out.cpu().double().numpy()
+    value = oracle.e4m3_decode(np.arange(256, dtype=np.uint8))
+    bs = geom.block_size
+    worst = 0.0
+    for r in range(meta.num_reqs):
+        n = int(meta.seq_lens[r])
+        nb = -(-n // bs)
+        blocks = torch.from_numpy(meta.block_table[r, :nb].astype(np.int64)).to(d)
+        kd = value[kc.index_select(0, blocks).cpu().numpy()] * ks.index_select(0, blocks).cpu().numpy()[..., None]
+        vd = value[vc.index_select(0, blocks).cpu().numpy()] * vs.index_select(0, blocks).cpu().numpy()[..., None]
+        ref = oracle.cross_attention_varlen(host(q[r * ql:(r + 1) * ql]), kd, vd, np.arange(nb)[None, :],
+                                            np.array([n]), np.array([0, ql]), 1.0 / math.sqrt(geom.head_dim))
+        got = got_all[r * ql:(r + 1) * ql]
+        assert np.isfinite(got).all()
+        worst = max(worst, float(np.abs(got - ref).max()))
+        assert worst <= ATTN_ATOL, (r, worst)
+    say(f"  {rows} rows x {geom.num_q_heads} heads: max abs err {worst:.3e}")
 
 
 def test_scatter_then_attention_chain():

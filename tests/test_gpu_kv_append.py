@@ -69,8 +69,10 @@ def test_append_parity(cid, size, rms):
 
 
 def test_append_full_size_mixed_step():
-    """Workload 4 at full size (about 77K rows through the MFMA GEMM): every
-    untouched byte keeps its bits; sampled rows match the oracle."""
+    """Workload 4 at full size (67,387 rows, 64,178 of them written, through
+    the tiled MFMA GEMM): every untouched byte keeps its bits; one random row
+    of every 128-row GEMM tile (each row spans every feature tile), every
+    request's last row and the batch's last row match the oracle."""
     say("kv_append full size: workload 4")
     w = DeviceWorkload(4, "full", layers=1, with_append=True)
     k0, v0 = w.k.clone(), w.v.clone()
@@ -78,9 +80,11 @@ def test_append_full_size_mixed_step():
     torch.cuda.synchronize()
     _untouched_equal(w, k0, v0)
     rng = np.random.default_rng(4)
+    t_count = w.meta.num_tokens
+    per_tile = [min(t0 + int(rng.integers(0, 128)), t_count - 1) for t0 in range(0, t_count, 128)]
     last = w.meta.cu_seqlens[1:] - 1
-    sample = np.unique(np.concatenate([last[:8], rng.integers(0, w.meta.num_tokens, size=40),
-                                       [w.meta.num_tokens - 1]]))
+    sample = np.unique(np.concatenate([per_tile, last, [t_count - 1]]))
+    say(f"  {len(sample)} rows checked ({len(per_tile)} tiles of 128)")
     match = _check_rows(w, k0, v0, sample, "bf16")
     assert np.mean(match) > 0.99
 
