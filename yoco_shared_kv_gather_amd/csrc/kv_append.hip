@@ -83,7 +83,8 @@ __global__ __launch_bounds__(256) void fold_rms_weight_kernel(const uint4* __res
 constexpr int kBM = 128;                     // tokens per workgroup tile
 constexpr int kBN = 256;                     // output features per workgroup tile
 constexpr int kBK = 32;
-constexpr int kLdsStride = kBK + 8;          // bf16 elements per staged row (16-byte pad)
+constexpr int kLdsStride = kBK;              // bf16 elements per staged row (4 chunks of 16 bytes, swizzled)
+static_assert(kBK == 32, "the row swizzle covers four 16-byte chunks");
 constexpr int kStage = (kBM + kBN) * kLdsStride;
 constexpr int kOutStride = kBN + 8;          // bf16 elements per row of the staged output tile
 constexpr int kGemmThreads = 256;
@@ -105,6 +106,8 @@ struct AppendArgs {
   int32_t bs_shift;
   int32_t num_kv_heads;
   int32_t n_tiles;            // ceil(2 * out_half / kBN)
+  int32_t num_tiles;          // token tiles x feature tiles
+  int32_t tiles_per_xcd;      // ceil(num_tiles / 8)
   int64_t num_slots;          // num_blocks * block_size
   float inv_hidden;
   float eps;
@@ -112,13 +115,21 @@ struct AppendArgs {
   float* v_scale;
 };
 
+// Staged rows hold their four 16-byte chunks in the order chunk ^ swz(row):
+// a fragment read (16 consecutive rows, one chunk) then touches distinct bank
+// groups in every 8 or 16 consecutive lanes (a padded row of 80 bytes left a
+// third of the LDS cycles in bank conflicts on gfx950).
+__device__ __forceinline__ int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+
 // One workgroup: 128 tokens x 256 output features, four wavefronts of 64 x 128
 // (4 x 8 MFMA tiles of 16x16), K step 32, two workgroups per compute unit
-// (K step 64 left one, with nothing to cover its LDS waits).  Workgroup id ->
-// (token tile = id / n_tiles, feature tile = id % n_tiles): consecutive workgroups go to
-// different XCDs, so each XCD keeps re-reading the same weight panels from its
-// own L2 while the XCDs share each activation tile through the last-level
-// cache.  Global -> registers -> LDS staging, two LDS stages, one barrier per
+// (K step 64 left one, with nothing to cover its LDS waits).  Workgroup b runs
+// on XCD b % 8, and XCD x takes the tiles [x*per, (x+1)*per) of the order
+// (token tile, feature tile) with the feature tile fastest: the feature
+// tiles of one activation panel run on one XCD at about the same time and
+// share the panel through its L2 (with the feature tile = b % 8, every panel
+// went to all eight XCDs, 3.5 GB of L2 misses for 0.4 GB of activations on
+// the mixed step).  Global -> registers -> LDS staging, two LDS stages, one barrier per
 // K step.  The epilogue scales by the row's rsqrt, rounds to bf16 into LDS and
 // writes each token's features as 16-byte chunks to its slot.  With kQD > 0
 // (the head_dim of an FP8 cache) the epilogue quantizes instead: a tile holds
@@ -141,8 +152,10 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)
   const int wave = tid >> 6;
   const int wm = wave >> 1;            // 64-row half of the tile
   const int wn = wave & 1;             // 128-column half of the tile
-  const int m0 = static_cast<int>(blockIdx.x / a.n_tiles) * kBM;
-  const int n0 = static_cast<int>(blockIdx.x % a.n_tiles) * kBN;
+  const int tile = static_cast<int>(blockIdx.x % 8) * a.tiles_per_xcd + static_cast<int>(blockIdx.x / 8);
+  if (tile >= a.num_tiles) return;
+  const int m0 = (tile / a.n_tiles) * kBM;
+  const int n0 = (tile % a.n_tiles) * kBN;
   const int n_total = 2 * a.out_half;
 
   // Staging map: thread moves chunk kc (8 bf16) of A rows rbase+kRp*i
@@ -183,7 +196,8 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)
     uint16_t* bs = as + kBM * kLdsStride;
 #pragma unroll
     for (int i = 0; i < kAP; ++i) {
-      *reinterpret_cast<uint4*>(&as[(rbase + kRp * i) * kLdsStride + kc * 8]) = r.a[i];
+      const int row = rbase + kRp * i;
+      *reinterpret_cast<uint4*>(&as[row * kLdsStride + ((kc ^ swz(row)) * 8)]) = r.a[i];
       // a repeated tile adds nothing (a select, not a branch: the stores,
       // loads and products of a half-iteration stay one block the
       // scheduler can interleave)
@@ -197,7 +211,10 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)
       }
     }
 #pragma unroll
-    for (int i = 0; i < kBP; ++i) *reinterpret_cast<uint4*>(&bs[(rbase + kRp * i) * kLdsStride + kc * 8]) = r.b[i];
+    for (int i = 0; i < kBP; ++i) {
+      const int row = rbase + kRp * i;
+      *reinterpret_cast<uint4*>(&bs[row * kLdsStride + ((kc ^ swz(row)) * 8)]) = r.b[i];
+    }
   };
 
   f32x4 acc[4][8];
@@ -208,7 +225,9 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)
 
   const int ktiles = a.hidden / kBK;
   const int frag_row = lane & 15;
-  const int frag_k = (lane >> 4) * 8;
+  // chunk lane/16 of rows congruent to frag_row mod 16 (t*16 and the
+  // wavefront's offset leave the swizzle bits alone)
+  const int frag_k = ((lane >> 4) ^ swz(frag_row)) * 8;
   auto mma = [&](int stage) {
     const uint16_t* as = lds + stage * kStage;
     const uint16_t* bs = as + kBM * kLdsStride;
@@ -910,7 +929,10 @@ int32_t append_impl(int32_t dtype, const void* x, int32_t num_tokens, int32_t hi
   a.v_scale = v_scale;
   a.n_tiles = static_cast<int32_t>(ceil_div(2 * out_half, kBN));
   const int64_t tiles = ceil_div(num_tokens, kBM) * a.n_tiles;
-  const dim3 grid(static_cast<uint32_t>(tiles)), block(kGemmThreads);
+  if (tiles > 0x7fffffff / 2) return fail(YOCO_ERR_UNSUPPORTED, "kv_append: %lld GEMM tiles", (long long)tiles);
+  a.num_tiles = static_cast<int32_t>(tiles);
+  a.tiles_per_xcd = static_cast<int32_t>(ceil_div(tiles, 8));
+  const dim3 grid(static_cast<uint32_t>(8 * a.tiles_per_xcd)), block(kGemmThreads);
   if (!quant) hipLaunchKernelGGL(kv_append_mfma_kernel<0>, grid, block, 0, s, a);
   else if (head_dim == 64) hipLaunchKernelGGL(kv_append_mfma_kernel<64>, grid, block, 0, s, a);
   else if (head_dim == 128) hipLaunchKernelGGL(kv_append_mfma_kernel<128>, grid, block, 0, s, a);
