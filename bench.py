@@ -67,9 +67,66 @@ def parse():
                    help="worker processes of the CPU baseline (0 = the usable host cores, at most 16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--seed", type=int, default=2024)
+    p.add_argument("--append-reference", action="store_true",
+                   help="only time yoco_kv_append of the workload's step against torch.mm (the vendor GEMM library) "
+                        "on the same [tokens x hidden] x [hidden x 2*Hkv*D] bf16 product")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB mebibytes (reference for HBM byte counters)")
     return p.parse_args()
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def append_reference(args):
+    """yoco_kv_append of the step's tokens (RMSNorm, the fused K/V projection,
+    the scatter into the cache) against a plain torch.mm of the same shape
+    (no normalisation, no scatter): both timed with events over 10 calls after
+    3 warm-up calls, the last-level cache flushed by a 1 GiB read before
+    each call."""
+    import torch
+
+    from yoco_shared_kv_gather_amd import binding as yb
+    from yoco_shared_kv_gather_amd import synth
+
+    dev = torch.device("cuda", 0)
+    meta = synth.make_metadata(args.workload, "full", args.seed)
+    geom = meta.geom
+    k, v = synth.make_cache(meta, dev, args.seed)
+    x, w_rms, w_k, w_v = synth.make_append_inputs(meta, dev, args.seed)
+    slots = torch.from_numpy(meta.slot_mapping).to(dev)
+    code = yb.DTYPE_BF16 if geom.dtype == "bf16" else yb.DTYPE_F32
+    ws = torch.zeros(max(16, yb.kv_append_workspace_size(code, geom.hidden, geom.num_kv_heads, geom.head_dim)),
+                     dtype=torch.uint8, device=dev)
+    w_t = torch.cat([w_k, w_v], 0).t().contiguous()            # [hidden][2*Hkv*D]
+    flush = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(3):
+            flush.sum(dtype=torch.int64)
+            fn()
+        times = []
+        for _ in range(10):
+            flush.sum(dtype=torch.int64)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.mean(times))
+
+    ours = timed(lambda: yb.kv_append(x, w_rms, 1e-6, w_k, w_v, slots, k, v, workspace=ws, stream=stream))
+    ref = timed(lambda: torch.mm(x, w_t))
+    flops = 2.0 * meta.num_tokens * geom.hidden * 2 * geom.num_kv_heads * geom.head_dim
+    out = {"workload": geom.name, "tokens": meta.num_tokens, "hidden": geom.hidden,
+           "features": 2 * geom.num_kv_heads * geom.head_dim, "tflop": round(flops / 1e12, 4),
+           "yoco_kv_append_us": round(ours, 2), "yoco_kv_append_tflops": round(flops / ours / 1e6, 1),
+           "yoco_kv_append_frac_of_2.5pf": round(flops / ours / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+           "torch_mm_us": round(ref, 2), "torch_mm_tflops": round(flops / ref / 1e6, 1),
+           "torch_mm_frac_of_2.5pf": round(flops / ref / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    print(json.dumps(out), flush=True)
 
 
 def copy_calibration(mib):
@@ -546,6 +603,9 @@ def main():
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
         return
+    if args.append_reference:
+        append_reference(args)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the hot path runs on a single MI355X).", file=sys.stderr)
@@ -684,6 +744,7 @@ def bench_cross(args, pool):
     wall = time.perf_counter() - t0
     step_ms = np.array([a.elapsed_time(c) for a, _, c in ev])
     layer_ms = np.array([b.elapsed_time(c) / L for _, b, c in ev])    # average call, inter-layer gaps included
+    head_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])         # the step's append + gather
     ms_per_step = float(step_ms.mean())
     tokens_per_s = num_rows / (ms_per_step * 1e-3)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step (events), wall {1e3 * wall / args.steps:.3f} ms/step")
@@ -753,6 +814,9 @@ def bench_cross(args, pool):
             "alternating_layer_order": not args.no_alternate,
             "parallelism": "single GPU",
         },
+        "append_gather_us": round(float(head_ms.mean()) * 1e3, 2),
+        "append_tflops": round(2.0 * meta.num_tokens * geom.hidden * 2 * geom.num_kv_heads * geom.head_dim /
+                               (float(head_ms.mean()) * 1e-3) / 1e12, 2),
         "step_hbm_gbps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "wall_ms_per_step": round(1e3 * wall / args.steps, 4),
