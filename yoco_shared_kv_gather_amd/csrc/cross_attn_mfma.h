@@ -50,12 +50,22 @@ struct MfmaLayout {
   static constexpr int kNT = kNK / 16;                                 // 16-key tiles per iteration
   static constexpr int kKS = D / 32;                                   // MFMA k-steps over head_dim
   static constexpr int kKL = kT == kFP8 ? D / 64 : D / 32;             // 16-byte K loads per tile per lane
-  static constexpr int kVC = kNK * kRowBytes / 16 / 64;                // 16-byte V chunks per lane per iteration
-  static constexpr int kChunksPerRow = kRowBytes / 16;
+  // FP8 at head_dim 256: the two wavefronts of a pair stream the same keys
+  // and each accumulates O^T for one half of head_dim (kDW columns), so the
+  // accumulators (and the V rows) of a wavefront are halved and two
+  // wavefronts fit per SIMD (decode64 FP8: 75.1k -> 83.9k tokens/s on one
+  // GPU).  bf16 rows are twice as long: the pair still spilled at two
+  // wavefronts per SIMD and gained nothing, so there one wavefront per SIMD
+  // covers all of head_dim, as everywhere else.
+  static constexpr bool kPair = D == 256 && kT == kFP8;
+  static constexpr int kDW = kPair ? D / 2 : D;                        // head_dim columns of a wavefront's O^T
+  static constexpr int kVRowBytes = kDW * kEb;                         // bytes of a V row a wavefront loads
+  static constexpr int kVC = kNK * kVRowBytes / 16 / 64;               // 16-byte V chunks per lane per iteration
+  static constexpr int kChunksPerRow = kVRowBytes / 16;
   // bf16 elements per LDS row of a V tile: the row stride is 8 banks mod 32,
   // so the four rows of one transposed read hit disjoint banks
-  static constexpr int kVStride = D + 16;
-  static_assert(kVC >= 1 && kNK * kRowBytes % (16 * 64) == 0, "V tile split");
+  static constexpr int kVStride = kDW + 16;
+  static_assert(kVC >= 1 && kNK * kVRowBytes % (16 * 64) == 0, "V tile split");
 };
 
 // Head_dim offset of the eight k-elements that lane group gi (= lane/16)
@@ -84,12 +94,12 @@ struct MfmaSmem {
   float ml[kWaves][VG][2];
   union __attribute__((aligned(16))) {
     uint16_t vt[kWaves][ML::kNK][ML::kVStride];     // per-wavefront V tile, bf16 row-major
-    float acc[kWaves][VG][D];                       // per-wavefront outputs for the final combine
+    float acc[kWaves][VG][ML::kDW];                 // per-wavefront outputs for the final combine
   } u;
 };
 
 template <int kT, int D, int G, int QPI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 2 : 1))) void cross_attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 128 || kT == kFP8 ? 2 : 1))) void cross_attn_mfma_kernel(AttnArgs a) {
   using ML = MfmaLayout<kT, D>;
   constexpr bool kVar = QPI > 0;
   constexpr bool kF8 = kT == kFP8;
@@ -98,7 +108,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
   static_assert(VG <= 16, "at most 16 query vectors per item");
   constexpr int kNK = ML::kNK, kNT = ML::kNT, kKS = ML::kKS, kKL = ML::kKL, kVC = ML::kVC;
   constexpr int kEb = ML::kEb;
-  constexpr int kDT = D / 16;                       // 16-row tiles of O^T
+  constexpr bool kPair = ML::kPair;
+  constexpr int kDW = ML::kDW;
+  constexpr int kDT = kDW / 16;                     // 16-row tiles of this wavefront's O^T
+  constexpr int kHalves = kPair ? 2 : 1;            // wavefronts sharing one key tile
+  constexpr int kGroups = kWaves / kHalves;         // wavefront groups taking every kGroups-th iteration
   using Smem = MfmaSmem<kT, D, VG, kVar>;
   __shared__ Smem sm;
 
@@ -108,6 +122,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
   const int l16 = lane & 15;                        // key (A/S rows) or query (B/S columns) within a tile
   const int gi = lane >> 4;                         // lane group
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int half = kPair ? (wave_u & 1) : 0;        // the head_dim half of this wavefront's O^T
+  const int group_u = kPair ? (wave_u >> 1) : wave_u;
   const bool reverse = (a.flags & YOCO_FLAG_REVERSE_ORDER) != 0;
   const int R = a.num_seqs;
   uint32_t* fetch_ctr = a.queue;
@@ -266,12 +282,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
 #pragma unroll
     for (int c = 0; c < kVC; ++c) {
       // the 64 chunks of one load instruction belong to 64 / kChunksPerRow <= 16
-      // consecutive keys of one tile
+      // consecutive keys of one tile; a wavefront loads its half of each row
       constexpr int kKeysPerInst = 64 / ML::kChunksPerRow;
       const int t = (c * kKeysPerInst) / 16;
       const int chunk = lane + 64 * c;
       const int key = chunk / ML::kChunksPerRow;
-      const int cb = (chunk - key * ML::kChunksPerRow) * 16;
+      const int cb = (chunk - key * ML::kChunksPerRow) * 16 + half * ML::kVRowBytes;
       const int j = base + key;
       rs.vmask |= ((rs.tmask >> t & 1u) != 0u && j >= it.start && j < it.end ? 1u : 0u) << c;
       rs.v[c] = *reinterpret_cast<const uint4*>(static_cast<const char*>(a.v) +
@@ -492,17 +508,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
       // neither register set is written conditionally: a conditional load
       // made the compiler copy whole register sets around the loop.
       Rows ra, rb;
-      int it = wave_u;
+      int it = group_u;
       if (it < num_iters) {
         load_rows(ra, cur, base0 + it * kNK);
         for (;;) {
-          load_rows(rb, cur, base0 + (it + kWaves) * kNK);
+          load_rows(rb, cur, base0 + (it + kGroups) * kNK);
           compute(ra);
-          it += kWaves;
+          it += kGroups;
           if (it >= num_iters) break;
-          load_rows(ra, cur, base0 + (it + kWaves) * kNK);
+          load_rows(ra, cur, base0 + (it + kGroups) * kNK);
           compute(rb);
-          it += kWaves;
+          it += kGroups;
           if (it >= num_iters) break;
         }
       }
@@ -543,15 +559,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
         const int d = e - h * D;
         const int64_t rh = out_row(h);
         if (rh < 0) continue;
-        float mx = sm.ml[0][h][0];
+        // the wavefronts holding column d: one per group (a pair's two
+        // wavefronts hold the same maximum and sum)
+        const int dh = kPair ? d / kDW : 0;
+        const int dd = d - dh * kDW;
+        float mx = sm.ml[dh][h][0];
 #pragma unroll
-        for (int w = 1; w < kWaves; ++w) mx = fmaxf(mx, sm.ml[w][h][0]);
+        for (int g = 1; g < kGroups; ++g) mx = fmaxf(mx, sm.ml[g * kHalves + dh][h][0]);
         float den = 0.0f, num = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
+        for (int g = 0; g < kGroups; ++g) {
+          const int w = g * kHalves + dh;
           const float f = exp2f(sm.ml[w][h][0] - mx);
           den = fmaf(f, sm.ml[w][h][1], den);
-          num = fmaf(f, sm.u.acc[w][h][d], num);
+          num = fmaf(f, sm.u.acc[w][h][dd], num);
         }
         if (np_r == 1) {
           a.out[rh * D + d] = den == 0.0f ? 0.0f : num / den;
