@@ -509,8 +509,8 @@ int32_t yoco_cross_attn_varlen(int32_t dtype, const void* q, int32_t num_rows,
  *   max_seqlen     an upper bound on any request's rows, or 0 if unknown.  It
  *                  only chooses the schedule: 1 runs the recurrent form (one
  *                  workgroup per request and head streaming its state), up to
- *                  1024 one chunkwise run per request, above (or 0) splits
- *                  long requests into 1024-row segments computed in parallel
+ *                  2048 one chunkwise run per request, above (or 0) splits
+ *                  long requests into 2048-row segments computed in parallel
  *                  (needs a workspace).  A request longer than max_seqlen is
  *                  still computed in full.
  *   state          fp32 [num_slots][num_heads][head_dim][head_dim] (key row,

@@ -216,14 +216,14 @@ def test_gated_retention_nothing_to_do():
 
 
 def test_gated_retention_workspace_follows_the_schedule():
-    # decode (max_seqlen 1) and one run per request (<= 1024 rows) need none;
-    # segments of 1024 rows need a state and a gate per (segment, head)
+    # decode (max_seqlen 1) and one run per request (<= 2048 rows) need none;
+    # segments of 2048 rows need a state and a gate per (segment, head)
     assert yb.gated_retention_workspace_size(5000, 8, 4, 128, 1) == 0
-    assert yb.gated_retention_workspace_size(5000, 8, 4, 128, 1024) == 0
-    segs = (8 + 5000 // 1024) * 4
+    assert yb.gated_retention_workspace_size(5000, 8, 4, 128, 2048) == 0
+    segs = (8 + 5000 // 2048) * 4
     rup = lambda x: -(-x // 256) * 256
     assert yb.gated_retention_workspace_size(5000, 8, 4, 128, 0) == rup(segs * 128 * 128 * 4) + rup(segs * 4)
-    assert yb.gated_retention_workspace_size(5000, 8, 4, 128, 1025) == rup(segs * 128 * 128 * 4) + rup(segs * 4)
+    assert yb.gated_retention_workspace_size(5000, 8, 4, 128, 2049) == rup(segs * 128 * 128 * 4) + rup(segs * 4)
     # more requests than a segmented launch schedules: one run per request
     assert yb.gated_retention_workspace_size(5000, 4096, 4, 64, 0) == 0
     assert yb.gated_retention_workspace_size(-1, 8, 4, 128, 0) == -1

@@ -64,12 +64,12 @@ def _run(t, out=None, max_seqlen=0):
     return out
 
 
-# max_seqlen picks the schedule: 1 the recurrent kernel, <= 1024 one chunkwise
-# run per request, 0 (unknown) 1024-row segments in two launches; every
+# max_seqlen picks the schedule: 1 the recurrent kernel, <= 2048 one chunkwise
+# run per request, 0 (unknown) 2048-row segments in two launches; every
 # schedule computes every request in full
-PLANS = {"recurrent": 1, "whole": 1024, "segmented": 0}
+PLANS = {"recurrent": 1, "whole": 2048, "segmented": 0}
 SHORT = [1, 31, 32, 33, 0, 100, 7, 64, 200]
-LONG = [3000, 1024, 1025, 0, 2048, 5, 1, 2100]
+LONG = [6000, 2048, 2049, 0, 4096, 5, 1, 4200]
 
 
 @pytest.mark.parametrize("plan", sorted(PLANS))
@@ -77,7 +77,7 @@ LONG = [3000, 1024, 1025, 0, 2048, 5, 1, 2100]
 @pytest.mark.parametrize("head_dim", [64, 128])
 def test_retention_matches_oracle(head_dim, lens, plan):
     """Requests of partial, whole and many chunks (short: up to 200 rows;
-    long: up to 3000 rows, so up to three segments), some starting from a
+    long: up to 6000 rows, so up to three segments), some starting from a
     zero state (slot -1), on every schedule; all outputs and every slot
     checked."""
     heads = 3 if lens is SHORT else 2
@@ -99,11 +99,11 @@ def test_retention_matches_oracle(head_dim, lens, plan):
 @pytest.mark.parametrize("plan", sorted(PLANS))
 @pytest.mark.parametrize("gamma_value", [0.0, 1.0])
 def test_retention_gate_edges(gamma_value, plan):
-    """gamma = 1 (no forgetting, the state sums every k^T v over 1300 rows,
+    """gamma = 1 (no forgetting, the state sums every k^T v over 2600 rows,
     two segments) and gamma = 0 (only the current token: o_t = (q_t . k_t)
     v_t), on every schedule."""
     say(f"retention: gamma = {gamma_value}, plan {plan}")
-    inp = synth.make_retention_inputs([1300, 5, 1], 2, 128)
+    inp = synth.make_retention_inputs([2600, 5, 1], 2, 128)
     inp.gamma.fill_(gamma_value)
     t = _to_dev(inp)
     out = _run(t, max_seqlen=PLANS[plan])
@@ -122,7 +122,7 @@ def test_retention_split_calls_carry_the_state():
     request two segments in the first call) and then five one-token decode
     steps on the recurrent kernel give the single oracle run's outputs and
     state."""
-    lens = np.array([40, 70, 1, 33, 3300], dtype=np.int64)
+    lens = np.array([40, 70, 1, 33, 6600], dtype=np.int64)
     steps = 5
     total = lens + steps
     say(f"retention: prefill {list(lens)} in two calls, then {steps} decode steps")

@@ -68,7 +68,7 @@ constexpr int kRowPad = 8;              // bf16 elements of padding per LDS row
 constexpr int kTrPad = 16;              // padding of the tiles read transposed
 constexpr float kMinLog2Gate = -64.0f;
 constexpr float kMinLazyScale = 0x1p-60f;   // smallest state scale kept apart from the state
-constexpr int kSegRows = 1024;          // rows per segment of a long request (a multiple of kC)
+constexpr int kSegRows = 2048;          // rows per segment of a long request (a multiple of kC)
 constexpr int kMaxSegReqs = 2048;       // requests a segmented launch can schedule
 
 // what a launch of the chunk kernel does
