@@ -9,8 +9,9 @@ the last-level (Infinity) cache in front of it, which no counter of this
 tool tells apart.  Averages cover the timed steps only: bench.py runs W
 warm-up steps and then K timed steps with the same kernels, so the last
 K / (W + K) of each kernel's dispatches are the timed ones.  The summary also
-records a hash of the HIP sources behind the profiled kernels, so bench.py can
-tell whether the measured traffic still describes the kernels it runs.
+records a hash of the code of the HIP sources behind the profiled kernels
+(comments and whitespace left out), so bench.py can tell whether the measured
+traffic still describes the kernels it runs.
 
 Expected layout of the rocprofv3 output directory (one `-d` per pass, `-o run`
 and `-f csv`):
@@ -62,14 +63,43 @@ def family_sources(stem: Optional[str]) -> List[str]:
     return files + [os.path.join(ROOT, "include", "yoco.h")]
 
 
+def code_only(text: str) -> str:
+    """C/C++ source without its comments, every run of whitespace as one
+    space: what the compiler sees, so that editing a comment leaves the hash
+    alone.  String and character literals are kept whole (a // inside one is
+    not a comment)."""
+    out = []
+    i, n = 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            out.append(" ")
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def source_hash(stem: Optional[str] = None) -> str:
-    """sha256 over the sources of profile `stem`'s kernels and the public
-    header, in name order (all sources without a stem)."""
+    """sha256 over the code (comments and whitespace left out) of profile
+    `stem`'s kernel sources and the public header, in name order (all
+    sources without a stem)."""
     h = hashlib.sha256()
     for path in family_sources(stem):
         h.update(os.path.basename(path).encode())
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            h.update(code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
