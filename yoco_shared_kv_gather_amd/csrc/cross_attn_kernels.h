@@ -627,8 +627,8 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < kCpl; ++i) {
         const int64_t c = off + static_cast<int64_t>((cl + kLpr * i) * kEpc) * kElemBytes;
-        rs.k[u][i] = *reinterpret_cast<const uint4*>(kb + c);
-        rs.v[u][i] = *reinterpret_cast<const uint4*>(vb + c);
+        rs.k[u][i] = yoco::load_stream(kb + c);
+        rs.v[u][i] = yoco::load_stream(vb + c);
       }
       if constexpr (kF8) {
         // the row's scales: element offset / D is the row index in [block][head][slot] order
@@ -672,8 +672,8 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < kCpl; ++i) {
         const int64_t c = off + static_cast<int64_t>((cl + kLpr * i) * kEpc) * kElemBytes;
-        rs.k[u][i] = *reinterpret_cast<const uint4*>(kb + c);
-        rs.v[u][i] = *reinterpret_cast<const uint4*>(vb + c);
+        rs.k[u][i] = yoco::load_stream(kb + c);
+        rs.v[u][i] = yoco::load_stream(vb + c);
       }
       if constexpr (kF8) {
         // the row's scales: element offset / D is the row index in [block][head][slot] order

@@ -352,9 +352,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       // waits for them right away and the prefetch is lost)
       const int off = s * row_elems + 8 * cc;
       if (s < n) {
-        if constexpr (kOut) rq[i] = *reinterpret_cast<const uint4*>(a.q + base + off);
-        rk[i] = *reinterpret_cast<const uint4*>(a.k + base + off);
-        rv[i] = *reinterpret_cast<const uint4*>(a.v + base + off);
+        if constexpr (kOut) rq[i] = yoco::load_stream(a.q + base + off);
+        rk[i] = yoco::load_stream(a.k + base + off);
+        rv[i] = yoco::load_stream(a.v + base + off);
       } else {
         rq[i] = rk[i] = rv[i] = make_uint4(0u, 0u, 0u, 0u);
       }
@@ -524,7 +524,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           const int t = 16 * tt + 4 * gi + e;
           if (t < n) {
 #pragma unroll
-            for (int ct = 0; ct < kCT; ++ct) ob[t * row_elems + 16 * ct + l16] = oacc[tt][ct][e];
+            for (int ct = 0; ct < kCT; ++ct) __builtin_nontemporal_store(oacc[tt][ct][e], ob + t * row_elems + 16 * ct + l16);
           }
         }
     }
@@ -607,7 +607,9 @@ __global__ __launch_bounds__(kThreads) void gated_retention_decode_kernel(RetArg
                               : nullptr;
   float4 s[kRows];
 #pragma unroll
-  for (int p = 0; p < kRows; ++p) s[p] = has_slot ? st[at(rg + kRG * p)] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int p = 0; p < kRows; ++p)
+    s[p] = has_slot ? yoco::load_stream_f4(reinterpret_cast<const float*>(st + at(rg + kRG * p)))
+                    : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 
   for (int t = start; t < end; ++t) {
     const int64_t row = (static_cast<int64_t>(t) * H + h) * D;
@@ -648,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void gated_retention_decode_kernel(RetArg
   }
   if (has_slot) {
 #pragma unroll
-    for (int p = 0; p < kRows; ++p) st[at(rg + kRG * p)] = s[p];
+    for (int p = 0; p < kRows; ++p) yoco::store_stream_f4(reinterpret_cast<float*>(st + at(rg + kRG * p)), s[p]);
   }
 }
 

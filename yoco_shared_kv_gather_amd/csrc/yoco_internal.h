@@ -39,6 +39,31 @@ inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// A 16-byte global load with the non-temporal hint (global_load ... nt), for
+// rows a kernel streams through once, such as the K/V cache rows an attention
+// layer reads: a plain streaming read reaches about 8% more bandwidth with it
+// on gfx950.  Only for loads that take whole 128-byte lines per instruction:
+// where one instruction reads half of each line and the next the other half,
+// the hint costs a second fetch of the line.
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 w = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+  return make_uint4(w.x, w.y, w.z, w.w);
+}
+
+// The same hint for 16 bytes of fp32 read or written once (a state that a
+// kernel reads, updates and writes back).
+__device__ __forceinline__ float4 load_stream_f4(const float* p) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  const f32x4v w = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+  return make_float4(w.x, w.y, w.z, w.w);
+}
+__device__ __forceinline__ void store_stream_f4(float* p, const float4& v) {
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  const f32x4v w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<f32x4v*>(p));
+}
+
 // fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
