@@ -290,8 +290,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
       const int cb = (chunk - key * ML::kChunksPerRow) * 16 + half * ML::kVRowBytes;
       const int j = base + key;
       rs.vmask |= ((rs.tmask >> t & 1u) != 0u && j >= it.start && j < it.end ? 1u : 0u) << c;
-      rs.v[c] = yoco::load_stream(static_cast<const char*>(a.v) +
-                                                 (tile_row[t] + (key - 16 * t)) * ML::kRowBytes + cb);
+      rs.v[c] = yoco::load_stream(static_cast<const char*>(a.v) + (tile_row[t] + (key - 16 * t)) * ML::kRowBytes + cb);
     }
   };
 

@@ -524,7 +524,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           const int t = 16 * tt + 4 * gi + e;
           if (t < n) {
 #pragma unroll
-            for (int ct = 0; ct < kCT; ++ct) __builtin_nontemporal_store(oacc[tt][ct][e], ob + t * row_elems + 16 * ct + l16);
+            for (int ct = 0; ct < kCT; ++ct)
+              __builtin_nontemporal_store(oacc[tt][ct][e], ob + t * row_elems + 16 * ct + l16);
           }
         }
     }
