@@ -81,13 +81,15 @@ typedef enum yoco_dtype { YOCO_DTYPE_F32 = 0, YOCO_DTYPE_BF16 = 1, YOCO_DTYPE_FP
 /* yoco_cross_attn flag: walk the (request, KV head, partition) work items in
  * reverse order.  Alternating it between consecutive cross layers makes the
  * first blocks a layer reads the last ones the previous layer read, which may
- * still sit in the GPU's last-level cache.  Results are bit-identical either
- * way. */
+ * still sit in the GPU's last-level cache (the kernels read K^/V^ rows with a
+ * streaming hint that mostly keeps them out of it).  Results are
+ * bit-identical either way. */
 #define YOCO_FLAG_REVERSE_ORDER 1u
 
-/* yoco_cross_attn_varlen flag: run the vector-ALU kernel even where the
- * matrix-core kernel is the default (an FP8 cache, or several query rows per
- * request).  Same results within the attention tolerance; for comparisons. */
+/* yoco_cross_attn and yoco_cross_attn_varlen flag: run the vector-ALU kernel
+ * even where the matrix-core kernel is the default (an FP8 cache, several
+ * query rows per request, or a bf16 cache at head_dim 256).  Same results
+ * within the attention tolerance; for comparisons. */
 #define YOCO_FLAG_VECTOR_KERNEL 2u
 
 /* The first YOCO_CROSS_ATTN_QUEUE_BYTES bytes of a yoco_cross_attn workspace
@@ -457,9 +459,9 @@ int32_t yoco_gather_logits(const void* hidden, int64_t num_tokens, int64_t row_b
  * With query_start_loc: num_seqs <= 2048 (YOCO_ERR_UNSUPPORTED beyond); a
  * work item streams its K^/V^ rows once for several query vectors (rows x
  * heads of one KV group): up to 16 on the matrix-core kernel, which runs an
- * FP8 cache and bf16 with several rows per request when block_size >= 16
- * (and the scales are 16-byte aligned), up to 8 on the vector kernel
- * otherwise or with YOCO_FLAG_VECTOR_KERNEL.  A NaN in a row that some of a request's rows read
+ * FP8 cache, bf16 with several rows per request and bf16 at head_dim 256
+ * when block_size >= 16 (and the scales are 16-byte aligned), up to 8 on the
+ * vector kernel otherwise or with YOCO_FLAG_VECTOR_KERNEL.  A NaN in a row that some of a request's rows read
  * may give NaN in all of that request's rows.  Errors as in yoco_cross_attn.
  */
 int64_t yoco_cross_attn_varlen_workspace_size(int32_t num_rows, int32_t num_seqs, int32_t num_q_heads,

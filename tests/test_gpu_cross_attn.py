@@ -28,11 +28,15 @@ def _max_err(got, ref):
 @pytest.mark.parametrize("cid,size", [(1, "full"), (2, "small"), (3, "small"), (4, "small"), (5, "small"),
                                       (1, "edge"), (2, "edge"), (3, "edge")])
 @pytest.mark.parametrize("partition_tokens", [0, 64])
-def test_parity_small(cid, size, partition_tokens):
-    say(f"cross_attn parity: workload {cid} {size} partition {partition_tokens}")
+@pytest.mark.parametrize("kernel", ["default", "vector"])
+def test_parity_small(cid, size, partition_tokens, kernel):
+    """Every output, with the kernel the library picks (the vector kernel, or
+    the matrix-core kernel at head_dim 256) and with the vector kernel forced."""
+    say(f"cross_attn parity: workload {cid} {size} partition {partition_tokens} {kernel}")
     w = DeviceWorkload(cid, size, layers=2)
+    force = yb.FLAG_VECTOR_KERNEL if kernel == "vector" else 0
     for layer in range(2):
-        out = w.attn(layer, partition_tokens=partition_tokens, flags=layer & 1)
+        out = w.attn(layer, partition_tokens=partition_tokens, flags=(layer & 1) | force)
         torch.cuda.synchronize()
         ref = oracle_attention_full(w, layer)
         err = _max_err(out, ref)

@@ -21,6 +21,8 @@ MAX_SLICE = 512                # block-table entries one item may span
 
 
 def keys_per_iteration(elem_bytes, head_dim):
+    if elem_bytes == 2 and head_dim == 256:
+        return 32                  # the four head_dim slices of a workgroup share 32-key iterations
     budget = 4096 if elem_bytes == 1 else 8192
     n = budget // (2 * head_dim * elem_bytes)
     return min(max(n, 16), 64)
@@ -64,6 +66,8 @@ BATCHES = [
     ([300, 40, 700, 5, 129, 2049], 4, 100, 16, 1, 128),
     ([1000, 17, 64, 65], 3, 1, 32, 2, 64),
     ([5000, 33], 1, 1000, 16, 1, 256),
+    ([5000, 33, 1, 700], 1, 1000, 16, 2, 256),
+    ([8192, 1024, 77], 4, 0, 16, 2, 256),
     ([524288], 1, 8192, 32, 2, 128),
     ([32768] * 4, 4, 0, 16, 2, 128),
 ]

@@ -234,12 +234,16 @@ int32_t run_cross_attn(const AttnCall& c, const char* who) {
   const int32_t nparts = num_partitions(span, part);
   if (nparts > kMaxParts)
     return fail(YOCO_ERR_UNSUPPORTED, "%s: %d partitions per request exceed %d", who, nparts, kMaxParts);
-  // Matrix cores where the work per byte outgrows the vector ALUs: an FP8
-  // cache, or several query rows per request (bf16); persistent schedule only.
-  // (It reads 16-key tiles that lie inside one block: block_size >= 16.)
-  const bool mfma = (c.flags & YOCO_FLAG_VECTOR_KERNEL) == 0 && c.num_seqs <= kMaxQueueSeqs &&
-                    c.block_size >= 16 && (!f8 || (aligned16(c.k_scale) && aligned16(c.v_scale))) &&
-                    (f8 || (c.dtype == YOCO_DTYPE_BF16 && c.qsl != nullptr && c.max_qlen > 1));
+  // Matrix cores where the work per byte outgrows the vector ALUs (an FP8
+  // cache, or several query rows per request), and for a bf16 cache at
+  // head_dim 256, where the matrix kernel's four head_dim slices per key tile
+  // stream faster than the vector kernel's 16 lanes per row (decode64: 110.5
+  // -> 104.6 us per layer); persistent schedule only.  (It reads 16-key tiles
+  // that lie inside one block: block_size >= 16.)
+  const bool mfma =
+      (c.flags & YOCO_FLAG_VECTOR_KERNEL) == 0 && c.num_seqs <= kMaxQueueSeqs && c.block_size >= 16 &&
+      (!f8 || (aligned16(c.k_scale) && aligned16(c.v_scale))) &&
+      (f8 || (c.dtype == YOCO_DTYPE_BF16 && ((c.qsl != nullptr && c.max_qlen > 1) || c.head_dim == 256)));
   const int rows_wide = (mfma ? 16 : 8) / group;
   const int qpi = c.qsl == nullptr ? 0 : (c.max_qlen > 1 ? rows_wide : 1);
   const int64_t groups = qpi == 0 ? 1 : yoco::ceil_div(c.max_qlen, qpi);

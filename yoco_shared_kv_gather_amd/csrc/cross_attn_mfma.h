@@ -24,6 +24,11 @@
 //       sums are fp32.  Each lane's O^T column belongs to its own query, so
 //       rescaling on a new maximum stays lane-local.
 //
+// At head_dim 256 several wavefronts share each key tile, each with a slice
+// of head_dim (bf16: four slices, the scores summed through LDS; FP8: two,
+// each computing the whole scores), which keeps two wavefronts per SIMD; a
+// bf16 cache at head_dim 256 takes this kernel also for one query row.
+//
 // The schedule, work items, partials and the merge kernel are those of the
 // VALU kernel; the item pipeline is simpler (the next item is fetched at the
 // start of the current one and its block-table slice and queries are loaded
@@ -46,19 +51,26 @@ struct MfmaLayout {
   // keys per wavefront iteration: about 8 KB of K^/V^ (bf16) or 4 KB (FP8,
   // which keeps two wavefronts per SIMD in registers), at least one tile
   static constexpr int kBudget = kT == kFP8 ? 4096 : 8192;
-  static constexpr int kNK = kBudget / (2 * kRowBytes) < 16 ? 16 : (kBudget / (2 * kRowBytes) > 64 ? 64 : kBudget / (2 * kRowBytes));
-  static constexpr int kNT = kNK / 16;                                 // 16-key tiles per iteration
-  static constexpr int kKS = D / 32;                                   // MFMA k-steps over head_dim
-  static constexpr int kKL = kT == kFP8 ? D / 64 : D / 32;             // 16-byte K loads per tile per lane
-  // FP8 at head_dim 256: the two wavefronts of a pair stream the same keys
-  // and each accumulates O^T for one half of head_dim (kDW columns), so the
-  // accumulators (and the V rows) of a wavefront are halved and two
-  // wavefronts fit per SIMD (decode64 FP8: 75.1k -> 83.9k tokens/s on one
-  // GPU).  bf16 rows are twice as long: the pair still spilled at two
-  // wavefronts per SIMD and gained nothing, so there one wavefront per SIMD
-  // covers all of head_dim, as everywhere else.
+  // head_dim 256, bf16: the four wavefronts of a workgroup stream the same
+  // keys, each with one 64-column slice of head_dim: its part of every score
+  // (the four parts summed through LDS, one barrier per iteration) and its
+  // 64 rows of O^T.  A wavefront then holds a quarter of the rows and
+  // accumulators, so two fit per SIMD, and no K row is read twice
+  // (decode64 with 4 rows per request: 138 -> 116 us per layer).
+  // head_dim 256, FP8: wavefront pairs stream the same keys, each computing
+  // the whole scores and its half of O^T (two per SIMD as well; the split
+  // into four, with 16 KB of rows per barrier, was slower: 74 -> 91 us).
+  static constexpr bool kSplit = D == 256 && kT == kBF16;
   static constexpr bool kPair = D == 256 && kT == kFP8;
-  static constexpr int kDW = kPair ? D / 2 : D;                        // head_dim columns of a wavefront's O^T
+  static constexpr int kSlices = kSplit ? 4 : kPair ? 2 : 1;          // wavefronts sharing one key tile
+  static constexpr int kNK = kSplit ? 32
+                           : kBudget / (2 * kRowBytes) < 16 ? 16
+                           : (kBudget / (2 * kRowBytes) > 64 ? 64 : kBudget / (2 * kRowBytes));
+  static constexpr int kNT = kNK / 16;                                 // 16-key tiles per iteration
+  static constexpr int kDW = D / kSlices;                              // head_dim columns of a wavefront's O^T
+  static constexpr int kKD = kSplit ? kDW : D;                         // head_dim columns of its scores
+  static constexpr int kKS = kKD / 32;                                 // MFMA k-steps over those columns
+  static constexpr int kKL = kT == kFP8 ? kKD / 64 : kKD / 32;         // 16-byte K loads per tile per lane
   static constexpr int kVRowBytes = kDW * kEb;                         // bytes of a V row a wavefront loads
   static constexpr int kVC = kNK * kVRowBytes / 16 / 64;               // 16-byte V chunks per lane per iteration
   static constexpr int kChunksPerRow = kVRowBytes / 16;
@@ -90,7 +102,13 @@ struct MfmaSmem {
   int32_t wsum[2 * kWaves];
   uint32_t next;
   int32_t blocks[kMaxSliceBlocks];
-  __attribute__((aligned(16))) uint16_t q[16][D + 8];   // the item's query vectors, bf16, rows past VG zero
+  union __attribute__((aligned(16))) {
+    uint16_t q[16][D + 8];       // the item's query vectors, bf16, rows past VG zero (read into registers)
+    // head_dim 256: each wavefront's part of the iteration's scores, in its
+    // MFMA output layout, by iteration parity (written once the queries are
+    // in registers)
+    mfma_f32x4 sc[ML::kSplit ? 2 : 1][ML::kSplit ? kWaves : 1][ML::kSplit ? ML::kNT : 1][64];
+  };
   float ml[kWaves][VG][2];
   union __attribute__((aligned(16))) {
     uint16_t vt[kWaves][ML::kNK][ML::kVStride];     // per-wavefront V tile, bf16 row-major
@@ -99,7 +117,7 @@ struct MfmaSmem {
 };
 
 template <int kT, int D, int G, int QPI>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 128 || kT == kFP8 ? 2 : 1))) void cross_attn_mfma_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void cross_attn_mfma_kernel(AttnArgs a) {
   using ML = MfmaLayout<kT, D>;
   constexpr bool kVar = QPI > 0;
   constexpr bool kF8 = kT == kFP8;
@@ -108,11 +126,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
   static_assert(VG <= 16, "at most 16 query vectors per item");
   constexpr int kNK = ML::kNK, kNT = ML::kNT, kKS = ML::kKS, kKL = ML::kKL, kVC = ML::kVC;
   constexpr int kEb = ML::kEb;
-  constexpr bool kPair = ML::kPair;
+  constexpr bool kSplit = ML::kSplit;
   constexpr int kDW = ML::kDW;
   constexpr int kDT = kDW / 16;                     // 16-row tiles of this wavefront's O^T
-  constexpr int kHalves = kPair ? 2 : 1;            // wavefronts sharing one key tile
-  constexpr int kGroups = kWaves / kHalves;         // wavefront groups taking every kGroups-th iteration
+  constexpr int kSlices = ML::kSlices;              // wavefronts sharing one key tile
+  constexpr int kGroups = kWaves / kSlices;         // wavefront groups taking every kGroups-th iteration
   using Smem = MfmaSmem<kT, D, VG, kVar>;
   __shared__ Smem sm;
 
@@ -122,8 +140,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
   const int l16 = lane & 15;                        // key (A/S rows) or query (B/S columns) within a tile
   const int gi = lane >> 4;                         // lane group
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int half = kPair ? (wave_u & 1) : 0;        // the head_dim half of this wavefront's O^T
-  const int group_u = kPair ? (wave_u >> 1) : wave_u;
+  const int slice = wave_u % kSlices;               // this wavefront's head_dim slice of O^T
+  const int group_u = wave_u / kSlices;
+  const int kslice = kSplit ? slice * kDW : 0;      // first head_dim column of its scores
   const bool reverse = (a.flags & YOCO_FLAG_REVERSE_ORDER) != 0;
   const int R = a.num_seqs;
   uint32_t* fetch_ctr = a.queue;
@@ -270,7 +289,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
       const char* kt = static_cast<const char*>(a.k) + tile_row[t] * ML::kRowBytes;
 #pragma unroll
       for (int c = 0; c < kKL; ++c) {
-        const int d = kF8 ? 64 * c + 16 * gi : 32 * c + 8 * gi;
+        const int d = kslice + (kF8 ? 64 * c + 16 * gi : 32 * c + 8 * gi);
         rs.k[t][c] = *reinterpret_cast<const uint4*>(kt + l16 * ML::kRowBytes + d * kEb);
       }
       if constexpr (kF8) {
@@ -282,12 +301,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
 #pragma unroll
     for (int c = 0; c < kVC; ++c) {
       // the 64 chunks of one load instruction belong to 64 / kChunksPerRow <= 16
-      // consecutive keys of one tile; a wavefront loads its half of each row
+      // consecutive keys of one tile; a wavefront loads its slice of each row
       constexpr int kKeysPerInst = 64 / ML::kChunksPerRow;
       const int t = (c * kKeysPerInst) / 16;
       const int chunk = lane + 64 * c;
       const int key = chunk / ML::kChunksPerRow;
-      const int cb = (chunk - key * ML::kChunksPerRow) * 16 + half * ML::kVRowBytes;
+      const int cb = (chunk - key * ML::kChunksPerRow) * 16 + slice * ML::kVRowBytes;
       const int j = base + key;
       rs.vmask |= ((rs.tmask >> t & 1u) != 0u && j >= it.start && j < it.end ? 1u : 0u) << c;
       rs.v[c] = yoco::load_stream(static_cast<const char*>(a.v) + (tile_row[t] + (key - 16 * t)) * ML::kRowBytes + cb);
@@ -305,7 +324,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
   int vis_lo = 0;                                   // keys this lane's query sees: [vis_lo, vis_lo + vis_len)
   uint32_t vis_len = 0u;                            // (0 when the lane's column holds no query)
 
-  auto compute = [&](const Rows& rs) {
+  auto compute = [&](const Rows& rs, const int buf) {
     uint16_t(*vt)[ML::kVStride] = sm.u.vt[wave];
     // the previous iteration's reads of this wavefront's tile come first
     __builtin_amdgcn_wave_barrier();
@@ -335,9 +354,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
     // LDS writes before reading them back
     __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
-    // S^T tiles
-    float s[kNT][4];
-    bool inrange[kNT][4];          // the key is a row of the item (its V and scale are real)
+    // S^T tiles (head_dim 256: this wavefront's slice of every score, the
+    // four slices then summed in wavefront order, the same sum in every
+    // wavefront)
+    mfma_f32x4 sacc[kNT];
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
       mfma_f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -355,6 +375,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
                                                          0, 0, 0);
         }
       }
+      sacc[t] = acc;
+    }
+    if constexpr (kSplit) {
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) sm.sc[buf][wave][t][lane] = sacc[t];
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) {
+        mfma_f32x4 sum = sm.sc[buf][0][t][lane];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) sum += sm.sc[buf][w][t][lane];
+        sacc[t] = sum;
+      }
+    }
+    float s[kNT][4];
+    bool inrange[kNT][4];          // the key is a row of the item (its V and scale are real)
+#pragma unroll
+    for (int t = 0; t < kNT; ++t) {
+      const mfma_f32x4 acc = sacc[t];
       const bool tile_ok = (rs.tmask >> t & 1u) != 0u;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -482,7 +521,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
     if (cur.num_blk > 0) {
 #pragma unroll
       for (int ks = 0; ks < kKS; ++ks)
-        qop[ks] = *reinterpret_cast<const mfma_bf16x8*>(&sm.q[l16][mfma_d_of<kT>(gi, ks)]);
+        qop[ks] = *reinterpret_cast<const mfma_bf16x8*>(&sm.q[l16][kslice + mfma_d_of<kT>(gi, ks)]);
+      if constexpr (kSplit) __syncthreads();        // the scores' LDS overlays the queries
       // this lane's query column: vector l16 = query row l16 / G, head l16 % G
       {
         const int qi = l16 / G;
@@ -512,11 +552,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
         load_rows(ra, cur, base0 + it * kNK);
         for (;;) {
           load_rows(rb, cur, base0 + (it + kGroups) * kNK);
-          compute(ra);
+          compute(ra, 0);
           it += kGroups;
           if (it >= num_iters) break;
           load_rows(ra, cur, base0 + (it + kGroups) * kNK);
-          compute(rb);
+          compute(rb, 1);
           it += kGroups;
           if (it >= num_iters) break;
         }
@@ -558,17 +598,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D <= 1
         const int d = e - h * D;
         const int64_t rh = out_row(h);
         if (rh < 0) continue;
-        // the wavefronts holding column d: one per group (a pair's two
-        // wavefronts hold the same maximum and sum)
-        const int dh = kPair ? d / kDW : 0;
+        // the wavefronts holding column d: one per group (the wavefronts of
+        // a group hold the same maximum and sum)
+        const int dh = d / kDW;
         const int dd = d - dh * kDW;
         float mx = sm.ml[dh][h][0];
 #pragma unroll
-        for (int g = 1; g < kGroups; ++g) mx = fmaxf(mx, sm.ml[g * kHalves + dh][h][0]);
+        for (int g = 1; g < kGroups; ++g) mx = fmaxf(mx, sm.ml[g * kSlices + dh][h][0]);
         float den = 0.0f, num = 0.0f;
 #pragma unroll
         for (int g = 0; g < kGroups; ++g) {
-          const int w = g * kHalves + dh;
+          const int w = g * kSlices + dh;
           const float f = exp2f(sm.ml[w][h][0] - mx);
           den = fmaf(f, sm.ml[w][h][1], den);
           num = fmaf(f, sm.u.acc[w][h][dd], num);
