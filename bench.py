@@ -762,9 +762,11 @@ def bench_cross(args, pool):
     attn_us = float(layer_ms.mean()) * 1e3
     achieved = layer_bytes / (attn_us * 1e-6) / 1e9
     group = geom.num_q_heads // geom.num_kv_heads
-    # the kernel the library picks: matrix cores for an FP8 cache or several
-    # query rows per request (bf16), with block_size >= 16 and <= 2048 requests
-    mfma = (args.fp8 or (geom.dtype == "bf16" and Q > 1)) and R <= 2048 and geom.block_size >= 16
+    # the kernel the library picks: matrix cores for an FP8 cache, several
+    # query rows per request (bf16) or bf16 at head_dim 256, with
+    # block_size >= 16 and <= 2048 requests
+    mfma = ((args.fp8 or (geom.dtype == "bf16" and (Q > 1 or geom.head_dim == 256))) and R <= 2048
+            and geom.block_size >= 16)
     rows_per_item = 0 if Q == 1 else (16 if mfma else 8) // group
     elem_type = 2 if args.fp8 else (1 if geom.dtype == "bf16" else 0)
     kname = "cross_attn_mfma_kernel" if mfma else "cross_attn_kernel"
