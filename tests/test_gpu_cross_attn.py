@@ -152,11 +152,13 @@ def test_queue_counters_left_zero_between_calls():
 
 
 @pytest.mark.parametrize("ctx", [[5], [5, 0, 17], [0], [0, 0, 1]])
-def test_fewer_work_items_than_queues(ctx):
+@pytest.mark.parametrize("head_dim", [128, 256])
+def test_fewer_work_items_than_queues(ctx, head_dim):
     """One to three work items: the grid shrinks to the item count and only
-    that many queues are used."""
-    say(f"cross_attn: contexts {ctx} with one KV head")
-    geom = synth.custom_geometry("bf16", 4, 1, 128, 16)
+    that many queues are used (vector kernel at head_dim 128, matrix-core
+    kernel with four head_dim slices at 256)."""
+    say(f"cross_attn: contexts {ctx} with one KV head, head_dim {head_dim}")
+    geom = synth.custom_geometry("bf16", 4, 1, head_dim, 16)
     meta, q, k, v, table, seq = _custom(geom, ctx, seed=11)
     out = yb.cross_attn(q, k, v, table, seq, meta.max_seq_len)
     torch.cuda.synchronize()
@@ -164,13 +166,16 @@ def test_fewer_work_items_than_queues(ctx):
 
 
 @pytest.mark.parametrize("num_reqs", [2048, 2049])
-def test_request_count_at_the_schedule_switch(num_reqs):
+@pytest.mark.parametrize("head_dim", [64, 256])
+def test_request_count_at_the_schedule_switch(num_reqs, head_dim):
     """2048 requests fill the persistent schedule's prefix exactly; one more
-    takes the one-workgroup-per-item schedule.  Both match the oracle."""
-    say(f"cross_attn: {num_reqs} requests")
+    takes the one-workgroup-per-item schedule (at head_dim 256 also the
+    switch from the matrix-core kernel to the vector kernel).  Both match
+    the oracle."""
+    say(f"cross_attn: {num_reqs} requests, head_dim {head_dim}")
     rng = np.random.default_rng(num_reqs)
     ctx = [int(c) for c in rng.integers(0, 48, size=num_reqs)]
-    geom = synth.custom_geometry("bf16", 2, 1, 64, 16)
+    geom = synth.custom_geometry("bf16", 2, 1, head_dim, 16)
     meta, q, k, v, table, seq = _custom(geom, ctx, seed=13)
     ref = _oracle(meta, q, k, v)
     # a max_seq_len far past what the table rows span: partitions beyond the
