@@ -34,6 +34,9 @@
 //     group is raised only when a score exceeds it by more than 2^8, so the
 //     accumulators are rescaled rarely; sums stay within 256x the true terms.
 //   * p.v in fp32 FMA; bf16 values widen with one shift or mask.
+//   * The 64/LPR row groups of a wavefront merge by a reduce-scatter over the
+//     lane's row bits (lane-half swaps, DPP, swizzle): each accumulator value
+//     is rescaled and added by one lane, which ends with head_dim/64 columns.
 //
 // yoco_cross_attn_varlen generalises the query side ("You Only Cache Once, in
 // vLLM", section "Implementation in vLLM": the cross-decoder metadata keeps

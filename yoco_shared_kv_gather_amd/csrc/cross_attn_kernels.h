@@ -158,6 +158,42 @@ __device__ __forceinline__ float dpp_add(float v) {
   return v + __builtin_bit_cast(float, other);
 }
 
+// One step of a reduce-scatter across lane bit M of a wavefront (M = 4, 8,
+// 16 or 32).  Every lane holds a, its value of the half that the lanes with
+// the bit clear keep, and b, its value of the half that the lanes with the
+// bit set keep; the result, in every lane, is the kept half's value from the
+// lane of the pair with the bit clear (c) and from the one with the bit set
+// (s).  M = 16, 32: one v_permlane16_swap / v_permlane32_swap (the swap moves
+// exactly the two halves that change hands); M = 8: DPP rotation by 8 within
+// each 16-lane row (= lane xor 8); M = 4: LDS swizzle with xor mask 4.
+template <int M>
+__device__ __forceinline__ void exchange_halves(float a, float b, float& c, float& s) {
+  static_assert(M == 4 || M == 8 || M == 16 || M == 32, "lane bit 2 to 5");
+  if constexpr (M == 16 || M == 32) {
+    typedef unsigned int u2 __attribute__((ext_vector_type(2)));
+    u2 r;
+    if constexpr (M == 16) {
+      r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    } else {
+      r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    }
+    c = __uint_as_float(r.x);
+    s = __uint_as_float(r.y);
+  } else {
+    const bool up = (threadIdx.x & M) != 0;
+    const int send = __float_as_int(up ? a : b);
+    int got;
+    if constexpr (M == 8) {
+      got = __builtin_amdgcn_update_dpp(0, send, 0x128, 0xf, 0xf, false);
+    } else {
+      got = __builtin_amdgcn_ds_swizzle(send, 0x101f);
+    }
+    const float recv = __int_as_float(got);
+    c = up ? recv : a;
+    s = up ? b : recv;
+  }
+}
+
 // Sum over aligned groups of kLanes lanes (4, 8 or 16), result in every lane.
 // quad_perm [1,0,3,2] and [2,3,0,1] pair lanes inside a quad; row_half_mirror
 // pairs each quad of 8 lanes with the other; row_mirror pairs the two halves
@@ -878,38 +914,51 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
         ++rd;
       }
 
-      // Combine the row groups of the wavefront (lanes with the same cl).
-#pragma unroll
-      for (int mask = kLpr; mask < 64; mask <<= 1) {
+      // Combine the row groups of the wavefront (lanes with the same cl) by
+      // a reduce-scatter over the lane's row bits, widest first: at each step
+      // the two lanes of a pair keep one half of their values each and take
+      // the partner's copy of that half, so every value is combined by one
+      // lane only; (m, l) are combined in both lanes of the pair, in the same
+      // operand order.  A lane ends with kNV * kLpr / 64 = D / 64 consecutive
+      // values (first value index `keep`) of every query vector.
+      constexpr int kNV = kCpl * kEpc;
+      constexpr int kKeep = kNV * kLpr / 64;
+      static_assert(kKeep >= 1 && kEpc % kKeep == 0, "kept values lie in one chunk");
+      int keep = 0;
+      auto combine_step = [&](auto mask_c, auto cur_c) {
+        constexpr int M = decltype(mask_c)::value;
+        constexpr int kHalf = decltype(cur_c)::value / 2;
+        keep += (lane & M) != 0 ? kHalf : 0;
 #pragma unroll
         for (int h = 0; h < VG; ++h) {
-          const float mo = __shfl_xor(m[h], mask, 64);
-          const float lo = __shfl_xor(lsum[h], mask, 64);
-          const float mx = fmaxf(m[h], mo);
-          const float fa = exp2f(m[h] - mx);
-          const float fb = exp2f(mo - mx);
-          lsum[h] = lsum[h] * fa + lo * fb;
-#pragma unroll
-          for (int i = 0; i < kCpl; ++i)
-#pragma unroll
-            for (int e = 0; e < kEpc; ++e) {
-              const float other = __shfl_xor(acc[h][i][e], mask, 64);
-              acc[h][i][e] = acc[h][i][e] * fa + other * fb;
-            }
+          float mc, ms, lc, ls;
+          exchange_halves<M>(m[h], m[h], mc, ms);
+          exchange_halves<M>(lsum[h], lsum[h], lc, ls);
+          const float mx = fmaxf(mc, ms);
+          const float fc = exp2f(mc - mx);
+          const float fs = exp2f(ms - mx);
+          lsum[h] = lc * fc + ls * fs;
           m[h] = mx;
-        }
-      }
-      if (row == 0) {
 #pragma unroll
-        for (int h = 0; h < VG; ++h) {
-#pragma unroll
-          for (int i = 0; i < kCpl; ++i)
-#pragma unroll
-            for (int e = 0; e < kEpc; ++e) sm.acc[wave][h][(cl + kLpr * i) * kEpc + e] = acc[h][i][e];
-          if (cl == 0) {
-            sm.ml[wave][h][0] = m[h];
-            sm.ml[wave][h][1] = lsum[h];
+          for (int j = 0; j < kHalf; ++j) {
+            float c, t;
+            exchange_halves<M>(acc[h][j / kEpc][j % kEpc], acc[h][(j + kHalf) / kEpc][(j + kHalf) % kEpc], c, t);
+            acc[h][j / kEpc][j % kEpc] = c * fc + t * fs;
           }
+        }
+      };
+      combine_step(std::integral_constant<int, 32>(), std::integral_constant<int, kNV>());
+      if constexpr (kLpr <= 16) combine_step(std::integral_constant<int, 16>(), std::integral_constant<int, kNV / 2>());
+      if constexpr (kLpr <= 8) combine_step(std::integral_constant<int, 8>(), std::integral_constant<int, kNV / 4>());
+      if constexpr (kLpr <= 4) combine_step(std::integral_constant<int, 4>(), std::integral_constant<int, kNV / 8>());
+      const int col0 = (cl + kLpr * (keep / kEpc)) * kEpc + keep % kEpc;
+#pragma unroll
+      for (int h = 0; h < VG; ++h) {
+#pragma unroll
+        for (int j = 0; j < kKeep; ++j) sm.acc[wave][h][col0 + j] = acc[h][0][j];
+        if (lane == 0) {
+          sm.ml[wave][h][0] = m[h];
+          sm.ml[wave][h][1] = lsum[h];
         }
       }
     }
