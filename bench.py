@@ -665,9 +665,10 @@ def bench_cross(args, pool):
     cu = torch.from_numpy(meta.cu_seqlens).to(dev)
     slots = torch.from_numpy(meta.slot_mapping).to(dev)
     code = yb.DTYPE_BF16 if geom.dtype == "bf16" else yb.DTYPE_F32
-    span = meta.max_seq_len if W <= 0 else min(meta.max_seq_len, W + Q - 1)
-    part, nparts = yb.describe_launch(R, geom.num_kv_heads, geom.head_dim, span, geom.block_size,
-                                      args.partition_tokens)
+    attn_dtype = yb.DTYPE_FP8_E4M3 if args.fp8 else code
+    part, piece, tail, nparts = yb.cross_attn_partition_split(R, geom.num_kv_heads, geom.head_dim, meta.max_seq_len,
+                                                              geom.block_size, args.partition_tokens, attn_dtype,
+                                                              Q if varlen else 1, W)
     if varlen:
         ws_bytes = yb.cross_attn_varlen_workspace_size(num_rows, R, geom.num_q_heads, geom.num_kv_heads,
                                                        geom.head_dim, meta.max_seq_len, Q, W, geom.block_size,
@@ -727,7 +728,8 @@ def bench_cross(args, pool):
             flush.sum(dtype=torch.int64)
         step()
     torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps); partition_tokens {part}, {nparts} partitions per request")
+    log(f"warmup done ({args.warmup} steps); partition_tokens {part} (last {tail} tokens in pieces of {piece}), "
+        f"at most {nparts} partitions per request")
 
     # Three events per step: step start, start of the cross layers, step end
     # (an event between every layer would add its own gap to every call).
@@ -812,6 +814,8 @@ def bench_cross(args, pool):
             "hidden": geom.hidden,
             "partition_tokens": part,
             "partitions_per_request": nparts,
+            "piece_tokens": piece,
+            "tail_tokens": tail,
             "llc_flushed_between_steps": not args.no_flush,
             "alternating_layer_order": not args.no_alternate,
             "parallelism": "single GPU",

@@ -79,10 +79,12 @@ typedef enum yoco_status {
 typedef enum yoco_dtype { YOCO_DTYPE_F32 = 0, YOCO_DTYPE_BF16 = 1, YOCO_DTYPE_FP8_E4M3 = 2 } yoco_dtype_t;
 
 /* yoco_cross_attn flag: walk the (request, KV head, partition) work items in
- * reverse order.  Alternating it between consecutive cross layers makes the
- * first blocks a layer reads the last ones the previous layer read, which may
- * still sit in the GPU's last-level cache (the kernels read K^/V^ rows with a
- * streaming hint that mostly keeps them out of it).  Results are
+ * reverse order (when contexts end in tail pieces, see partition_tokens:
+ * the full partitions and, separately, the pieces, which still come last).
+ * Alternating it between consecutive cross layers
+ * makes the first blocks a layer reads the last ones the previous layer read,
+ * which may still sit in the GPU's last-level cache (the kernels read K^/V^
+ * rows with a streaming hint that mostly keeps them out of it).  Results are
  * bit-identical either way. */
 #define YOCO_FLAG_REVERSE_ORDER 1u
 
@@ -311,13 +313,18 @@ int32_t yoco_kv_append_fp8(int32_t dtype, const void* x, int32_t num_tokens, int
  *                [0, min(max_seq_len, max_blocks_per_seq*block_size)].
  *   max_seq_len  an upper bound of seq_lens; sizes the split into partitions.
  *   scale        softmax scale; the pages' value is 1/sqrt(head_dim).
- *   partition_tokens  split-KV partition size P: 0 picks one from the
- *                shape (yoco_cross_attn_partition_tokens), otherwise a
- *                positive multiple of 64 spanning at most 511 blocks and at
- *                most 16384 tokens (YOCO_ERR_UNSUPPORTED beyond).  A context
- *                of n tokens is split into ceil(n/P) partitions of P tokens
- *                (the last one shorter); the shorter pieces come after all
- *                full partitions in the schedule.
+ *   partition_tokens  split-KV partition size P: a positive multiple of
+ *                64 spanning at most 511 blocks and at most 16384 tokens
+ *                (YOCO_ERR_UNSUPPORTED beyond); a context of n tokens is
+ *                split into ceil(n/P) partitions of P tokens (the last one
+ *                shorter).  0 lets the library pick P from the shape and the
+ *                kernel that runs; with at most 2048 requests on the
+ *                vector-ALU kernel it also cuts the last T tokens of every
+ *                context into pieces of Ps = P/4 tokens (rounded down to a
+ *                multiple of 64; only when that is 256 or more).
+ *                yoco_cross_attn_partition_split returns the plan.  The
+ *                shorter pieces come after all full partitions in the
+ *                schedule, so the work ends on short items.
  *   flags        YOCO_FLAG_REVERSE_ORDER or 0.
  *   out          fp32 [num_seqs][num_q_heads][head_dim].
  *   workspace    device scratch of at least yoco_cross_attn_workspace_size()
@@ -343,9 +350,26 @@ int32_t yoco_kv_append_fp8(int32_t dtype, const void* x, int32_t num_tokens, int
  * Results are deterministic: the same inputs give the same bits, with or
  * without YOCO_FLAG_REVERSE_ORDER.
  */
+/* P of the vector-ALU kernel's plan for these sizes (partition_tokens itself
+ * when positive); yoco_cross_attn_partition_split gives either kernel's whole
+ * plan. */
 int32_t yoco_cross_attn_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim,
                                          int32_t max_seq_len, int32_t block_size,
                                          int32_t partition_tokens);
+/* The split of every context into partitions that yoco_cross_attn
+ * (max_query_len 1, window 0) or yoco_cross_attn_varlen makes for these
+ * arguments (an FP8 cache's scale arrays taken as 16-byte aligned): writes
+ * split[0] = P, split[1] = Ps, split[2] = T (host array of three) and returns
+ * the most partitions any query's key range gets (-1 for invalid arguments).
+ * A key range of m tokens has big = m > T ? (m - T) / P : 0 partitions of P
+ * tokens, then the rest, m - big * P tokens, in pieces of Ps tokens (an
+ * empty range has one empty piece).  An explicit partition_tokens, more than
+ * 2048 requests, or the matrix-core kernel give Ps = P and T = 0.  (The
+ * workspace helpers size for either kernel and do not take the cache type.) */
+int32_t yoco_cross_attn_partition_split(int32_t dtype, int32_t num_seqs, int32_t max_query_len,
+                                        int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                                        int32_t window, int32_t block_size, int32_t partition_tokens,
+                                        uint32_t flags, int32_t* split);
 int64_t yoco_cross_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t max_seq_len, int32_t block_size,
                                        int32_t partition_tokens);

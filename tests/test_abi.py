@@ -90,6 +90,76 @@ def test_workspace_and_partition_sizes():
     assert yb.kv_append_workspace_size(yb.DTYPE_F32, 256, 1, 64) == 0
 
 
+SPLIT_SHAPES = [
+    # (num_seqs, num_kv_heads, head_dim, max_seq_len, block_size)
+    (32, 8, 128, 32768, 16),       # decode32x32k
+    (1, 8, 128, 524288, 32),       # long512k
+    (48, 8, 128, 32768, 16),       # mixed48
+    (64, 2, 256, 8192, 16),        # decode64
+    (4, 2, 128, 1000, 16),
+    (2, 1, 64, 5000, 1),
+    (3000, 8, 128, 5000, 16),      # one workgroup per item: no pieces
+]
+
+
+def _split_parts(m, P, Ps, T):
+    big = (m - T) // P if m > T else 0
+    rest = m - big * P
+    return [P] * big + ([Ps] * (rest // Ps) + ([rest % Ps] if rest % Ps else []) if m > 0 else [0])
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES)
+@pytest.mark.parametrize("dtype", [yb.DTYPE_F32, yb.DTYPE_BF16, yb.DTYPE_FP8_E4M3])
+def test_partition_split_tiles_every_range(shape, dtype):
+    """The split the library reports: full partitions of P tokens, then pieces
+    of Ps (the last one shorter) covering at least min(m, T) tokens; together
+    they tile every key range of m <= max_seq_len tokens, and the reported
+    count is the most any such range gets (attained, so the workspace holds no
+    idle slots beyond it).  Pieces only on the vector-ALU kernel's persistent
+    schedule (the matrix-core kernel runs an FP8 cache and bf16 at head_dim
+    256 when block_size >= 16)."""
+    R, hkv, d, max_len, bs = shape
+    P, Ps, T, most = yb.cross_attn_partition_split(R, hkv, d, max_len, bs, 0, dtype)
+    matrix = R <= 2048 and bs >= 16 and (dtype == yb.DTYPE_FP8_E4M3 or (dtype == yb.DTYPE_BF16 and d == 256))
+    if not matrix:
+        assert P == yb.cross_attn_partition_tokens(R, hkv, d, max_len, bs, 0)
+    assert P % 64 == 0 and Ps % 64 == 0 and 64 <= Ps <= P and 0 <= T <= max_len
+    if R > 2048 or matrix or P // 4 // 64 * 64 < 256:
+        assert (Ps, T) == (P, 0)
+    else:
+        assert Ps == P // 4 // 64 * 64 and T > 0
+    lens = set(range(0, min(max_len, 3 * P) + 1)) | set(range(max(0, max_len - 3 * P), max_len + 1))
+    lens |= {T + k * P + e for k in range(0, max_len // P + 1) for e in (-1, 0, 1)}
+    seen = 0
+    for m in sorted(x for x in lens if 0 <= x <= max_len):
+        parts = _split_parts(m, P, Ps, T)
+        big = (m - T) // P if m > T else 0
+        if m == 0:
+            assert parts == [0]
+        else:
+            assert sum(parts) == m and min(parts) > 0
+            assert parts[:big] == [P] * big and all(x <= Ps for x in parts[big:])
+            assert m - big * P >= min(m, T)              # the pieces hold the last T tokens at least
+        seen = max(seen, len(parts))
+    assert seen == most
+    # an explicit partition size is taken as is
+    assert yb.cross_attn_partition_split(R, hkv, d, max_len, bs, 128, dtype)[:3] == (128, 128, 0)
+
+
+@pytest.mark.parametrize("shape", SPLIT_SHAPES)
+def test_workspace_holds_either_kernels_partitions(shape):
+    """The workspace helpers do not take the cache type: they size for the
+    larger of the vector-ALU kernel's plan (fp32 cache) and the matrix-core
+    kernel's (FP8 cache)."""
+    R, hkv, d, max_len, bs = shape
+    most = max(yb.cross_attn_partition_split(R, hkv, d, max_len, bs, 0, dt)[3]
+               for dt in (yb.DTYPE_F32, yb.DTYPE_FP8_E4M3))
+    ws = yb.cross_attn_workspace_size(R, 8 * hkv, hkv, d, max_len, bs, 0)
+    acc = R * 8 * hkv * most * d * 4
+    assert most == 1 and ws == yb.CROSS_ATTN_QUEUE_BYTES or \
+        ws == yb.CROSS_ATTN_QUEUE_BYTES + -(-acc // 256) * 256 + R * 8 * hkv * most * 2 * 4
+
+
 def _append(**kw):
     args = dict(dtype=1, x=FAKE, T=4, hidden=256, w=FAKE, eps=1e-6, wk=FAKE, wv=FAKE, slots=FAKE, k=FAKE, v=FAKE,
                 nb=8, hkv=2, bs=16, d=128, ws=FAKE, ws_bytes=1 << 30, stream=None)

@@ -32,17 +32,26 @@ def range_lo(n, ql, window):
     return 0 if window <= 0 else max(n - ql - window + 1, 0)
 
 
-def tiles_of_batch(seq_lens, ql, window, part, bs, num_kv_heads, nk, aligned_standin=True):
+def partitions(m, split):
+    """(start, length) of every partition of a key range of m tokens under the
+    library's split (P, Ps, T): full partitions of P tokens, then the rest in
+    pieces of Ps tokens."""
+    P, Ps, T = split
+    big = (m - T) // P if m > T else 0
+    rest = m - big * P
+    small = 1 if m <= 0 else -(-rest // Ps)
+    return [(p * P, P) if p < big else (big * P + (p - big) * Ps, Ps) for p in range(big + small)]
+
+
+def tiles_of_batch(seq_lens, ql, window, split, bs, num_kv_heads, nk, aligned_standin=True):
     """Yield (first row, slice entry, entries in slice, row within block) of
     every 16-row tile load of every item, as the kernel computes them."""
     shift = bs.bit_length() - 1
     for n in seq_lens:
         lo = range_lo(n, ql, window)
-        m = n - lo
-        nparts = max(1, -(-m // part)) if m > 0 else 1
-        for p in range(nparts):
-            start = lo + p * part
-            end = min(start + part, n)
+        for off, size in partitions(n - lo, split):
+            start = lo + off
+            end = min(start + size, n)
             if end <= start:
                 continue
             first_blk = start >> shift
@@ -77,10 +86,11 @@ BATCHES = [
 def test_every_tile_stays_in_its_block(seq_lens, ql, window, bs, eb, d):
     hkv = 8
     span = max(seq_lens) if window <= 0 else min(max(seq_lens), window + ql - 1)
-    part = yb.cross_attn_partition_tokens(len(seq_lens), hkv, d, span, bs, 0)
-    assert part > 0 and part % 64 == 0
+    dtype = yb.DTYPE_FP8_E4M3 if eb == 1 else yb.DTYPE_BF16
+    P, Ps, T, _ = yb.cross_attn_partition_split(len(seq_lens), hkv, d, max(seq_lens), bs, 0, dtype, ql, window)
+    assert P > 0 and P % 64 == 0 and Ps % 64 == 0 and 0 < Ps <= P and T >= 0
     nk = keys_per_iteration(eb, d)
-    for row, entry, entries in tiles_of_batch(seq_lens, ql, window, part, bs, hkv, nk):
+    for row, entry, entries in tiles_of_batch(seq_lens, ql, window, (P, Ps, T), bs, hkv, nk):
         assert 0 <= entry < entries <= MAX_SLICE
         assert row % 16 == 0 and row + 15 < bs
 
@@ -89,7 +99,8 @@ def test_unaligned_standin_would_leave_the_block():
     """With the item's own start as the stand-in, a windowed batch has tiles
     whose 16 rows run past the end of their block."""
     seq_lens, ql, window, bs, eb, d = BATCHES[0]
-    part = yb.cross_attn_partition_tokens(len(seq_lens), 8, d, min(max(seq_lens), window + ql - 1), bs, 0)
-    rows = [row for row, _, _ in tiles_of_batch(seq_lens, ql, window, part, bs, 8, keys_per_iteration(eb, d),
+    split = yb.cross_attn_partition_split(len(seq_lens), 8, d, max(seq_lens), bs, 0,
+                                          yb.DTYPE_FP8_E4M3 if eb == 1 else yb.DTYPE_BF16, ql, window)[:3]
+    rows = [row for row, _, _ in tiles_of_batch(seq_lens, ql, window, split, bs, 8, keys_per_iteration(eb, d),
                                                 aligned_standin=False)]
     assert max(rows) + 15 >= bs

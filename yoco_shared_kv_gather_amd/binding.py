@@ -49,6 +49,7 @@ SIGNATURES = {
     "yoco_kv_append": (_i32, [_i32, _vp, _i32, _i32, _vp, _f32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                               _vp, _i64, _vp]),
     "yoco_cross_attn_partition_tokens": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "yoco_cross_attn_partition_split": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _u32, _vp]),
     "yoco_cross_attn_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "yoco_cross_attn": (_i32, [_i32, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _f32,
                                _i32, _u32, _vp, _vp, _i64, _vp]),
@@ -248,6 +249,18 @@ def cross_attn_partition_tokens(num_seqs, num_kv_heads, head_dim, max_seq_len, b
                                                        partition_tokens))
 
 
+def cross_attn_partition_split(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens=0,
+                               dtype=DTYPE_BF16, max_query_len=1, window=0, flags=0):
+    """(P, Ps, T, most partitions per key range) of the split of every context
+    into partitions that the attention call with these arguments makes, or
+    None for invalid arguments."""
+    split = (ctypes.c_int32 * 3)()
+    most = int(lib().yoco_cross_attn_partition_split(dtype, num_seqs, max_query_len, num_kv_heads, head_dim,
+                                                     max_seq_len, window, block_size, partition_tokens, flags,
+                                                     split))
+    return None if most < 0 else (int(split[0]), int(split[1]), int(split[2]), most)
+
+
 def cross_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size,
                               partition_tokens=0) -> int:
     return int(lib().yoco_cross_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len,
@@ -432,7 +445,11 @@ def library_path() -> str:
     return LIB_PATH
 
 
-def describe_launch(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens=0) -> Tuple[int, int]:
-    """(partition_tokens, partitions per request) that yoco_cross_attn will use."""
-    p = cross_attn_partition_tokens(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens)
-    return p, max(1, -(-max(max_seq_len, 1) // p))
+def describe_launch(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens=0,
+                    dtype=DTYPE_BF16, max_query_len=1, window=0, flags=0) -> Tuple[int, int]:
+    """(full partition tokens, most partitions per key range) that the attention call will use."""
+    split = cross_attn_partition_split(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens,
+                                       dtype, max_query_len, window, flags)
+    if split is None:
+        raise ValueError("invalid sizes for a cross-attention launch")
+    return split[0], split[3]

@@ -93,21 +93,33 @@ int32_t max_partition(int32_t block_size) {
   return static_cast<int32_t>(cap < 16384 ? cap : 16384);
 }
 
+// `matrix`: the call runs the matrix-core kernel, which starts every item
+// from an empty pipeline (its next-item fetch and first tile are not
+// overlapped with the previous item), so it wants at least about 2048 items
+// when every context is full length; the vector kernel, which hands items
+// over while the next one's first rows are in flight, at least about 1024.
 int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
-                          int32_t block_size, int32_t requested) {
+                          int32_t block_size, int32_t requested, bool matrix) {
   if (requested > 0) return requested;
   const int64_t pairs = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
   const int64_t len = max_seq_len > 0 ? max_seq_len : 1;
   const int64_t d = head_dim > 0 ? head_dim : 128;
   int64_t p;
   if (num_seqs <= kMaxQueueSeqs) {
-    // Persistent schedule: items of about 512 KB of bf16 K^/V^ (P*D = 2^17:
-    // measured best on all four workloads within ~1.5%), but at least about
-    // 1024 items when every context is full length (two per resident
-    // workgroup) and at most 256 partitions per request, so the merge stays
-    // small next to the stream.
-    p = yoco::round_up((int64_t{1} << 17) / d, 64);
-    const int64_t p_items = yoco::round_up(yoco::ceil_div(len, yoco::ceil_div(1024, pairs)), 64);
+    // Persistent schedule: items of about 2 MB of bf16 K^/V^ (P*D = 2^19),
+    // but at least about 1024 items (matrix kernel 2048) when every context
+    // is full length and at most 256 partitions per request, so the merge
+    // stays small next to the stream.  Each item ends in a hand-over
+    // (combine, write the partial, stage the next slice) during which the
+    // workgroup has little in flight, so with the tail pieces below taking
+    // care of the queue's end, long items pay: decode32x32k 694 us per layer
+    // at P*D = 2^17, 668 at 2^18, 658 at 2^19, 670 at 2^20; mixed48 380,
+    // 364, 363, 372 us.  Matrix kernel without pieces, against 2^17:
+    // decode32x32k with an FP8 cache 401 -> 365 us, with four query rows
+    // 763 -> 691 us.
+    p = yoco::round_up((int64_t{1} << 19) / d, 64);
+    const int64_t min_items = matrix ? 2048 : 1024;
+    const int64_t p_items = yoco::round_up(yoco::ceil_div(len, yoco::ceil_div(min_items, pairs)), 64);
     if (p > p_items) p = p_items;
     if (p < 256) p = 256;
     const int64_t p_merge = yoco::round_up(yoco::ceil_div(len, 256), 64);
@@ -123,9 +135,83 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t head_d
   return static_cast<int32_t>(p);
 }
 
-int32_t num_partitions(int32_t max_seq_len, int32_t part_tokens) {
-  const int64_t np = yoco::ceil_div(max_seq_len > 0 ? max_seq_len : 1, part_tokens);
-  return static_cast<int32_t>(np);
+// Tail pieces, when the library picks the partition for the vector kernel's
+// persistent schedule: the last T tokens of every context (and whatever is left over
+// from the full partitions) are cut into pieces of P/4 tokens, which the
+// schedule runs after every full partition.  The queue then ends on short
+// items instead of leaving workgroups idle while the last ones finish a full
+// partition (which cost about 3% of a layer on decode32x32k and 8% on
+// long512k, with 2048-token partitions).  T is derived from the sizes alone
+// (no device query, so the workspace helpers give the same plan): with
+// every context full length the pieces are about two rounds of a nominal
+// 512 resident workgroups, T = 256 P / (requests x KV heads).
+constexpr int kPieceDiv = 4;
+constexpr int64_t kMinPiece = 256;
+constexpr int64_t kNominalSlots = 512;
+
+Split resolve_split(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                    int32_t block_size, int32_t requested, bool matrix) {
+  Split s;
+  s.P = resolve_partition(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, requested, matrix);
+  s.Ps = s.P;
+  s.T = 0;
+  // The matrix-core kernel pays a full pipeline start per item, which costs
+  // more than the pieces save (long512k with an FP8 cache: 184 us per layer
+  // without, 200 with).
+  if (requested > 0 || num_seqs > kMaxQueueSeqs || matrix) return s;
+  const int64_t ps = s.P / kPieceDiv / 64 * 64;
+  if (ps < kMinPiece) return s;
+  const int64_t pairs = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
+  int64_t t = yoco::round_up(yoco::ceil_div(kNominalSlots / 2 * s.P, pairs), ps);
+  const int64_t len = max_seq_len > 0 ? max_seq_len : 1;
+  if (t > len) t = len;
+  s.Ps = static_cast<int32_t>(ps);
+  s.T = static_cast<int32_t>(t);
+  return s;
+}
+
+// Whether a call runs the matrix-core kernel: where the work per byte
+// outgrows the vector ALUs (an FP8 cache, or several query rows per request),
+// and for a bf16 cache at head_dim 256, where the matrix kernel's four
+// head_dim slices per key tile stream faster than the vector kernel's 16
+// lanes per row (decode64: 110.5 -> 104.6 us per layer); persistent schedule
+// only.  (It reads 16-key tiles that lie inside one block: block_size >= 16;
+// an FP8 cache's scale arrays must be 16-byte aligned.)
+bool matrix_kernel(int32_t dtype, int32_t num_seqs, bool several_rows, int32_t head_dim, int32_t block_size,
+                   uint32_t flags, bool scales_aligned) {
+  const bool f8 = dtype == YOCO_DTYPE_FP8_E4M3;
+  return (flags & YOCO_FLAG_VECTOR_KERNEL) == 0 && num_seqs <= kMaxQueueSeqs && block_size >= 16 &&
+         (!f8 || scales_aligned) && (f8 || (dtype == YOCO_DTYPE_BF16 && (several_rows || head_dim == 256)));
+}
+
+// Partition slots a workspace needs for calls of these sizes with any cache
+// type and flags: the larger of the two kernels' plans.
+int32_t workspace_parts(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t span, int32_t block_size,
+                        int32_t requested);
+
+// Most partitions of any key range of at most len tokens (the workspace's
+// partition slots).  Over ranges with the same number b of full partitions
+// the count grows with the length, and the longest such range has b plus
+// ceil((T + P - 1) / Ps) pieces; so the maximum is at len itself or at the
+// longest range with one full partition fewer.
+int32_t max_parts(const Split& s, int32_t len) {
+  const int32_t m = len > 0 ? len : 0;
+  int32_t best = s.parts(m);
+  const int32_t nb = s.big(m);
+  if (nb >= 1) {
+    const int64_t m2 = static_cast<int64_t>(s.T) + static_cast<int64_t>(nb) * s.P - 1;
+    const int32_t alt = s.parts(static_cast<int32_t>(m2));
+    if (alt > best) best = alt;
+  }
+  return best;
+}
+
+int32_t workspace_parts(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t span, int32_t block_size,
+                        int32_t requested) {
+  const int32_t v = max_parts(resolve_split(num_seqs, num_kv_heads, head_dim, span, block_size, requested, false), span);
+  if (num_seqs > kMaxQueueSeqs || block_size < 16) return v;        // no matrix-core kernel for these sizes
+  const int32_t m = max_parts(resolve_split(num_seqs, num_kv_heads, head_dim, span, block_size, requested, true), span);
+  return v > m ? v : m;
 }
 
 // Workspace: [work-queue counters, kQueueHeaderBytes][acc fp32 num_seqs*Hq*num_parts*D | pad to 256]
@@ -232,21 +318,13 @@ int32_t run_cross_attn(const AttnCall& c, const char* who) {
     return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: q, caches and out must be 16-byte aligned", who);
 
   const int32_t span = effective_len(c.max_seq_len, c.max_qlen, c.window);
-  const int32_t part = resolve_partition(c.num_seqs, c.num_kv_heads, c.head_dim, span, c.block_size,
-                                         c.partition_tokens);
-  const int32_t nparts = num_partitions(span, part);
+  const bool mfma = matrix_kernel(c.dtype, c.num_seqs, c.qsl != nullptr && c.max_qlen > 1, c.head_dim, c.block_size,
+                                  c.flags, aligned16(c.k_scale) && aligned16(c.v_scale));
+  const Split split = resolve_split(c.num_seqs, c.num_kv_heads, c.head_dim, span, c.block_size,
+                                    c.partition_tokens, mfma);
+  const int32_t nparts = max_parts(split, span);
   if (nparts > kMaxParts)
     return fail(YOCO_ERR_UNSUPPORTED, "%s: %d partitions per request exceed %d", who, nparts, kMaxParts);
-  // Matrix cores where the work per byte outgrows the vector ALUs (an FP8
-  // cache, or several query rows per request), and for a bf16 cache at
-  // head_dim 256, where the matrix kernel's four head_dim slices per key tile
-  // stream faster than the vector kernel's 16 lanes per row (decode64: 110.5
-  // -> 104.6 us per layer); persistent schedule only.  (It reads 16-key tiles
-  // that lie inside one block: block_size >= 16.)
-  const bool mfma =
-      (c.flags & YOCO_FLAG_VECTOR_KERNEL) == 0 && c.num_seqs <= kMaxQueueSeqs && c.block_size >= 16 &&
-      (!f8 || (aligned16(c.k_scale) && aligned16(c.v_scale))) &&
-      (f8 || (c.dtype == YOCO_DTYPE_BF16 && ((c.qsl != nullptr && c.max_qlen > 1) || c.head_dim == 256)));
   const int rows_wide = (mfma ? 16 : 8) / group;
   const int qpi = c.qsl == nullptr ? 0 : (c.max_qlen > 1 ? rows_wide : 1);
   const int64_t groups = qpi == 0 ? 1 : yoco::ceil_div(c.max_qlen, qpi);
@@ -285,7 +363,7 @@ int32_t run_cross_attn(const AttnCall& c, const char* who) {
   a.max_blocks = c.max_blocks_per_seq;
   const int64_t cap = static_cast<int64_t>(c.max_blocks_per_seq) * c.block_size;
   a.len_cap = static_cast<int32_t>(cap < c.max_seq_len ? cap : c.max_seq_len);
-  a.part_tokens = part;
+  a.split = split;
   a.num_parts = nparts;
   a.scale_log2 = c.scale * kLog2e;
   a.flags = c.flags;
@@ -404,8 +482,9 @@ extern "C" int32_t yoco_cross_attn_noalloc(int32_t dtype, const void* q, int32_t
   // the scratch the call needs, checked before anything is looked up or launched
   if (num_seqs >= 0 && num_q_heads > 0 && num_kv_heads > 0 && head_dim > 0 && max_seq_len >= 0 && block_size > 0 &&
       partition_tokens >= 0) {
-    const int32_t p = resolve_partition(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens);
-    const int64_t need = workspace_layout(num_seqs, num_q_heads, head_dim, num_partitions(max_seq_len, p)).total;
+    const bool mfma = matrix_kernel(dtype, num_seqs, false, head_dim, block_size, flags, true);
+    const Split sp = resolve_split(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens, mfma);
+    const int64_t need = workspace_layout(num_seqs, num_q_heads, head_dim, max_parts(sp, max_seq_len)).total;
     if (need > YOCO_CROSS_ATTN_NOALLOC_SCRATCH_BYTES)
       return yoco::fail(YOCO_ERR_WORKSPACE_TOO_SMALL,
                         "%s: the call needs %lld bytes of scratch, the static scratch holds %lld (use "
@@ -428,7 +507,23 @@ extern "C" int32_t yoco_cross_attn_partition_tokens(int32_t num_seqs, int32_t nu
                                                     int32_t max_seq_len, int32_t block_size,
                                                     int32_t partition_tokens) {
   if (partition_tokens < 0 || max_seq_len < 0 || block_size <= 0) return -1;
-  return resolve_partition(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens);
+  return resolve_partition(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens, false);
+}
+
+extern "C" int32_t yoco_cross_attn_partition_split(int32_t dtype, int32_t num_seqs, int32_t max_query_len,
+                                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                                                   int32_t window, int32_t block_size, int32_t partition_tokens,
+                                                   uint32_t flags, int32_t* split) {
+  if (partition_tokens < 0 || max_seq_len < 0 || max_query_len < 0 || window < 0 || block_size <= 0 ||
+      split == nullptr)
+    return -1;
+  const int32_t span = effective_len(max_seq_len, max_query_len, window);
+  const bool mfma = matrix_kernel(dtype, num_seqs, max_query_len > 1, head_dim, block_size, flags, true);
+  const Split s = resolve_split(num_seqs, num_kv_heads, head_dim, span, block_size, partition_tokens, mfma);
+  split[0] = s.P;
+  split[1] = s.Ps;
+  split[2] = s.T;
+  return max_parts(s, span);
 }
 
 extern "C" int64_t yoco_cross_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
@@ -437,8 +532,9 @@ extern "C" int64_t yoco_cross_attn_workspace_size(int32_t num_seqs, int32_t num_
   if (num_seqs < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_seq_len < 0 ||
       block_size <= 0 || partition_tokens < 0)
     return -1;
-  const int32_t p = resolve_partition(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens);
-  return workspace_layout(num_seqs, num_q_heads, head_dim, num_partitions(max_seq_len, p)).total;
+  return workspace_layout(num_seqs, num_q_heads, head_dim,
+                          workspace_parts(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens))
+      .total;
 }
 
 extern "C" int64_t yoco_cross_attn_varlen_workspace_size(int32_t num_rows, int32_t num_seqs, int32_t num_q_heads,
@@ -450,8 +546,9 @@ extern "C" int64_t yoco_cross_attn_varlen_workspace_size(int32_t num_rows, int32
       max_query_len < 0 || window < 0 || block_size <= 0 || partition_tokens < 0)
     return -1;
   const int32_t span = effective_len(max_seq_len, max_query_len, window);
-  const int32_t p = resolve_partition(num_seqs, num_kv_heads, head_dim, span, block_size, partition_tokens);
-  return workspace_layout(num_rows, num_q_heads, head_dim, num_partitions(span, p)).total;
+  return workspace_layout(num_rows, num_q_heads, head_dim,
+                          workspace_parts(num_seqs, num_kv_heads, head_dim, span, block_size, partition_tokens))
+      .total;
 }
 
 extern "C" int32_t yoco_cross_attn(int32_t dtype, const void* q, int32_t num_seqs, int32_t num_q_heads,

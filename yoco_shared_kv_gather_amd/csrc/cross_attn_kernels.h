@@ -27,6 +27,34 @@ constexpr int kQueueLineWords = 32;        // the two queue counters sit on sepa
 constexpr int64_t kQueueHeaderBytes = 2048; // queue counters, the rest reserved
 static_assert(kQueueHeaderBytes == YOCO_CROSS_ATTN_QUEUE_BYTES, "queue header size");
 
+// How the key range of one context (m tokens) is cut into partitions.  The
+// first big(m) partitions hold P tokens each ("big"); the rest -- at least
+// min(m, T) and fewer than T + P tokens -- is cut into pieces of Ps tokens,
+// the last one shorter ("small"; an empty range has one, empty, small
+// partition).  T = 0 with Ps = P gives ceil(m/P) partitions of P tokens.
+// The persistent schedule numbers every big item before every small one, so
+// the work ends on short items.
+struct Split {
+  int32_t P;    // tokens of a full partition
+  int32_t Ps;   // tokens of a tail piece (Ps <= P)
+  int32_t T;    // tokens at the end of every range that go into pieces
+  __host__ __device__ int big(int m) const { return m > T ? (m - T) / P : 0; }
+  __host__ __device__ int small(int m) const {
+    const int rest = m - big(m) * P;
+    return m <= 0 ? 1 : rest / Ps + (rest % Ps != 0 ? 1 : 0);
+  }
+  __host__ __device__ int parts(int m) const { return big(m) + small(m); }
+  // parts(m) == 1, without a division: T = 0 comes with Ps = P, and T > 0
+  // is at least Ps unless every range is shorter than Ps.
+  __host__ __device__ bool single(int m) const { return m <= Ps; }
+  // First token (relative to the range's start) and length of partition
+  // `part` of a range with nbig big partitions.
+  __host__ __device__ int start(int nbig, int part) const {
+    return part < nbig ? part * P : nbig * P + (part - nbig) * Ps;
+  }
+  __host__ __device__ int len(int nbig, int part) const { return part < nbig ? P : Ps; }
+};
+
 struct AttnArgs {
   const void* q;
   const void* k;
@@ -47,8 +75,8 @@ struct AttnArgs {
   int32_t bs_shift;
   int32_t max_blocks;
   int32_t len_cap;      // seq_lens are clamped to [0, len_cap]
-  int32_t part_tokens;
-  int32_t num_parts;
+  Split split;          // partitions of each context's key range
+  int32_t num_parts;    // partition slots per query row in the workspace (max over contexts)
   float scale_log2;     // scale * log2(e)
   uint32_t flags;
   const int32_t* qsl;   // query_start_loc [num_seqs+1] (several query rows per request), nullptr otherwise
@@ -208,15 +236,6 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Partitions of a context of n tokens: ceil(n/P) pieces of P tokens (the
-// last one shorter; an empty context has one, empty, partition).  For the
-// schedule they fall in two groups: the n/P full pieces ("big"), and the
-// shorter last piece if there is one ("small").  All big items are scheduled
-// before all small ones, so the work ends on the short pieces.
-__host__ __device__ inline int big_parts(int n, int P) { return n > 0 ? n / P : 0; }
-__host__ __device__ inline int small_parts(int n, int P) { return n <= 0 || n % P != 0 ? 1 : 0; }
-__host__ __device__ inline int parts_of(int n, int P) { return big_parts(n, P) + small_parts(n, P); }
-
 // Merge the partials of one (query row, query head):
 //   out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p,  M = max_p m_p.
 // S workgroups per (request, query row of the request, head), each for D/S
@@ -253,8 +272,9 @@ __global__ __launch_bounds__(kThreads) void cross_attn_merge_kernel(AttnArgs a) 
     row = qb + qi;
   }
   if (qi >= ql) return;
-  const int np = parts_of(n - range_lo(n, ql, a.window), a.part_tokens);
-  if (np <= 1) return;
+  const int m = n - range_lo(n, ql, a.window);
+  if (a.split.single(m)) return;
+  const int np = a.split.parts(m);
   const int64_t rh = static_cast<int64_t>(row) * a.num_q_heads + h;
   const float2* ml = reinterpret_cast<const float2*>(a.ws_ml) + rh * a.num_parts;
   const float4* acc = reinterpret_cast<const float4*>(a.ws_acc + rh * a.num_parts * D) + part_of_d * kSlices;
@@ -372,8 +392,10 @@ struct Item {
 // ballots): readfirstlane keeps them in scalar registers.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-__device__ __forceinline__ Item make_item(const AttnArgs& a, bool valid, int r, int g, int part, int n, int lo,
-                                          int row0, int nq, int pbase) {
+// `off` and `len`: the partition's first token relative to lo, and its
+// length (the caller knows whether it is a full partition or a piece).
+__device__ __forceinline__ Item make_item(bool valid, int r, int g, int part, int off, int len, int n, int lo,
+                                          int row0, int nq, int pbase, int bs_shift) {
   Item it;
   it.valid = valid;
   it.r = valid ? uniform(r) : 0;
@@ -384,12 +406,12 @@ __device__ __forceinline__ Item make_item(const AttnArgs& a, bool valid, int r, 
   it.row0 = valid ? uniform(row0) : 0;
   it.nq = valid ? uniform(nq) : 0;
   it.pbase = valid ? uniform(pbase) : 0;
-  it.start = it.lo + it.part * a.part_tokens;
-  it.end = min(it.start + a.part_tokens, it.n);
+  it.start = it.lo + (valid ? uniform(off) : 0);
+  it.end = min(it.start + (valid ? uniform(len) : 0), it.n);
   // An item without rows stages (harmlessly) the first table entry of its
   // row: its start may lie past the row's last entry.
-  it.first_blk = it.end > it.start ? it.start >> a.bs_shift : 0;
-  it.num_blk = it.end > it.start ? ((it.end - 1) >> a.bs_shift) - it.first_blk + 1 : 0;
+  it.first_blk = it.end > it.start ? it.start >> bs_shift : 0;
+  it.num_blk = it.end > it.start ? ((it.end - 1) >> bs_shift) - it.first_blk + 1 : 0;
   return it;
 }
 
@@ -503,8 +525,8 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
       const int ql = qlen_of(i);
       const int m = n - range_lo(n, ql, a.window);
       const int groups = kVar ? (ql + kQ - 1) / kQ : 1;
-      nb = big_parts(m, a.part_tokens) * a.num_kv_heads * groups;
-      ns = small_parts(m, a.part_tokens) * a.num_kv_heads * groups;
+      nb = a.split.big(m) * a.num_kv_heads * groups;
+      ns = a.split.small(m) * a.num_kv_heads * groups;
     };
     int local_b = 0, local_s = 0;
     for (int i = lo; i < hi; ++i) {
@@ -553,8 +575,15 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
   // Item number k of the persistent schedule.  Within a request, the KV head
   // varies fastest, then the query-row group, then the partition.
   auto item_at = [&](uint32_t k) -> Item {
-    if (k >= total) return make_item(a, false, 0, 0, 0, 0, 0, 0, 0, 0);
-    const uint32_t kk = reverse ? total - 1u - k : k;
+    if (k >= total) return make_item(false, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, a.bs_shift);
+    // The reverse order reverses the whole order when every context is cut
+    // into full partitions only (T = 0), so a layer starts where the previous
+    // one ended; with tail pieces it reverses the big items and, separately,
+    // the small ones, so the pieces stay last.
+    const bool k_big = k < total_big;
+    const uint32_t kk = !reverse ? k
+                        : a.split.T == 0 ? total - 1u - k
+                        : (k_big ? total_big - 1u - k : total + total_big - 1u - k);
     const bool big = kk < total_big;
     const int32_t* pref = big ? sm.pref : sm.pref2;
     const uint32_t j = big ? kk : kk - total_big;
@@ -569,12 +598,16 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     const int rem = idx - sub * per;
     const int qgrp = rem / a.num_kv_heads;
     const int g = rem - qgrp * a.num_kv_heads;
-    const int part = big ? sub : big_parts(n - lo, a.part_tokens) + sub;
+    // a full partition starts at sub * P; piece sub after the nbig full ones
+    const int nbig = big ? 0 : a.split.big(n - lo);
+    const int part = nbig + sub;
+    const int off = big ? sub * a.split.P : nbig * a.split.P + sub * a.split.Ps;
+    const int len = big ? a.split.P : a.split.Ps;
     if constexpr (kVar) {
-      return make_item(a, true, r, g, part, n, lo, sm.qs[r] + qgrp * kQ, min(kQ, ql - qgrp * kQ),
-                       n - ql + qgrp * kQ);
+      return make_item(true, r, g, part, off, len, n, lo, sm.qs[r] + qgrp * kQ, min(kQ, ql - qgrp * kQ),
+                       n - ql + qgrp * kQ, a.bs_shift);
     } else {
-      return make_item(a, true, r, g, part, n, lo, r, 1, n - 1);
+      return make_item(true, r, g, part, off, len, n, lo, r, 1, n - 1, a.bs_shift);
     }
   };
 
@@ -833,9 +866,11 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     const int r = static_cast<int>(rg / a.num_kv_heads);
     int n = a.seq_lens[r];
     n = n < 0 ? 0 : (n > a.len_cap ? a.len_cap : n);
-    cur = make_item(a, true, r, static_cast<int>(rg % a.num_kv_heads), part, n, range_lo(n, 1, a.window), r, 1,
-                    n - 1);
-    nxt = make_item(a, false, 0, 0, 0, 0, 0, 0, 0, 0);
+    const int lo = range_lo(n, 1, a.window);
+    const int nbig = a.split.big(n - lo);
+    cur = make_item(true, r, static_cast<int>(rg % a.num_kv_heads), part, a.split.start(nbig, part),
+                    a.split.len(nbig, part), n, lo, r, 1, n - 1, a.bs_shift);
+    nxt = make_item(false, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, a.bs_shift);
   }
 
   RowSet<kT, D> buf_a, buf_b;
@@ -983,7 +1018,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
     };
     if (cur.num_blk > 0) {
       // Combine the four wavefronts, then finish (one partition) or publish.
-      const int np_r = parts_of(cur.n - cur.lo, a.part_tokens);
+      const bool whole = a.split.single(cur.n - cur.lo);
       for (int e = tid; e < VG * D; e += kThreads) {
         const int h = e / D;
         const int d = e - h * D;
@@ -999,7 +1034,7 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
           den = fmaf(f, sm.ml[w][h][1], den);
           num = fmaf(f, sm.acc[w][h][d], num);
         }
-        if (np_r == 1) {
+        if (whole) {
           a.out[rh * D + d] = den == 0.0f ? 0.0f : num / den;
         } else {
           const int64_t slot = rh * a.num_parts + cur.part;

@@ -175,8 +175,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const int ql = qlen_of(i);
       const int m = n - range_lo(n, ql, a.window);
       const int groups = kVar ? (ql + kQ - 1) / kQ : 1;
-      nb = big_parts(m, a.part_tokens) * a.num_kv_heads * groups;
-      ns = small_parts(m, a.part_tokens) * a.num_kv_heads * groups;
+      nb = a.split.big(m) * a.num_kv_heads * groups;
+      ns = a.split.small(m) * a.num_kv_heads * groups;
     };
     int local_b = 0, local_s = 0;
     for (int i = lo; i < hi; ++i) {
@@ -223,8 +223,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
 
   auto item_at = [&](uint32_t k) -> Item {
-    if (k >= total) return make_item(a, false, 0, 0, 0, 0, 0, 0, 0, 0);
-    const uint32_t kk = reverse ? total - 1u - k : k;
+    if (k >= total) return make_item(false, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, a.bs_shift);
+    // reversed as a whole without tail pieces, else within the big and
+    // within the small items (the pieces stay last)
+    const bool k_big = k < total_big;
+    const uint32_t kk = !reverse ? k
+                        : a.split.T == 0 ? total - 1u - k
+                        : (k_big ? total_big - 1u - k : total + total_big - 1u - k);
     const bool big = kk < total_big;
     const int32_t* pref = big ? sm.pref : sm.pref2;
     const uint32_t j = big ? kk : kk - total_big;
@@ -239,12 +244,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int rem = idx - sub * per;
     const int qgrp = rem / a.num_kv_heads;
     const int g = rem - qgrp * a.num_kv_heads;
-    const int part = big ? sub : big_parts(n - lo, a.part_tokens) + sub;
+    // a full partition starts at sub * P; piece sub after the nbig full ones
+    const int nbig = big ? 0 : a.split.big(n - lo);
+    const int part = nbig + sub;
+    const int off = big ? sub * a.split.P : nbig * a.split.P + sub * a.split.Ps;
+    const int len = big ? a.split.P : a.split.Ps;
     if constexpr (kVar) {
-      return make_item(a, true, r, g, part, n, lo, sm.qs[r] + qgrp * kQ, min(kQ, ql - qgrp * kQ),
-                       n - ql + qgrp * kQ);
+      return make_item(true, r, g, part, off, len, n, lo, sm.qs[r] + qgrp * kQ, min(kQ, ql - qgrp * kQ),
+                       n - ql + qgrp * kQ, a.bs_shift);
     } else {
-      return make_item(a, true, r, g, part, n, lo, r, 1, n - 1);
+      return make_item(true, r, g, part, off, len, n, lo, r, 1, n - 1, a.bs_shift);
     }
   };
 
@@ -592,7 +601,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     };
     if (cur.num_blk > 0) {
-      const int np_r = parts_of(cur.n - cur.lo, a.part_tokens);
+      const bool whole = a.split.single(cur.n - cur.lo);
       for (int e = tid; e < VG * D; e += kThreads) {
         const int h = e / D;
         const int d = e - h * D;
@@ -613,7 +622,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
           den = fmaf(f, sm.ml[w][h][1], den);
           num = fmaf(f, sm.u.acc[w][h][dd], num);
         }
-        if (np_r == 1) {
+        if (whole) {
           a.out[rh * D + d] = den == 0.0f ? 0.0f : num / den;
         } else {
           const int64_t slot = rh * a.num_parts + cur.part;
