@@ -59,6 +59,9 @@ def parse():
                    help="time the self-decoder's gated retention instead (16 layers, 24 heads x 128) over the "
                         "mixed step's rows or 64 decode tokens")
     p.add_argument("--no-flush", action="store_true", help="keep the last-level cache warm between steps")
+    p.add_argument("--vector-kernel", action="store_true",
+                   help="run the vector-ALU attention kernel where the matrix-core kernel is the default "
+                        "(YOCO_FLAG_VECTOR_KERNEL; for comparison)")
     p.add_argument("--no-alternate", action="store_true",
                    help="every cross layer walks its work items in the same order (no last-level-cache reuse "
                         "between consecutive layers; for comparison)")
@@ -668,7 +671,8 @@ def bench_cross(args, pool):
     attn_dtype = yb.DTYPE_FP8_E4M3 if args.fp8 else code
     part, piece, tail, nparts = yb.cross_attn_partition_split(R, geom.num_kv_heads, geom.head_dim, meta.max_seq_len,
                                                               geom.block_size, args.partition_tokens, attn_dtype,
-                                                              Q if varlen else 1, W)
+                                                              Q if varlen else 1, W,
+                                                              yb.FLAG_VECTOR_KERNEL if args.vector_kernel else 0)
     if varlen:
         ws_bytes = yb.cross_attn_varlen_workspace_size(num_rows, R, geom.num_q_heads, geom.num_kv_heads,
                                                        geom.head_dim, meta.max_seq_len, Q, W, geom.block_size,
@@ -699,7 +703,8 @@ def bench_cross(args, pool):
     def order(layer):
         """Work order of a layer: odd layers reversed, so each layer starts on
         the blocks the previous one read last (unless --no-alternate)."""
-        return 0 if args.no_alternate else (layer & 1) * yb.FLAG_REVERSE_ORDER
+        force = yb.FLAG_VECTOR_KERNEL if args.vector_kernel else 0
+        return force | (0 if args.no_alternate else (layer & 1) * yb.FLAG_REVERSE_ORDER)
 
     def step(ev_layers_start=None):
         if args.fp8:
@@ -768,7 +773,7 @@ def bench_cross(args, pool):
     # query rows per request (bf16) or bf16 at head_dim 256, with
     # block_size >= 16 and <= 2048 requests
     mfma = ((args.fp8 or (geom.dtype == "bf16" and (Q > 1 or geom.head_dim == 256))) and R <= 2048
-            and geom.block_size >= 16)
+            and geom.block_size >= 16 and not args.vector_kernel)
     rows_per_item = 0 if Q == 1 else (16 if mfma else 8) // group
     elem_type = 2 if args.fp8 else (1 if geom.dtype == "bf16" else 0)
     kname = "cross_attn_mfma_kernel" if mfma else "cross_attn_kernel"

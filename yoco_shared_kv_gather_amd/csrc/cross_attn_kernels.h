@@ -853,10 +853,13 @@ __global__ __launch_bounds__(kThreads) void cross_attn_kernel(AttnArgs a) {
   // The first item (workgroup w starts with item w; the persistent schedule
   // fetches the next one while it runs).
   Item cur, nxt;
-  bool nxt_known = !persistent;
+  // with a workgroup for every item (the grid is at most the item count) no
+  // fetch can return an item: none is made
+  const bool grid_covers = persistent && gridDim.x >= total;
+  bool nxt_known = !persistent || grid_covers;
   if (persistent) {
     cur = item_at(blockIdx.x);
-    nxt = cur;
+    nxt = grid_covers ? make_item(false, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, a.bs_shift) : cur;
   } else {
     const uint32_t items = static_cast<uint32_t>(R) * a.num_kv_heads * a.num_parts;
     const uint32_t item = reverse ? items - 1u - blockIdx.x : blockIdx.x;

@@ -29,11 +29,9 @@
 // each computing the whole scores), which keeps two wavefronts per SIMD; a
 // bf16 cache at head_dim 256 takes this kernel also for one query row.
 //
-// The schedule, work items, partials and the merge kernel are those of the
-// VALU kernel; the item pipeline is simpler (the next item is fetched at the
-// start of the current one and its block-table slice and queries are loaded
-// into registers while the current one streams; rows are double-buffered
-// within an item).
+// The schedule, work items, partials, item pipeline and the merge kernel are
+// those of the VALU kernel: the next item is fetched before the current one's
+// last iteration, whose row request is already the next item's first tile.
 
 #pragma once
 
@@ -283,18 +281,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   };
 
   const int off_mask = a.block_size - 1;
-  auto load_rows = [&](Rows& rs, const Item& it, int base) {
+  // Block ids of this wavefront's first tiles of the next item (from the
+  // block table while that item's slice is not in LDS yet).
+  int32_t st_nb[kNT];
+  // Rows of an iteration starting at `base` of the item with key range
+  // [start, end), first slice entry first_blk and KV head g; block ids from
+  // the LDS slice, or (next) from st_nb.  Both sources are read, so there is
+  // no branch around the loads.
+  auto load_rows = [&](Rows& rs, int start, int end, int first_blk, int g, int base, bool next) {
     rs.base = base;
     rs.tmask = 0u;
     int64_t tile_row[kNT];         // cache row (block*Hkv + g)*bs + slot of each tile's first key
 #pragma unroll
     for (int t = 0; t < kNT; ++t) {
       const int p0 = base + 16 * t;
-      const int in = p0 < it.end ? p0 : (it.start & ~15);
-      const int blk = uniform(sm.blocks[(in >> a.bs_shift) - it.first_blk]);
+      const int in = p0 < end ? p0 : (start & ~15);
+      const int lds_blk = sm.blocks[next ? 0 : (in >> a.bs_shift) - first_blk];
+      const int blk = uniform(next ? st_nb[t] : lds_blk);
       const bool ok = blk >= 0;
       rs.tmask |= ok ? (1u << t) : 0u;
-      tile_row[t] = (static_cast<int64_t>(ok ? blk : 0) * a.num_kv_heads + it.g) * a.block_size + (in & off_mask);
+      tile_row[t] = (static_cast<int64_t>(ok ? blk : 0) * a.num_kv_heads + g) * a.block_size + (in & off_mask);
       const char* kt = static_cast<const char*>(a.k) + tile_row[t] * ML::kRowBytes;
 #pragma unroll
       for (int c = 0; c < kKL; ++c) {
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       const int key = chunk / ML::kChunksPerRow;
       const int cb = (chunk - key * ML::kChunksPerRow) * 16 + slice * ML::kVRowBytes;
       const int j = base + key;
-      rs.vmask |= ((rs.tmask >> t & 1u) != 0u && j >= it.start && j < it.end ? 1u : 0u) << c;
+      rs.vmask |= ((rs.tmask >> t & 1u) != 0u && j >= start && j < end ? 1u : 0u) << c;
       rs.v[c] = yoco::load_stream(static_cast<const char*>(a.v) + (tile_row[t] + (key - 16 * t)) * ML::kRowBytes + cb);
     }
   };
@@ -483,9 +489,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   uint4 st_q[kQPer];
   auto stage_load = [&](const Item& it) {
     if (it.num_blk > 0) {
-      const int32_t* table = a.block_table + static_cast<int64_t>(it.r) * a.max_blocks + it.first_blk;
+      const int32_t* row_table = a.block_table + static_cast<int64_t>(it.r) * a.max_blocks;
+      const int32_t* table = row_table + it.first_blk;
 #pragma unroll
       for (int k = 0; k < kTblPer; ++k) st_tbl[k] = table[min(tid + kThreads * k, it.num_blk - 1)];
+      // the tiles of this wavefront's first iteration (as load_rows places them)
+      const int base = (it.start & ~15) + group_u * kNK;
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) {
+        const int p0 = base + 16 * t;
+        const int in = p0 < it.end ? p0 : (it.start & ~15);
+        st_nb[t] = valid_block(row_table[in >> a.bs_shift]);
+      }
     }
 #pragma unroll
     for (int k = 0; k < kQPer; ++k) {
@@ -516,16 +531,56 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   };
 
-  // ---- items
+  // ---- items, pipelined as in the VALU kernel: the next item is known
+  // before the current one's last iteration (fetched at the start of a short
+  // item, or three rounds before the end of a longer one), that iteration
+  // requests this wavefront's first rows of it, and its slice and queries go
+  // to LDS while the finished item is combined.  A wavefront runs its
+  // iterations in pairs (ra, then rb; an odd count ends with a masked
+  // stand-in in rb), so the next item's first rows always land in ra and
+  // only one register set lives across the hand-over.
   Item cur = item_at(blockIdx.x);
-  if (cur.valid) stage_load(cur);
-  while (cur.valid) {
-    // next item now (the queue counter sits on its own line)
-    if (tid == 0) sm.next = gridDim.x + atomicAdd(fetch_ctr, 1u);
+  Item nxt = make_item(false, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, a.bs_shift);
+  if (cur.valid) {
+    stage_load(cur);
     stage_store(cur);
-    __syncthreads();
-    const Item nxt = item_at(static_cast<uint32_t>(uniform(static_cast<int>(sm.next))));
-    if (nxt.valid) stage_load(nxt);
+  }
+  __syncthreads();
+  Rows ra, rb;                                      // ra: this wavefront's first rows of `cur`
+  if (cur.valid && cur.num_blk > 0)
+    load_rows(ra, cur.start, cur.end, cur.first_blk, cur.g, (cur.start & ~15) + group_u * kNK, false);
+  while (cur.valid) {
+    const int base0 = cur.start & ~15;              // iterations start 16-aligned
+    const int num_iters = cur.num_blk > 0 ? (cur.end - base0 + kNK - 1) / kNK : 0;
+    const int rounds = num_iters / kGroups;         // iterations every wavefront group has
+    // with a workgroup for every item no fetch can return one: none is made
+    const bool fetch = gridDim.x < total;
+    const bool late = fetch && rounds >= 3;
+    if (fetch && !late) {
+      if (tid == 0) sm.next = gridDim.x + atomicAdd(fetch_ctr, 1u);
+      __syncthreads();
+      nxt = item_at(static_cast<uint32_t>(uniform(static_cast<int>(sm.next))));
+      stage_load(nxt);
+    }
+    uint32_t pending = 0;
+    auto late_fetch = [&](int rd) {
+      if (!late) return;
+      if (rd == rounds - 3 && tid == 0) pending = atomicAdd(fetch_ctr, 1u);
+      if (rd == rounds - 2) {
+        if (tid == 0) sm.next = gridDim.x + pending;
+        __syncthreads();
+        nxt = item_at(static_cast<uint32_t>(uniform(static_cast<int>(sm.next))));
+        stage_load(nxt);
+      }
+    };
+    // Rows of iteration i of `cur`; past its end (second of a pair) this
+    // wavefront's first rows of `nxt` when that has rows, else a masked
+    // stand-in.
+    auto load_step = [&](Rows& rs, int i, bool may_next) {
+      const bool next = may_next && i >= num_iters && nxt.valid && nxt.num_blk > 0;
+      load_rows(rs, next ? nxt.start : cur.start, next ? nxt.end : cur.end, next ? nxt.first_blk : cur.first_blk,
+                next ? nxt.g : cur.g, next ? (nxt.start & ~15) + group_u * kNK : base0 + i * kNK, next);
+    };
 
     if (cur.num_blk > 0) {
 #pragma unroll
@@ -549,28 +604,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       l_run = 0.0f;
 #pragma unroll
       for (int dt = 0; dt < kDT; ++dt) oacc[dt] = mfma_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      const int base0 = cur.start & ~15;           // iterations start 16-aligned
-      const int num_iters = (cur.end - base0 + kNK - 1) / kNK;
-      // The next iteration's rows are always requested, also past the item's
-      // end (load_rows then reads the item's first rows and masks them), so
-      // neither register set is written conditionally: a conditional load
-      // made the compiler copy whole register sets around the loop.
-      Rows ra, rb;
+      // The next iteration's rows are always requested (past the item's end
+      // the next item's, or a masked stand-in), so neither register set is
+      // written conditionally: a conditional load made the compiler copy
+      // whole register sets around the loop.  The late fetch acts at rounds
+      // every wavefront reaches with real iterations, before any padding.
       int it = group_u;
-      if (it < num_iters) {
-        load_rows(ra, cur, base0 + it * kNK);
-        for (;;) {
-          load_rows(rb, cur, base0 + (it + kGroups) * kNK);
-          compute(ra, 0);
-          it += kGroups;
-          if (it >= num_iters) break;
-          load_rows(ra, cur, base0 + (it + kGroups) * kNK);
-          compute(rb, 1);
-          it += kGroups;
-          if (it >= num_iters) break;
-        }
+      int rd = 0;
+      while (it < num_iters) {
+        late_fetch(rd);
+        load_step(rb, it + kGroups, false);
+        compute(ra, 0);
+        it += kGroups;
+        ++rd;
+        late_fetch(rd);
+        load_step(ra, it + kGroups, true);
+        compute(rb, 1);                             // past the end: the masked stand-in
+        it += kGroups;
+        ++rd;
       }
     }
+    // a wavefront without an iteration of this item requests its first rows
+    // of the next one now
+    if (group_u >= num_iters && nxt.valid && nxt.num_blk > 0) load_step(ra, num_iters, true);
     __syncthreads();                                 // every wavefront done with its V tile
 
     if (cur.num_blk > 0) {
@@ -590,8 +646,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         }
       }
     }
+    // the next item's slice and queries (the queries' LDS is free again)
+    if (nxt.valid) stage_store(nxt);
     __syncthreads();
-
     auto out_row = [&](int v) -> int64_t {
       if constexpr (kVar) {
         const int i = v / G;
@@ -642,7 +699,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     __syncthreads();                                 // sm reused by the next item
     cur = nxt;
+    nxt = make_item(false, 0, 0, 0, 0, 0, 0, 0, 0, 0, 0, a.bs_shift);
   }
+
 
   if (tid == 0) {
     const uint32_t d = atomicAdd(done_ctr, 1u);
