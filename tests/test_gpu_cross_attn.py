@@ -187,3 +187,60 @@ def test_request_count_at_the_schedule_switch(num_reqs, head_dim):
             err = _max_err(out, ref)
             say(f"  max_seq_len {max_len} partition {part}: max abs err {err:.3e}")
             assert err <= ATTN_ATOL
+
+
+def test_tail_pieces_every_output_both_orders():
+    """A batch whose default split ends every context in tail pieces (full
+    partitions of P tokens, then the last T or more tokens in pieces of P/4),
+    with contexts from 1 to 4096 tokens: every output against the oracle, and
+    the reverse order -- the full partitions and the pieces each reversed,
+    the pieces still last -- gives the same bits."""
+    rng = np.random.default_rng(77)
+    ctx = [4096] * 4 + [int(c) for c in rng.integers(1, 4097, size=28)]
+    geom = synth.custom_geometry("bf16", 32, 8, 128, 16)
+    meta, q, k, v, table, seq = _custom(geom, ctx, seed=21)
+    P, Ps, T, most = yb.cross_attn_partition_split(len(ctx), 8, 128, meta.max_seq_len, 16)
+    say(f"cross_attn: 32 requests up to 4096 tokens, P {P}, pieces of {Ps} over the last {T}")
+    assert T > 0 and Ps < P
+    ref = _oracle(meta, q, k, v)
+    a = yb.cross_attn(q, k, v, table, seq, meta.max_seq_len)
+    b = yb.cross_attn(q, k, v, table, seq, meta.max_seq_len, flags=yb.FLAG_REVERSE_ORDER)
+    torch.cuda.synchronize()
+    err = _max_err(a, ref)
+    say(f"  max abs err {err:.3e}")
+    assert err <= ATTN_ATOL
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("several", [False, True])
+def test_matrix_kernel_many_items_both_orders(several):
+    """The matrix-core kernel with more work items than resident workgroups
+    (FP8 cache, 32 requests x 8 KV heads up to 4096 tokens, some contexts
+    empty), so every workgroup hands items over with the next item's first
+    tile already requested: every output against the oracle over the
+    dequantized cache, and the reverse order gives the same bits."""
+    rng = np.random.default_rng(78)
+    ctx = [4096, 0, 4096, 1] + [int(c) for c in rng.integers(0, 4097, size=28)]
+    qlens = [min(c, 1 + i % 4) for i, c in enumerate(ctx)] if several else [1 if c > 0 else 0 for c in ctx]
+    geom = synth.custom_geometry("bf16", 32, 8, 128, 16)
+    meta = synth.make_varlen_metadata(geom, ctx, qlens, seed=22)
+    d = dev()
+    kc, ks, vc, vs = synth.make_fp8_cache(meta, d, 22)
+    rows = int(meta.cu_seqlens[-1])
+    q = synth.make_queries(meta, d, 22, num_layers=1, rows=rows)[0]
+    table = torch.from_numpy(meta.block_table).to(d)
+    seq = torch.from_numpy(meta.seq_lens).to(d)
+    qsl = torch.from_numpy(meta.cu_seqlens).to(d)
+    ql = max(qlens)
+    say(f"cross_attn_varlen FP8: 32 requests up to 4096 tokens, up to {ql} rows each")
+    kd = oracle.dequantize_cache(kc.cpu().numpy(), ks.cpu().numpy())
+    vd = oracle.dequantize_cache(vc.cpu().numpy(), vs.cpu().numpy())
+    ref = oracle.cross_attention_varlen(host(q), kd, vd, meta.block_table, meta.seq_lens, meta.cu_seqlens,
+                                        1.0 / math.sqrt(128), 0)
+    outs = [yb.cross_attn_varlen(q, kc, vc, table, seq, meta.max_seq_len, query_start_loc=qsl, max_query_len=ql,
+                                 k_scale=ks, v_scale=vs, flags=f) for f in (0, yb.FLAG_REVERSE_ORDER)]
+    torch.cuda.synchronize()
+    err = _max_err(outs[0], ref)
+    say(f"  max abs err {err:.3e}")
+    assert err <= ATTN_ATOL
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
