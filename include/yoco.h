@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define YOCO_ABI_VERSION 5
+#define YOCO_ABI_VERSION 6
 
 typedef enum yoco_status {
   YOCO_OK = 0,

@@ -19,7 +19,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 # the CPU tests load); by default the one built next to this file.
 LIB_PATH = os.environ.get("YOCO_LIBRARY") or os.path.join(PKG_DIR, "libyoco.so")
 
-ABI_VERSION = 5
+ABI_VERSION = 6
 YOCO_OK = 0
 YOCO_ERR_INVALID_ARGUMENT = 1
 YOCO_ERR_UNSUPPORTED = 2
