@@ -362,22 +362,25 @@ def cross_attention_varlen(q, k_cache, v_cache, block_table, seq_lens, query_sta
 E4M3_MAX = 448.0
 
 
+def _e4m3_value(c: int) -> float:
+    """Value of one FP8 E4M3 (finite-only) code."""
+    sign = -1.0 if c & 0x80 else 1.0
+    e = (c >> 3) & 0xF
+    m = c & 0x7
+    if e == 0xF and m == 0x7:
+        return np.nan
+    if e == 0:
+        return sign * m * 2.0 ** -9                    # subnormal: 0.mmm * 2^-6
+    return sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+# every code's value, from the formula above (a cache holds millions of codes)
+_E4M3_VALUES = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
 def e4m3_decode(codes) -> np.ndarray:
     """Value of every FP8 E4M3 (finite-only) code, as float64."""
-    codes = np.asarray(codes, dtype=np.uint8)
-    out = np.empty(codes.shape, dtype=np.float64)
-    for idx, c in np.ndenumerate(codes):
-        c = int(c)
-        sign = -1.0 if c & 0x80 else 1.0
-        e = (c >> 3) & 0xF
-        m = c & 0x7
-        if e == 0xF and m == 0x7:
-            out[idx] = np.nan
-        elif e == 0:
-            out[idx] = sign * m * 2.0 ** -9            # subnormal: 0.mmm * 2^-6
-        else:
-            out[idx] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
-    return out
+    return _E4M3_VALUES[np.asarray(codes, dtype=np.uint8).astype(np.intp)]
 
 
 def e4m3_encode(x) -> np.ndarray:
