@@ -318,10 +318,10 @@ int32_t yoco_kv_append_fp8(int32_t dtype, const void* x, int32_t num_tokens, int
  *                (YOCO_ERR_UNSUPPORTED beyond); a context of n tokens is
  *                split into ceil(n/P) partitions of P tokens (the last one
  *                shorter).  0 lets the library pick P from the shape and the
- *                kernel that runs; with at most 2048 requests on the
- *                vector-ALU kernel it also cuts the last T tokens of every
- *                context into pieces of Ps = P/4 tokens (rounded down to a
- *                multiple of 64; only when that is 256 or more).
+ *                kernel that runs; with at most 2048 requests it also cuts
+ *                the last T tokens of every context into pieces of Ps = P/4
+ *                tokens (rounded down to a multiple of 64; only when that is
+ *                256 or more).
  *                yoco_cross_attn_partition_split returns the plan.  The
  *                shorter pieces come after all full partitions in the
  *                schedule, so the work ends on short items.
@@ -363,9 +363,9 @@ int32_t yoco_cross_attn_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
  * the most partitions any query's key range gets (-1 for invalid arguments).
  * A key range of m tokens has big = m > T ? (m - T) / P : 0 partitions of P
  * tokens, then the rest, m - big * P tokens, in pieces of Ps tokens (an
- * empty range has one empty piece).  An explicit partition_tokens, more than
- * 2048 requests, or the matrix-core kernel give Ps = P and T = 0.  (The
- * workspace helpers size for either kernel and do not take the cache type.) */
+ * empty range has one empty piece).  An explicit partition_tokens, or more
+ * than 2048 requests, give Ps = P and T = 0.  (The workspace helpers size for
+ * either kernel and do not take the cache type.) */
 int32_t yoco_cross_attn_partition_split(int32_t dtype, int32_t num_seqs, int32_t max_query_len,
                                         int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
                                         int32_t window, int32_t block_size, int32_t partition_tokens,

@@ -115,16 +115,16 @@ def test_partition_split_tiles_every_range(shape, dtype):
     of Ps (the last one shorter) covering at least min(m, T) tokens; together
     they tile every key range of m <= max_seq_len tokens, and the reported
     count is the most any such range gets (attained, so the workspace holds no
-    idle slots beyond it).  Pieces only on the vector-ALU kernel's persistent
-    schedule (the matrix-core kernel runs an FP8 cache and bf16 at head_dim
-    256 when block_size >= 16)."""
+    idle slots beyond it).  Pieces on the persistent schedule of either kernel
+    (the matrix-core kernel, which runs an FP8 cache and bf16 at head_dim 256
+    when block_size >= 16, with at least ~2048 items instead of ~1024)."""
     R, hkv, d, max_len, bs = shape
     P, Ps, T, most = yb.cross_attn_partition_split(R, hkv, d, max_len, bs, 0, dtype)
     matrix = R <= 2048 and bs >= 16 and (dtype == yb.DTYPE_FP8_E4M3 or (dtype == yb.DTYPE_BF16 and d == 256))
     if not matrix:
         assert P == yb.cross_attn_partition_tokens(R, hkv, d, max_len, bs, 0)
     assert P % 64 == 0 and Ps % 64 == 0 and 64 <= Ps <= P and 0 <= T <= max_len
-    if R > 2048 or matrix or P // 4 // 64 * 64 < 256:
+    if R > 2048 or P // 4 // 64 * 64 < 256:
         assert (Ps, T) == (P, 0)
     else:
         assert Ps == P // 4 // 64 * 64 and T > 0

@@ -212,14 +212,20 @@ def test_tail_pieces_every_output_both_orders():
     assert torch.equal(a.view(torch.int32), b.view(torch.int32))
 
 
-@pytest.mark.parametrize("mode", ["fp8", "several_rows"])
-def test_tail_pieces_vector_kernel_varlen_both_orders(mode):
-    """Tail pieces on the vector-ALU kernel through yoco_cross_attn_varlen
-    (forced with YOCO_FLAG_VECTOR_KERNEL): an FP8 cache with one row per
-    request, or a bf16 cache with up to four rows per request; every output
-    against the oracle, and both orders give the same bits."""
+@pytest.mark.parametrize("mode", ["fp8", "several_rows", "fp8_matrix"])
+def test_tail_pieces_varlen_both_orders(mode):
+    """Tail pieces through yoco_cross_attn_varlen: on the vector-ALU kernel
+    (forced with YOCO_FLAG_VECTOR_KERNEL) with an FP8 cache and one row per
+    request, or a bf16 cache with up to four rows per request; and on the
+    matrix-core kernel with an FP8 cache (8 requests up to 32K tokens, whose
+    split there has pieces).  Every output against the oracle, and both
+    orders give the same bits."""
     rng = np.random.default_rng(79)
-    ctx = [4096] * 4 + [int(c) for c in rng.integers(1, 4097, size=28)]
+    if mode == "fp8_matrix":
+        ctx = [32768, 32768] + [int(c) for c in rng.integers(1, 32769, size=6)]
+    else:
+        ctx = [4096] * 4 + [int(c) for c in rng.integers(1, 4097, size=28)]
+    force = 0 if mode == "fp8_matrix" else yb.FLAG_VECTOR_KERNEL
     qlens = [min(c, 1 + i % 4) for i, c in enumerate(ctx)] if mode == "several_rows" else [1] * len(ctx)
     geom = synth.custom_geometry("bf16", 32, 8, 128, 16)
     meta = synth.make_varlen_metadata(geom, ctx, qlens, seed=23)
@@ -230,7 +236,7 @@ def test_tail_pieces_vector_kernel_varlen_both_orders(mode):
     seq = torch.from_numpy(meta.seq_lens).to(d)
     qsl = torch.from_numpy(meta.cu_seqlens).to(d)
     ql = max(qlens)
-    if mode == "fp8":
+    if mode.startswith("fp8"):
         kc, ks, vc, vs = synth.make_fp8_cache(meta, d, 23)
         kd = oracle.dequantize_cache(kc.cpu().numpy(), ks.cpu().numpy())
         vd = oracle.dequantize_cache(vc.cpu().numpy(), vs.cpu().numpy())
@@ -239,14 +245,13 @@ def test_tail_pieces_vector_kernel_varlen_both_orders(mode):
         kc, vc = synth.make_cache(meta, d, 23)
         kd, vd = host(kc), host(vc)
         dtype, extra = yb.DTYPE_BF16, {}
-    P, Ps, T, most = yb.cross_attn_partition_split(len(ctx), 8, 128, meta.max_seq_len, 16, 0, dtype, ql, 0,
-                                                   yb.FLAG_VECTOR_KERNEL)
-    say(f"cross_attn_varlen vector kernel, {mode}: P {P}, pieces of {Ps} over the last {T}")
+    P, Ps, T, most = yb.cross_attn_partition_split(len(ctx), 8, 128, meta.max_seq_len, 16, 0, dtype, ql, 0, force)
+    say(f"cross_attn_varlen {mode}: P {P}, pieces of {Ps} over the last {T}")
     assert T > 0 and Ps < P
     ref = oracle.cross_attention_varlen(host(q), kd, vd, meta.block_table, meta.seq_lens, meta.cu_seqlens,
                                         1.0 / math.sqrt(128), 0)
     outs = [yb.cross_attn_varlen(q, kc, vc, table, seq, meta.max_seq_len, query_start_loc=qsl, max_query_len=ql,
-                                 flags=yb.FLAG_VECTOR_KERNEL | f, **extra) for f in (0, yb.FLAG_REVERSE_ORDER)]
+                                 flags=force | f, **extra) for f in (0, yb.FLAG_REVERSE_ORDER)]
     torch.cuda.synchronize()
     err = _max_err(outs[0], ref)
     say(f"  max abs err {err:.3e}")

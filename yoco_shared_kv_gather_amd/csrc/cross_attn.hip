@@ -135,8 +135,8 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t head_d
   return static_cast<int32_t>(p);
 }
 
-// Tail pieces, when the library picks the partition for the vector kernel's
-// persistent schedule: the last T tokens of every context (and whatever is left over
+// Tail pieces, when the library picks the partition for the persistent
+// schedule: the last T tokens of every context (and whatever is left over
 // from the full partitions) are cut into pieces of P/4 tokens, which the
 // schedule runs after every full partition.  The queue then ends on short
 // items instead of leaving workgroups idle while the last ones finish a full
@@ -155,10 +155,11 @@ Split resolve_split(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, in
   s.P = resolve_partition(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, requested, matrix);
   s.Ps = s.P;
   s.T = 0;
-  // The matrix-core kernel pays a full pipeline start per item, which costs
-  // more than the pieces save (long512k with an FP8 cache: 184 us per layer
-  // without, 200 with).
-  if (requested > 0 || num_seqs > kMaxQueueSeqs || matrix) return s;
+  // (Both kernels: since the matrix-core kernel pipelines its items, the
+  // pieces pay there too -- mixed48 with an FP8 cache 214.9 -> 205.6 us per
+  // layer, long512k FP8 189.0 -> 185.9 -- except with four query rows on
+  // long512k, 360.8 -> 366.5.)
+  if (requested > 0 || num_seqs > kMaxQueueSeqs) return s;
   const int64_t ps = s.P / kPieceDiv / 64 * 64;
   if (ps < kMinPiece) return s;
   const int64_t pairs = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
