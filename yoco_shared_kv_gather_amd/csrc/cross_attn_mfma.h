@@ -477,10 +477,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   };
 
-  // ---- an item's block-table slice and query vectors: loaded into
-  // registers one item ahead (while the previous item streams), stored to LDS
-  // when the item starts.  Indices are clamped into range so the loads need
-  // no branch; what they stand in for is masked at the store.
+  // ---- an item's block-table slice and query vectors (and the block ids of
+  // this wavefront's first tiles): loaded into registers while the previous
+  // item streams, stored to LDS during its hand-over.  Indices are clamped
+  // into range so the loads need no branch; what they stand in for is masked
+  // at the store.
   constexpr int kTblPer = kMaxSliceBlocks / kThreads;
   constexpr int kQChunks = 16 * (D / 8);                 // 16-byte chunks of the 16 query vectors
   constexpr int kQPer = (kQChunks + kThreads - 1) / kThreads;
