@@ -320,8 +320,8 @@ int32_t yoco_kv_append_fp8(int32_t dtype, const void* x, int32_t num_tokens, int
  *                shorter).  0 lets the library pick P from the shape and the
  *                kernel that runs; with at most 2048 requests it also cuts
  *                the last T tokens of every context into pieces of Ps = P/4
- *                tokens (rounded down to a multiple of 64; only when that is
- *                256 or more).
+ *                tokens (rounded down to a multiple of 64, at least 256;
+ *                only when that is less than P).
  *                yoco_cross_attn_partition_split returns the plan.  The
  *                shorter pieces come after all full partitions in the
  *                schedule, so the work ends on short items.

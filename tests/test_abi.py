@@ -124,10 +124,11 @@ def test_partition_split_tiles_every_range(shape, dtype):
     if not matrix:
         assert P == yb.cross_attn_partition_tokens(R, hkv, d, max_len, bs, 0)
     assert P % 64 == 0 and Ps % 64 == 0 and 64 <= Ps <= P and 0 <= T <= max_len
-    if R > 2048 or P // 4 // 64 * 64 < 256:
+    piece = max(P // 4 // 64 * 64, 256)
+    if R > 2048 or piece >= P:
         assert (Ps, T) == (P, 0)
     else:
-        assert Ps == P // 4 // 64 * 64 and T > 0
+        assert Ps == piece and T > 0
     lens = set(range(0, min(max_len, 3 * P) + 1)) | set(range(max(0, max_len - 3 * P), max_len + 1))
     lens |= {T + k * P + e for k in range(0, max_len // P + 1) for e in (-1, 0, 1)}
     seen = 0

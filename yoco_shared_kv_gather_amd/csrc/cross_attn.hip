@@ -137,11 +137,14 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t head_d
 
 // Tail pieces, when the library picks the partition for the persistent
 // schedule: the last T tokens of every context (and whatever is left over
-// from the full partitions) are cut into pieces of P/4 tokens, which the
-// schedule runs after every full partition.  The queue then ends on short
-// items instead of leaving workgroups idle while the last ones finish a full
-// partition (which cost about 3% of a layer on decode32x32k and 8% on
-// long512k, with 2048-token partitions).  T is derived from the sizes alone
+// from the full partitions) are cut into pieces of P/4 tokens (at least 256,
+// and only when that is less than P), which the schedule runs after every
+// full partition.  The queue then ends on short items instead of leaving
+// workgroups idle while the last ones finish a full partition (which cost
+// about 3% of a layer on decode32x32k and 8% on long512k, with 2048-token
+// partitions; with 512-token partitions at head_dim 256, 256-token pieces
+// took decode64 from 102.0 to 98.7 us per layer, 71.8 to 68.2 with an FP8
+// cache, where 128-token pieces or twice the tail were slower).  T is derived from the sizes alone
 // (no device query, so the workspace helpers give the same plan): with
 // every context full length the pieces are about two rounds of a nominal
 // 512 resident workgroups, T = 256 P / (requests x KV heads).
@@ -160,8 +163,8 @@ Split resolve_split(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, in
   // layer, long512k FP8 189.0 -> 185.9 -- except with four query rows on
   // long512k, 360.8 -> 366.5.)
   if (requested > 0 || num_seqs > kMaxQueueSeqs) return s;
-  const int64_t ps = s.P / kPieceDiv / 64 * 64;
-  if (ps < kMinPiece) return s;
+  const int64_t ps = s.P / kPieceDiv / 64 * 64 > kMinPiece ? s.P / kPieceDiv / 64 * 64 : kMinPiece;
+  if (ps >= s.P) return s;
   const int64_t pairs = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
   int64_t t = yoco::round_up(yoco::ceil_div(kNominalSlots / 2 * s.P, pairs), ps);
   const int64_t len = max_seq_len > 0 ? max_seq_len : 1;
