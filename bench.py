@@ -769,11 +769,10 @@ def bench_cross(args, pool):
     attn_us = float(layer_ms.mean()) * 1e3
     achieved = layer_bytes / (attn_us * 1e-6) / 1e9
     group = geom.num_q_heads // geom.num_kv_heads
-    # the kernel the library picks: matrix cores for an FP8 cache, several
-    # query rows per request (bf16) or bf16 at head_dim 256, with
-    # block_size >= 16 and <= 2048 requests
-    mfma = ((args.fp8 or (geom.dtype == "bf16" and (Q > 1 or geom.head_dim == 256))) and R <= 2048
-            and geom.block_size >= 16 and not args.vector_kernel)
+    # the kernel the library picks for this call
+    mfma = yb.cross_attn_kernel(R, geom.num_kv_heads, geom.head_dim, meta.max_seq_len, geom.block_size,
+                                args.partition_tokens, attn_dtype, Q, W,
+                                yb.FLAG_VECTOR_KERNEL if args.vector_kernel else 0) == "matrix"
     rows_per_item = 0 if Q == 1 else (16 if mfma else 8) // group
     elem_type = 2 if args.fp8 else (1 if geom.dtype == "bf16" else 0)
     kname = "cross_attn_mfma_kernel" if mfma else "cross_attn_kernel"

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define YOCO_ABI_VERSION 6
+#define YOCO_ABI_VERSION 7
 
 typedef enum yoco_status {
   YOCO_OK = 0,
@@ -90,7 +90,8 @@ typedef enum yoco_dtype { YOCO_DTYPE_F32 = 0, YOCO_DTYPE_BF16 = 1, YOCO_DTYPE_FP
 
 /* yoco_cross_attn and yoco_cross_attn_varlen flag: run the vector-ALU kernel
  * even where the matrix-core kernel is the default (an FP8 cache, several
- * query rows per request, or a bf16 cache at head_dim 256).  Same results
+ * query rows per request, or a bf16 cache at head_dim 256 with partitions of
+ * at least 512 tokens; yoco_cross_attn_kernel tells which).  Same results
  * within the attention tolerance; for comparisons. */
 #define YOCO_FLAG_VECTOR_KERNEL 2u
 
@@ -370,6 +371,14 @@ int32_t yoco_cross_attn_partition_split(int32_t dtype, int32_t num_seqs, int32_t
                                         int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
                                         int32_t window, int32_t block_size, int32_t partition_tokens,
                                         uint32_t flags, int32_t* split);
+/* The attention kernel that yoco_cross_attn (max_query_len 1, window 0) or
+ * yoco_cross_attn_varlen runs for these arguments (an FP8 cache's scale
+ * arrays taken as 16-byte aligned): 1 the matrix-core kernel, 0 the
+ * vector-ALU kernel, -1 for invalid arguments.  Host only; for profiling and
+ * reports (the results agree within the attention tolerance either way). */
+int32_t yoco_cross_attn_kernel(int32_t dtype, int32_t num_seqs, int32_t max_query_len, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t max_seq_len, int32_t window, int32_t block_size,
+                               int32_t partition_tokens, uint32_t flags);
 int64_t yoco_cross_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                        int32_t head_dim, int32_t max_seq_len, int32_t block_size,
                                        int32_t partition_tokens);
@@ -484,7 +493,8 @@ int32_t yoco_gather_logits(const void* hidden, int64_t num_tokens, int64_t row_b
  * work item streams its K^/V^ rows once for several query vectors (rows x
  * heads of one KV group): up to 16 on the matrix-core kernel, which runs an
  * FP8 cache, bf16 with several rows per request and bf16 at head_dim 256
- * when block_size >= 16 (and the scales are 16-byte aligned), up to 8 on the
+ * (when that kernel's partitions hold at least 512 tokens) when
+ * block_size >= 16 (and the scales are 16-byte aligned), up to 8 on the
  * vector kernel otherwise or with YOCO_FLAG_VECTOR_KERNEL.  A NaN in a row that some of a request's rows read
  * may give NaN in all of that request's rows.  Errors as in yoco_cross_attn.
  */

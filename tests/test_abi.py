@@ -108,6 +108,34 @@ def _split_parts(m, P, Ps, T):
     return [P] * big + ([Ps] * (rest // Ps) + ([rest % Ps] if rest % Ps else []) if m > 0 else [0])
 
 
+def test_kernel_choice():
+    """Which attention kernel a call runs: the matrix cores for an FP8 cache,
+    for several query rows per request, and for bf16 at head_dim 256 while
+    that kernel's partitions hold at least 512 tokens; the vector ALUs
+    otherwise, when forced, below block_size 16 or above 2048 requests."""
+    bf, f8, f32 = yb.DTYPE_BF16, yb.DTYPE_FP8_E4M3, yb.DTYPE_F32
+    k = yb.cross_attn_kernel
+    d64 = (64, 2, 256, 8192, 16)                       # decode64's sizes
+    assert k(*d64, dtype=bf) == "matrix"
+    assert yb.cross_attn_partition_split(*d64, dtype=bf)[0] >= 512
+    for w in (512, 1024, 2048, 4096):                  # 256-token partitions on the matrix cores
+        assert yb.cross_attn_partition_split(*d64, dtype=f8, window=w)[0] < 512
+        assert k(*d64, dtype=bf, window=w) == "vector"
+        assert k(*d64, dtype=bf, window=w, max_query_len=4) == "matrix"
+        assert k(*d64, dtype=f8, window=w) == "matrix"
+    assert k(*d64, dtype=bf, partition_tokens=256) == "vector"
+    assert k(*d64, dtype=bf, partition_tokens=512) == "matrix"
+    assert k(32, 8, 128, 32768, 16, dtype=bf) == "vector"
+    assert k(32, 8, 128, 32768, 16, dtype=bf, max_query_len=4) == "matrix"
+    assert k(32, 8, 128, 32768, 16, dtype=f8) == "matrix"
+    assert k(32, 8, 128, 32768, 16, dtype=f32, max_query_len=4) == "vector"
+    assert k(32, 8, 128, 32768, 16, dtype=f8, flags=yb.FLAG_VECTOR_KERNEL) == "vector"
+    assert k(32, 8, 128, 32768, 8, dtype=f8) == "vector"
+    assert k(4096, 8, 128, 32768, 16, dtype=f8) == "vector"
+    assert k(32, 8, 128, 32768, 0, dtype=f8) is None
+    assert k(32, 8, 128, -1, 16, dtype=f8) is None
+
+
 @pytest.mark.parametrize("shape", SPLIT_SHAPES)
 @pytest.mark.parametrize("dtype", [yb.DTYPE_F32, yb.DTYPE_BF16, yb.DTYPE_FP8_E4M3])
 def test_partition_split_tiles_every_range(shape, dtype):
@@ -116,11 +144,12 @@ def test_partition_split_tiles_every_range(shape, dtype):
     they tile every key range of m <= max_seq_len tokens, and the reported
     count is the most any such range gets (attained, so the workspace holds no
     idle slots beyond it).  Pieces on the persistent schedule of either kernel
-    (the matrix-core kernel, which runs an FP8 cache and bf16 at head_dim 256
-    when block_size >= 16, with at least ~2048 items instead of ~1024)."""
+    (the matrix-core kernel, which runs an FP8 cache, several rows and bf16 at
+    head_dim 256 with long enough partitions when block_size >= 16, with at
+    least ~2048 items instead of ~1024)."""
     R, hkv, d, max_len, bs = shape
     P, Ps, T, most = yb.cross_attn_partition_split(R, hkv, d, max_len, bs, 0, dtype)
-    matrix = R <= 2048 and bs >= 16 and (dtype == yb.DTYPE_FP8_E4M3 or (dtype == yb.DTYPE_BF16 and d == 256))
+    matrix = yb.cross_attn_kernel(R, hkv, d, max_len, bs, 0, dtype) == "matrix"
     if not matrix:
         assert P == yb.cross_attn_partition_tokens(R, hkv, d, max_len, bs, 0)
     assert P % 64 == 0 and Ps % 64 == 0 and 64 <= Ps <= P and 0 <= T <= max_len

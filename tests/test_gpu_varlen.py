@@ -198,7 +198,7 @@ def test_spec_decode_step_chain():
     assert _max_err(out, case.oracle()) <= ATTN_ATOL
 
 
-@pytest.mark.parametrize("cid,ql,window", [(3, 4, 0), (4, 3, 2048), (5, 2, 0), (5, 1, 8192), (2, 4, 0)])
+@pytest.mark.parametrize("cid,ql,window", [(3, 4, 0), (4, 3, 2048), (5, 2, 0), (5, 1, 8192), (2, 4, 0), (2, 1, 512)])
 def test_varlen_full_size_every_output(cid, ql, window):
     """Full-size workloads with ql query rows per request (every request) and
     an optional window: every output row and head against the oracle, one

@@ -19,7 +19,7 @@ PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 # the CPU tests load); by default the one built next to this file.
 LIB_PATH = os.environ.get("YOCO_LIBRARY") or os.path.join(PKG_DIR, "libyoco.so")
 
-ABI_VERSION = 6
+ABI_VERSION = 7
 YOCO_OK = 0
 YOCO_ERR_INVALID_ARGUMENT = 1
 YOCO_ERR_UNSUPPORTED = 2
@@ -50,6 +50,7 @@ SIGNATURES = {
                               _vp, _i64, _vp]),
     "yoco_cross_attn_partition_tokens": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "yoco_cross_attn_partition_split": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _u32, _vp]),
+    "yoco_cross_attn_kernel": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _u32]),
     "yoco_cross_attn_workspace_size": (_i64, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "yoco_cross_attn": (_i32, [_i32, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _i32, _vp, _i32, _f32,
                                _i32, _u32, _vp, _vp, _i64, _vp]),
@@ -259,6 +260,15 @@ def cross_attn_partition_split(num_seqs, num_kv_heads, head_dim, max_seq_len, bl
                                                      max_seq_len, window, block_size, partition_tokens, flags,
                                                      split))
     return None if most < 0 else (int(split[0]), int(split[1]), int(split[2]), most)
+
+
+def cross_attn_kernel(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens=0,
+                      dtype=DTYPE_BF16, max_query_len=1, window=0, flags=0):
+    """The attention kernel the call with these arguments runs: "matrix"
+    (matrix cores) or "vector" (vector ALUs), or None for invalid arguments."""
+    kind = int(lib().yoco_cross_attn_kernel(dtype, num_seqs, max_query_len, num_kv_heads, head_dim, max_seq_len,
+                                            window, block_size, partition_tokens, flags))
+    return None if kind < 0 else ("matrix" if kind == 1 else "vector")
 
 
 def cross_attn_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim, max_seq_len, block_size,

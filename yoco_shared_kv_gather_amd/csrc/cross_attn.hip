@@ -178,14 +178,28 @@ Split resolve_split(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, in
 // outgrows the vector ALUs (an FP8 cache, or several query rows per request),
 // and for a bf16 cache at head_dim 256, where the matrix kernel's four
 // head_dim slices per key tile stream faster than the vector kernel's 16
-// lanes per row (decode64: 110.5 -> 104.6 us per layer); persistent schedule
-// only.  (It reads 16-key tiles that lie inside one block: block_size >= 16;
-// an FP8 cache's scale arrays must be 16-byte aligned.)
-bool matrix_kernel(int32_t dtype, int32_t num_seqs, bool several_rows, int32_t head_dim, int32_t block_size,
-                   uint32_t flags, bool scales_aligned) {
+// lanes per row (decode64: 110.5 -> 104.6 us per layer) -- as long as its
+// items stay long: where its plan (at least ~2048 items) cuts the contexts
+// into partitions shorter than kMinMatrixBf16Partition tokens, the vector
+// kernel's lighter item hand-over wins (decode64 with a window of 512, 1024,
+// 2048, 4096 tokens: 25.8 / 36.9 / 58.5 / 83.6 us per layer on the matrix
+// cores, 24.5 / 34.3 / 55.7 / 81.5 on the vector ALUs; no window: 98.2
+// against 105.2).  Persistent schedule only.  (It reads 16-key tiles that
+// lie inside one block: block_size >= 16; an FP8 cache's scale arrays must be
+// 16-byte aligned.)  span is the length the partitions of the longest key
+// range cover (effective_len).
+constexpr int32_t kMinMatrixBf16Partition = 512;
+
+bool matrix_kernel(int32_t dtype, int32_t num_seqs, bool several_rows, int32_t num_kv_heads, int32_t head_dim,
+                   int32_t span, int32_t block_size, int32_t partition_tokens, uint32_t flags,
+                   bool scales_aligned) {
   const bool f8 = dtype == YOCO_DTYPE_FP8_E4M3;
-  return (flags & YOCO_FLAG_VECTOR_KERNEL) == 0 && num_seqs <= kMaxQueueSeqs && block_size >= 16 &&
-         (!f8 || scales_aligned) && (f8 || (dtype == YOCO_DTYPE_BF16 && (several_rows || head_dim == 256)));
+  if ((flags & YOCO_FLAG_VECTOR_KERNEL) != 0 || num_seqs > kMaxQueueSeqs || block_size < 16) return false;
+  if (f8) return scales_aligned;
+  if (dtype != YOCO_DTYPE_BF16) return false;
+  if (several_rows) return true;
+  return head_dim == 256 && resolve_partition(num_seqs, num_kv_heads, head_dim, span, block_size, partition_tokens,
+                                              true) >= kMinMatrixBf16Partition;
 }
 
 // Partition slots a workspace needs for calls of these sizes with any cache
@@ -322,8 +336,9 @@ int32_t run_cross_attn(const AttnCall& c, const char* who) {
     return fail(YOCO_ERR_INVALID_ARGUMENT, "%s: q, caches and out must be 16-byte aligned", who);
 
   const int32_t span = effective_len(c.max_seq_len, c.max_qlen, c.window);
-  const bool mfma = matrix_kernel(c.dtype, c.num_seqs, c.qsl != nullptr && c.max_qlen > 1, c.head_dim, c.block_size,
-                                  c.flags, aligned16(c.k_scale) && aligned16(c.v_scale));
+  const bool mfma = matrix_kernel(c.dtype, c.num_seqs, c.qsl != nullptr && c.max_qlen > 1, c.num_kv_heads,
+                                  c.head_dim, span, c.block_size, c.partition_tokens, c.flags,
+                                  aligned16(c.k_scale) && aligned16(c.v_scale));
   const Split split = resolve_split(c.num_seqs, c.num_kv_heads, c.head_dim, span, c.block_size,
                                     c.partition_tokens, mfma);
   const int32_t nparts = max_parts(split, span);
@@ -486,7 +501,8 @@ extern "C" int32_t yoco_cross_attn_noalloc(int32_t dtype, const void* q, int32_t
   // the scratch the call needs, checked before anything is looked up or launched
   if (num_seqs >= 0 && num_q_heads > 0 && num_kv_heads > 0 && head_dim > 0 && max_seq_len >= 0 && block_size > 0 &&
       partition_tokens >= 0) {
-    const bool mfma = matrix_kernel(dtype, num_seqs, false, head_dim, block_size, flags, true);
+    const bool mfma = matrix_kernel(dtype, num_seqs, false, num_kv_heads, head_dim, max_seq_len, block_size,
+                                    partition_tokens, flags, true);
     const Split sp = resolve_split(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens, mfma);
     const int64_t need = workspace_layout(num_seqs, num_q_heads, head_dim, max_parts(sp, max_seq_len)).total;
     if (need > YOCO_CROSS_ATTN_NOALLOC_SCRATCH_BYTES)
@@ -522,12 +538,27 @@ extern "C" int32_t yoco_cross_attn_partition_split(int32_t dtype, int32_t num_se
       split == nullptr)
     return -1;
   const int32_t span = effective_len(max_seq_len, max_query_len, window);
-  const bool mfma = matrix_kernel(dtype, num_seqs, max_query_len > 1, head_dim, block_size, flags, true);
+  const bool mfma = matrix_kernel(dtype, num_seqs, max_query_len > 1, num_kv_heads, head_dim, span, block_size,
+                                  partition_tokens, flags, true);
   const Split s = resolve_split(num_seqs, num_kv_heads, head_dim, span, block_size, partition_tokens, mfma);
   split[0] = s.P;
   split[1] = s.Ps;
   split[2] = s.T;
   return max_parts(s, span);
+}
+
+extern "C" int32_t yoco_cross_attn_kernel(int32_t dtype, int32_t num_seqs, int32_t max_query_len,
+                                          int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
+                                          int32_t window, int32_t block_size, int32_t partition_tokens,
+                                          uint32_t flags) {
+  if (partition_tokens < 0 || max_seq_len < 0 || max_query_len < 0 || window < 0 || block_size <= 0 ||
+      num_seqs < 0 || num_kv_heads <= 0 || head_dim <= 0)
+    return -1;
+  const int32_t span = effective_len(max_seq_len, max_query_len, window);
+  return matrix_kernel(dtype, num_seqs, max_query_len > 1, num_kv_heads, head_dim, span, block_size,
+                       partition_tokens, flags, true)
+             ? 1
+             : 0;
 }
 
 extern "C" int64_t yoco_cross_attn_workspace_size(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
