@@ -250,8 +250,8 @@ class OraclePool:
 
 
 def start_cpu_pool(args):
-    """The CPU baseline's workers: one per usable core, at most 16 (a GPU machine
-    grants one GPU's share of its CPUs)."""
+    """The CPU baseline's workers: one per usable core, at most 16 (about one
+    GPU's share of a multi-GPU host's CPUs)."""
     if args.no_cpu_baseline:
         return None
     _, usable = host_cores()
