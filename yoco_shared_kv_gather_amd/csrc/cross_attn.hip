@@ -144,10 +144,11 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t head_d
 // about 3% of a layer on decode32x32k and 8% on long512k, with 2048-token
 // partitions; with 512-token partitions at head_dim 256, 256-token pieces
 // took decode64 from 102.0 to 98.7 us per layer, 71.8 to 68.2 with an FP8
-// cache, where 128-token pieces or twice the tail were slower).  T is derived from the sizes alone
-// (no device query, so the workspace helpers give the same plan): with
-// every context full length the pieces are about two rounds of a nominal
-// 512 resident workgroups, T = 256 P / (requests x KV heads).
+// cache, where 128-token pieces or twice the tail were slower).  T is
+// derived from the sizes alone (no device query, so the workspace helpers
+// give the same plan): with every context full length the pieces are about
+// two rounds of a nominal 512 resident workgroups, T = 256 P / (requests x
+// KV heads).
 constexpr int kPieceDiv = 4;
 constexpr int64_t kMinPiece = 256;
 constexpr int64_t kNominalSlots = 512;
