@@ -111,16 +111,17 @@ def _split_parts(m, P, Ps, T):
 def test_kernel_choice():
     """Which attention kernel a call runs: the matrix cores for an FP8 cache,
     for several query rows per request, and for bf16 at head_dim 256 while
-    that kernel's partitions hold at least 512 tokens; the vector ALUs
-    otherwise, when forced, below block_size 16 or above 2048 requests."""
+    its partitions hold at least 512 tokens; the vector ALUs otherwise, when
+    forced, below block_size 16 or above 2048 requests."""
     bf, f8, f32 = yb.DTYPE_BF16, yb.DTYPE_FP8_E4M3, yb.DTYPE_F32
     k = yb.cross_attn_kernel
     d64 = (64, 2, 256, 8192, 16)                       # decode64's sizes
     assert k(*d64, dtype=bf) == "matrix"
     assert yb.cross_attn_partition_split(*d64, dtype=bf)[0] >= 512
-    for w in (512, 1024, 2048, 4096):                  # 256-token partitions on the matrix cores
-        assert yb.cross_attn_partition_split(*d64, dtype=f8, window=w)[0] < 512
-        assert k(*d64, dtype=bf, window=w) == "vector"
+    for w in (512, 1024, 2048, 4096):
+        short = yb.cross_attn_partition_split(*d64, dtype=bf, window=w)[0] < 512
+        assert short == (w <= 2048)
+        assert k(*d64, dtype=bf, window=w) == ("vector" if short else "matrix")
         assert k(*d64, dtype=bf, window=w, max_query_len=4) == "matrix"
         assert k(*d64, dtype=f8, window=w) == "matrix"
     assert k(*d64, dtype=bf, partition_tokens=256) == "vector"
@@ -146,11 +147,11 @@ def test_partition_split_tiles_every_range(shape, dtype):
     idle slots beyond it).  Pieces on the persistent schedule of either kernel
     (the matrix-core kernel, which runs an FP8 cache, several rows and bf16 at
     head_dim 256 with long enough partitions when block_size >= 16, with at
-    least ~2048 items instead of ~1024)."""
+    least ~2048 items instead of ~1024 over an FP8 cache)."""
     R, hkv, d, max_len, bs = shape
     P, Ps, T, most = yb.cross_attn_partition_split(R, hkv, d, max_len, bs, 0, dtype)
     matrix = yb.cross_attn_kernel(R, hkv, d, max_len, bs, 0, dtype) == "matrix"
-    if not matrix:
+    if not (matrix and dtype == yb.DTYPE_FP8_E4M3):       # the bf16 matrix plan is the vector kernel's
         assert P == yb.cross_attn_partition_tokens(R, hkv, d, max_len, bs, 0)
     assert P % 64 == 0 and Ps % 64 == 0 and 64 <= Ps <= P and 0 <= T <= max_len
     piece = max(P // 4 // 64 * 64, 256)
@@ -179,11 +180,11 @@ def test_partition_split_tiles_every_range(shape, dtype):
 @pytest.mark.parametrize("shape", SPLIT_SHAPES)
 def test_workspace_holds_either_kernels_partitions(shape):
     """The workspace helpers do not take the cache type: they size for the
-    larger of the vector-ALU kernel's plan (fp32 cache) and the matrix-core
-    kernel's (FP8 cache)."""
+    largest of the plans of an fp32 cache (vector ALUs), a bf16 cache (either
+    kernel, one plan) and an FP8 cache (matrix cores, twice the item floor)."""
     R, hkv, d, max_len, bs = shape
     most = max(yb.cross_attn_partition_split(R, hkv, d, max_len, bs, 0, dt)[3]
-               for dt in (yb.DTYPE_F32, yb.DTYPE_FP8_E4M3))
+               for dt in (yb.DTYPE_F32, yb.DTYPE_BF16, yb.DTYPE_FP8_E4M3))
     ws = yb.cross_attn_workspace_size(R, 8 * hkv, hkv, d, max_len, bs, 0)
     acc = R * 8 * hkv * most * d * 4
     assert most == 1 and ws == yb.CROSS_ATTN_QUEUE_BYTES or \

@@ -93,13 +93,15 @@ int32_t max_partition(int32_t block_size) {
   return static_cast<int32_t>(cap < 16384 ? cap : 16384);
 }
 
-// `matrix`: the call runs the matrix-core kernel, which starts every item
-// from an empty pipeline (its next-item fetch and first tile are not
-// overlapped with the previous item), so it wants at least about 2048 items
-// when every context is full length; the vector kernel, which hands items
-// over while the next one's first rows are in flight, at least about 1024.
+// `fp8_matrix`: the call runs the matrix-core kernel over an 8-bit cache,
+// whose items are short in time for their tokens (half the bytes), so it
+// wants at least about 2048 items when every context is full length; the
+// vector kernel and the matrix-core kernel over a bf16 cache at least about
+// 1024.  Measured against a 2048-item floor for both matrix cases: bf16
+// decode64 98.3 -> 97.1 us per layer, long512k with four rows 364.8 -> 357.0;
+// FP8 long512k 184.7 -> 188.9 (worse), FP8 decode64 unchanged.
 int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
-                          int32_t block_size, int32_t requested, bool matrix) {
+                          int32_t block_size, int32_t requested, bool fp8_matrix) {
   if (requested > 0) return requested;
   const int64_t pairs = static_cast<int64_t>(num_seqs > 0 ? num_seqs : 1) * (num_kv_heads > 0 ? num_kv_heads : 1);
   const int64_t len = max_seq_len > 0 ? max_seq_len : 1;
@@ -107,7 +109,7 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t head_d
   int64_t p;
   if (num_seqs <= kMaxQueueSeqs) {
     // Persistent schedule: items of about 2 MB of bf16 K^/V^ (P*D = 2^19),
-    // but at least about 1024 items (matrix kernel 2048) when every context
+    // but at least about 1024 items (2048 for fp8_matrix) when every context
     // is full length and at most 256 partitions per request, so the merge
     // stays small next to the stream.  Each item ends in a hand-over
     // (combine, write the partial, stage the next slice) during which the
@@ -118,7 +120,7 @@ int32_t resolve_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t head_d
     // decode32x32k with an FP8 cache 401 -> 365 us, with four query rows
     // 763 -> 691 us.
     p = yoco::round_up((int64_t{1} << 19) / d, 64);
-    const int64_t min_items = matrix ? 2048 : 1024;
+    const int64_t min_items = fp8_matrix ? 2048 : 1024;
     const int64_t p_items = yoco::round_up(yoco::ceil_div(len, yoco::ceil_div(min_items, pairs)), 64);
     if (p > p_items) p = p_items;
     if (p < 256) p = 256;
@@ -154,9 +156,9 @@ constexpr int64_t kMinPiece = 256;
 constexpr int64_t kNominalSlots = 512;
 
 Split resolve_split(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t max_seq_len,
-                    int32_t block_size, int32_t requested, bool matrix) {
+                    int32_t block_size, int32_t requested, bool fp8_matrix) {
   Split s;
-  s.P = resolve_partition(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, requested, matrix);
+  s.P = resolve_partition(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, requested, fp8_matrix);
   s.Ps = s.P;
   s.T = 0;
   // (Both kernels: since the matrix-core kernel pipelines its items, the
@@ -180,12 +182,13 @@ Split resolve_split(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, in
 // and for a bf16 cache at head_dim 256, where the matrix kernel's four
 // head_dim slices per key tile stream faster than the vector kernel's 16
 // lanes per row (decode64: 110.5 -> 104.6 us per layer) -- as long as its
-// items stay long: where its plan (at least ~2048 items) cuts the contexts
-// into partitions shorter than kMinMatrixBf16Partition tokens, the vector
-// kernel's lighter item hand-over wins (decode64 with a window of 512, 1024,
-// 2048, 4096 tokens: 25.8 / 36.9 / 58.5 / 83.6 us per layer on the matrix
-// cores, 24.5 / 34.3 / 55.7 / 81.5 on the vector ALUs; no window: 98.2
-// against 105.2).  Persistent schedule only.  (It reads 16-key tiles that
+// items stay long: where the plan cuts the contexts into partitions shorter
+// than kMinMatrixBf16Partition tokens, the vector kernel's lighter item
+// hand-over wins (decode64 with a window of 512, 1024, 2048 tokens, 256-token
+// partitions: 25.8 / 36.9 / 58.5 us per layer on the matrix cores, 24.5 /
+// 34.3 / 55.7 on the vector ALUs; with 4096 tokens, 512-token partitions:
+// 81.2 against 81.6; no window: 97.1 against 105.2).  Persistent schedule
+// only.  (It reads 16-key tiles that
 // lie inside one block: block_size >= 16; an FP8 cache's scale arrays must be
 // 16-byte aligned.)  span is the length the partitions of the longest key
 // range cover (effective_len).
@@ -200,11 +203,13 @@ bool matrix_kernel(int32_t dtype, int32_t num_seqs, bool several_rows, int32_t n
   if (dtype != YOCO_DTYPE_BF16) return false;
   if (several_rows) return true;
   return head_dim == 256 && resolve_partition(num_seqs, num_kv_heads, head_dim, span, block_size, partition_tokens,
-                                              true) >= kMinMatrixBf16Partition;
+                                              false) >= kMinMatrixBf16Partition;
 }
 
 // Partition slots a workspace needs for calls of these sizes with any cache
-// type and flags: the larger of the two kernels' plans.
+// type and flags: the larger of the two plans, the vector kernel's (which the
+// matrix-core kernel shares over a bf16 cache) and the matrix-core kernel's
+// over an 8-bit cache.
 int32_t workspace_parts(int32_t num_seqs, int32_t num_kv_heads, int32_t head_dim, int32_t span, int32_t block_size,
                         int32_t requested);
 
@@ -341,7 +346,7 @@ int32_t run_cross_attn(const AttnCall& c, const char* who) {
                                   c.head_dim, span, c.block_size, c.partition_tokens, c.flags,
                                   aligned16(c.k_scale) && aligned16(c.v_scale));
   const Split split = resolve_split(c.num_seqs, c.num_kv_heads, c.head_dim, span, c.block_size,
-                                    c.partition_tokens, mfma);
+                                    c.partition_tokens, mfma && c.dtype == YOCO_DTYPE_FP8_E4M3);
   const int32_t nparts = max_parts(split, span);
   if (nparts > kMaxParts)
     return fail(YOCO_ERR_UNSUPPORTED, "%s: %d partitions per request exceed %d", who, nparts, kMaxParts);
@@ -504,7 +509,8 @@ extern "C" int32_t yoco_cross_attn_noalloc(int32_t dtype, const void* q, int32_t
       partition_tokens >= 0) {
     const bool mfma = matrix_kernel(dtype, num_seqs, false, num_kv_heads, head_dim, max_seq_len, block_size,
                                     partition_tokens, flags, true);
-    const Split sp = resolve_split(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens, mfma);
+    const Split sp = resolve_split(num_seqs, num_kv_heads, head_dim, max_seq_len, block_size, partition_tokens,
+                                   mfma && dtype == YOCO_DTYPE_FP8_E4M3);
     const int64_t need = workspace_layout(num_seqs, num_q_heads, head_dim, max_parts(sp, max_seq_len)).total;
     if (need > YOCO_CROSS_ATTN_NOALLOC_SCRATCH_BYTES)
       return yoco::fail(YOCO_ERR_WORKSPACE_TOO_SMALL,
@@ -541,7 +547,8 @@ extern "C" int32_t yoco_cross_attn_partition_split(int32_t dtype, int32_t num_se
   const int32_t span = effective_len(max_seq_len, max_query_len, window);
   const bool mfma = matrix_kernel(dtype, num_seqs, max_query_len > 1, num_kv_heads, head_dim, span, block_size,
                                   partition_tokens, flags, true);
-  const Split s = resolve_split(num_seqs, num_kv_heads, head_dim, span, block_size, partition_tokens, mfma);
+  const Split s = resolve_split(num_seqs, num_kv_heads, head_dim, span, block_size, partition_tokens,
+                                mfma && dtype == YOCO_DTYPE_FP8_E4M3);
   split[0] = s.P;
   split[1] = s.Ps;
   split[2] = s.T;
