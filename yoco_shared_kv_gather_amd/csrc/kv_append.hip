@@ -198,17 +198,20 @@ __global__ __launch_bounds__(kGemmThreads) __attribute__((amdgpu_waves_per_eu(2)
     for (int i = 0; i < kAP; ++i) {
       const int row = rbase + kRp * i;
       *reinterpret_cast<uint4*>(&as[row * kLdsStride + ((kc ^ swz(row)) * 8)]) = r.a[i];
-      // a repeated tile adds nothing (a select, not a branch: the stores,
-      // loads and products of a half-iteration stay one block the
-      // scheduler can interleave)
+      // a repeated tile adds nothing (one select per chunk, not a branch:
+      // the stores, loads and products of a half-iteration stay one block
+      // the scheduler can interleave; a select per element cost 0.8% on
+      // mixed48's 67,387 rows, 884.5 -> 877.7 us)
       const uint32_t* u = reinterpret_cast<const uint32_t*>(&r.a[i]);
+      float part = 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float lo = real ? bf16_lo(u[e]) : 0.0f;
-        const float hi = real ? bf16_hi(u[e]) : 0.0f;
-        sumsq[i] = fmaf(lo, lo, sumsq[i]);
-        sumsq[i] = fmaf(hi, hi, sumsq[i]);
+        const float lo = bf16_lo(u[e]);
+        const float hi = bf16_hi(u[e]);
+        part = fmaf(lo, lo, part);
+        part = fmaf(hi, hi, part);
       }
+      sumsq[i] += real ? part : 0.0f;
     }
 #pragma unroll
     for (int i = 0; i < kBP; ++i) {
