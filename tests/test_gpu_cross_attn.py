@@ -291,3 +291,34 @@ def test_matrix_kernel_many_items_both_orders(several):
     say(f"  max abs err {err:.3e}")
     assert err <= ATTN_ATOL
     assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+
+
+@pytest.mark.gpu
+def test_kernel_query_names_the_kernel_that_runs():
+    """yoco_cross_attn_kernel names the kernel a call launches, checked through
+    the results on decode64's full size (bf16 at head_dim 256): where it
+    reports the vector ALUs, forcing the vector kernel gives the same bits;
+    where it reports the matrix cores, the outputs differ (the kernels sum in
+    different orders), and both agree with the oracle."""
+    w = DeviceWorkload(2, "full", layers=1)
+    g = w.geom
+    for window in (0, 512):
+        kind = yb.cross_attn_kernel(w.meta.num_reqs, g.num_kv_heads, g.head_dim, w.meta.max_seq_len, g.block_size,
+                                    dtype=yb.DTYPE_BF16, window=window)
+        say(f"decode64 full, window {window}: {kind} kernel")
+
+        def run(flags):
+            if window == 0:
+                return w.attn(0, flags=flags)
+            return yb.cross_attn_varlen(w.q[0], w.k, w.v, w.block_table, w.seq_lens, w.meta.max_seq_len,
+                                        window=window, flags=flags)
+
+        default, forced = run(0), run(yb.FLAG_VECTOR_KERNEL)
+        torch.cuda.synchronize()
+        assert kind == ("matrix" if window == 0 else "vector")
+        assert torch.equal(default, forced) == (kind == "vector")
+        ref = oracle.cross_attention_varlen(host(w.q[0]), host(w.k), host(w.v), w.meta.block_table,
+                                            w.meta.seq_lens, np.arange(w.meta.num_reqs + 1),
+                                            1.0 / math.sqrt(g.head_dim), window)
+        for out in (default, forced):
+            assert _max_err(out, ref) <= ATTN_ATOL
